@@ -1,0 +1,138 @@
+"""Workload shapes and seeded synthetic inputs for the TANGO / WANGO block.
+
+This module holds no arithmetic of the method: it names the five workload
+shapes and draws the seeded inputs that both the HIP path and the CPU checker
+consume.  Inputs are drawn in float64 with numpy's PCG64 generator in the order
+h, W_g, W_v, W_q, W_k, W_o, scaled to N(0, 1) activations and N(0, 1/fan_in)
+weights, and rounded once to the I/O dtype (float64 -> float32 -> bfloat16,
+round to nearest even).  Both sides use the same rounded values.
+"""
+from __future__ import annotations
+
+import math
+from dataclasses import dataclass, replace
+from typing import Optional
+
+import numpy as np
+
+
+@dataclass(frozen=True)
+class Workload:
+    """One block workload.  ``mode`` is "tango" (full prefix) or "wango"
+    (window + running sums).  ``repeats`` is the number of shared-weight
+    applications.  ``dtype`` is the storage dtype of activations and weights
+    ("f32" or "bf16"); accumulation is always float32."""
+    name: str
+    mode: str
+    dtype: str
+    B: int
+    T: int
+    d_model: int
+    d_gate: int
+    n_heads: int
+    head_dim: int
+    window: int = 0
+    chunk: int = 0
+    repeats: int = 1
+    seed: int = 0
+    theta: float = math.log(10.0)      # cosine-similarity scale 10
+    rope_base: float = 10000.0
+    rms_eps: float = 1e-6
+    null_bias: Optional[float] = None  # None: null gate off
+
+    @property
+    def tokens(self) -> int:
+        return self.B * self.T
+
+    def scaled(self, **kw) -> "Workload":
+        return replace(self, **kw)
+
+
+# The five workloads: TANGO fp32 T=256; TANGO bf16 B=8 T=2048; TANGO bf16 T=8192
+# applied 4 times; WANGO bf16 T=8192 window 256 (two heads of 64); WANGO bf16
+# B=2 T=65536 window 512 applied 8 times.
+WORKLOADS = {
+    "tango_f32_t256": Workload("tango_f32_t256", "tango", "f32", 1, 256, 512, 1024, 1, 128,
+                               seed=0),
+    "tango_bf16_b8_t2048": Workload("tango_bf16_b8_t2048", "tango", "bf16", 8, 2048, 512, 2048,
+                                    1, 128, seed=1),
+    "tango_bf16_t8192_r4": Workload("tango_bf16_t8192_r4", "tango", "bf16", 1, 8192, 512, 2048,
+                                    1, 128, repeats=4, seed=2),
+    "wango_bf16_t8192_w256": Workload("wango_bf16_t8192_w256", "wango", "bf16", 1, 8192, 512,
+                                      2048, 2, 64, window=256, chunk=128, seed=3),
+    "wango_bf16_b2_t65536_w512_r8": Workload("wango_bf16_b2_t65536_w512_r8", "wango", "bf16", 2,
+                                             65536, 512, 2048, 1, 128, window=512, chunk=128,
+                                             repeats=8, seed=4),
+}
+WORKLOAD_ORDER = list(WORKLOADS)
+
+
+def round_f32(a: np.ndarray) -> np.ndarray:
+    """float64 -> float32 (round to nearest even)."""
+    return np.asarray(a, dtype=np.float32)
+
+
+def round_bf16(a: np.ndarray) -> np.ndarray:
+    """float64 -> float32 -> bfloat16 (round to nearest even at each step),
+    returned as float32 values that bfloat16 represents exactly."""
+    a32 = np.ascontiguousarray(np.asarray(a, dtype=np.float32))
+    u = a32.view(np.uint32).astype(np.uint64)
+    lsb = (u >> np.uint64(16)) & np.uint64(1)
+    r = (u + np.uint64(0x7FFF) + lsb) & np.uint64(0xFFFF0000)
+    out = r.astype(np.uint32).view(np.float32)
+    nan = np.isnan(a32)
+    if nan.any():
+        out = np.where(nan, np.float32(np.nan), out)
+    return out
+
+
+def quantize(a: np.ndarray, dtype: str) -> np.ndarray:
+    if dtype == "f32":
+        return round_f32(a)
+    if dtype == "bf16":
+        return round_bf16(a)
+    raise ValueError(dtype)
+
+
+@dataclass
+class Inputs:
+    """Seeded inputs as float32 arrays whose values the I/O dtype holds exactly."""
+    h: np.ndarray      # [B, T, d]
+    w_g: np.ndarray    # [F, d]
+    w_v: np.ndarray    # [F, d]
+    w_q: np.ndarray    # [H*d_h, d]
+    w_k: np.ndarray    # [H*d_h, d]
+    w_o: np.ndarray    # [d, F]
+    gain: Optional[np.ndarray]       # [d] float32 or None (= 1)
+    theta: np.ndarray                # [H] float32
+    null_bias: Optional[np.ndarray]  # [H] float32 or None (null gate off)
+
+
+def make_inputs(w: Workload, seed: Optional[int] = None, gain: Optional[np.ndarray] = None,
+                h_override: Optional[np.ndarray] = None) -> Inputs:
+    """Draw the inputs of workload ``w`` (seed defaults to the workload's)."""
+    rng = np.random.Generator(np.random.PCG64(w.seed if seed is None else seed))
+    d, F, hd = w.d_model, w.d_gate, w.n_heads * w.head_dim
+    h = rng.standard_normal((w.B, w.T, d))
+    w_g = rng.standard_normal((F, d)) / math.sqrt(d)
+    w_v = rng.standard_normal((F, d)) / math.sqrt(d)
+    w_q = rng.standard_normal((hd, d)) / math.sqrt(d)
+    w_k = rng.standard_normal((hd, d)) / math.sqrt(d)
+    w_o = rng.standard_normal((d, F)) / math.sqrt(F)
+    if h_override is not None:
+        h = h_override
+    q = lambda a: quantize(a, w.dtype)  # noqa: E731
+    theta = np.full(w.n_heads, w.theta, dtype=np.float32)
+    nb = None if w.null_bias is None else np.full(w.n_heads, w.null_bias, dtype=np.float32)
+    gq = None if gain is None else q(gain)
+    return Inputs(q(h), q(w_g), q(w_v), q(w_q), q(w_k), q(w_o), gq, theta, nb)
+
+
+def small_workload(mode: str = "tango", dtype: str = "bf16", B: int = 1, T: int = 200,
+                   d_model: int = 128, d_gate: int = 256, n_heads: int = 1, head_dim: int = 64,
+                   window: int = 64, chunk: int = 64, repeats: int = 1, seed: int = 7,
+                   **kw) -> Workload:
+    """A small workload of the same structure, for tests the checker finishes fast."""
+    return Workload(f"small_{mode}", mode, dtype, B, T, d_model, d_gate, n_heads, head_dim,
+                    window=window if mode == "wango" else 0,
+                    chunk=chunk if mode == "wango" else 0, repeats=repeats, seed=seed, **kw)

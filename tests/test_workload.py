@@ -1,0 +1,33 @@
+"""Seeded input generator: determinism, shapes and dtype rounding."""
+import numpy as np
+import torch
+
+from cross_token_gated_amd import workload as wl
+
+
+def test_bf16_rounding_matches_torch():
+    rng = np.random.default_rng(0)
+    a = np.concatenate([rng.standard_normal(100000) * 10.0 ** rng.integers(-8, 8, 100000),
+                        [0.0, -0.0, 1 + 2 ** -8, 1 + 3 * 2 ** -8, 65504.0, 1e-40]])
+    ours = wl.round_bf16(a)
+    ref = torch.from_numpy(a.astype(np.float32)).to(torch.bfloat16).to(torch.float32).numpy()
+    np.testing.assert_array_equal(ours, ref)
+
+
+def test_inputs_are_deterministic_and_quantized():
+    w = wl.small_workload(T=33, d_model=64, d_gate=128, head_dim=32)
+    a, b = wl.make_inputs(w), wl.make_inputs(w)
+    for f in ("h", "w_g", "w_v", "w_q", "w_k", "w_o"):
+        x, y = getattr(a, f), getattr(b, f)
+        np.testing.assert_array_equal(x, y)
+        np.testing.assert_array_equal(wl.round_bf16(x), x)
+    assert a.h.shape == (1, 33, 64) and a.w_o.shape == (64, 128)
+    assert abs(float(a.w_g.std()) * 8.0 - 1.0) < 0.05
+
+
+def test_workload_table():
+    t = wl.WORKLOADS
+    assert [t[k].T for k in wl.WORKLOAD_ORDER] == [256, 2048, 8192, 8192, 65536]
+    assert t["wango_bf16_t8192_w256"].n_heads * t["wango_bf16_t8192_w256"].head_dim == 128
+    assert t["tango_bf16_t8192_r4"].repeats == 4
+    assert t["wango_bf16_b2_t65536_w512_r8"].repeats == 8

@@ -1,0 +1,154 @@
+"""Python binding of libtango.so with the C ABI's names.
+
+Argument marshalling only: tensors are torch tensors on the GPU (torch owns
+the device memory and the stream); every step of the block runs in the HIP
+kernels of libtango.so.  There is no fallback path: if the library is not
+built, every call raises.
+"""
+from __future__ import annotations
+
+import ctypes
+from dataclasses import dataclass
+from typing import Optional
+
+import torch
+
+from . import _lib
+from ._lib import Shape, Weights, check, load
+
+ROW_PAD = 128   # intermediate rows are padded per sequence to a multiple of this
+
+
+def padded_len(T: int) -> int:
+    return (T + ROW_PAD - 1) // ROW_PAD * ROW_PAD
+
+
+_DTYPES = {torch.float32: _lib.TANGO_F32, torch.bfloat16: _lib.TANGO_BF16}
+
+
+@dataclass
+class BlockWeights:
+    """Device tensors of one block ([F, d] gate/value, [H*d_h, d] query/key,
+    [d, F] output, optional [d] RMSNorm gain, [H] float32 temperature logits
+    theta and optional [H] float32 null-gate biases)."""
+    w_g: torch.Tensor
+    w_v: torch.Tensor
+    w_q: torch.Tensor
+    w_k: torch.Tensor
+    w_o: torch.Tensor
+    theta: torch.Tensor
+    n_heads: int
+    head_dim: int
+    gain: Optional[torch.Tensor] = None
+    null_bias: Optional[torch.Tensor] = None
+
+    def c_struct(self) -> Weights:
+        p = lambda t: None if t is None else t.data_ptr()  # noqa: E731
+        return Weights(p(self.w_g), p(self.w_v), p(self.w_q), p(self.w_k), p(self.w_o),
+                       p(self.gain), p(self.theta), p(self.null_bias))
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    return None if t is None else t.data_ptr()
+
+
+def _stream(stream) -> Optional[int]:
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return stream.cuda_stream
+
+
+def make_shape(B: int, T: int, d: int, F: int, H: int, dh: int, dtype: torch.dtype,
+               rope_base: float = 10000.0, rms_eps: float = 1e-6,
+               io_dtype: Optional[torch.dtype] = None) -> Shape:
+    """dtype: weights and intermediate activations; io_dtype: x and out
+    (defaults to dtype)."""
+    io_dtype = dtype if io_dtype is None else io_dtype
+    for t in (dtype, io_dtype):
+        if t not in _DTYPES:
+            raise TypeError(f"unsupported dtype {t}")
+    return Shape(B, T, d, F, H, dh, _DTYPES[dtype], _DTYPES[io_dtype], rope_base, rms_eps)
+
+
+def shape_of(x: torch.Tensor, w: BlockWeights, rope_base: float = 10000.0,
+             rms_eps: float = 1e-6) -> Shape:
+    """Shape of a call: compute dtype from the weights, I/O dtype from x."""
+    B, T, d = x.shape
+    return make_shape(B, T, d, w.w_g.shape[0], w.n_heads, w.head_dim, w.w_g.dtype, rope_base,
+                      rms_eps, io_dtype=x.dtype)
+
+
+def tango_workspace_size(shape: Shape) -> int:
+    return int(load().tango_workspace_size(ctypes.byref(shape)))
+
+
+def wango_workspace_size(shape: Shape, window: int, phi_dim: int, chunk: int) -> int:
+    return int(load().wango_workspace_size(ctypes.byref(shape), window, phi_dim, chunk))
+
+
+def workspace(nbytes: int, device) -> torch.Tensor:
+    """A byte tensor usable as a workspace (torch allocations are 256-byte aligned)."""
+    return torch.empty(max(int(nbytes), 1), dtype=torch.uint8, device=device)
+
+
+def tango_block_fwd(x: torch.Tensor, w: BlockWeights, out: Optional[torch.Tensor] = None,
+                    ws: Optional[torch.Tensor] = None, rope_base: float = 10000.0,
+                    rms_eps: float = 1e-6, stream=None) -> torch.Tensor:
+    """One TANGO block: returns out[B, T, d] (out may be x for in place)."""
+    shape = shape_of(x, w, rope_base, rms_eps)
+    if out is None:
+        out = torch.empty_like(x)
+    if ws is None:
+        ws = workspace(tango_workspace_size(shape), x.device)
+    cw = w.c_struct()
+    check(load().tango_block_fwd(ctypes.byref(shape), ctypes.byref(cw), _ptr(x), _ptr(out),
+                                 _ptr(ws), ws.numel(), _stream(stream)))
+    return out
+
+
+def wango_block_fwd(x: torch.Tensor, w: BlockWeights, window: int, phi_dim: int, chunk: int,
+                    out: Optional[torch.Tensor] = None, ws: Optional[torch.Tensor] = None,
+                    rope_base: float = 10000.0, rms_eps: float = 1e-6, stream=None) -> torch.Tensor:
+    """One WANGO block: returns out[B, T, d] (out may be x for in place)."""
+    shape = shape_of(x, w, rope_base, rms_eps)
+    if out is None:
+        out = torch.empty_like(x)
+    if ws is None:
+        ws = workspace(wango_workspace_size(shape, window, phi_dim, chunk), x.device)
+    cw = w.c_struct()
+    check(load().wango_block_fwd(ctypes.byref(shape), ctypes.byref(cw), window, phi_dim, chunk,
+                                 _ptr(x), _ptr(out), _ptr(ws), ws.numel(), _stream(stream)))
+    return out
+
+
+# ---- stage entry points ---------------------------------------------------------
+
+def tango_stage_proj(shape: Shape, w: BlockWeights, x, gp, v, qh, kh, stream=None) -> None:
+    cw = w.c_struct()
+    check(load().tango_stage_proj(ctypes.byref(shape), ctypes.byref(cw), _ptr(x), _ptr(gp),
+                                  _ptr(v), _ptr(qh), _ptr(kh), _stream(stream)))
+
+
+def tango_stage_aggregate(shape: Shape, theta, null_bias, qh, kh, gp, gbar, ws, stream=None) -> None:
+    check(load().tango_stage_aggregate(ctypes.byref(shape), _ptr(theta), _ptr(null_bias), _ptr(qh),
+                                       _ptr(kh), _ptr(gp), _ptr(gbar), _ptr(ws), ws.numel(),
+                                       _stream(stream)))
+
+
+def tango_stage_out(shape: Shape, w_o, x, gbar, v, out, stream=None) -> None:
+    check(load().tango_stage_out(ctypes.byref(shape), _ptr(w_o), _ptr(x), _ptr(gbar), _ptr(v),
+                                 _ptr(out), _stream(stream)))
+
+
+def wango_stage_scan(shape: Shape, theta, window: int, chunk: int, qh, kh, gp, n_old, z_old, ws,
+                     stream=None) -> None:
+    check(load().wango_stage_scan(ctypes.byref(shape), _ptr(theta), window, chunk, _ptr(qh),
+                                  _ptr(kh), _ptr(gp), _ptr(n_old), _ptr(z_old), _ptr(ws),
+                                  ws.numel(), _stream(stream)))
+
+
+def wango_stage_band(shape: Shape, theta, null_bias, window: int, qh, kh, gp, n_old, z_old, gbar,
+                     stream=None) -> None:
+    check(load().wango_stage_band(ctypes.byref(shape), _ptr(theta), _ptr(null_bias), window,
+                                  _ptr(qh), _ptr(kh), _ptr(gp), _ptr(n_old), _ptr(z_old),
+                                  _ptr(gbar), _stream(stream)))

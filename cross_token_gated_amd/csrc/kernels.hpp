@@ -1,0 +1,100 @@
+// kernels.hpp - argument blocks and launchers of the gfx950 kernels (internal).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace tango {
+
+// Rows of every intermediate buffer are padded per sequence to a multiple of
+// this many positions; padded rows hold zeros.
+constexpr int kRowPad = 128;
+
+struct ProjArgs {
+  const void* x;       // [B, T, d] in the I/O dtype
+  const void* w_g;     // [F, d]
+  const void* w_v;     // [F, d]
+  const void* w_q;     // [HD, d]
+  const void* w_k;     // [HD, d]
+  const void* gain;    // [d] or null
+  void* gp;            // packed gates [B*Tp/32][4][F][8]
+  void* v;             // [B*Tp, F]
+  void* qh;            // [B*Tp, HD]
+  void* kh;            // [B*Tp, HD]
+  int B, T, Tp, d, F, HD, dh;
+  float rope_base, eps;
+};
+
+struct OutArgs {
+  const void* x;       // [B, T, d] in the I/O dtype
+  const void* w_o;     // [d, F]
+  const void* gbar;    // [B*Tp, F]
+  const void* v;       // [B*Tp, F]
+  void* out;           // [B, T, d] in the I/O dtype
+  int B, T, Tp, d, F;
+};
+
+// Aggregation (TANGO full prefix, or the WANGO window band + combine).
+struct AggArgs {
+  const void* qh;          // [B*Tp, H*dh]
+  const void* kh;          // [B*Tp, H*dh]
+  const void* gp;          // packed gates
+  void* gbar;              // [B*Tp, F]
+  const float* theta;      // [H]
+  const float* null_bias;  // [H] or null
+  const float* n_old;      // WANGO: blocked [B*Tp/16][F/16][64][4]
+  const float* z_old;      // WANGO: [B*Tp, H]
+  float* part;             // TANGO split mode: partial numerators
+  float* part_den;         // TANGO split mode: partial denominators
+  int* counters;           // TANGO split mode: one per split tile
+  int B, T, Tp, F, H, dh, window;
+  int split;               // 1: split the long tiles in two (last finisher combines)
+};
+
+// WANGO older-prefix scan.
+struct ScanArgs {
+  const void* qh;
+  const void* kh;
+  const void* gp;
+  const float* theta;
+  float* n_old;            // blocked [B*Tp/16][F/16][64][4]
+  float* z_old;            // [B*Tp, H]
+  float* seg_state;        // [B][H][nseg][dh][F/H] segment sums, then exclusive prefixes
+  float* seg_z;            // [B][H][nseg][dh]
+  int B, T, Tp, F, H, dh, window, chunk;
+  int nseg, chunks_per_seg;
+};
+
+// Plan of the TANGO aggregation grid for a shape.
+struct AggPlan {
+  int fs;          // gate columns per workgroup
+  int nfc;         // column chunks per head
+  int rtiles;      // 64-row tiles per sequence
+  int split;       // 1 = split mode
+  int64_t items;   // work items
+  int64_t n_split_tiles;
+};
+
+AggPlan tango_agg_plan(int B, int Tp, int F, int H, bool bf);
+size_t tango_agg_scratch_bytes(const AggPlan& p, int F, int H);
+
+struct ScanPlan {
+  int nseg, chunks_per_seg, fs;
+};
+ScanPlan wango_scan_plan(int B, int Tp, int F, int H, int chunk, int window, bool bf);
+
+// bf: bf16 weights/activations (else float32); io_bf: bf16 x/out (else float32)
+hipError_t launch_proj(const ProjArgs& a, bool bf, bool io_bf, hipStream_t s);
+hipError_t launch_out(const OutArgs& a, bool bf, bool io_bf, hipStream_t s);
+hipError_t launch_tango_agg(const AggArgs& a, const AggPlan& p, bool bf, hipStream_t s);
+hipError_t launch_wango_band(const AggArgs& a, bool bf, hipStream_t s);
+hipError_t launch_wango_scan(const ScanArgs& a, const ScanPlan& p, bool bf, hipStream_t s);
+hipError_t launch_zero_i32(int* p, int64_t n, hipStream_t s);
+
+// Raise the dynamic-LDS limit of the kernels that need more than 64 KB
+// (once per device).
+hipError_t gemm_kernels_init();
+hipError_t scan_kernels_init();
+
+}  // namespace tango

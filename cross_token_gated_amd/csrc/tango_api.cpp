@@ -1,0 +1,551 @@
+// tango_api.cpp - the C ABI of include/tango.h: validation, workspace layout,
+// launch order and error reporting.  No memory is allocated here; every
+// kernel runs on the caller's stream.
+#include "../../include/tango.h"
+
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <mutex>
+#include <string>
+
+#include "kernels.hpp"
+
+namespace {
+
+using namespace tango;
+
+thread_local std::string g_last_error;
+
+int fail(int code, const char* fmt, ...) __attribute__((format(printf, 2, 3)));
+int fail(int code, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return code;
+}
+
+int ok() {
+  g_last_error.clear();
+  return TANGO_OK;
+}
+
+int hip_fail(hipError_t e, const char* where) {
+  return fail(TANGO_ERR_HIP, "%s: %s", where, hipGetErrorString(e));
+}
+
+size_t align256(size_t n) { return (n + 255) & ~(size_t)255; }
+
+int64_t pad_rows(int64_t T) { return (T + kRowPad - 1) / kRowPad * kRowPad; }
+
+size_t elem_size(int dtype) { return dtype == TANGO_BF16 ? 2 : 4; }
+
+// ---- validation -----------------------------------------------------------
+
+int check_shape(const tango_shape_t* s) {
+  if (!s) return fail(TANGO_ERR_NULL, "shape is NULL");
+  if (s->dtype != TANGO_F32 && s->dtype != TANGO_BF16)
+    return fail(TANGO_ERR_DTYPE, "dtype %d is neither TANGO_F32 (0) nor TANGO_BF16 (1)", s->dtype);
+  if (s->io_dtype != TANGO_F32 && s->io_dtype != TANGO_BF16)
+    return fail(TANGO_ERR_DTYPE, "io_dtype %d is neither TANGO_F32 (0) nor TANGO_BF16 (1)", s->io_dtype);
+  if (s->batch < 1 || s->seq_len < 1 || s->d_model < 1 || s->d_gate < 1 || s->n_heads < 1 ||
+      s->head_dim < 1)
+    return fail(TANGO_ERR_SHAPE, "sizes must be >= 1 (B=%d T=%d d=%d F=%d H=%d d_h=%d)", s->batch,
+                s->seq_len, s->d_model, s->d_gate, s->n_heads, s->head_dim);
+  if (s->d_gate % s->n_heads != 0)
+    return fail(TANGO_ERR_SHAPE, "d_gate %d is not a multiple of n_heads %d", s->d_gate, s->n_heads);
+  if (!(s->rms_eps > 0.f) || !std::isfinite(s->rms_eps))
+    return fail(TANGO_ERR_SHAPE, "rms_eps must be finite and > 0");
+  if (!(s->rope_base >= 0.f) || !std::isfinite(s->rope_base))
+    return fail(TANGO_ERR_SHAPE, "rope_base must be finite and >= 0");
+  if ((int64_t)s->batch * pad_rows(s->seq_len) > ((int64_t)1 << 26))
+    return fail(TANGO_ERR_UNSUPPORTED, "batch * padded seq_len exceeds 2^26 rows");
+  if (s->d_model % 128 != 0 || s->d_model > 4096)
+    return fail(TANGO_ERR_UNSUPPORTED, "d_model %d: need a multiple of 128, at most 4096", s->d_model);
+  if (s->d_gate % 64 != 0 || (s->d_gate / s->n_heads) % 64 != 0)
+    return fail(TANGO_ERR_UNSUPPORTED, "d_gate %d: need d_gate and d_gate/n_heads multiples of 64",
+                s->d_gate);
+  if (s->head_dim != 32 && s->head_dim != 64 && s->head_dim != 128)
+    return fail(TANGO_ERR_UNSUPPORTED, "head_dim %d: supported are 32, 64 and 128", s->head_dim);
+  if ((int64_t)s->n_heads * s->head_dim > 1024)
+    return fail(TANGO_ERR_UNSUPPORTED, "n_heads * head_dim exceeds 1024");
+  return TANGO_OK;
+}
+
+int check_wango(const tango_shape_t* s, int32_t window, int32_t phi_dim, int32_t chunk) {
+  if (window < 1) return fail(TANGO_ERR_SHAPE, "window %d < 1", window);
+  if (phi_dim != s->head_dim)
+    return fail(TANGO_ERR_SHAPE, "phi_dim %d must equal head_dim %d (phi acts elementwise)", phi_dim,
+                s->head_dim);
+  if (chunk != 64 && chunk != 128)
+    return fail(TANGO_ERR_UNSUPPORTED, "chunk %d: supported are 64 and 128", chunk);
+  if (window % chunk != 0)
+    return fail(TANGO_ERR_UNSUPPORTED, "window %d is not a multiple of chunk %d", window, chunk);
+  return TANGO_OK;
+}
+
+bool aligned(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+
+struct Range {
+  const void* p;
+  size_t n;
+  const char* name;
+};
+
+bool overlap(const Range& a, const Range& b) {
+  if (!a.p || !b.p || !a.n || !b.n) return false;
+  const uintptr_t a0 = (uintptr_t)a.p, b0 = (uintptr_t)b.p;
+  return a0 < b0 + b.n && b0 < a0 + a.n;
+}
+
+// Each output must not overlap any input or other output; out may equal x
+// exactly (in place).
+int check_ranges(const Range* ins, int nin, const Range* outs, int nout, const void* inplace_x,
+                 const void* inplace_out) {
+  for (int i = 0; i < nin; ++i)
+    if (ins[i].p && !aligned(ins[i].p)) return fail(TANGO_ERR_ALIGN, "%s is not 16-byte aligned", ins[i].name);
+  for (int o = 0; o < nout; ++o)
+    if (outs[o].p && !aligned(outs[o].p))
+      return fail(TANGO_ERR_ALIGN, "%s is not 16-byte aligned", outs[o].name);
+  for (int o = 0; o < nout; ++o) {
+    for (int i = 0; i < nin; ++i) {
+      // the one permitted overlap: out == x exactly (in place)
+      if (inplace_out && outs[o].p == inplace_out && ins[i].p == inplace_x && inplace_x == inplace_out &&
+          outs[o].n == ins[i].n)
+        continue;
+      if (overlap(outs[o], ins[i]))
+        return fail(TANGO_ERR_ALIAS, "%s overlaps %s", outs[o].name, ins[i].name);
+    }
+    for (int o2 = o + 1; o2 < nout; ++o2)
+      if (overlap(outs[o], outs[o2]))
+        return fail(TANGO_ERR_ALIAS, "%s overlaps %s", outs[o].name, outs[o2].name);
+  }
+  return TANGO_OK;
+}
+
+// ---- workspace layout -------------------------------------------------------
+
+struct Layout {
+  size_t gp, v, qh, kh, gbar;           // offsets
+  size_t part, part_den, counters;      // TANGO split scratch
+  size_t n_old, z_old, seg_state, seg_z;
+  size_t total;
+  AggPlan agg;
+  ScanPlan scan;
+};
+
+Layout make_layout(const tango_shape_t* s, bool wango, int32_t window, int32_t chunk) {
+  Layout L{};
+  const size_t es = elem_size(s->dtype);
+  const int64_t M = (int64_t)s->batch * pad_rows(s->seq_len);
+  const int64_t F = s->d_gate, HD = (int64_t)s->n_heads * s->head_dim;
+  size_t off = 0;
+  auto take = [&](size_t bytes) {
+    const size_t o = off;
+    off = align256(off + bytes);
+    return o;
+  };
+  L.gp = take(M * F * es);
+  L.v = take(M * F * es);
+  L.qh = take(M * HD * es);
+  L.kh = take(M * HD * es);
+  L.gbar = take(M * F * es);
+  const bool bf = s->dtype == TANGO_BF16;
+  if (!wango) {
+    L.agg = tango_agg_plan(s->batch, (int)pad_rows(s->seq_len), s->d_gate, s->n_heads, bf);
+    const int64_t n = L.agg.n_split_tiles;
+    L.part = take((size_t)n * 2 * 64 * L.agg.fs * sizeof(float));
+    L.part_den = take((size_t)n * 2 * 64 * sizeof(float));
+    L.counters = take((size_t)n * sizeof(int));
+  } else {
+    L.scan = wango_scan_plan(s->batch, (int)pad_rows(s->seq_len), s->d_gate, s->n_heads, chunk, window, bf);
+    L.n_old = take(M * F * sizeof(float));
+    L.z_old = take(M * s->n_heads * sizeof(float));
+    const int64_t bh = (int64_t)s->batch * s->n_heads;
+    L.seg_state = take((size_t)bh * L.scan.nseg * s->head_dim * (F / s->n_heads) * sizeof(float));
+    L.seg_z = take((size_t)bh * L.scan.nseg * s->head_dim * sizeof(float));
+  }
+  L.total = off;
+  return L;
+}
+
+// ---- one-time kernel attributes (per device) ----------------------------------
+
+std::mutex g_init_mu;
+bool g_init_done[64];
+
+int ensure_init() {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+  if (dev < 0 || dev >= 64) return fail(TANGO_ERR_HIP, "device index %d out of range", dev);
+  std::lock_guard<std::mutex> lk(g_init_mu);
+  if (g_init_done[dev]) return TANGO_OK;
+  if ((e = gemm_kernels_init()) != hipSuccess) return hip_fail(e, "kernel attributes");
+  if ((e = scan_kernels_init()) != hipSuccess) return hip_fail(e, "kernel attributes");
+  g_init_done[dev] = true;
+  return TANGO_OK;
+}
+
+// ---- argument blocks ------------------------------------------------------------
+
+ProjArgs proj_args(const tango_shape_t* s, const tango_weights_t* w, const void* x, void* gp, void* v,
+                   void* qh, void* kh) {
+  ProjArgs a{};
+  a.x = x;
+  a.w_g = w->w_g;
+  a.w_v = w->w_v;
+  a.w_q = w->w_q;
+  a.w_k = w->w_k;
+  a.gain = w->rms_gain;
+  a.gp = gp;
+  a.v = v;
+  a.qh = qh;
+  a.kh = kh;
+  a.B = s->batch;
+  a.T = s->seq_len;
+  a.Tp = (int)pad_rows(s->seq_len);
+  a.d = s->d_model;
+  a.F = s->d_gate;
+  a.HD = s->n_heads * s->head_dim;
+  a.dh = s->head_dim;
+  a.rope_base = s->rope_base;
+  a.eps = s->rms_eps;
+  return a;
+}
+
+OutArgs out_args(const tango_shape_t* s, const void* w_o, const void* x, const void* gbar, const void* v,
+                 void* out) {
+  OutArgs a{};
+  a.x = x;
+  a.w_o = w_o;
+  a.gbar = gbar;
+  a.v = v;
+  a.out = out;
+  a.B = s->batch;
+  a.T = s->seq_len;
+  a.Tp = (int)pad_rows(s->seq_len);
+  a.d = s->d_model;
+  a.F = s->d_gate;
+  return a;
+}
+
+AggArgs agg_args(const tango_shape_t* s, const float* theta, const float* null_bias, const void* qh,
+                 const void* kh, const void* gp, void* gbar) {
+  AggArgs a{};
+  a.qh = qh;
+  a.kh = kh;
+  a.gp = gp;
+  a.gbar = gbar;
+  a.theta = theta;
+  a.null_bias = null_bias;
+  a.B = s->batch;
+  a.T = s->seq_len;
+  a.Tp = (int)pad_rows(s->seq_len);
+  a.F = s->d_gate;
+  a.H = s->n_heads;
+  a.dh = s->head_dim;
+  return a;
+}
+
+ScanArgs scan_args(const tango_shape_t* s, const float* theta, int32_t window, int32_t chunk,
+                   const void* qh, const void* kh, const void* gp, float* n_old, float* z_old,
+                   float* seg_state, float* seg_z) {
+  ScanArgs a{};
+  a.qh = qh;
+  a.kh = kh;
+  a.gp = gp;
+  a.theta = theta;
+  a.n_old = n_old;
+  a.z_old = z_old;
+  a.seg_state = seg_state;
+  a.seg_z = seg_z;
+  a.B = s->batch;
+  a.T = s->seq_len;
+  a.Tp = (int)pad_rows(s->seq_len);
+  a.F = s->d_gate;
+  a.H = s->n_heads;
+  a.dh = s->head_dim;
+  a.window = window;
+  a.chunk = chunk;
+  return a;
+}
+
+int check_weights(const tango_weights_t* w, bool need_all) {
+  if (!w) return fail(TANGO_ERR_NULL, "weights is NULL");
+  if (need_all && (!w->w_g || !w->w_v || !w->w_q || !w->w_k || !w->w_o))
+    return fail(TANGO_ERR_NULL, "a weight matrix pointer is NULL");
+  if (!w->theta) return fail(TANGO_ERR_NULL, "theta is NULL");
+  return TANGO_OK;
+}
+
+template <typename Fn>
+int guarded(Fn fn) {
+  try {
+    return fn();
+  } catch (...) {
+    return fail(TANGO_ERR_HIP, "unexpected C++ exception inside the library");
+  }
+}
+
+int block_common(const tango_shape_t* s, const tango_weights_t* w, bool wango, int32_t window,
+                 int32_t phi_dim, int32_t chunk, const void* x, void* out, void* ws, size_t ws_bytes,
+                 void* stream) {
+  int rc = check_shape(s);
+  if (rc) return rc;
+  if ((rc = check_weights(w, true))) return rc;
+  if (wango && (rc = check_wango(s, window, phi_dim, chunk))) return rc;
+  if (!x || !out) return fail(TANGO_ERR_NULL, "x or out is NULL");
+  if (!ws) return fail(TANGO_ERR_NULL, "workspace is NULL");
+  const Layout L = make_layout(s, wango, window, chunk);
+  if (ws_bytes < L.total)
+    return fail(TANGO_ERR_WORKSPACE, "workspace of %zu bytes is smaller than the %zu needed", ws_bytes,
+                L.total);
+  const size_t es = elem_size(s->dtype);
+  const size_t d = s->d_model, F = s->d_gate, HD = (size_t)s->n_heads * s->head_dim;
+  const size_t xb = (size_t)s->batch * s->seq_len * d * elem_size(s->io_dtype);
+  const Range ins[] = {{x, xb, "x"},
+                       {w->w_g, F * d * es, "w_g"},
+                       {w->w_v, F * d * es, "w_v"},
+                       {w->w_q, HD * d * es, "w_q"},
+                       {w->w_k, HD * d * es, "w_k"},
+                       {w->w_o, d * F * es, "w_o"},
+                       {w->rms_gain, d * es, "rms_gain"},
+                       {w->theta, s->n_heads * sizeof(float), "theta"},
+                       {w->null_bias, s->n_heads * sizeof(float), "null_bias"}};
+  const Range outs[] = {{out, xb, "out"}, {ws, L.total, "workspace"}};
+  if ((rc = check_ranges(ins, 9, outs, 2, x, out))) return rc;
+  if ((rc = ensure_init())) return rc;
+
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  const bool bf = s->dtype == TANGO_BF16;
+  char* base = static_cast<char*>(ws);
+  void* gp = base + L.gp;
+  void* v = base + L.v;
+  void* qh = base + L.qh;
+  void* kh = base + L.kh;
+  void* gbar = base + L.gbar;
+  const bool io_bf = s->io_dtype == TANGO_BF16;
+  hipError_t e = launch_proj(proj_args(s, w, x, gp, v, qh, kh), bf, io_bf, st);
+  if (e != hipSuccess) return hip_fail(e, "projection kernel");
+  AggArgs aa = agg_args(s, w->theta, w->null_bias, qh, kh, gp, gbar);
+  if (!wango) {
+    aa.part = reinterpret_cast<float*>(base + L.part);
+    aa.part_den = reinterpret_cast<float*>(base + L.part_den);
+    aa.counters = reinterpret_cast<int*>(base + L.counters);
+    e = launch_tango_agg(aa, L.agg, bf, st);
+    if (e != hipSuccess) return hip_fail(e, "aggregation kernel");
+  } else {
+    float* n_old = reinterpret_cast<float*>(base + L.n_old);
+    float* z_old = reinterpret_cast<float*>(base + L.z_old);
+    ScanArgs sa = scan_args(s, w->theta, window, chunk, qh, kh, gp, n_old, z_old,
+                            reinterpret_cast<float*>(base + L.seg_state),
+                            reinterpret_cast<float*>(base + L.seg_z));
+    e = launch_wango_scan(sa, L.scan, bf, st);
+    if (e != hipSuccess) return hip_fail(e, "scan kernels");
+    aa.n_old = n_old;
+    aa.z_old = z_old;
+    aa.window = window;
+    e = launch_wango_band(aa, bf, st);
+    if (e != hipSuccess) return hip_fail(e, "band kernel");
+  }
+  e = launch_out(out_args(s, w->w_o, x, gbar, v, out), bf, io_bf, st);
+  if (e != hipSuccess) return hip_fail(e, "output kernel");
+  return ok();
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t tango_workspace_size(const tango_shape_t* shape) {
+  if (check_shape(shape)) return 0;
+  return make_layout(shape, false, 0, 0).total;
+}
+
+size_t wango_workspace_size(const tango_shape_t* shape, int32_t window, int32_t phi_dim, int32_t chunk) {
+  if (check_shape(shape) || check_wango(shape, window, phi_dim, chunk)) return 0;
+  return make_layout(shape, true, window, chunk).total;
+}
+
+int tango_block_fwd(const tango_shape_t* shape, const tango_weights_t* weights, const void* x, void* out,
+                    void* workspace, size_t workspace_bytes, void* hip_stream) {
+  return guarded([&] {
+    return block_common(shape, weights, false, 0, 0, 0, x, out, workspace, workspace_bytes, hip_stream);
+  });
+}
+
+int wango_block_fwd(const tango_shape_t* shape, const tango_weights_t* weights, int32_t window,
+                    int32_t phi_dim, int32_t chunk, const void* x, void* out, void* workspace,
+                    size_t workspace_bytes, void* hip_stream) {
+  return guarded([&] {
+    return block_common(shape, weights, true, window, phi_dim, chunk, x, out, workspace, workspace_bytes,
+                        hip_stream);
+  });
+}
+
+const char* tango_status_string(int status) {
+  switch (status) {
+    case TANGO_OK: return "TANGO_OK";
+    case TANGO_ERR_NULL: return "TANGO_ERR_NULL: a required pointer is NULL";
+    case TANGO_ERR_SHAPE: return "TANGO_ERR_SHAPE: inconsistent sizes";
+    case TANGO_ERR_DTYPE: return "TANGO_ERR_DTYPE: unknown dtype or io_dtype";
+    case TANGO_ERR_ALIGN: return "TANGO_ERR_ALIGN: pointer not 16-byte aligned";
+    case TANGO_ERR_UNSUPPORTED: return "TANGO_ERR_UNSUPPORTED: shape not covered by the kernels";
+    case TANGO_ERR_WORKSPACE: return "TANGO_ERR_WORKSPACE: workspace too small";
+    case TANGO_ERR_ALIAS: return "TANGO_ERR_ALIAS: buffers overlap";
+    case TANGO_ERR_HIP: return "TANGO_ERR_HIP: HIP runtime error";
+    default: return "unknown tango status";
+  }
+}
+
+const char* tango_last_error(void) { return g_last_error.c_str(); }
+
+int tango_version(void) { return TANGO_ABI_VERSION; }
+
+int tango_stage_proj(const tango_shape_t* shape, const tango_weights_t* weights, const void* x, void* gp,
+                     void* v, void* qh, void* kh, void* hip_stream) {
+  return guarded([&] {
+    int rc = check_shape(shape);
+    if (rc) return rc;
+    if ((rc = check_weights(weights, true))) return rc;
+    if (!x || !gp || !v || !qh || !kh) return fail(TANGO_ERR_NULL, "a buffer pointer is NULL");
+    const tango_shape_t* s = shape;
+    const size_t es = elem_size(s->dtype), M = (size_t)s->batch * pad_rows(s->seq_len);
+    const size_t d = s->d_model, F = s->d_gate, HD = (size_t)s->n_heads * s->head_dim;
+    const Range ins[] = {{x, (size_t)s->batch * s->seq_len * d * elem_size(s->io_dtype), "x"},
+                         {weights->w_g, F * d * es, "w_g"},
+                         {weights->w_v, F * d * es, "w_v"},
+                         {weights->w_q, HD * d * es, "w_q"},
+                         {weights->w_k, HD * d * es, "w_k"},
+                         {weights->rms_gain, d * es, "rms_gain"}};
+    const Range outs[] = {{gp, M * F * es, "gp"}, {v, M * F * es, "v"}, {qh, M * HD * es, "qh"},
+                          {kh, M * HD * es, "kh"}};
+    if ((rc = check_ranges(ins, 6, outs, 4, nullptr, nullptr))) return rc;
+    if ((rc = ensure_init())) return rc;
+    hipError_t e = launch_proj(proj_args(s, weights, x, gp, v, qh, kh), s->dtype == TANGO_BF16,
+                               s->io_dtype == TANGO_BF16, static_cast<hipStream_t>(hip_stream));
+    return e == hipSuccess ? ok() : hip_fail(e, "projection kernel");
+  });
+}
+
+int tango_stage_aggregate(const tango_shape_t* shape, const float* theta, const float* null_bias,
+                          const void* qh, const void* kh, const void* gp, void* gbar, void* workspace,
+                          size_t workspace_bytes, void* hip_stream) {
+  return guarded([&] {
+    int rc = check_shape(shape);
+    if (rc) return rc;
+    if (!theta || !qh || !kh || !gp || !gbar || !workspace)
+      return fail(TANGO_ERR_NULL, "a buffer pointer is NULL");
+    const tango_shape_t* s = shape;
+    const Layout L = make_layout(s, false, 0, 0);
+    if (workspace_bytes < L.total)
+      return fail(TANGO_ERR_WORKSPACE, "workspace of %zu bytes is smaller than the %zu needed",
+                  workspace_bytes, L.total);
+    const size_t es = elem_size(s->dtype), M = (size_t)s->batch * pad_rows(s->seq_len);
+    const size_t F = s->d_gate, HD = (size_t)s->n_heads * s->head_dim;
+    const Range ins[] = {{qh, M * HD * es, "qh"}, {kh, M * HD * es, "kh"}, {gp, M * F * es, "gp"},
+                         {theta, s->n_heads * sizeof(float), "theta"},
+                         {null_bias, s->n_heads * sizeof(float), "null_bias"}};
+    const Range outs[] = {{gbar, M * F * es, "gbar"}, {workspace, L.total, "workspace"}};
+    if ((rc = check_ranges(ins, 5, outs, 2, nullptr, nullptr))) return rc;
+    if ((rc = ensure_init())) return rc;
+    char* base = static_cast<char*>(workspace);
+    AggArgs aa = agg_args(s, theta, null_bias, qh, kh, gp, gbar);
+    aa.part = reinterpret_cast<float*>(base + L.part);
+    aa.part_den = reinterpret_cast<float*>(base + L.part_den);
+    aa.counters = reinterpret_cast<int*>(base + L.counters);
+    hipError_t e = launch_tango_agg(aa, L.agg, s->dtype == TANGO_BF16, static_cast<hipStream_t>(hip_stream));
+    return e == hipSuccess ? ok() : hip_fail(e, "aggregation kernel");
+  });
+}
+
+int tango_stage_out(const tango_shape_t* shape, const void* w_o, const void* x, const void* gbar,
+                    const void* v, void* out, void* hip_stream) {
+  return guarded([&] {
+    int rc = check_shape(shape);
+    if (rc) return rc;
+    if (!w_o || !x || !gbar || !v || !out) return fail(TANGO_ERR_NULL, "a buffer pointer is NULL");
+    const tango_shape_t* s = shape;
+    const size_t es = elem_size(s->dtype), M = (size_t)s->batch * pad_rows(s->seq_len);
+    const size_t d = s->d_model, F = s->d_gate;
+    const size_t xb = (size_t)s->batch * s->seq_len * d * elem_size(s->io_dtype);
+    const Range ins[] = {{w_o, d * F * es, "w_o"}, {x, xb, "x"}, {gbar, M * F * es, "gbar"},
+                         {v, M * F * es, "v"}};
+    const Range outs[] = {{out, xb, "out"}};
+    if ((rc = check_ranges(ins, 4, outs, 1, x, out))) return rc;
+    if ((rc = ensure_init())) return rc;
+    hipError_t e = launch_out(out_args(s, w_o, x, gbar, v, out), s->dtype == TANGO_BF16,
+                              s->io_dtype == TANGO_BF16, static_cast<hipStream_t>(hip_stream));
+    return e == hipSuccess ? ok() : hip_fail(e, "output kernel");
+  });
+}
+
+int wango_stage_scan(const tango_shape_t* shape, const float* theta, int32_t window, int32_t chunk,
+                     const void* qh, const void* kh, const void* gp, void* n_old, void* z_old,
+                     void* workspace, size_t workspace_bytes, void* hip_stream) {
+  return guarded([&] {
+    int rc = check_shape(shape);
+    if (rc) return rc;
+    if ((rc = check_wango(shape, window, shape->head_dim, chunk))) return rc;
+    if (!theta || !qh || !kh || !gp || !n_old || !z_old || !workspace)
+      return fail(TANGO_ERR_NULL, "a buffer pointer is NULL");
+    const tango_shape_t* s = shape;
+    const Layout L = make_layout(s, true, window, chunk);
+    if (workspace_bytes < L.total)
+      return fail(TANGO_ERR_WORKSPACE, "workspace of %zu bytes is smaller than the %zu needed",
+                  workspace_bytes, L.total);
+    const size_t es = elem_size(s->dtype), M = (size_t)s->batch * pad_rows(s->seq_len);
+    const size_t F = s->d_gate, HD = (size_t)s->n_heads * s->head_dim;
+    const Range ins[] = {{qh, M * HD * es, "qh"}, {kh, M * HD * es, "kh"}, {gp, M * F * es, "gp"},
+                         {theta, s->n_heads * sizeof(float), "theta"}};
+    const Range outs[] = {{n_old, M * F * sizeof(float), "n_old"},
+                          {z_old, M * s->n_heads * sizeof(float), "z_old"},
+                          {workspace, L.total, "workspace"}};
+    if ((rc = check_ranges(ins, 4, outs, 3, nullptr, nullptr))) return rc;
+    if ((rc = ensure_init())) return rc;
+    char* base = static_cast<char*>(workspace);
+    ScanArgs sa = scan_args(s, theta, window, chunk, qh, kh, gp, static_cast<float*>(n_old),
+                            static_cast<float*>(z_old), reinterpret_cast<float*>(base + L.seg_state),
+                            reinterpret_cast<float*>(base + L.seg_z));
+    hipError_t e = launch_wango_scan(sa, L.scan, s->dtype == TANGO_BF16, static_cast<hipStream_t>(hip_stream));
+    return e == hipSuccess ? ok() : hip_fail(e, "scan kernels");
+  });
+}
+
+int wango_stage_band(const tango_shape_t* shape, const float* theta, const float* null_bias, int32_t window,
+                     const void* qh, const void* kh, const void* gp, const float* n_old, const float* z_old,
+                     void* gbar, void* hip_stream) {
+  return guarded([&] {
+    int rc = check_shape(shape);
+    if (rc) return rc;
+    if (window < 1) return fail(TANGO_ERR_SHAPE, "window %d < 1", window);
+    if (!theta || !qh || !kh || !gp || !n_old || !z_old || !gbar)
+      return fail(TANGO_ERR_NULL, "a buffer pointer is NULL");
+    const tango_shape_t* s = shape;
+    const size_t es = elem_size(s->dtype), M = (size_t)s->batch * pad_rows(s->seq_len);
+    const size_t F = s->d_gate, HD = (size_t)s->n_heads * s->head_dim;
+    const Range ins[] = {{qh, M * HD * es, "qh"}, {kh, M * HD * es, "kh"}, {gp, M * F * es, "gp"},
+                         {n_old, M * F * sizeof(float), "n_old"},
+                         {z_old, M * s->n_heads * sizeof(float), "z_old"},
+                         {theta, s->n_heads * sizeof(float), "theta"},
+                         {null_bias, s->n_heads * sizeof(float), "null_bias"}};
+    const Range outs[] = {{gbar, M * F * es, "gbar"}};
+    if ((rc = check_ranges(ins, 7, outs, 1, nullptr, nullptr))) return rc;
+    if ((rc = ensure_init())) return rc;
+    AggArgs aa = agg_args(s, theta, null_bias, qh, kh, gp, gbar);
+    aa.n_old = n_old;
+    aa.z_old = z_old;
+    aa.window = window;
+    hipError_t e = launch_wango_band(aa, s->dtype == TANGO_BF16, static_cast<hipStream_t>(hip_stream));
+    return e == hipSuccess ? ok() : hip_fail(e, "band kernel");
+  });
+}
+
+}  // extern "C"

@@ -20,8 +20,11 @@ import numpy as np
 class Workload:
     """One block workload.  ``mode`` is "tango" (full prefix) or "wango"
     (window + running sums).  ``repeats`` is the number of shared-weight
-    applications.  ``dtype`` is the storage dtype of activations and weights
-    ("f32" or "bf16"); accumulation is always float32."""
+    applications.  ``dtype`` is the dtype of the weights and of every
+    intermediate activation ("f32" or "bf16"); accumulation is always float32.
+    ``io_dtype`` is the dtype of the residual stream x/out between
+    applications; the bf16 workloads carry it in float32.  The input values
+    are rounded to ``dtype`` in either case."""
     name: str
     mode: str
     dtype: str
@@ -39,6 +42,11 @@ class Workload:
     rope_base: float = 10000.0
     rms_eps: float = 1e-6
     null_bias: Optional[float] = None  # None: null gate off
+    io_dtype: str = ""                 # dtype of the residual stream x/out ("" = dtype)
+
+    @property
+    def io(self) -> str:
+        return self.io_dtype or self.dtype
 
     @property
     def tokens(self) -> int:
@@ -55,14 +63,15 @@ WORKLOADS = {
     "tango_f32_t256": Workload("tango_f32_t256", "tango", "f32", 1, 256, 512, 1024, 1, 128,
                                seed=0),
     "tango_bf16_b8_t2048": Workload("tango_bf16_b8_t2048", "tango", "bf16", 8, 2048, 512, 2048,
-                                    1, 128, seed=1),
+                                    1, 128, seed=1, io_dtype="f32"),
     "tango_bf16_t8192_r4": Workload("tango_bf16_t8192_r4", "tango", "bf16", 1, 8192, 512, 2048,
-                                    1, 128, repeats=4, seed=2),
+                                    1, 128, repeats=4, seed=2, io_dtype="f32"),
     "wango_bf16_t8192_w256": Workload("wango_bf16_t8192_w256", "wango", "bf16", 1, 8192, 512,
-                                      2048, 2, 64, window=256, chunk=128, seed=3),
+                                      2048, 2, 64, window=256, chunk=128, seed=3,
+                                      io_dtype="f32"),
     "wango_bf16_b2_t65536_w512_r8": Workload("wango_bf16_b2_t65536_w512_r8", "wango", "bf16", 2,
                                              65536, 512, 2048, 1, 128, window=512, chunk=128,
-                                             repeats=8, seed=4),
+                                             repeats=8, seed=4, io_dtype="f32"),
 }
 WORKLOAD_ORDER = list(WORKLOADS)
 

@@ -1,0 +1,193 @@
+/*
+ * tango.h - C ABI of the MI355X (gfx950) TANGO / WANGO block forward library.
+ *
+ * The operation is the gated-aggregation block of "TANGO: Token-Aggregated
+ * Nonlinear Gating Operators for Natural and Formal Language Modeling"
+ * (arXiv 2608.22117 v1):
+ *
+ *   x_i    = RMSNorm(h_i)                                       (§2.1)
+ *   g_i    = SiLU(W_g x_i),  v_i = W_v x_i                      (§2.1, eq. 2)
+ *   q_ia, k_ia = per-head W_q x_i, W_k x_i; RoPE, unit length   (§2.1)
+ *   l_ija  = tau_a q_ia . k_ja,  tau_a = exp(min(theta_a, log 20))   (§2.1, eq. 4)
+ *   gbar_ia = sum_j m_ija g_ja / (sum_j m_ija + n_i exp(b_a))   (§2.1, eq. 5)
+ *   h+_i   = h_i + W_o (gbar_i * v_i)                           (§2.1, eq. 3)
+ *
+ * with m_ija = exp(l_ija) over the whole causal prefix for TANGO (§2.2, eq. 6),
+ * and for WANGO exp(l_ija) inside the trailing window of W positions and
+ * phi(sqrt(tau) q)^T phi(sqrt(tau) k) for older sources, phi(u) =
+ * max(ELU(u)+1+1e-4, 1e-4)/sqrt(d_h), carried as running sums (§2.2, eqs. 7-10).
+ *
+ * Readings where the text is open: RMSNorm eps = shape.rms_eps with an optional
+ * gain; heads own contiguous column blocks of the gate and of q/k; RoPE rotates
+ * interleaved pairs (2c, 2c+1) by angle i * rope_base^(-2c/d_h) at the 0-based
+ * position i of each batch row (rope_base = 0 turns it off); a zero-length q or
+ * k is divided by 1e-12; ELU alpha = 1; n_i = i + 1; the WANGO feature map
+ * keeps the head width (phi_dim must equal head_dim).
+ *
+ * Conventions for every entry point:
+ *  - All tensor pointers are DEVICE pointers owned by the caller, row-major and
+ *    contiguous, 16-byte aligned.  x and out have shape->io_dtype; the five
+ *    weight matrices, the gain and the intermediate activations have
+ *    shape->dtype; theta, null_bias and every float32 buffer below are float32.
+ *    Accumulation is float32 for both dtypes.
+ *  - Calls are asynchronous on `hip_stream` (a hipStream_t; NULL = the default
+ *    stream) and never synchronise the host.  The library allocates no memory
+ *    on any call and keeps no per-call state; scratch space is the caller's
+ *    `workspace`, whose minimum size the *_workspace_size functions return.
+ *  - A workspace must not be shared by calls that can run concurrently.
+ *  - Inputs are never modified.  `out` may equal `x` (in place); any other
+ *    overlap between `out`, `workspace` and the inputs is TANGO_ERR_ALIAS.
+ *  - Every argument is validated before anything is launched: on a non-zero
+ *    status nothing was written.  A launch failure returns TANGO_ERR_HIP.
+ *    tango_last_error() then holds a message for the calling thread.
+ *  - No C++ exception and no abort crosses this interface.
+ *
+ * Supported shapes (otherwise TANGO_ERR_UNSUPPORTED; F % H != 0,
+ * phi_dim != head_dim and window < 1 are TANGO_ERR_SHAPE):
+ *    batch >= 1, seq_len >= 1, batch * seq_len <= 2^26,
+ *    d_model % 128 == 0 and d_model <= 4096,
+ *    d_gate % 64 == 0, (d_gate / n_heads) % 64 == 0,
+ *    head_dim in {32, 64, 128}, n_heads * head_dim <= 1024,
+ *    WANGO: chunk in {64, 128}, window % chunk == 0.
+ */
+#ifndef TANGO_H_
+#define TANGO_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define TANGO_ABI_VERSION 1
+
+typedef enum { TANGO_F32 = 0, TANGO_BF16 = 1 } tango_dtype_t;
+
+typedef enum {
+  TANGO_OK = 0,
+  TANGO_ERR_NULL = -1,        /* a required pointer is NULL                        */
+  TANGO_ERR_SHAPE = -2,       /* inconsistent sizes (F % H, phi_dim, window < 1 ...) */
+  TANGO_ERR_DTYPE = -3,       /* dtype or io_dtype is not TANGO_F32 or TANGO_BF16  */
+  TANGO_ERR_ALIGN = -4,       /* a pointer is not 16-byte aligned                  */
+  TANGO_ERR_UNSUPPORTED = -5, /* a consistent shape the kernels do not cover        */
+  TANGO_ERR_WORKSPACE = -6,   /* workspace smaller than *_workspace_size()          */
+  TANGO_ERR_ALIAS = -7,       /* outputs overlap inputs or the workspace            */
+  TANGO_ERR_HIP = -8          /* the HIP runtime reported an error                  */
+} tango_status_t;
+
+/* Sizes of one block call.  B sequences of T positions, residual width d,
+ * gate width F split over H heads of F/H gate columns and d_h query/key
+ * columns each. */
+typedef struct {
+  int32_t batch;      /* B                                                */
+  int32_t seq_len;    /* T                                                */
+  int32_t d_model;    /* d                                                */
+  int32_t d_gate;     /* F                                                */
+  int32_t n_heads;    /* H                                                */
+  int32_t head_dim;   /* d_h                                              */
+  int32_t dtype;      /* tango_dtype_t: dtype of the weights and of every
+                         intermediate activation (accumulation is float32) */
+  int32_t io_dtype;   /* tango_dtype_t: dtype of x and out, the residual
+                         stream (float32 keeps it exact between stacked
+                         applications)                                     */
+  float rope_base;    /* RoPE base (10000 in the shipped workloads); 0 = off */
+  float rms_eps;      /* RMSNorm epsilon (1e-6 in the shipped workloads)  */
+} tango_shape_t;
+
+/* Block parameters ([TANGO] §2.1; the count in Table 1 fixes this list):
+ * bias-free projections, one RMSNorm gain, a temperature logit and a null-gate
+ * bias per head. */
+typedef struct {
+  const void* w_g;        /* [F, d]                                          */
+  const void* w_v;        /* [F, d]                                          */
+  const void* w_q;        /* [H*d_h, d]                                      */
+  const void* w_k;        /* [H*d_h, d]                                      */
+  const void* w_o;        /* [d, F]                                          */
+  const void* rms_gain;   /* [d] in dtype, or NULL for a gain of 1           */
+  const float* theta;     /* [H]; tau_a = exp(min(theta_a, log 20))  (eq. 4) */
+  const float* null_bias; /* [H] b_a, or NULL: null gate off          (eq. 5) */
+} tango_weights_t;
+
+/* ---- Whole block --------------------------------------------------------- */
+
+/* Bytes of workspace tango_block_fwd needs for `shape`; 0 if the shape is
+ * invalid (the call itself then reports why). */
+size_t tango_workspace_size(const tango_shape_t* shape);
+
+/* TANGO block ([TANGO] §2.1 eqs. 2-5, §2.2 eq. 6): out[B,T,d] = h+ for
+ * x[B,T,d] = h.  Apply it R times with out == x for the shared-weight stack of
+ * §2.3 eq. 11 (the stream is stored in dtype between applications). */
+int tango_block_fwd(const tango_shape_t* shape, const tango_weights_t* weights,
+                    const void* x, void* out, void* workspace, size_t workspace_bytes,
+                    void* hip_stream);
+
+/* Bytes of workspace wango_block_fwd needs; 0 if the arguments are invalid. */
+size_t wango_workspace_size(const tango_shape_t* shape, int32_t window, int32_t phi_dim,
+                            int32_t chunk);
+
+/* WANGO block ([TANGO] §2.2 eqs. 7-10): window of `window` positions
+ * (counting the destination), feature map of width phi_dim (= head_dim), and
+ * the older-prefix running sums carried across chunks of `chunk` positions.
+ * The result does not depend on `chunk` except through float rounding. */
+int wango_block_fwd(const tango_shape_t* shape, const tango_weights_t* weights,
+                    int32_t window, int32_t phi_dim, int32_t chunk,
+                    const void* x, void* out, void* workspace, size_t workspace_bytes,
+                    void* hip_stream);
+
+/* ---- Diagnostics --------------------------------------------------------- */
+
+const char* tango_status_string(int status);  /* static string, never NULL        */
+const char* tango_last_error(void);           /* thread-local detail, never NULL  */
+int tango_version(void);                      /* TANGO_ABI_VERSION                */
+
+/* ---- Stage entry points (for stage-by-stage parity tests) ---------------
+ *
+ * They run one kernel of the block on caller buffers.  Intermediate layouts:
+ *   Tp        = seq_len rounded up to a multiple of 128 (rows >= T are padding
+ *               that the projection stage writes as zeros);
+ *   V, gbar   = [B, Tp, F] row-major, dtype;
+ *   qh, kh    = [B, Tp, H*d_h] row-major, dtype, unit length per head;
+ *   gp        = the gates g in the source-packed layout [B][Tp/32][4][F][8]:
+ *               element (b, blk, grp, f, s) holds g[b, t, f] for
+ *               t = 32*blk + (s < 4 ? 4*grp + s : 16 + 4*grp + (s - 4));
+ *   n_old     = [B, Tp, F] float32, z_old = [B, Tp, H] float32: the WANGO
+ *               older-prefix numerator phi(sqrt(tau) q)^T S and denominator
+ *               phi(sqrt(tau) q)^T z of eq. 10 (zero for i < window).
+ */
+
+/* Projections ([TANGO] §2.1 eq. 2 and the head paragraph): RMSNorm, SiLU gate
+ * (packed), features, RoPE + unit-norm queries and keys. */
+int tango_stage_proj(const tango_shape_t* shape, const tango_weights_t* weights,
+                     const void* x, void* gp, void* v, void* qh, void* kh, void* hip_stream);
+
+/* TANGO aggregation ([TANGO] eqs. 4-6): gbar from qh, kh, gp.  Needs the same
+ * workspace as tango_block_fwd (it uses the split-sum scratch area). */
+int tango_stage_aggregate(const tango_shape_t* shape, const float* theta,
+                          const float* null_bias, const void* qh, const void* kh,
+                          const void* gp, void* gbar, void* workspace, size_t workspace_bytes,
+                          void* hip_stream);
+
+/* Output projection and residual ([TANGO] eq. 3): out = x + (gbar * v) W_o^T. */
+int tango_stage_out(const tango_shape_t* shape, const void* w_o, const void* x,
+                    const void* gbar, const void* v, void* out, void* hip_stream);
+
+/* WANGO older-prefix running sums ([TANGO] eqs. 8-10): n_old, z_old.  Needs
+ * the workspace of wango_block_fwd (segment-state scratch). */
+int wango_stage_scan(const tango_shape_t* shape, const float* theta, int32_t window,
+                     int32_t chunk, const void* qh, const void* kh, const void* gp,
+                     void* n_old, void* z_old, void* workspace, size_t workspace_bytes,
+                     void* hip_stream);
+
+/* WANGO window band and joint normalisation ([TANGO] eqs. 5, 7 and the
+ * joint-normalisation paragraph of §2.2): gbar from the window exp weights plus
+ * n_old, z_old and the null term. */
+int wango_stage_band(const tango_shape_t* shape, const float* theta, const float* null_bias,
+                     int32_t window, const void* qh, const void* kh, const void* gp,
+                     const float* n_old, const float* z_old, void* gbar, void* hip_stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* TANGO_H_ */

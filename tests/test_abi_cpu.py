@@ -1,0 +1,148 @@
+"""The C-ABI library on the host: it loads, exports every symbol the header
+declares, and rejects bad arguments before anything reaches the GPU.
+
+None of these calls launches a kernel: each one fails validation (or only
+computes a size), which happens before any HIP call.
+"""
+import ctypes
+import os
+import re
+
+import pytest
+
+from cross_token_gated_amd import _lib
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "tango.h")
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(_lib.LIB_PATH):
+        from cross_token_gated_amd import build
+        build.build(verbose=False)
+    return _lib.load()
+
+
+def header_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\**\s+\**(\w+)\s*\(", text, re.M)))
+
+
+def test_header_and_binding_agree():
+    assert header_functions() == sorted(_lib.EXPORTS)
+
+
+def test_library_exports_every_declared_symbol(lib):
+    for name in header_functions():
+        assert hasattr(lib, name), name
+    assert lib.tango_version() == 1
+    for code in range(-8, 1):
+        assert lib.tango_status_string(code).decode().startswith(_lib.STATUS[code])
+
+
+def shape(**kw):
+    base = dict(batch=1, seq_len=256, d_model=512, d_gate=2048, n_heads=1, head_dim=128, dtype=1,
+                io_dtype=1, rope_base=10000.0, rms_eps=1e-6)
+    base.update(kw)
+    return _lib.Shape(**base)
+
+
+FAKE = 0x7F0000000000   # never dereferenced: every call below fails validation first
+
+
+def weights(**kw):
+    base = dict(w_g=FAKE + 0x10000000, w_v=FAKE + 0x20000000, w_q=FAKE + 0x30000000,
+                w_k=FAKE + 0x31000000, w_o=FAKE + 0x40000000, rms_gain=None,
+                theta=FAKE + 0x50000000, null_bias=None)
+    base.update(kw)
+    return _lib.Weights(**base)
+
+
+def call_tango(lib, s, w=None, x=FAKE, out=FAKE + 0x60000000, ws=FAKE + 0x80000000, nbytes=None):
+    w = weights() if w is None else w
+    if nbytes is None:
+        nbytes = lib.tango_workspace_size(ctypes.byref(s))
+    return lib.tango_block_fwd(ctypes.byref(s), ctypes.byref(w), x, out, ws, nbytes, None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(dtype=7), "TANGO_ERR_DTYPE"),
+    (dict(io_dtype=-1), "TANGO_ERR_DTYPE"),
+    (dict(batch=0), "TANGO_ERR_SHAPE"),
+    (dict(seq_len=0), "TANGO_ERR_SHAPE"),
+    (dict(d_gate=2048, n_heads=3), "TANGO_ERR_SHAPE"),
+    (dict(rms_eps=0.0), "TANGO_ERR_SHAPE"),
+    (dict(rope_base=-1.0), "TANGO_ERR_SHAPE"),
+    (dict(d_model=448), "TANGO_ERR_UNSUPPORTED"),
+    (dict(head_dim=96), "TANGO_ERR_UNSUPPORTED"),
+    (dict(d_gate=2080), "TANGO_ERR_UNSUPPORTED"),
+    (dict(d_gate=1024 + 64, n_heads=17), "TANGO_ERR_UNSUPPORTED"),
+    (dict(batch=1 << 20, seq_len=1 << 10), "TANGO_ERR_UNSUPPORTED"),
+])
+def test_shape_errors(lib, kw, code):
+    s = shape(**kw)
+    assert call_tango(lib, s, nbytes=1 << 40) == _lib.STATUS_CODE[code]
+    assert lib.tango_last_error().decode()
+    assert lib.tango_workspace_size(ctypes.byref(s)) == 0
+
+
+def test_null_pointers(lib):
+    s = shape()
+    assert lib.tango_block_fwd(None, None, None, None, None, 0, None) == -1
+    assert call_tango(lib, s, x=None) == -1
+    assert call_tango(lib, s, ws=None) == -1
+    assert call_tango(lib, s, w=weights(w_o=None)) == -1
+    assert call_tango(lib, s, w=weights(theta=None)) == -1
+
+
+def test_workspace_too_small(lib):
+    s = shape()
+    n = lib.tango_workspace_size(ctypes.byref(s))
+    assert n > 0
+    assert call_tango(lib, s, nbytes=n - 1) == _lib.STATUS_CODE["TANGO_ERR_WORKSPACE"]
+
+
+def test_alignment_and_aliasing(lib):
+    s = shape()
+    assert call_tango(lib, s, x=FAKE + 8) == _lib.STATUS_CODE["TANGO_ERR_ALIGN"]
+    assert call_tango(lib, s, out=FAKE + 0x10000000 + 256) == _lib.STATUS_CODE["TANGO_ERR_ALIAS"]  # out over w_g
+    n = lib.tango_workspace_size(ctypes.byref(s))
+    assert call_tango(lib, s, ws=FAKE + 4096, nbytes=n) == _lib.STATUS_CODE["TANGO_ERR_ALIAS"]    # ws over x
+    assert call_tango(lib, s, out=FAKE + 1024) == _lib.STATUS_CODE["TANGO_ERR_ALIAS"]   # partial overlap with x
+
+
+@pytest.mark.parametrize("args,code", [
+    ((0, 128, 128), "TANGO_ERR_SHAPE"),         # window < 1
+    ((256, 64, 128), "TANGO_ERR_SHAPE"),        # phi_dim != head_dim
+    ((256, 128, 32), "TANGO_ERR_UNSUPPORTED"),  # chunk
+    ((192, 128, 128), "TANGO_ERR_UNSUPPORTED"), # window % chunk
+])
+def test_wango_argument_errors(lib, args, code):
+    s = shape()
+    w = weights()
+    window, phi, chunk = args
+    assert lib.wango_workspace_size(ctypes.byref(s), window, phi, chunk) == 0
+    rc = lib.wango_block_fwd(ctypes.byref(s), ctypes.byref(w), window, phi, chunk, FAKE,
+                             FAKE + 0x60000000, FAKE + 0x80000000, 1 << 40, None)
+    assert rc == _lib.STATUS_CODE[code]
+
+
+def test_workspace_sizes_cover_the_layout(lib):
+    # TANGO at T=8192: gates, features, gbar (3 x 32 MiB), q/k (2 x 2 MiB),
+    # and the float32 split partials
+    n = lib.tango_workspace_size(ctypes.byref(shape(seq_len=8192)))
+    assert n >= 3 * 8192 * 2048 * 2 + 2 * 8192 * 128 * 2
+    n5 = lib.wango_workspace_size(ctypes.byref(shape(batch=2, seq_len=65536)), 512, 128, 128)
+    assert n5 >= 2 * 65536 * 2048 * (3 * 2 + 4)
+
+
+def test_stage_entry_points_validate(lib):
+    s = shape()
+    w = weights()
+    assert lib.tango_stage_proj(ctypes.byref(s), ctypes.byref(w), None, FAKE, FAKE, FAKE, FAKE, None) == -1
+    assert lib.tango_stage_aggregate(ctypes.byref(s), FAKE, None, FAKE, FAKE, FAKE, FAKE, FAKE, 0, None) == -6
+    assert lib.tango_stage_out(ctypes.byref(shape(dtype=3)), FAKE, FAKE, FAKE, FAKE, FAKE, None) == -3
+    assert lib.wango_stage_scan(ctypes.byref(s), FAKE, 0, 128, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 0, None) == -2
+    assert lib.wango_stage_band(ctypes.byref(s), FAKE, None, 0, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None) == -2

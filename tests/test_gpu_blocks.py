@@ -1,0 +1,91 @@
+"""Whole-block parity against the float64 oracle, through the C ABI.
+
+Small blocks of every mode and dtype, then the shipped workloads at their full
+sizes (the stacked ones with every application), plus determinism, in-place
+versus out-of-place and non-default streams.  The bar is max|err|/rms of the
+output: 2e-2 for bf16 storage, 1e-4 for float32.
+"""
+import numpy as np
+import pytest
+import torch
+
+from cross_token_gated_amd import api
+from cross_token_gated_amd import workload as wl
+from tests import helpers as H
+from tests.gpu_common import announce, block_weights, dev_tensor, host, run_workload
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    from cross_token_gated_amd import _lib
+    _lib.load()
+
+
+SMALL = [
+    dict(mode="tango", dtype="bf16", io_dtype="f32", B=2, T=300, d_model=256, d_gate=512, n_heads=1,
+         head_dim=128, repeats=2),
+    dict(mode="tango", dtype="bf16", io_dtype="bf16", B=1, T=500, d_model=256, d_gate=512, n_heads=2,
+         head_dim=64),
+    dict(mode="tango", dtype="f32", B=1, T=200, d_model=128, d_gate=256, n_heads=2, head_dim=64, repeats=2),
+    dict(mode="wango", dtype="bf16", io_dtype="f32", B=1, T=700, d_model=128, d_gate=512, n_heads=2,
+         head_dim=64, window=128, chunk=128, repeats=2),
+    dict(mode="wango", dtype="bf16", io_dtype="bf16", B=2, T=250, d_model=128, d_gate=256, n_heads=1,
+         head_dim=128, window=64, chunk=64),
+    dict(mode="wango", dtype="f32", B=1, T=300, d_model=128, d_gate=128, n_heads=1, head_dim=32,
+         window=64, chunk=64),
+]
+
+
+@pytest.mark.parametrize("case", SMALL, ids=lambda c: f"{c['mode']}-{c['dtype']}-io{c.get('io_dtype', c['dtype'])}-B{c['B']}-T{c['T']}-R{c.get('repeats', 1)}")
+@pytest.mark.parametrize("null", [False, True])
+def test_small_block(case, null):
+    w = wl.small_workload(**case, null_bias=(-1.0 if null else None))
+    inp = wl.make_inputs(w)
+    announce(f"small_block {case} null={null}")
+    out = run_workload(w, inp)
+    torch.cuda.synchronize()
+    ref = H.oracle_stack(w, inp)
+    assert H.err_ratio(host(out), ref) < H.tol(w.dtype)
+
+
+@pytest.mark.parametrize("name", ["tango_f32_t256", "tango_bf16_b8_t2048", "tango_bf16_t8192_r4",
+                                  "wango_bf16_t8192_w256"])
+def test_workload_full_size(name):
+    w = wl.WORKLOADS[name]
+    inp = wl.make_inputs(w)
+    announce(f"workload {name}")
+    out = run_workload(w, inp)
+    torch.cuda.synchronize()
+    got = host(out)
+    ref = H.oracle_stack(w, inp)
+    e = H.err_ratio(got, ref)
+    h0 = np.asarray(inp.h, np.float64)
+    d = H.rms_ratio(got - h0, ref - h0)
+    print(f"{name}: max|err|/rms = {e:.3e}; rms error of the total update {d:.3e}")
+    assert e < H.tol(w.dtype)
+
+
+@pytest.mark.parametrize("mode", ["tango", "wango"])
+def test_deterministic_inplace_and_streams(mode):
+    kw = dict(window=128, chunk=64) if mode == "wango" else {}
+    w = wl.small_workload(mode=mode, dtype="bf16", B=1, T=900, d_model=128, d_gate=256, n_heads=1,
+                          head_dim=64, **kw)
+    inp = wl.make_inputs(w)
+    bw = block_weights(w, inp)
+    x = dev_tensor(inp.h, w.io)
+    announce(f"determinism {mode}")
+    fwd = api.tango_block_fwd if mode == "tango" else (
+        lambda x, bw, **k: api.wango_block_fwd(x, bw, w.window, w.head_dim, w.chunk, **k))
+    a = fwd(x, bw)
+    b = fwd(x, bw)
+    s = torch.cuda.Stream()
+    with torch.cuda.stream(s):
+        c = fwd(x, bw, stream=s)
+    s.synchronize()
+    xin = x.clone()
+    d = fwd(xin, bw, out=xin)
+    torch.cuda.synchronize()
+    assert torch.equal(a, b) and torch.equal(a, c) and torch.equal(a, d)

@@ -31,3 +31,20 @@ def test_workload_table():
     assert t["wango_bf16_t8192_w256"].n_heads * t["wango_bf16_t8192_w256"].head_dim == 128
     assert t["tango_bf16_t8192_r4"].repeats == 4
     assert t["wango_bf16_b2_t65536_w512_r8"].repeats == 8
+
+
+def test_layout_packers_roundtrip():
+    from tests import helpers as H
+    rng = np.random.default_rng(1)
+    g = rng.standard_normal((256, 48))
+    np.testing.assert_array_equal(H.unpack_gates(H.pack_gates(g), 256, 48), g)
+    gp = H.pack_gates(g)
+    # element (blk, grp, f, s) is g[32 blk + perm(grp, s), f]
+    for blk, grp, f, s in [(0, 0, 0, 0), (1, 3, 47, 7), (5, 2, 10, 4), (7, 1, 3, 3)]:
+        t = 32 * blk + (4 * grp + s if s < 4 else 16 + 4 * grp + s - 4)
+        assert gp[blk, grp, f, s] == g[t, f]
+    n = rng.standard_normal((64, 32))
+    nb = H.block_nold(n)
+    np.testing.assert_array_equal(H.unblock_nold(nb, 64, 32), n)
+    # lane l of block (ib, fb) holds row 16 ib + l % 16, columns 16 fb + 4 (l // 16) + r
+    assert nb[1, 1, 37, 2] == n[16 + 37 % 16, 16 + 4 * (37 // 16) + 2]

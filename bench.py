@@ -1,0 +1,242 @@
+"""Benchmark of the TANGO / WANGO block forward on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
+
+One step runs every part of the block forward once at T = 8192 tokens:
+  * TANGO, bf16 compute, B = 1, T = 8192, d = 512, F = 2048, q/k width 128,
+    scale 10, the shared block applied 4 times (projection, full-prefix
+    aggregation, output projection, four times over);
+  * WANGO, bf16 compute, B = 1, T = 8192, same widths as two heads of 64,
+    window 256, prefix-scan chunk 128, one application (projection, running-sum
+    scan, window band + combine, output projection).
+Inputs are seeded synthetic tensors already resident in HBM.  The value is
+sequence tokens per second: (8192 + 8192) tokens / step time.
+
+Alongside, with HIP events on the launch stream:
+  * roofline: the TANGO aggregation kernel (the dominant one), useful MFMA
+    flops 2 * (causal pairs) * (q/k width + F) per launch over its average
+    launch time, against 2.5 PFLOP/s dense bf16;
+  * roofline_scan: the WANGO running-sum scan (three launches), algorithmic
+    HBM bytes (q, k, g read once; n_old, z_old written once) over its time,
+    against 8 TB/s;
+  * cpu_baseline: the float64 CPU oracle on a bounded sample of the same work
+    (one of the four TANGO applications, scaled by 4, plus the WANGO block).
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_BF16_FLOPS = 2.5e15   # MI355X dense bf16 MFMA
+PEAK_HBM_BYTES = 8.0e12    # MI355X HBM3E
+
+TANGO = "tango_bf16_t8192_r4"
+WANGO = "wango_bf16_t8192_w256"
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--kernel-loops", type=int, default=None,
+                    help="launches per roofline measurement (default: --steps)")
+    return ap.parse_args()
+
+
+def tango_flops(w) -> float:
+    pairs = w.B * w.T * (w.T + 1) // 2
+    return 2.0 * pairs * (w.n_heads * w.head_dim + w.d_gate)
+
+
+def scan_bytes(w) -> float:
+    hd = w.n_heads * w.head_dim
+    return float(w.B * w.T * (2 * hd * 2 + w.d_gate * 2 + w.d_gate * 4 + w.n_heads * 4))
+
+
+def cpu_baseline(wt, wg) -> dict:
+    """The float64 oracle, untuned, on a bounded sample of the step."""
+    import numpy as np
+
+    import oracle.tango_oracle as O
+    from cross_token_gated_amd import workload as wl
+    from tests import helpers as H
+
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max(int(i.get("num_threads", 1)) for i in threadpool_info()) if threadpool_info() else 1
+    except Exception:  # noqa: BLE001
+        cores = len(os.sched_getaffinity(0))
+    secs = 0.0
+    for w, scale in ((wt, wt.repeats), (wg, 1)):
+        inp = wl.make_inputs(w)
+        h = np.asarray(inp.h[0], dtype=np.float64)
+        p, cfg = H.oracle_params(inp), H.oracle_config(w)
+        t0 = time.perf_counter()
+        O.block_sequence(h, p, cfg)
+        secs += (time.perf_counter() - t0) * scale
+    tokens = wt.tokens + wg.tokens
+    return {"value": tokens / secs, "unit": "tokens/s", "cores": cores, "kind": "oracle",
+            "sample": (f"one of the {wt.repeats} TANGO T={wt.T} applications (time x{wt.repeats}) "
+                       f"plus the WANGO T={wg.T} application, float64 numpy; "
+                       f"{secs:.1f} s for one step")}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only; --gpus {args.gpus} is not supported "
+              f"(the block forward needs no collectives; see the sharding notes in DESIGN.md)",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    from cross_token_gated_amd import api
+    from cross_token_gated_amd import workload as wl
+    from tests.gpu_common import block_weights, dev_f32, dev_tensor
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    dev = torch.device("cuda:0")
+    wt, wg = wl.WORKLOADS[TANGO], wl.WORKLOADS[WANGO]
+    it, ig = wl.make_inputs(wt), wl.make_inputs(wg)
+    bt, bg = block_weights(wt, it), block_weights(wg, ig)
+    xt = dev_tensor(it.h, wt.io)
+    xg = dev_tensor(ig.h, wg.io)
+    ping, pong, outg = torch.empty_like(xt), torch.empty_like(xt), torch.empty_like(xg)
+    st = api.shape_of(xt, bt, wt.rope_base, wt.rms_eps)
+    sg = api.shape_of(xg, bg, wg.rope_base, wg.rms_eps)
+    ws_t = api.workspace(api.tango_workspace_size(st), dev)
+    ws_g = api.workspace(api.wango_workspace_size(sg, wg.window, wg.head_dim, wg.chunk), dev)
+    stream = torch.cuda.current_stream()
+
+    def step():
+        src = xt
+        for r in range(wt.repeats):            # x -> ping -> pong -> ping -> pong
+            dst = ping if r % 2 == 0 else pong
+            api.tango_block_fwd(src, bt, out=dst, ws=ws_t, rope_base=wt.rope_base,
+                                rms_eps=wt.rms_eps, stream=stream)
+            src = dst
+        api.wango_block_fwd(xg, bg, wg.window, wg.head_dim, wg.chunk, out=outg, ws=ws_g,
+                            rope_base=wg.rope_base, rms_eps=wg.rms_eps, stream=stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t_wall = time.perf_counter()
+    e0.record(stream)
+    for _ in range(args.steps):
+        step()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t_wall
+    ms_step = e0.elapsed_time(e1) / args.steps
+    tokens = wt.tokens + wg.tokens
+    print(f"[bench] {args.steps} steps: {ms_step:.3f} ms/step (host wall {1e3 * wall / args.steps:.3f})",
+          file=sys.stderr, flush=True)
+
+    # ---- per-workload breakdown and the dominant kernels, same stream ----
+    loops = args.kernel_loops or args.steps
+    Tp = api.padded_len(wt.T)
+    M = wt.B * Tp
+    F, HD = wt.d_gate, wt.n_heads * wt.head_dim
+    gp = torch.empty(M * F, dtype=torch.bfloat16, device=dev)
+    v = torch.empty(M, F, dtype=torch.bfloat16, device=dev)
+    qh = torch.empty(M, HD, dtype=torch.bfloat16, device=dev)
+    kh = torch.empty(M, HD, dtype=torch.bfloat16, device=dev)
+    gbar = torch.empty(M, F, dtype=torch.bfloat16, device=dev)
+    api.tango_stage_proj(st, bt, xt, gp, v, qh, kh, stream=stream)
+
+    def timed(fn, n):
+        fn()
+        torch.cuda.synchronize()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        for _ in range(n):
+            fn()
+        b.record(stream)
+        torch.cuda.synchronize()
+        return a.elapsed_time(b) / n
+
+    def tango_only():
+        src = xt
+        for r in range(wt.repeats):
+            dst = ping if r % 2 == 0 else pong
+            api.tango_block_fwd(src, bt, out=dst, ws=ws_t, stream=stream)
+            src = dst
+
+    ms_tango = timed(tango_only, loops)
+    ms_wango = timed(lambda: api.wango_block_fwd(xg, bg, wg.window, wg.head_dim, wg.chunk, out=outg,
+                                                 ws=ws_g, stream=stream), loops)
+    ms_agg = timed(lambda: api.tango_stage_aggregate(st, bt.theta, None, qh, kh, gp, gbar, ws_t,
+                                                     stream=stream), loops)
+    # WANGO scan inputs (two heads of 64)
+    Mg = wg.B * api.padded_len(wg.T)
+    HDg = wg.n_heads * wg.head_dim
+    gpg = torch.empty(Mg * wg.d_gate, dtype=torch.bfloat16, device=dev)
+    vg = torch.empty(Mg, wg.d_gate, dtype=torch.bfloat16, device=dev)
+    qg = torch.empty(Mg, HDg, dtype=torch.bfloat16, device=dev)
+    kg = torch.empty(Mg, HDg, dtype=torch.bfloat16, device=dev)
+    api.tango_stage_proj(sg, bg, xg, gpg, vg, qg, kg, stream=stream)
+    n_old = torch.empty(Mg * wg.d_gate, dtype=torch.float32, device=dev)
+    z_old = torch.empty(Mg, wg.n_heads, dtype=torch.float32, device=dev)
+    ms_scan = timed(lambda: api.wango_stage_scan(sg, bg.theta, wg.window, wg.chunk, qg, kg, gpg, n_old,
+                                                 z_old, ws_g, stream=stream), loops)
+
+    agg_flops = tango_flops(wt)
+    achieved = agg_flops / (ms_agg * 1e-3)
+    sbytes = scan_bytes(wg)
+    s_ach = sbytes / (ms_scan * 1e-3)
+    result = {
+        "metric": "block fwd tokens/s at T=8192 (TANGO & WANGO); % MFMA peak / % HBM peak",
+        "value": tokens / (ms_step * 1e-3),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic: seeded N(0,1) activations, N(0,1/fan_in) weights, rounded to bf16",
+        "config": {"workload": "tango_t8192_x4+wango_t8192_w256",
+                   "tango": {"B": wt.B, "T": wt.T, "d_model": wt.d_model, "d_gate": wt.d_gate,
+                             "qk_dim": HD, "heads": wt.n_heads, "repeats": wt.repeats},
+                   "wango": {"B": wg.B, "T": wg.T, "d_model": wg.d_model, "d_gate": wg.d_gate,
+                             "qk_dim": HDg, "heads": wg.n_heads, "window": wg.window,
+                             "phi_dim": wg.head_dim, "chunk": wg.chunk},
+                   "residual_dtype": "f32", "parallelism": "single GPU"},
+        "per_workload": {
+            TANGO: {"tokens_per_s": wt.tokens / (ms_tango * 1e-3), "ms": ms_tango,
+                    "ms_per_application": ms_tango / wt.repeats},
+            WANGO: {"tokens_per_s": wg.tokens / (ms_wango * 1e-3), "ms": ms_wango},
+        },
+        "roofline": {"kernel": "agg_kernel (TANGO aggregation, T=8192)", "bound": "mfma",
+                     "achieved": achieved / 1e12, "peak": PEAK_BF16_FLOPS / 1e12, "unit": "TFLOP/s",
+                     "frac": achieved / PEAK_BF16_FLOPS, "traffic": None,
+                     "flops_per_launch": agg_flops, "ms_per_launch": ms_agg},
+        "roofline_scan": {"kernel": "WANGO running-sum scan (3 launches, T=8192)", "bound": "hbm",
+                          "achieved": s_ach / 1e9, "peak": PEAK_HBM_BYTES / 1e9, "unit": "GB/s",
+                          "frac": s_ach / PEAK_HBM_BYTES, "traffic": None,
+                          "bytes_per_launch": sbytes, "ms_per_launch": ms_scan},
+    }
+    print(f"[bench] tango {ms_tango:.3f} ms, wango {ms_wango:.3f} ms, aggregation {ms_agg:.3f} ms "
+          f"({result['roofline']['frac'] * 100:.1f}% of bf16 peak), scan {ms_scan:.4f} ms "
+          f"({result['roofline_scan']['frac'] * 100:.1f}% of HBM peak)", file=sys.stderr, flush=True)
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"] = cpu_baseline(wt, wg)
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

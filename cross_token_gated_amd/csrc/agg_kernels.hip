@@ -15,14 +15,22 @@
 // cancels in the ratio (the null and older-prefix terms are scaled by e^{-tau}
 // to match) and every weight stays in [e^{-40}, 1], far from float32 limits.
 // With no running maximum, partial sums over disjoint source ranges combine by
-// plain addition.
+// plain addition and the accumulators are never rescaled.
 //
-// Workgroup: 8 waves over a 64-row destination tile and FS = 8 * WCOLS gate
-// columns of one head.  Per 64-source block the waves compute S^T = K Q^T (two
-// 16x16 blocks each), turn it into weights, and publish them through LDS; then
-// every wave multiplies its own WCOLS gate columns: gbar^T += G^T P^T, with the
-// gates read straight from the packed layout (their k order is the row order
-// of the S^T accumulators, so no transpose is needed anywhere).
+// Workgroup: 4 waves (one per SIMD, so each wave owns the whole 512-entry
+// register file; the float32 accumulator block lives in AGPRs) over a BR-row
+// destination tile and FS = 4 * WCOLS gate columns of one head.  Per step of
+// 64 sources:
+//   * the key block is staged once in LDS (double-buffered, fetched two steps
+//     ahead);
+//   * each wave computes S^T = K Q^T for its share of destination rows against
+//     all 64 sources and writes the weights to LDS -- one step ahead, between
+//     the two halves of the current step's product;
+//   * every wave multiplies its own WCOLS gate columns: gbar^T += G^T P^T, the
+//     gates read straight from the packed layout in global memory (their k
+//     order is the row order of the S^T accumulators), double-buffered in
+//     registers.
+// One barrier per step.
 //
 // TANGO load balance: with B*H*column-chunks*(tiles/2) >= 256 the long and the
 // short tile of a causal pair share one workgroup.  Otherwise each long tile is
@@ -36,77 +44,103 @@ namespace tango {
 
 namespace {
 
+// Destination rows per tile and gate columns per wave.  The narrow variant
+// (16 columns per wave) serves heads whose gate width is not a multiple of
+// 8 * WIDE; there a wave whose columns lie past the head's width skips the
+// product (a wave-uniform branch).
 template <typename T> struct AggCfg;
-template <> struct AggCfg<bf16> { static constexpr int WAVES = 8, WCOLS = 128; };
-template <> struct AggCfg<float> { static constexpr int WAVES = 8, WCOLS = 64; };
+template <> struct AggCfg<bf16> { static constexpr int BR = 128, WIDE = 64; };
+template <> struct AggCfg<float> { static constexpr int BR = 64, WIDE = 32; };
+constexpr int kNarrow = 16;
 
-constexpr int BR = 64;   // destination rows per tile
-constexpr int BC = 64;   // sources per step
-constexpr int kAggThreads = 512;
+constexpr int kWaves = 8;                 // two waves per SIMD
+constexpr int BC = 64;                    // sources per step
+constexpr int kAggThreads = 64 * kWaves;
 
 enum JobKind { kFull = 0, kPart0 = 1, kPart1 = 2 };
 struct Job {
-  int tile, jb0, jb1, kind;
+  int tile, jb0, jb1, kind;   // destination tile; source steps jb0..jb1 (64 each)
   int64_t split_id;
 };
 
-template <typename T, int MODE, int DH>
+template <typename T, int DH> struct AggLds {
+  static constexpr int BR = AggCfg<T>::BR;
+  static constexpr int KSTR = DH + 16 / (int)sizeof(T);    // row stride of a key block
+  static constexpr int PSTR = BC + 16 / (int)sizeof(T);    // row stride of the weights
+  T ks[2][BC * KSTR];
+  T ps[2][BR * PSTR];
+  float den[kWaves][BR];
+  int flag;
+};
+
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+template <typename T, int MODE, int DH, int WCOLS>
 __global__ __launch_bounds__(kAggThreads) void agg_kernel(AggArgs a, int nfc, int rtiles,
                                                           int64_t items) {
-  constexpr int WAVES = AggCfg<T>::WAVES, WCOLS = AggCfg<T>::WCOLS;
-  constexpr int FS = WAVES * WCOLS, NFB = WCOLS / 16;
-  constexpr int PS = BC + 16 / (int)sizeof(T);   // LDS row stride of P
+  constexpr int BR = AggCfg<T>::BR;
+  constexpr int FS = kWaves * WCOLS, NFB = WCOLS / 16, NIB = BR / 16;
+  constexpr int JBW = NIB * (BC / 16) / kWaves;  // S^T source blocks per wave (one dest block)
+  constexpr int NSPLIT = kWaves / NIB;           // waves sharing one destination block
   constexpr int KS = DH / 32;
-  __shared__ __align__(16) T Ps[2][BR * PS];
-  __shared__ float den_s[2][BR];
-  __shared__ int flag_s;
+  constexpr int SPT = BR / BC;                    // source steps per destination tile
+  using L = AggLds<T, DH>;
+  constexpr int KSTR = L::KSTR, PSTR = L::PSTR;
+  constexpr int PE = 16 / (int)sizeof(T);        // elements per 16-byte piece
+  constexpr int KPIECES = BC * DH / PE;           // 16-byte pieces of a key block
+  constexpr int KPT = (KPIECES + kAggThreads - 1) / kAggThreads;   // per thread (last may be idle)
+  static_assert(KPIECES % kAggThreads == 0 || KPIECES < kAggThreads, "key block pieces");
+  static_assert(JBW >= 1, "tile shape");
+  __shared__ L sm;
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform (SGPR)
   const int li = lane & 15, lg = lane >> 4;
+  const int wib = wave % NIB;                      // destination block of this wave's S^T
+  const int wjb = (wave / NIB) * JBW;              // its first source block
 
   // Work item of this workgroup.  Consecutive items go to one XCD (workgroup
   // w runs on XCD w % 8), so the workgroups of one XCD share gate columns.
   const int64_t q8 = gridDim.x / 8;
-  const int64_t L = (int64_t)(blockIdx.x % 8) * q8 + blockIdx.x / 8;
-  if (L >= items) return;
+  const int64_t item = (int64_t)(blockIdx.x % 8) * q8 + blockIdx.x / 8;
+  if (item >= items) return;
 
   const int R = rtiles, half = R / 2;
-  Job jobs[2];
+  Job job0 = {0, 0, 0, kFull, 0}, job1 = {0, 0, 0, kFull, 0};
   int njobs = 1;
   int64_t grp;
   if (MODE == 0) {
     const int P = a.split ? 2 * half + (R & 1) : half + (R & 1);
-    grp = L / P;
-    const int p = (int)(L % P);
-    const int64_t split_base = grp * half;
+    grp = item / P;
+    const int p = (int)(item % P);
     if (a.split) {
       if (p == 2 * half) {
-        jobs[0] = {half, 0, half, kFull, 0};
+        job0 = {half, 0, (half + 1) * SPT - 1, kFull, 0};          // middle tile (R odd)
       } else {
-        const int k = p >> 1, rl = R - 1 - k;
-        const int64_t sid = split_base + (half - 1 - k);
+        const int k = p >> 1, rl = R - 1 - k;                      // short tile k, long tile rl
+        const int64_t sid = grp * half + (half - 1 - k);
         if ((p & 1) == 0) {
-          jobs[0] = {rl, rl + 1 - half, rl, kPart0, sid};
+          job0 = {rl, (rl + 1 - half) * SPT, (rl + 1) * SPT - 1, kPart0, sid};
         } else {
-          jobs[0] = {rl, 0, rl - half, kPart1, sid};
-          jobs[1] = {k, 0, k, kFull, 0};
+          job0 = {rl, 0, (rl + 1 - half) * SPT - 1, kPart1, sid};
+          job1 = {k, 0, (k + 1) * SPT - 1, kFull, 0};
           njobs = 2;
         }
       }
     } else {
       if (p == half) {
-        jobs[0] = {half, 0, half, kFull, 0};
+        job0 = {half, 0, (half + 1) * SPT - 1, kFull, 0};
       } else {
-        jobs[0] = {R - 1 - p, 0, R - 1 - p, kFull, 0};
-        jobs[1] = {p, 0, p, kFull, 0};
+        job0 = {R - 1 - p, 0, (R - p) * SPT - 1, kFull, 0};
+        job1 = {p, 0, (p + 1) * SPT - 1, kFull, 0};
         njobs = 2;
       }
     }
   } else {
-    grp = L / R;
-    const int r = (int)(L % R);
+    grp = item / R;
+    const int r = (int)(item % R);
     const int lo = r * BR - a.window + 1;
-    jobs[0] = {r, lo > 0 ? lo / BC : 0, r, kFull, 0};
+    job0 = {r, lo > 0 ? lo / BC : 0, (r + 1) * SPT - 1, kFull, 0};
   }
   const int fc = (int)(grp % nfc);
   const int64_t bh = grp / nfc;
@@ -114,15 +148,14 @@ __global__ __launch_bounds__(kAggThreads) void agg_kernel(AggArgs a, int nfc, in
   const int64_t b = bh / a.H;
 
   const int F = a.F, HD = a.H * DH, Fh = F / a.H, Tp = a.Tp;
-  const int f_base = fc * FS + wave * WCOLS;         // within the head
-  int nfb_valid = (Fh - f_base) / 16;
-  nfb_valid = nfb_valid < 0 ? 0 : (nfb_valid > NFB ? NFB : nfb_valid);
-  const int64_t col0 = (int64_t)h * Fh + f_base;      // global gate column
-  const int64_t mseq = b * Tp;                        // first row of the sequence
+  const int f_base = fc * FS + wave * WCOLS;          // within the head
+  const bool has_cols = f_base < Fh;                   // wave-uniform; always true when FS divides Fh
+  const int64_t col0 = (int64_t)h * Fh + f_base;       // global gate column
+  const int64_t mseq = b * Tp;                         // first row of the sequence
 
   const float tau = __expf(fminf(a.theta[h], 2.995732273553991f));   // log 20
   const float ktau = tau * kLog2e;
-  const float escale = __expf(-tau);                  // e^{-tau}: the fixed shift
+  const float escale = __expf(-tau);                   // e^{-tau}: the fixed shift
   const float null_w = a.null_bias ? __expf(a.null_bias[h] - tau) : 0.f;
 
   const T* __restrict__ qh = static_cast<const T*>(a.qh);
@@ -130,145 +163,200 @@ __global__ __launch_bounds__(kAggThreads) void agg_kernel(AggArgs a, int nfc, in
   const T* __restrict__ gp = static_cast<const T*>(a.gp);
   T* __restrict__ gbar = static_cast<T*>(a.gbar);
 
-  const int wi = wave & 3;              // i-block of this wave's S^T blocks
-  const int wj = 2 * (wave >> 2);       // first of its two j-blocks
+  // key block jb -> registers (this thread's pieces) -> LDS buffer
+  auto key_fetch = [&](int jb, u32x4 (&kr)[KPT]) {
+#pragma unroll
+    for (int p = 0; p < KPT; ++p) {
+      const int piece = tid + p * kAggThreads;
+      if (KPIECES % kAggThreads != 0 && piece >= KPIECES) break;
+      const int row = piece / (DH / PE), c = (piece % (DH / PE)) * PE;
+      kr[p] = *reinterpret_cast<const u32x4*>(kh + (mseq + (int64_t)jb * BC + row) * HD + h * DH + c);
+    }
+  };
+  auto key_stash = [&](int buf, const u32x4 (&kr)[KPT]) {
+#pragma unroll
+    for (int p = 0; p < KPT; ++p) {
+      const int piece = tid + p * kAggThreads;
+      if (KPIECES % kAggThreads != 0 && piece >= KPIECES) break;
+      const int row = piece / (DH / PE), c = (piece % (DH / PE)) * PE;
+      *reinterpret_cast<u32x4*>(&sm.ks[buf][row * KSTR + c]) = kr[p];
+    }
+  };
+  auto gate_fetch = [&](int jb, int ks, Frag<T> (&gf)[NFB]) {
+    if (!has_cols) return;
+    const int64_t blk = (mseq + (int64_t)jb * BC) / 32 + ks;
+#pragma unroll
+    for (int fb = 0; fb < NFB; ++fb) gf[fb] = load_frag<T>(gp + packed_offset(blk, lg, col0 + fb * 16 + li, F));
+  };
 
-  for (int jn = 0; jn < njobs; ++jn) {
-    const Job job = jn == 0 ? jobs[0] : jobs[1];
+  // one destination tile over a range of source steps (called once or twice)
+  auto run_job = [&](const Job job) {
     const int i0 = job.tile * BR;
     // B operand of S^T = K Q^T: column i of Q^T = query row i (linear k slots).
     Frag<T> qf[KS];
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks)
-      qf[ks] = load_frag<T>(qh + (mseq + i0 + wi * 16 + li) * HD + h * DH + ks * 32 + lg * 8);
+      qf[ks] = load_frag<T>(qh + (mseq + i0 + wib * 16 + li) * HD + h * DH + ks * 32 + lg * 8);
 
-    f32x4 acc[4][NFB];
+    f32x4 acc[NIB][NFB];
 #pragma unroll
-    for (int ib = 0; ib < 4; ++ib)
+    for (int ib = 0; ib < NIB; ++ib)
 #pragma unroll
       for (int fb = 0; fb < NFB; ++fb) acc[ib][fb] = f32x4{0.f, 0.f, 0.f, 0.f};
     float rowsum = 0.f;
-    const int i_me = i0 + wi * 16 + li;   // this lane's destination in S^T
+    const int i_me = i0 + wib * 16 + li;     // this lane's destination in S^T
 
-    int buf = 0;
-    for (int jb = job.jb0; jb <= job.jb1; ++jb, buf ^= 1) {
+    // weights of source step jb (key block in ks[buf]) into ps[buf]
+    auto weights = [&](int jb, int buf) {
       const int j0 = jb * BC;
-      // ---- weights of this source block ----
 #pragma unroll
-      for (int jj = 0; jj < 2; ++jj) {
-        const int jblk = wj + jj;
+      for (int jj = wjb; jj < wjb + JBW; ++jj) {
         f32x4 s = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int ks = 0; ks < KS; ++ks) {
-          Frag<T> kf = load_frag<T>(kh + (mseq + j0 + jblk * 16 + li) * HD + h * DH + ks * 32 + lg * 8);
-          mma(s, kf, qf[ks]);
-        }
+        for (int ks = 0; ks < KS; ++ks)
+          mma(s, load_frag<T>(&sm.ks[buf][(jj * 16 + li) * KSTR + ks * 32 + lg * 8]), qf[ks]);
         Quad<T> pq;
         float psum = 0.f;
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
-          const int j = j0 + jblk * 16 + lg * 4 + r;
+          const int j = j0 + jj * 16 + lg * 4 + r;
           bool ok = j <= i_me;
           if (MODE == 1) ok = ok && (j > i_me - a.window);
-          const float p = ok ? exp2f(ktau * (s[r] - 1.0f)) : 0.f;
+          // the argument lies in [-2 tau log2 e, 0] >= -58: v_exp_f32 needs no range fix-up
+          const float p = ok ? __builtin_amdgcn_exp2f(ktau * (s[r] - 1.0f)) : 0.f;
           pq[r] = cvt<T>(p);
           psum += tof<T>(pq[r]);
         }
         rowsum += psum;
-        store_quad<T>(&Ps[buf][(wi * 16 + li) * PS + jblk * 16 + lg * 4], pq);
+        store_quad<T>(&sm.ps[buf][(wib * 16 + li) * PSTR + jj * 16 + lg * 4], pq);
       }
-      __syncthreads();
-      // ---- gbar^T += G^T P^T over the 64 sources ----
-      if (nfb_valid > 0) {
+    };
+    // gbar^T += G^T P^T over one half (32 sources) of the step in ps[buf]
+    auto product = [&](int buf, int ks, const Frag<T> (&gf)[NFB]) {
+      if (!has_cols) return;
 #pragma unroll
-        for (int ks = 0; ks < BC / 32; ++ks) {
-          const int64_t blk = (mseq + j0) / 32 + ks;
-          Frag<T> gf[NFB];
+      for (int ih = 0; ih < NIB; ih += 4) {
+        Frag<T> pf[4];
 #pragma unroll
-          for (int fb = 0; fb < NFB; ++fb)
-            if (fb < nfb_valid) gf[fb] = load_frag<T>(gp + packed_offset(blk, lg, col0 + fb * 16 + li, F));
-          Frag<T> pf[4];
-#pragma unroll
-          for (int ib = 0; ib < 4; ++ib) {
-            const T* prow = &Ps[buf][(ib * 16 + li) * PS + ks * 32];
-            pf[ib] = join(load_quad<T>(prow + lg * 4), load_quad<T>(prow + 16 + lg * 4));
-          }
-#pragma unroll
-          for (int fb = 0; fb < NFB; ++fb)
-            if (fb < nfb_valid)
-#pragma unroll
-              for (int ib = 0; ib < 4; ++ib) mma(acc[ib][fb], gf[fb], pf[ib]);
+        for (int q = 0; q < 4; ++q) {
+          const T* prow = &sm.ps[buf][((ih + q) * 16 + li) * PSTR + ks * 32];
+          pf[q] = join(load_quad<T>(prow + lg * 4), load_quad<T>(prow + 16 + lg * 4));
         }
+#pragma unroll
+        for (int fb = 0; fb < NFB; ++fb)
+#pragma unroll
+          for (int q = 0; q < 4; ++q) mma(acc[ih + q][fb], gf[fb], pf[q]);
       }
+    };
+
+    // prologue: key steps jb0 and jb0+1 in LDS, weights of jb0
+    {
+      u32x4 kr[KPT];
+      key_fetch(job.jb0, kr);
+      key_stash(0, kr);
+      __syncthreads();
+      if (job.jb0 + 1 <= job.jb1) {
+        key_fetch(job.jb0 + 1, kr);
+        key_stash(1, kr);
+      }
+      weights(job.jb0, 0);
+      __syncthreads();
+    }
+    Frag<T> ga[NFB], gb[NFB];
+    gate_fetch(job.jb0, 0, ga);
+    for (int jb = job.jb0; jb <= job.jb1; ++jb) {
+      const int buf = (jb - job.jb0) & 1;
+      const bool more = jb + 1 <= job.jb1;
+      const bool more2 = jb + 2 <= job.jb1;
+      u32x4 kr[KPT];
+      if (more2) key_fetch(jb + 2, kr);
+      gate_fetch(jb, 1, gb);
+      product(buf, 0, ga);
+      if (more) gate_fetch(jb + 1, 0, ga);
+      if (more) weights(jb + 1, buf ^ 1);
+      product(buf, 1, gb);
+      if (more2) key_stash(buf, kr);   // ks[buf] was last read by weights(jb) one step ago
+      __syncthreads();
     }
 
-    // ---- row sums: over lane groups, then over the two waves of an i-block ----
-    const float rs = group_sum(rowsum);
-    if (lg == 0) den_s[wave >> 2][wi * 16 + li] = rs;
+    // ---- row sums: over lane groups, then over the waves sharing a block ----
+    {
+      const float rs = group_sum(rowsum);
+      if (lg == 0) sm.den[wave / NIB][wib * 16 + li] = rs;
+    }
     __syncthreads();
-    float den[4];
+    float den[NIB];
 #pragma unroll
-    for (int ib = 0; ib < 4; ++ib) den[ib] = den_s[0][ib * 16 + li] + den_s[1][ib * 16 + li];
+    for (int ib = 0; ib < NIB; ++ib) {
+      den[ib] = sm.den[0][ib * 16 + li];
+#pragma unroll
+      for (int q = 1; q < NSPLIT; ++q) den[ib] += sm.den[q][ib * 16 + li];
+    }
 
     bool finish = job.kind == kFull;
+    bool combine = false;              // add the partner's partial while storing
+    int64_t obase = 0, odbase = 0;
     if (job.kind != kFull) {
       // write this partial, then the second of the two workgroups combines
       const int slot = job.kind == kPart0 ? 0 : 1;
       const int64_t pbase = (job.split_id * 2 + slot) * (int64_t)BR * FS;
+      if (has_cols) {
 #pragma unroll
-      for (int fb = 0; fb < NFB; ++fb)
-        if (fb < nfb_valid)
+        for (int fb = 0; fb < NFB; ++fb)
 #pragma unroll
-          for (int ib = 0; ib < 4; ++ib)
+          for (int ib = 0; ib < NIB; ++ib)
             *reinterpret_cast<f32x4*>(a.part + pbase +
                                       ((int64_t)(ib * (FS / 16) + wave * NFB + fb) * 64 + lane) * 4) =
                 acc[ib][fb];
-      if (wave == 0) a.part_den[(job.split_id * 2 + slot) * BR + lane] = den_s[0][lane] + den_s[1][lane];
+      }
+      if (wave == 0)
+        for (int ib = 0; ib < NIB; ++ib)
+          if (lg == 0) a.part_den[(job.split_id * 2 + slot) * BR + ib * 16 + li] = den[ib];
       __threadfence();
       __syncthreads();
-      if (tid == 0) flag_s = atomicAdd(&a.counters[job.split_id], 1);
+      if (tid == 0) sm.flag = atomicAdd(&a.counters[job.split_id], 1);
       __syncthreads();
-      if (flag_s == 1) {
+      if (sm.flag == 1) {
         __threadfence();
         const int other = 1 - slot;
-        const int64_t obase = (job.split_id * 2 + other) * (int64_t)BR * FS;
-#pragma unroll
-        for (int fb = 0; fb < NFB; ++fb)
-          if (fb < nfb_valid)
-#pragma unroll
-            for (int ib = 0; ib < 4; ++ib)
-              acc[ib][fb] += *reinterpret_cast<const f32x4*>(
-                  a.part + obase + ((int64_t)(ib * (FS / 16) + wave * NFB + fb) * 64 + lane) * 4);
-#pragma unroll
-        for (int ib = 0; ib < 4; ++ib) den[ib] += a.part_den[(job.split_id * 2 + other) * BR + ib * 16 + li];
+        obase = (job.split_id * 2 + other) * (int64_t)BR * FS;
+        odbase = (job.split_id * 2 + other) * BR;
         if (tid == 0) a.counters[job.split_id] = 0;
+        combine = true;
         finish = true;
       }
     }
 
-    if (finish) {
+    if (finish && has_cols) {
 #pragma unroll
-      for (int ib = 0; ib < 4; ++ib) {
+      for (int ib = 0; ib < NIB; ++ib) {
         const int i = i0 + ib * 16 + li;
-        float dsum = den[ib] + null_w * (float)(i + 1);
+        // the two partials are added first: mine + other is the same float
+        // whichever workgroup finishes last
+        float dsum = den[ib];
+        if (combine) dsum += a.part_den[odbase + ib * 16 + li];
+        dsum += null_w * (float)(i + 1);
         if (MODE == 1) dsum += escale * a.z_old[(mseq + i) * a.H + h];
         const float inv = 1.0f / dsum;
 #pragma unroll
         for (int fb = 0; fb < NFB; ++fb) {
-          if (fb < nfb_valid) {
-            f32x4 num = acc[ib][fb];
-            if (MODE == 1) {
-              const int64_t nblk = ((mseq + i0) / 16 + ib) * (F / 16) + (col0 / 16 + fb);
-              const f32x4 no = *reinterpret_cast<const f32x4*>(a.n_old + (nblk * 64 + lane) * 4);
-              num += escale * no;
-            }
-            store_quad<T>(gbar + (mseq + i) * F + col0 + fb * 16 + lg * 4, cvt_quad<T>(num * inv));
+          f32x4 num = acc[ib][fb];
+          if (combine)
+            num += *reinterpret_cast<const f32x4*>(
+                a.part + obase + ((int64_t)(ib * (FS / 16) + wave * NFB + fb) * 64 + lane) * 4);
+          if (MODE == 1) {
+            const int64_t nblk = ((mseq + i0) / 16 + ib) * (F / 16) + (col0 / 16 + fb);
+            const f32x4 no = *reinterpret_cast<const f32x4*>(a.n_old + (nblk * 64 + lane) * 4);
+            num += escale * no;
           }
+          store_quad<T>(gbar + (mseq + i) * F + col0 + fb * 16 + lg * 4, cvt_quad<T>(num * inv));
         }
       }
     }
-    __syncthreads();   // den_s and Ps are reused by the next job
-  }
+    __syncthreads();   // LDS is reused by the next job
+  };
+  run_job(job0);
+  if (njobs == 2) run_job(job1);
 }
 
 __global__ void zero_i32_kernel(int* p, int64_t n) {
@@ -276,27 +364,37 @@ __global__ void zero_i32_kernel(int* p, int64_t n) {
   if (i < n) p[i] = 0;
 }
 
-template <typename T, int MODE>
-hipError_t launch_agg_t(const AggArgs& a, int nfc, int rtiles, int64_t items, hipStream_t s) {
+template <typename T, int MODE, int WC>
+hipError_t launch_agg_w(const AggArgs& a, int nfc, int rtiles, int64_t items, hipStream_t s) {
   const int64_t q8 = ceil_div(items, 8);
   dim3 grid((unsigned)(8 * q8)), block(kAggThreads);
   switch (a.dh) {
-    case 32: hipLaunchKernelGGL((agg_kernel<T, MODE, 32>), grid, block, 0, s, a, nfc, rtiles, items); break;
-    case 64: hipLaunchKernelGGL((agg_kernel<T, MODE, 64>), grid, block, 0, s, a, nfc, rtiles, items); break;
-    case 128: hipLaunchKernelGGL((agg_kernel<T, MODE, 128>), grid, block, 0, s, a, nfc, rtiles, items); break;
+    case 32: hipLaunchKernelGGL((agg_kernel<T, MODE, 32, WC>), grid, block, 0, s, a, nfc, rtiles, items); break;
+    case 64: hipLaunchKernelGGL((agg_kernel<T, MODE, 64, WC>), grid, block, 0, s, a, nfc, rtiles, items); break;
+    case 128: hipLaunchKernelGGL((agg_kernel<T, MODE, 128, WC>), grid, block, 0, s, a, nfc, rtiles, items); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
+}
+
+template <typename T> bool wide_ok(int Fh) { return Fh % (kWaves * AggCfg<T>::WIDE) == 0; }
+template <typename T> int agg_fs(int Fh) { return kWaves * (wide_ok<T>(Fh) ? AggCfg<T>::WIDE : kNarrow); }
+
+template <typename T, int MODE>
+hipError_t launch_agg_t(const AggArgs& a, int nfc, int rtiles, int64_t items, hipStream_t s) {
+  if (wide_ok<T>(a.F / a.H)) return launch_agg_w<T, MODE, AggCfg<T>::WIDE>(a, nfc, rtiles, items, s);
+  return launch_agg_w<T, MODE, kNarrow>(a, nfc, rtiles, items, s);
 }
 
 }  // namespace
 
 AggPlan tango_agg_plan(int B, int Tp, int F, int H, bool bf) {
   AggPlan p;
-  p.fs = bf ? AggCfg<bf16>::WAVES * AggCfg<bf16>::WCOLS : AggCfg<float>::WAVES * AggCfg<float>::WCOLS;
   const int Fh = F / H;
-  p.nfc = (int)ceil_div(Fh, p.fs);
-  p.rtiles = Tp / BR;
+  p.fs = bf ? agg_fs<bf16>(Fh) : agg_fs<float>(Fh);
+  p.br = bf ? AggCfg<bf16>::BR : AggCfg<float>::BR;
+  p.nfc = (int)ceil_div(Fh, p.fs);   // waves past the head's width skip
+  p.rtiles = Tp / p.br;
   const int half = p.rtiles / 2;
   const int64_t groups = (int64_t)B * H * p.nfc;
   const int64_t pair_items = groups * (half + (p.rtiles & 1));
@@ -304,12 +402,6 @@ AggPlan tango_agg_plan(int B, int Tp, int F, int H, bool bf) {
   p.items = p.split ? groups * (2 * half + (p.rtiles & 1)) : pair_items;
   p.n_split_tiles = p.split ? groups * half : 0;
   return p;
-}
-
-size_t tango_agg_scratch_bytes(const AggPlan& p, int, int) {
-  const int64_t n = p.n_split_tiles;
-  return (size_t)n * 2 * BR * p.fs * sizeof(float) + (size_t)n * 2 * BR * sizeof(float) +
-         (size_t)n * sizeof(int);
 }
 
 hipError_t launch_tango_agg(const AggArgs& a, const AggPlan& p, bool bf, hipStream_t s) {
@@ -324,9 +416,11 @@ hipError_t launch_tango_agg(const AggArgs& a, const AggPlan& p, bool bf, hipStre
 }
 
 hipError_t launch_wango_band(const AggArgs& a, bool bf, hipStream_t s) {
-  const int fs = bf ? AggCfg<bf16>::WAVES * AggCfg<bf16>::WCOLS : AggCfg<float>::WAVES * AggCfg<float>::WCOLS;
-  const int nfc = (int)ceil_div(a.F / a.H, fs);
-  const int rtiles = a.Tp / BR;
+  const int Fh = a.F / a.H;
+  const int fs = bf ? agg_fs<bf16>(Fh) : agg_fs<float>(Fh);
+  const int br = bf ? AggCfg<bf16>::BR : AggCfg<float>::BR;
+  const int nfc = (int)ceil_div(Fh, fs);
+  const int rtiles = a.Tp / br;
   const int64_t items = (int64_t)a.B * a.H * nfc * rtiles;
   return bf ? launch_agg_t<bf16, 1>(a, nfc, rtiles, items, s)
             : launch_agg_t<float, 1>(a, nfc, rtiles, items, s);

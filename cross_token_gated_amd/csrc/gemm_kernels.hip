@@ -89,8 +89,11 @@ __device__ __forceinline__ void gemm_mainloop(f32x4 (&acc)[GemmCfg<T>::BM / 32][
   constexpr int RPP = kThreads / PR;               // rows per pass (32)
   constexpr int PA = C::BM / RPP, PB = C::BN / RPP;
   constexpr int S = op_stride<T>();
-  T* As[2] = {lds, lds + op_tile_elems<T>(C::BM)};
-  T* Bs[2] = {lds + 2 * op_tile_elems<T>(C::BM), lds + 2 * op_tile_elems<T>(C::BM) + op_tile_elems<T>(C::BN)};
+  // tile addresses are computed from the LDS base (not picked from an array
+  // of pointers), so every access stays a ds_read / ds_write
+  constexpr int TA = op_tile_elems<T>(C::BM), TB = op_tile_elems<T>(C::BN);
+  auto As = [&](int buf) { return lds + buf * TA; };
+  auto Bs = [&](int buf) { return lds + 2 * TA + buf * TB; };
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wr = wave >> 1, wc = wave & 1;
   const int prow = tid / PR, pcol = tid % PR;
@@ -104,10 +107,10 @@ __device__ __forceinline__ void gemm_mainloop(f32x4 (&acc)[GemmCfg<T>::BM / 32][
   auto stash = [&](int buf) {
 #pragma unroll
     for (int p = 0; p < PA; ++p)
-      *reinterpret_cast<u32x4*>(As[buf] + (prow + p * RPP) * S + pcol * piece_elems<T>()) = ra[p];
+      *reinterpret_cast<u32x4*>(As(buf) + (prow + p * RPP) * S + pcol * piece_elems<T>()) = ra[p];
 #pragma unroll
     for (int p = 0; p < PB; ++p)
-      *reinterpret_cast<u32x4*>(Bs[buf] + (prow + p * RPP) * S + pcol * piece_elems<T>()) = rb[p];
+      *reinterpret_cast<u32x4*>(Bs(buf) + (prow + p * RPP) * S + pcol * piece_elems<T>()) = rb[p];
   };
   fetch(0);
   stash(0);
@@ -115,7 +118,7 @@ __device__ __forceinline__ void gemm_mainloop(f32x4 (&acc)[GemmCfg<T>::BM / 32][
   for (int kt = 0; kt < nk; ++kt) {
     const int buf = kt & 1;
     if (kt + 1 < nk) fetch(kt + 1);
-    tile_mma<T>(acc, As[buf], Bs[buf], wr, wc, lane);
+    tile_mma<T>(acc, As(buf), Bs(buf), wr, wc, lane);
     if (kt + 1 < nk) stash(buf ^ 1);
     __syncthreads();
   }

@@ -69,6 +69,7 @@ struct ScanArgs {
 // Plan of the TANGO aggregation grid for a shape.
 struct AggPlan {
   int fs;          // gate columns per workgroup
+  int br;          // destination rows per tile
   int nfc;         // column chunks per head
   int rtiles;      // 64-row tiles per sequence
   int split;       // 1 = split mode
@@ -77,7 +78,6 @@ struct AggPlan {
 };
 
 AggPlan tango_agg_plan(int B, int Tp, int F, int H, bool bf);
-size_t tango_agg_scratch_bytes(const AggPlan& p, int F, int H);
 
 struct ScanPlan {
   int nseg, chunks_per_seg, fs;

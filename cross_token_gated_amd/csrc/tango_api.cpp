@@ -160,8 +160,8 @@ Layout make_layout(const tango_shape_t* s, bool wango, int32_t window, int32_t c
   if (!wango) {
     L.agg = tango_agg_plan(s->batch, (int)pad_rows(s->seq_len), s->d_gate, s->n_heads, bf);
     const int64_t n = L.agg.n_split_tiles;
-    L.part = take((size_t)n * 2 * 64 * L.agg.fs * sizeof(float));
-    L.part_den = take((size_t)n * 2 * 64 * sizeof(float));
+    L.part = take((size_t)n * 2 * L.agg.br * L.agg.fs * sizeof(float));
+    L.part_den = take((size_t)n * 2 * L.agg.br * sizeof(float));
     L.counters = take((size_t)n * sizeof(int));
   } else {
     L.scan = wango_scan_plan(s->batch, (int)pad_rows(s->seq_len), s->d_gate, s->n_heads, chunk, window, bf);

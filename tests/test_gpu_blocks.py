@@ -89,3 +89,26 @@ def test_deterministic_inplace_and_streams(mode):
     d = fwd(xin, bw, out=xin)
     torch.cuda.synchronize()
     assert torch.equal(a, b) and torch.equal(a, c) and torch.equal(a, d)
+
+
+def test_long_wango_sampled_rows():
+    """WANGO, B=2, T=65536, window 512, 8 shared applications: sampled output
+    rows against float64 oracle values stored by
+    tests/golden/make_wango_t65536_golden.py (the full oracle takes minutes)."""
+    import os
+    path = os.path.join(os.path.dirname(__file__), "golden", "wango_t65536_samples.npz")
+    gold = np.load(path, allow_pickle=False)
+    w = wl.WORKLOADS[str(gold["workload"])]
+    inp = wl.make_inputs(w)
+    announce(f"workload {w.name} (sampled rows)")
+    out = run_workload(w, inp)
+    torch.cuda.synchronize()
+    rows = torch.from_numpy(gold["rows"]).to(out.device)
+    got = out.index_select(1, rows).double().cpu().numpy()
+    e = float(np.max(np.abs(got - gold["expected"]))) / float(gold["rms"])
+    h0 = np.asarray(inp.h, np.float64)[:, gold["rows"], :]
+    d = H.rms_ratio(got - h0, gold["expected"] - h0)
+    print(f"{w.name}: max|err|/rms over {gold['rows'].size} rows x {w.B} = {e:.3e}; "
+          f"rms error of the total update {d:.3e}")
+    assert np.isfinite(got).all()
+    assert e < H.tol(w.dtype)

@@ -58,6 +58,9 @@ def tango_flops(w) -> float:
 
 
 def scan_bytes(w) -> float:
+    """Algorithmic HBM bytes of the running-sum scan: query and key features
+    read once (2 x H*d_h, bf16), gates read once (F, bf16), n_old written once
+    (F, float32), z_old written once (H, float32), per token."""
     hd = w.n_heads * w.head_dim
     return float(w.B * w.T * (2 * hd * 2 + w.d_gate * 2 + w.d_gate * 4 + w.n_heads * 4))
 
@@ -186,11 +189,13 @@ def main():
     vg = torch.empty(Mg, wg.d_gate, dtype=torch.bfloat16, device=dev)
     qg = torch.empty(Mg, HDg, dtype=torch.bfloat16, device=dev)
     kg = torch.empty(Mg, HDg, dtype=torch.bfloat16, device=dev)
-    api.tango_stage_proj(sg, bg, xg, gpg, vg, qg, kg, stream=stream)
+    fqg = torch.empty(Mg, HDg, dtype=torch.bfloat16, device=dev)
+    fkg = torch.empty(Mg * HDg, dtype=torch.bfloat16, device=dev)
+    api.wango_stage_proj(sg, bg, xg, gpg, vg, qg, kg, fqg, fkg, stream=stream)
     n_old = torch.empty(Mg * wg.d_gate, dtype=torch.float32, device=dev)
     z_old = torch.empty(Mg, wg.n_heads, dtype=torch.float32, device=dev)
-    ms_scan = timed(lambda: api.wango_stage_scan(sg, bg.theta, wg.window, wg.chunk, qg, kg, gpg, n_old,
-                                                 z_old, ws_g, stream=stream), loops)
+    ms_scan = timed(lambda: api.wango_stage_scan(sg, wg.window, wg.chunk, fqg, fkg, gpg, n_old, z_old,
+                                                 ws_g, stream=stream), loops)
 
     agg_flops = tango_flops(wt)
     achieved = agg_flops / (ms_agg * 1e-3)

@@ -129,6 +129,12 @@ def tango_stage_proj(shape: Shape, w: BlockWeights, x, gp, v, qh, kh, stream=Non
                                   _ptr(v), _ptr(qh), _ptr(kh), _stream(stream)))
 
 
+def wango_stage_proj(shape: Shape, w: BlockWeights, x, gp, v, qh, kh, fq, fk, stream=None) -> None:
+    cw = w.c_struct()
+    check(load().wango_stage_proj(ctypes.byref(shape), ctypes.byref(cw), _ptr(x), _ptr(gp),
+                                  _ptr(v), _ptr(qh), _ptr(kh), _ptr(fq), _ptr(fk), _stream(stream)))
+
+
 def tango_stage_aggregate(shape: Shape, theta, null_bias, qh, kh, gp, gbar, ws, stream=None) -> None:
     check(load().tango_stage_aggregate(ctypes.byref(shape), _ptr(theta), _ptr(null_bias), _ptr(qh),
                                        _ptr(kh), _ptr(gp), _ptr(gbar), _ptr(ws), ws.numel(),
@@ -140,15 +146,14 @@ def tango_stage_out(shape: Shape, w_o, x, gbar, v, out, stream=None) -> None:
                                  _ptr(out), _stream(stream)))
 
 
-def wango_stage_scan(shape: Shape, theta, window: int, chunk: int, qh, kh, gp, n_old, z_old, ws,
+def wango_stage_scan(shape: Shape, window: int, chunk: int, fq, fk, gp, n_old, z_old, ws,
                      stream=None) -> None:
-    check(load().wango_stage_scan(ctypes.byref(shape), _ptr(theta), window, chunk, _ptr(qh),
-                                  _ptr(kh), _ptr(gp), _ptr(n_old), _ptr(z_old), _ptr(ws),
-                                  ws.numel(), _stream(stream)))
+    check(load().wango_stage_scan(ctypes.byref(shape), window, chunk, _ptr(fq), _ptr(fk), _ptr(gp),
+                                  _ptr(n_old), _ptr(z_old), _ptr(ws), ws.numel(), _stream(stream)))
 
 
-def wango_stage_band(shape: Shape, theta, null_bias, window: int, qh, kh, gp, n_old, z_old, gbar,
-                     stream=None) -> None:
-    check(load().wango_stage_band(ctypes.byref(shape), _ptr(theta), _ptr(null_bias), window,
+def wango_stage_band(shape: Shape, theta, null_bias, window: int, chunk: int, qh, kh, gp, n_old,
+                     z_old, gbar, stream=None) -> None:
+    check(load().wango_stage_band(ctypes.byref(shape), _ptr(theta), _ptr(null_bias), window, chunk,
                                   _ptr(qh), _ptr(kh), _ptr(gp), _ptr(n_old), _ptr(z_old),
                                   _ptr(gbar), _stream(stream)))

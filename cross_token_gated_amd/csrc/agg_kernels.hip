@@ -139,8 +139,11 @@ __global__ __launch_bounds__(kAggThreads) void agg_kernel(AggArgs a, int nfc, in
   } else {
     grp = item / R;
     const int r = (int)(item % R);
-    const int lo = r * BR - a.window + 1;
-    job0 = {r, lo > 0 ? lo / BC : 0, (r + 1) * SPT - 1, kFull, 0};
+    // first source: the start of the chunk holding row i0 - W (the older
+    // sources of that chunk are read pairwise here), or 0
+    const int i0 = r * BR;
+    const int lo = i0 >= a.window ? (i0 - a.window) / a.chunk * a.chunk : 0;
+    job0 = {r, lo / BC, (r + 1) * SPT - 1, kFull, 0};
   }
   const int fc = (int)(grp % nfc);
   const int64_t bh = grp / nfc;
@@ -155,6 +158,7 @@ __global__ __launch_bounds__(kAggThreads) void agg_kernel(AggArgs a, int nfc, in
 
   const float tau = __expf(fminf(a.theta[h], 2.995732273553991f));   // log 20
   const float ktau = tau * kLog2e;
+  const float stau = sqrtf(tau), isd = 1.0f / sqrtf((float)DH);      // WANGO features
   const float escale = __expf(-tau);                   // e^{-tau}: the fixed shift
   const float null_w = a.null_bias ? __expf(a.null_bias[h] - tau) : 0.f;
 
@@ -198,6 +202,16 @@ __global__ __launch_bounds__(kAggThreads) void agg_kernel(AggArgs a, int nfc, in
     for (int ks = 0; ks < KS; ++ks)
       qf[ks] = load_frag<T>(qh + (mseq + i0 + wib * 16 + li) * HD + h * DH + ks * 32 + lg * 8);
 
+    // WANGO: phi(sqrt(tau) q) of the same fragment, for the older sources of
+    // the chunk next to the window
+    Frag<T> fqf[KS];
+    if (MODE == 1) {
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) fqf[ks][e] = cvt<T>(phi_feature(stau * tof<T>(qf[ks][e]), isd));
+    }
+
     f32x4 acc[NIB][NFB];
 #pragma unroll
     for (int ib = 0; ib < NIB; ++ib)
@@ -205,25 +219,40 @@ __global__ __launch_bounds__(kAggThreads) void agg_kernel(AggArgs a, int nfc, in
       for (int fb = 0; fb < NFB; ++fb) acc[ib][fb] = f32x4{0.f, 0.f, 0.f, 0.f};
     float rowsum = 0.f;
     const int i_me = i0 + wib * 16 + li;     // this lane's destination in S^T
+    // older sources of destination i read pairwise here: C floor((i-W)/C) <= j <= i-W
+    const int jphi_lo = (MODE == 1 && i_me >= a.window) ? (i_me - a.window) / a.chunk * a.chunk : 0;
 
     // weights of source step jb (key block in ks[buf]) into ps[buf]
     auto weights = [&](int jb, int buf) {
       const int j0 = jb * BC;
+      // WANGO: does this step hold older sources of some row of the tile?
+      const bool phi_step = MODE == 1 && i0 + BR - 1 >= a.window && j0 <= i0 + BR - 1 - a.window;
 #pragma unroll
       for (int jj = wjb; jj < wjb + JBW; ++jj) {
-        f32x4 s = {0.f, 0.f, 0.f, 0.f};
+        f32x4 s = {0.f, 0.f, 0.f, 0.f}, sphi = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int ks = 0; ks < KS; ++ks)
-          mma(s, load_frag<T>(&sm.ks[buf][(jj * 16 + li) * KSTR + ks * 32 + lg * 8]), qf[ks]);
+        for (int ks = 0; ks < KS; ++ks) {
+          const Frag<T> kf = load_frag<T>(&sm.ks[buf][(jj * 16 + li) * KSTR + ks * 32 + lg * 8]);
+          mma(s, kf, qf[ks]);
+          if (phi_step) {
+            Frag<T> fkf;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) fkf[e] = cvt<T>(phi_feature(stau * tof<T>(kf[e]), isd));
+            mma(sphi, fkf, fqf[ks]);
+          }
+        }
         Quad<T> pq;
         float psum = 0.f;
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
           const int j = j0 + jj * 16 + lg * 4 + r;
-          bool ok = j <= i_me;
-          if (MODE == 1) ok = ok && (j > i_me - a.window);
-          // the argument lies in [-2 tau log2 e, 0] >= -58: v_exp_f32 needs no range fix-up
-          const float p = ok ? __builtin_amdgcn_exp2f(ktau * (s[r] - 1.0f)) : 0.f;
+          float p = 0.f;
+          if (j <= i_me && (MODE == 0 || j > i_me - a.window)) {
+            // the argument lies in [-2 tau log2 e, 0] >= -58: v_exp_f32 needs no range fix-up
+            p = __builtin_amdgcn_exp2f(ktau * (s[r] - 1.0f));
+          } else if (phi_step && i_me >= a.window && j <= i_me - a.window && j >= jphi_lo) {
+            p = escale * sphi[r];   // same e^{-tau} scale as the exp weights
+          }
           pq[r] = cvt<T>(p);
           psum += tof<T>(pq[r]);
         }

@@ -99,6 +99,19 @@ __host__ __device__ __forceinline__ int perm_slot(int g, int s) {
   return s < 4 ? 4 * g + s : 16 + 4 * g + (s - 4);
 }
 
+// Position of feature e (0..31 within a group of 32) in the permuted feature
+// order: slot s of lane group g holds feature perm_slot(g, s), stored at 8g + s.
+__host__ __device__ __forceinline__ int feature_slot(int e32) {
+  return e32 < 16 ? (e32 >> 2) * 8 + (e32 & 3) : ((e32 - 16) >> 2) * 8 + 4 + (e32 & 3);
+}
+
+// WANGO positive feature map phi(u) = max(ELU(u) + 1 + 1e-4, 1e-4) / sqrt(d_h)
+// ([TANGO] §2.2 eq. 8), ELU with alpha = 1; inv_sqrt_dh = 1 / sqrt(d_h).
+__device__ __forceinline__ float phi_feature(float u, float inv_sqrt_dh) {
+  const float elu1 = u > 0.f ? u + 1.0f : __expf(u);   // ELU(u) + 1
+  return fmaxf(elu1 + 1e-4f, 1e-4f) * inv_sqrt_dh;
+}
+
 // Offset (in elements) of g[row m, column f] in the packed gate layout
 // [M/32][4][F][8], M = all (batch, padded position) rows.
 __host__ __device__ __forceinline__ int64_t packed_offset(int64_t blk, int grp, int64_t f,

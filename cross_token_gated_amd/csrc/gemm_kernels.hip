@@ -321,10 +321,46 @@ __global__ __launch_bounds__(kThreads) void proj_kernel(ProjArgs args) {
       const float inv = 1.0f / fmaxf(sqrtf(ss), 1e-12f);
       if (ok) {
         const int n = n0 + hcol;
-        T* dst = n < 2 * F + HD ? static_cast<T*>(args.qh) + (m0 + row) * HD + (n - 2 * F)
-                                : static_cast<T*>(args.kh) + (m0 + row) * HD + (n - 2 * F - HD);
-        dst[2 * c] = cvt<T>(u0 * inv);
-        dst[2 * c + 1] = cvt<T>(u1 * inv);
+        const bool is_q = n < 2 * F + HD;
+        const int e = is_q ? n - 2 * F : n - 2 * F - HD;   // column within q or k
+        T* dst = (is_q ? static_cast<T*>(args.qh) : static_cast<T*>(args.kh)) + (m0 + row) * HD + e;
+        const T w0 = cvt<T>(u0 * inv), w1 = cvt<T>(u1 * inv);
+        dst[2 * c] = w0;
+        dst[2 * c + 1] = w1;
+        if (args.fq) {
+          // WANGO features phi(sqrt(tau) u) ([TANGO] §2.2 eq. 8) of the stored
+          // unit vector: queries go out directly in the permuted feature order,
+          // keys back into the tile for the packed store below
+          const float st = sqrtf(__expf(fminf(args.theta[e / dh], 2.995732273553991f)));
+          const float isd = 1.0f / sqrtf((float)dh);
+          const float p0 = phi_feature(st * tof<T>(w0), isd), p1 = phi_feature(st * tof<T>(w1), isd);
+          if (is_q) {
+            T* fq = static_cast<T*>(args.fq) + (m0 + row) * HD + (e + 2 * c) / 32 * 32 +
+                    feature_slot((e + 2 * c) % 32);
+            fq[0] = cvt<T>(p0);
+            fq[1] = cvt<T>(p1);
+          } else {
+            Cs[row * kCStride + hcol + 2 * c] = p0;
+            Cs[row * kCStride + hcol + 2 * c + 1] = p1;
+          }
+        }
+      }
+    }
+    if (args.fk) {
+      // key features in the source-packed layout, as the gates
+      __syncthreads();
+      const int k_lo = max(c_lo, 2 * F + HD - n0);
+      if (k_lo < c_hi) {
+        T* fk = static_cast<T*>(args.fk);
+        constexpr int NRB = C::BM / 32;
+        const int ncols = c_hi - k_lo;
+        for (int it = tid; it < NRB * 4 * ncols; it += kThreads) {
+          const int c2 = k_lo + it % ncols, grp = (it / ncols) & 3, rb = it / (4 * ncols);
+          Frag<T> out;
+#pragma unroll
+          for (int s2 = 0; s2 < 8; ++s2) out[s2] = cvt<T>(Cs[(rb * 32 + perm_slot(grp, s2)) * kCStride + c2]);
+          store_frag<T>(fk + packed_offset(m0 / 32 + rb, grp, n0 + c2 - 2 * F - HD, HD), out);
+        }
       }
     }
   }

@@ -22,6 +22,9 @@ struct ProjArgs {
   void* v;             // [B*Tp, F]
   void* qh;            // [B*Tp, HD]
   void* kh;            // [B*Tp, HD]
+  void* fq;            // WANGO only (else null): phi(sqrt(tau) q) [B*Tp, HD], permuted feature order
+  void* fk;            // WANGO only (else null): phi(sqrt(tau) k), source-packed [B*Tp/32][4][HD][8]
+  const float* theta;  // [H], for the WANGO features
   int B, T, Tp, d, F, HD, dh;
   float rope_base, eps;
 };
@@ -49,15 +52,15 @@ struct AggArgs {
   float* part_den;         // TANGO split mode: partial denominators
   int* counters;           // TANGO split mode: one per split tile
   int B, T, Tp, F, H, dh, window;
+  int chunk;               // WANGO: n_old holds the state read-out at chunk boundaries
   int split;               // 1: split the long tiles in two (last finisher combines)
 };
 
 // WANGO older-prefix scan.
 struct ScanArgs {
-  const void* qh;
-  const void* kh;
+  const void* fq;          // phi(sqrt(tau) q), permuted feature order [B*Tp, HD]
+  const void* fk;          // phi(sqrt(tau) k), source-packed [B*Tp/32][4][HD][8]
   const void* gp;
-  const float* theta;
   float* n_old;            // blocked [B*Tp/16][F/16][64][4]
   float* z_old;            // [B*Tp, H]
   float* seg_state;        // [B][H][nseg][dh][F/H] segment sums, then exclusive prefixes
@@ -82,7 +85,7 @@ AggPlan tango_agg_plan(int B, int Tp, int F, int H, bool bf);
 struct ScanPlan {
   int nseg, chunks_per_seg, fs;
 };
-ScanPlan wango_scan_plan(int B, int Tp, int F, int H, int chunk, int window, bool bf);
+ScanPlan wango_scan_plan(int B, int Tp, int F, int H, int chunk);
 
 // bf: bf16 weights/activations (else float32); io_bf: bf16 x/out (else float32)
 hipError_t launch_proj(const ProjArgs& a, bool bf, bool io_bf, hipStream_t s);
@@ -95,6 +98,5 @@ hipError_t launch_zero_i32(int* p, int64_t n, hipStream_t s);
 // Raise the dynamic-LDS limit of the kernels that need more than 64 KB
 // (once per device).
 hipError_t gemm_kernels_init();
-hipError_t scan_kernels_init();
 
 }  // namespace tango

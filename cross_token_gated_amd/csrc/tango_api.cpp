@@ -133,6 +133,7 @@ int check_ranges(const Range* ins, int nin, const Range* outs, int nout, const v
 
 struct Layout {
   size_t gp, v, qh, kh, gbar;           // offsets
+  size_t fq, fk;                        // WANGO features
   size_t part, part_den, counters;      // TANGO split scratch
   size_t n_old, z_old, seg_state, seg_z;
   size_t total;
@@ -164,7 +165,10 @@ Layout make_layout(const tango_shape_t* s, bool wango, int32_t window, int32_t c
     L.part_den = take((size_t)n * 2 * L.agg.br * sizeof(float));
     L.counters = take((size_t)n * sizeof(int));
   } else {
-    L.scan = wango_scan_plan(s->batch, (int)pad_rows(s->seq_len), s->d_gate, s->n_heads, chunk, window, bf);
+    (void)window;
+    L.scan = wango_scan_plan(s->batch, (int)pad_rows(s->seq_len), s->d_gate, s->n_heads, chunk);
+    L.fq = take(M * HD * es);
+    L.fk = take(M * HD * es);
     L.n_old = take(M * F * sizeof(float));
     L.z_old = take(M * s->n_heads * sizeof(float));
     const int64_t bh = (int64_t)s->batch * s->n_heads;
@@ -188,7 +192,6 @@ int ensure_init() {
   std::lock_guard<std::mutex> lk(g_init_mu);
   if (g_init_done[dev]) return TANGO_OK;
   if ((e = gemm_kernels_init()) != hipSuccess) return hip_fail(e, "kernel attributes");
-  if ((e = scan_kernels_init()) != hipSuccess) return hip_fail(e, "kernel attributes");
   g_init_done[dev] = true;
   return TANGO_OK;
 }
@@ -204,6 +207,7 @@ ProjArgs proj_args(const tango_shape_t* s, const tango_weights_t* w, const void*
   a.w_q = w->w_q;
   a.w_k = w->w_k;
   a.gain = w->rms_gain;
+  a.theta = w->theta;
   a.gp = gp;
   a.v = v;
   a.qh = qh;
@@ -254,14 +258,13 @@ AggArgs agg_args(const tango_shape_t* s, const float* theta, const float* null_b
   return a;
 }
 
-ScanArgs scan_args(const tango_shape_t* s, const float* theta, int32_t window, int32_t chunk,
-                   const void* qh, const void* kh, const void* gp, float* n_old, float* z_old,
-                   float* seg_state, float* seg_z) {
+ScanArgs scan_args(const tango_shape_t* s, int32_t window, int32_t chunk, const void* fq,
+                   const void* fk, const void* gp, float* n_old, float* z_old, float* seg_state,
+                   float* seg_z) {
   ScanArgs a{};
-  a.qh = qh;
-  a.kh = kh;
+  a.fq = fq;
+  a.fk = fk;
   a.gp = gp;
-  a.theta = theta;
   a.n_old = n_old;
   a.z_old = z_old;
   a.seg_state = seg_state;
@@ -332,7 +335,12 @@ int block_common(const tango_shape_t* s, const tango_weights_t* w, bool wango, i
   void* kh = base + L.kh;
   void* gbar = base + L.gbar;
   const bool io_bf = s->io_dtype == TANGO_BF16;
-  hipError_t e = launch_proj(proj_args(s, w, x, gp, v, qh, kh), bf, io_bf, st);
+  ProjArgs pa = proj_args(s, w, x, gp, v, qh, kh);
+  if (wango) {
+    pa.fq = base + L.fq;
+    pa.fk = base + L.fk;
+  }
+  hipError_t e = launch_proj(pa, bf, io_bf, st);
   if (e != hipSuccess) return hip_fail(e, "projection kernel");
   AggArgs aa = agg_args(s, w->theta, w->null_bias, qh, kh, gp, gbar);
   if (!wango) {
@@ -344,7 +352,7 @@ int block_common(const tango_shape_t* s, const tango_weights_t* w, bool wango, i
   } else {
     float* n_old = reinterpret_cast<float*>(base + L.n_old);
     float* z_old = reinterpret_cast<float*>(base + L.z_old);
-    ScanArgs sa = scan_args(s, w->theta, window, chunk, qh, kh, gp, n_old, z_old,
+    ScanArgs sa = scan_args(s, window, chunk, base + L.fq, base + L.fk, gp, n_old, z_old,
                             reinterpret_cast<float*>(base + L.seg_state),
                             reinterpret_cast<float*>(base + L.seg_z));
     e = launch_wango_scan(sa, L.scan, bf, st);
@@ -352,6 +360,7 @@ int block_common(const tango_shape_t* s, const tango_weights_t* w, bool wango, i
     aa.n_old = n_old;
     aa.z_old = z_old;
     aa.window = window;
+    aa.chunk = chunk;
     e = launch_wango_band(aa, bf, st);
     if (e != hipSuccess) return hip_fail(e, "band kernel");
   }
@@ -487,14 +496,44 @@ int tango_stage_out(const tango_shape_t* shape, const void* w_o, const void* x, 
   });
 }
 
-int wango_stage_scan(const tango_shape_t* shape, const float* theta, int32_t window, int32_t chunk,
-                     const void* qh, const void* kh, const void* gp, void* n_old, void* z_old,
-                     void* workspace, size_t workspace_bytes, void* hip_stream) {
+int wango_stage_proj(const tango_shape_t* shape, const tango_weights_t* weights, const void* x, void* gp,
+                     void* v, void* qh, void* kh, void* fq, void* fk, void* hip_stream) {
+  return guarded([&] {
+    int rc = check_shape(shape);
+    if (rc) return rc;
+    if ((rc = check_weights(weights, true))) return rc;
+    if (!x || !gp || !v || !qh || !kh || !fq || !fk) return fail(TANGO_ERR_NULL, "a buffer pointer is NULL");
+    const tango_shape_t* s = shape;
+    const size_t es = elem_size(s->dtype), M = (size_t)s->batch * pad_rows(s->seq_len);
+    const size_t d = s->d_model, F = s->d_gate, HD = (size_t)s->n_heads * s->head_dim;
+    const Range ins[] = {{x, (size_t)s->batch * s->seq_len * d * elem_size(s->io_dtype), "x"},
+                         {weights->w_g, F * d * es, "w_g"},
+                         {weights->w_v, F * d * es, "w_v"},
+                         {weights->w_q, HD * d * es, "w_q"},
+                         {weights->w_k, HD * d * es, "w_k"},
+                         {weights->rms_gain, d * es, "rms_gain"},
+                         {weights->theta, s->n_heads * sizeof(float), "theta"}};
+    const Range outs[] = {{gp, M * F * es, "gp"}, {v, M * F * es, "v"}, {qh, M * HD * es, "qh"},
+                          {kh, M * HD * es, "kh"}, {fq, M * HD * es, "fq"}, {fk, M * HD * es, "fk"}};
+    if ((rc = check_ranges(ins, 7, outs, 6, nullptr, nullptr))) return rc;
+    if ((rc = ensure_init())) return rc;
+    ProjArgs pa = proj_args(s, weights, x, gp, v, qh, kh);
+    pa.fq = fq;
+    pa.fk = fk;
+    hipError_t e = launch_proj(pa, s->dtype == TANGO_BF16, s->io_dtype == TANGO_BF16,
+                               static_cast<hipStream_t>(hip_stream));
+    return e == hipSuccess ? ok() : hip_fail(e, "projection kernel");
+  });
+}
+
+int wango_stage_scan(const tango_shape_t* shape, int32_t window, int32_t chunk, const void* fq,
+                     const void* fk, const void* gp, void* n_old, void* z_old, void* workspace,
+                     size_t workspace_bytes, void* hip_stream) {
   return guarded([&] {
     int rc = check_shape(shape);
     if (rc) return rc;
     if ((rc = check_wango(shape, window, shape->head_dim, chunk))) return rc;
-    if (!theta || !qh || !kh || !gp || !n_old || !z_old || !workspace)
+    if (!fq || !fk || !gp || !n_old || !z_old || !workspace)
       return fail(TANGO_ERR_NULL, "a buffer pointer is NULL");
     const tango_shape_t* s = shape;
     const Layout L = make_layout(s, true, window, chunk);
@@ -503,15 +542,14 @@ int wango_stage_scan(const tango_shape_t* shape, const float* theta, int32_t win
                   workspace_bytes, L.total);
     const size_t es = elem_size(s->dtype), M = (size_t)s->batch * pad_rows(s->seq_len);
     const size_t F = s->d_gate, HD = (size_t)s->n_heads * s->head_dim;
-    const Range ins[] = {{qh, M * HD * es, "qh"}, {kh, M * HD * es, "kh"}, {gp, M * F * es, "gp"},
-                         {theta, s->n_heads * sizeof(float), "theta"}};
+    const Range ins[] = {{fq, M * HD * es, "fq"}, {fk, M * HD * es, "fk"}, {gp, M * F * es, "gp"}};
     const Range outs[] = {{n_old, M * F * sizeof(float), "n_old"},
                           {z_old, M * s->n_heads * sizeof(float), "z_old"},
                           {workspace, L.total, "workspace"}};
-    if ((rc = check_ranges(ins, 4, outs, 3, nullptr, nullptr))) return rc;
+    if ((rc = check_ranges(ins, 3, outs, 3, nullptr, nullptr))) return rc;
     if ((rc = ensure_init())) return rc;
     char* base = static_cast<char*>(workspace);
-    ScanArgs sa = scan_args(s, theta, window, chunk, qh, kh, gp, static_cast<float*>(n_old),
+    ScanArgs sa = scan_args(s, window, chunk, fq, fk, gp, static_cast<float*>(n_old),
                             static_cast<float*>(z_old), reinterpret_cast<float*>(base + L.seg_state),
                             reinterpret_cast<float*>(base + L.seg_z));
     hipError_t e = launch_wango_scan(sa, L.scan, s->dtype == TANGO_BF16, static_cast<hipStream_t>(hip_stream));
@@ -520,12 +558,12 @@ int wango_stage_scan(const tango_shape_t* shape, const float* theta, int32_t win
 }
 
 int wango_stage_band(const tango_shape_t* shape, const float* theta, const float* null_bias, int32_t window,
-                     const void* qh, const void* kh, const void* gp, const float* n_old, const float* z_old,
-                     void* gbar, void* hip_stream) {
+                     int32_t chunk, const void* qh, const void* kh, const void* gp, const float* n_old,
+                     const float* z_old, void* gbar, void* hip_stream) {
   return guarded([&] {
     int rc = check_shape(shape);
     if (rc) return rc;
-    if (window < 1) return fail(TANGO_ERR_SHAPE, "window %d < 1", window);
+    if ((rc = check_wango(shape, window, shape->head_dim, chunk))) return rc;
     if (!theta || !qh || !kh || !gp || !n_old || !z_old || !gbar)
       return fail(TANGO_ERR_NULL, "a buffer pointer is NULL");
     const tango_shape_t* s = shape;
@@ -543,6 +581,7 @@ int wango_stage_band(const tango_shape_t* shape, const float* theta, const float
     aa.n_old = n_old;
     aa.z_old = z_old;
     aa.window = window;
+    aa.chunk = chunk;
     hipError_t e = launch_wango_band(aa, s->dtype == TANGO_BF16, static_cast<hipStream_t>(hip_stream));
     return e == hipSuccess ? ok() : hip_fail(e, "band kernel");
   });

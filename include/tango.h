@@ -143,7 +143,8 @@ int tango_version(void);                      /* TANGO_ABI_VERSION              
 
 /* ---- Stage entry points (for stage-by-stage parity tests) ---------------
  *
- * They run one kernel of the block on caller buffers.  Intermediate layouts:
+ * They run one kernel (or the kernels of one step) of the block on caller
+ * buffers.  Intermediate layouts:
  *   Tp        = seq_len rounded up to a multiple of 128 (rows >= T are padding
  *               that the projection stage writes as zeros);
  *   V, gbar   = [B, Tp, F] row-major, dtype;
@@ -151,15 +152,31 @@ int tango_version(void);                      /* TANGO_ABI_VERSION              
  *   gp        = the gates g in the source-packed layout [B][Tp/32][4][F][8]:
  *               element (b, blk, grp, f, s) holds g[b, t, f] for
  *               t = 32*blk + (s < 4 ? 4*grp + s : 16 + 4*grp + (s - 4));
- *   n_old     = [B, Tp, F] float32, z_old = [B, Tp, H] float32: the WANGO
- *               older-prefix numerator phi(sqrt(tau) q)^T S and denominator
- *               phi(sqrt(tau) q)^T z of eq. 10 (zero for i < window).
+ *   fk        = phi(sqrt(tau) k) (the WANGO key features of [TANGO] eq. 8) in
+ *               the same source-packed layout over the H*d_h feature columns;
+ *   fq        = phi(sqrt(tau) q), [B, Tp, H*d_h], with the features of every
+ *               group of 32 stored in the order e = 4*grp + s (s < 4) or
+ *               16 + 4*grp + (s - 4), at position 8*grp + s of the group;
+ *   n_old     = float32 in 16 x 16 blocks [B*Tp/16][F/16][64][4]: entry
+ *               (blk_i, blk_f, l, r) holds row 16*blk_i + l % 16 and column
+ *               16*blk_f + 4*(l / 16) + r;
+ *   z_old     = [B, Tp, H] float32.
+ * The WANGO scan leaves in n_old, z_old the read-out phi(sqrt(tau) q_i)^T S and
+ * phi(sqrt(tau) q_i)^T z of the running sums of eq. 10 over the sources before
+ * c_i = chunk * floor((i - window) / chunk) (zero for i < window); the band
+ * stage adds the older sources c_i <= j <= i - window pairwise.
  */
 
-/* Projections ([TANGO] §2.1 eq. 2 and the head paragraph): RMSNorm, SiLU gate
- * (packed), features, RoPE + unit-norm queries and keys. */
+/* TANGO projections ([TANGO] §2.1 eq. 2 and the head paragraph): RMSNorm,
+ * SiLU gate (packed), features, RoPE + unit-norm queries and keys. */
 int tango_stage_proj(const tango_shape_t* shape, const tango_weights_t* weights,
                      const void* x, void* gp, void* v, void* qh, void* kh, void* hip_stream);
+
+/* WANGO projections: as tango_stage_proj, plus the features fq, fk of eq. 8
+ * (needs weights->theta). */
+int wango_stage_proj(const tango_shape_t* shape, const tango_weights_t* weights,
+                     const void* x, void* gp, void* v, void* qh, void* kh, void* fq, void* fk,
+                     void* hip_stream);
 
 /* TANGO aggregation ([TANGO] eqs. 4-6): gbar from qh, kh, gp.  Needs the same
  * workspace as tango_block_fwd (it uses the split-sum scratch area). */
@@ -172,18 +189,18 @@ int tango_stage_aggregate(const tango_shape_t* shape, const float* theta,
 int tango_stage_out(const tango_shape_t* shape, const void* w_o, const void* x,
                     const void* gbar, const void* v, void* out, void* hip_stream);
 
-/* WANGO older-prefix running sums ([TANGO] eqs. 8-10): n_old, z_old.  Needs
- * the workspace of wango_block_fwd (segment-state scratch). */
-int wango_stage_scan(const tango_shape_t* shape, const float* theta, int32_t window,
-                     int32_t chunk, const void* qh, const void* kh, const void* gp,
-                     void* n_old, void* z_old, void* workspace, size_t workspace_bytes,
-                     void* hip_stream);
+/* WANGO running sums ([TANGO] eqs. 8-10): n_old, z_old as described above.
+ * Needs the workspace of wango_block_fwd (segment-state scratch). */
+int wango_stage_scan(const tango_shape_t* shape, int32_t window, int32_t chunk,
+                     const void* fq, const void* fk, const void* gp, void* n_old, void* z_old,
+                     void* workspace, size_t workspace_bytes, void* hip_stream);
 
 /* WANGO window band and joint normalisation ([TANGO] eqs. 5, 7 and the
- * joint-normalisation paragraph of §2.2): gbar from the window exp weights plus
- * n_old, z_old and the null term. */
+ * joint-normalisation paragraph of §2.2): gbar from the window exp weights,
+ * the pairwise phi weights of the older sources in the chunk next to the
+ * window, n_old, z_old and the null term. */
 int wango_stage_band(const tango_shape_t* shape, const float* theta, const float* null_bias,
-                     int32_t window, const void* qh, const void* kh, const void* gp,
+                     int32_t window, int32_t chunk, const void* qh, const void* kh, const void* gp,
                      const float* n_old, const float* z_old, void* gbar, void* hip_stream);
 
 #ifdef __cplusplus

@@ -270,16 +270,22 @@ def wango_old_running(qh, kh, g, tau, window):
     return n_old, z_old
 
 
-def wango_old_blocked(qh, kh, g, tau, window, block=64):
+def wango_old_blocked(qh, kh, g, tau, window, block=64, split=False):
     """Same quantities as :func:`wango_old_running`, with the prefix sums taken
     in blocks of ``block`` source positions (the text uses blocks of 64): the
     state S, z holds every source before the block; within the block, a source
-    j is visible to destination i exactly when j <= i - W."""
+    j is visible to destination i exactly when j <= i - W.
+
+    With split=True the two terms are returned apart: (n_state, z_state) read
+    out of the state at the block boundary, and (n_intra, z_intra) from the
+    sources of the block itself; their sums are the two returned otherwise."""
     t_len, H, dh = qh.shape
     F = g.shape[1]
     fh = F // H
     n_old = np.zeros((t_len, F))
     z_old = np.zeros((t_len, H))
+    n_in = np.zeros((t_len, F))
+    z_in = np.zeros((t_len, H))
     for a in range(H):
         st = math.sqrt(tau[a])
         fq = phi(st * qh[:, a, :], dh)
@@ -294,11 +300,15 @@ def wango_old_blocked(qh, kh, g, tau, window, block=64):
                 # destinations whose boundary i - W falls inside this source block
                 sel = (np.arange(s0, s1)[None, :] <= np.arange(d0, d1)[:, None] - window)
                 w = np.where(sel, fq[d0:d1] @ fk[s0:s1].T, 0.0)
-                n_old[d0:d1, a * fh:(a + 1) * fh] = fq[d0:d1] @ S + w @ ga[s0:s1]
-                z_old[d0:d1, a] = fq[d0:d1] @ z + w.sum(axis=1)
+                n_old[d0:d1, a * fh:(a + 1) * fh] = fq[d0:d1] @ S
+                z_old[d0:d1, a] = fq[d0:d1] @ z
+                n_in[d0:d1, a * fh:(a + 1) * fh] = w @ ga[s0:s1]
+                z_in[d0:d1, a] = w.sum(axis=1)
             S += fk[s0:s1].T @ ga[s0:s1]
             z += fk[s0:s1].sum(axis=0)
-    return n_old, z_old
+    if split:
+        return n_old, z_old, n_in, z_in
+    return n_old + n_in, z_old + z_in
 
 
 def wango_band(qh, kh, g, tau, window):

@@ -51,6 +51,22 @@ def unpack_gates(gp: np.ndarray, M: int, F: int) -> np.ndarray:
     return out.reshape(M, F)
 
 
+def permute_features(a: np.ndarray) -> np.ndarray:
+    """[..., D] (D % 32 == 0) -> the permuted feature order of include/tango.h:
+    position 8g + s of each group of 32 holds feature perm(g, s)."""
+    D = a.shape[-1]
+    src = np.concatenate([32 * c + _PERM.reshape(-1) for c in range(D // 32)])
+    return np.ascontiguousarray(a[..., src])
+
+
+def unpermute_features(a: np.ndarray) -> np.ndarray:
+    D = a.shape[-1]
+    src = np.concatenate([32 * c + _PERM.reshape(-1) for c in range(D // 32)])
+    out = np.empty_like(a)
+    out[..., src] = a
+    return out
+
+
 def unblock_nold(nb: np.ndarray, M: int, F: int) -> np.ndarray:
     """[M/16, F/16, 64, 4] -> [M, F]: lane l holds row l%16, columns 4(l/16)+r."""
     a = nb.reshape(M // 16, F // 16, 4, 16, 4)        # ib, fb, lg, li, r

@@ -144,5 +144,7 @@ def test_stage_entry_points_validate(lib):
     assert lib.tango_stage_proj(ctypes.byref(s), ctypes.byref(w), None, FAKE, FAKE, FAKE, FAKE, None) == -1
     assert lib.tango_stage_aggregate(ctypes.byref(s), FAKE, None, FAKE, FAKE, FAKE, FAKE, FAKE, 0, None) == -6
     assert lib.tango_stage_out(ctypes.byref(shape(dtype=3)), FAKE, FAKE, FAKE, FAKE, FAKE, None) == -3
-    assert lib.wango_stage_scan(ctypes.byref(s), FAKE, 0, 128, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 0, None) == -2
-    assert lib.wango_stage_band(ctypes.byref(s), FAKE, None, 0, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None) == -2
+    assert lib.wango_stage_proj(ctypes.byref(s), ctypes.byref(w), FAKE, FAKE, FAKE, FAKE, FAKE, None, FAKE, None) == -1
+    assert lib.wango_stage_scan(ctypes.byref(s), 0, 128, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 0, None) == -2
+    assert lib.wango_stage_scan(ctypes.byref(s), 256, 96, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 0, None) == -5
+    assert lib.wango_stage_band(ctypes.byref(s), FAKE, None, 0, 128, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None) == -2

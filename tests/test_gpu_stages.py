@@ -195,6 +195,7 @@ SCAN_CASES = [
     dict(dtype="bf16", B=1, T=700, d_model=128, d_gate=512, n_heads=2, head_dim=64, window=128, chunk=64),
     dict(dtype="bf16", B=2, T=333, d_model=128, d_gate=256, n_heads=1, head_dim=32, window=64, chunk=64),
     dict(dtype="bf16", B=1, T=100, d_model=128, d_gate=256, n_heads=1, head_dim=64, window=256, chunk=128),
+    dict(dtype="bf16", B=1, T=3000, d_model=128, d_gate=1024, n_heads=2, head_dim=64, window=256, chunk=128),
     dict(dtype="f32", B=1, T=400, d_model=128, d_gate=128, n_heads=1, head_dim=64, window=128, chunk=128),
 ]
 
@@ -203,12 +204,58 @@ def _scan_ids(c):
     return f"{c['dtype']}-B{c['B']}-T{c['T']}-H{c['n_heads']}-dh{c['head_dim']}-W{c['window']}-C{c['chunk']}"
 
 
+def _phi_inputs(w, inp, qh, kh):
+    """Oracle features phi(sqrt(tau) q), phi(sqrt(tau) k) of the stored unit
+    vectors, rounded to the dtype, in the layouts of include/tango.h."""
+    tau = O.temperature(np.asarray(inp.theta, np.float64))
+    st = np.sqrt(tau)[None, None, :, None]
+    fq = _q(O.phi(st * qh, w.head_dim), w.dtype)          # [B, T, H, dh]
+    fk = _q(O.phi(st * kh, w.head_dim), w.dtype)
+    Tp, HD = H.padded_len(w.T), w.n_heads * w.head_dim
+    fq_d = dev_tensor(H.permute_features(H.pad_rows(fq.reshape(w.B, w.T, HD), Tp)), w.dtype)
+    fk_d = dev_tensor(H.pack_gates(H.pad_rows(fk.reshape(w.B, w.T, HD), Tp)), w.dtype)
+    return fq, fk, fq_d, fk_d
+
+
+@pytest.mark.parametrize("case", SCAN_CASES[:3] + SCAN_CASES[5:], ids=_scan_ids)
+def test_stage_wango_proj(case):
+    w = wl.small_workload(mode="wango", **case)
+    inp = wl.make_inputs(w)
+    parts, *_ = _stage_inputs(w, inp)
+    bw = block_weights(w, inp)
+    x = dev_tensor(inp.h, w.dtype)
+    shape = api.shape_of(x, bw, w.rope_base, w.rms_eps)
+    Tp, HD, F = H.padded_len(w.T), w.n_heads * w.head_dim, w.d_gate
+    M = w.B * Tp
+    dt = x.dtype
+    bufs = dict(gp=torch.full((M * F,), float("nan"), dtype=dt, device="cuda:0"),
+                v=torch.full((M, F), float("nan"), dtype=dt, device="cuda:0"),
+                qh=torch.full((M, HD), float("nan"), dtype=dt, device="cuda:0"),
+                kh=torch.full((M, HD), float("nan"), dtype=dt, device="cuda:0"),
+                fq=torch.full((M, HD), float("nan"), dtype=dt, device="cuda:0"),
+                fk=torch.full((M * HD,), float("nan"), dtype=dt, device="cuda:0"))
+    announce(f"stage_wango_proj {case}")
+    api.wango_stage_proj(shape, bw, x, bufs["gp"], bufs["v"], bufs["qh"], bufs["kh"], bufs["fq"], bufs["fk"])
+    torch.cuda.synchronize()
+    tau = O.temperature(np.asarray(inp.theta, np.float64))
+    st = np.sqrt(tau)[None, :, None]
+    fq_ref = np.stack([O.phi(st * p["qh"], w.head_dim).reshape(w.T, HD) for p in parts])
+    fk_ref = np.stack([O.phi(st * p["kh"], w.head_dim).reshape(w.T, HD) for p in parts])
+    fq_got = H.unpad_rows(H.unpermute_features(host(bufs["fq"])), w.B, w.T)
+    fk_got = H.unpad_rows(H.unpack_gates(host(bufs["fk"]), M, HD), w.B, w.T)
+    H.check_stage(fq_got, fq_ref, w.dtype, "phi_q")
+    H.check_stage(fk_got, fk_ref, w.dtype, "phi_k")
+    g_got = H.unpad_rows(H.unpack_gates(host(bufs["gp"]), M, F), w.B, w.T)
+    H.check_stage(g_got, np.stack([p["g"] for p in parts]), w.dtype, "g")
+
+
 @pytest.mark.parametrize("case", SCAN_CASES, ids=_scan_ids)
 def test_stage_wango_scan(case):
     w = wl.small_workload(mode="wango", **case)
     inp = wl.make_inputs(w)
     _, g, v, qh, kh = _stage_inputs(w, inp)
     gp, _, qd, kd = _upload_intermediates(w, g, v, qh, kh)
+    _, _, fq_d, fk_d = _phi_inputs(w, inp, qh, kh)
     Tp, F, Hh = H.padded_len(w.T), w.d_gate, w.n_heads
     M = w.B * Tp
     shape = api.make_shape(w.B, w.T, w.d_model, F, Hh, w.head_dim, qd.dtype)
@@ -216,18 +263,21 @@ def test_stage_wango_scan(case):
     n_old = torch.full((M * F,), float("nan"), dtype=torch.float32, device="cuda:0")
     z_old = torch.full((M, Hh), float("nan"), dtype=torch.float32, device="cuda:0")
     announce(f"stage_wango_scan {case}")
-    api.wango_stage_scan(shape, dev_f32(inp.theta), w.window, w.chunk, qd, kd, gp, n_old, z_old, ws)
+    api.wango_stage_scan(shape, w.window, w.chunk, fq_d, fk_d, gp, n_old, z_old, ws)
     torch.cuda.synchronize()
     n_got = H.unpad_rows(H.unblock_nold(host(n_old), M, F), w.B, w.T)
     z_got = H.unpad_rows(host(z_old), w.B, w.T)
     tau = O.temperature(np.asarray(inp.theta, np.float64))
-    refs = [O.wango_old_blocked(qh[b], kh[b], g[b], tau, w.window) for b in range(w.B)]
+    # the state read-out at chunk boundaries: the first term of the oracle's
+    # blocked running sums with blocks of `chunk` positions
+    refs = [O.wango_old_blocked(qh[b], kh[b], g[b], tau, w.window, block=w.chunk, split=True)
+            for b in range(w.B)]
     n_ref = np.stack([r[0] for r in refs])
     z_ref = np.stack([r[1] for r in refs])
-    if w.T <= w.window:
-        assert np.all(n_got == 0) and np.all(z_got == 0)
+    lim = min(w.T, w.window + w.chunk)   # destinations before this read an empty state
+    assert np.all(n_got[:, :lim] == 0) and np.all(z_got[:, :lim] == 0)
+    if w.T <= lim:
         return
-    assert np.all(n_got[:, : w.window] == 0) and np.all(z_got[:, : w.window] == 0)
     H.check_stage(n_got, n_ref, w.dtype, "n_old")
     H.check_stage(z_got, z_ref, w.dtype, "z_old")
 
@@ -235,8 +285,10 @@ def test_stage_wango_scan(case):
 BAND_CASES = [
     dict(dtype="bf16", B=1, T=1000, d_model=128, d_gate=256, n_heads=1, head_dim=128, window=128, chunk=128),
     dict(dtype="bf16", B=2, T=333, d_model=128, d_gate=512, n_heads=2, head_dim=64, window=64, chunk=64),
+    dict(dtype="bf16", B=1, T=700, d_model=128, d_gate=512, n_heads=2, head_dim=64, window=192, chunk=64),
     dict(dtype="bf16", B=1, T=200, d_model=128, d_gate=256, n_heads=4, head_dim=32, window=512, chunk=128),
     dict(dtype="f32", B=1, T=300, d_model=128, d_gate=128, n_heads=1, head_dim=64, window=128, chunk=64),
+    dict(dtype="f32", B=1, T=400, d_model=128, d_gate=128, n_heads=1, head_dim=64, window=128, chunk=128),
 ]
 
 
@@ -252,7 +304,8 @@ def test_stage_wango_band(case, null):
     Tp, F, Hh = H.padded_len(w.T), w.d_gate, w.n_heads
     M = w.B * Tp
     tau = O.temperature(np.asarray(inp.theta, np.float64))
-    refs = [O.wango_old_blocked(qh[b], kh[b], g[b], tau, w.window) for b in range(w.B)]
+    refs = [O.wango_old_blocked(qh[b], kh[b], g[b], tau, w.window, block=w.chunk, split=True)
+            for b in range(w.B)]
     n_old = np.stack([r[0] for r in refs]).astype(np.float32)
     z_old = np.stack([r[1] for r in refs]).astype(np.float32)
     nd = dev_f32(H.block_nold(H.pad_rows(n_old, Tp)))
@@ -261,7 +314,7 @@ def test_stage_wango_band(case, null):
     gbar = torch.full((M, F), float("nan"), dtype=qd.dtype, device="cuda:0")
     announce(f"stage_wango_band {case} null={null}")
     api.wango_stage_band(shape, dev_f32(inp.theta), None if nbias is None else dev_f32(nbias),
-                         w.window, qd, kd, gp, nd, zd, gbar)
+                         w.window, w.chunk, qd, kd, gp, nd, zd, gbar)
     torch.cuda.synchronize()
     got = H.unpad_rows(host(gbar), w.B, w.T)
     ref = _agg_ref(w, inp, qh, kh, g, nbias)

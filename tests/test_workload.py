@@ -43,6 +43,9 @@ def test_layout_packers_roundtrip():
     for blk, grp, f, s in [(0, 0, 0, 0), (1, 3, 47, 7), (5, 2, 10, 4), (7, 1, 3, 3)]:
         t = 32 * blk + (4 * grp + s if s < 4 else 16 + 4 * grp + s - 4)
         assert gp[blk, grp, f, s] == g[t, f]
+    f = rng.standard_normal((5, 64))
+    np.testing.assert_array_equal(H.unpermute_features(H.permute_features(f)), f)
+    assert H.permute_features(f)[2, 32 + 8 * 3 + 5] == f[2, 32 + 16 + 4 * 3 + 1]
     n = rng.standard_normal((64, 32))
     nb = H.block_nold(n)
     np.testing.assert_array_equal(H.unblock_nold(nb, 64, 32), n)

@@ -157,7 +157,7 @@ def main():
     qh = torch.empty(M, HD, dtype=torch.bfloat16, device=dev)
     kh = torch.empty(M, HD, dtype=torch.bfloat16, device=dev)
     gbar = torch.empty(M, F, dtype=torch.bfloat16, device=dev)
-    api.tango_stage_proj(st, bt, xt, gp, v, qh, kh, stream=stream)
+    api.tango_stage_proj(st, bt, xt, gp, v, qh, kh, ws=ws_t, stream=stream)
 
     def timed(fn, n):
         fn()
@@ -191,7 +191,7 @@ def main():
     kg = torch.empty(Mg, HDg, dtype=torch.bfloat16, device=dev)
     fqg = torch.empty(Mg, HDg, dtype=torch.bfloat16, device=dev)
     fkg = torch.empty(Mg * HDg, dtype=torch.bfloat16, device=dev)
-    api.wango_stage_proj(sg, bg, xg, gpg, vg, qg, kg, fqg, fkg, stream=stream)
+    api.wango_stage_proj(sg, bg, xg, gpg, vg, qg, kg, fqg, fkg, ws=ws_g, stream=stream)
     n_old = torch.empty(Mg * wg.d_gate, dtype=torch.float32, device=dev)
     z_old = torch.empty(Mg, wg.n_heads, dtype=torch.float32, device=dev)
     ms_scan = timed(lambda: api.wango_stage_scan(sg, wg.window, wg.chunk, fqg, fkg, gpg, n_old, z_old,

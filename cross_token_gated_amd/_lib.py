@@ -21,7 +21,7 @@ STATUS_CODE = {v: k for k, v in STATUS.items()}
 EXPORTS = [
     "tango_workspace_size", "tango_block_fwd", "wango_workspace_size", "wango_block_fwd",
     "tango_status_string", "tango_last_error", "tango_version",
-    "tango_stage_proj", "wango_stage_proj", "tango_stage_aggregate", "tango_stage_out",
+    "tango_proj_workspace_size", "tango_stage_proj", "wango_stage_proj", "tango_stage_aggregate", "tango_stage_out",
     "wango_stage_scan", "wango_stage_band",
 ]
 
@@ -69,8 +69,9 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
         "tango_status_string": (ctypes.c_char_p, [ctypes.c_int]),
         "tango_last_error": (ctypes.c_char_p, []),
         "tango_version": (ctypes.c_int, []),
-        "tango_stage_proj": (ctypes.c_int, [S, W, vp, vp, vp, vp, vp, vp]),
-        "wango_stage_proj": (ctypes.c_int, [S, W, vp, vp, vp, vp, vp, vp, vp, vp]),
+        "tango_proj_workspace_size": (sz, [S]),
+        "tango_stage_proj": (ctypes.c_int, [S, W, vp, vp, vp, vp, vp, vp, sz, vp]),
+        "wango_stage_proj": (ctypes.c_int, [S, W, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]),
         "tango_stage_aggregate": (ctypes.c_int, [S, vp, vp, vp, vp, vp, vp, vp, sz, vp]),
         "tango_stage_out": (ctypes.c_int, [S, vp, vp, vp, vp, vp, vp]),
         "wango_stage_scan": (ctypes.c_int, [S, i32, i32, vp, vp, vp, vp, vp, vp, sz, vp]),

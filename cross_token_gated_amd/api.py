@@ -123,16 +123,26 @@ def wango_block_fwd(x: torch.Tensor, w: BlockWeights, window: int, phi_dim: int,
 
 # ---- stage entry points ---------------------------------------------------------
 
-def tango_stage_proj(shape: Shape, w: BlockWeights, x, gp, v, qh, kh, stream=None) -> None:
+def tango_proj_workspace_size(shape: Shape) -> int:
+    return int(load().tango_proj_workspace_size(ctypes.byref(shape)))
+
+
+def tango_stage_proj(shape: Shape, w: BlockWeights, x, gp, v, qh, kh, ws=None, stream=None) -> None:
     cw = w.c_struct()
+    if ws is None:
+        ws = workspace(tango_proj_workspace_size(shape), x.device)
     check(load().tango_stage_proj(ctypes.byref(shape), ctypes.byref(cw), _ptr(x), _ptr(gp),
-                                  _ptr(v), _ptr(qh), _ptr(kh), _stream(stream)))
+                                  _ptr(v), _ptr(qh), _ptr(kh), _ptr(ws), ws.numel(), _stream(stream)))
 
 
-def wango_stage_proj(shape: Shape, w: BlockWeights, x, gp, v, qh, kh, fq, fk, stream=None) -> None:
+def wango_stage_proj(shape: Shape, w: BlockWeights, x, gp, v, qh, kh, fq, fk, ws=None,
+                     stream=None) -> None:
     cw = w.c_struct()
+    if ws is None:
+        ws = workspace(tango_proj_workspace_size(shape), x.device)
     check(load().wango_stage_proj(ctypes.byref(shape), ctypes.byref(cw), _ptr(x), _ptr(gp),
-                                  _ptr(v), _ptr(qh), _ptr(kh), _ptr(fq), _ptr(fk), _stream(stream)))
+                                  _ptr(v), _ptr(qh), _ptr(kh), _ptr(fq), _ptr(fk), _ptr(ws),
+                                  ws.numel(), _stream(stream)))
 
 
 def tango_stage_aggregate(shape: Shape, theta, null_bias, qh, kh, gp, gbar, ws, stream=None) -> None:

@@ -13,9 +13,33 @@
 // KO (§2.1, eq. 3): out_m = h_m + (gbar_m * v_m) W_o^T, the gated product
 // formed while the A tile is staged, the residual added in the epilogue.
 //
-// Both use a 256-thread workgroup (four waves in a 2 x 2 grid) over a BM x BN
-// output tile; K streams through double-buffered LDS tiles of BK columns, and
-// every 16 x 16 block is an MFMA accumulator (see common.hpp).
+// Both use a 256-thread workgroup (four waves) over a BM x BN output tile.  K
+// streams through double-buffered LDS tiles of BK columns; global loads run D
+// k-tiles ahead in registers and are converted (gating) only when they are
+// written to LDS, so their latency overlaps D tiles of MFMA work.  Every
+// 16 x 16 output block is an MFMA accumulator (see common.hpp).
+//
+// The KP input rows are prepared once by KX (one wave per row): the RMSNorm
+// scale r_m and the parts of h_m * gain in the compute dtype, so the KP main
+// loop only copies (the 34 or so column tiles of a row tile would otherwise
+// each redo the conversion).
+//
+// In bf16 the weights are exact, but the activation operand of both products
+// (h * gain, and gbar * v) is a float32 value.  It is carried as two bf16
+// parts, hi = bf16(e) and lo = bf16(e - hi), each multiplied on MFMA into the
+// same float32 accumulator, so the product sees e to about 2^-16 relative
+// instead of 2^-9: without it the error of a stack of eight shared-weight
+// applications at the first positions of a sequence (whose aggregate is their
+// own gate, so their updates are the largest) exceeds 2e-2 of the output rms.
+//
+// Row tiles never straddle two sequences (the padded length is a multiple of
+// 128), so a workgroup resolves its (batch, position) once.  The 1-D grid is
+// mapped so that each of the eight XCDs (own L2 each) receives a contiguous
+// range of tiles, walked in groups of GM row tiles with the row tile varying
+// fastest (column tiles from the last): the A rows of a group stay in that
+// XCD's L2 while the B tiles sweep.
+#include <type_traits>
+
 #include "common.hpp"
 #include "kernels.hpp"
 
@@ -23,135 +47,322 @@ namespace tango {
 
 namespace {
 
-template <typename T> struct GemmCfg;
-template <> struct GemmCfg<bf16> {
-  static constexpr int BM = 128, BN = 128, BK = 64;
-};
-template <> struct GemmCfg<float> {
-  static constexpr int BM = 64, BN = 128, BK = 32;
-};
-
 constexpr int kThreads = 256;
-
-// LDS row stride of an operand tile (elements): BK plus 16 bytes of padding.
-template <typename T> constexpr int op_stride() { return GemmCfg<T>::BK + 16 / (int)sizeof(T); }
-// LDS row stride of the fp32 output tile.
+constexpr int kGroupRows = 8;    // GM: row tiles per launch group
+constexpr int kEpiRows = 64;     // output rows staged in LDS per epilogue pass
 constexpr int kCStride = 128 + 4;
 
-template <typename T> constexpr int op_tile_elems(int rows) { return rows * op_stride<T>(); }
+// BM x BN output tile, BK-wide k-tiles, WM x WN waves, register prefetch D
+// k-tiles ahead, AS parts (1, or hi and lo) of the A operand.
+template <int BM_, int BN_, int BK_, int WM_, int WN_, int D_, int AS_>
+struct TileCfg {
+  static constexpr int BM = BM_, BN = BN_, BK = BK_, WM = WM_, WN = WN_, D = D_, AS = AS_;
+  static constexpr int WTM = BM / WM, WTN = BN / WN;   // wave tile
+  static constexpr int IB = WTM / 16, JB = WTN / 16;   // 16 x 16 blocks per wave
+  static_assert(WM * WN * 64 == kThreads, "four waves");
+  static_assert(BN <= 128 && BM % kEpiRows == 0 && BK % 32 == 0, "tile shape");
+  static_assert(D >= 1 && D <= 4, "prefetch depth");
+  static_assert(AS == 1 || AS == 2, "operand parts");
+};
 
-template <typename T> constexpr size_t gemm_lds_bytes() {
-  using C = GemmCfg<T>;
-  size_t ops = 2 * (size_t)(op_tile_elems<T>(C::BM) + op_tile_elems<T>(C::BN)) * sizeof(T);
-  size_t out = (size_t)C::BM * kCStride * sizeof(float);
-  return (ops > out ? ops : out) + (size_t)C::BM * sizeof(float);
-}
+template <typename T> struct ProjCfg;
+template <> struct ProjCfg<bf16> : TileCfg<128, 128, 32, 2, 2, 3, 2> {};
+template <> struct ProjCfg<float> : TileCfg<64, 128, 32, 2, 2, 1, 1> {};
+template <typename T> struct OutCfg;
+template <> struct OutCfg<bf16> : TileCfg<128, 128, 32, 2, 2, 4, 2> {};
+template <> struct OutCfg<float> : TileCfg<64, 128, 32, 2, 2, 1, 1> {};
 
-// 16-byte piece = PE elements.
 template <typename T> constexpr int piece_elems() { return 16 / (int)sizeof(T); }
 
+// LDS operand layout.  A tile of R rows x BK columns is stored as blocks of
+// 16 rows x 32 columns; the 16-byte pieces of a block (row r, k group g =
+// columns 8g .. 8g + 7, in PPF chunks h of PE elements: PPF = 1 for bf16, 2
+// for float32) live in 256-byte regions, one per (chunk, group), at position
+// (r + 4g) mod 16.  An MFMA fragment read (16 lanes per group: rows 0..15 of
+// one group) then covers one whole region, and the loaders (four consecutive
+// lanes fetch 64 contiguous bytes of one row, which keeps the global loads
+// coalesced) write 16 distinct positions per 16 lanes.  On gfx950 both run at
+// the full LDS width; a padded row-major tile reads at half of it.
+template <typename T> constexpr int frag_chunks() { return (int)sizeof(T) / 2; }   // PPF
+template <class CF, typename T> constexpr int tile_chunks(int rows) {
+  return rows / 16 * (CF::BK / 32) * frag_chunks<T>();
+}
+// Byte offset of piece (row, piece kp along the row) in a tile.
+template <class CF, typename T>
+__device__ __forceinline__ int piece_offset(int row, int kp) {
+  constexpr int PE = 16 / (int)sizeof(T), PPF = frag_chunks<T>(), NKB = CF::BK / 32;
+  const int kb = kp * PE / 32, within = kp % (32 / PE);
+  const int g = within / PPF, h = within % PPF, r = row & 15;
+  const int region = (((row >> 4) * NKB + kb) * PPF + h) * 4 + g;
+  return region * 256 + ((r + 4 * g) & 15) * 16;
+}
+template <class CF, typename T> constexpr size_t ops_bytes() {
+  return 2 * (size_t)tile_chunks<CF, T>(CF::AS * CF::BM + CF::BN) * 1024;
+}
+constexpr size_t kEpiBytes = (size_t)kEpiRows * kCStride * sizeof(float);
+// Operand buffers (reused for the epilogue tile), then BM row scales.
+template <class CF, typename T> constexpr size_t main_bytes() {
+  return (ops_bytes<CF, T>() > kEpiBytes ? ops_bytes<CF, T>() : kEpiBytes) +
+         (size_t)CF::BM * sizeof(float);
+}
+
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+// One 16-byte LDS piece per operand part.
+template <int AS> struct Parts {
+  u32x4 p[AS];
+};
 
-// The MFMA inner product of one BK-wide LDS tile for one wave.
-// Wave tile: WM x WN = (BM/2) x (BN/2); blocks IB x JB of 16 x 16.
-template <typename T>
-__device__ __forceinline__ void tile_mma(f32x4 (&acc)[GemmCfg<T>::BM / 32][GemmCfg<T>::BN / 32],
-                                         const T* __restrict__ As, const T* __restrict__ Bs,
-                                         int wr, int wc, int lane) {
-  using C = GemmCfg<T>;
-  constexpr int IB = C::BM / 32, JB = C::BN / 32, S = op_stride<T>();
-  const int row = lane & 15, grp = lane >> 4;
+// Round PE float32 values to T parts: hi = T(e), and with AS = 2 also
+// lo = T(e - hi) (e - hi is exact in float32).
+template <typename T, int AS, int PE>
+__device__ __forceinline__ Parts<AS> split_parts(const float (&e)[PE]) {
+  Parts<AS> out;
+  T* hi = reinterpret_cast<T*>(&out.p[0]);
 #pragma unroll
-  for (int ks = 0; ks < C::BK / 32; ++ks) {
-    Frag<T> a[IB], b[JB];
+  for (int q = 0; q < PE; ++q) hi[q] = cvt<T>(e[q]);
+  if constexpr (AS == 2) {
+    T* lo = reinterpret_cast<T*>(&out.p[1]);
 #pragma unroll
-    for (int i = 0; i < IB; ++i)
-      a[i] = load_frag<T>(As + (wr * (C::BM / 2) + i * 16 + row) * S + ks * 32 + grp * 8);
-#pragma unroll
-    for (int j = 0; j < JB; ++j)
-      b[j] = load_frag<T>(Bs + (wc * (C::BN / 2) + j * 16 + row) * S + ks * 32 + grp * 8);
-#pragma unroll
-    for (int i = 0; i < IB; ++i)
-#pragma unroll
-      for (int j = 0; j < JB; ++j) mma(acc[i][j], a[i], b[j]);
+    for (int q = 0; q < PE; ++q) lo[q] = cvt<T>(e[q] - tof<T>(hi[q]));
   }
+  return out;
 }
 
-// Generic double-buffered main loop.  load_a(pass, row, kpiece, kt) /
-// load_b(row, kpiece, kt) return one 16-byte piece of the A (BM x BK) / B
-// (BN x BK) tile of k-tile kt; `pass` is the compile-time index of the row
-// pass (row = this thread's first row + pass * rows-per-pass).
-template <typename T, typename LA, typename LB>
-__device__ __forceinline__ void gemm_mainloop(f32x4 (&acc)[GemmCfg<T>::BM / 32][GemmCfg<T>::BN / 32],
-                                              T* lds, int nk, LA load_a, LB load_b) {
-  using C = GemmCfg<T>;
-  constexpr int PR = C::BK / piece_elems<T>();     // pieces per row (8)
-  constexpr int RPP = kThreads / PR;               // rows per pass (32)
-  constexpr int PA = C::BM / RPP, PB = C::BN / RPP;
-  constexpr int S = op_stride<T>();
-  // tile addresses are computed from the LDS base (not picked from an array
-  // of pointers), so every access stays a ds_read / ds_write
-  constexpr int TA = op_tile_elems<T>(C::BM), TB = op_tile_elems<T>(C::BN);
-  auto As = [&](int buf) { return lds + buf * TA; };
-  auto Bs = [&](int buf) { return lds + 2 * TA + buf * TB; };
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int wr = wave >> 1, wc = wave & 1;
-  const int prow = tid / PR, pcol = tid % PR;
-  u32x4 ra[PA], rb[PB];
-  auto fetch = [&](int kt) {
-#pragma unroll
-    for (int p = 0; p < PA; ++p) ra[p] = load_a(p, prow + p * RPP, pcol, kt);
-#pragma unroll
-    for (int p = 0; p < PB; ++p) rb[p] = load_b(prow + p * RPP, pcol, kt);
-  };
-  auto stash = [&](int buf) {
-#pragma unroll
-    for (int p = 0; p < PA; ++p)
-      *reinterpret_cast<u32x4*>(As(buf) + (prow + p * RPP) * S + pcol * piece_elems<T>()) = ra[p];
-#pragma unroll
-    for (int p = 0; p < PB; ++p)
-      *reinterpret_cast<u32x4*>(Bs(buf) + (prow + p * RPP) * S + pcol * piece_elems<T>()) = rb[p];
-  };
-  fetch(0);
-  stash(0);
-  __syncthreads();
-  for (int kt = 0; kt < nk; ++kt) {
-    const int buf = kt & 1;
-    if (kt + 1 < nk) fetch(kt + 1);
-    tile_mma<T>(acc, As(buf), Bs(buf), wr, wc, lane);
-    if (kt + 1 < nk) stash(buf ^ 1);
-    __syncthreads();
-  }
-}
-
-// Write the wave accumulators, times the row scale rs[row] (or 1), to the fp32
-// LDS tile Cs[BM][kCStride].
-template <typename T>
-__device__ __forceinline__ void acc_to_lds(const f32x4 (&acc)[GemmCfg<T>::BM / 32][GemmCfg<T>::BN / 32],
-                                           float* Cs, const float* rs) {
-  using C = GemmCfg<T>;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int wr = wave >> 1, wc = wave & 1, col = lane & 15, grp = lane >> 4;
-#pragma unroll
-  for (int i = 0; i < C::BM / 32; ++i)
-#pragma unroll
-    for (int j = 0; j < C::BN / 32; ++j)
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int row = wr * (C::BM / 2) + i * 16 + grp * 4 + r;
-        const float s = rs ? rs[row] : 1.0f;
-        Cs[row * kCStride + wc * (C::BN / 2) + j * 16 + col] = acc[i][j][r] * s;
-      }
-}
-
-template <typename T> __device__ __forceinline__ u32x4 as_piece(const T* p) {
-  return *reinterpret_cast<const u32x4*>(p);
-}
-
-// N consecutive residual-stream values (float32 or bf16) as floats.
 template <typename IO, int N> struct IOVec {
   typedef IO type __attribute__((ext_vector_type(N)));
 };
+
+template <int V> using IC = std::integral_constant<int, V>;
+
+// Output tile of this workgroup (see the file header for the order).
+struct TilePos {
+  int64_t m_tile;
+  int n_tile;
+};
+__device__ __forceinline__ TilePos tile_of(int64_t nm, int nn) {
+  const int64_t L = blockIdx.x, NT = nm * nn;
+  const int64_t q = NT / 8, r = NT % 8, x = L % 8;
+  const int64_t t = x * q + (x < r ? x : r) + L / 8;   // contiguous range per XCD
+  const int64_t gsz = (int64_t)kGroupRows * nn;
+  const int64_t g = t / gsz, w = t - g * gsz;
+  const int64_t first = g * kGroupRows;
+  const int64_t rows = nm - first < kGroupRows ? nm - first : kGroupRows;
+  // last column tile first: in KP those hold the queries and keys, whose
+  // epilogue is the longest, so they start early instead of forming a tail
+  return {first + w % rows, nn - 1 - (int)(w / rows)};
+}
+
+// The MFMA inner product of one BK-wide LDS tile for one wave.
+// Fragment (row block rb, k block kb) of a tile, this lane.
+template <class CF, typename T>
+__device__ __forceinline__ Frag<T> lds_frag(const T* tile, int rb, int kb, int lane) {
+  constexpr int PPF = frag_chunks<T>(), NKB = CF::BK / 32;
+  const int r = lane & 15, g = lane >> 4;
+  const unsigned char* base = reinterpret_cast<const unsigned char*>(tile) +
+                              ((rb * NKB + kb) * PPF * 4 + g) * 256 + ((r + 4 * g) & 15) * 16;
+  if constexpr (PPF == 1) {
+    return load_frag<T>(reinterpret_cast<const T*>(base));
+  } else {
+    return join(load_quad<T>(reinterpret_cast<const T*>(base)),
+                load_quad<T>(reinterpret_cast<const T*>(base + 4 * 256)));
+  }
+}
+
+template <class CF, typename T>
+__device__ __forceinline__ void tile_mma(f32x4 (&acc)[CF::IB][CF::JB], const T* __restrict__ As,
+                                         const T* __restrict__ Bs, int wr, int wc, int lane) {
+#pragma unroll
+  for (int ks = 0; ks < CF::BK / 32; ++ks) {
+    Frag<T> b[CF::JB];
+#pragma unroll
+    for (int j = 0; j < CF::JB; ++j) b[j] = lds_frag<CF, T>(Bs, wc * CF::JB + j, ks, lane);
+#pragma unroll
+    for (int i = 0; i < CF::IB; ++i) {
+#pragma unroll
+      for (int part = 0; part < CF::AS; ++part) {   // A parts live BM rows apart
+        const Frag<T> a = lds_frag<CF, T>(As, part * (CF::BM / 16) + wr * CF::IB + i, ks, lane);
+#pragma unroll
+        for (int j = 0; j < CF::JB; ++j) mma(acc[i][j], a, b[j]);
+      }
+    }
+  }
+}
+
+// Piece loaded by this thread in pass p: PR = BK / PE consecutive threads
+// cover one row of the tile.
+template <class CF, typename T> struct PiecePos {
+  int row, kp;
+};
+template <class CF, typename T>
+__device__ __forceinline__ PiecePos<CF, T> piece_pos(int tid, int p) {
+  constexpr int PR = CF::BK / (16 / (int)sizeof(T)), RPP = kThreads / PR;
+  return {tid / PR + p * RPP, tid % PR};
+}
+
+// Main loop.  SA / SB supply this thread's 16-byte pieces of the A (BM x BK)
+// and B (BN x BK) tiles (pass p: the piece at piece_pos(tid, p)):
+// fetch(raw, p, k0) issues the global load for the k-tile starting at column
+// k0, convert(raw, p) turns it into the 16-byte pieces stored to LDS (one per
+// operand part).  At the top of step kt,
+// LDS buffer kt & 1 holds tile kt and register set (kt + j) % D holds tile
+// kt + j for j = 1..D.
+template <class CF, typename T, class SA, class SB>
+__device__ __forceinline__ void gemm_mainloop(f32x4 (&acc)[CF::IB][CF::JB], T* lds, int nk, SA& sa,
+                                              SB& sb) {
+  constexpr int PE = piece_elems<T>(), D = CF::D;
+  constexpr int PA = tile_chunks<CF, T>(CF::BM) / 4, PB = tile_chunks<CF, T>(CF::BN) / 4;
+  constexpr int TA = tile_chunks<CF, T>(CF::AS * CF::BM) * 64 * PE;   // elements
+  constexpr int TB = tile_chunks<CF, T>(CF::BN) * 64 * PE;
+  constexpr int PART = tile_chunks<CF, T>(CF::BM) * 64 * PE;          // A part stride
+  const int tid = threadIdx.x, lane = tid & 63;
+  int a_off[PA], b_off[PB];   // byte offsets of this thread's pieces in a tile
+#pragma unroll
+  for (int p = 0; p < PA; ++p) {
+    const PiecePos<CF, T> pp = piece_pos<CF, T>(tid, p);
+    a_off[p] = piece_offset<CF, T>(pp.row, pp.kp);
+  }
+#pragma unroll
+  for (int p = 0; p < PB; ++p) {
+    const PiecePos<CF, T> pp = piece_pos<CF, T>(tid, p);
+    b_off[p] = piece_offset<CF, T>(pp.row, pp.kp);
+  }
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wr = wave / CF::WN, wc = wave % CF::WN;
+  typename SA::raw ra[D][PA];
+  typename SB::raw rb[D][PB];
+  auto fetch = [&](auto set, int kt) {
+    constexpr int s = decltype(set)::value;
+#pragma unroll
+    for (int p = 0; p < PA; ++p) sa.fetch(ra[s][p], p, kt * CF::BK);
+#pragma unroll
+    for (int p = 0; p < PB; ++p) sb.fetch(rb[s][p], p, kt * CF::BK);
+  };
+  auto stash = [&](auto set, int kt) {
+    constexpr int s = decltype(set)::value;
+    unsigned char* As = reinterpret_cast<unsigned char*>(lds + (kt & 1) * TA);
+    unsigned char* Bs = reinterpret_cast<unsigned char*>(lds + 2 * TA + (kt & 1) * TB);
+#pragma unroll
+    for (int p = 0; p < PA; ++p) {
+      const Parts<CF::AS> pa = sa.convert(ra[s][p], p);
+#pragma unroll
+      for (int part = 0; part < CF::AS; ++part)
+        *reinterpret_cast<u32x4*>(As + part * PART * (int)sizeof(T) + a_off[p]) = pa.p[part];
+    }
+#pragma unroll
+    for (int p = 0; p < PB; ++p) *reinterpret_cast<u32x4*>(Bs + b_off[p]) = sb.convert(rb[s][p], p);
+  };
+  // Fetches past the last tile re-read the last one (never stashed): every
+  // step issues the same loads, so the wait before a stash only covers the
+  // set being stashed.
+  auto step = [&](auto set, int kt) {
+    tile_mma<CF, T>(acc, lds + (kt & 1) * TA, lds + 2 * TA + (kt & 1) * TB, wr, wc, lane);
+    if (kt + 1 < nk) stash(set, kt + 1);
+    fetch(set, min(kt + 1 + D, nk - 1));
+    __syncthreads();
+  };
+  fetch(IC<0>{}, 0);
+  stash(IC<0>{}, 0);
+  fetch(IC<1 % D>{}, min(1, nk - 1));
+  if constexpr (D > 1) fetch(IC<2 % D>{}, min(2, nk - 1));
+  if constexpr (D > 2) fetch(IC<3 % D>{}, min(3, nk - 1));
+  if constexpr (D > 3) fetch(IC<4 % D>{}, min(4, nk - 1));
+  __syncthreads();
+  // step kt uses register set (kt + 1) % D; the loop is unrolled by D so that
+  // the set is a compile-time index
+  int kt = 0;
+  for (; kt + D <= nk; kt += D) {
+    step(IC<1 % D>{}, kt);
+    if constexpr (D > 1) step(IC<2 % D>{}, kt + 1);
+    if constexpr (D > 2) step(IC<3 % D>{}, kt + 2);
+    if constexpr (D > 3) step(IC<4 % D>{}, kt + 3);
+  }
+  if (kt < nk) step(IC<1 % D>{}, kt);
+  if constexpr (D > 1) if (kt + 1 < nk) step(IC<2 % D>{}, kt + 1);
+  if constexpr (D > 2) if (kt + 2 < nk) step(IC<3 % D>{}, kt + 2);
+}
+
+// Rows of plain T matrices (the weights): one pointer per pass, at the
+// piece's row and column; a row past the end points at a valid row and is
+// replaced by zeros when stored.
+template <typename T, int P> struct RowSource {
+  struct raw {
+    u32x4 v;
+  };
+  const T* ptr[P];
+  bool ok[P];
+  __device__ __forceinline__ void fetch(raw& r, int p, int k0) const {
+    r.v = *reinterpret_cast<const u32x4*>(ptr[p] + k0);
+  }
+  __device__ __forceinline__ u32x4 convert(const raw& r, int p) const {
+    return ok[p] ? r.v : u32x4{0u, 0u, 0u, 0u};
+  }
+};
+
+// A of KP: the AS parts of the prepared rows (plain copies).
+template <typename T, int P, int AS> struct PartsSource {
+  struct raw {
+    u32x4 v[AS];
+  };
+  const T* ptr[P];      // part 0 at the piece; part q lies q * part_stride further
+  int64_t part_stride;
+  __device__ __forceinline__ void fetch(raw& r, int p, int k0) const {
+#pragma unroll
+    for (int q = 0; q < AS; ++q) r.v[q] = *reinterpret_cast<const u32x4*>(ptr[p] + q * part_stride + k0);
+  }
+  __device__ __forceinline__ Parts<AS> convert(const raw& r, int) const {
+    Parts<AS> out;
+#pragma unroll
+    for (int q = 0; q < AS; ++q) out.p[q] = r.v[q];
+    return out;
+  }
+};
+
+// A of KO: gbar * v, formed in float and rounded to T parts.
+template <typename T, int P, int AS> struct GatedSource {
+  static constexpr int PE = piece_elems<T>();
+  struct raw {
+    u32x4 g, v;
+  };
+  const T* gptr[P];     // at the piece's row and column
+  const T* vptr[P];
+  __device__ __forceinline__ void fetch(raw& r, int p, int k0) const {
+    r.g = *reinterpret_cast<const u32x4*>(gptr[p] + k0);
+    r.v = *reinterpret_cast<const u32x4*>(vptr[p] + k0);
+  }
+  __device__ __forceinline__ Parts<AS> convert(const raw& r, int) const {
+    const T* ge = reinterpret_cast<const T*>(&r.g);
+    const T* ve = reinterpret_cast<const T*>(&r.v);
+    float e[PE];
+#pragma unroll
+    for (int q = 0; q < PE; ++q) e[q] = tof<T>(ge[q]) * tof<T>(ve[q]);
+    return split_parts<T, AS, PE>(e);
+  }
+};
+
+// Write the accumulator blocks that fall into epilogue pass `pass` (tile rows
+// [64 pass, 64 pass + 64)), times the row scale rs[row] (or 1), to the fp32
+// LDS tile Cs[64][kCStride].
+template <class CF>
+__device__ __forceinline__ void acc_to_lds(const f32x4 (&acc)[CF::IB][CF::JB], float* Cs,
+                                           const float* rs, int pass) {
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wr = wave / CF::WN, wc = wave % CF::WN, col = lane & 15, grp = lane >> 4;
+#pragma unroll
+  for (int i = 0; i < CF::IB; ++i) {
+    const int r0 = wr * CF::WTM + i * 16;
+    if (r0 / kEpiRows != pass) continue;
+#pragma unroll
+    for (int j = 0; j < CF::JB; ++j)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int row = r0 + grp * 4 + r;
+        const float s = rs ? rs[row] : 1.0f;
+        Cs[(row - pass * kEpiRows) * kCStride + wc * CF::WTN + j * 16 + col] = acc[i][j][r] * s;
+      }
+  }
+}
+
 template <typename IO, int N>
 __device__ __forceinline__ void load_io(const IO* p, float (&v)[N]) {
   const typename IOVec<IO, N>::type r = *reinterpret_cast<const typename IOVec<IO, N>::type*>(p);
@@ -169,197 +380,228 @@ __device__ __forceinline__ void store_io(IO* p, const float (&v)[N]) {
 }  // namespace
 
 // ---------------------------------------------------------------------------
-// KP: fused RMSNorm + [W_g; W_v; W_q; W_k] projection + epilogue.
-// Grid: (ceil(N/BN), M_pad/BM) with N = 2F + 2HD, M_pad = B * Tp.
+// KX: RMSNorm scales and operand parts of the KP input rows, one wave per
+// padded row m:  rinv[m] = 1 / sqrt(mean(h_m^2) + eps)  ([TANGO] §2.1, the
+// RMSNorm before eq. 2) and the AS parts of h_m * gain in T; rows past the end
+// of a sequence are zero.  Grid: M_pad / 4 workgroups of 256.
 // ---------------------------------------------------------------------------
-template <typename T, typename IO>
-__global__ __launch_bounds__(kThreads) void proj_kernel(ProjArgs args) {
-  using C = GemmCfg<T>;
-  constexpr int PE = piece_elems<T>();
-  constexpr int PR = C::BK / PE;
-  constexpr int RPP = kThreads / PR;
-  constexpr int PA = C::BM / RPP;
-  extern __shared__ __align__(16) unsigned char smem_raw[];
-  T* lds = reinterpret_cast<T*>(smem_raw);
-  float* rs = reinterpret_cast<float*>(smem_raw + gemm_lds_bytes<T>() - C::BM * sizeof(float));
-
-  const int d = args.d, F = args.F, HD = args.HD, T_len = args.T, Tp = args.Tp;
-  const int N = 2 * F + 2 * HD;
-  const int n0 = blockIdx.x * C::BN;
-  const int64_t m0 = (int64_t)blockIdx.y * C::BM;
-  const IO* __restrict__ x = static_cast<const IO*>(args.x);
-  const T* __restrict__ gain = static_cast<const T*>(args.gain);
-  const int tid = threadIdx.x;
-  const int prow = tid / PR, pcol = tid % PR;
-
-  float ssq[PA];  // sums of squares of this thread's h pieces, per row pass
-#pragma unroll
-  for (int p = 0; p < PA; ++p) ssq[p] = 0.f;
-
-  auto load_a = [&](int pass, int row, int kp, int kt) -> u32x4 {
-    const int64_t m = m0 + row;
-    const int64_t b = m / Tp, t = m % Tp;
-    const int k = kt * C::BK + kp * PE;
-    u32x4 z = {0u, 0u, 0u, 0u};
-    if (t >= T_len) return z;
-    float e[PE];
-    load_io<IO, PE>(x + (b * T_len + t) * d + k, e);
-    float sq = 0.f;
-#pragma unroll
-    for (int q = 0; q < PE; ++q) sq += e[q] * e[q];
-    ssq[pass] += sq;
-    u32x4 out;
-    T* o = reinterpret_cast<T*>(&out);
-    if (gain) {
-#pragma unroll
-      for (int q = 0; q < PE; ++q) o[q] = cvt<T>(e[q] * tof<T>(gain[k + q]));
+template <typename T, typename IO, int AS>
+__global__ __launch_bounds__(kThreads) void prep_kernel(ProjArgs args) {
+  const int lane = threadIdx.x & 63;
+  const int64_t m = (int64_t)blockIdx.x * (kThreads / 64) + (threadIdx.x >> 6);
+  const int d = args.d, Tp = args.Tp, T_len = args.T;
+  const int64_t M = (int64_t)args.B * Tp;
+  if (m >= M) return;
+  const int64_t b = m / Tp;
+  const int t = (int)(m - b * Tp);
+  T* out = static_cast<T*>(args.xs) + m * d;
+  const T* gain = static_cast<const T*>(args.gain);
+  const IO* src = static_cast<const IO*>(args.x) + (b * T_len + (t < T_len ? t : 0)) * d;
+  float ss = 0.f;
+  for (int k = lane * 8; k < d; k += 64 * 8) {
+    float e[8];
+    if (t < T_len) {
+      load_io<IO, 8>(src + k, e);
     } else {
 #pragma unroll
-      for (int q = 0; q < PE; ++q) o[q] = cvt<T>(e[q]);
+      for (int q = 0; q < 8; ++q) e[q] = 0.f;
     }
-    return out;
-  };
-  auto load_b = [&](int row, int kp, int kt) -> u32x4 {
-    const int n = n0 + row;
-    const int k = kt * C::BK + kp * PE;
-    u32x4 z = {0u, 0u, 0u, 0u};
-    const T* w;
+#pragma unroll
+    for (int q = 0; q < 8; ++q) ss += e[q] * e[q];
+    if (gain) {
+      const Frag<T> g = load_frag<T>(gain + k);
+#pragma unroll
+      for (int q = 0; q < 8; ++q) e[q] *= tof<T>(g[q]);
+    }
+    Frag<T> hi;
+#pragma unroll
+    for (int q = 0; q < 8; ++q) hi[q] = cvt<T>(e[q]);
+    store_frag<T>(out + k, hi);
+    if constexpr (AS == 2) {
+      Frag<T> lo;
+#pragma unroll
+      for (int q = 0; q < 8; ++q) lo[q] = cvt<T>(e[q] - tof<T>(hi[q]));
+      store_frag<T>(out + M * d + k, lo);
+    }
+  }
+  ss = wave_sum(ss);
+  if (lane == 0) args.rinv[m] = t < T_len ? 1.0f / sqrtf(ss / (float)d + args.eps) : 0.f;
+}
+
+// ---------------------------------------------------------------------------
+// KP: [W_g; W_v; W_q; W_k] projection of the prepared rows + epilogue.
+// 1-D grid over (M_pad / BM) x ceil(N / BN) tiles, N = 2F + 2HD, M_pad = B * Tp.
+// ---------------------------------------------------------------------------
+template <typename T, typename IO>
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2)))
+void proj_kernel(ProjArgs args) {
+  using CF = ProjCfg<T>;
+  constexpr int PA = tile_chunks<CF, T>(CF::BM) / 4, PB = tile_chunks<CF, T>(CF::BN) / 4;
+  extern __shared__ __align__(16) unsigned char smem_raw[];
+  T* lds = reinterpret_cast<T*>(smem_raw);
+  float* rs = reinterpret_cast<float*>(smem_raw + main_bytes<CF, T>() - CF::BM * sizeof(float));
+
+  const int d = args.d, F = args.F, HD = args.HD, Tp = args.Tp;
+  const int N = 2 * F + 2 * HD;
+  const int64_t M = (int64_t)args.B * Tp;
+  const TilePos tp = tile_of(M / CF::BM, (int)ceil_div(N, CF::BN));
+  const int n0 = tp.n_tile * CF::BN;
+  const int64_t m0 = tp.m_tile * CF::BM;
+  const int64_t bseq = m0 / Tp;
+  const int t0 = (int)(m0 - bseq * Tp);   // position of the tile's first row
+  const int tid = threadIdx.x;
+
+  PartsSource<T, PA, CF::AS> sa;
+  sa.part_stride = M * d;
+#pragma unroll
+  for (int p = 0; p < PA; ++p) {
+    const PiecePos<CF, T> pp = piece_pos<CF, T>(tid, p);
+    sa.ptr[p] = static_cast<const T*>(args.xs) + (m0 + pp.row) * d + pp.kp * piece_elems<T>();
+  }
+  RowSource<T, PB> sb;
+#pragma unroll
+  for (int p = 0; p < PB; ++p) {
+    const PiecePos<CF, T> pp = piece_pos<CF, T>(tid, p);
+    const int n = n0 + pp.row;
+    const T* w = static_cast<const T*>(args.w_g);
     if (n < F) w = static_cast<const T*>(args.w_g) + (int64_t)n * d;
     else if (n < 2 * F) w = static_cast<const T*>(args.w_v) + (int64_t)(n - F) * d;
     else if (n < 2 * F + HD) w = static_cast<const T*>(args.w_q) + (int64_t)(n - 2 * F) * d;
     else if (n < N) w = static_cast<const T*>(args.w_k) + (int64_t)(n - 2 * F - HD) * d;
-    else return z;
-    return as_piece<T>(w + k);
-  };
-
-  f32x4 acc[C::BM / 32][C::BN / 32];
-#pragma unroll
-  for (int i = 0; i < C::BM / 32; ++i)
-#pragma unroll
-    for (int j = 0; j < C::BN / 32; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
-
-  gemm_mainloop<T>(acc, lds, d / C::BK, load_a, load_b);
-
-  // RMSNorm row scales: reduce the squares over the PR threads of each row.
-#pragma unroll
-  for (int p = 0; p < PA; ++p) {
-    float v = ssq[p];
-#pragma unroll
-    for (int off = 1; off < PR; off <<= 1) v += __shfl_xor(v, off, 64);
-    if (pcol == 0) rs[prow + p * RPP] = 1.0f / sqrtf(v / (float)d + args.eps);
+    sb.ptr[p] = w + pp.kp * piece_elems<T>();
+    sb.ok[p] = n < N;
   }
+
+  f32x4 acc[CF::IB][CF::JB];
+#pragma unroll
+  for (int i = 0; i < CF::IB; ++i)
+#pragma unroll
+    for (int j = 0; j < CF::JB; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  gemm_mainloop<CF, T>(acc, lds, d / CF::BK, sa, sb);
+
+  // RMSNorm row scales (the rows are distinct from the operand buffers)
+  if (tid < CF::BM) rs[tid] = args.rinv[m0 + tid];
   __syncthreads();
   float* Cs = reinterpret_cast<float*>(smem_raw);
-  acc_to_lds<T>(acc, Cs, rs);
-  __syncthreads();
 
-  // ---- epilogue ----
-  // gates: packed layout, 8 rows (one permuted 32-row group slot set) per item
-  if (n0 < F) {
-    T* gp = static_cast<T*>(args.gp);
-    constexpr int NRB = C::BM / 32;
-    for (int it = tid; it < NRB * 4 * C::BN; it += kThreads) {
-      const int c = it % C::BN, grp = (it / C::BN) & 3, rb = it / (4 * C::BN);
-      const int n = n0 + c;
-      if (n >= F) continue;
-      Frag<T> out;
+  const int dh = args.dh;
+  const int half = dh >> 1;                      // lanes per (row, head)
+  const int lane = tid & 63, wave = tid >> 6;
+  const int per_wave = 64 / half;                // (row, head) items per wave pass
+  const int sub = lane / half, cpair = lane % half;
+  // rotation of pair c at position i: angle i * base^(-2c/d_h), taken in
+  // revolutions in float64 and reduced to [-1/2, 1/2] before the float32
+  // sine and cosine (v_sin_f32 / v_cos_f32 take revolutions)
+  const bool has_qk = n0 + CF::BN > 2 * F;
+  const double rev_freq = has_qk && args.rope_base > 0.f
+      ? pow((double)args.rope_base, -2.0 * (double)cpair / (double)dh) * 0.15915494309189533577
+      : 0.0;
+
+  for (int pass = 0; pass < CF::BM / kEpiRows; ++pass) {
+    if (pass) __syncthreads();   // the previous pass is done with Cs
+    acc_to_lds<CF>(acc, Cs, rs, pass);
+    __syncthreads();
+    const int64_t mp = m0 + pass * kEpiRows;   // first row of this pass
+    const int tpos = t0 + pass * kEpiRows;     // its position in the sequence
+    constexpr int NRB = kEpiRows / 32;
+
+    // gates: packed layout, 8 rows (one permuted 32-row group slot set) per item
+    if (n0 < F) {
+      T* gp = static_cast<T*>(args.gp);
+      for (int it = tid; it < NRB * 4 * CF::BN; it += kThreads) {
+        const int c = it % CF::BN, grp = (it / CF::BN) & 3, rb = it / (4 * CF::BN);
+        const int n = n0 + c;
+        if (n >= F) continue;
+        Frag<T> out;
 #pragma unroll
-      for (int s = 0; s < 8; ++s) {
-        const float a = Cs[(rb * 32 + perm_slot(grp, s)) * kCStride + c];
-        out[s] = cvt<T>(a / (1.0f + __expf(-a)));
+        for (int s = 0; s < 8; ++s) {
+          const float a = Cs[(rb * 32 + perm_slot(grp, s)) * kCStride + c];
+          out[s] = cvt<T>(a * __builtin_amdgcn_rcpf(1.0f + __expf(-a)));
+        }
+        store_frag<T>(gp + packed_offset(mp / 32 + rb, grp, n, F), out);
       }
-      store_frag<T>(gp + packed_offset(m0 / 32 + rb, grp, n, F), out);
     }
-  }
-  // features: row-major [M_pad, F]
-  if (n0 + C::BN > F && n0 < 2 * F) {
-    T* v = static_cast<T*>(args.v);
-    constexpr int P8 = C::BN / 8;
-    for (int it = tid; it < C::BM * P8; it += kThreads) {
-      const int row = it / P8, c = (it % P8) * 8;
-      const int n = n0 + c;
-      if (n < F || n >= 2 * F) continue;
-      Frag<T> out;
+    // features: row-major [M_pad, F]
+    if (n0 + CF::BN > F && n0 < 2 * F) {
+      T* v = static_cast<T*>(args.v);
+      constexpr int P8 = CF::BN / 8;
+      for (int it = tid; it < kEpiRows * P8; it += kThreads) {
+        const int row = it / P8, c = (it % P8) * 8;
+        const int n = n0 + c;
+        if (n < F || n >= 2 * F) continue;
+        Frag<T> out;
 #pragma unroll
-      for (int s = 0; s < 8; ++s) out[s] = cvt<T>(Cs[row * kCStride + c + s]);
-      store_frag<T>(v + (m0 + row) * F + (n - F), out);
-    }
-  }
-  // queries and keys: RoPE on interleaved pairs, then unit length per head
-  if (n0 + C::BN > 2 * F) {
-    const int dh = args.dh;
-    const int half = dh >> 1;                      // lanes per (row, head)
-    const int lane = tid & 63, wave = tid >> 6;
-    const int per_wave = 64 / half;                // (row, head) items per wave pass
-    const int sub = lane / half, c = lane % half;
-    const int c_lo = n0 < 2 * F ? 2 * F - n0 : 0;  // first q/k column in tile
-    const int c_hi = min(C::BN, N - n0);
-    const int heads_in_tile = (c_hi - c_lo) / dh;
-    const int items = C::BM * heads_in_tile;
-    const double inv_freq = args.rope_base > 0.f
-        ? pow((double)args.rope_base, -2.0 * (double)c / (double)dh) : 0.0;
-    for (int base = wave * per_wave; base < items; base += 4 * per_wave) {
-      const int item = base + sub;
-      const bool ok = item < items;
-      const int row = ok ? item / heads_in_tile : 0;
-      const int hcol = c_lo + (ok ? item % heads_in_tile : 0) * dh;
-      float u0 = ok ? Cs[row * kCStride + hcol + 2 * c] : 0.f;
-      float u1 = ok ? Cs[row * kCStride + hcol + 2 * c + 1] : 0.f;
-      if (args.rope_base > 0.f) {
-        const int64_t pos = (m0 + row) % Tp;
-        double ang = (double)pos * inv_freq;
-        ang = fmod(ang, 6.283185307179586476925286766559);
-        double sn, cs;
-        sincos(ang, &sn, &cs);
-        const float fs = (float)sn, fc = (float)cs;
-        const float r0 = u0 * fc - u1 * fs, r1 = u0 * fs + u1 * fc;
-        u0 = r0;
-        u1 = r1;
+        for (int s = 0; s < 8; ++s) out[s] = cvt<T>(Cs[row * kCStride + c + s]);
+        store_frag<T>(v + (mp + row) * F + (n - F), out);
       }
-      float ss = u0 * u0 + u1 * u1;
-      for (int off = 1; off < half; off <<= 1) ss += __shfl_xor(ss, off, 64);
-      const float inv = 1.0f / fmaxf(sqrtf(ss), 1e-12f);
-      if (ok) {
-        const int n = n0 + hcol;
-        const bool is_q = n < 2 * F + HD;
-        const int e = is_q ? n - 2 * F : n - 2 * F - HD;   // column within q or k
-        T* dst = (is_q ? static_cast<T*>(args.qh) : static_cast<T*>(args.kh)) + (m0 + row) * HD + e;
-        const T w0 = cvt<T>(u0 * inv), w1 = cvt<T>(u1 * inv);
-        dst[2 * c] = w0;
-        dst[2 * c + 1] = w1;
-        if (args.fq) {
-          // WANGO features phi(sqrt(tau) u) ([TANGO] §2.2 eq. 8) of the stored
-          // unit vector: queries go out directly in the permuted feature order,
-          // keys back into the tile for the packed store below
-          const float st = sqrtf(__expf(fminf(args.theta[e / dh], 2.995732273553991f)));
-          const float isd = 1.0f / sqrtf((float)dh);
-          const float p0 = phi_feature(st * tof<T>(w0), isd), p1 = phi_feature(st * tof<T>(w1), isd);
-          if (is_q) {
-            T* fq = static_cast<T*>(args.fq) + (m0 + row) * HD + (e + 2 * c) / 32 * 32 +
-                    feature_slot((e + 2 * c) % 32);
-            fq[0] = cvt<T>(p0);
-            fq[1] = cvt<T>(p1);
-          } else {
-            Cs[row * kCStride + hcol + 2 * c] = p0;
-            Cs[row * kCStride + hcol + 2 * c + 1] = p1;
+    }
+    // queries and keys: RoPE on interleaved pairs, then unit length per head
+    if (has_qk) {
+      const int c_lo = n0 < 2 * F ? 2 * F - n0 : 0;  // first q/k column in tile
+      const int c_hi = min(CF::BN, N - n0);
+      const int heads_in_tile = (c_hi - c_lo) / dh;
+      const int items = kEpiRows * heads_in_tile;
+      for (int base = wave * per_wave; base < items; base += 4 * per_wave) {
+        const int item = base + sub;
+        const bool ok = item < items;
+        const int row = ok ? item / heads_in_tile : 0;
+        const int hcol = c_lo + (ok ? item % heads_in_tile : 0) * dh;
+        float u0 = ok ? Cs[row * kCStride + hcol + 2 * cpair] : 0.f;
+        float u1 = ok ? Cs[row * kCStride + hcol + 2 * cpair + 1] : 0.f;
+        if (args.rope_base > 0.f) {
+          const double rev = (double)(tpos + row) * rev_freq;
+          const float fr = (float)(rev - rint(rev));
+          const float fs = __builtin_amdgcn_sinf(fr), fc = __builtin_amdgcn_cosf(fr);
+          const float r0 = u0 * fc - u1 * fs, r1 = u0 * fs + u1 * fc;
+          u0 = r0;
+          u1 = r1;
+        }
+        float ss = u0 * u0 + u1 * u1;
+        for (int off = 1; off < half; off <<= 1) ss += __shfl_xor(ss, off, 64);
+        const float inv = 1.0f / fmaxf(sqrtf(ss), 1e-12f);
+        if (ok) {
+          const int n = n0 + hcol;
+          const bool is_q = n < 2 * F + HD;
+          const int e = is_q ? n - 2 * F : n - 2 * F - HD;   // column within q or k
+          T* dst = (is_q ? static_cast<T*>(args.qh) : static_cast<T*>(args.kh)) + (mp + row) * HD + e;
+          const T w0 = cvt<T>(u0 * inv), w1 = cvt<T>(u1 * inv);
+          dst[2 * cpair] = w0;
+          dst[2 * cpair + 1] = w1;
+          if (args.fq) {
+            // WANGO features phi(sqrt(tau) u) ([TANGO] §2.2 eq. 8) of the stored
+            // unit vector: queries go out directly in the permuted feature order,
+            // keys back into the tile for the packed store below
+            const float st = sqrtf(__expf(fminf(args.theta[e / dh], 2.995732273553991f)));
+            const float isd = 1.0f / sqrtf((float)dh);
+            const float p0 = phi_feature(st * tof<T>(w0), isd), p1 = phi_feature(st * tof<T>(w1), isd);
+            if (is_q) {
+              T* fq = static_cast<T*>(args.fq) + (mp + row) * HD + (e + 2 * cpair) / 32 * 32 +
+                      feature_slot((e + 2 * cpair) % 32);
+              fq[0] = cvt<T>(p0);
+              fq[1] = cvt<T>(p1);
+            } else {
+              Cs[row * kCStride + hcol + 2 * cpair] = p0;
+              Cs[row * kCStride + hcol + 2 * cpair + 1] = p1;
+            }
           }
         }
       }
-    }
-    if (args.fk) {
-      // key features in the source-packed layout, as the gates
-      __syncthreads();
-      const int k_lo = max(c_lo, 2 * F + HD - n0);
-      if (k_lo < c_hi) {
-        T* fk = static_cast<T*>(args.fk);
-        constexpr int NRB = C::BM / 32;
-        const int ncols = c_hi - k_lo;
-        for (int it = tid; it < NRB * 4 * ncols; it += kThreads) {
-          const int c2 = k_lo + it % ncols, grp = (it / ncols) & 3, rb = it / (4 * ncols);
-          Frag<T> out;
+      if (args.fk) {
+        // key features in the source-packed layout, as the gates
+        __syncthreads();
+        const int k_lo = max(c_lo, 2 * F + HD - n0);
+        if (k_lo < c_hi) {
+          T* fk = static_cast<T*>(args.fk);
+          const int ncols = c_hi - k_lo;
+          for (int it = tid; it < NRB * 4 * ncols; it += kThreads) {
+            const int c2 = k_lo + it % ncols, grp = (it / ncols) & 3, rb = it / (4 * ncols);
+            Frag<T> out;
 #pragma unroll
-          for (int s2 = 0; s2 < 8; ++s2) out[s2] = cvt<T>(Cs[(rb * 32 + perm_slot(grp, s2)) * kCStride + c2]);
-          store_frag<T>(fk + packed_offset(m0 / 32 + rb, grp, n0 + c2 - 2 * F - HD, HD), out);
+            for (int s2 = 0; s2 < 8; ++s2)
+              out[s2] = cvt<T>(Cs[(rb * 32 + perm_slot(grp, s2)) * kCStride + c2]);
+            store_frag<T>(fk + packed_offset(mp / 32 + rb, grp, n0 + c2 - 2 * F - HD, HD), out);
+          }
         }
       }
     }
@@ -367,65 +609,65 @@ __global__ __launch_bounds__(kThreads) void proj_kernel(ProjArgs args) {
 }
 
 // ---------------------------------------------------------------------------
-// KO: out = x + (gbar * v) W_o^T.  Grid: (d/BN, M_pad/BM).
+// KO: out = x + (gbar * v) W_o^T.  1-D grid over (M_pad / BM) x (d / BN) tiles.
 // ---------------------------------------------------------------------------
 template <typename T, typename IO>
 __global__ __launch_bounds__(kThreads) void out_kernel(OutArgs args) {
-  using C = GemmCfg<T>;
-  constexpr int PE = piece_elems<T>();
+  using CF = OutCfg<T>;
+  constexpr int PA = tile_chunks<CF, T>(CF::BM) / 4, PB = tile_chunks<CF, T>(CF::BN) / 4;
   extern __shared__ __align__(16) unsigned char smem_raw[];
   T* lds = reinterpret_cast<T*>(smem_raw);
   const int d = args.d, F = args.F, T_len = args.T, Tp = args.Tp;
-  const int n0 = blockIdx.x * C::BN;
-  const int64_t m0 = (int64_t)blockIdx.y * C::BM;
-  const T* __restrict__ gbar = static_cast<const T*>(args.gbar);
-  const T* __restrict__ v = static_cast<const T*>(args.v);
-  const T* __restrict__ wo = static_cast<const T*>(args.w_o);
+  const TilePos tp = tile_of((int64_t)args.B * Tp / CF::BM, d / CF::BN);
+  const int n0 = tp.n_tile * CF::BN;
+  const int64_t m0 = tp.m_tile * CF::BM;
+  const int64_t bseq = m0 / Tp;
+  const int t0 = (int)(m0 - bseq * Tp);
+  const int tid = threadIdx.x;
 
-  auto load_a = [&](int, int row, int kp, int kt) -> u32x4 {
-    const int64_t m = m0 + row;
-    const int k = kt * C::BK + kp * PE;
-    u32x4 ga = as_piece<T>(gbar + m * F + k);
-    u32x4 va = as_piece<T>(v + m * F + k);
-    const T* ge = reinterpret_cast<const T*>(&ga);
-    const T* ve = reinterpret_cast<const T*>(&va);
-    u32x4 out;
-    T* o = reinterpret_cast<T*>(&out);
+  GatedSource<T, PA, CF::AS> sa;
 #pragma unroll
-    for (int q = 0; q < PE; ++q) o[q] = cvt<T>(tof<T>(ge[q]) * tof<T>(ve[q]));
-    return out;
-  };
-  auto load_b = [&](int row, int kp, int kt) -> u32x4 {
-    const int k = kt * C::BK + kp * PE;
-    return as_piece<T>(wo + (int64_t)(n0 + row) * F + k);
-  };
+  for (int p = 0; p < PA; ++p) {
+    const PiecePos<CF, T> pp = piece_pos<CF, T>(tid, p);
+    const int64_t off = (m0 + pp.row) * F + pp.kp * piece_elems<T>();
+    sa.gptr[p] = static_cast<const T*>(args.gbar) + off;
+    sa.vptr[p] = static_cast<const T*>(args.v) + off;
+  }
+  RowSource<T, PB> sb;
+#pragma unroll
+  for (int p = 0; p < PB; ++p) {
+    const PiecePos<CF, T> pp = piece_pos<CF, T>(tid, p);
+    sb.ptr[p] = static_cast<const T*>(args.w_o) + (int64_t)(n0 + pp.row) * F + pp.kp * piece_elems<T>();
+    sb.ok[p] = true;
+  }
 
-  f32x4 acc[C::BM / 32][C::BN / 32];
+  f32x4 acc[CF::IB][CF::JB];
 #pragma unroll
-  for (int i = 0; i < C::BM / 32; ++i)
+  for (int i = 0; i < CF::IB; ++i)
 #pragma unroll
-    for (int j = 0; j < C::BN / 32; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int j = 0; j < CF::JB; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  gemm_mainloop<T>(acc, lds, F / C::BK, load_a, load_b);
+  gemm_mainloop<CF, T>(acc, lds, F / CF::BK, sa, sb);
 
   float* Cs = reinterpret_cast<float*>(smem_raw);
-  acc_to_lds<T>(acc, Cs, nullptr);
-  __syncthreads();
-
   const IO* __restrict__ x = static_cast<const IO*>(args.x);
   IO* out = static_cast<IO*>(args.out);
-  constexpr int P8 = C::BN / 8;
-  for (int it = threadIdx.x; it < C::BM * P8; it += kThreads) {
-    const int row = it / P8, c = (it % P8) * 8;
-    const int64_t m = m0 + row;
-    const int64_t b = m / Tp, t = m % Tp;
-    if (t >= T_len) continue;
-    const int64_t off = (b * T_len + t) * d + n0 + c;
-    float o[8];
-    load_io<IO, 8>(x + off, o);
+  constexpr int P8 = CF::BN / 8;
+  for (int pass = 0; pass < CF::BM / kEpiRows; ++pass) {
+    if (pass) __syncthreads();   // the previous pass is done with Cs
+    acc_to_lds<CF>(acc, Cs, nullptr, pass);
+    __syncthreads();
+    for (int it = tid; it < kEpiRows * P8; it += kThreads) {
+      const int row = it / P8, c = (it % P8) * 8;
+      const int t = t0 + pass * kEpiRows + row;
+      if (t >= T_len) continue;
+      const int64_t off = (bseq * T_len + t) * d + n0 + c;
+      float o[8];
+      load_io<IO, 8>(x + off, o);
 #pragma unroll
-    for (int s = 0; s < 8; ++s) o[s] += Cs[row * kCStride + c + s];
-    store_io<IO, 8>(out + off, o);
+      for (int s = 0; s < 8; ++s) o[s] += Cs[row * kCStride + c + s];
+      store_io<IO, 8>(out + off, o);
+    }
   }
 }
 
@@ -434,18 +676,25 @@ __global__ __launch_bounds__(kThreads) void out_kernel(OutArgs args) {
 // ---------------------------------------------------------------------------
 template <typename T, typename IO>
 hipError_t launch_proj_t(const ProjArgs& a, hipStream_t s) {
-  using C = GemmCfg<T>;
+  using CF = ProjCfg<T>;
+  const int64_t M = (int64_t)a.B * a.Tp;
+  hipLaunchKernelGGL((prep_kernel<T, IO, CF::AS>), dim3((unsigned)(M / (kThreads / 64))), dim3(kThreads),
+                     0, s, a);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
   const int N = 2 * a.F + 2 * a.HD;
-  dim3 grid((unsigned)ceil_div(N, C::BN), (unsigned)((int64_t)a.B * a.Tp / C::BM));
-  hipLaunchKernelGGL((proj_kernel<T, IO>), grid, dim3(kThreads), gemm_lds_bytes<T>(), s, a);
+  const int64_t tiles = (M / CF::BM) * ceil_div(N, CF::BN);
+  const size_t lds = main_bytes<CF, T>();
+  hipLaunchKernelGGL((proj_kernel<T, IO>), dim3((unsigned)tiles), dim3(kThreads), lds, s, a);
   return hipGetLastError();
 }
 
 template <typename T, typename IO>
 hipError_t launch_out_t(const OutArgs& a, hipStream_t s) {
-  using C = GemmCfg<T>;
-  dim3 grid((unsigned)(a.d / C::BN), (unsigned)((int64_t)a.B * a.Tp / C::BM));
-  hipLaunchKernelGGL((out_kernel<T, IO>), grid, dim3(kThreads), gemm_lds_bytes<T>(), s, a);
+  using CF = OutCfg<T>;
+  const int64_t tiles = ((int64_t)a.B * a.Tp / CF::BM) * (a.d / CF::BN);
+  const size_t lds = main_bytes<CF, T>();
+  hipLaunchKernelGGL((out_kernel<T, IO>), dim3((unsigned)tiles), dim3(kThreads), lds, s, a);
   return hipGetLastError();
 }
 
@@ -458,6 +707,11 @@ hipError_t launch_out(const OutArgs& a, bool bf, bool io_bf, hipStream_t s) {
   return io_bf ? launch_out_t<float, bf16>(a, s) : launch_out_t<float, float>(a, s);
 }
 
+size_t proj_parts_bytes(int64_t rows, int d, bool bf) {
+  const size_t per = bf ? (size_t)ProjCfg<bf16>::AS * sizeof(bf16) : (size_t)ProjCfg<float>::AS * sizeof(float);
+  return per * rows * d;
+}
+
 namespace {
 template <typename K> hipError_t raise_lds(K* k, size_t bytes) {
   return hipFuncSetAttribute(reinterpret_cast<const void*>(k), hipFuncAttributeMaxDynamicSharedMemorySize,
@@ -467,12 +721,16 @@ template <typename K> hipError_t raise_lds(K* k, size_t bytes) {
 
 hipError_t gemm_kernels_init() {
   hipError_t e;
-#define TANGO_RAISE(K, T) \
-  if ((e = raise_lds(&K, gemm_lds_bytes<T>())) != hipSuccess) return e;
-  TANGO_RAISE((proj_kernel<bf16, bf16>), bf16) TANGO_RAISE((proj_kernel<bf16, float>), bf16)
-  TANGO_RAISE((proj_kernel<float, bf16>), float) TANGO_RAISE((proj_kernel<float, float>), float)
-  TANGO_RAISE((out_kernel<bf16, bf16>), bf16) TANGO_RAISE((out_kernel<bf16, float>), bf16)
-  TANGO_RAISE((out_kernel<float, bf16>), float) TANGO_RAISE((out_kernel<float, float>), float)
+#define TANGO_RAISE(K, BYTES) \
+  if ((e = raise_lds(&K, BYTES)) != hipSuccess) return e;
+  TANGO_RAISE((proj_kernel<bf16, bf16>), (main_bytes<ProjCfg<bf16>, bf16>()))
+  TANGO_RAISE((proj_kernel<bf16, float>), (main_bytes<ProjCfg<bf16>, bf16>()))
+  TANGO_RAISE((proj_kernel<float, bf16>), (main_bytes<ProjCfg<float>, float>()))
+  TANGO_RAISE((proj_kernel<float, float>), (main_bytes<ProjCfg<float>, float>()))
+  TANGO_RAISE((out_kernel<bf16, bf16>), (main_bytes<OutCfg<bf16>, bf16>()))
+  TANGO_RAISE((out_kernel<bf16, float>), (main_bytes<OutCfg<bf16>, bf16>()))
+  TANGO_RAISE((out_kernel<float, bf16>), (main_bytes<OutCfg<float>, float>()))
+  TANGO_RAISE((out_kernel<float, float>), (main_bytes<OutCfg<float>, float>()))
 #undef TANGO_RAISE
   return hipSuccess;
 }

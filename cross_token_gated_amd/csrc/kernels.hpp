@@ -25,9 +25,14 @@ struct ProjArgs {
   void* fq;            // WANGO only (else null): phi(sqrt(tau) q) [B*Tp, HD], permuted feature order
   void* fk;            // WANGO only (else null): phi(sqrt(tau) k), source-packed [B*Tp/32][4][HD][8]
   const float* theta;  // [H], for the WANGO features
+  void* xs;            // scratch: [parts][B*Tp, d] parts of h * gain (padded rows zero)
+  float* rinv;         // scratch: [B*Tp] RMSNorm row scales
   int B, T, Tp, d, F, HD, dh;
   float rope_base, eps;
 };
+
+// Bytes of the operand parts xs for `rows` padded rows of width d.
+size_t proj_parts_bytes(int64_t rows, int d, bool bf);
 
 struct OutArgs {
   const void* x;       // [B, T, d] in the I/O dtype

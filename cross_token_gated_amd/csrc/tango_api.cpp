@@ -133,6 +133,7 @@ int check_ranges(const Range* ins, int nin, const Range* outs, int nout, const v
 
 struct Layout {
   size_t gp, v, qh, kh, gbar;           // offsets
+  size_t xs, rinv;                      // projection input parts, RMSNorm scales
   size_t fq, fk;                        // WANGO features
   size_t part, part_den, counters;      // TANGO split scratch
   size_t n_old, z_old, seg_state, seg_z;
@@ -158,6 +159,8 @@ Layout make_layout(const tango_shape_t* s, bool wango, int32_t window, int32_t c
   L.kh = take(M * HD * es);
   L.gbar = take(M * F * es);
   const bool bf = s->dtype == TANGO_BF16;
+  L.xs = take(proj_parts_bytes(M, s->d_model, bf));
+  L.rinv = take(M * sizeof(float));
   if (!wango) {
     L.agg = tango_agg_plan(s->batch, (int)pad_rows(s->seq_len), s->d_gate, s->n_heads, bf);
     const int64_t n = L.agg.n_split_tiles;
@@ -297,6 +300,56 @@ int guarded(Fn fn) {
   }
 }
 
+// Scratch of the projection stage calls: input parts at offset 0, then the
+// row scales.
+struct ProjScratch {
+  size_t rinv, total;
+};
+ProjScratch proj_scratch(const tango_shape_t* s) {
+  const int64_t M = (int64_t)s->batch * pad_rows(s->seq_len);
+  ProjScratch p{};
+  p.rinv = align256(proj_parts_bytes(M, s->d_model, s->dtype == TANGO_BF16));
+  p.total = p.rinv + M * sizeof(float);
+  return p;
+}
+
+// Projection stage (fq, fk non-null: the WANGO features too).
+int stage_proj_common(const tango_shape_t* s, const tango_weights_t* weights, const void* x, void* gp,
+                      void* v, void* qh, void* kh, void* fq, void* fk, void* ws, size_t ws_bytes,
+                      void* stream) {
+  int rc = check_shape(s);
+  if (rc) return rc;
+  if ((rc = check_weights(weights, true))) return rc;
+  if (!x || !gp || !v || !qh || !kh || !ws) return fail(TANGO_ERR_NULL, "a buffer pointer is NULL");
+  const ProjScratch ps = proj_scratch(s);
+  if (ws_bytes < ps.total)
+    return fail(TANGO_ERR_WORKSPACE, "workspace of %zu bytes is smaller than the %zu needed", ws_bytes,
+                ps.total);
+  const bool wango = fq != nullptr;
+  const size_t es = elem_size(s->dtype), M = (size_t)s->batch * pad_rows(s->seq_len);
+  const size_t d = s->d_model, F = s->d_gate, HD = (size_t)s->n_heads * s->head_dim;
+  const Range ins[] = {{x, (size_t)s->batch * s->seq_len * d * elem_size(s->io_dtype), "x"},
+                       {weights->w_g, F * d * es, "w_g"},
+                       {weights->w_v, F * d * es, "w_v"},
+                       {weights->w_q, HD * d * es, "w_q"},
+                       {weights->w_k, HD * d * es, "w_k"},
+                       {weights->rms_gain, d * es, "rms_gain"},
+                       {wango ? weights->theta : nullptr, s->n_heads * sizeof(float), "theta"}};
+  const Range outs[] = {{gp, M * F * es, "gp"}, {v, M * F * es, "v"}, {qh, M * HD * es, "qh"},
+                        {kh, M * HD * es, "kh"}, {ws, ps.total, "workspace"},
+                        {fq, M * HD * es, "fq"}, {fk, M * HD * es, "fk"}};
+  if ((rc = check_ranges(ins, 7, outs, wango ? 7 : 5, nullptr, nullptr))) return rc;
+  if ((rc = ensure_init())) return rc;
+  ProjArgs pa = proj_args(s, weights, x, gp, v, qh, kh);
+  pa.xs = ws;
+  pa.rinv = reinterpret_cast<float*>(static_cast<char*>(ws) + ps.rinv);
+  pa.fq = fq;
+  pa.fk = fk;
+  hipError_t e = launch_proj(pa, s->dtype == TANGO_BF16, s->io_dtype == TANGO_BF16,
+                             static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? ok() : hip_fail(e, "projection kernel");
+}
+
 int block_common(const tango_shape_t* s, const tango_weights_t* w, bool wango, int32_t window,
                  int32_t phi_dim, int32_t chunk, const void* x, void* out, void* ws, size_t ws_bytes,
                  void* stream) {
@@ -336,6 +389,8 @@ int block_common(const tango_shape_t* s, const tango_weights_t* w, bool wango, i
   void* gbar = base + L.gbar;
   const bool io_bf = s->io_dtype == TANGO_BF16;
   ProjArgs pa = proj_args(s, w, x, gp, v, qh, kh);
+  pa.xs = base + L.xs;
+  pa.rinv = reinterpret_cast<float*>(base + L.rinv);
   if (wango) {
     pa.fq = base + L.fq;
     pa.fk = base + L.fk;
@@ -418,29 +473,17 @@ const char* tango_last_error(void) { return g_last_error.c_str(); }
 
 int tango_version(void) { return TANGO_ABI_VERSION; }
 
+size_t tango_proj_workspace_size(const tango_shape_t* shape) {
+  if (check_shape(shape)) return 0;
+  return proj_scratch(shape).total;
+}
+
 int tango_stage_proj(const tango_shape_t* shape, const tango_weights_t* weights, const void* x, void* gp,
-                     void* v, void* qh, void* kh, void* hip_stream) {
+                     void* v, void* qh, void* kh, void* workspace, size_t workspace_bytes,
+                     void* hip_stream) {
   return guarded([&] {
-    int rc = check_shape(shape);
-    if (rc) return rc;
-    if ((rc = check_weights(weights, true))) return rc;
-    if (!x || !gp || !v || !qh || !kh) return fail(TANGO_ERR_NULL, "a buffer pointer is NULL");
-    const tango_shape_t* s = shape;
-    const size_t es = elem_size(s->dtype), M = (size_t)s->batch * pad_rows(s->seq_len);
-    const size_t d = s->d_model, F = s->d_gate, HD = (size_t)s->n_heads * s->head_dim;
-    const Range ins[] = {{x, (size_t)s->batch * s->seq_len * d * elem_size(s->io_dtype), "x"},
-                         {weights->w_g, F * d * es, "w_g"},
-                         {weights->w_v, F * d * es, "w_v"},
-                         {weights->w_q, HD * d * es, "w_q"},
-                         {weights->w_k, HD * d * es, "w_k"},
-                         {weights->rms_gain, d * es, "rms_gain"}};
-    const Range outs[] = {{gp, M * F * es, "gp"}, {v, M * F * es, "v"}, {qh, M * HD * es, "qh"},
-                          {kh, M * HD * es, "kh"}};
-    if ((rc = check_ranges(ins, 6, outs, 4, nullptr, nullptr))) return rc;
-    if ((rc = ensure_init())) return rc;
-    hipError_t e = launch_proj(proj_args(s, weights, x, gp, v, qh, kh), s->dtype == TANGO_BF16,
-                               s->io_dtype == TANGO_BF16, static_cast<hipStream_t>(hip_stream));
-    return e == hipSuccess ? ok() : hip_fail(e, "projection kernel");
+    return stage_proj_common(shape, weights, x, gp, v, qh, kh, nullptr, nullptr, workspace,
+                             workspace_bytes, hip_stream);
   });
 }
 
@@ -497,32 +540,12 @@ int tango_stage_out(const tango_shape_t* shape, const void* w_o, const void* x, 
 }
 
 int wango_stage_proj(const tango_shape_t* shape, const tango_weights_t* weights, const void* x, void* gp,
-                     void* v, void* qh, void* kh, void* fq, void* fk, void* hip_stream) {
+                     void* v, void* qh, void* kh, void* fq, void* fk, void* workspace,
+                     size_t workspace_bytes, void* hip_stream) {
   return guarded([&] {
-    int rc = check_shape(shape);
-    if (rc) return rc;
-    if ((rc = check_weights(weights, true))) return rc;
-    if (!x || !gp || !v || !qh || !kh || !fq || !fk) return fail(TANGO_ERR_NULL, "a buffer pointer is NULL");
-    const tango_shape_t* s = shape;
-    const size_t es = elem_size(s->dtype), M = (size_t)s->batch * pad_rows(s->seq_len);
-    const size_t d = s->d_model, F = s->d_gate, HD = (size_t)s->n_heads * s->head_dim;
-    const Range ins[] = {{x, (size_t)s->batch * s->seq_len * d * elem_size(s->io_dtype), "x"},
-                         {weights->w_g, F * d * es, "w_g"},
-                         {weights->w_v, F * d * es, "w_v"},
-                         {weights->w_q, HD * d * es, "w_q"},
-                         {weights->w_k, HD * d * es, "w_k"},
-                         {weights->rms_gain, d * es, "rms_gain"},
-                         {weights->theta, s->n_heads * sizeof(float), "theta"}};
-    const Range outs[] = {{gp, M * F * es, "gp"}, {v, M * F * es, "v"}, {qh, M * HD * es, "qh"},
-                          {kh, M * HD * es, "kh"}, {fq, M * HD * es, "fq"}, {fk, M * HD * es, "fk"}};
-    if ((rc = check_ranges(ins, 7, outs, 6, nullptr, nullptr))) return rc;
-    if ((rc = ensure_init())) return rc;
-    ProjArgs pa = proj_args(s, weights, x, gp, v, qh, kh);
-    pa.fq = fq;
-    pa.fk = fk;
-    hipError_t e = launch_proj(pa, s->dtype == TANGO_BF16, s->io_dtype == TANGO_BF16,
-                               static_cast<hipStream_t>(hip_stream));
-    return e == hipSuccess ? ok() : hip_fail(e, "projection kernel");
+    if (!fq || !fk) return fail(TANGO_ERR_NULL, "a buffer pointer is NULL");
+    return stage_proj_common(shape, weights, x, gp, v, qh, kh, fq, fk, workspace, workspace_bytes,
+                             hip_stream);
   });
 }
 

@@ -60,7 +60,7 @@
 extern "C" {
 #endif
 
-#define TANGO_ABI_VERSION 1
+#define TANGO_ABI_VERSION 2
 
 typedef enum { TANGO_F32 = 0, TANGO_BF16 = 1 } tango_dtype_t;
 
@@ -167,16 +167,23 @@ int tango_version(void);                      /* TANGO_ABI_VERSION              
  * stage adds the older sources c_i <= j <= i - window pairwise.
  */
 
+/* Bytes of scratch the projection stages need for `shape` (the RMSNorm row
+ * scales and the dtype parts of the normalised input rows); 0 if the shape is
+ * invalid. */
+size_t tango_proj_workspace_size(const tango_shape_t* shape);
+
 /* TANGO projections ([TANGO] §2.1 eq. 2 and the head paragraph): RMSNorm,
- * SiLU gate (packed), features, RoPE + unit-norm queries and keys. */
+ * SiLU gate (packed), features, RoPE + unit-norm queries and keys.  workspace:
+ * at least tango_proj_workspace_size(shape) bytes of scratch. */
 int tango_stage_proj(const tango_shape_t* shape, const tango_weights_t* weights,
-                     const void* x, void* gp, void* v, void* qh, void* kh, void* hip_stream);
+                     const void* x, void* gp, void* v, void* qh, void* kh, void* workspace,
+                     size_t workspace_bytes, void* hip_stream);
 
 /* WANGO projections: as tango_stage_proj, plus the features fq, fk of eq. 8
  * (needs weights->theta). */
 int wango_stage_proj(const tango_shape_t* shape, const tango_weights_t* weights,
                      const void* x, void* gp, void* v, void* qh, void* kh, void* fq, void* fk,
-                     void* hip_stream);
+                     void* workspace, size_t workspace_bytes, void* hip_stream);
 
 /* TANGO aggregation ([TANGO] eqs. 4-6): gbar from qh, kh, gp.  Needs the same
  * workspace as tango_block_fwd (it uses the split-sum scratch area). */

@@ -37,7 +37,8 @@ def test_header_and_binding_agree():
 def test_library_exports_every_declared_symbol(lib):
     for name in header_functions():
         assert hasattr(lib, name), name
-    assert lib.tango_version() == 1
+    version = int(re.search(r"#define TANGO_ABI_VERSION (\d+)", open(HEADER).read()).group(1))
+    assert lib.tango_version() == version
     for code in range(-8, 1):
         assert lib.tango_status_string(code).decode().startswith(_lib.STATUS[code])
 
@@ -141,10 +142,17 @@ def test_workspace_sizes_cover_the_layout(lib):
 def test_stage_entry_points_validate(lib):
     s = shape()
     w = weights()
-    assert lib.tango_stage_proj(ctypes.byref(s), ctypes.byref(w), None, FAKE, FAKE, FAKE, FAKE, None) == -1
+    assert lib.tango_stage_proj(ctypes.byref(s), ctypes.byref(w), None, FAKE, FAKE, FAKE, FAKE, FAKE,
+                                1 << 40, None) == -1
+    n = lib.tango_proj_workspace_size(ctypes.byref(s))
+    assert n > 0
+    assert lib.tango_stage_proj(ctypes.byref(s), ctypes.byref(w), FAKE, FAKE + 0x1000000,
+                                FAKE + 0x2000000, FAKE + 0x3000000, FAKE + 0x4000000,
+                                FAKE + 0x5000000, n - 1, None) == -6
     assert lib.tango_stage_aggregate(ctypes.byref(s), FAKE, None, FAKE, FAKE, FAKE, FAKE, FAKE, 0, None) == -6
     assert lib.tango_stage_out(ctypes.byref(shape(dtype=3)), FAKE, FAKE, FAKE, FAKE, FAKE, None) == -3
-    assert lib.wango_stage_proj(ctypes.byref(s), ctypes.byref(w), FAKE, FAKE, FAKE, FAKE, FAKE, None, FAKE, None) == -1
+    assert lib.wango_stage_proj(ctypes.byref(s), ctypes.byref(w), FAKE, FAKE, FAKE, FAKE, FAKE, None, FAKE,
+                                FAKE, 1 << 40, None) == -1
     assert lib.wango_stage_scan(ctypes.byref(s), 0, 128, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 0, None) == -2
     assert lib.wango_stage_scan(ctypes.byref(s), 256, 96, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 0, None) == -5
     assert lib.wango_stage_band(ctypes.byref(s), FAKE, None, 0, 128, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None) == -2

@@ -78,8 +78,10 @@ def test_stage_proj(case, with_gain):
     v = torch.full((M, F), float("nan"), dtype=dt, device="cuda:0")
     qh = torch.full((M, HD), float("nan"), dtype=dt, device="cuda:0")
     kh = torch.full((M, HD), float("nan"), dtype=dt, device="cuda:0")
+    ws = api.workspace(api.tango_proj_workspace_size(shape), "cuda:0")
+    ws.fill_(0xFF)   # scratch contents must not matter
     announce(f"stage_proj {case} gain={with_gain}")
-    api.tango_stage_proj(shape, bw, x, gp, v, qh, kh)
+    api.tango_stage_proj(shape, bw, x, gp, v, qh, kh, ws=ws)
     torch.cuda.synchronize()
     g_got = H.unpad_rows(H.unpack_gates(host(gp), M, F), w.B, w.T)
     v_got = H.unpad_rows(host(v), w.B, w.T)

@@ -63,17 +63,36 @@ struct Job {
   int64_t split_id;
 };
 
+// LDS operand layout.  The key block (BC sources x DH) and the weights
+// (BR destinations x BC sources) are MFMA operands read by every wave.  A
+// block of 16 rows x 32 k is stored as 256-byte regions, one per (chunk h,
+// k group g) with g covering k = 8g .. 8g + 7 in the order of the fragment's
+// slots (PPF chunks of 16 bytes per fragment: 1 for bf16, 2 for float32);
+// row r of the block sits at position (r + 4g) mod 16 of its region.  Each
+// group of 16 lanes of an MFMA fragment read then covers one region, and a
+// loader whose four consecutive lanes fetch 64 contiguous bytes of one row
+// writes 16 distinct positions: both at the full gfx950 LDS width.
+template <typename T> constexpr int frag_chunks() { return (int)sizeof(T) / 2; }
+__device__ __forceinline__ int region_pos(int region, int r, int g) {
+  return region * 256 + ((r + 4 * g) & 15) * 16;
+}
+
 template <typename T, int DH> struct AggLds {
   static constexpr int BR = AggCfg<T>::BR;
-  static constexpr int KSTR = DH + 16 / (int)sizeof(T);    // row stride of a key block
-  static constexpr int PSTR = BC + 16 / (int)sizeof(T);    // row stride of the weights
-  T ks[2][BC * KSTR];
-  T ps[2][BR * PSTR];
+  T ks[2][BC * DH];   // key blocks, region layout (16-source block jj, k block, chunk, group)
+  T ps[2][BR * BC];   // weights, region layout (16-destination block, 32-source half, chunk, group)
   float den[kWaves][BR];
   int flag;
 };
 
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+// Index of accumulator element r of 16 x 16 block blk, lane `lane`, in a
+// partial: element-major within a block, so each store instruction writes
+// 256 contiguous bytes.
+__device__ __forceinline__ int64_t part_index(int blk, int r, int lane) {
+  return ((int64_t)blk * 4 + r) * 64 + lane;
+}
 
 template <typename T, int MODE, int DH, int WCOLS>
 __global__ __launch_bounds__(kAggThreads) void agg_kernel(AggArgs a, int nfc, int rtiles,
@@ -85,12 +104,11 @@ __global__ __launch_bounds__(kAggThreads) void agg_kernel(AggArgs a, int nfc, in
   constexpr int KS = DH / 32;
   constexpr int SPT = BR / BC;                    // source steps per destination tile
   using L = AggLds<T, DH>;
-  constexpr int KSTR = L::KSTR, PSTR = L::PSTR;
   constexpr int PE = 16 / (int)sizeof(T);        // elements per 16-byte piece
-  constexpr int KPIECES = BC * DH / PE;           // 16-byte pieces of a key block
-  constexpr int KPT = (KPIECES + kAggThreads - 1) / kAggThreads;   // per thread (last may be idle)
-  static_assert(KPIECES % kAggThreads == 0 || KPIECES < kAggThreads, "key block pieces");
-  static_assert(JBW >= 1, "tile shape");
+  constexpr int PPF = frag_chunks<T>();
+  constexpr int KCH = (BC / 16) * KS * PPF;       // 64-piece chunks of a key block
+  constexpr int KPT = (KCH + kWaves - 1) / kWaves;   // per wave (the last may be partial)
+  static_assert(JBW >= 2 && JBW % 2 == 0, "tile shape");
   __shared__ L sm;
 
   const int tid = threadIdx.x, lane = tid & 63;
@@ -167,23 +185,44 @@ __global__ __launch_bounds__(kAggThreads) void agg_kernel(AggArgs a, int nfc, in
   const T* __restrict__ gp = static_cast<const T*>(a.gp);
   T* __restrict__ gbar = static_cast<T*>(a.gbar);
 
-  // key block jb -> registers (this thread's pieces) -> LDS buffer
+  // key block jb -> registers -> LDS buffer.  Chunk c = wave + kWaves p of
+  // the block (16-source block jj, k block kb, chunk ch); lane l fetches row
+  // l / 4 and k group l % 4 of it.
+  auto key_chunk = [&](int p, int& row, int& col, int& off) {
+    const int c = wave + kWaves * p;
+    const int jj = c / (KS * PPF), kb = (c / PPF) % KS, ch = c % PPF;
+    const int r = lane >> 2, g = lane & 3;
+    row = jj * 16 + r;
+    col = kb * 32 + g * 8 + ch * PE;
+    off = region_pos(((jj * KS + kb) * PPF + ch) * 4 + g, r, g);
+  };
   auto key_fetch = [&](int jb, u32x4 (&kr)[KPT]) {
 #pragma unroll
     for (int p = 0; p < KPT; ++p) {
-      const int piece = tid + p * kAggThreads;
-      if (KPIECES % kAggThreads != 0 && piece >= KPIECES) break;
-      const int row = piece / (DH / PE), c = (piece % (DH / PE)) * PE;
-      kr[p] = *reinterpret_cast<const u32x4*>(kh + (mseq + (int64_t)jb * BC + row) * HD + h * DH + c);
+      if (KCH % kWaves != 0 && wave + kWaves * p >= KCH) break;   // wave-uniform
+      int row, col, off;
+      key_chunk(p, row, col, off);
+      kr[p] = *reinterpret_cast<const u32x4*>(kh + (mseq + (int64_t)jb * BC + row) * HD + h * DH + col);
     }
   };
   auto key_stash = [&](int buf, const u32x4 (&kr)[KPT]) {
 #pragma unroll
     for (int p = 0; p < KPT; ++p) {
-      const int piece = tid + p * kAggThreads;
-      if (KPIECES % kAggThreads != 0 && piece >= KPIECES) break;
-      const int row = piece / (DH / PE), c = (piece % (DH / PE)) * PE;
-      *reinterpret_cast<u32x4*>(&sm.ks[buf][row * KSTR + c]) = kr[p];
+      if (KCH % kWaves != 0 && wave + kWaves * p >= KCH) break;
+      int row, col, off;
+      key_chunk(p, row, col, off);
+      *reinterpret_cast<u32x4*>(reinterpret_cast<unsigned char*>(sm.ks[buf]) + off) = kr[p];
+    }
+  };
+  // MFMA fragment (16-row block rb, k block kb) of a region-layout tile
+  auto lds_frag = [&](const T* tile, int nkb, int rb, int kb) -> Frag<T> {
+    const unsigned char* base = reinterpret_cast<const unsigned char*>(tile) +
+                                region_pos((rb * nkb + kb) * PPF * 4 + lg, li, lg);
+    if constexpr (PPF == 1) {
+      return load_frag<T>(reinterpret_cast<const T*>(base));
+    } else {
+      return join(load_quad<T>(reinterpret_cast<const T*>(base)),
+                  load_quad<T>(reinterpret_cast<const T*>(base + 4 * 256)));
     }
   };
   auto gate_fetch = [&](int jb, int ks, Frag<T> (&gf)[NFB]) {
@@ -228,11 +267,12 @@ __global__ __launch_bounds__(kAggThreads) void agg_kernel(AggArgs a, int nfc, in
       // WANGO: does this step hold older sources of some row of the tile?
       const bool phi_step = MODE == 1 && i0 + BR - 1 >= a.window && j0 <= i0 + BR - 1 - a.window;
 #pragma unroll
-      for (int jj = wjb; jj < wjb + JBW; ++jj) {
+      for (int t = 0; t < JBW; ++t) {
+        const int jj = wjb + t;   // wjb is even, so jj & 1 == t & 1
         f32x4 s = {0.f, 0.f, 0.f, 0.f}, sphi = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks) {
-          const Frag<T> kf = load_frag<T>(&sm.ks[buf][(jj * 16 + li) * KSTR + ks * 32 + lg * 8]);
+          const Frag<T> kf = lds_frag(sm.ks[buf], KS, jj, ks);
           mma(s, kf, qf[ks]);
           if (phi_step) {
             Frag<T> fkf;
@@ -257,7 +297,12 @@ __global__ __launch_bounds__(kAggThreads) void agg_kernel(AggArgs a, int nfc, in
           psum += tof<T>(pq[r]);
         }
         rowsum += psum;
-        store_quad<T>(&sm.ps[buf][(wib * 16 + li) * PSTR + jj * 16 + lg * 4], pq);
+        // the weights of sources 4 lg + r of block jj are slots r (jj even)
+        // or 4 + r (jj odd) of this lane's fragment for the half jj / 2: the
+        // first or second 8 bytes of the piece (bf16), or chunk 0 or 1 (float32)
+        unsigned char* base = reinterpret_cast<unsigned char*>(sm.ps[buf]) +
+                              region_pos((wib * 2 + (jj >> 1)) * PPF * 4 + lg, li, lg);
+        store_quad<T>(reinterpret_cast<T*>(base + (t & 1) * (PPF == 1 ? 8 : 4 * 256)), pq);
       }
     };
     // gbar^T += G^T P^T over one half (32 sources) of the step in ps[buf]
@@ -267,10 +312,7 @@ __global__ __launch_bounds__(kAggThreads) void agg_kernel(AggArgs a, int nfc, in
       for (int ih = 0; ih < NIB; ih += 4) {
         Frag<T> pf[4];
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          const T* prow = &sm.ps[buf][((ih + q) * 16 + li) * PSTR + ks * 32];
-          pf[q] = join(load_quad<T>(prow + lg * 4), load_quad<T>(prow + 16 + lg * 4));
-        }
+        for (int q = 0; q < 4; ++q) pf[q] = lds_frag(sm.ps[buf], 2, ih + q, ks);
 #pragma unroll
         for (int fb = 0; fb < NFB; ++fb)
 #pragma unroll
@@ -326,7 +368,11 @@ __global__ __launch_bounds__(kAggThreads) void agg_kernel(AggArgs a, int nfc, in
     bool combine = false;              // add the partner's partial while storing
     int64_t obase = 0, odbase = 0;
     if (job.kind != kFull) {
-      // write this partial, then the second of the two workgroups combines
+      // Write this partial, then the second of the two workgroups combines.
+      // The partials and the counter are accessed with agent-scope atomics
+      // (coherent stores and loads that bypass the per-XCD L2s): an agent-
+      // scope fence would instead write back and invalidate the whole L2 of
+      // the XCD, evicting the keys and gates the other workgroups stream.
       const int slot = job.kind == kPart0 ? 0 : 1;
       const int64_t pbase = (job.split_id * 2 + slot) * (int64_t)BR * FS;
       if (has_cols) {
@@ -334,23 +380,27 @@ __global__ __launch_bounds__(kAggThreads) void agg_kernel(AggArgs a, int nfc, in
         for (int fb = 0; fb < NFB; ++fb)
 #pragma unroll
           for (int ib = 0; ib < NIB; ++ib)
-            *reinterpret_cast<f32x4*>(a.part + pbase +
-                                      ((int64_t)(ib * (FS / 16) + wave * NFB + fb) * 64 + lane) * 4) =
-                acc[ib][fb];
+#pragma unroll
+            for (int r = 0; r < 4; ++r)
+              __hip_atomic_store(a.part + pbase + part_index(ib * (FS / 16) + wave * NFB + fb, r, lane),
+                                 acc[ib][fb][r], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       }
-      if (wave == 0)
+      if (wave == 0 && lg == 0)
         for (int ib = 0; ib < NIB; ++ib)
-          if (lg == 0) a.part_den[(job.split_id * 2 + slot) * BR + ib * 16 + li] = den[ib];
-      __threadfence();
-      __syncthreads();
-      if (tid == 0) sm.flag = atomicAdd(&a.counters[job.split_id], 1);
+          __hip_atomic_store(a.part_den + (job.split_id * 2 + slot) * BR + ib * 16 + li, den[ib],
+                             __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      __builtin_amdgcn_s_waitcnt(0);   // this thread's partial stores are complete
+      __syncthreads();                 // ... and every thread's
+      if (tid == 0)
+        sm.flag = __hip_atomic_fetch_add(&a.counters[job.split_id], 1, __ATOMIC_RELAXED,
+                                         __HIP_MEMORY_SCOPE_AGENT);
       __syncthreads();
       if (sm.flag == 1) {
-        __threadfence();
         const int other = 1 - slot;
         obase = (job.split_id * 2 + other) * (int64_t)BR * FS;
         odbase = (job.split_id * 2 + other) * BR;
-        if (tid == 0) a.counters[job.split_id] = 0;
+        if (tid == 0)
+          __hip_atomic_store(&a.counters[job.split_id], 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         combine = true;
         finish = true;
       }
@@ -363,16 +413,21 @@ __global__ __launch_bounds__(kAggThreads) void agg_kernel(AggArgs a, int nfc, in
         // the two partials are added first: mine + other is the same float
         // whichever workgroup finishes last
         float dsum = den[ib];
-        if (combine) dsum += a.part_den[odbase + ib * 16 + li];
+        if (combine)
+          dsum += __hip_atomic_load(a.part_den + odbase + ib * 16 + li, __ATOMIC_RELAXED,
+                                    __HIP_MEMORY_SCOPE_AGENT);
         dsum += null_w * (float)(i + 1);
         if (MODE == 1) dsum += escale * a.z_old[(mseq + i) * a.H + h];
         const float inv = 1.0f / dsum;
 #pragma unroll
         for (int fb = 0; fb < NFB; ++fb) {
           f32x4 num = acc[ib][fb];
-          if (combine)
-            num += *reinterpret_cast<const f32x4*>(
-                a.part + obase + ((int64_t)(ib * (FS / 16) + wave * NFB + fb) * 64 + lane) * 4);
+          if (combine) {
+#pragma unroll
+            for (int r = 0; r < 4; ++r)
+              num[r] += __hip_atomic_load(a.part + obase + part_index(ib * (FS / 16) + wave * NFB + fb, r, lane),
+                                          __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+          }
           if (MODE == 1) {
             const int64_t nblk = ((mseq + i0) / 16 + ib) * (F / 16) + (col0 / 16 + fb);
             const f32x4 no = *reinterpret_cast<const f32x4*>(a.n_old + (nblk * 64 + lane) * 4);

@@ -58,27 +58,44 @@ __device__ __forceinline__ ScanWg scan_wg(int64_t id, int nslices, int H, int ns
   return w;
 }
 
-// S (this wave's DH x 16*NFB slice; DH/16 x NFB accumulator blocks) += phi_K^T G
-// over the CH sources starting at row0, and Sz += phi_K^T 1 when with_z.
-template <typename T, int DH, int CH, int NFB>
-__device__ __forceinline__ void state_update(f32x4 (&S)[DH / 16][NFB], f32x4 (&Sz)[DH / 16], bool with_z,
-                                             const T* __restrict__ fk, const T* __restrict__ gp,
-                                             int64_t row0, int HD, int hcol, int64_t col, int F, int li,
-                                             int lg) {
+// A unit of sources in registers: the gate fragments of this wave's columns
+// and the key-feature fragments (A operand of S += phi_K^T G).  Loads run one
+// unit ahead of the MFMAs; the unit is 64 sources, 32 for d_h = 128 (whose
+// key fragments are twice as many registers).
+template <int DH> constexpr int unit_len() { return DH >= 128 ? 32 : 64; }
+template <typename T, int DH, int NFB> struct UnitRegs {
+  static constexpr int U = unit_len<DH>();
+  Frag<T> g[U / 32][NFB];
+  Frag<T> k[U / 32][DH / 16];
+};
+
+template <typename T, int DH, int NFB>
+__device__ __forceinline__ void load_unit(UnitRegs<T, DH, NFB>& c, const T* __restrict__ fk,
+                                          const T* __restrict__ gp, int64_t row0, int HD, int hcol,
+                                          int64_t col, int F, int li, int lg) {
 #pragma unroll
-  for (int ks = 0; ks < CH / 32; ++ks) {
+  for (int ks = 0; ks < unit_len<DH>() / 32; ++ks) {
     const int64_t blk = row0 / 32 + ks;
-    Frag<T> g[NFB];
 #pragma unroll
-    for (int fb = 0; fb < NFB; ++fb) g[fb] = load_frag<T>(gp + packed_offset(blk, lg, col + fb * 16 + li, F));
+    for (int fb = 0; fb < NFB; ++fb) c.g[ks][fb] = load_frag<T>(gp + packed_offset(blk, lg, col + fb * 16 + li, F));
+#pragma unroll
+    for (int eb = 0; eb < DH / 16; ++eb) c.k[ks][eb] = load_frag<T>(fk + packed_offset(blk, lg, hcol + eb * 16 + li, HD));
+  }
+}
+
+// S (this wave's DH x 16*NFB slice; DH/16 x NFB accumulator blocks) += phi_K^T G
+// over one unit, and Sz += phi_K^T 1 when with_z.
+template <typename T, int DH, int NFB>
+__device__ __forceinline__ void apply_unit(f32x4 (&S)[DH / 16][NFB], f32x4 (&Sz)[DH / 16], bool with_z,
+                                           const UnitRegs<T, DH, NFB>& c) {
+#pragma unroll
+  for (int ks = 0; ks < unit_len<DH>() / 32; ++ks)
 #pragma unroll
     for (int eb = 0; eb < DH / 16; ++eb) {
-      const Frag<T> a = load_frag<T>(fk + packed_offset(blk, lg, hcol + eb * 16 + li, HD));
 #pragma unroll
-      for (int fb = 0; fb < NFB; ++fb) mma(S[eb][fb], a, g[fb]);
-      if (with_z) mma(Sz[eb], a, ones_frag<T>());
+      for (int fb = 0; fb < NFB; ++fb) mma(S[eb][fb], c.k[ks][eb], c.g[ks][fb]);
+      if (with_z) mma(Sz[eb], c.k[ks][eb], ones_frag<T>());
     }
-  }
 }
 
 // Pass 1: per-segment sums (all segments but the last).
@@ -105,8 +122,22 @@ __global__ __launch_bounds__(kScanThreads) void scan_partial_kernel(ScanArgs a) 
   }
   const int nchunks = a.Tp / CH;
   const int c0 = w.seg * a.chunks_per_seg, c1 = min(nchunks, c0 + a.chunks_per_seg);
-  for (int c = c0; c < c1; ++c)
-    state_update<T, DH, CH, NFB>(S, Sz, with_z, fk, gp, mseq + (int64_t)c * CH, HD, w.h * DH, col, a.F, li, lg);
+  // two register sets: unit u + 1 loads while unit u is applied
+  constexpr int UPC = CH / unit_len<DH>();   // units per chunk
+  const int u0 = c0 * UPC, u1 = c1 * UPC;
+  UnitRegs<T, DH, NFB> r0, r1;
+  auto load = [&](UnitRegs<T, DH, NFB>& r, int u) {
+    load_unit<T, DH, NFB>(r, fk, gp, mseq + (int64_t)min(u, u1 - 1) * unit_len<DH>(), HD, w.h * DH, col, a.F, li, lg);
+  };
+  if (u0 < u1) load(r0, u0);
+  for (int u = u0; u < u1; u += 2) {
+    load(r1, u + 1);
+    apply_unit<T, DH, NFB>(S, Sz, with_z, r0);
+    if (u + 1 < u1) {
+      load(r0, u + 2);
+      apply_unit<T, DH, NFB>(S, Sz, with_z, r1);
+    }
+  }
 
   float* dst = a.seg_state + (((w.b * a.H + w.h) * a.nseg + w.seg) * (int64_t)DH) * Fh;
 #pragma unroll
@@ -124,31 +155,37 @@ __global__ __launch_bounds__(kScanThreads) void scan_partial_kernel(ScanArgs a) 
   }
 }
 
-// Pass 2: exclusive prefix over segments, in place.  One thread per state element.
+// Pass 2: exclusive prefix over segments, in place.  One thread per state
+// element; the segment values are loaded in independent batches of kBatch so
+// that the memory latency is paid once per batch, not once per segment.
+constexpr int kBatch = 16;
+__device__ __forceinline__ void exclusive_prefix(float* p, int64_t stride, int nseg) {
+  float run = 0.f;
+  for (int s0 = 0; s0 < nseg - 1; s0 += kBatch) {   // the last segment has no sum of its own
+    float v[kBatch];
+#pragma unroll
+    for (int u = 0; u < kBatch; ++u)
+      if (s0 + u < nseg - 1) v[u] = p[(int64_t)(s0 + u) * stride];
+#pragma unroll
+    for (int u = 0; u < kBatch; ++u)
+      if (s0 + u < nseg - 1) {
+        p[(int64_t)(s0 + u) * stride] = run;
+        run += v[u];
+      }
+  }
+  p[(int64_t)(nseg - 1) * stride] = run;
+}
+
 __global__ void scan_prefix_kernel(float* state, float* segz, int64_t per_bh, int nseg, int64_t nbh,
                                    int dh) {
   const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   if (i < nbh * per_bh) {
     const int64_t bh = i / per_bh, e = i % per_bh;
-    float* p = state + bh * nseg * per_bh + e;
-    float run = 0.f;
-    for (int s = 0; s + 1 < nseg; ++s) {   // the last segment has no sum of its own
-      const float v = p[(int64_t)s * per_bh];
-      p[(int64_t)s * per_bh] = run;
-      run += v;
-    }
-    p[(int64_t)(nseg - 1) * per_bh] = run;
+    exclusive_prefix(state + bh * nseg * per_bh + e, per_bh, nseg);
   }
   if (i < nbh * dh) {
     const int64_t bh = i / dh, e = i % dh;
-    float* p = segz + bh * nseg * dh + e;
-    float run = 0.f;
-    for (int s = 0; s + 1 < nseg; ++s) {
-      const float v = p[(int64_t)s * dh];
-      p[(int64_t)s * dh] = run;
-      run += v;
-    }
-    p[(int64_t)(nseg - 1) * dh] = run;
+    exclusive_prefix(segz + bh * nseg * dh + e, dh, nseg);
   }
 }
 
@@ -202,7 +239,14 @@ __global__ __launch_bounds__(kScanThreads) void scan_main_kernel(ScanArgs a) {
     }
   }
 
-  for (int c = c0; c < c1; ++c) {
+  constexpr int UPC = CH / unit_len<DH>();   // units per chunk
+  const int u0 = c0 * UPC, u1 = c1 * UPC;
+  UnitRegs<T, DH, NFB> r0, r1;
+  auto load = [&](UnitRegs<T, DH, NFB>& r, int u) {
+    load_unit<T, DH, NFB>(r, fk, gp, mseq + (int64_t)min(u, u1 - 1) * unit_len<DH>(), HD, w.h * DH, col, F, li, lg);
+  };
+  // read-out of S_{<cCH} for destination chunk c + lag: n_old^T = S^T phi_Q^T
+  auto readout = [&](int c) {
     const int dchunk = c + lag;
     if (dchunk < nchunks) {
       // read-out of S_{<cCH} for destination chunk d: n_old^T = S^T phi_Q^T
@@ -236,8 +280,18 @@ __global__ __launch_bounds__(kScanThreads) void scan_main_kernel(ScanArgs a) {
         }
       }
     }
-    // S += phi_K(c)^T G(c)
-    state_update<T, DH, CH, NFB>(S, Sz, with_z, fk, gp, mseq + (int64_t)c * CH, HD, w.h * DH, col, F, li, lg);
+  };
+  // the read-out for chunk c comes before its first unit is applied
+  if (u0 < u1) load(r0, u0);
+  for (int u = u0; u < u1; u += 2) {
+    load(r1, u + 1);
+    if (u % UPC == 0) readout(u / UPC);
+    apply_unit<T, DH, NFB>(S, Sz, with_z, r0);
+    if (u + 1 < u1) {
+      load(r0, u + 2);
+      if ((u + 1) % UPC == 0) readout((u + 1) / UPC);
+      apply_unit<T, DH, NFB>(S, Sz, with_z, r1);
+    }
   }
 }
 

@@ -21,6 +21,11 @@ Alongside, with HIP events on the launch stream:
     against 8 TB/s;
   * cpu_baseline: the float64 CPU oracle on a bounded sample of the same work
     (one of the four TANGO applications, scaled by 4, plus the WANGO block).
+The "traffic" of the two rooflines is the HBM traffic per launch measured by
+rocprofv3 counters (FETCH_SIZE and WRITE_SIZE, scaled by what they read for a
+plain copy of known size, which --copy-calibration runs), read from
+profiles/hbm_traffic_t8192.md; it is reported only while the sha256 of the
+kernel's sources still matches the one recorded there, else null.
 """
 from __future__ import annotations
 
@@ -49,7 +54,42 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--kernel-loops", type=int, default=None,
                     help="launches per roofline measurement (default: --steps)")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="also run a plain 256 MiB device copy (for counter calibration)")
     return ap.parse_args()
+
+
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic_t8192.md")
+KERNEL_SOURCES = {
+    "agg_kernel": ["agg_kernels.hip", "common.hpp", "kernels.hpp"],
+    "scan": ["scan_kernels.hip", "common.hpp", "kernels.hpp"],
+}
+
+
+def source_hash(key: str) -> str:
+    import hashlib
+    h = hashlib.sha256()
+    for name in KERNEL_SOURCES[key]:
+        with open(os.path.join(ROOT, "cross_token_gated_amd", "csrc", name), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def recorded_traffic(key: str):
+    """HBM bytes per launch recorded for `key`, or None if absent or stale."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            lines = f.read().splitlines()
+    except OSError:
+        return None
+    for line in lines:
+        cells = [c.strip() for c in line.strip().strip("|").split("|")]
+        if len(cells) >= 5 and cells[0] == key:
+            try:
+                return float(cells[4]) if cells[1] == source_hash(key) else None
+            except ValueError:
+                return None
+    return None
 
 
 def tango_flops(w) -> float:
@@ -228,16 +268,23 @@ def main():
         },
         "roofline": {"kernel": "agg_kernel (TANGO aggregation, T=8192)", "bound": "mfma",
                      "achieved": achieved / 1e12, "peak": PEAK_BF16_FLOPS / 1e12, "unit": "TFLOP/s",
-                     "frac": achieved / PEAK_BF16_FLOPS, "traffic": None,
+                     "frac": achieved / PEAK_BF16_FLOPS, "traffic": recorded_traffic("agg_kernel"),
                      "flops_per_launch": agg_flops, "ms_per_launch": ms_agg},
         "roofline_scan": {"kernel": "WANGO running-sum scan (3 launches, T=8192)", "bound": "hbm",
                           "achieved": s_ach / 1e9, "peak": PEAK_HBM_BYTES / 1e9, "unit": "GB/s",
-                          "frac": s_ach / PEAK_HBM_BYTES, "traffic": None,
+                          "frac": s_ach / PEAK_HBM_BYTES, "traffic": recorded_traffic("scan"),
                           "bytes_per_launch": sbytes, "ms_per_launch": ms_scan},
     }
     print(f"[bench] tango {ms_tango:.3f} ms, wango {ms_wango:.3f} ms, aggregation {ms_agg:.3f} ms "
           f"({result['roofline']['frac'] * 100:.1f}% of bf16 peak), scan {ms_scan:.4f} ms "
           f"({result['roofline_scan']['frac'] * 100:.1f}% of HBM peak)", file=sys.stderr, flush=True)
+    if args.copy_calibration:
+        # a plain device copy of known size: 2^28 bytes read, 2^28 bytes written
+        src = torch.ones(1 << 26, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(wt, wg)
     print(json.dumps(result), flush=True)

@@ -100,10 +100,12 @@ template <class CF, typename T> constexpr size_t ops_bytes() {
   return 2 * (size_t)tile_chunks<CF, T>(CF::AS * CF::BM + CF::BN) * 1024;
 }
 constexpr size_t kEpiBytes = (size_t)kEpiRows * kCStride * sizeof(float);
-// Operand buffers (reused for the epilogue tile), then BM row scales.
+// Operand buffers (reused for the epilogue tile), then BM row scales, then
+// the RoPE frequencies of one head (at most 64 pairs, float64).
+constexpr int kMaxPairs = 64;
 template <class CF, typename T> constexpr size_t main_bytes() {
   return (ops_bytes<CF, T>() > kEpiBytes ? ops_bytes<CF, T>() : kEpiBytes) +
-         (size_t)CF::BM * sizeof(float);
+         (size_t)CF::BM * sizeof(float) + kMaxPairs * sizeof(double);
 }
 
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
@@ -439,7 +441,9 @@ void proj_kernel(ProjArgs args) {
   constexpr int PA = tile_chunks<CF, T>(CF::BM) / 4, PB = tile_chunks<CF, T>(CF::BN) / 4;
   extern __shared__ __align__(16) unsigned char smem_raw[];
   T* lds = reinterpret_cast<T*>(smem_raw);
-  float* rs = reinterpret_cast<float*>(smem_raw + main_bytes<CF, T>() - CF::BM * sizeof(float));
+  constexpr size_t kRsOff = main_bytes<CF, T>() - kMaxPairs * sizeof(double) - CF::BM * sizeof(float);
+  float* rs = reinterpret_cast<float*>(smem_raw + kRsOff);
+  double* rev_freq = reinterpret_cast<double*>(smem_raw + kRsOff + CF::BM * sizeof(float));
 
   const int d = args.d, F = args.F, HD = args.HD, Tp = args.Tp;
   const int N = 2 * F + 2 * HD;
@@ -480,23 +484,51 @@ void proj_kernel(ProjArgs args) {
 
   gemm_mainloop<CF, T>(acc, lds, d / CF::BK, sa, sb);
 
-  // RMSNorm row scales (the rows are distinct from the operand buffers)
+  const int dh = args.dh;
+  const bool has_qk = n0 + CF::BN > 2 * F;
+  // RMSNorm row scales, and for the query/key tiles the RoPE rotation rate of
+  // pair c, base^(-2c/d_h) in revolutions per position (float64: positions
+  // reach 65,535); both live past the operand buffers
   if (tid < CF::BM) rs[tid] = args.rinv[m0 + tid];
+  if (has_qk && tid < dh / 2)
+    rev_freq[tid] = args.rope_base > 0.f
+        ? pow((double)args.rope_base, -2.0 * (double)tid / (double)dh) * 0.15915494309189533577
+        : 0.0;
   __syncthreads();
   float* Cs = reinterpret_cast<float*>(smem_raw);
 
-  const int dh = args.dh;
-  const int half = dh >> 1;                      // lanes per (row, head)
-  const int lane = tid & 63, wave = tid >> 6;
-  const int per_wave = 64 / half;                // (row, head) items per wave pass
-  const int sub = lane / half, cpair = lane % half;
-  // rotation of pair c at position i: angle i * base^(-2c/d_h), taken in
-  // revolutions in float64 and reduced to [-1/2, 1/2] before the float32
-  // sine and cosine (v_sin_f32 / v_cos_f32 take revolutions)
-  const bool has_qk = n0 + CF::BN > 2 * F;
-  const double rev_freq = has_qk && args.rope_base > 0.f
-      ? pow((double)args.rope_base, -2.0 * (double)cpair / (double)dh) * 0.15915494309189533577
-      : 0.0;
+  if (n0 + CF::BN <= F) {
+    // Gate tile: a lane holds column l % 16 of two stacked 16-row blocks, rows
+    // 4 (l / 16) + r and 16 + 4 (l / 16) + r of a 32-row block: exactly the 8
+    // slots of its piece of the packed layout, stored with SiLU applied.
+    T* gp = static_cast<T*>(args.gp);
+    const int lane = tid & 63, col = lane & 15, grp = lane >> 4;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int wr = wave / CF::WN, wc = wave % CF::WN;
+    static_assert(CF::IB % 2 == 0, "32-row blocks");
+#pragma unroll
+    for (int i = 0; i < CF::IB; i += 2) {
+      const int r0 = wr * CF::WTM + i * 16;
+      float sl[4], sh[4];
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        sl[r] = rs[r0 + grp * 4 + r];
+        sh[r] = rs[r0 + 16 + grp * 4 + r];
+      }
+#pragma unroll
+      for (int j = 0; j < CF::JB; ++j) {
+        Frag<T> out;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const float a = acc[i][j][r] * sl[r], b = acc[i + 1][j][r] * sh[r];
+          out[r] = cvt<T>(a * __builtin_amdgcn_rcpf(1.0f + __expf(-a)));
+          out[4 + r] = cvt<T>(b * __builtin_amdgcn_rcpf(1.0f + __expf(-b)));
+        }
+        store_frag<T>(gp + packed_offset((m0 + r0) / 32, grp, n0 + wc * CF::WTN + j * 16 + col, F), out);
+      }
+    }
+    return;
+  }
 
   for (int pass = 0; pass < CF::BM / kEpiRows; ++pass) {
     if (pass) __syncthreads();   // the previous pass is done with Cs
@@ -536,54 +568,75 @@ void proj_kernel(ProjArgs args) {
         store_frag<T>(v + (mp + row) * F + (n - F), out);
       }
     }
-    // queries and keys: RoPE on interleaved pairs, then unit length per head
+    // queries and keys: RoPE on interleaved pairs, then unit length per head.
+    // A thread takes 16 pairs (32 columns) of one row; the dh / 32 threads of a
+    // (row, head) are consecutive lanes and reduce the squared norm together.
     if (has_qk) {
       const int c_lo = n0 < 2 * F ? 2 * F - n0 : 0;  // first q/k column in tile
       const int c_hi = min(CF::BN, N - n0);
-      const int heads_in_tile = (c_hi - c_lo) / dh;
-      const int items = kEpiRows * heads_in_tile;
-      for (int base = wave * per_wave; base < items; base += 4 * per_wave) {
-        const int item = base + sub;
-        const bool ok = item < items;
-        const int row = ok ? item / heads_in_tile : 0;
-        const int hcol = c_lo + (ok ? item % heads_in_tile : 0) * dh;
-        float u0 = ok ? Cs[row * kCStride + hcol + 2 * cpair] : 0.f;
-        float u1 = ok ? Cs[row * kCStride + hcol + 2 * cpair + 1] : 0.f;
-        if (args.rope_base > 0.f) {
-          const double rev = (double)(tpos + row) * rev_freq;
-          const float fr = (float)(rev - rint(rev));
-          const float fs = __builtin_amdgcn_sinf(fr), fc = __builtin_amdgcn_cosf(fr);
-          const float r0 = u0 * fc - u1 * fs, r1 = u0 * fs + u1 * fc;
-          u0 = r0;
-          u1 = r1;
+      const int nq = (c_hi - c_lo) / 32;             // 32-column quarters per row
+      const int qph = dh / 32;                       // quarters per head
+      const float isd = 1.0f / sqrtf((float)dh);
+      for (int item = tid; item < kEpiRows * nq; item += kThreads) {   // block-uniform trip count
+        const int row = item / nq, q = item % nq;
+        const int hcol = c_lo + q * 32;             // first column of this quarter in the tile
+        const int pair0 = (q % qph) * 16;           // first pair within the head
+        float u[32];
+#pragma unroll
+        for (int e4 = 0; e4 < 8; ++e4) {
+          const f32x4 t4 = *reinterpret_cast<const f32x4*>(&Cs[row * kCStride + hcol + e4 * 4]);
+#pragma unroll
+          for (int r = 0; r < 4; ++r) u[e4 * 4 + r] = t4[r];
         }
-        float ss = u0 * u0 + u1 * u1;
-        for (int off = 1; off < half; off <<= 1) ss += __shfl_xor(ss, off, 64);
+        if (args.rope_base > 0.f) {
+          const double pos = (double)(tpos + row);
+#pragma unroll
+          for (int p = 0; p < 16; ++p) {
+            const double rev = pos * rev_freq[pair0 + p];
+            const float fr = (float)(rev - rint(rev));
+            const float fs = __builtin_amdgcn_sinf(fr), fc = __builtin_amdgcn_cosf(fr);
+            const float a0 = u[2 * p], a1 = u[2 * p + 1];
+            u[2 * p] = a0 * fc - a1 * fs;
+            u[2 * p + 1] = a0 * fs + a1 * fc;
+          }
+        }
+        float ss = 0.f;
+#pragma unroll
+        for (int e = 0; e < 32; ++e) ss += u[e] * u[e];
+        for (int off = 1; off < qph; off <<= 1) ss += __shfl_xor(ss, off, 64);
         const float inv = 1.0f / fmaxf(sqrtf(ss), 1e-12f);
-        if (ok) {
-          const int n = n0 + hcol;
-          const bool is_q = n < 2 * F + HD;
-          const int e = is_q ? n - 2 * F : n - 2 * F - HD;   // column within q or k
-          T* dst = (is_q ? static_cast<T*>(args.qh) : static_cast<T*>(args.kh)) + (mp + row) * HD + e;
-          const T w0 = cvt<T>(u0 * inv), w1 = cvt<T>(u1 * inv);
-          dst[2 * cpair] = w0;
-          dst[2 * cpair + 1] = w1;
-          if (args.fq) {
-            // WANGO features phi(sqrt(tau) u) ([TANGO] §2.2 eq. 8) of the stored
-            // unit vector: queries go out directly in the permuted feature order,
-            // keys back into the tile for the packed store below
-            const float st = sqrtf(__expf(fminf(args.theta[e / dh], 2.995732273553991f)));
-            const float isd = 1.0f / sqrtf((float)dh);
-            const float p0 = phi_feature(st * tof<T>(w0), isd), p1 = phi_feature(st * tof<T>(w1), isd);
-            if (is_q) {
-              T* fq = static_cast<T*>(args.fq) + (mp + row) * HD + (e + 2 * cpair) / 32 * 32 +
-                      feature_slot((e + 2 * cpair) % 32);
-              fq[0] = cvt<T>(p0);
-              fq[1] = cvt<T>(p1);
-            } else {
-              Cs[row * kCStride + hcol + 2 * cpair] = p0;
-              Cs[row * kCStride + hcol + 2 * cpair + 1] = p1;
+        const int n = n0 + hcol;
+        const bool is_q = n < 2 * F + HD;
+        const int e0 = is_q ? n - 2 * F : n - 2 * F - HD;   // first column within q or k
+        Frag<T> w[4];
+#pragma unroll
+        for (int e = 0; e < 32; ++e) w[e / 8][e % 8] = cvt<T>(u[e] * inv);
+        T* dst = (is_q ? static_cast<T*>(args.qh) : static_cast<T*>(args.kh)) + (mp + row) * HD + e0;
+#pragma unroll
+        for (int c8 = 0; c8 < 4; ++c8) store_frag<T>(dst + c8 * 8, w[c8]);
+        if (args.fq) {
+          // WANGO features phi(sqrt(tau) u) ([TANGO] §2.2 eq. 8) of the stored
+          // unit vector: queries go out in the permuted feature order of their
+          // group of 32, keys back into the tile for the packed store below
+          const float st = sqrtf(__expf(fminf(args.theta[e0 / dh], 2.995732273553991f)));
+          float ph[32];
+#pragma unroll
+          for (int e = 0; e < 32; ++e) ph[e] = phi_feature(st * tof<T>(w[e / 8][e % 8]), isd);
+          if (is_q) {
+            Frag<T> fqv[4];
+#pragma unroll
+            for (int e = 0; e < 32; ++e) {
+              const int slot = feature_slot(e);
+              fqv[slot / 8][slot % 8] = cvt<T>(ph[e]);
             }
+            T* fqd = static_cast<T*>(args.fq) + (mp + row) * HD + e0;
+#pragma unroll
+            for (int c8 = 0; c8 < 4; ++c8) store_frag<T>(fqd + c8 * 8, fqv[c8]);
+          } else {
+#pragma unroll
+            for (int e4 = 0; e4 < 8; ++e4)
+              *reinterpret_cast<f32x4*>(&Cs[row * kCStride + hcol + e4 * 4]) =
+                  f32x4{ph[e4 * 4], ph[e4 * 4 + 1], ph[e4 * 4 + 2], ph[e4 * 4 + 3]};
           }
         }
       }

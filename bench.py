@@ -14,11 +14,16 @@ sequence tokens per second: (8192 + 8192) tokens / step time.
 
 Alongside, with HIP events on the launch stream:
   * roofline: the TANGO aggregation kernel (the dominant one), useful MFMA
-    flops 2 * (causal pairs) * (q/k width + F) per launch over its average
-    launch time, against 2.5 PFLOP/s dense bf16;
-  * roofline_scan: the WANGO running-sum scan (three launches), algorithmic
-    HBM bytes (q, k, g read once; n_old, z_old written once) over its time,
-    against 8 TB/s;
+    flops 2 * (causal pairs) * (q/k width + F) per launch over its median
+    launch time (each launch between its own events), against 2.5 PFLOP/s
+    dense bf16;
+  * roofline_scan: the WANGO running-sum scan (two launches), algorithmic
+    HBM bytes (q, k, g read once; n_old, z_old written once) over its median
+    time, against 8 TB/s.  A 512 MiB read runs before each timed scan, so its
+    inputs come from HBM, not from the 256 MB Infinity Cache that the
+    producing projection would otherwise leave them in (the warm-cache median
+    is reported beside it).  The flush reads rather than fills: a fill leaves
+    dirty lines whose write-back would land in the timed launch;
   * cpu_baseline: the float64 CPU oracle on a bounded sample of the same work
     (one of the four TANGO applications, scaled by 4, plus the WANGO block).
 The "traffic" of the two rooflines is the HBM traffic per launch measured by
@@ -210,6 +215,32 @@ def main():
         torch.cuda.synchronize()
         return a.elapsed_time(b) / n
 
+    # 512 MiB, twice the MI355X Infinity Cache: reading it evicts every earlier
+    # line from the L2s and the cache before a cold-cache launch.  A read, not a
+    # fill: a fill leaves the cache full of dirty lines whose write-back would
+    # then be charged to the timed kernel (a cold 32 MiB read measured 16 us
+    # after a fill, 9 us after a read of the same buffer, 6 us warm).
+    flush_buf = torch.ones(1 << 27, dtype=torch.float32, device=dev)
+    flush_sink = torch.empty((), dtype=torch.float32, device=dev)
+
+    def timed_each(fn, n, flush):
+        """Median and mean of n launches of fn, each bracketed by its own events
+        on the launch stream; with flush, a 512 MiB read runs before each."""
+        fn()
+        torch.cuda.synchronize()
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+              for _ in range(n)]
+        for a, b in ev:
+            if flush:
+                torch.sum(flush_buf, 0, out=flush_sink)
+            a.record(stream)
+            fn()
+            b.record(stream)
+        torch.cuda.synchronize()
+        t = sorted(a.elapsed_time(b) for a, b in ev)
+        med = t[n // 2] if n % 2 else 0.5 * (t[n // 2 - 1] + t[n // 2])
+        return med, sum(t) / n
+
     def tango_only():
         src = xt
         for r in range(wt.repeats):
@@ -220,8 +251,9 @@ def main():
     ms_tango = timed(tango_only, loops)
     ms_wango = timed(lambda: api.wango_block_fwd(xg, bg, wg.window, wg.head_dim, wg.chunk, out=outg,
                                                  ws=ws_g, stream=stream), loops)
-    ms_agg = timed(lambda: api.tango_stage_aggregate(st, bt.theta, None, qh, kh, gp, gbar, ws_t,
-                                                     stream=stream), loops)
+    ms_agg, ms_agg_mean = timed_each(lambda: api.tango_stage_aggregate(st, bt.theta, None, qh, kh, gp,
+                                                                       gbar, ws_t, stream=stream),
+                                     loops, flush=False)
     # WANGO scan inputs (two heads of 64)
     Mg = wg.B * api.padded_len(wg.T)
     HDg = wg.n_heads * wg.head_dim
@@ -234,8 +266,10 @@ def main():
     api.wango_stage_proj(sg, bg, xg, gpg, vg, qg, kg, fqg, fkg, ws=ws_g, stream=stream)
     n_old = torch.empty(Mg * wg.d_gate, dtype=torch.float32, device=dev)
     z_old = torch.empty(Mg, wg.n_heads, dtype=torch.float32, device=dev)
-    ms_scan = timed(lambda: api.wango_stage_scan(sg, wg.window, wg.chunk, fqg, fkg, gpg, n_old, z_old,
-                                                 ws_g, stream=stream), loops)
+    scan_call = lambda: api.wango_stage_scan(sg, wg.window, wg.chunk, fqg, fkg, gpg, n_old, z_old,  # noqa: E731
+                                             ws_g, stream=stream)
+    ms_scan_warm, _ = timed_each(scan_call, loops, flush=False)
+    ms_scan, ms_scan_mean = timed_each(scan_call, loops, flush=True)
 
     agg_flops = tango_flops(wt)
     achieved = agg_flops / (ms_agg * 1e-3)
@@ -269,11 +303,14 @@ def main():
         "roofline": {"kernel": "agg_kernel (TANGO aggregation, T=8192)", "bound": "mfma",
                      "achieved": achieved / 1e12, "peak": PEAK_BF16_FLOPS / 1e12, "unit": "TFLOP/s",
                      "frac": achieved / PEAK_BF16_FLOPS, "traffic": recorded_traffic("agg_kernel"),
-                     "flops_per_launch": agg_flops, "ms_per_launch": ms_agg},
-        "roofline_scan": {"kernel": "WANGO running-sum scan (3 launches, T=8192)", "bound": "hbm",
+                     "flops_per_launch": agg_flops, "ms_per_launch": ms_agg,
+                     "ms_per_launch_mean": ms_agg_mean},
+        "roofline_scan": {"kernel": "WANGO running-sum scan (2 launches, T=8192)", "bound": "hbm",
                           "achieved": s_ach / 1e9, "peak": PEAK_HBM_BYTES / 1e9, "unit": "GB/s",
                           "frac": s_ach / PEAK_HBM_BYTES, "traffic": recorded_traffic("scan"),
-                          "bytes_per_launch": sbytes, "ms_per_launch": ms_scan},
+                          "bytes_per_launch": sbytes, "ms_per_launch": ms_scan,
+                          "ms_per_launch_mean": ms_scan_mean, "cache": "flushed before each launch",
+                          "ms_per_launch_warm_cache": ms_scan_warm},
     }
     print(f"[bench] tango {ms_tango:.3f} ms, wango {ms_wango:.3f} ms, aggregation {ms_agg:.3f} ms "
           f"({result['roofline']['frac'] * 100:.1f}% of bf16 peak), scan {ms_scan:.4f} ms "

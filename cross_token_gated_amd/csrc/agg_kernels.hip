@@ -488,8 +488,9 @@ AggPlan tango_agg_plan(int B, int Tp, int F, int H, bool bf) {
   return p;
 }
 
-hipError_t launch_tango_agg(const AggArgs& a, const AggPlan& p, bool bf, hipStream_t s) {
-  if (p.split && p.n_split_tiles > 0) {
+hipError_t launch_tango_agg(const AggArgs& a, const AggPlan& p, bool bf, bool counters_clear,
+                            hipStream_t s) {
+  if (p.split && p.n_split_tiles > 0 && !counters_clear) {
     hipError_t e = launch_zero_i32(a.counters, p.n_split_tiles, s);
     if (e != hipSuccess) return e;
   }

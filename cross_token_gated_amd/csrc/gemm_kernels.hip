@@ -390,6 +390,9 @@ __device__ __forceinline__ void store_io(IO* p, const float (&v)[N]) {
 template <typename T, typename IO, int AS>
 __global__ __launch_bounds__(kThreads) void prep_kernel(ProjArgs args) {
   const int lane = threadIdx.x & 63;
+  for (int64_t i = (int64_t)blockIdx.x * kThreads + threadIdx.x; i < args.zero_n;
+       i += (int64_t)gridDim.x * kThreads)
+    args.zero[i] = 0;
   const int64_t m = (int64_t)blockIdx.x * (kThreads / 64) + (threadIdx.x >> 6);
   const int d = args.d, Tp = args.Tp, T_len = args.T;
   const int64_t M = (int64_t)args.B * Tp;

@@ -27,6 +27,8 @@ struct ProjArgs {
   const float* theta;  // [H], for the WANGO features
   void* xs;            // scratch: [parts][B*Tp, d] parts of h * gain (padded rows zero)
   float* rinv;         // scratch: [B*Tp] RMSNorm row scales
+  int* zero;           // optional: zero_n ints the row-prep kernel clears (the
+  int64_t zero_n;      //   aggregation's split counters), else null / 0
   int B, T, Tp, d, F, HD, dh;
   float rope_base, eps;
 };
@@ -68,10 +70,11 @@ struct ScanArgs {
   const void* gp;
   float* n_old;            // blocked [B*Tp/16][F/16][64][4]
   float* z_old;            // [B*Tp, H]
-  float* seg_state;        // [B][H][nseg][dh][F/H] segment sums, then exclusive prefixes
+  float* seg_state;        // segment sums: [B][H][column slice][nseg] blocks of dh x slice, accumulator order
   float* seg_z;            // [B][H][nseg][dh]
   int B, T, Tp, F, H, dh, window, chunk;
   int nseg, chunks_per_seg;
+  int slice;               // gate columns per workgroup (64 or 128)
 };
 
 // Plan of the TANGO aggregation grid for a shape.
@@ -95,7 +98,10 @@ ScanPlan wango_scan_plan(int B, int Tp, int F, int H, int chunk);
 // bf: bf16 weights/activations (else float32); io_bf: bf16 x/out (else float32)
 hipError_t launch_proj(const ProjArgs& a, bool bf, bool io_bf, hipStream_t s);
 hipError_t launch_out(const OutArgs& a, bool bf, bool io_bf, hipStream_t s);
-hipError_t launch_tango_agg(const AggArgs& a, const AggPlan& p, bool bf, hipStream_t s);
+// counters_clear: the split counters were already cleared earlier on the
+// stream (by the row-prep kernel of the same block); else a fill kernel runs.
+hipError_t launch_tango_agg(const AggArgs& a, const AggPlan& p, bool bf, bool counters_clear,
+                            hipStream_t s);
 hipError_t launch_wango_band(const AggArgs& a, bool bf, hipStream_t s);
 hipError_t launch_wango_scan(const ScanArgs& a, const ScanPlan& p, bool bf, hipStream_t s);
 hipError_t launch_zero_i32(int* p, int64_t n, hipStream_t s);

@@ -19,12 +19,16 @@
 // kernel: keys source-packed (the A operand of the state update
 // S += phi_K^T G), queries in the permuted feature order (the B operand of the
 // read-out n_old^T = S^T phi_Q^T, whose A operand is the state accumulator
-// itself).  No LDS is used.  z rides along as the state of a column of ones,
-// kept by one wave per (sequence, head).
+// itself).  z rides along as the state of a column of ones, kept by one wave
+// per (sequence, head).
 //
 // The sequence is cut into segments so that many workgroups run at once:
-// pass 1 sums every segment's contribution, pass 2 turns the sums into
-// exclusive prefixes, pass 3 replays each segment from its prefix.
+// pass 1 sums every segment's contribution (all but the last segment); pass 2
+// adds the sums of the segments before its own to get its starting state, then
+// replays its segment and emits the read-outs.  Both passes are bound by the
+// latency of their loads, so each wave keeps a ring of register sets of source
+// units with all but one in flight, and pass 2 stages the query
+// features of the next chunk through LDS while the current chunk runs.
 #include "common.hpp"
 #include "kernels.hpp"
 
@@ -34,12 +38,27 @@ namespace {
 
 constexpr int kScanWaves = 4;
 constexpr int kScanThreads = 64 * kScanWaves;
+// Source-unit register sets per wave (ring depth): all but one are in flight.
+// (Five or six sets for bf16 measured no faster than four.)
+template <typename T, int DH, bool MAIN> constexpr int ring_sets() { return sizeof(T) == 4 ? 2 : 4; }
+// Segment sums loaded per batch while the starting state is summed: about 64
+// registers of loads in flight.
+template <int DH, int NFB> constexpr int prefix_batch() {
+  return (DH / 16) * NFB >= 16 ? 1 : 16 / ((DH / 16) * NFB);
+}
 
 template <typename T> __device__ __forceinline__ Frag<T> ones_frag() {
   Frag<T> f;
 #pragma unroll
   for (int s = 0; s < 8; ++s) f[s] = cvt<T>(1.0f);
   return f;
+}
+
+// Workgroup barrier that orders LDS only: global loads stay in flight across it.
+__device__ __forceinline__ void lds_sync() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
 }
 
 // Workgroup decode: (b, h, column slice of kScanWaves * 16 * NFB, segment).
@@ -59,9 +78,8 @@ __device__ __forceinline__ ScanWg scan_wg(int64_t id, int nslices, int H, int ns
 }
 
 // A unit of sources in registers: the gate fragments of this wave's columns
-// and the key-feature fragments (A operand of S += phi_K^T G).  Loads run one
-// unit ahead of the MFMAs; the unit is 64 sources, 32 for d_h = 128 (whose
-// key fragments are twice as many registers).
+// and the key-feature fragments (A operand of S += phi_K^T G).  The unit is 64
+// sources, 32 for d_h = 128 (whose key fragments are twice as many registers).
 template <int DH> constexpr int unit_len() { return DH >= 128 ? 32 : 64; }
 template <typename T, int DH, int NFB> struct UnitRegs {
   static constexpr int U = unit_len<DH>();
@@ -91,19 +109,53 @@ __device__ __forceinline__ void apply_unit(f32x4 (&S)[DH / 16][NFB], f32x4 (&Sz)
 #pragma unroll
   for (int ks = 0; ks < unit_len<DH>() / 32; ++ks)
 #pragma unroll
-    for (int eb = 0; eb < DH / 16; ++eb) {
+    for (int eb = 0; eb < DH / 16; ++eb)
 #pragma unroll
       for (int fb = 0; fb < NFB; ++fb) mma(S[eb][fb], c.k[ks][eb], c.g[ks][fb]);
-      if (with_z) mma(Sz[eb], c.k[ks][eb], ones_frag<T>());
+  if (with_z) {
+#pragma unroll
+    for (int ks = 0; ks < unit_len<DH>() / 32; ++ks)
+#pragma unroll
+      for (int eb = 0; eb < DH / 16; ++eb) mma(Sz[eb], c.k[ks][eb], ones_frag<T>());
+  }
+}
+
+// Offset (floats) of a wave's accumulator block (eb, fb) in the segment sums,
+// stored in accumulator order: block-contiguous, lane-major, 4 floats a lane.
+template <int DH, int NFB>
+__device__ __forceinline__ int64_t seg_block(int64_t slice_seg, int wave, int eb, int fb, int lane) {
+  constexpr int FSC = kScanWaves * 16 * NFB;
+  return slice_seg * (int64_t)(DH * FSC) + (((wave * (DH / 16) + eb) * NFB + fb) * 64 + lane) * 4;
+}
+
+// One segment: its source units in order through a ring of NS register sets.  MAIN adds, before the first unit of every chunk, the read-out of the
+// state for the destination chunk that chunk feeds (through `boundary`).
+template <typename T, int DH, int NFB, int UPC, int NS, typename Boundary>
+__device__ __forceinline__ void walk_units(f32x4 (&S)[DH / 16][NFB], f32x4 (&Sz)[DH / 16], bool with_z,
+                                           UnitRegs<T, DH, NFB> (&R)[NS], int u0, int u1,
+                                           const T* fk, const T* gp, int64_t mseq, int HD, int hcol,
+                                           int64_t col, int F, int li, int lg, Boundary&& boundary) {
+  auto load = [&](UnitRegs<T, DH, NFB>& r, int u) {
+    load_unit<T, DH, NFB>(r, fk, gp, mseq + (int64_t)min(u, u1 - 1) * unit_len<DH>(), HD, hcol, col, F, li, lg);
+  };
+  for (int u = u0; u < u1; u += NS) {
+#pragma unroll
+    for (int j = 0; j < NS; ++j) {
+      load(R[(j + NS - 1) % NS], u + j + NS - 1);
+      if ((u + j) % UPC == 0 && u + j < u1) boundary((u + j) / UPC);
+      if (u + j < u1) apply_unit<T, DH, NFB>(S, Sz, with_z, R[j]);
     }
+  }
 }
 
 // Pass 1: per-segment sums (all segments but the last).
 template <typename T, int DH, int CH, int NFB>
-__global__ __launch_bounds__(kScanThreads) void scan_partial_kernel(ScanArgs a) {
+__global__ __launch_bounds__(kScanThreads) __attribute__((amdgpu_waves_per_eu(1, 1)))
+void scan_partial_kernel(ScanArgs a) {
   constexpr int FSC = kScanWaves * 16 * NFB;
   const int Fh = a.F / a.H, HD = a.H * DH;
-  const ScanWg w = scan_wg(blockIdx.x, Fh / FSC, a.H, a.nseg - 1);
+  const int nslices = Fh / FSC;
+  const ScanWg w = scan_wg(blockIdx.x, nslices, a.H, a.nseg - 1);
   const int lane = threadIdx.x & 63, li = lane & 15, lg = lane >> 4;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const bool with_z = w.fsl == 0 && wave == 0;
@@ -122,79 +174,43 @@ __global__ __launch_bounds__(kScanThreads) void scan_partial_kernel(ScanArgs a) 
   }
   const int nchunks = a.Tp / CH;
   const int c0 = w.seg * a.chunks_per_seg, c1 = min(nchunks, c0 + a.chunks_per_seg);
-  // two register sets: unit u + 1 loads while unit u is applied
-  constexpr int UPC = CH / unit_len<DH>();   // units per chunk
+  constexpr int UPC = CH / unit_len<DH>(), NS = ring_sets<T, DH, false>();
   const int u0 = c0 * UPC, u1 = c1 * UPC;
-  UnitRegs<T, DH, NFB> r0, r1;
-  auto load = [&](UnitRegs<T, DH, NFB>& r, int u) {
-    load_unit<T, DH, NFB>(r, fk, gp, mseq + (int64_t)min(u, u1 - 1) * unit_len<DH>(), HD, w.h * DH, col, a.F, li, lg);
-  };
-  if (u0 < u1) load(r0, u0);
-  for (int u = u0; u < u1; u += 2) {
-    load(r1, u + 1);
-    apply_unit<T, DH, NFB>(S, Sz, with_z, r0);
-    if (u + 1 < u1) {
-      load(r0, u + 2);
-      apply_unit<T, DH, NFB>(S, Sz, with_z, r1);
-    }
-  }
+  UnitRegs<T, DH, NFB> R[NS];
+#pragma unroll
+  for (int j = 0; j < NS - 1; ++j)
+    load_unit<T, DH, NFB>(R[j], fk, gp, mseq + (int64_t)min(u0 + j, u1 - 1) * unit_len<DH>(), HD, w.h * DH,
+                          col, a.F, li, lg);
+  walk_units<T, DH, NFB, UPC, NS>(S, Sz, with_z, R, u0, u1, fk, gp, mseq, HD, w.h * DH, col, a.F, li, lg,
+                                  [](int) {});
 
-  float* dst = a.seg_state + (((w.b * a.H + w.h) * a.nseg + w.seg) * (int64_t)DH) * Fh;
+  const int64_t slice_seg = (((w.b * a.H + w.h) * nslices + w.fsl) * (int64_t)a.nseg + w.seg);
 #pragma unroll
   for (int eb = 0; eb < DH / 16; ++eb)
 #pragma unroll
     for (int fb = 0; fb < NFB; ++fb)
-#pragma unroll
-      for (int r = 0; r < 4; ++r) dst[(int64_t)(eb * 16 + lg * 4 + r) * Fh + cf + fb * 16 + li] = S[eb][fb][r];
+      *reinterpret_cast<f32x4*>(a.seg_state + seg_block<DH, NFB>(slice_seg, wave, eb, fb, lane)) = S[eb][fb];
   if (with_z && li == 0) {
     float* zd = a.seg_z + ((w.b * a.H + w.h) * a.nseg + w.seg) * DH;
 #pragma unroll
-    for (int eb = 0; eb < DH / 16; ++eb)
-#pragma unroll
-      for (int r = 0; r < 4; ++r) zd[eb * 16 + lg * 4 + r] = Sz[eb][r];
+    for (int eb = 0; eb < DH / 16; ++eb) *reinterpret_cast<f32x4*>(zd + eb * 16 + lg * 4) = Sz[eb];
   }
 }
 
-// Pass 2: exclusive prefix over segments, in place.  One thread per state
-// element; the segment values are loaded in independent batches of kBatch so
-// that the memory latency is paid once per batch, not once per segment.
-constexpr int kBatch = 16;
-__device__ __forceinline__ void exclusive_prefix(float* p, int64_t stride, int nseg) {
-  float run = 0.f;
-  for (int s0 = 0; s0 < nseg - 1; s0 += kBatch) {   // the last segment has no sum of its own
-    float v[kBatch];
-#pragma unroll
-    for (int u = 0; u < kBatch; ++u)
-      if (s0 + u < nseg - 1) v[u] = p[(int64_t)(s0 + u) * stride];
-#pragma unroll
-    for (int u = 0; u < kBatch; ++u)
-      if (s0 + u < nseg - 1) {
-        p[(int64_t)(s0 + u) * stride] = run;
-        run += v[u];
-      }
-  }
-  p[(int64_t)(nseg - 1) * stride] = run;
-}
-
-__global__ void scan_prefix_kernel(float* state, float* segz, int64_t per_bh, int nseg, int64_t nbh,
-                                   int dh) {
-  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  if (i < nbh * per_bh) {
-    const int64_t bh = i / per_bh, e = i % per_bh;
-    exclusive_prefix(state + bh * nseg * per_bh + e, per_bh, nseg);
-  }
-  if (i < nbh * dh) {
-    const int64_t bh = i / dh, e = i % dh;
-    exclusive_prefix(segz + bh * nseg * dh + e, dh, nseg);
-  }
-}
-
-// Pass 3: replay each segment from its prefix and emit n_old, z_old.
+// Pass 2: the segment's starting state (sum of the sums of the segments before
+// it), then the replay of its sources with the read-outs of n_old, z_old.
 template <typename T, int DH, int CH, int NFB>
-__global__ __launch_bounds__(kScanThreads) void scan_main_kernel(ScanArgs a) {
+__global__ __launch_bounds__(kScanThreads) __attribute__((amdgpu_waves_per_eu(1, 1)))
+void scan_main_kernel(ScanArgs a) {
   constexpr int FSC = kScanWaves * 16 * NFB, NIB = CH / 16, KE = DH / 32;
+  constexpr int QF = NIB * KE * 64;                 // query fragments per chunk
+  constexpr int QPT = QF / kScanThreads;            // ... per thread
+  constexpr int NQB = sizeof(T) == 2 ? 2 : 1;       // LDS query buffers
+  static_assert(QF % kScanThreads == 0, "query fragments per chunk");
+  __shared__ Frag<T> qs[NQB][QF];
   const int Fh = a.F / a.H, HD = a.H * DH, F = a.F;
-  const ScanWg w = scan_wg(blockIdx.x, Fh / FSC, a.H, a.nseg);
+  const int nslices = Fh / FSC;
+  const ScanWg w = scan_wg(blockIdx.x, nslices, a.H, a.nseg);
   const int lane = threadIdx.x & 63, li = lane & 15, lg = lane >> 4;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const bool with_z = w.fsl == 0 && wave == 0;
@@ -206,21 +222,89 @@ __global__ __launch_bounds__(kScanThreads) void scan_main_kernel(ScanArgs a) {
   const T* gp = static_cast<const T*>(a.gp);
   const int nchunks = a.Tp / CH, lag = a.window / CH;
   const int c0 = w.seg * a.chunks_per_seg, c1 = min(nchunks, c0 + a.chunks_per_seg);
+  constexpr int UPC = CH / unit_len<DH>(), NS = ring_sets<T, DH, true>();
+  const int u0 = c0 * UPC, u1 = c1 * UPC;
 
-  // state prefix of this segment
+  // query features of a destination chunk, fragment order, QPT per thread
+  Frag<T> qn[QPT];
+  auto load_q = [&](int c) {
+    const int64_t drow = mseq + (int64_t)min(c + lag, nchunks - 1) * CH;
+#pragma unroll
+    for (int q = 0; q < QPT; ++q) {
+      const int f = threadIdx.x + q * kScanThreads;
+      const int fl = f & 63, ke = (f >> 6) % KE, ib = f / (64 * KE);
+      qn[q] = load_frag<T>(fq + (drow + ib * 16 + (fl & 15)) * HD + w.h * DH + ke * 32 + (fl >> 4) * 8);
+    }
+  };
+  load_q(c0);   // first: the ring loads issued after it keep later waits on it precise
+
+  // first source units in flight
+  UnitRegs<T, DH, NFB> R[NS];
+#pragma unroll
+  for (int j = 0; j < NS - 1; ++j)
+    load_unit<T, DH, NFB>(R[j], fk, gp, mseq + (int64_t)min(u0 + j, u1 - 1) * unit_len<DH>(), HD, w.h * DH,
+                          col, F, li, lg);
+  // starting state: sum of the segment sums before this one
   f32x4 S[DH / 16][NFB], Sz[DH / 16];
+#pragma unroll
+  for (int eb = 0; eb < DH / 16; ++eb) {
+    Sz[eb] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int fb = 0; fb < NFB; ++fb) S[eb][fb] = f32x4{0.f, 0.f, 0.f, 0.f};
+  }
   {
-    const float* src = a.seg_state + (((w.b * a.H + w.h) * a.nseg + w.seg) * (int64_t)DH) * Fh;
-    const float* zs = a.seg_z + ((w.b * a.H + w.h) * a.nseg + w.seg) * DH;
+    const int64_t slice0 = ((w.b * a.H + w.h) * nslices + w.fsl) * (int64_t)a.nseg;
+    const float* zs = a.seg_z + (w.b * a.H + w.h) * (int64_t)a.nseg * DH;
+    // two batches in flight; loads past the last predecessor re-read it and are dropped
+    constexpr int PB = prefix_batch<DH, NFB>();
+    using Batch = f32x4[PB][DH / 16][NFB];
+    auto load_batch = [&](Batch& v, int s0) {
 #pragma unroll
-    for (int eb = 0; eb < DH / 16; ++eb)
+      for (int p = 0; p < PB; ++p)
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int e = eb * 16 + lg * 4 + r;
-        Sz[eb][r] = (w.seg == 0 || !with_z) ? 0.f : zs[e];
+        for (int eb = 0; eb < DH / 16; ++eb)
 #pragma unroll
-        for (int fb = 0; fb < NFB; ++fb) S[eb][fb][r] = w.seg == 0 ? 0.f : src[(int64_t)e * Fh + cf + fb * 16 + li];
+          for (int fb = 0; fb < NFB; ++fb)
+            v[p][eb][fb] = *reinterpret_cast<const f32x4*>(
+                a.seg_state + seg_block<DH, NFB>(slice0 + min(s0 + p, w.seg - 1), wave, eb, fb, lane));
+    };
+    auto add_batch = [&](const Batch& v, int s0) {
+#pragma unroll
+      for (int p = 0; p < PB; ++p) {
+        const float keep = s0 + p < w.seg ? 1.f : 0.f;
+#pragma unroll
+        for (int eb = 0; eb < DH / 16; ++eb)
+#pragma unroll
+          for (int fb = 0; fb < NFB; ++fb) S[eb][fb] += keep * v[p][eb][fb];
       }
+    };
+    if (w.seg > 0) {
+      Batch va, vb;
+      load_batch(va, 0);
+      for (int s0 = 0; s0 < w.seg; s0 += 2 * PB) {
+        load_batch(vb, s0 + PB);
+        add_batch(va, s0);
+        load_batch(va, s0 + 2 * PB);
+        add_batch(vb, s0 + PB);
+      }
+    }
+    if (with_z) {
+      constexpr int ZB = 8;
+      for (int s0 = 0; s0 < w.seg; s0 += ZB) {
+        f32x4 zv[ZB][DH / 16];
+#pragma unroll
+        for (int p = 0; p < ZB; ++p)
+#pragma unroll
+          for (int eb = 0; eb < DH / 16; ++eb)
+            zv[p][eb] = *reinterpret_cast<const f32x4*>(zs + (int64_t)min(s0 + p, w.seg - 1) * DH + eb * 16 + lg * 4);
+#pragma unroll
+        for (int p = 0; p < ZB; ++p) {
+          const float keep = s0 + p < w.seg ? 1.f : 0.f;
+#pragma unroll
+          for (int eb = 0; eb < DH / 16; ++eb) Sz[eb] += keep * zv[p][eb];
+        }
+      }
+    }
   }
 
   // destinations with no older chunk: zeros
@@ -239,17 +323,16 @@ __global__ __launch_bounds__(kScanThreads) void scan_main_kernel(ScanArgs a) {
     }
   }
 
-  constexpr int UPC = CH / unit_len<DH>();   // units per chunk
-  const int u0 = c0 * UPC, u1 = c1 * UPC;
-  UnitRegs<T, DH, NFB> r0, r1;
-  auto load = [&](UnitRegs<T, DH, NFB>& r, int u) {
-    load_unit<T, DH, NFB>(r, fk, gp, mseq + (int64_t)min(u, u1 - 1) * unit_len<DH>(), HD, w.h * DH, col, F, li, lg);
-  };
-  // read-out of S_{<cCH} for destination chunk c + lag: n_old^T = S^T phi_Q^T
-  auto readout = [&](int c) {
+  // chunk c: stage its query features, read S_{<cCH} out for destination chunk
+  // c + lag (n_old^T = S^T phi_Q^T), then fetch the next chunk's features
+  auto boundary = [&](int c) {
+    Frag<T>* buf = qs[NQB == 2 ? (c & 1) : 0];
+    if constexpr (NQB == 1) lds_sync();   // the previous read-out is done with the buffer
+#pragma unroll
+    for (int q = 0; q < QPT; ++q) buf[threadIdx.x + q * kScanThreads] = qn[q];
+    lds_sync();
     const int dchunk = c + lag;
     if (dchunk < nchunks) {
-      // read-out of S_{<cCH} for destination chunk d: n_old^T = S^T phi_Q^T
       Frag<T> sa[KE][NFB], za[KE];
 #pragma unroll
       for (int ke = 0; ke < KE; ++ke) {
@@ -262,8 +345,7 @@ __global__ __launch_bounds__(kScanThreads) void scan_main_kernel(ScanArgs a) {
       for (int ib = 0; ib < NIB; ++ib) {
         Frag<T> qb[KE];
 #pragma unroll
-        for (int ke = 0; ke < KE; ++ke)
-          qb[ke] = load_frag<T>(fq + (drow + ib * 16 + li) * HD + w.h * DH + ke * 32 + lg * 8);
+        for (int ke = 0; ke < KE; ++ke) qb[ke] = buf[(ib * KE + ke) * 64 + lane];
 #pragma unroll
         for (int fb = 0; fb < NFB; ++fb) {
           f32x4 n = {0.f, 0.f, 0.f, 0.f};
@@ -280,19 +362,9 @@ __global__ __launch_bounds__(kScanThreads) void scan_main_kernel(ScanArgs a) {
         }
       }
     }
+    if (c + 1 < c1) load_q(c + 1);   // after the stores: waits on it stay precise
   };
-  // the read-out for chunk c comes before its first unit is applied
-  if (u0 < u1) load(r0, u0);
-  for (int u = u0; u < u1; u += 2) {
-    load(r1, u + 1);
-    if (u % UPC == 0) readout(u / UPC);
-    apply_unit<T, DH, NFB>(S, Sz, with_z, r0);
-    if (u + 1 < u1) {
-      load(r0, u + 2);
-      if ((u + 1) % UPC == 0) readout((u + 1) / UPC);
-      apply_unit<T, DH, NFB>(S, Sz, with_z, r1);
-    }
-  }
+  walk_units<T, DH, NFB, UPC, NS>(S, Sz, with_z, R, u0, u1, fk, gp, mseq, HD, w.h * DH, col, F, li, lg, boundary);
 }
 
 template <typename T, int DH, int CH, int NFB>
@@ -305,11 +377,6 @@ hipError_t launch_scan_t(const ScanArgs& a, hipStream_t s) {
                        dim3(kScanThreads), 0, s, a);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    const int64_t per_bh = (int64_t)DH * Fh, nbh = (int64_t)a.B * a.H;
-    hipLaunchKernelGGL(scan_prefix_kernel, dim3((unsigned)ceil_div(nbh * per_bh, 256)), dim3(256), 0, s,
-                       a.seg_state, a.seg_z, per_bh, a.nseg, nbh, DH);
-    e = hipGetLastError();
-    if (e != hipSuccess) return e;
   }
   hipLaunchKernelGGL((scan_main_kernel<T, DH, CH, NFB>), dim3((unsigned)(groups * a.nseg)),
                      dim3(kScanThreads), 0, s, a);
@@ -318,7 +385,7 @@ hipError_t launch_scan_t(const ScanArgs& a, hipStream_t s) {
 
 template <typename T, int DH, int CH>
 hipError_t launch_scan_nfb(const ScanArgs& a, hipStream_t s) {
-  if ((a.F / a.H) % (kScanWaves * 32) == 0) return launch_scan_t<T, DH, CH, 2>(a, s);
+  if (a.slice == kScanWaves * 32) return launch_scan_t<T, DH, CH, 2>(a, s);
   return launch_scan_t<T, DH, CH, 1>(a, s);
 }
 
@@ -337,9 +404,14 @@ hipError_t launch_scan_dh(const ScanArgs& a, hipStream_t s) {
 ScanPlan wango_scan_plan(int B, int Tp, int F, int H, int chunk) {
   ScanPlan p;
   const int nchunks = Tp / chunk;
-  p.fs = ((F / H) % (kScanWaves * 32) == 0) ? kScanWaves * 32 : kScanWaves * 16;
-  const int64_t groups = (int64_t)B * H * ((F / H) / p.fs);
-  int64_t nseg = ceil_div(384, groups);
+  // Column slices of 128 when there are enough of them, else of 64: more
+  // slices need fewer segments, and every segment re-reads the sums of the
+  // segments before it.
+  const int Fh = F / H;
+  const bool wide = Fh % (kScanWaves * 32) == 0 && (int64_t)B * H * (Fh / (kScanWaves * 32)) >= 32;
+  p.fs = wide ? kScanWaves * 32 : kScanWaves * 16;
+  const int64_t groups = (int64_t)B * H * (Fh / p.fs);
+  int64_t nseg = ceil_div(256, groups);   // about one workgroup per compute unit
   if (nseg < 1) nseg = 1;
   if (nseg > nchunks) nseg = nchunks;
   p.chunks_per_seg = (int)ceil_div(nchunks, nseg);
@@ -351,6 +423,7 @@ hipError_t launch_wango_scan(const ScanArgs& a, const ScanPlan& p, bool bf, hipS
   ScanArgs aa = a;
   aa.nseg = p.nseg;
   aa.chunks_per_seg = p.chunks_per_seg;
+  aa.slice = p.fs;
   if (bf) return a.chunk == 128 ? launch_scan_dh<bf16, 128>(aa, s) : launch_scan_dh<bf16, 64>(aa, s);
   return a.chunk == 128 ? launch_scan_dh<float, 128>(aa, s) : launch_scan_dh<float, 64>(aa, s);
 }

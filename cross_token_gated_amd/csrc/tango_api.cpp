@@ -394,6 +394,9 @@ int block_common(const tango_shape_t* s, const tango_weights_t* w, bool wango, i
   if (wango) {
     pa.fq = base + L.fq;
     pa.fk = base + L.fk;
+  } else if (L.agg.split) {
+    pa.zero = reinterpret_cast<int*>(base + L.counters);
+    pa.zero_n = L.agg.n_split_tiles;
   }
   hipError_t e = launch_proj(pa, bf, io_bf, st);
   if (e != hipSuccess) return hip_fail(e, "projection kernel");
@@ -402,7 +405,7 @@ int block_common(const tango_shape_t* s, const tango_weights_t* w, bool wango, i
     aa.part = reinterpret_cast<float*>(base + L.part);
     aa.part_den = reinterpret_cast<float*>(base + L.part_den);
     aa.counters = reinterpret_cast<int*>(base + L.counters);
-    e = launch_tango_agg(aa, L.agg, bf, st);
+    e = launch_tango_agg(aa, L.agg, bf, true, st);
     if (e != hipSuccess) return hip_fail(e, "aggregation kernel");
   } else {
     float* n_old = reinterpret_cast<float*>(base + L.n_old);
@@ -513,7 +516,8 @@ int tango_stage_aggregate(const tango_shape_t* shape, const float* theta, const 
     aa.part = reinterpret_cast<float*>(base + L.part);
     aa.part_den = reinterpret_cast<float*>(base + L.part_den);
     aa.counters = reinterpret_cast<int*>(base + L.counters);
-    hipError_t e = launch_tango_agg(aa, L.agg, s->dtype == TANGO_BF16, static_cast<hipStream_t>(hip_stream));
+    hipError_t e = launch_tango_agg(aa, L.agg, s->dtype == TANGO_BF16, false,
+                                    static_cast<hipStream_t>(hip_stream));
     return e == hipSuccess ? ok() : hip_fail(e, "aggregation kernel");
   });
 }

@@ -121,16 +121,19 @@ def temperature(theta: np.ndarray) -> np.ndarray:
     return np.exp(np.minimum(np.asarray(theta, dtype=np.float64), LOG_TAU_MAX))
 
 
-def rope(u: np.ndarray, base: float) -> np.ndarray:
+def rope(u: np.ndarray, base: float, positions: Optional[np.ndarray] = None) -> np.ndarray:
     """Rotary position embedding on u [T, H, d_h] ([TANGO] §2.1, applied before
     unit normalisation).  Reading: interleaved pairs (2c, 2c+1), angle
-    i * base^(-2c/d_h) at 0-based position i.  base == 0 returns u unchanged."""
+    i * base^(-2c/d_h) at 0-based position i (row t sits at position t unless
+    ``positions`` gives the position of every row).  base == 0 returns u unchanged."""
     if base == 0:
         return u.copy()
     t_len, _, dh = u.shape
+    pos = np.arange(t_len, dtype=np.float64) if positions is None else \
+        np.asarray(positions, dtype=np.float64)
     c = np.arange(dh // 2, dtype=np.float64)
     inv_freq = base ** (-2.0 * c / dh)                      # [d_h/2]
-    ang = np.arange(t_len, dtype=np.float64)[:, None] * inv_freq[None, :]
+    ang = pos[:, None] * inv_freq[None, :]
     cos = np.cos(ang)[:, None, :]
     sin = np.sin(ang)[:, None, :]
     u0 = u[..., 0::2]
@@ -152,9 +155,11 @@ def unit_normalize(u: np.ndarray) -> np.ndarray:
 # Projections of one sequence
 # --------------------------------------------------------------------------
 
-def project(h: np.ndarray, p: BlockParams, cfg: BlockConfig) -> dict:
+def project(h: np.ndarray, p: BlockParams, cfg: BlockConfig,
+            positions: Optional[np.ndarray] = None) -> dict:
     """One sequence h [T, d] -> x, g, v [T, F], unit q, k [T, H, d_h]
-    ([TANGO] §2.1, eq. 2 and the head paragraph that follows eq. 3)."""
+    ([TANGO] §2.1, eq. 2 and the head paragraph that follows eq. 3).  Row t
+    sits at position t unless ``positions`` says otherwise (only RoPE sees it)."""
     t_len = h.shape[0]
     H, dh = cfg.n_heads, cfg.head_dim
     x = rms_norm(h, p.gain, cfg.rms_eps)
@@ -163,8 +168,8 @@ def project(h: np.ndarray, p: BlockParams, cfg: BlockConfig) -> dict:
     v = x @ p.w_v.T
     q = (x @ p.w_q.T).reshape(t_len, H, dh)
     k = (x @ p.w_k.T).reshape(t_len, H, dh)
-    q = unit_normalize(rope(q, cfg.rope_base))
-    k = unit_normalize(rope(k, cfg.rope_base))
+    q = unit_normalize(rope(q, cfg.rope_base, positions))
+    k = unit_normalize(rope(k, cfg.rope_base, positions))
     return {"x": x, "a": a, "g": g, "v": v, "qh": q, "kh": k}
 
 

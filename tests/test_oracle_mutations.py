@@ -43,12 +43,13 @@ def _null_unscaled(null_bias, head, rows):
     return np.full_like(n, math.exp(float(null_bias[head])))
 
 
-def _rope_wrong_sign(u, base):
+def _rope_wrong_sign(u, base, positions=None):
     if base == 0:
         return u.copy()
     t, _, dh = u.shape
     inv = base ** (-2.0 * np.arange(dh // 2) / dh)
-    ang = np.arange(t)[:, None] * inv[None]
+    pos = np.arange(t) if positions is None else np.asarray(positions, dtype=np.float64)
+    ang = pos[:, None] * inv[None]
     c, s = np.cos(ang)[:, None], np.sin(ang)[:, None]
     out = np.empty_like(u)
     out[..., 0::2] = u[..., 0::2] * c + u[..., 1::2] * s

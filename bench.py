@@ -1,6 +1,6 @@
 """Benchmark of the TANGO / WANGO block forward on one MI355X.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline] [--no-decode]
 
 One step runs every part of the block forward once at T = 8192 tokens:
   * TANGO, bf16 compute, B = 1, T = 8192, d = 512, F = 2048, q/k width 128,
@@ -24,6 +24,11 @@ Alongside, with HIP events on the launch stream:
     producing projection would otherwise leave them in (the warm-cache median
     is reported beside it).  The flush reads rather than fills: a fill leaves
     dirty lines whose write-back would land in the timed launch;
+  * decode: one autoregressive decode step (every layer) at position 8192 of
+    the decode workloads -- TANGO, 16 sequences, 4 stacked layers each with its
+    own key/gate cache; WANGO, 64 sequences, window 256 -- as decoded tokens
+    per second, and the algorithmic HBM bytes of the step (weights, the state
+    each layer must touch, x and out) over its median time against 8 TB/s;
   * cpu_baseline: the float64 CPU oracle on a bounded sample of the same work
     (one of the four TANGO applications, scaled by 4, plus the WANGO block).
 The "traffic" of the two rooflines is the HBM traffic per launch measured by
@@ -59,6 +64,7 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--kernel-loops", type=int, default=None,
                     help="launches per roofline measurement (default: --steps)")
+    ap.add_argument("--no-decode", action="store_true", help="skip the decode-step measurement")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a plain 256 MiB device copy (for counter calibration)")
     return ap.parse_args()
@@ -136,6 +142,120 @@ def cpu_baseline(wt, wg) -> dict:
             "sample": (f"one of the {wt.repeats} TANGO T={wt.T} applications (time x{wt.repeats}) "
                        f"plus the WANGO T={wg.T} application, float64 numpy; "
                        f"{secs:.1f} s for one step")}
+
+
+def _align256(n: int) -> int:
+    return (n + 255) // 256 * 256
+
+
+def decode_bytes(w, es: int, io_es: int) -> float:
+    """Algorithmic HBM bytes of one decode step over all layers: the weights
+    once per layer, the state each layer must touch (TANGO: keys and gates of
+    positions 0..p read, the new row written; WANGO: S read and written, the
+    window's and the leaving token's keys and gates read, the new row
+    written), x read and out written."""
+    p = w.T - 1
+    HD, F, d = w.n_heads * w.head_dim, w.d_gate, w.d_model
+    weights = ((2 * F + 2 * HD) * d + d * F) * es
+    row = (HD + F) * es
+    if w.mode == "tango":
+        state = w.B * (p + 1) * row + w.B * row
+    else:
+        state = 2 * w.B * w.n_heads * w.head_dim * (F // w.n_heads) * 4 + w.B * (w.window + 2) * row
+    return float(w.repeats * (weights + state + 2 * w.B * d * io_es))
+
+
+def decode_bench(steps: int, warmup: int, dev, stream) -> dict:
+    """One decode step (every layer) at position T - 1 of the decode workloads,
+    timed with HIP events.  The state is filled with synthetic content of the
+    right kind (unit keys, SiLU gates, positive running sums) rather than by
+    decoding 8192 positions first: every decode kernel does the same work
+    whatever the values (the parity tests decode real prefixes)."""
+    import torch
+
+    from cross_token_gated_amd import api
+    from cross_token_gated_amd import workload as wl
+    from tests.gpu_common import TORCH_DTYPE, block_weights
+
+    out = {}
+    for name, w in wl.DECODE_WORKLOADS.items():
+        inp = wl.make_inputs(w.scaled(T=1))          # weights and one input row per sequence
+        bw = block_weights(w, inp, dev)
+        io = TORCH_DTYPE[w.io]
+        es, io_es = (2 if w.dtype == "bf16" else 4), (2 if w.io == "bf16" else 4)
+        cap = w.T if w.mode == "tango" else 1
+        shape = api.decode_shape(w.B, cap, bw, io, w.d_model, w.rope_base, w.rms_eps)
+        if w.mode == "tango":
+            ns, nw = api.tango_decode_state_size(shape), api.tango_decode_workspace_size(shape)
+            rows = w.T
+        else:
+            ns = api.wango_decode_state_size(shape, w.window, w.head_dim)
+            nw = api.wango_decode_workspace_size(shape, w.window, w.head_dim)
+            rows = w.window + 1
+        HD, F = w.n_heads * w.head_dim, w.d_gate
+        gen = torch.Generator(device=dev)
+        gen.manual_seed(w.seed)
+        states = []
+        for _ in range(w.repeats):
+            st = torch.empty(ns, dtype=torch.uint8, device=dev)
+            kb = w.B * rows * HD * es
+            k = st[:kb].view(TORCH_DTYPE[w.dtype]).view(w.B * rows, w.n_heads, w.head_dim)
+            g = st[_align256(kb):_align256(kb) + w.B * rows * F * es].view(TORCH_DTYPE[w.dtype]).view(w.B * rows, F)
+            for r0 in range(0, w.B * rows, 8192):
+                r1 = min(w.B * rows, r0 + 8192)
+                kk = torch.randn(r1 - r0, w.n_heads, w.head_dim, device=dev, generator=gen)
+                k[r0:r1] = torch.nn.functional.normalize(kk, dim=-1).to(k.dtype)
+                g[r0:r1] = torch.nn.functional.silu(torch.randn(r1 - r0, F, device=dev, generator=gen)).to(g.dtype)
+            if w.mode == "wango":
+                so = _align256(_align256(kb) + w.B * rows * F * es)
+                ne = w.B * w.n_heads * w.head_dim * (F // w.n_heads)
+                st[so:so + ne * 4].view(torch.float32).copy_(
+                    torch.rand(ne, device=dev, generator=gen) * (w.T - w.window) * 0.02)
+                zo = _align256(so + ne * 4)
+                nz = w.B * 2 * w.n_heads * w.head_dim
+                st[zo:zo + nz * 4].view(torch.float32).copy_(
+                    torch.rand(nz, device=dev, generator=gen) * (w.T - w.window) * 0.02)
+            states.append(st)
+        ws = api.workspace(nw, dev)
+        x = torch.randn(w.B, w.d_model, device=dev, generator=gen).to(io)
+        y = torch.empty_like(x)
+        pos = torch.full((w.B,), w.T - 1, dtype=torch.int32, device=dev)
+
+        def step():
+            cur, nxt = x, y
+            for r in range(w.repeats):
+                if w.mode == "tango":
+                    api.tango_decode_step(shape, bw, pos, cur, nxt, states[r], ws, stream)
+                else:
+                    api.wango_decode_step(shape, bw, w.window, w.head_dim, pos, cur, nxt, states[r], ws,
+                                          stream)
+                cur, nxt = nxt, cur
+
+        for _ in range(warmup):
+            step()
+        torch.cuda.synchronize()
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+              for _ in range(steps)]
+        for a, b in ev:
+            a.record(stream)
+            step()
+            b.record(stream)
+        torch.cuda.synchronize()
+        t = sorted(a.elapsed_time(b) for a, b in ev)
+        ms = t[steps // 2] if steps % 2 else 0.5 * (t[steps // 2 - 1] + t[steps // 2])
+        nbytes = decode_bytes(w, es, io_es)
+        ach = nbytes / (ms * 1e-3)
+        out[name] = {
+            "tokens_per_s": w.B / (ms * 1e-3), "ms_per_step": ms, "sequences": w.B, "position": w.T - 1,
+            "layers": w.repeats, "window": w.window or None,
+            "roofline": {"kernel": "whole decode step (row prep, projections, aggregation, output) x layers",
+                         "bound": "hbm", "achieved": ach / 1e9, "peak": PEAK_HBM_BYTES / 1e9, "unit": "GB/s",
+                         "frac": ach / PEAK_HBM_BYTES, "bytes_per_step": nbytes}}
+        print(f"[bench] decode {name}: {ms * 1e3:.1f} us/step, {w.B / (ms * 1e-3):.0f} tokens/s, "
+              f"{ach / 1e9:.0f} GB/s ({100 * ach / PEAK_HBM_BYTES:.1f}% of HBM peak)", file=sys.stderr, flush=True)
+        del states, ws
+        torch.cuda.empty_cache()
+    return out
 
 
 def main():
@@ -322,6 +442,8 @@ def main():
         for _ in range(3):
             dst.copy_(src)
         torch.cuda.synchronize()
+    if not args.no_decode:
+        result["decode"] = decode_bench(loops, min(args.warmup, 3), dev, stream)
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(wt, wg)
     print(json.dumps(result), flush=True)

@@ -23,6 +23,8 @@ EXPORTS = [
     "tango_status_string", "tango_last_error", "tango_version",
     "tango_proj_workspace_size", "tango_stage_proj", "wango_stage_proj", "tango_stage_aggregate", "tango_stage_out",
     "wango_stage_scan", "wango_stage_band",
+    "tango_decode_state_size", "tango_decode_workspace_size", "tango_decode_step",
+    "wango_decode_state_size", "wango_decode_workspace_size", "wango_decode_step",
 ]
 
 
@@ -76,6 +78,12 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
         "tango_stage_out": (ctypes.c_int, [S, vp, vp, vp, vp, vp, vp]),
         "wango_stage_scan": (ctypes.c_int, [S, i32, i32, vp, vp, vp, vp, vp, vp, sz, vp]),
         "wango_stage_band": (ctypes.c_int, [S, vp, vp, i32, i32, vp, vp, vp, vp, vp, vp, vp]),
+        "tango_decode_state_size": (sz, [S]),
+        "tango_decode_workspace_size": (sz, [S]),
+        "tango_decode_step": (ctypes.c_int, [S, W, vp, vp, vp, vp, sz, vp, sz, vp]),
+        "wango_decode_state_size": (sz, [S, i32, i32]),
+        "wango_decode_workspace_size": (sz, [S, i32, i32]),
+        "wango_decode_step": (ctypes.c_int, [S, W, i32, i32, vp, vp, vp, vp, sz, vp, sz, vp]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(lib, name)

@@ -167,3 +167,47 @@ def wango_stage_band(shape: Shape, theta, null_bias, window: int, chunk: int, qh
     check(load().wango_stage_band(ctypes.byref(shape), _ptr(theta), _ptr(null_bias), window, chunk,
                                   _ptr(qh), _ptr(kh), _ptr(gp), _ptr(n_old), _ptr(z_old),
                                   _ptr(gbar), _stream(stream)))
+
+
+# ---- autoregressive decode ---------------------------------------------------------
+
+def decode_shape(B: int, capacity: int, w: BlockWeights, io_dtype: torch.dtype, d: int,
+                 rope_base: float = 10000.0, rms_eps: float = 1e-6) -> Shape:
+    """Shape of a decode call: B sequences; capacity = TANGO cache positions
+    (WANGO: any value >= 1)."""
+    return make_shape(B, capacity, d, w.w_g.shape[0], w.n_heads, w.head_dim, w.w_g.dtype, rope_base,
+                      rms_eps, io_dtype=io_dtype)
+
+
+def tango_decode_state_size(shape: Shape) -> int:
+    return int(load().tango_decode_state_size(ctypes.byref(shape)))
+
+
+def tango_decode_workspace_size(shape: Shape) -> int:
+    return int(load().tango_decode_workspace_size(ctypes.byref(shape)))
+
+
+def wango_decode_state_size(shape: Shape, window: int, phi_dim: int) -> int:
+    return int(load().wango_decode_state_size(ctypes.byref(shape), window, phi_dim))
+
+
+def wango_decode_workspace_size(shape: Shape, window: int, phi_dim: int) -> int:
+    return int(load().wango_decode_workspace_size(ctypes.byref(shape), window, phi_dim))
+
+
+def tango_decode_step(shape: Shape, w: BlockWeights, pos: torch.Tensor, x: torch.Tensor, out: torch.Tensor,
+                      state: torch.Tensor, ws: torch.Tensor, stream=None) -> None:
+    """One TANGO decode step: out[B, d] at positions pos[B] (int32, device)."""
+    cw = w.c_struct()
+    check(load().tango_decode_step(ctypes.byref(shape), ctypes.byref(cw), _ptr(pos), _ptr(x), _ptr(out),
+                                   _ptr(state), state.numel(), _ptr(ws), ws.numel(), _stream(stream)))
+
+
+def wango_decode_step(shape: Shape, w: BlockWeights, window: int, phi_dim: int, pos: torch.Tensor,
+                      x: torch.Tensor, out: torch.Tensor, state: torch.Tensor, ws: torch.Tensor,
+                      stream=None) -> None:
+    """One WANGO decode step: out[B, d] at positions pos[B] (int32, device)."""
+    cw = w.c_struct()
+    check(load().wango_decode_step(ctypes.byref(shape), ctypes.byref(cw), window, phi_dim, _ptr(pos),
+                                   _ptr(x), _ptr(out), _ptr(state), state.numel(), _ptr(ws), ws.numel(),
+                                   _stream(stream)))

@@ -754,6 +754,20 @@ hipError_t launch_out_t(const OutArgs& a, hipStream_t s) {
   return hipGetLastError();
 }
 
+template <typename T, typename IO>
+hipError_t launch_prep_t(const ProjArgs& a, hipStream_t s) {
+  using CF = ProjCfg<T>;
+  const int64_t M = (int64_t)a.B * a.Tp;
+  hipLaunchKernelGGL((prep_kernel<T, IO, CF::AS>), dim3((unsigned)(M / (kThreads / 64))), dim3(kThreads),
+                     0, s, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_prep(const ProjArgs& a, bool bf, bool io_bf, hipStream_t s) {
+  if (bf) return io_bf ? launch_prep_t<bf16, bf16>(a, s) : launch_prep_t<bf16, float>(a, s);
+  return io_bf ? launch_prep_t<float, bf16>(a, s) : launch_prep_t<float, float>(a, s);
+}
+
 hipError_t launch_proj(const ProjArgs& a, bool bf, bool io_bf, hipStream_t s) {
   if (bf) return io_bf ? launch_proj_t<bf16, bf16>(a, s) : launch_proj_t<bf16, float>(a, s);
   return io_bf ? launch_proj_t<float, bf16>(a, s) : launch_proj_t<float, float>(a, s);

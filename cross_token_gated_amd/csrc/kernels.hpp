@@ -110,4 +110,42 @@ hipError_t launch_zero_i32(int* p, int64_t n, hipStream_t s);
 // (once per device).
 hipError_t gemm_kernels_init();
 
+// Row-prep kernel alone (RMSNorm scales and operand parts of h * gain).
+hipError_t launch_prep(const ProjArgs& a, bool bf, bool io_bf, hipStream_t s);
+
+// ---- autoregressive decode -------------------------------------------------
+
+constexpr int kDecChunk = 128;        // TANGO cache positions per workgroup
+constexpr int kDecMaxWindow = 2048;   // largest WANGO window of the decode kernels
+
+struct DecArgs {
+  int B;                   // sequences (one new token each)
+  int Mp;                  // B rounded up to kRowPad (rows of the scratch operands)
+  int d, F, H, dh, HD;
+  int P;                   // state rows per sequence: TANGO capacity, WANGO window + 1
+  int window;              // WANGO window W; 0 = TANGO
+  int nch;                 // TANGO: chunks of kDecChunk positions per sequence
+  float rope_base;
+  const int* pos;          // [B] position of each new token (device)
+  const void *w_g, *w_v, *w_q, *w_k, *w_o;
+  const float* theta;
+  const float* null_bias;  // or null
+  void* kc;                // state: unit keys [B][P][HD]
+  void* gc;                // state: gates [B][P][F]
+  float* S;                // WANGO state: [B][H][dh][F/H]
+  float* z;                // WANGO state: [B][2][H][dh], the copy after position p in slot p % 2
+  const void* xs;          // scratch: operand parts of h * gain [AS][Mp][d]
+  const float* rinv;       // scratch: RMSNorm scales [Mp]
+  void* v;                 // scratch: [Mp][F]
+  void* q;                 // scratch: unit queries [Mp][HD]
+  float* part;             // scratch (TANGO): [B][nch][F + 64] partial sums
+  void* gv;                // scratch: operand parts of gbar * v [AS][Mp][F]
+  const void* x;           // [B][d] in the I/O dtype
+  void* out;               // [B][d] in the I/O dtype (may equal x)
+};
+
+// Operand parts of the decode GEMMs for the compute dtype (2 for bf16).
+int decode_parts(bool bf);
+hipError_t launch_decode(const DecArgs& a, bool bf, bool io_bf, hipStream_t s);
+
 }  // namespace tango

@@ -614,4 +614,206 @@ int wango_stage_band(const tango_shape_t* shape, const float* theta, const float
   });
 }
 
+
+// ---- autoregressive decode -----------------------------------------------------
+
+}  // extern "C"
+
+namespace {
+
+struct DecLayout {
+  // state
+  size_t kc, gc, S, z, state_total;
+  // workspace
+  size_t xs, rinv, v, q, part, gv, ws_total;
+  int P, nch;
+  int64_t Mp;
+};
+
+int check_decode(const tango_shape_t* s, bool wango, int32_t window, int32_t phi_dim) {
+  int rc = check_shape(s);
+  if (rc) return rc;
+  if (wango) {
+    if (window < 1) return fail(TANGO_ERR_SHAPE, "window %d < 1", window);
+    if (phi_dim != s->head_dim)
+      return fail(TANGO_ERR_SHAPE, "phi_dim %d must equal head_dim %d (phi acts elementwise)", phi_dim,
+                  s->head_dim);
+    if (window > kDecMaxWindow)
+      return fail(TANGO_ERR_UNSUPPORTED, "window %d: the decode kernels take at most %d", window,
+                  kDecMaxWindow);
+  }
+  if (s->n_heads > 32) return fail(TANGO_ERR_UNSUPPORTED, "n_heads %d: decode takes at most 32", s->n_heads);
+  return TANGO_OK;
+}
+
+DecLayout make_dec_layout(const tango_shape_t* s, bool wango, int32_t window) {
+  DecLayout L{};
+  const size_t es = elem_size(s->dtype);
+  const int64_t B = s->batch, F = s->d_gate, HD = (int64_t)s->n_heads * s->head_dim;
+  L.P = wango ? window + 1 : s->seq_len;
+  L.nch = wango ? 0 : (L.P + kDecChunk - 1) / kDecChunk;
+  L.Mp = pad_rows(B);
+  size_t off = 0;
+  auto take = [&](size_t bytes) {
+    const size_t o = off;
+    off = align256(off + bytes);
+    return o;
+  };
+  L.kc = take((size_t)B * L.P * HD * es);
+  L.gc = take((size_t)B * L.P * F * es);
+  if (wango) {
+    L.S = take((size_t)B * s->n_heads * s->head_dim * (F / s->n_heads) * sizeof(float));
+    L.z = take((size_t)B * 2 * s->n_heads * s->head_dim * sizeof(float));
+  }
+  L.state_total = off;
+  off = 0;
+  const bool bf = s->dtype == TANGO_BF16;
+  L.xs = take(proj_parts_bytes(L.Mp, s->d_model, bf));
+  L.rinv = take((size_t)L.Mp * sizeof(float));
+  L.v = take((size_t)L.Mp * F * es);
+  L.q = take((size_t)L.Mp * HD * es);
+  if (!wango) L.part = take((size_t)B * L.nch * (F + 64) * sizeof(float));
+  L.gv = take((size_t)decode_parts(bf) * L.Mp * F * es);
+  L.ws_total = off;
+  return L;
+}
+
+int decode_common(const tango_shape_t* s, const tango_weights_t* w, bool wango, int32_t window,
+                  int32_t phi_dim, const int32_t* pos, const void* x, void* out, void* state,
+                  size_t state_bytes, void* ws, size_t ws_bytes, void* stream) {
+  int rc = check_decode(s, wango, window, phi_dim);
+  if (rc) return rc;
+  if ((rc = check_weights(w, true))) return rc;
+  if (!pos || !x || !out) return fail(TANGO_ERR_NULL, "pos, x or out is NULL");
+  if (!state) return fail(TANGO_ERR_NULL, "state is NULL");
+  if (!ws) return fail(TANGO_ERR_NULL, "workspace is NULL");
+  const DecLayout L = make_dec_layout(s, wango, window);
+  if (state_bytes < L.state_total)
+    return fail(TANGO_ERR_WORKSPACE, "state of %zu bytes is smaller than the %zu needed", state_bytes,
+                L.state_total);
+  if (ws_bytes < L.ws_total)
+    return fail(TANGO_ERR_WORKSPACE, "workspace of %zu bytes is smaller than the %zu needed", ws_bytes,
+                L.ws_total);
+  const size_t es = elem_size(s->dtype);
+  const size_t d = s->d_model, F = s->d_gate, HD = (size_t)s->n_heads * s->head_dim;
+  const size_t xb = (size_t)s->batch * d * elem_size(s->io_dtype);
+  const Range ins[] = {{x, xb, "x"},
+                       {pos, (size_t)s->batch * sizeof(int32_t), "pos"},
+                       {w->w_g, F * d * es, "w_g"},
+                       {w->w_v, F * d * es, "w_v"},
+                       {w->w_q, HD * d * es, "w_q"},
+                       {w->w_k, HD * d * es, "w_k"},
+                       {w->w_o, d * F * es, "w_o"},
+                       {w->rms_gain, d * es, "rms_gain"},
+                       {w->theta, s->n_heads * sizeof(float), "theta"},
+                       {w->null_bias, s->n_heads * sizeof(float), "null_bias"}};
+  const Range outs[] = {{out, xb, "out"}, {state, L.state_total, "state"}, {ws, L.ws_total, "workspace"}};
+  // pos only needs 4-byte alignment
+  for (const Range& r : ins)
+    if (r.p && r.p != pos && !aligned(r.p)) return fail(TANGO_ERR_ALIGN, "%s is not 16-byte aligned", r.name);
+  if (((uintptr_t)pos & 3u) != 0) return fail(TANGO_ERR_ALIGN, "pos is not 4-byte aligned");
+  Range ins16[9];
+  int n16 = 0;
+  for (const Range& r : ins)
+    if (r.p != pos) ins16[n16++] = r;
+  if ((rc = check_ranges(ins16, n16, outs, 3, x, out))) return rc;
+  for (const Range& o : outs)
+    if (overlap(o, ins[1])) return fail(TANGO_ERR_ALIAS, "%s overlaps pos", o.name);
+  if ((rc = ensure_init())) return rc;
+
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  const bool bf = s->dtype == TANGO_BF16, io_bf = s->io_dtype == TANGO_BF16;
+  char* sb = static_cast<char*>(state);
+  char* wb = static_cast<char*>(ws);
+  // row prep over the B new tokens taken as one sequence of B rows
+  ProjArgs pa{};
+  pa.x = x;
+  pa.gain = w->rms_gain;
+  pa.xs = wb + L.xs;
+  pa.rinv = reinterpret_cast<float*>(wb + L.rinv);
+  pa.B = 1;
+  pa.T = s->batch;
+  pa.Tp = (int)L.Mp;
+  pa.d = s->d_model;
+  pa.eps = s->rms_eps;
+  hipError_t e = launch_prep(pa, bf, io_bf, st);
+  if (e != hipSuccess) return hip_fail(e, "row-prep kernel");
+  DecArgs a{};
+  a.B = s->batch;
+  a.Mp = (int)L.Mp;
+  a.d = s->d_model;
+  a.F = s->d_gate;
+  a.H = s->n_heads;
+  a.dh = s->head_dim;
+  a.HD = (int)HD;
+  a.P = L.P;
+  a.window = wango ? window : 0;
+  a.nch = L.nch;
+  a.rope_base = s->rope_base;
+  a.pos = pos;
+  a.w_g = w->w_g;
+  a.w_v = w->w_v;
+  a.w_q = w->w_q;
+  a.w_k = w->w_k;
+  a.w_o = w->w_o;
+  a.theta = w->theta;
+  a.null_bias = w->null_bias;
+  a.kc = sb + L.kc;
+  a.gc = sb + L.gc;
+  a.S = wango ? reinterpret_cast<float*>(sb + L.S) : nullptr;
+  a.z = wango ? reinterpret_cast<float*>(sb + L.z) : nullptr;
+  a.xs = wb + L.xs;
+  a.rinv = reinterpret_cast<const float*>(wb + L.rinv);
+  a.v = wb + L.v;
+  a.q = wb + L.q;
+  a.part = wango ? nullptr : reinterpret_cast<float*>(wb + L.part);
+  a.gv = wb + L.gv;
+  a.x = x;
+  a.out = out;
+  e = launch_decode(a, bf, io_bf, st);
+  return e == hipSuccess ? ok() : hip_fail(e, "decode kernels");
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t tango_decode_state_size(const tango_shape_t* shape) {
+  if (check_decode(shape, false, 0, 0)) return 0;
+  return make_dec_layout(shape, false, 0).state_total;
+}
+
+size_t tango_decode_workspace_size(const tango_shape_t* shape) {
+  if (check_decode(shape, false, 0, 0)) return 0;
+  return make_dec_layout(shape, false, 0).ws_total;
+}
+
+size_t wango_decode_state_size(const tango_shape_t* shape, int32_t window, int32_t phi_dim) {
+  if (check_decode(shape, true, window, phi_dim)) return 0;
+  return make_dec_layout(shape, true, window).state_total;
+}
+
+size_t wango_decode_workspace_size(const tango_shape_t* shape, int32_t window, int32_t phi_dim) {
+  if (check_decode(shape, true, window, phi_dim)) return 0;
+  return make_dec_layout(shape, true, window).ws_total;
+}
+
+int tango_decode_step(const tango_shape_t* shape, const tango_weights_t* weights, const int32_t* pos,
+                      const void* x, void* out, void* state, size_t state_bytes, void* workspace,
+                      size_t workspace_bytes, void* hip_stream) {
+  return guarded([&] {
+    return decode_common(shape, weights, false, 0, 0, pos, x, out, state, state_bytes, workspace,
+                         workspace_bytes, hip_stream);
+  });
+}
+
+int wango_decode_step(const tango_shape_t* shape, const tango_weights_t* weights, int32_t window,
+                      int32_t phi_dim, const int32_t* pos, const void* x, void* out, void* state,
+                      size_t state_bytes, void* workspace, size_t workspace_bytes, void* hip_stream) {
+  return guarded([&] {
+    return decode_common(shape, weights, true, window, phi_dim, pos, x, out, state, state_bytes, workspace,
+                         workspace_bytes, hip_stream);
+  });
+}
+
 }  // extern "C"

@@ -75,6 +75,20 @@ WORKLOADS = {
 }
 WORKLOAD_ORDER = list(WORKLOADS)
 
+# Decode workloads: one new token per sequence at position 8192 -- the state
+# holds the 8192 earlier positions -- in the geometry of the T = 8192 workloads
+# above (TANGO: one head of 128, stacked 4 times, each application with its own
+# state; WANGO: two heads of 64, window 256).  B is the number of sequences
+# decoded together; T - 1 is the position of the timed step.
+DECODE_WORKLOADS = {
+    "tango_decode_bf16_b16_p8192_r4": Workload("tango_decode_bf16_b16_p8192_r4", "tango", "bf16", 16,
+                                               8193, 512, 2048, 1, 128, repeats=4, seed=5,
+                                               io_dtype="f32"),
+    "wango_decode_bf16_b64_p8192_w256": Workload("wango_decode_bf16_b64_p8192_w256", "wango", "bf16",
+                                                 64, 8193, 512, 2048, 2, 64, window=256, seed=6,
+                                                 io_dtype="f32"),
+}
+
 
 def round_f32(a: np.ndarray) -> np.ndarray:
     """float64 -> float32 (round to nearest even)."""

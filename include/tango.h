@@ -60,7 +60,7 @@
 extern "C" {
 #endif
 
-#define TANGO_ABI_VERSION 2
+#define TANGO_ABI_VERSION 3
 
 typedef enum { TANGO_F32 = 0, TANGO_BF16 = 1 } tango_dtype_t;
 
@@ -134,6 +134,51 @@ int wango_block_fwd(const tango_shape_t* shape, const tango_weights_t* weights,
                     int32_t window, int32_t phi_dim, int32_t chunk,
                     const void* x, void* out, void* workspace, size_t workspace_bytes,
                     void* hip_stream);
+
+/* ---- Autoregressive decode ----------------------------------------------
+ *
+ * One new token per sequence per call.  A step returns the block output at the
+ * token's position p -- row p of the block forward over the sequence's prefix,
+ * since no source lies after its destination (eq. 5) -- and advances a state
+ * kept between calls.  TANGO's state is every unit key and gate so far (eq. 6
+ * sums over the whole prefix).  WANGO's is the running sums S, z of §2.2
+ * eq. 10, to which the token leaving the window is added when the position
+ * advances, plus the keys and gates of the last window + 1 positions: a state
+ * whose size does not depend on the position (§6.1).
+ *
+ *   shape      batch = B sequences; seq_len = TANGO cache capacity P (positions
+ *              0 .. P-1 can be decoded); WANGO ignores seq_len (>= 1).
+ *   pos        DEVICE int32 [B]: position of each sequence's new token.  Position
+ *              0 starts a sequence afresh (no state needs clearing first); a step
+ *              at p > 0 must follow the step at p - 1 of the same sequence on
+ *              the same state.  A sequence with pos < 0 (TANGO: or >= P) is
+ *              skipped: its out row is NaN and its state is not touched.  (Only
+ *              the kernels see pos, so this is not a validation error.)
+ *   x, out     [B, d] in io_dtype; out may equal x.
+ *   state      DEVICE buffer of *_decode_state_size bytes, kept by the caller
+ *              between steps, one per stacked application; never shared by
+ *              calls that can run concurrently.  Layout (dtype unless noted):
+ *                keys  [B][R][H*d_h] unit keys,  gates [B][R][F],
+ *                TANGO: R = P, position j in row j;
+ *                WANGO: R = window + 1, position j in row j mod R, then
+ *                  S [B][H][d_h][F/H] float32 and z [B][2][H][d_h] float32
+ *                  (after the step at p, z is in copy p mod 2);
+ *              each array starts at a 256-byte boundary.
+ *   workspace  per-call scratch of *_decode_workspace_size bytes.
+ * Supported shapes: those of the block calls, with n_heads <= 32 and (WANGO)
+ * window <= 2048; the size functions return 0 for anything else.
+ */
+size_t tango_decode_state_size(const tango_shape_t* shape);
+size_t tango_decode_workspace_size(const tango_shape_t* shape);
+int tango_decode_step(const tango_shape_t* shape, const tango_weights_t* weights, const int32_t* pos,
+                      const void* x, void* out, void* state, size_t state_bytes, void* workspace,
+                      size_t workspace_bytes, void* hip_stream);
+
+size_t wango_decode_state_size(const tango_shape_t* shape, int32_t window, int32_t phi_dim);
+size_t wango_decode_workspace_size(const tango_shape_t* shape, int32_t window, int32_t phi_dim);
+int wango_decode_step(const tango_shape_t* shape, const tango_weights_t* weights, int32_t window,
+                      int32_t phi_dim, const int32_t* pos, const void* x, void* out, void* state,
+                      size_t state_bytes, void* workspace, size_t workspace_bytes, void* hip_stream);
 
 /* ---- Diagnostics --------------------------------------------------------- */
 

@@ -131,3 +131,26 @@ def oracle_config(w: wl.Workload) -> O.BlockConfig:
 def oracle_stack(w: wl.Workload, inp: wl.Inputs, form: str = "direct") -> np.ndarray:
     return O.block_stack(np.asarray(inp.h, dtype=np.float64), oracle_params(inp), oracle_config(w),
                          repeats=w.repeats, io_dtype=w.io, form=form)
+
+
+def oracle_block_rows(h_seq: np.ndarray, p: O.BlockParams, cfg: O.BlockConfig, rows) -> np.ndarray:
+    """Rows ``rows`` of one block application over one sequence h_seq [T, d],
+    composed from the oracle's own pieces (projections of every position, the
+    pairwise weights of just those destination rows, the null term): for long
+    sequences where the whole forward would take minutes."""
+    h_seq = np.asarray(h_seq, dtype=np.float64)
+    parts = O.project(h_seq, p, cfg)
+    tau = O.temperature(p.theta)
+    H = cfg.n_heads
+    fh = parts["g"].shape[1] // H
+    out = []
+    for i in rows:
+        gbar = np.empty(parts["g"].shape[1])
+        for a in range(H):
+            sl = slice(int(i), int(i) + 1)
+            m = O.pair_weights(parts["qh"], parts["kh"], tau, a, sl, cfg.mode, cfg.window)[0]
+            num = m @ parts["g"][:, a * fh:(a + 1) * fh]
+            den = m.sum() + O.null_weight(p.null_bias, a, sl)[0]
+            gbar[a * fh:(a + 1) * fh] = num / den
+        out.append(h_seq[i] + p.w_o @ (gbar * parts["v"][i]))
+    return np.stack(out)

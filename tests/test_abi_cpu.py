@@ -156,3 +156,36 @@ def test_stage_entry_points_validate(lib):
     assert lib.wango_stage_scan(ctypes.byref(s), 0, 128, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 0, None) == -2
     assert lib.wango_stage_scan(ctypes.byref(s), 256, 96, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 0, None) == -5
     assert lib.wango_stage_band(ctypes.byref(s), FAKE, None, 0, 128, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None) == -2
+
+
+def test_decode_entry_points_validate(lib):
+    s = shape(batch=16, seq_len=8448)
+    w = weights()
+    ns, nw = lib.tango_decode_state_size(ctypes.byref(s)), lib.tango_decode_workspace_size(ctypes.byref(s))
+    # state: keys and gates of every position of every sequence
+    assert ns >= 16 * 8448 * (128 + 2048) * 2 and nw > 0
+    pos = FAKE + 0x90000000
+    args = lambda **kw: dict(dict(pos=pos, x=FAKE, out=FAKE + 0x60000000, st=FAKE + 0x100000000, ns=ns,  # noqa: E731
+                                  ws=FAKE + 0x200000000, nw=nw), **kw)
+
+    def call(**kw):
+        a = args(**kw)
+        return lib.tango_decode_step(ctypes.byref(s), ctypes.byref(w), a["pos"], a["x"], a["out"], a["st"],
+                                     a["ns"], a["ws"], a["nw"], None)
+    assert call(pos=None) == -1
+    assert call(st=None) == -1
+    assert call(ns=ns - 1) == -6
+    assert call(nw=nw - 1) == -6
+    assert call(pos=pos + 2) == -4                    # pos needs 4-byte alignment only
+    assert call(out=FAKE + 0x100000000 + 4096) == -7  # out inside the state
+    assert call(st=FAKE + 0x10000000) == -7           # state over w_g
+    # WANGO: window + 1 ring rows, S and z
+    nsw = lib.wango_decode_state_size(ctypes.byref(shape(batch=64)), 256, 128)
+    assert nsw >= 64 * 257 * (128 + 2048) * 2 + 64 * 128 * 2048 * 4
+    assert lib.wango_decode_state_size(ctypes.byref(shape()), 0, 128) == 0
+    assert lib.wango_decode_state_size(ctypes.byref(shape()), 256, 64) == 0
+    assert lib.wango_decode_state_size(ctypes.byref(shape()), 4096, 128) == 0
+    rc = lib.wango_decode_step(ctypes.byref(shape()), ctypes.byref(w), 4096, 128, pos, FAKE, FAKE + 0x60000000,
+                               FAKE + 0x100000000, 1 << 40, FAKE + 0x200000000, 1 << 40, None)
+    assert rc == _lib.STATUS_CODE["TANGO_ERR_UNSUPPORTED"]
+    assert lib.tango_decode_state_size(ctypes.byref(shape(d_gate=64 * 33, n_heads=33, head_dim=32))) == 0

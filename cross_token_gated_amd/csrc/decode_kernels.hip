@@ -11,9 +11,10 @@
 //
 // One step of one block is four or five launches on the caller's stream:
 //   prep  (the forward's row-prep kernel) RMSNorm scale, operand parts of h*gain;
-//   dproj the projections of the new tokens as a skinny MFMA GEMM (16 weight
-//         rows per wave); SiLU gates and RoPE + unit keys go straight into the
-//         state at the token's position, features and unit queries to scratch;
+//   dproj the projections of the new tokens as a skinny MFMA GEMM; SiLU gates
+//         and RoPE-rotated keys go straight into the state at the token's
+//         position, features and rotated queries to scratch (queries and keys
+//         are normalised where they are read);
 //   TANGO dagg  streams the key/gate cache in chunks of kChunk positions: exp
 //               weights e^{tau (s - 1)} (static shift: |s| <= 1), float32
 //               partial numerators and denominators per chunk;
@@ -21,7 +22,10 @@
 //   WANGO dband per (sequence, head, column block): adds the leaving token to S
 //               and z, reads phi_q^T S out, adds the window's exp-weighted
 //               gates, divides, forms gbar * v;
-//   dout  out = x + (gbar * v) W_o^T as a skinny MFMA GEMM, K split over waves.
+//   dout  out = x + (gbar * v) W_o^T as a skinny MFMA GEMM, K split over
+//         workgroups and waves.
+// The two GEMMs deal their k-steps to the 8 waves of a workgroup so that every
+// load is in flight at once, and take as many 16-token tiles as the batch needs.
 // The older-prefix terms carry the same e^{-tau} factor as the window weights,
 // so the shift cancels in the ratio (as in the forward kernels).
 #include "common.hpp"
@@ -33,8 +37,6 @@ namespace {
 
 constexpr int kDecWaves = 8;
 constexpr int kDecThreads = 64 * kDecWaves;
-constexpr int kDecTokens = 64;                 // tokens (4 m-tiles of 16) per workgroup
-constexpr int kDecMT = kDecTokens / 16;
 constexpr int kAggThreadsD = 256;
 constexpr int kBandThreads = 256;
 
@@ -54,128 +56,121 @@ __device__ __forceinline__ bool pos_ok(const DecArgs& a, int p) {
   return p >= 0 && (a.window > 0 || p < a.P);
 }
 
+// acc[mt] += W[16 rows, k] X[16 tokens of tile mt, k]^T over `steps` k-steps of
+// 32 starting at k_first, k_stride apart.  wr and xr point at this lane's row
+// and first k-slot; the AS operand parts of X are part_stride elements apart.
+// The k-steps go in batches of NB whose loads are all issued before the first
+// product; a batch past the last step reloads the last step and multiplies it
+// by a zeroed A, so there is no branch for the compiler to wait at.
+template <typename T, int MT, int AS, int NB>
+__device__ __forceinline__ void skinny_mma(f32x4 (&acc)[MT], const T* wr, const T* xr, int64_t x_row16,
+                                           int64_t part_stride, int k_first, int k_stride, int steps) {
+  for (int s0 = 0; s0 < steps; s0 += NB) {
+    Frag<T> A[NB], X[NB][MT][AS];
+#pragma unroll
+    for (int u = 0; u < NB; ++u) {
+      const int k0 = k_first + min(s0 + u, steps - 1) * k_stride;
+      A[u] = load_frag<T>(wr + k0);
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+        for (int part = 0; part < AS; ++part) X[u][mt][part] = load_frag<T>(xr + part * part_stride + mt * x_row16 + k0);
+    }
+    // keep the loads ahead of the products: the scheduler would otherwise pair
+    // each load with its product and wait for them one at a time
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int u = 0; u < NB; ++u) {
+      const Frag<T> Au = s0 + u < steps ? A[u] : Frag<T>{};
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+        for (int part = 0; part < AS; ++part) mma(acc[mt], Au, X[u][mt][part]);
+    }
+  }
+}
+
 // ---------------------------------------------------------------------------
-// dproj: [g | v | q | k] rows of the new tokens.  Workgroup: 8 waves x 16
-// weight rows = 128 rows of the stacked [W_g; W_v; W_q; W_k] against up to 64
-// tokens.  A head of q or k (d_h in {32, 64, 128}, starting at a multiple of
-// d_h past 2F, which is a multiple of 128) never straddles two workgroups, so
-// its norm is reduced through LDS.
+// dproj: [g | v | q | k] rows of the new tokens.  Workgroup: 16 rows of the
+// stacked [W_g; W_v; W_q; W_k] against MT tiles of 16 tokens; the k-steps of 32
+// are dealt round robin to the 8 waves, each of which has all of its loads in
+// flight at once, and the accumulators are summed through LDS.  Queries and
+// keys leave with RoPE applied but not normalised (a head's norm would span
+// several workgroups): the aggregation kernels normalise them on read.
 // ---------------------------------------------------------------------------
-template <typename T, int AS>
+template <typename T, int AS, int MT>
 __global__ __launch_bounds__(kDecThreads) void dproj_kernel(DecArgs a) {
-  __shared__ float nrm[kDecWaves][kDecTokens];
+  __shared__ f32x4 red[kDecWaves][MT][64];
   const int lane = threadIdx.x & 63, li = lane & 15, lg = lane >> 4;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int F = a.F, HD = a.HD, d = a.d;
-  const int N = 2 * F + 2 * HD;
-  const int n0 = blockIdx.x * (kDecWaves * 16) + wave * 16;
-  const int m0 = blockIdx.y * kDecTokens;
-  const bool live = n0 < N;
+  const int n0 = blockIdx.x * 16;                   // N = 2F + 2HD is a multiple of 16
+  const int m0 = blockIdx.y * MT * 16;
   const int cls = n0 < F ? 0 : n0 < 2 * F ? 1 : n0 < 2 * F + HD ? 2 : 3;
   const int wrow = cls == 0 ? n0 : cls == 1 ? n0 - F : cls == 2 ? n0 - 2 * F : n0 - 2 * F - HD;
   const T* W = static_cast<const T*>(cls == 0 ? a.w_g : cls == 1 ? a.w_v : cls == 2 ? a.w_q : a.w_k);
   const T* xs = static_cast<const T*>(a.xs);
 
-  f32x4 acc[kDecMT];
+  f32x4 acc[MT];
 #pragma unroll
-  for (int mt = 0; mt < kDecMT; ++mt) acc[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
-  if (live) {
-    const T* wr = W + (int64_t)(wrow + li) * d + lg * 8;
-    const T* xr = xs + (int64_t)(m0 + li) * d + lg * 8;
-#pragma unroll 2
-    for (int k0 = 0; k0 < d; k0 += 32) {
-      const Frag<T> A = load_frag<T>(wr + k0);
+  for (int mt = 0; mt < MT; ++mt) acc[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
+  const int nks = d / 32;
+  skinny_mma<T, MT, AS, 2>(acc, W + (int64_t)(wrow + li) * d + lg * 8, xs + (int64_t)(m0 + li) * d + lg * 8,
+                           (int64_t)16 * d, (int64_t)a.Mp * d, wave * 32, kDecWaves * 32,
+                           (nks - wave + kDecWaves - 1) / kDecWaves);
 #pragma unroll
-      for (int mt = 0; mt < kDecMT; ++mt)
-#pragma unroll
-        for (int part = 0; part < AS; ++part)
-          mma(acc[mt], A, load_frag<T>(xr + ((int64_t)part * a.Mp + mt * 16) * d + k0));
-    }
-  }
-
-  // epilogue: lane (li, lg) holds rows n0 + 4 lg + r of token m0 + 16 mt + li
-  float val[kDecMT][4];
-  int pos[kDecMT];
-#pragma unroll
-  for (int mt = 0; mt < kDecMT; ++mt) {
-    const int m = m0 + mt * 16 + li;
-    const float rs = a.rinv[m];                     // zero for padding rows
-    pos[mt] = m < a.B ? a.pos[m] : -1;
-#pragma unroll
-    for (int r = 0; r < 4; ++r) val[mt][r] = acc[mt][r] * rs;
-  }
-  const int col = n0 + 4 * lg;                      // first of this lane's 4 rows
-  if (live && cls == 0) {
-#pragma unroll
-    for (int mt = 0; mt < kDecMT; ++mt) {
-      const int m = m0 + mt * 16 + li;
-      if (m < a.B && pos_ok(a, pos[mt])) {
-        f32x4 g;
-#pragma unroll
-        for (int r = 0; r < 4; ++r) g[r] = silu_f(val[mt][r]);
-        store_quad<T>(static_cast<T*>(a.gc) + state_row(a, m, pos[mt]) * F + col, cvt_quad<T>(g));
-      }
-    }
-  } else if (live && cls == 1) {
-#pragma unroll
-    for (int mt = 0; mt < kDecMT; ++mt) {
-      const int m = m0 + mt * 16 + li;
-      if (m < a.B)
-        store_quad<T>(static_cast<T*>(a.v) + (int64_t)m * F + col - F,
-                      cvt_quad<T>(f32x4{val[mt][0], val[mt][1], val[mt][2], val[mt][3]}));
-    }
-  }
-  // queries and keys: RoPE on the pairs (4 lg, 4 lg + 1), (4 lg + 2, 4 lg + 3),
-  // then the squared norm of this wave's 16 rows of the head
-  const bool qk = live && cls >= 2;
-  const int e0 = qk ? col - (cls == 2 ? 2 * F : 2 * F + HD) : 0;   // column within q or k
-  if (qk && a.rope_base > 0.f) {
-    const int c0 = (e0 % a.dh) / 2;
-    // rotation rate of pairs c0, c0 + 1 in revolutions per position (float64:
-    // a float32 angle at large positions would be off by ~1e-3 rad)
-    const double f0 = pow((double)a.rope_base, -2.0 * c0 / a.dh) * 0.15915494309189533577;
-    const double f1 = pow((double)a.rope_base, -2.0 * (c0 + 1) / a.dh) * 0.15915494309189533577;
-#pragma unroll
-    for (int mt = 0; mt < kDecMT; ++mt) {
-      const double p = (double)max(pos[mt], 0);
-#pragma unroll
-      for (int h2 = 0; h2 < 2; ++h2) {
-        const double rev = p * (h2 ? f1 : f0);
-        const float fr = (float)(rev - rint(rev));
-        const float fs = __builtin_amdgcn_sinf(fr), fc = __builtin_amdgcn_cosf(fr);
-        const float u0 = val[mt][2 * h2], u1 = val[mt][2 * h2 + 1];
-        val[mt][2 * h2] = u0 * fc - u1 * fs;
-        val[mt][2 * h2 + 1] = u0 * fs + u1 * fc;
-      }
-    }
-  }
-#pragma unroll
-  for (int mt = 0; mt < kDecMT; ++mt) {
-    float ss = 0.f;
-#pragma unroll
-    for (int r = 0; r < 4; ++r) ss += val[mt][r] * val[mt][r];
-    ss = group_sum(ss);                              // the wave's 16 rows, token li
-    if (lg == 0) nrm[wave][mt * 16 + li] = ss;
-  }
+  for (int mt = 0; mt < MT; ++mt) red[wave][mt][lane] = acc[mt];
   __syncthreads();
-  if (qk) {
-    const int wph = a.dh / 16;                       // waves per head
-    const int hw0 = wave - (e0 % a.dh) / 16;         // first wave of this head
+  if (threadIdx.x >= MT * 64) return;
+  // thread (mt, l2) holds rows n0 + 4 lg2 + r of token m0 + 16 mt + li2
+  const int mt = threadIdx.x >> 6, l2 = threadIdx.x & 63, li2 = l2 & 15, lg2 = l2 >> 4;
+  const int m = m0 + mt * 16 + li2;
+  if (m >= a.B) return;
+  f32x4 sum = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int mt = 0; mt < kDecMT; ++mt) {
-      const int m = m0 + mt * 16 + li;
-      float tot = 0.f;
-      for (int w2 = 0; w2 < wph; ++w2) tot += nrm[hw0 + w2][mt * 16 + li];
-      const float inv = 1.0f / fmaxf(sqrtf(tot), 1e-12f);
-      const f32x4 u = {val[mt][0] * inv, val[mt][1] * inv, val[mt][2] * inv, val[mt][3] * inv};
-      if (m < a.B) {
-        if (cls == 2)
-          store_quad<T>(static_cast<T*>(a.q) + (int64_t)m * HD + e0, cvt_quad<T>(u));
-        else if (pos_ok(a, pos[mt]))
-          store_quad<T>(static_cast<T*>(a.kc) + state_row(a, m, pos[mt]) * HD + e0, cvt_quad<T>(u));
-      }
+  for (int w2 = 0; w2 < kDecWaves; ++w2) sum += red[w2][mt][l2];
+  const float rs = a.rinv[m];
+  float val[4];
+#pragma unroll
+  for (int r = 0; r < 4; ++r) val[r] = sum[r] * rs;
+  const int p = a.pos[m];
+  const int col = n0 + 4 * lg2;
+  if (cls == 0) {
+    if (pos_ok(a, p)) {
+      f32x4 g;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) g[r] = silu_f(val[r]);
+      store_quad<T>(static_cast<T*>(a.gc) + state_row(a, m, p) * F + col, cvt_quad<T>(g));
+    }
+    return;
+  }
+  if (cls == 1) {
+    store_quad<T>(static_cast<T*>(a.v) + (int64_t)m * F + col - F, cvt_quad<T>(f32x4{val[0], val[1], val[2], val[3]}));
+    return;
+  }
+  // queries and keys: RoPE on the pairs (4 lg2, 4 lg2 + 1), (4 lg2 + 2, 4 lg2 + 3)
+  const int e0 = col - (cls == 2 ? 2 * F : 2 * F + HD);   // column within q or k
+  if (a.rope_base > 0.f) {
+    const int c0 = (e0 % a.dh) / 2;
+    // rotation rate of pair c in revolutions per position (float64: a float32
+    // angle at large positions would be off by ~1e-3 rad)
+    const double pp = (double)max(p, 0);
+#pragma unroll
+    for (int h2 = 0; h2 < 2; ++h2) {
+      const double f = pow((double)a.rope_base, -2.0 * (c0 + h2) / a.dh) * 0.15915494309189533577;
+      const double rev = pp * f;
+      const float fr = (float)(rev - rint(rev));
+      const float fs = __builtin_amdgcn_sinf(fr), fc = __builtin_amdgcn_cosf(fr);
+      const float u0 = val[2 * h2], u1 = val[2 * h2 + 1];
+      val[2 * h2] = u0 * fc - u1 * fs;
+      val[2 * h2 + 1] = u0 * fs + u1 * fc;
     }
   }
+  const Quad<T> u = cvt_quad<T>(f32x4{val[0], val[1], val[2], val[3]});
+  if (cls == 2)
+    store_quad<T>(static_cast<T*>(a.q) + (int64_t)m * HD + e0, u);
+  else if (pos_ok(a, p))
+    store_quad<T>(static_cast<T*>(a.kc) + state_row(a, m, p) * HD + e0, u);
 }
 
 // ---------------------------------------------------------------------------
@@ -198,20 +193,32 @@ __global__ __launch_bounds__(kAggThreadsD) void dagg_kernel(DecArgs a) {
   const int F = a.F, HD = a.HD, H = a.H, dh = a.dh, Fh = F / H;
   const T* kc = static_cast<const T*>(a.kc);
   const T* gc = static_cast<const T*>(a.gc);
+  __shared__ float qinv[32];
   for (int i = tid; i < HD; i += kAggThreadsD) qs[i] = tof<T>(static_cast<const T*>(a.q)[b * HD + i]);
   __syncthreads();
-  // exp weights, one (source, head) item per thread and pass
+  if (tid < H) {
+    float ss = 0.f;
+    for (int e = 0; e < dh; ++e) ss += qs[tid * dh + e] * qs[tid * dh + e];
+    qinv[tid] = 1.0f / fmaxf(sqrtf(ss), 1e-12f);   // unit query ([TANGO] §2.1)
+  }
+  __syncthreads();
+  // exp weights, one (source, head) item per thread and pass; s = q.k / |q| |k|
   for (int it = tid; it < kDecChunk * H; it += kAggThreadsD) {
     const int jl = it / H, h = it - (it / H) * H;
     float w = 0.f;
     if (jl < nj) {
       const T* kr = kc + (b * a.P + j0 + jl) * HD + h * dh;
-      float s = 0.f;
+      float s = 0.f, kk = 0.f;
       for (int e = 0; e < dh; e += 8) {
         const Frag<T> kf = load_frag<T>(kr + e);
 #pragma unroll
-        for (int s8 = 0; s8 < 8; ++s8) s += qs[h * dh + e + s8] * tof<T>(kf[s8]);
+        for (int s8 = 0; s8 < 8; ++s8) {
+          const float kv = tof<T>(kf[s8]);
+          s += qs[h * dh + e + s8] * kv;
+          kk += kv * kv;
+        }
       }
+      s *= qinv[h] / fmaxf(sqrtf(kk), 1e-12f);
       w = __builtin_amdgcn_exp2f(tau_of(a.theta, h) * kLog2e * (s - 1.0f));
     }
     pw[jl * H + h] = w;
@@ -270,40 +277,70 @@ __device__ __forceinline__ void form_gv(const DecArgs& a, int64_t m, int col, co
 
 // ---------------------------------------------------------------------------
 // TANGO dcomb: gbar = sum of chunk numerators / (sum of denominators + null).
+// Workgroup: 256 columns of one sequence; 32 column groups of 8 x 8 chunk
+// groups, summed through LDS.
 // ---------------------------------------------------------------------------
+constexpr int kCombCols = 256, kCombGroups = 8;
 template <typename T, int AS>
 __global__ __launch_bounds__(256) void dcomb_kernel(DecArgs a) {
+  __shared__ float red[kCombGroups][kCombCols];
+  __shared__ float rden[kCombGroups][32];       // per column group: a block may span heads
   const int64_t b = blockIdx.y;
-  const int col = (blockIdx.x * 256 + threadIdx.x) * 8;
-  if (col >= a.F) return;
+  const int cgp = threadIdx.x & 31, chg = threadIdx.x >> 5;
+  const int col = blockIdx.x * kCombCols + cgp * 8;
   const int p = a.pos[b];
-  float gv[8];
-  if (!pos_ok(a, p)) {
-#pragma unroll
-    for (int e = 0; e < 8; ++e) gv[e] = __builtin_nanf("");
-    store_gv<T, AS>(a, b, col, gv);
-    return;
-  }
+  const bool ok = pos_ok(a, p);
   const int h = col / (a.F / a.H);
-  const int nc = p / kDecChunk + 1;
+  const int nc = ok ? p / kDecChunk + 1 : 0;
   const int64_t stride = a.F + 64;
   const float* part = a.part + b * a.nch * stride;
   float num[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
   float den = 0.f;
-#pragma unroll 4
-  for (int c = 0; c < nc; ++c) {
-    const f32x4 n0 = *reinterpret_cast<const f32x4*>(part + c * stride + col);
-    const f32x4 n1 = *reinterpret_cast<const f32x4*>(part + c * stride + col + 4);
+  if (col < a.F) {
+    // every load of this thread's chunks in flight at once, in batches of 8
+    for (int c0 = chg; c0 < nc; c0 += 8 * kCombGroups) {
+      f32x4 n0[8], n1[8];
+      float dn[8];
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      num[e] += n0[e];
-      num[4 + e] += n1[e];
+      for (int u = 0; u < 8; ++u) {
+        const int c = min(c0 + u * kCombGroups, nc - 1);
+        n0[u] = *reinterpret_cast<const f32x4*>(part + c * stride + col);
+        n1[u] = *reinterpret_cast<const f32x4*>(part + c * stride + col + 4);
+        dn[u] = part[c * stride + a.F + h];
+      }
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        const float keep = c0 + u * kCombGroups < nc ? 1.f : 0.f;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          num[e] += keep * n0[u][e];
+          num[4 + e] += keep * n1[u][e];
+        }
+        den += keep * dn[u];
+      }
     }
-    den += part[c * stride + a.F + h];
   }
-  if (a.null_bias) den += (float)(p + 1) * __expf(a.null_bias[h] - tau_of(a.theta, h));
-  form_gv<T>(a, b, col, num, den, gv);
-  store_gv<T, AS>(a, b, col, gv);
+#pragma unroll
+  for (int e = 0; e < 8; ++e) red[chg][cgp * 8 + e] = num[e];
+  rden[chg][cgp] = den;
+  __syncthreads();
+  if (chg == 0 && col < a.F) {
+    float gv[8];
+    if (!ok) {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) gv[e] = __builtin_nanf("");
+    } else {
+      float tot[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f}, dt = 0.f;
+      for (int g2 = 0; g2 < kCombGroups; ++g2) {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) tot[e] += red[g2][cgp * 8 + e];
+        dt += rden[g2][cgp];
+      }
+      if (a.null_bias) dt += (float)(p + 1) * __expf(a.null_bias[h] - tau_of(a.theta, h));
+      form_gv<T>(a, b, col, tot, dt, gv);
+    }
+    store_gv<T, AS>(a, b, col, gv);
+  }
 }
 
 // ---------------------------------------------------------------------------
@@ -341,24 +378,41 @@ __global__ __launch_bounds__(kBandThreads) void dband_kernel(DecArgs a) {
   const float escale = __expf(-tau);
   const bool fold = p >= W;                        // token p - W leaves the window
   const int64_t so = fold ? state_row(a, b, p - W) : 0;
-  if (tid < dh) {
-    const float qv = tof<T>(static_cast<const T*>(a.q)[b * HD + h * dh + tid]);
-    qs[tid] = qv;
-    fq[tid] = phi_feature(stau * qv, isd);
-    fk[tid] = fold ? phi_feature(stau * tof<T>(kc[so * HD + h * dh + tid]), isd) : 0.f;
+  if (wave < 2) {
+    // wave 0: the unit query and its features; wave 1: the features of the
+    // leaving token's unit key (d_h <= 128: two elements a lane)
+    const T* src = wave == 0 ? static_cast<const T*>(a.q) + b * HD + h * dh : kc + so * HD + h * dh;
+    const bool on = wave == 0 || fold;
+    const float u0 = on && lane < dh ? tof<T>(src[lane]) : 0.f;
+    const float u1 = on && lane + 64 < dh ? tof<T>(src[lane + 64]) : 0.f;
+    const float inv = 1.0f / fmaxf(sqrtf(wave_sum(u0 * u0 + u1 * u1)), 1e-12f);
+    float* feat = wave == 0 ? fq : fk;
+    if (lane < dh) {
+      if (wave == 0) qs[lane] = u0 * inv;
+      feat[lane] = on ? phi_feature(stau * u0 * inv, isd) : 0.f;
+    }
+    if (lane + 64 < dh) {
+      if (wave == 0) qs[lane + 64] = u1 * inv;
+      feat[lane + 64] = on ? phi_feature(stau * u1 * inv, isd) : 0.f;
+    }
   }
   __syncthreads();
-  // window exp weights, j in [p - nw + 1, p]
+  // window exp weights, j in [p - nw + 1, p]; s = q.k / |k| with the unit query
   const int nw = min(W, p + 1);
   const int jlo = p - nw + 1;
   for (int t = tid; t < nw; t += kBandThreads) {
     const T* kr = kc + state_row(a, b, jlo + t) * HD + h * dh;
-    float s = 0.f;
+    float s = 0.f, kk = 0.f;
     for (int e = 0; e < dh; e += 8) {
       const Frag<T> kf = load_frag<T>(kr + e);
 #pragma unroll
-      for (int s8 = 0; s8 < 8; ++s8) s += qs[e + s8] * tof<T>(kf[s8]);
+      for (int s8 = 0; s8 < 8; ++s8) {
+        const float kv = tof<T>(kf[s8]);
+        s += qs[e + s8] * kv;
+        kk += kv * kv;
+      }
     }
+    s /= fmaxf(sqrtf(kk), 1e-12f);
     pw[t] = __builtin_amdgcn_exp2f(tau * kLog2e * (s - 1.0f));
   }
   __syncthreads();
@@ -435,64 +489,81 @@ __global__ __launch_bounds__(kBandThreads) void dband_kernel(DecArgs a) {
 
 // ---------------------------------------------------------------------------
 // dout: out = x + (gbar * v) W_o^T.  Workgroup: 16 output columns (rows of
-// W_o) x up to 64 tokens; the k-steps of 32 are dealt round robin to the 8
-// waves and their accumulators summed through LDS.
+// W_o) x MT tiles of 16 tokens x one of kOutSplit quarters of K; its k-steps
+// of 32 are dealt round robin to the 8 waves (all loads in flight at once) and
+// summed through LDS.  The quarters meet through float32 partials: the last
+// workgroup of a tile to finish (an atomic counter, cleared by the row-prep
+// kernel of the same step) adds them in a fixed order, so the result does not
+// depend on which finished first.  The partials and the counter use
+// agent-scope atomic stores and loads (coherent across the XCD L2s).
 // ---------------------------------------------------------------------------
-template <typename T, typename IO, int AS>
+template <typename T, typename IO, int AS, int MT>
 __global__ __launch_bounds__(kDecThreads) void dout_kernel(DecArgs a) {
-  __shared__ f32x4 red[kDecWaves][kDecMT][64];
+  __shared__ f32x4 red[kDecWaves][MT][64];
+  __shared__ int last;
   const int lane = threadIdx.x & 63, li = lane & 15, lg = lane >> 4;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int F = a.F, d = a.d;
   const int n0 = blockIdx.x * 16;
-  const int m0 = blockIdx.y * kDecTokens;
-  const T* wr = static_cast<const T*>(a.w_o) + (int64_t)(n0 + li) * F + lg * 8;
-  const T* gr = static_cast<const T*>(a.gv) + (int64_t)(m0 + li) * F + lg * 8;
-  f32x4 acc[kDecMT];
+  const int m0 = blockIdx.y * MT * 16;
+  const int kq = blockIdx.z;
+  const int nks = F / 32;
+  const int ks0 = kq * nks / kOutSplit, ks1 = (kq + 1) * nks / kOutSplit;
+  f32x4 acc[MT];
 #pragma unroll
-  for (int mt = 0; mt < kDecMT; ++mt) acc[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
-  for (int k0 = wave * 32; k0 < F; k0 += kDecWaves * 32) {
-    const Frag<T> A = load_frag<T>(wr + k0);
+  for (int mt = 0; mt < MT; ++mt) acc[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
+  skinny_mma<T, MT, AS, 2>(acc, static_cast<const T*>(a.w_o) + (int64_t)(n0 + li) * F + lg * 8,
+                           static_cast<const T*>(a.gv) + (int64_t)(m0 + li) * F + lg * 8, (int64_t)16 * F,
+                           (int64_t)a.Mp * F, (ks0 + wave) * 32, kDecWaves * 32,
+                           (ks1 - ks0 - wave + kDecWaves - 1) / kDecWaves);
 #pragma unroll
-    for (int mt = 0; mt < kDecMT; ++mt)
-#pragma unroll
-      for (int part = 0; part < AS; ++part)
-        mma(acc[mt], A, load_frag<T>(gr + ((int64_t)part * a.Mp + mt * 16) * F + k0));
-  }
-#pragma unroll
-  for (int mt = 0; mt < kDecMT; ++mt) red[wave][mt][lane] = acc[mt];
+  for (int mt = 0; mt < MT; ++mt) red[wave][mt][lane] = acc[mt];
   __syncthreads();
-  if (threadIdx.x < kDecMT * 64) {
-    const int mt = threadIdx.x >> 6, l2 = threadIdx.x & 63;
-    const int m = m0 + mt * 16 + (l2 & 15);
-    if (m < a.B) {
-      f32x4 s = {0.f, 0.f, 0.f, 0.f};
+  const int mt = threadIdx.x >> 6, l2 = threadIdx.x & 63;
+  const int m = m0 + mt * 16 + (l2 & 15);
+  const int n = n0 + 4 * (l2 >> 4);
+  // partial of this quarter: [kOutSplit][Mp][d] float32
+  float* opart = a.opart + ((int64_t)kq * a.Mp + m) * d + n;
+  if (threadIdx.x < MT * 64) {
+    f32x4 s4 = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int w2 = 0; w2 < kDecWaves; ++w2) s += red[w2][mt][l2];
-      const int n = n0 + 4 * (l2 >> 4);
-      const IO* xr = static_cast<const IO*>(a.x) + (int64_t)m * d + n;
-      IO* orow = static_cast<IO*>(a.out) + (int64_t)m * d + n;
-      f32x4 o;
+    for (int w2 = 0; w2 < kDecWaves; ++w2) s4 += red[w2][mt][l2];
 #pragma unroll
-      for (int r = 0; r < 4; ++r) o[r] = tof<IO>(xr[r]) + s[r];
-#pragma unroll
-      for (int r = 0; r < 4; ++r) orow[r] = cvt<IO>(o[r]);
-    }
+    for (int r = 0; r < 4; ++r) __hip_atomic_store(opart + r, s4[r], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+  if (threadIdx.x == 0)
+    last = __hip_atomic_fetch_add(a.ocount + blockIdx.y * gridDim.x + blockIdx.x, 1, __ATOMIC_RELAXED,
+                                  __HIP_MEMORY_SCOPE_AGENT) == kOutSplit - 1;
+  __syncthreads();
+  if (!last || threadIdx.x >= MT * 64 || m >= a.B) return;
+  f32x4 s = {0.f, 0.f, 0.f, 0.f};
+  for (int q2 = 0; q2 < kOutSplit; ++q2) {
+    const float* src = a.opart + ((int64_t)q2 * a.Mp + m) * d + n;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) s[r] += __hip_atomic_load(src + r, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
+  const IO* xr = static_cast<const IO*>(a.x) + (int64_t)m * d + n;
+  IO* orow = static_cast<IO*>(a.out) + (int64_t)m * d + n;
+  float o[4];
+#pragma unroll
+  for (int r = 0; r < 4; ++r) o[r] = tof<IO>(xr[r]) + s[r];
+#pragma unroll
+  for (int r = 0; r < 4; ++r) orow[r] = cvt<IO>(o[r]);
 }
 
-template <typename T, int AS>
-hipError_t launch_decode_t(const DecArgs& a, bool io_bf, hipStream_t s) {
+template <typename T, int AS, int MT>
+hipError_t launch_decode_mt(const DecArgs& a, bool io_bf, hipStream_t s) {
   const int N = 2 * a.F + 2 * a.HD;
-  const unsigned mg = (unsigned)ceil_div(a.B, kDecTokens);
-  hipLaunchKernelGGL((dproj_kernel<T, AS>), dim3((unsigned)ceil_div(N, kDecWaves * 16), mg),
-                     dim3(kDecThreads), 0, s, a);
+  const unsigned mg = (unsigned)ceil_div(a.B, MT * 16);
+  hipLaunchKernelGGL((dproj_kernel<T, AS, MT>), dim3((unsigned)(N / 16), mg), dim3(kDecThreads), 0, s, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   if (a.window == 0) {
     hipLaunchKernelGGL((dagg_kernel<T>), dim3((unsigned)a.nch, (unsigned)a.B), dim3(kAggThreadsD), 0, s, a);
     if ((e = hipGetLastError()) != hipSuccess) return e;
-    hipLaunchKernelGGL((dcomb_kernel<T, AS>), dim3((unsigned)ceil_div(a.F, 256 * 8), (unsigned)a.B), dim3(256),
+    hipLaunchKernelGGL((dcomb_kernel<T, AS>), dim3((unsigned)ceil_div(a.F, kCombCols), (unsigned)a.B), dim3(256),
                        0, s, a);
   } else {
     const int Fh = a.F / a.H;
@@ -508,12 +579,20 @@ hipError_t launch_decode_t(const DecArgs& a, bool io_bf, hipStream_t s) {
                          dim3(kBandThreads), 0, s, a);
   }
   if ((e = hipGetLastError()) != hipSuccess) return e;
-  const dim3 og((unsigned)(a.d / 16), mg);
+  const dim3 og((unsigned)(a.d / 16), mg, kOutSplit);
   if (io_bf)
-    hipLaunchKernelGGL((dout_kernel<T, bf16, AS>), og, dim3(kDecThreads), 0, s, a);
+    hipLaunchKernelGGL((dout_kernel<T, bf16, AS, MT>), og, dim3(kDecThreads), 0, s, a);
   else
-    hipLaunchKernelGGL((dout_kernel<T, float, AS>), og, dim3(kDecThreads), 0, s, a);
+    hipLaunchKernelGGL((dout_kernel<T, float, AS, MT>), og, dim3(kDecThreads), 0, s, a);
   return hipGetLastError();
+}
+
+// Token tiles per workgroup of the two GEMMs: as few as the batch needs.
+template <typename T, int AS>
+hipError_t launch_decode_t(const DecArgs& a, bool io_bf, hipStream_t s) {
+  if (a.B <= 16) return launch_decode_mt<T, AS, 1>(a, io_bf, s);
+  if (a.B <= 32) return launch_decode_mt<T, AS, 2>(a, io_bf, s);
+  return launch_decode_mt<T, AS, 4>(a, io_bf, s);
 }
 
 }  // namespace

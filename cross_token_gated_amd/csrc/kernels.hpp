@@ -116,6 +116,7 @@ hipError_t launch_prep(const ProjArgs& a, bool bf, bool io_bf, hipStream_t s);
 // ---- autoregressive decode -------------------------------------------------
 
 constexpr int kDecChunk = 128;        // TANGO cache positions per workgroup
+constexpr int kOutSplit = 4;          // K quarters of the decode output GEMM
 constexpr int kDecMaxWindow = 2048;   // largest WANGO window of the decode kernels
 
 struct DecArgs {
@@ -130,16 +131,18 @@ struct DecArgs {
   const void *w_g, *w_v, *w_q, *w_k, *w_o;
   const float* theta;
   const float* null_bias;  // or null
-  void* kc;                // state: unit keys [B][P][HD]
+  void* kc;                // state: RoPE-rotated keys [B][P][HD] (normalised on read)
   void* gc;                // state: gates [B][P][F]
   float* S;                // WANGO state: [B][H][dh][F/H]
   float* z;                // WANGO state: [B][2][H][dh], the copy after position p in slot p % 2
   const void* xs;          // scratch: operand parts of h * gain [AS][Mp][d]
   const float* rinv;       // scratch: RMSNorm scales [Mp]
   void* v;                 // scratch: [Mp][F]
-  void* q;                 // scratch: unit queries [Mp][HD]
+  void* q;                 // scratch: RoPE-rotated queries [Mp][HD] (normalised on read)
   float* part;             // scratch (TANGO): [B][nch][F + 64] partial sums
   void* gv;                // scratch: operand parts of gbar * v [AS][Mp][F]
+  float* opart;            // scratch: output partials [kOutSplit][Mp][d]
+  int* ocount;             // scratch: one counter per output tile, zero at entry
   const void* x;           // [B][d] in the I/O dtype
   void* out;               // [B][d] in the I/O dtype (may equal x)
 };

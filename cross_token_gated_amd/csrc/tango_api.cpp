@@ -625,7 +625,8 @@ struct DecLayout {
   // state
   size_t kc, gc, S, z, state_total;
   // workspace
-  size_t xs, rinv, v, q, part, gv, ws_total;
+  size_t xs, rinv, v, q, part, gv, opart, ocount, ws_total;
+  int64_t n_ocount;
   int P, nch;
   int64_t Mp;
 };
@@ -674,6 +675,9 @@ DecLayout make_dec_layout(const tango_shape_t* s, bool wango, int32_t window) {
   L.q = take((size_t)L.Mp * HD * es);
   if (!wango) L.part = take((size_t)B * L.nch * (F + 64) * sizeof(float));
   L.gv = take((size_t)decode_parts(bf) * L.Mp * F * es);
+  L.opart = take((size_t)kOutSplit * L.Mp * s->d_model * sizeof(float));
+  L.n_ocount = (int64_t)(s->d_model / 16) * ((B + 15) / 16);   // output tiles (16 tokens or more each)
+  L.ocount = take((size_t)L.n_ocount * sizeof(int));
   L.ws_total = off;
   return L;
 }
@@ -736,6 +740,8 @@ int decode_common(const tango_shape_t* s, const tango_weights_t* w, bool wango, 
   pa.Tp = (int)L.Mp;
   pa.d = s->d_model;
   pa.eps = s->rms_eps;
+  pa.zero = reinterpret_cast<int*>(wb + L.ocount);   // the output GEMM's counters
+  pa.zero_n = L.n_ocount;
   hipError_t e = launch_prep(pa, bf, io_bf, st);
   if (e != hipSuccess) return hip_fail(e, "row-prep kernel");
   DecArgs a{};
@@ -768,6 +774,8 @@ int decode_common(const tango_shape_t* s, const tango_weights_t* w, bool wango, 
   a.q = wb + L.q;
   a.part = wango ? nullptr : reinterpret_cast<float*>(wb + L.part);
   a.gv = wb + L.gv;
+  a.opart = reinterpret_cast<float*>(wb + L.opart);
+  a.ocount = reinterpret_cast<int*>(wb + L.ocount);
   a.x = x;
   a.out = out;
   e = launch_decode(a, bf, io_bf, st);

@@ -158,7 +158,10 @@ int wango_block_fwd(const tango_shape_t* shape, const tango_weights_t* weights,
  *   state      DEVICE buffer of *_decode_state_size bytes, kept by the caller
  *              between steps, one per stacked application; never shared by
  *              calls that can run concurrently.  Layout (dtype unless noted):
- *                keys  [B][R][H*d_h] unit keys,  gates [B][R][F],
+ *                keys  [B][R][H*d_h] RoPE-rotated keys, stored before the
+ *                      unit-length division (the kernels divide by each
+ *                      head's norm where they read a key),
+ *                gates [B][R][F],
  *                TANGO: R = P, position j in row j;
  *                WANGO: R = window + 1, position j in row j mod R, then
  *                  S [B][H][d_h][F/H] float32 and z [B][2][H][d_h] float32

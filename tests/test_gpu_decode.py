@@ -127,16 +127,19 @@ def test_decode_steps(case, null):
 
 
 @pytest.mark.parametrize("mode", ["tango", "wango"])
-def test_decode_stack(mode):
-    """Two stacked applications, each with its own state; the stream between
-    them is stored in the I/O dtype (bf16 here), as in the forward stack."""
-    w = wl.small_workload(mode=mode, dtype="bf16", io_dtype="bf16", B=2, T=30, d_model=128, d_gate=128,
-                          n_heads=2, head_dim=32, window=4, repeats=2)
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_decode_stack(mode, dtype):
+    """Three stacked applications, each with its own state; the stream between
+    them is stored in the I/O dtype (float32, as in the shipped workloads; a
+    bf16 stream rounded between and after tiny layers already spends most of
+    the bf16 bar on storage alone, and the single-layer cases cover it)."""
+    w = wl.small_workload(mode=mode, dtype=dtype, io_dtype="f32", B=2, T=30, d_model=128, d_gate=128,
+                          n_heads=2, head_dim=32, window=4, repeats=3)
     inp = wl.make_inputs(w)
-    announce(f"decode stack {mode}")
+    announce(f"decode stack {mode} {dtype}")
     outs, pos_all = decode_run(w, inp, [0, 2])
     ref = [O.block_stack(np.asarray(inp.h[b:b + 1], np.float64), H.oracle_params(inp), H.oracle_config(w),
-                         repeats=2, io_dtype="bf16")[0] for b in range(w.B)]
+                         repeats=3, io_dtype="f32")[0] for b in range(w.B)]
     check_against_oracle(w, inp, outs, pos_all, ref)
 
 

@@ -1,6 +1,6 @@
 """Benchmark of the TANGO / WANGO block forward on one MI355X.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline] [--no-decode]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline] [--no-decode] [--no-pages]
 
 One step runs every part of the block forward once at T = 8192 tokens:
   * TANGO, bf16 compute, B = 1, T = 8192, d = 512, F = 2048, q/k width 128,
@@ -29,6 +29,10 @@ Alongside, with HIP events on the launch stream:
     own key/gate cache; WANGO, 64 sequences, window 256 -- as decoded tokens
     per second, and the algorithmic HBM bytes of the step (weights, the state
     each layer must touch, x and out) over its median time against 8 TB/s;
+  * pages_geometry: one forward (4 applications) of the block in the pages'
+    own geometry at T = 8192 (16 heads of 32, F = 28,480, window and block
+    64), with the block's operation count as the pages tally it (Table 5
+    without the vocabulary projection) per second;
   * cpu_baseline: the float64 CPU oracle on a bounded sample of the same work
     (one of the four TANGO applications, scaled by 4, plus the WANGO block).
 The "traffic" of the two rooflines is the HBM traffic per launch measured by
@@ -65,6 +69,7 @@ def parse():
     ap.add_argument("--kernel-loops", type=int, default=None,
                     help="launches per roofline measurement (default: --steps)")
     ap.add_argument("--no-decode", action="store_true", help="skip the decode-step measurement")
+    ap.add_argument("--no-pages", action="store_true", help="skip the pages'-geometry forward")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a plain 256 MiB device copy (for counter calibration)")
     return ap.parse_args()
@@ -163,6 +168,77 @@ def decode_bytes(w, es: int, io_es: int) -> float:
     else:
         state = 2 * w.B * w.n_heads * w.head_dim * (F // w.n_heads) * 4 + w.B * (w.window + 2) * row
     return float(w.repeats * (weights + state + 2 * w.B * d * io_es))
+
+
+def pages_block_macs(w) -> float:
+    """MACs of w.repeats block applications as the pages count them ([TANGO]
+    §3 and Table 5): linear projections T(2dF + 2dHd_h + Fd); pairs over the
+    full T x T grid for TANGO, 3W pairs per token plus the running-sum update
+    and read-out 2 d_h F per token for WANGO.  The output vocabulary
+    projection that Table 5 adds is not part of the block and is left out."""
+    T, d, F, H, dh = w.T, w.d_model, w.d_gate, w.n_heads, w.head_dim
+    linear = T * (2 * d * F + 2 * d * H * dh + F * d)
+    if w.mode == "tango":
+        pairs = T * T * (H * dh + F)
+    else:
+        pairs = T * 3 * w.window * (H * dh + F) + T * 2 * dh * F
+    return float(w.repeats * (linear + pairs))
+
+
+def pages_bench(steps: int, warmup: int, dev, stream) -> dict:
+    """One forward (all 4 applications) of the pages' geometry at T = 8192:
+    16 heads of 32, F = 28,480, window and prefix-sum block 64."""
+    import torch
+
+    from cross_token_gated_amd import api
+    from cross_token_gated_amd import workload as wl
+    from tests.gpu_common import block_weights, dev_tensor
+
+    out = {}
+    for name, w in wl.PAGES_WORKLOADS.items():
+        inp = wl.make_inputs(w)
+        bw = block_weights(w, inp, dev)
+        x = dev_tensor(inp.h, w.io, dev)
+        ping, pong = torch.empty_like(x), torch.empty_like(x)
+        shape = api.shape_of(x, bw, w.rope_base, w.rms_eps)
+        n = (api.tango_workspace_size(shape) if w.mode == "tango"
+             else api.wango_workspace_size(shape, w.window, w.head_dim, w.chunk))
+        ws = api.workspace(n, dev)
+
+        def fwd():
+            src = x
+            for r in range(w.repeats):
+                dst = ping if r % 2 == 0 else pong
+                if w.mode == "tango":
+                    api.tango_block_fwd(src, bw, out=dst, ws=ws, rope_base=w.rope_base, rms_eps=w.rms_eps,
+                                        stream=stream)
+                else:
+                    api.wango_block_fwd(src, bw, w.window, w.head_dim, w.chunk, out=dst, ws=ws,
+                                        rope_base=w.rope_base, rms_eps=w.rms_eps, stream=stream)
+                src = dst
+
+        for _ in range(warmup):
+            fwd()
+        torch.cuda.synchronize()
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+              for _ in range(steps)]
+        for a, b in ev:
+            a.record(stream)
+            fwd()
+            b.record(stream)
+        torch.cuda.synchronize()
+        t = sorted(a.elapsed_time(b) for a, b in ev)
+        ms = t[steps // 2] if steps % 2 else 0.5 * (t[steps // 2 - 1] + t[steps // 2])
+        macs = pages_block_macs(w)
+        out[name] = {"ms_per_forward": ms, "tokens_per_s": w.tokens / (ms * 1e-3),
+                     "applications": w.repeats, "pages_block_macs": macs,
+                     "pages_macs_per_s": macs / (ms * 1e-3)}
+        print(f"[bench] pages geometry {name}: {ms:.2f} ms per forward ({w.repeats} applications), "
+              f"{w.tokens / (ms * 1e-3):.0f} tokens/s, {macs / (ms * 1e-3) / 1e12:.0f} T MAC/s of the pages' "
+              f"count", file=sys.stderr, flush=True)
+        del ws, x, ping, pong
+        torch.cuda.empty_cache()
+    return out
 
 
 def decode_bench(steps: int, warmup: int, dev, stream) -> dict:
@@ -444,6 +520,8 @@ def main():
         torch.cuda.synchronize()
     if not args.no_decode:
         result["decode"] = decode_bench(loops, min(args.warmup, 3), dev, stream)
+    if not args.no_pages:
+        result["pages_geometry"] = pages_bench(min(loops, 5), 1, dev, stream)
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(wt, wg)
     print(json.dumps(result), flush=True)

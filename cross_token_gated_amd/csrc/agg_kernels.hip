@@ -44,14 +44,15 @@ namespace tango {
 
 namespace {
 
-// Destination rows per tile and gate columns per wave.  The narrow variant
-// (16 columns per wave) serves heads whose gate width is not a multiple of
-// 8 * WIDE; there a wave whose columns lie past the head's width skips the
-// product (a wave-uniform branch).
+// Destination rows per tile and gate columns per wave: WIDE where the head's
+// gate width is a multiple of 8 * WIDE, else 32 where it is a multiple of 256,
+// else 16 (narrow); in the narrow variant a wave whose columns lie past the
+// head's width skips the product (a wave-uniform branch).
 template <typename T> struct AggCfg;
 template <> struct AggCfg<bf16> { static constexpr int BR = 128, WIDE = 64; };
 template <> struct AggCfg<float> { static constexpr int BR = 64, WIDE = 32; };
 constexpr int kNarrow = 16;
+constexpr int kMid = 32;
 
 constexpr int kWaves = 8;                 // two waves per SIMD
 constexpr int BC = 64;                    // sources per step
@@ -433,7 +434,10 @@ __global__ __launch_bounds__(kAggThreads) void agg_kernel(AggArgs a, int nfc, in
             const f32x4 no = *reinterpret_cast<const f32x4*>(a.n_old + (nblk * 64 + lane) * 4);
             num += escale * no;
           }
-          store_quad<T>(gbar + (mseq + i) * F + col0 + fb * 16 + lg * 4, cvt_quad<T>(num * inv));
+          // gbar is not head-padded: columns past the head's width are pad
+          const int c = f_base + fb * 16 + lg * 4;
+          if (c < a.Fho)
+            store_quad<T>(gbar + (mseq + i) * a.Fo + (int64_t)h * a.Fho + c, cvt_quad<T>(num * inv));
         }
       }
     }
@@ -461,12 +465,18 @@ hipError_t launch_agg_w(const AggArgs& a, int nfc, int rtiles, int64_t items, hi
   return hipGetLastError();
 }
 
-template <typename T> bool wide_ok(int Fh) { return Fh % (kWaves * AggCfg<T>::WIDE) == 0; }
-template <typename T> int agg_fs(int Fh) { return kWaves * (wide_ok<T>(Fh) ? AggCfg<T>::WIDE : kNarrow); }
+template <typename T> int agg_wcols(int Fh) {
+  if (Fh % (kWaves * AggCfg<T>::WIDE) == 0) return AggCfg<T>::WIDE;
+  if (Fh % (kWaves * kMid) == 0) return kMid;
+  return kNarrow;
+}
+template <typename T> int agg_fs(int Fh) { return kWaves * agg_wcols<T>(Fh); }
 
 template <typename T, int MODE>
 hipError_t launch_agg_t(const AggArgs& a, int nfc, int rtiles, int64_t items, hipStream_t s) {
-  if (wide_ok<T>(a.F / a.H)) return launch_agg_w<T, MODE, AggCfg<T>::WIDE>(a, nfc, rtiles, items, s);
+  const int wc = agg_wcols<T>(a.F / a.H);
+  if (wc == AggCfg<T>::WIDE) return launch_agg_w<T, MODE, AggCfg<T>::WIDE>(a, nfc, rtiles, items, s);
+  if (wc == kMid) return launch_agg_w<T, MODE, kMid>(a, nfc, rtiles, items, s);
   return launch_agg_w<T, MODE, kNarrow>(a, nfc, rtiles, items, s);
 }
 

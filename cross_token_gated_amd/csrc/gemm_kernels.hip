@@ -320,6 +320,12 @@ template <typename T, int P, int AS> struct PartsSource {
 };
 
 // A of KO: gbar * v, formed in float and rounded to T parts.
+// Column of gate column n (0 .. F-1) in the head-padded gate layout: head a's
+// columns start at a * Fhp.
+__device__ __forceinline__ int pad_col(int n, int Fh, int Fhp) {
+  return Fh == Fhp ? n : n + (n / Fh) * (Fhp - Fh);
+}
+
 template <typename T, int P, int AS> struct GatedSource {
   static constexpr int PE = piece_elems<T>();
   struct raw {
@@ -527,7 +533,9 @@ void proj_kernel(ProjArgs args) {
           out[r] = cvt<T>(a * __builtin_amdgcn_rcpf(1.0f + __expf(-a)));
           out[4 + r] = cvt<T>(b * __builtin_amdgcn_rcpf(1.0f + __expf(-b)));
         }
-        store_frag<T>(gp + packed_offset((m0 + r0) / 32, grp, n0 + wc * CF::WTN + j * 16 + col, F), out);
+        store_frag<T>(gp + packed_offset((m0 + r0) / 32, grp,
+                                         pad_col(n0 + wc * CF::WTN + j * 16 + col, args.Fh, args.Fhp), args.Fp),
+                      out);
       }
     }
     return;
@@ -554,7 +562,7 @@ void proj_kernel(ProjArgs args) {
           const float a = Cs[(rb * 32 + perm_slot(grp, s)) * kCStride + c];
           out[s] = cvt<T>(a * __builtin_amdgcn_rcpf(1.0f + __expf(-a)));
         }
-        store_frag<T>(gp + packed_offset(mp / 32 + rb, grp, n, F), out);
+        store_frag<T>(gp + packed_offset(mp / 32 + rb, grp, pad_col(n, args.Fh, args.Fhp), args.Fp), out);
       }
     }
     // features: row-major [M_pad, F]
@@ -754,12 +762,39 @@ hipError_t launch_out_t(const OutArgs& a, hipStream_t s) {
   return hipGetLastError();
 }
 
+// Pad columns of the head-padded packed gates: one 16-byte piece (8 rows of
+// one column) per thread and item.
+template <typename T>
+__global__ void zero_pad_kernel(T* gp, int64_t M, int H, int Fh, int Fhp) {
+  const int npad = Fhp - Fh, Fp = H * Fhp;
+  const int64_t n_g = (M / 32) * 4 * H * (int64_t)npad;
+  const u32x4 z = {0u, 0u, 0u, 0u};
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n_g; i += (int64_t)gridDim.x * blockDim.x) {
+    const int c = (int)(i % npad);
+    const int64_t r = i / npad;
+    const int h = (int)(r % H);
+    const int64_t bg = r / H;                               // (blk, grp)
+    *reinterpret_cast<u32x4*>(gp + (bg * Fp + h * Fhp + Fh + c) * 8) = z;
+  }
+}
+
 template <typename T, typename IO>
 hipError_t launch_prep_t(const ProjArgs& a, hipStream_t s) {
   using CF = ProjCfg<T>;
   const int64_t M = (int64_t)a.B * a.Tp;
   hipLaunchKernelGGL((prep_kernel<T, IO, CF::AS>), dim3((unsigned)(M / (kThreads / 64))), dim3(kThreads),
                      0, s, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_zero_pad(void* gp, int64_t M, int H, int Fh, int Fhp, bool bf, hipStream_t s) {
+  if (Fh == Fhp) return hipSuccess;
+  const unsigned grid = 1024;
+  if (bf)
+    hipLaunchKernelGGL(zero_pad_kernel<bf16>, dim3(grid), dim3(256), 0, s, static_cast<bf16*>(gp), M, H, Fh, Fhp);
+  else
+    hipLaunchKernelGGL(zero_pad_kernel<float>, dim3(grid), dim3(256), 0, s, static_cast<float*>(gp), M, H, Fh,
+                       Fhp);
   return hipGetLastError();
 }
 

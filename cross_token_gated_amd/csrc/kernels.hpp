@@ -30,6 +30,8 @@ struct ProjArgs {
   int* zero;           // optional: zero_n ints the row-prep kernel clears (the
   int64_t zero_n;      //   aggregation's split counters), else null / 0
   int B, T, Tp, d, F, HD, dh;
+  int Fh, Fhp, Fp;     // gate columns per head, padded to a multiple of 64, and H * Fhp:
+                       // gp holds head a's column c at a * Fhp + c (v is not padded)
   float rope_base, eps;
 };
 
@@ -58,7 +60,8 @@ struct AggArgs {
   float* part;             // TANGO split mode: partial numerators
   float* part_den;         // TANGO split mode: partial denominators
   int* counters;           // TANGO split mode: one per split tile
-  int B, T, Tp, F, H, dh, window;
+  int B, T, Tp, F, H, dh, window;   // F: gate columns of gp and n_old (head-padded)
+  int Fo, Fho;             // gbar: [B*Tp, Fo] with Fho columns per head (not padded)
   int chunk;               // WANGO: n_old holds the state read-out at chunk boundaries
   int split;               // 1: split the long tiles in two (last finisher combines)
 };
@@ -109,6 +112,10 @@ hipError_t launch_zero_i32(int* p, int64_t n, hipStream_t s);
 // Raise the dynamic-LDS limit of the kernels that need more than 64 KB
 // (once per device).
 hipError_t gemm_kernels_init();
+
+// Zero the pad columns (Fh .. Fhp-1 of every head) of the packed gates, [M
+// rows][H * Fhp], before the projection fills the rest.
+hipError_t launch_zero_pad(void* gp, int64_t M, int H, int Fh, int Fhp, bool bf, hipStream_t s);
 
 // Row-prep kernel alone (RMSNorm scales and operand parts of h * gain).
 hipError_t launch_prep(const ProjArgs& a, bool bf, bool io_bf, hipStream_t s);

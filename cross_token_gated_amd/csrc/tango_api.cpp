@@ -46,6 +46,16 @@ int64_t pad_rows(int64_t T) { return (T + kRowPad - 1) / kRowPad * kRowPad; }
 
 size_t elem_size(int dtype) { return dtype == TANGO_BF16 ? 2 : 4; }
 
+// Gate columns per head, and padded to a multiple of 64: the intermediate
+// gates, features and gbar hold head a's column c at a * head_pad + c, the pad
+// columns zero, so every kernel that walks one head's columns works on whole
+// 64-column blocks.
+int head_width(const tango_shape_t* s) { return s->d_gate / s->n_heads; }
+// (only the packed gates and the WANGO read-out n_old are head-padded; v and
+// gbar keep d_gate columns)
+int head_pad(const tango_shape_t* s) { return (head_width(s) + 63) / 64 * 64; }
+int64_t gate_pad(const tango_shape_t* s) { return (int64_t)s->n_heads * head_pad(s); }
+
 // ---- validation -----------------------------------------------------------
 
 int check_shape(const tango_shape_t* s) {
@@ -68,8 +78,8 @@ int check_shape(const tango_shape_t* s) {
     return fail(TANGO_ERR_UNSUPPORTED, "batch * padded seq_len exceeds 2^26 rows");
   if (s->d_model % 128 != 0 || s->d_model > 4096)
     return fail(TANGO_ERR_UNSUPPORTED, "d_model %d: need a multiple of 128, at most 4096", s->d_model);
-  if (s->d_gate % 64 != 0 || (s->d_gate / s->n_heads) % 64 != 0)
-    return fail(TANGO_ERR_UNSUPPORTED, "d_gate %d: need d_gate and d_gate/n_heads multiples of 64",
+  if (s->d_gate % 64 != 0 || (s->d_gate / s->n_heads) % 4 != 0)
+    return fail(TANGO_ERR_UNSUPPORTED, "d_gate %d: need d_gate a multiple of 64 and d_gate/n_heads of 4",
                 s->d_gate);
   if (s->head_dim != 32 && s->head_dim != 64 && s->head_dim != 128)
     return fail(TANGO_ERR_UNSUPPORTED, "head_dim %d: supported are 32, 64 and 128", s->head_dim);
@@ -146,7 +156,8 @@ Layout make_layout(const tango_shape_t* s, bool wango, int32_t window, int32_t c
   Layout L{};
   const size_t es = elem_size(s->dtype);
   const int64_t M = (int64_t)s->batch * pad_rows(s->seq_len);
-  const int64_t F = s->d_gate, HD = (int64_t)s->n_heads * s->head_dim;
+  const int64_t F = gate_pad(s), HD = (int64_t)s->n_heads * s->head_dim;   // padded gate width
+  const int64_t Fv = s->d_gate;                                              // v, gbar: not padded
   size_t off = 0;
   auto take = [&](size_t bytes) {
     const size_t o = off;
@@ -154,22 +165,22 @@ Layout make_layout(const tango_shape_t* s, bool wango, int32_t window, int32_t c
     return o;
   };
   L.gp = take(M * F * es);
-  L.v = take(M * F * es);
+  L.v = take(M * Fv * es);
   L.qh = take(M * HD * es);
   L.kh = take(M * HD * es);
-  L.gbar = take(M * F * es);
+  L.gbar = take(M * Fv * es);
   const bool bf = s->dtype == TANGO_BF16;
   L.xs = take(proj_parts_bytes(M, s->d_model, bf));
   L.rinv = take(M * sizeof(float));
   if (!wango) {
-    L.agg = tango_agg_plan(s->batch, (int)pad_rows(s->seq_len), s->d_gate, s->n_heads, bf);
+    L.agg = tango_agg_plan(s->batch, (int)pad_rows(s->seq_len), (int)F, s->n_heads, bf);
     const int64_t n = L.agg.n_split_tiles;
     L.part = take((size_t)n * 2 * L.agg.br * L.agg.fs * sizeof(float));
     L.part_den = take((size_t)n * 2 * L.agg.br * sizeof(float));
     L.counters = take((size_t)n * sizeof(int));
   } else {
     (void)window;
-    L.scan = wango_scan_plan(s->batch, (int)pad_rows(s->seq_len), s->d_gate, s->n_heads, chunk);
+    L.scan = wango_scan_plan(s->batch, (int)pad_rows(s->seq_len), (int)F, s->n_heads, chunk);
     L.fq = take(M * HD * es);
     L.fk = take(M * HD * es);
     L.n_old = take(M * F * sizeof(float));
@@ -220,6 +231,9 @@ ProjArgs proj_args(const tango_shape_t* s, const tango_weights_t* w, const void*
   a.Tp = (int)pad_rows(s->seq_len);
   a.d = s->d_model;
   a.F = s->d_gate;
+  a.Fh = head_width(s);
+  a.Fhp = head_pad(s);
+  a.Fp = (int)gate_pad(s);
   a.HD = s->n_heads * s->head_dim;
   a.dh = s->head_dim;
   a.rope_base = s->rope_base;
@@ -255,7 +269,9 @@ AggArgs agg_args(const tango_shape_t* s, const float* theta, const float* null_b
   a.B = s->batch;
   a.T = s->seq_len;
   a.Tp = (int)pad_rows(s->seq_len);
-  a.F = s->d_gate;
+  a.F = (int)gate_pad(s);   // the kernels walk the head-padded gate columns
+  a.Fo = s->d_gate;         // gbar is not padded
+  a.Fho = head_width(s);
   a.H = s->n_heads;
   a.dh = s->head_dim;
   return a;
@@ -275,7 +291,7 @@ ScanArgs scan_args(const tango_shape_t* s, int32_t window, int32_t chunk, const 
   a.B = s->batch;
   a.T = s->seq_len;
   a.Tp = (int)pad_rows(s->seq_len);
-  a.F = s->d_gate;
+  a.F = (int)gate_pad(s);
   a.H = s->n_heads;
   a.dh = s->head_dim;
   a.window = window;
@@ -335,11 +351,15 @@ int stage_proj_common(const tango_shape_t* s, const tango_weights_t* weights, co
                        {weights->w_k, HD * d * es, "w_k"},
                        {weights->rms_gain, d * es, "rms_gain"},
                        {wango ? weights->theta : nullptr, s->n_heads * sizeof(float), "theta"}};
-  const Range outs[] = {{gp, M * F * es, "gp"}, {v, M * F * es, "v"}, {qh, M * HD * es, "qh"},
+  const size_t Fp = gate_pad(s);
+  const Range outs[] = {{gp, M * Fp * es, "gp"}, {v, M * F * es, "v"}, {qh, M * HD * es, "qh"},
                         {kh, M * HD * es, "kh"}, {ws, ps.total, "workspace"},
                         {fq, M * HD * es, "fq"}, {fk, M * HD * es, "fk"}};
   if ((rc = check_ranges(ins, 7, outs, wango ? 7 : 5, nullptr, nullptr))) return rc;
   if ((rc = ensure_init())) return rc;
+  hipError_t ez = launch_zero_pad(gp, (int64_t)M, s->n_heads, head_width(s), head_pad(s),
+                                  s->dtype == TANGO_BF16, static_cast<hipStream_t>(stream));
+  if (ez != hipSuccess) return hip_fail(ez, "pad-column fill");
   ProjArgs pa = proj_args(s, weights, x, gp, v, qh, kh);
   pa.xs = ws;
   pa.rinv = reinterpret_cast<float*>(static_cast<char*>(ws) + ps.rinv);
@@ -398,7 +418,10 @@ int block_common(const tango_shape_t* s, const tango_weights_t* w, bool wango, i
     pa.zero = reinterpret_cast<int*>(base + L.counters);
     pa.zero_n = L.agg.n_split_tiles;
   }
-  hipError_t e = launch_proj(pa, bf, io_bf, st);
+  hipError_t e = launch_zero_pad(gp, (int64_t)s->batch * pad_rows(s->seq_len), s->n_heads, head_width(s),
+                                 head_pad(s), bf, st);
+  if (e != hipSuccess) return hip_fail(e, "pad-column fill");
+  e = launch_proj(pa, bf, io_bf, st);
   if (e != hipSuccess) return hip_fail(e, "projection kernel");
   AggArgs aa = agg_args(s, w->theta, w->null_bias, qh, kh, gp, gbar);
   if (!wango) {
@@ -504,11 +527,11 @@ int tango_stage_aggregate(const tango_shape_t* shape, const float* theta, const 
       return fail(TANGO_ERR_WORKSPACE, "workspace of %zu bytes is smaller than the %zu needed",
                   workspace_bytes, L.total);
     const size_t es = elem_size(s->dtype), M = (size_t)s->batch * pad_rows(s->seq_len);
-    const size_t F = s->d_gate, HD = (size_t)s->n_heads * s->head_dim;
+    const size_t F = gate_pad(s), HD = (size_t)s->n_heads * s->head_dim;   // head-padded gate width
     const Range ins[] = {{qh, M * HD * es, "qh"}, {kh, M * HD * es, "kh"}, {gp, M * F * es, "gp"},
                          {theta, s->n_heads * sizeof(float), "theta"},
                          {null_bias, s->n_heads * sizeof(float), "null_bias"}};
-    const Range outs[] = {{gbar, M * F * es, "gbar"}, {workspace, L.total, "workspace"}};
+    const Range outs[] = {{gbar, M * (size_t)s->d_gate * es, "gbar"}, {workspace, L.total, "workspace"}};
     if ((rc = check_ranges(ins, 5, outs, 2, nullptr, nullptr))) return rc;
     if ((rc = ensure_init())) return rc;
     char* base = static_cast<char*>(workspace);
@@ -568,7 +591,7 @@ int wango_stage_scan(const tango_shape_t* shape, int32_t window, int32_t chunk, 
       return fail(TANGO_ERR_WORKSPACE, "workspace of %zu bytes is smaller than the %zu needed",
                   workspace_bytes, L.total);
     const size_t es = elem_size(s->dtype), M = (size_t)s->batch * pad_rows(s->seq_len);
-    const size_t F = s->d_gate, HD = (size_t)s->n_heads * s->head_dim;
+    const size_t F = gate_pad(s), HD = (size_t)s->n_heads * s->head_dim;   // head-padded gate width
     const Range ins[] = {{fq, M * HD * es, "fq"}, {fk, M * HD * es, "fk"}, {gp, M * F * es, "gp"}};
     const Range outs[] = {{n_old, M * F * sizeof(float), "n_old"},
                           {z_old, M * s->n_heads * sizeof(float), "z_old"},
@@ -595,13 +618,13 @@ int wango_stage_band(const tango_shape_t* shape, const float* theta, const float
       return fail(TANGO_ERR_NULL, "a buffer pointer is NULL");
     const tango_shape_t* s = shape;
     const size_t es = elem_size(s->dtype), M = (size_t)s->batch * pad_rows(s->seq_len);
-    const size_t F = s->d_gate, HD = (size_t)s->n_heads * s->head_dim;
+    const size_t F = gate_pad(s), HD = (size_t)s->n_heads * s->head_dim;   // head-padded gate width
     const Range ins[] = {{qh, M * HD * es, "qh"}, {kh, M * HD * es, "kh"}, {gp, M * F * es, "gp"},
                          {n_old, M * F * sizeof(float), "n_old"},
                          {z_old, M * s->n_heads * sizeof(float), "z_old"},
                          {theta, s->n_heads * sizeof(float), "theta"},
                          {null_bias, s->n_heads * sizeof(float), "null_bias"}};
-    const Range outs[] = {{gbar, M * F * es, "gbar"}};
+    const Range outs[] = {{gbar, M * (size_t)s->d_gate * es, "gbar"}};
     if ((rc = check_ranges(ins, 7, outs, 1, nullptr, nullptr))) return rc;
     if ((rc = ensure_init())) return rc;
     AggArgs aa = agg_args(s, theta, null_bias, qh, kh, gp, gbar);
@@ -644,6 +667,8 @@ int check_decode(const tango_shape_t* s, bool wango, int32_t window, int32_t phi
                   kDecMaxWindow);
   }
   if (s->n_heads > 32) return fail(TANGO_ERR_UNSUPPORTED, "n_heads %d: decode takes at most 32", s->n_heads);
+  if (head_width(s) % 64 != 0)
+    return fail(TANGO_ERR_UNSUPPORTED, "d_gate / n_heads = %d: decode needs a multiple of 64", head_width(s));
   return TANGO_OK;
 }
 

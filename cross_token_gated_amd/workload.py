@@ -75,6 +75,17 @@ WORKLOADS = {
 }
 WORKLOAD_ORDER = list(WORKLOADS)
 
+# The pages' own geometry ([TANGO] §2.3 and Table 5: d = 512, H = 16 heads
+# of 32, gate width F = 28,480 so F/H = 1,780, window and prefix-sum block 64,
+# one block applied 4 times) at the 8,192-token context of the FineWeb-Edu runs.
+PAGES_WORKLOADS = {
+    "tango_pages_t8192_r4": Workload("tango_pages_t8192_r4", "tango", "bf16", 1, 8192, 512, 28480, 16,
+                                     32, repeats=4, seed=8, io_dtype="f32"),
+    "wango_pages_t8192_w64_r4": Workload("wango_pages_t8192_w64_r4", "wango", "bf16", 1, 8192, 512,
+                                         28480, 16, 32, window=64, chunk=64, repeats=4, seed=9,
+                                         io_dtype="f32"),
+}
+
 # Decode workloads: one new token per sequence at position 8192 -- the state
 # holds the 8192 earlier positions -- in the geometry of the T = 8192 workloads
 # above (TANGO: one head of 128, stacked 4 times, each application with its own

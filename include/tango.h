@@ -46,7 +46,7 @@
  * phi_dim != head_dim and window < 1 are TANGO_ERR_SHAPE):
  *    batch >= 1, seq_len >= 1, batch * seq_len <= 2^26,
  *    d_model % 128 == 0 and d_model <= 4096,
- *    d_gate % 64 == 0, (d_gate / n_heads) % 64 == 0,
+ *    d_gate % 64 == 0, (d_gate / n_heads) % 4 == 0,
  *    head_dim in {32, 64, 128}, n_heads * head_dim <= 1024,
  *    WANGO: chunk in {64, 128}, window % chunk == 0.
  */
@@ -60,7 +60,7 @@
 extern "C" {
 #endif
 
-#define TANGO_ABI_VERSION 3
+#define TANGO_ABI_VERSION 4
 
 typedef enum { TANGO_F32 = 0, TANGO_BF16 = 1 } tango_dtype_t;
 
@@ -168,8 +168,9 @@ int wango_block_fwd(const tango_shape_t* shape, const tango_weights_t* weights,
  *                  (after the step at p, z is in copy p mod 2);
  *              each array starts at a 256-byte boundary.
  *   workspace  per-call scratch of *_decode_workspace_size bytes.
- * Supported shapes: those of the block calls, with n_heads <= 32 and (WANGO)
- * window <= 2048; the size functions return 0 for anything else.
+ * Supported shapes: those of the block calls, with n_heads <= 32,
+ * (d_gate / n_heads) % 64 == 0 and (WANGO) window <= 2048; the size functions
+ * return 0 for anything else.
  */
 size_t tango_decode_state_size(const tango_shape_t* shape);
 size_t tango_decode_workspace_size(const tango_shape_t* shape);
@@ -195,9 +196,14 @@ int tango_version(void);                      /* TANGO_ABI_VERSION              
  * buffers.  Intermediate layouts:
  *   Tp        = seq_len rounded up to a multiple of 128 (rows >= T are padding
  *               that the projection stage writes as zeros);
- *   V, gbar   = [B, Tp, F] row-major, dtype;
+ *   Fh, Fhp   = d_gate / n_heads, and rounded up to a multiple of 64;
+ *   F'        = n_heads * Fhp (= d_gate when Fh is a multiple of 64): gp and
+ *               n_old have F' columns, head a's gate column c at a * Fhp + c,
+ *               and the projection stages write zeros into the gates' pad
+ *               columns c >= Fh;
+ *   V, gbar   = [B, Tp, d_gate] row-major, dtype (not padded);
  *   qh, kh    = [B, Tp, H*d_h] row-major, dtype, unit length per head;
- *   gp        = the gates g in the source-packed layout [B][Tp/32][4][F][8]:
+ *   gp        = the gates g in the source-packed layout [B][Tp/32][4][F'][8]:
  *               element (b, blk, grp, f, s) holds g[b, t, f] for
  *               t = 32*blk + (s < 4 ? 4*grp + s : 16 + 4*grp + (s - 4));
  *   fk        = phi(sqrt(tau) k) (the WANGO key features of [TANGO] eq. 8) in
@@ -205,7 +211,7 @@ int tango_version(void);                      /* TANGO_ABI_VERSION              
  *   fq        = phi(sqrt(tau) q), [B, Tp, H*d_h], with the features of every
  *               group of 32 stored in the order e = 4*grp + s (s < 4) or
  *               16 + 4*grp + (s - 4), at position 8*grp + s of the group;
- *   n_old     = float32 in 16 x 16 blocks [B*Tp/16][F/16][64][4]: entry
+ *   n_old     = float32 in 16 x 16 blocks [B*Tp/16][F'/16][64][4]: entry
  *               (blk_i, blk_f, l, r) holds row 16*blk_i + l % 16 and column
  *               16*blk_f + 4*(l / 16) + r;
  *   z_old     = [B, Tp, H] float32.

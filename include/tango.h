@@ -196,11 +196,13 @@ int tango_version(void);                      /* TANGO_ABI_VERSION              
  * buffers.  Intermediate layouts:
  *   Tp        = seq_len rounded up to a multiple of 128 (rows >= T are padding
  *               that the projection stage writes as zeros);
- *   Fh, Fhp   = d_gate / n_heads, and rounded up to a multiple of 64;
- *   F'        = n_heads * Fhp (= d_gate when Fh is a multiple of 64): gp and
- *               n_old have F' columns, head a's gate column c at a * Fhp + c,
- *               and the projection stages write zeros into the gates' pad
- *               columns c >= Fh;
+ *   Fh, Fhp   = d_gate / n_heads, and the padded head width: Fh itself when
+ *               it is a multiple of 64; otherwise, for the WANGO stages, Fh
+ *               rounded up to a multiple of 64, and for the TANGO stages to a
+ *               multiple of 512 if that is at most 1.2 Fh, else of 64;
+ *   F'        = n_heads * Fhp: gp and n_old have F' columns, head a's gate
+ *               column c at a * Fhp + c, and the projection stages write zeros
+ *               into the gates' pad columns c >= Fh;
  *   V, gbar   = [B, Tp, d_gate] row-major, dtype (not padded);
  *   qh, kh    = [B, Tp, H*d_h] row-major, dtype, unit length per head;
  *   gp        = the gates g in the source-packed layout [B][Tp/32][4][F'][8]:

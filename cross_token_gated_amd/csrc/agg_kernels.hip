@@ -257,20 +257,33 @@ __global__ __launch_bounds__(kAggThreads) void agg_kernel(AggArgs a, int nfc, in
     for (int ib = 0; ib < NIB; ++ib)
 #pragma unroll
       for (int fb = 0; fb < NFB; ++fb) acc[ib][fb] = f32x4{0.f, 0.f, 0.f, 0.f};
-    float rowsum = 0.f;
+    // Row sums of this wave's weights.  bfloat16: a fragment of ones times
+    // the weights of each 32-source half (every row of rsum then holds the
+    // column sums); float32: plain adds in rsum[0], summed over lane groups
+    // at the end.
+    f32x4 rsum = {0.f, 0.f, 0.f, 0.f};
+    Frag<T> ones;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) ones[e] = cvt<T>(1.0f);
     const int i_me = i0 + wib * 16 + li;     // this lane's destination in S^T
     // older sources of destination i read pairwise here: C floor((i-W)/C) <= j <= i-W
     const int jphi_lo = (MODE == 1 && i_me >= a.window) ? (i_me - a.window) / a.chunk * a.chunk : 0;
 
-    // weights of source step jb (key block in ks[buf]) into ps[buf]
+    // weights of source step jb (key block in ks[buf]) into ps[buf].  The
+    // S^T accumulator starts at -1, so it holds s - 1 and the weight is
+    // exp2(tau log2e (s - 1)) in one multiply.  A wave whose sources all lie at
+    // or before its first destination needs no causal mask (TANGO: every step
+    // but the diagonal ones).
     auto weights = [&](int jb, int buf) {
       const int j0 = jb * BC;
       // WANGO: does this step hold older sources of some row of the tile?
       const bool phi_step = MODE == 1 && i0 + BR - 1 >= a.window && j0 <= i0 + BR - 1 - a.window;
+      const bool unmasked = MODE == 0 && j0 + (wjb + JBW) * 16 - 1 <= i0 + wib * 16;   // wave-uniform
+      Quad<T> pq_even;
 #pragma unroll
       for (int t = 0; t < JBW; ++t) {
         const int jj = wjb + t;   // wjb is even, so jj & 1 == t & 1
-        f32x4 s = {0.f, 0.f, 0.f, 0.f}, sphi = {0.f, 0.f, 0.f, 0.f};
+        f32x4 s = {-1.f, -1.f, -1.f, -1.f}, sphi = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks) {
           const Frag<T> kf = lds_frag(sm.ks[buf], KS, jj, ks);
@@ -283,21 +296,31 @@ __global__ __launch_bounds__(kAggThreads) void agg_kernel(AggArgs a, int nfc, in
           }
         }
         Quad<T> pq;
-        float psum = 0.f;
+        if (unmasked) {
+          // the argument lies in [-2 tau log2 e, 0] >= -58: v_exp_f32 needs no range fix-up
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const int j = j0 + jj * 16 + lg * 4 + r;
-          float p = 0.f;
-          if (j <= i_me && (MODE == 0 || j > i_me - a.window)) {
-            // the argument lies in [-2 tau log2 e, 0] >= -58: v_exp_f32 needs no range fix-up
-            p = __builtin_amdgcn_exp2f(ktau * (s[r] - 1.0f));
-          } else if (phi_step && i_me >= a.window && j <= i_me - a.window && j >= jphi_lo) {
-            p = escale * sphi[r];   // same e^{-tau} scale as the exp weights
+          for (int r = 0; r < 4; ++r) pq[r] = cvt<T>(__builtin_amdgcn_exp2f(ktau * s[r]));
+        } else {
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            const int j = j0 + jj * 16 + lg * 4 + r;
+            float p = 0.f;
+            if (j <= i_me && (MODE == 0 || j > i_me - a.window)) {
+              p = __builtin_amdgcn_exp2f(ktau * s[r]);
+            } else if (phi_step && i_me >= a.window && j <= i_me - a.window && j >= jphi_lo) {
+              p = escale * sphi[r];   // same e^{-tau} scale as the exp weights
+            }
+            pq[r] = cvt<T>(p);
           }
-          pq[r] = cvt<T>(p);
-          psum += tof<T>(pq[r]);
         }
-        rowsum += psum;
+        if constexpr (sizeof(T) == 2) {
+          // blocks t - 1 and t make one half: a lane's 8 weights of column li
+          if (t & 1) mma(rsum, ones, join(pq_even, pq));
+          else pq_even = pq;
+        } else {
+#pragma unroll
+          for (int r = 0; r < 4; ++r) rsum[0] += pq[r];
+        }
         // the weights of sources 4 lg + r of block jj are slots r (jj even)
         // or 4 + r (jj odd) of this lane's fragment for the half jj / 2: the
         // first or second 8 bytes of the piece (bf16), or chunk 0 or 1 (float32)
@@ -353,7 +376,7 @@ __global__ __launch_bounds__(kAggThreads) void agg_kernel(AggArgs a, int nfc, in
 
     // ---- row sums: over lane groups, then over the waves sharing a block ----
     {
-      const float rs = group_sum(rowsum);
+      const float rs = sizeof(T) == 2 ? rsum[0] : group_sum(rsum[0]);
       if (lg == 0) sm.den[wave / NIB][wib * 16 + li] = rs;
     }
     __syncthreads();

@@ -69,13 +69,16 @@ struct Job {
 // block of 16 rows x 32 k is stored as 256-byte regions, one per (chunk h,
 // k group g) with g covering k = 8g .. 8g + 7 in the order of the fragment's
 // slots (PPF chunks of 16 bytes per fragment: 1 for bf16, 2 for float32);
-// row r of the block sits at position (r + 4g) mod 16 of its region.  Each
-// group of 16 lanes of an MFMA fragment read then covers one region, and a
-// loader whose four consecutive lanes fetch 64 contiguous bytes of one row
-// writes 16 distinct positions: both at the full gfx950 LDS width.
+// row r of the block sits at position r xor g of its region.  An MFMA
+// fragment read (lanes 16g .. 16g + 15: rows 0 .. 15 of group g) then covers
+// one region, which gfx950 serves at its full 256 bytes per clock, and so
+// does the key loader (four consecutive lanes fetch the 64 contiguous bytes
+// of one row, keeping its global loads coalesced) at the LDS write rate.
+// Measured on gfx950: a rotation by 4g instead halves the read rate, and the
+// plain order r makes the loader's writes 4-way conflicted.
 template <typename T> constexpr int frag_chunks() { return (int)sizeof(T) / 2; }
 __device__ __forceinline__ int region_pos(int region, int r, int g) {
-  return region * 256 + ((r + 4 * g) & 15) * 16;
+  return region * 256 + (r ^ g) * 16;
 }
 
 template <typename T, int DH> struct AggLds {
@@ -188,9 +191,11 @@ __global__ __launch_bounds__(kAggThreads) void agg_kernel(AggArgs a, int nfc, in
 
   // key block jb -> registers -> LDS buffer.  Chunk c = wave + kWaves p of
   // the block (16-source block jj, k block kb, chunk ch); lane l fetches row
-  // l / 4 and k group l % 4 of it.
+  // l / 4 and k group l % 4 of it.  A wave past the last chunk (small heads)
+  // fetches a copy of chunk c mod KCH and does not store it, so that every
+  // wave issues the same loads.
   auto key_chunk = [&](int p, int& row, int& col, int& off) {
-    const int c = wave + kWaves * p;
+    const int c = (wave + kWaves * p) % KCH;
     const int jj = c / (KS * PPF), kb = (c / PPF) % KS, ch = c % PPF;
     const int r = lane >> 2, g = lane & 3;
     row = jj * 16 + r;
@@ -200,7 +205,6 @@ __global__ __launch_bounds__(kAggThreads) void agg_kernel(AggArgs a, int nfc, in
   auto key_fetch = [&](int jb, u32x4 (&kr)[KPT]) {
 #pragma unroll
     for (int p = 0; p < KPT; ++p) {
-      if (KCH % kWaves != 0 && wave + kWaves * p >= KCH) break;   // wave-uniform
       int row, col, off;
       key_chunk(p, row, col, off);
       kr[p] = *reinterpret_cast<const u32x4*>(kh + (mseq + (int64_t)jb * BC + row) * HD + h * DH + col);
@@ -209,7 +213,7 @@ __global__ __launch_bounds__(kAggThreads) void agg_kernel(AggArgs a, int nfc, in
   auto key_stash = [&](int buf, const u32x4 (&kr)[KPT]) {
 #pragma unroll
     for (int p = 0; p < KPT; ++p) {
-      if (KCH % kWaves != 0 && wave + kWaves * p >= KCH) break;
+      if (KCH % kWaves != 0 && wave + kWaves * p >= KCH) break;   // wave-uniform
       int row, col, off;
       key_chunk(p, row, col, off);
       *reinterpret_cast<u32x4*>(reinterpret_cast<unsigned char*>(sm.ks[buf]) + off) = kr[p];
@@ -226,11 +230,15 @@ __global__ __launch_bounds__(kAggThreads) void agg_kernel(AggArgs a, int nfc, in
                   load_quad<T>(reinterpret_cast<const T*>(base + 4 * 256)));
     }
   };
+  // A wave past the head's width (narrow variant) reads the head's first
+  // columns and multiplies them like the others; only its stores are
+  // skipped.  Every step then issues the same loads and MFMAs in every wave,
+  // which keeps the compiler's load-counter waits exact across the loop.
+  const int64_t gcol0 = has_cols ? col0 : (int64_t)h * Fh;
   auto gate_fetch = [&](int jb, int ks, Frag<T> (&gf)[NFB]) {
-    if (!has_cols) return;
     const int64_t blk = (mseq + (int64_t)jb * BC) / 32 + ks;
 #pragma unroll
-    for (int fb = 0; fb < NFB; ++fb) gf[fb] = load_frag<T>(gp + packed_offset(blk, lg, col0 + fb * 16 + li, F));
+    for (int fb = 0; fb < NFB; ++fb) gf[fb] = load_frag<T>(gp + packed_offset(blk, lg, gcol0 + fb * 16 + li, F));
   };
 
   // one destination tile over a range of source steps (called once or twice)
@@ -331,7 +339,6 @@ __global__ __launch_bounds__(kAggThreads) void agg_kernel(AggArgs a, int nfc, in
     };
     // gbar^T += G^T P^T over one half (32 sources) of the step in ps[buf]
     auto product = [&](int buf, int ks, const Frag<T> (&gf)[NFB]) {
-      if (!has_cols) return;
 #pragma unroll
       for (int ih = 0; ih < NIB; ih += 4) {
         Frag<T> pf[4];
@@ -357,20 +364,23 @@ __global__ __launch_bounds__(kAggThreads) void agg_kernel(AggArgs a, int nfc, in
       weights(job.jb0, 0);
       __syncthreads();
     }
+    // Every step issues the same global loads (past the last step they
+    // re-read it, and such keys land in a buffer no later step reads): with
+    // no load or consumer under a condition, the compiler's load-counter
+    // waits stay exact across the loop instead of draining every load.
     Frag<T> ga[NFB], gb[NFB];
     gate_fetch(job.jb0, 0, ga);
     for (int jb = job.jb0; jb <= job.jb1; ++jb) {
       const int buf = (jb - job.jb0) & 1;
       const bool more = jb + 1 <= job.jb1;
-      const bool more2 = jb + 2 <= job.jb1;
       u32x4 kr[KPT];
-      if (more2) key_fetch(jb + 2, kr);
+      key_fetch(min(jb + 2, job.jb1), kr);
       gate_fetch(jb, 1, gb);
       product(buf, 0, ga);
-      if (more) gate_fetch(jb + 1, 0, ga);
+      gate_fetch(min(jb + 1, job.jb1), 0, ga);
       if (more) weights(jb + 1, buf ^ 1);
       product(buf, 1, gb);
-      if (more2) key_stash(buf, kr);   // ks[buf] was last read by weights(jb) one step ago
+      key_stash(buf, kr);   // ks[buf] was last read by weights(jb) one step ago
       __syncthreads();
     }
 

@@ -78,11 +78,13 @@ template <typename T> constexpr int piece_elems() { return 16 / (int)sizeof(T); 
 // 16 rows x 32 columns; the 16-byte pieces of a block (row r, k group g =
 // columns 8g .. 8g + 7, in PPF chunks h of PE elements: PPF = 1 for bf16, 2
 // for float32) live in 256-byte regions, one per (chunk, group), at position
-// (r + 4g) mod 16.  An MFMA fragment read (16 lanes per group: rows 0..15 of
-// one group) then covers one whole region, and the loaders (four consecutive
-// lanes fetch 64 contiguous bytes of one row, which keeps the global loads
-// coalesced) write 16 distinct positions per 16 lanes.  On gfx950 both run at
-// the full LDS width; a padded row-major tile reads at half of it.
+// r xor g.  An MFMA fragment read (16 lanes per group: rows 0..15 of one
+// group) then covers one whole region, which gfx950 serves at its full 256
+// bytes per clock, and the loaders (four consecutive lanes fetch 64
+// contiguous bytes of one row, which keeps the global loads coalesced) write
+// at the LDS write rate.  Measured on gfx950: a rotation (r + 4g) mod 16
+// halves the read rate, and the plain order r makes the loader's writes
+// 4-way conflicted.
 template <typename T> constexpr int frag_chunks() { return (int)sizeof(T) / 2; }   // PPF
 template <class CF, typename T> constexpr int tile_chunks(int rows) {
   return rows / 16 * (CF::BK / 32) * frag_chunks<T>();
@@ -94,7 +96,7 @@ __device__ __forceinline__ int piece_offset(int row, int kp) {
   const int kb = kp * PE / 32, within = kp % (32 / PE);
   const int g = within / PPF, h = within % PPF, r = row & 15;
   const int region = (((row >> 4) * NKB + kb) * PPF + h) * 4 + g;
-  return region * 256 + ((r + 4 * g) & 15) * 16;
+  return region * 256 + (r ^ g) * 16;
 }
 template <class CF, typename T> constexpr size_t ops_bytes() {
   return 2 * (size_t)tile_chunks<CF, T>(CF::AS * CF::BM + CF::BN) * 1024;
@@ -161,7 +163,7 @@ __device__ __forceinline__ Frag<T> lds_frag(const T* tile, int rb, int kb, int l
   constexpr int PPF = frag_chunks<T>(), NKB = CF::BK / 32;
   const int r = lane & 15, g = lane >> 4;
   const unsigned char* base = reinterpret_cast<const unsigned char*>(tile) +
-                              ((rb * NKB + kb) * PPF * 4 + g) * 256 + ((r + 4 * g) & 15) * 16;
+                              ((rb * NKB + kb) * PPF * 4 + g) * 256 + (r ^ g) * 16;
   if constexpr (PPF == 1) {
     return load_frag<T>(reinterpret_cast<const T*>(base));
   } else {

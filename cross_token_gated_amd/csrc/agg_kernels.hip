@@ -194,28 +194,32 @@ __global__ __launch_bounds__(kAggThreads) void agg_kernel(AggArgs a, int nfc, in
   // l / 4 and k group l % 4 of it.  A wave past the last chunk (small heads)
   // fetches a copy of chunk c mod KCH and does not store it, so that every
   // wave issues the same loads.
-  auto key_chunk = [&](int p, int& row, int& col, int& off) {
+  // (The global addresses are split into a wave-uniform 64-bit base and a
+  // 32-bit lane offset.)
+  const int k_lane = (lane >> 2) * HD + (lane & 3) * 8;
+  auto key_chunk = [&](int p, int& row0, int& col, int& off) {
     const int c = (wave + kWaves * p) % KCH;
     const int jj = c / (KS * PPF), kb = (c / PPF) % KS, ch = c % PPF;
     const int r = lane >> 2, g = lane & 3;
-    row = jj * 16 + r;
-    col = kb * 32 + g * 8 + ch * PE;
+    row0 = jj * 16;
+    col = kb * 32 + ch * PE;
     off = region_pos(((jj * KS + kb) * PPF + ch) * 4 + g, r, g);
   };
   auto key_fetch = [&](int jb, u32x4 (&kr)[KPT]) {
 #pragma unroll
     for (int p = 0; p < KPT; ++p) {
-      int row, col, off;
-      key_chunk(p, row, col, off);
-      kr[p] = *reinterpret_cast<const u32x4*>(kh + (mseq + (int64_t)jb * BC + row) * HD + h * DH + col);
+      int row0, col, off;
+      key_chunk(p, row0, col, off);
+      const T* base = kh + (mseq + (int64_t)jb * BC + row0) * HD + h * DH + col;   // wave-uniform
+      kr[p] = *reinterpret_cast<const u32x4*>(base + k_lane);
     }
   };
   auto key_stash = [&](int buf, const u32x4 (&kr)[KPT]) {
 #pragma unroll
     for (int p = 0; p < KPT; ++p) {
       if (KCH % kWaves != 0 && wave + kWaves * p >= KCH) break;   // wave-uniform
-      int row, col, off;
-      key_chunk(p, row, col, off);
+      int row0, col, off;
+      key_chunk(p, row0, col, off);
       *reinterpret_cast<u32x4*>(reinterpret_cast<unsigned char*>(sm.ks[buf]) + off) = kr[p];
     }
   };
@@ -235,10 +239,12 @@ __global__ __launch_bounds__(kAggThreads) void agg_kernel(AggArgs a, int nfc, in
   // skipped.  Every step then issues the same loads and MFMAs in every wave,
   // which keeps the compiler's load-counter waits exact across the loop.
   const int64_t gcol0 = has_cols ? col0 : (int64_t)h * Fh;
+  const int g_lane = (lg * F + li) * 8;   // packed_offset(blk, lg, col, F) - packed_offset(blk, 0, col - li, F)
   auto gate_fetch = [&](int jb, int ks, Frag<T> (&gf)[NFB]) {
     const int64_t blk = (mseq + (int64_t)jb * BC) / 32 + ks;
+    const T* base = gp + packed_offset(blk, 0, gcol0, F);   // wave-uniform
 #pragma unroll
-    for (int fb = 0; fb < NFB; ++fb) gf[fb] = load_frag<T>(gp + packed_offset(blk, lg, gcol0 + fb * 16 + li, F));
+    for (int fb = 0; fb < NFB; ++fb) gf[fb] = load_frag<T>(base + g_lane + fb * 16 * 8);
   };
 
   // one destination tile over a range of source steps (called once or twice)

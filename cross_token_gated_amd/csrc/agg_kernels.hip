@@ -17,20 +17,20 @@
 // With no running maximum, partial sums over disjoint source ranges combine by
 // plain addition and the accumulators are never rescaled.
 //
-// Workgroup: 4 waves (one per SIMD, so each wave owns the whole 512-entry
-// register file; the float32 accumulator block lives in AGPRs) over a BR-row
-// destination tile and FS = 4 * WCOLS gate columns of one head.  Per step of
-// 64 sources:
+// Workgroup: 8 waves (two per SIMD) over a BR-row destination tile and
+// FS = 8 * WCOLS gate columns of one head.  Per step of 64 sources:
 //   * the key block is staged once in LDS (double-buffered, fetched two steps
 //     ahead);
-//   * each wave computes S^T = K Q^T for its share of destination rows against
-//     all 64 sources and writes the weights to LDS -- one step ahead, between
-//     the two halves of the current step's product;
+//   * wave w computes S^T = K Q^T for destination block w against all 64
+//     sources, exponentiates, and writes the weights to LDS -- one step
+//     ahead, between the two halves of the current step's product -- and
+//     takes its row sums with one MFMA against a fragment of ones per half;
 //   * every wave multiplies its own WCOLS gate columns: gbar^T += G^T P^T, the
 //     gates read straight from the packed layout in global memory (their k
 //     order is the row order of the S^T accumulators), double-buffered in
 //     registers.
-// One barrier per step.
+// One barrier per step; every step issues the same loads, so the compiler's
+// load-counter waits stay exact across the loop.
 //
 // TANGO load balance: with B*H*column-chunks*(tiles/2) >= 256 the long and the
 // short tile of a causal pair share one workgroup.  Otherwise each long tile is

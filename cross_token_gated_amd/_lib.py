@@ -25,6 +25,7 @@ EXPORTS = [
     "wango_stage_scan", "wango_stage_band",
     "tango_decode_state_size", "tango_decode_workspace_size", "tango_decode_step",
     "wango_decode_state_size", "wango_decode_workspace_size", "wango_decode_step",
+    "tango_aggregate_fwd_train", "tango_aggregate_bwd_workspace_size", "tango_aggregate_bwd",
 ]
 
 
@@ -84,6 +85,10 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
         "wango_decode_state_size": (sz, [S, i32, i32]),
         "wango_decode_workspace_size": (sz, [S, i32, i32]),
         "wango_decode_step": (ctypes.c_int, [S, W, i32, i32, vp, vp, vp, vp, sz, vp, sz, vp]),
+        "tango_aggregate_fwd_train": (ctypes.c_int, [S, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]),
+        "tango_aggregate_bwd_workspace_size": (sz, [S]),
+        "tango_aggregate_bwd": (ctypes.c_int, [S, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz,
+                                               vp]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(lib, name)

@@ -18,7 +18,8 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libtango.so")
-SOURCES = ["gemm_kernels.hip", "agg_kernels.hip", "scan_kernels.hip", "decode_kernels.hip", "tango_api.cpp"]
+SOURCES = ["gemm_kernels.hip", "agg_kernels.hip", "scan_kernels.hip", "decode_kernels.hip", "bwd_kernels.hip",
+           "tango_api.cpp"]
 ARCH = "gfx950"
 
 

@@ -458,7 +458,14 @@ __global__ __launch_bounds__(kAggThreads) void agg_kernel(AggArgs a, int nfc, in
                                     __HIP_MEMORY_SCOPE_AGENT);
         dsum += null_w * (float)(i + 1);
         if (MODE == 1) dsum += escale * a.z_old[(mseq + i) * a.H + h];
-        const float inv = 1.0f / dsum;
+        // TANGO options: the denominator for a later backward pass (one
+        // writer per row: column chunk 0, wave 0); the numerator alone; rows
+        // stored in reverse order (rows past the end are not stored then)
+        if (MODE == 0 && a.den_out && fc == 0 && wave == 0 && lg == 0 && i < a.T)
+          a.den_out[(mseq + i) * a.H + h] = dsum;
+        const float inv = (MODE == 0 && a.num_only) ? 1.0f : 1.0f / dsum;
+        const int64_t orow = (MODE == 0 && a.rev_out) ? mseq + (a.T - 1 - i) : mseq + i;
+        const bool ostore = !(MODE == 0 && a.rev_out) || i < a.T;
 #pragma unroll
         for (int fb = 0; fb < NFB; ++fb) {
           f32x4 num = acc[ib][fb];
@@ -475,8 +482,8 @@ __global__ __launch_bounds__(kAggThreads) void agg_kernel(AggArgs a, int nfc, in
           }
           // gbar is not head-padded: columns past the head's width are pad
           const int c = f_base + fb * 16 + lg * 4;
-          if (c < a.Fho)
-            store_quad<T>(gbar + (mseq + i) * a.Fo + (int64_t)h * a.Fho + c, cvt_quad<T>(num * inv));
+          if (c < a.Fho && ostore)
+            store_quad<T>(gbar + orow * a.Fo + (int64_t)h * a.Fho + c, cvt_quad<T>(num * inv));
         }
       }
     }

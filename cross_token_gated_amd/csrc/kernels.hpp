@@ -64,6 +64,10 @@ struct AggArgs {
   int Fo, Fho;             // gbar: [B*Tp, Fo] with Fho columns per head (not padded)
   int chunk;               // WANGO: n_old holds the state read-out at chunk boundaries
   int split;               // 1: split the long tiles in two (last finisher combines)
+  // TANGO options (all off when zero / null):
+  float* den_out;          // [B*Tp, H]: the ratio's denominator, e^{-tau} units (rows < T)
+  int num_only;            // 1: write the numerator alone (no row sums, no null, no division)
+  int rev_out;             // 1: row i of a sequence is stored at row T - 1 - i (rows < T only)
 };
 
 // WANGO older-prefix scan.
@@ -119,6 +123,50 @@ hipError_t launch_zero_pad(void* gp, int64_t M, int H, int Fh, int Fhp, bool bf,
 
 // Row-prep kernel alone (RMSNorm scales and operand parts of h * gain).
 hipError_t launch_prep(const ProjArgs& a, bool bf, bool io_bf, hipStream_t s);
+
+// ---- backward of the TANGO aggregation -------------------------------------
+
+struct BwdArgs {
+  // inputs (bf16 unless noted)
+  const void* qh;          // [B*Tp, H*dh] unit queries (forward)
+  const void* kh;          // [B*Tp, H*dh] unit keys
+  const void* gp;          // packed gates [B*Tp/32][4][Fp][8] (forward, head-padded)
+  const void* gbar;        // [B*Tp, F] forward output
+  const void* dgbar;       // [B*Tp, F] incoming gradient
+  const float* den;        // [B*Tp, H] forward denominators (e^{-tau} units), float32
+  const float* theta;      // [H]
+  const float* null_bias;  // [H] or null
+  // scratch
+  void* u_rm;              // [B*Tp][H][FhC] u = dgbar / den, row-major
+  void* g_rm;              // [B*Tp][H][FhC] gates, row-major
+  void* qp;                // [B*Tp/32][4][H*dh][8] packed queries
+  void* kp;                // packed keys
+  void* q_rev;             // [B*Tp, H*dh] queries, every sequence reversed
+  void* k_rev;             // keys, reversed
+  void* u_rev_pk;          // packed reversed u, [B*Tp/32][4][Fp][8]
+  float* delta;            // [H][B*Tp] float32
+  float* part_q;           // [nchunk][B*Tp][H*dh] float32 chunk partials of dq
+  float* part_k;           // same for dk
+  float* part_theta;       // [items] float32
+  // outputs
+  float* dq;               // [B*Tp, H*dh] float32 (zero on rows past the end)
+  float* dk;               // [B*Tp, H*dh]
+  float* dtheta;           // [H]
+  float* dnull;            // [H] or null
+  int B, T, Tp, H, dh;
+  int F, Fh;               // gate columns (unpadded) in all and per head
+  int Fhp, Fp;             // head-padded width of the packed gates, H * Fhp
+  int FhC;                 // head width of u_rm / g_rm (a multiple of 256)
+};
+
+struct BwdPlan {
+  int FhC, nchunk, rtiles, half;
+  int64_t items;
+};
+BwdPlan tango_bwd_plan(int B, int Tp, int Fh, int H);
+hipError_t launch_tango_bwd_prep(const BwdArgs& a, const BwdPlan& p, hipStream_t s);
+hipError_t launch_tango_dqk(const BwdArgs& a, const BwdPlan& p, hipStream_t s);
+hipError_t launch_tango_bwd_finish(const BwdArgs& a, const BwdPlan& p, hipStream_t s);
 
 // ---- autoregressive decode -------------------------------------------------
 

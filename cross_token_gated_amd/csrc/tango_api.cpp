@@ -554,6 +554,183 @@ int tango_stage_aggregate(const tango_shape_t* shape, const float* theta, const 
   });
 }
 
+// ---- backward of the TANGO aggregation ------------------------------------
+
+int tango_aggregate_fwd_train(const tango_shape_t* shape, const float* theta, const float* null_bias,
+                              const void* qh, const void* kh, const void* gp, void* gbar, float* den,
+                              void* workspace, size_t workspace_bytes, void* hip_stream) {
+  return guarded([&] {
+    int rc = check_shape(shape);
+    if (rc) return rc;
+    if (!theta || !qh || !kh || !gp || !gbar || !den || !workspace)
+      return fail(TANGO_ERR_NULL, "a buffer pointer is NULL");
+    const tango_shape_t* s = shape;
+    const Layout L = make_layout(s, false, 0, 0);
+    if (workspace_bytes < L.total)
+      return fail(TANGO_ERR_WORKSPACE, "workspace of %zu bytes is smaller than the %zu needed",
+                  workspace_bytes, L.total);
+    const size_t es = elem_size(s->dtype), M = (size_t)s->batch * pad_rows(s->seq_len);
+    const size_t F = gate_pad(s, false), HD = (size_t)s->n_heads * s->head_dim;
+    const Range ins[] = {{qh, M * HD * es, "qh"}, {kh, M * HD * es, "kh"}, {gp, M * F * es, "gp"},
+                         {theta, s->n_heads * sizeof(float), "theta"},
+                         {null_bias, s->n_heads * sizeof(float), "null_bias"}};
+    const Range outs[] = {{gbar, M * (size_t)s->d_gate * es, "gbar"},
+                          {den, M * s->n_heads * sizeof(float), "den"},
+                          {workspace, L.total, "workspace"}};
+    if ((rc = check_ranges(ins, 5, outs, 3, nullptr, nullptr))) return rc;
+    if ((rc = ensure_init())) return rc;
+    char* base = static_cast<char*>(workspace);
+    AggArgs aa = agg_args(s, theta, null_bias, qh, kh, gp, gbar, false);
+    aa.part = reinterpret_cast<float*>(base + L.part);
+    aa.part_den = reinterpret_cast<float*>(base + L.part_den);
+    aa.counters = reinterpret_cast<int*>(base + L.counters);
+    aa.den_out = den;
+    hipError_t e = launch_tango_agg(aa, L.agg, s->dtype == TANGO_BF16, false,
+                                    static_cast<hipStream_t>(hip_stream));
+    return e == hipSuccess ? ok() : hip_fail(e, "aggregation kernel");
+  });
+}
+
+namespace {
+
+struct BwdLayout {
+  size_t u_rm, g_rm, qp, kp, q_rev, k_rev, u_rev_pk, delta, part_q, part_k, part_theta;
+  size_t part, part_den, counters;   // split scratch of the reversed aggregation (dg)
+  size_t total;
+  BwdPlan plan;
+  AggPlan agg;
+};
+
+BwdLayout make_bwd_layout(const tango_shape_t* s) {
+  BwdLayout L{};
+  const int64_t M = (int64_t)s->batch * pad_rows(s->seq_len);
+  const int64_t HD = (int64_t)s->n_heads * s->head_dim, Fp = gate_pad(s, false);
+  L.plan = tango_bwd_plan(s->batch, (int)pad_rows(s->seq_len), head_width(s), s->n_heads);
+  L.agg = tango_agg_plan(s->batch, (int)pad_rows(s->seq_len), (int)Fp, s->n_heads, true);
+  size_t off = 0;
+  auto take = [&](size_t bytes) {
+    const size_t o = off;
+    off = align256(off + bytes);
+    return o;
+  };
+  const size_t es = 2;   // bfloat16
+  L.u_rm = take((size_t)M * s->n_heads * L.plan.FhC * es);
+  L.g_rm = take((size_t)M * s->n_heads * L.plan.FhC * es);
+  L.qp = take((size_t)M * HD * es);
+  L.kp = take((size_t)M * HD * es);
+  L.q_rev = take((size_t)M * HD * es);
+  L.k_rev = take((size_t)M * HD * es);
+  L.u_rev_pk = take((size_t)M * Fp * es);
+  L.delta = take((size_t)M * s->n_heads * sizeof(float));
+  L.part_q = take((size_t)L.plan.nchunk * M * HD * sizeof(float));
+  L.part_k = take((size_t)L.plan.nchunk * M * HD * sizeof(float));
+  L.part_theta = take((size_t)L.plan.items * sizeof(float));
+  const int64_t n = L.agg.n_split_tiles;
+  L.part = take((size_t)n * 2 * L.agg.br * L.agg.fs * sizeof(float));
+  L.part_den = take((size_t)n * 2 * L.agg.br * sizeof(float));
+  L.counters = take((size_t)n * sizeof(int));
+  L.total = off;
+  return L;
+}
+
+int check_bwd_shape(const tango_shape_t* s) {
+  int rc = check_shape(s);
+  if (rc) return rc;
+  if (s->dtype != TANGO_BF16)
+    return fail(TANGO_ERR_UNSUPPORTED, "the aggregation backward is implemented for bfloat16 only");
+  return TANGO_OK;
+}
+
+}  // namespace
+
+size_t tango_aggregate_bwd_workspace_size(const tango_shape_t* shape) {
+  if (!shape || check_bwd_shape(shape) != TANGO_OK) return 0;
+  return make_bwd_layout(shape).total;
+}
+
+int tango_aggregate_bwd(const tango_shape_t* shape, const float* theta, const float* null_bias,
+                        const void* qh, const void* kh, const void* gp, const void* gbar,
+                        const float* den, const void* dgbar, float* dq, float* dk, void* dg,
+                        float* dtheta, float* dnull, void* workspace, size_t workspace_bytes,
+                        void* hip_stream) {
+  return guarded([&] {
+    int rc = check_bwd_shape(shape);
+    if (rc) return rc;
+    if (!theta || !qh || !kh || !gp || !gbar || !den || !dgbar || !dq || !dk || !dg || !dtheta ||
+        !workspace)
+      return fail(TANGO_ERR_NULL, "a buffer pointer is NULL");
+    if ((null_bias == nullptr) != (dnull == nullptr))
+      return fail(TANGO_ERR_NULL, "null_bias and dnull must both be given or both be NULL");
+    const tango_shape_t* s = shape;
+    const BwdLayout L = make_bwd_layout(s);
+    if (workspace_bytes < L.total)
+      return fail(TANGO_ERR_WORKSPACE, "workspace of %zu bytes is smaller than the %zu needed",
+                  workspace_bytes, L.total);
+    const size_t M = (size_t)s->batch * pad_rows(s->seq_len);
+    const size_t F = s->d_gate, Fp = gate_pad(s, false), HD = (size_t)s->n_heads * s->head_dim;
+    const size_t H = s->n_heads;
+    const Range ins[] = {{qh, M * HD * 2, "qh"},          {kh, M * HD * 2, "kh"},
+                         {gp, M * Fp * 2, "gp"},          {gbar, M * F * 2, "gbar"},
+                         {den, M * H * sizeof(float), "den"}, {dgbar, M * F * 2, "dgbar"},
+                         {theta, H * sizeof(float), "theta"}, {null_bias, H * sizeof(float), "null_bias"}};
+    const Range outs[] = {{dq, M * HD * sizeof(float), "dq"},  {dk, M * HD * sizeof(float), "dk"},
+                          {dg, M * F * 2, "dg"},               {dtheta, H * sizeof(float), "dtheta"},
+                          {dnull, H * sizeof(float), "dnull"}, {workspace, L.total, "workspace"}};
+    if ((rc = check_ranges(ins, 8, outs, 6, nullptr, nullptr))) return rc;
+    if ((rc = ensure_init())) return rc;
+    const hipStream_t st = static_cast<hipStream_t>(hip_stream);
+    char* base = static_cast<char*>(workspace);
+    BwdArgs a{};
+    a.qh = qh;
+    a.kh = kh;
+    a.gp = gp;
+    a.gbar = gbar;
+    a.dgbar = dgbar;
+    a.den = den;
+    a.theta = theta;
+    a.null_bias = null_bias;
+    a.u_rm = base + L.u_rm;
+    a.g_rm = base + L.g_rm;
+    a.qp = base + L.qp;
+    a.kp = base + L.kp;
+    a.q_rev = base + L.q_rev;
+    a.k_rev = base + L.k_rev;
+    a.u_rev_pk = base + L.u_rev_pk;
+    a.delta = reinterpret_cast<float*>(base + L.delta);
+    a.part_q = reinterpret_cast<float*>(base + L.part_q);
+    a.part_k = reinterpret_cast<float*>(base + L.part_k);
+    a.part_theta = reinterpret_cast<float*>(base + L.part_theta);
+    a.dq = dq;
+    a.dk = dk;
+    a.dtheta = dtheta;
+    a.dnull = dnull;
+    a.B = s->batch;
+    a.T = s->seq_len;
+    a.Tp = (int)pad_rows(s->seq_len);
+    a.H = s->n_heads;
+    a.dh = s->head_dim;
+    a.F = s->d_gate;
+    a.Fh = head_width(s);
+    a.Fhp = head_pad(s, false);
+    a.Fp = (int)Fp;
+    a.FhC = L.plan.FhC;
+    hipError_t e = launch_tango_bwd_prep(a, L.plan, st);
+    if (e != hipSuccess) return hip_fail(e, "backward prep kernels");
+    // dg: the aggregation of the time-reversed problem, numerator only
+    AggArgs aa = agg_args(s, theta, nullptr, a.k_rev, a.q_rev, a.u_rev_pk, dg, false);
+    aa.part = reinterpret_cast<float*>(base + L.part);
+    aa.part_den = reinterpret_cast<float*>(base + L.part_den);
+    aa.counters = reinterpret_cast<int*>(base + L.counters);
+    aa.num_only = 1;
+    aa.rev_out = 1;
+    if ((e = launch_tango_agg(aa, L.agg, true, false, st)) != hipSuccess)
+      return hip_fail(e, "reversed aggregation (dg)");
+    if ((e = launch_tango_dqk(a, L.plan, st)) != hipSuccess) return hip_fail(e, "dq / dk kernels");
+    if ((e = launch_tango_bwd_finish(a, L.plan, st)) != hipSuccess) return hip_fail(e, "backward finish");
+    return ok();
+  });
+}
+
 int tango_stage_out(const tango_shape_t* shape, const void* w_o, const void* x, const void* gbar,
                     const void* v, void* out, void* hip_stream) {
   return guarded([&] {

@@ -60,7 +60,7 @@
 extern "C" {
 #endif
 
-#define TANGO_ABI_VERSION 4
+#define TANGO_ABI_VERSION 5
 
 typedef enum { TANGO_F32 = 0, TANGO_BF16 = 1 } tango_dtype_t;
 
@@ -265,6 +265,47 @@ int wango_stage_scan(const tango_shape_t* shape, int32_t window, int32_t chunk,
 int wango_stage_band(const tango_shape_t* shape, const float* theta, const float* null_bias,
                      int32_t window, int32_t chunk, const void* qh, const void* kh, const void* gp,
                      const float* n_old, const float* z_old, void* gbar, void* hip_stream);
+
+/* ---- Backward pass of the TANGO aggregation --------------------------------
+ *
+ * The pages train this block in bfloat16 ([TANGO] §3, training recipe); these
+ * two calls are the aggregation's part of a training step.  bfloat16 only
+ * (TANGO_ERR_UNSUPPORTED for float32).  Layouts as for the stage entry points.
+ *
+ * tango_aggregate_fwd_train: tango_stage_aggregate that also writes
+ *   den [B, Tp, H] float32: the denominator of the ratio of eq. 5 in units of
+ *   e^{-tau} (sum_{j<=i} e^{tau (q_i.k_j - 1)} + n_i e^{b - tau}), rows < T;
+ *   the backward pass reads it.  Same workspace as tango_stage_aggregate.
+ *
+ * tango_aggregate_bwd: given the forward's qh, kh, gp, gbar, den and the
+ *   incoming gradient dgbar ([B, Tp, d_gate] bf16; rows >= T ignored), writes
+ *   the gradients of sum(dgbar * gbar):
+ *     dq, dk [B, Tp, H*d_h] float32 with respect to the unit vectors qh, kh
+ *            as given (the normalisation and RoPE before them are the caller's
+ *            chain rule); rows >= T are written as zeros;
+ *     dg     [B, Tp, d_gate] bf16 with respect to the gates (not packed);
+ *            rows >= T are not written;
+ *     dtheta [H] float32 with respect to theta (zero where theta >= log 20,
+ *            the clip of eq. 4);
+ *     dnull  [H] float32 with respect to the null bias b of eq. 5 (NULL iff
+ *            null_bias is NULL).
+ *   Formulas: u_i = dgbar_i / den_i, delta_i = -u_i . gbar_i,
+ *   dg_j = sum_{i>=j} w_ij u_i, ds_ij = tau w_ij (u_i . g_j + delta_i),
+ *   dq_i = sum_j ds_ij k_j, dk_j = sum_i ds_ij q_i, dtheta = sum ds_ij s_ij,
+ *   dnull = sum_i delta_i n_i e^{b - tau}, with w_ij = e^{tau (s_ij - 1)}.
+ *   workspace: at least tango_aggregate_bwd_workspace_size(shape) bytes of
+ *   scratch (0 is returned for an invalid or unsupported shape).  The call
+ *   runs on hip_stream without synchronising; buffers must not overlap. */
+int tango_aggregate_fwd_train(const tango_shape_t* shape, const float* theta,
+                              const float* null_bias, const void* qh, const void* kh,
+                              const void* gp, void* gbar, float* den, void* workspace,
+                              size_t workspace_bytes, void* hip_stream);
+size_t tango_aggregate_bwd_workspace_size(const tango_shape_t* shape);
+int tango_aggregate_bwd(const tango_shape_t* shape, const float* theta, const float* null_bias,
+                        const void* qh, const void* kh, const void* gp, const void* gbar,
+                        const float* den, const void* dgbar, float* dq, float* dk, void* dg,
+                        float* dtheta, float* dnull, void* workspace, size_t workspace_bytes,
+                        void* hip_stream);
 
 #ifdef __cplusplus
 }

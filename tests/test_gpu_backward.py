@@ -1,0 +1,137 @@
+"""Parity of the TANGO aggregation backward pass (GPU, through the C ABI).
+
+The library's gradients of sum(dgbar * gbar) are compared with the float64
+oracle of ``oracle/backward_oracle.py`` (itself pinned by central differences
+of the forward oracle) on the same bf16 inputs.  The GPU side runs the forward
+that saves the denominators, then the backward.
+
+Tolerances.  Every intermediate the backward stores is bf16 (u = dgbar/den,
+the gates it reads, gbar and the exp weights of the forward, ds before the
+last products): 2^-9 of each value, the floor of the forward stages too.
+  * dq, dk, dg: rms(err)/rms(ref) <= 1e-2 (measured 2.6e-3 .. 4.2e-3 on these
+    cases).  max|err|/rms(ref) <= 0.3: the largest entries are 10-50 times the
+    rms (rows near the start of a sequence have small denominators, so large
+    u), each with a few 2^-9 roundings, so the largest errors reach
+    0.1-0.2 rms (measured up to 0.157 at T = 1000).
+  * dtheta = sum_ij ds_ij s_ij = sum_i q_i . dq_i is a sum whose terms nearly
+    cancel (the ds of destination i sum to u_i.num_i c_i/den_i), so its error
+    is measured against the size of its terms: |err| <= 1e-2 sum_i |q_i . dq_i|
+    (oracle values).  Redoing the oracle in float64 with the forward's weights,
+    gbar and u rounded to bf16 moves dtheta by up to 1.2% of its value on
+    these cases, far less of that scale.
+  * dnull: 5e-2 of the largest head's value (measured within 1%).
+"""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import oracle.backward_oracle as BW
+import oracle.tango_oracle as O
+from cross_token_gated_amd import api
+from tests import helpers as H
+from tests.gpu_common import announce, dev_f32, dev_tensor, host
+
+pytestmark = pytest.mark.gpu
+
+BARS = (1e-2, 0.3)
+THETA_BAR = 1e-2
+SCALAR_BAR = 5e-2
+
+CASES = [
+    dict(B=1, T=200, H=1, dh=128, Fh=256),
+    dict(B=2, T=300, H=2, dh=64, Fh=320),      # head width padded to 512 inside the backward
+    dict(B=1, T=257, H=4, dh=32, Fh=128),
+    dict(B=1, T=1000, H=1, dh=128, Fh=512),
+    dict(B=3, T=64, H=2, dh=64, Fh=64),
+]
+
+
+def _bf16(a):
+    return torch.from_numpy(np.asarray(a, dtype=np.float32)).to(torch.bfloat16).to(torch.float64).numpy()
+
+
+def _inputs(case, seed):
+    rng = np.random.default_rng(seed)
+    B, T, Hh, dh, Fh = case["B"], case["T"], case["H"], case["dh"], case["Fh"]
+    q = rng.standard_normal((B, T, Hh, dh))
+    k = rng.standard_normal((B, T, Hh, dh))
+    q = _bf16(q / np.linalg.norm(q, axis=-1, keepdims=True))
+    k = _bf16(k / np.linalg.norm(k, axis=-1, keepdims=True))
+    g = _bf16(rng.standard_normal((B, T, Hh * Fh)))
+    dgbar = _bf16(rng.standard_normal((B, T, Hh * Fh)))
+    theta = np.linspace(math.log(5.0), math.log(15.0), Hh).astype(np.float32)
+    nb = np.linspace(-1.0, 0.5, Hh).astype(np.float32)
+    return q, k, g, dgbar, theta, nb
+
+
+def _check(got, ref, what):
+    r, m = H.rms_ratio(got, ref), H.err_ratio(got, ref)
+    print(f"{what}: rms ratio {r:.2e} (bar {BARS[0]:.0e}), max ratio {m:.2e} (bar {BARS[1]:.0e})")
+    assert r <= BARS[0] and m <= BARS[1], (what, r, m)
+
+
+@pytest.mark.parametrize("case", CASES, ids=lambda c: f"B{c['B']}-T{c['T']}-H{c['H']}-dh{c['dh']}-Fh{c['Fh']}")
+@pytest.mark.parametrize("null", [False, True])
+def test_aggregate_backward(case, null):
+    B, T, Hh, dh, Fh = case["B"], case["T"], case["H"], case["dh"], case["Fh"]
+    F, HD, Tp = Hh * Fh, Hh * dh, H.padded_len(T)
+    M = B * Tp
+    q, k, g, dgbar, theta, nb = _inputs(case, 11 + T)
+    nb = nb if null else None
+    shape = api.make_shape(B, T, 128, F, Hh, dh, torch.bfloat16)
+    qd = dev_tensor(H.pad_rows(q.reshape(B, T, HD), Tp), "bf16")
+    kd = dev_tensor(H.pad_rows(k.reshape(B, T, HD), Tp), "bf16")
+    gp = dev_tensor(H.pack_gates(H.pad_rows(g, Tp)).reshape(-1), "bf16")
+    th = dev_f32(theta)
+    nbd = None if nb is None else dev_f32(nb)
+    # the incoming gradient's padded rows hold garbage: they must be ignored
+    dg_rows = H.pad_rows(dgbar, Tp).reshape(B, Tp, F)
+    dg_rows[:, T:] = 7.0
+    dgd = dev_tensor(dg_rows.reshape(M, F), "bf16")
+    gbar = torch.full((M, F), float("nan"), dtype=torch.bfloat16, device="cuda:0")
+    den = torch.full((M, Hh), float("nan"), dtype=torch.float32, device="cuda:0")
+    wsf = api.workspace(api.tango_workspace_size(shape), "cuda:0")
+    announce(f"aggregate_backward {case} null={null}")
+    api.tango_aggregate_fwd_train(shape, th, nbd, qd, kd, gp, gbar, den, wsf)
+    dq = torch.full((M, HD), float("nan"), dtype=torch.float32, device="cuda:0")
+    dk = torch.full((M, HD), float("nan"), dtype=torch.float32, device="cuda:0")
+    dgo = torch.full((M, F), float("nan"), dtype=torch.bfloat16, device="cuda:0")
+    dth = torch.full((Hh,), float("nan"), dtype=torch.float32, device="cuda:0")
+    dnl = None if nb is None else torch.full((Hh,), float("nan"), dtype=torch.float32, device="cuda:0")
+    wsb = api.workspace(api.tango_aggregate_bwd_workspace_size(shape), "cuda:0")
+    wsb.fill_(0xFF)   # scratch contents must not matter
+    api.tango_aggregate_bwd(shape, th, nbd, qd, kd, gp, gbar, den, dgd, dq, dk, dgo, dth, dnl, wsb)
+    torch.cuda.synchronize()
+
+    refs = [BW.tango_aggregate_backward(q[b], k[b], g[b], theta, nb, dgbar[b]) for b in range(B)]
+    dq_ref = np.stack([r[0].reshape(T, HD) for r in refs])
+    dk_ref = np.stack([r[1].reshape(T, HD) for r in refs])
+    dg_ref = np.stack([r[2] for r in refs])
+    _check(H.unpad_rows(host(dq), B, T), dq_ref, "dq")
+    _check(H.unpad_rows(host(dk), B, T), dk_ref, "dk")
+    _check(H.unpad_rows(host(dgo), B, T), dg_ref, "dg")
+    assert np.all(host(dq).reshape(B, Tp, HD)[:, T:] == 0)
+    assert np.all(host(dk).reshape(B, Tp, HD)[:, T:] == 0)
+    dth_ref = sum(r[3] for r in refs)
+    print("dtheta", host(dth), dth_ref, "dnull", None if dnl is None else host(dnl),
+          None if nb is None else sum(r[4] for r in refs))
+    # scale of the sum: sum_i |q_i . dq_i| per head (oracle values)
+    scale = np.abs(np.einsum("bthe,bthe->bth", q, dq_ref.reshape(B, T, Hh, dh))).sum(axis=(0, 1))
+    err = np.abs(host(dth) - dth_ref)
+    print("dtheta error / scale", err / scale)
+    assert np.all(err <= THETA_BAR * scale), (err, scale)
+    if nb is not None:
+        dnl_ref = sum(r[4] for r in refs)
+        np.testing.assert_allclose(host(dnl), dnl_ref, rtol=SCALAR_BAR,
+                                   atol=SCALAR_BAR * np.abs(dnl_ref).max())
+    # the saved denominators, in e^{-tau} units
+    tau = O.temperature(theta)
+    den_ref = np.stack([BW.aggregate_denominators(q[b], k[b], theta, nb) for b in range(B)]) * np.exp(-tau)
+    np.testing.assert_allclose(H.unpad_rows(host(den), B, T), den_ref, rtol=1e-2)
+
+
+def test_aggregate_backward_rejects_float32():
+    shape = api.make_shape(1, 64, 128, 256, 1, 128, torch.float32)
+    assert api.tango_aggregate_bwd_workspace_size(shape) == 0

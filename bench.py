@@ -1,6 +1,7 @@
 """Benchmark of the TANGO / WANGO block forward on one MI355X.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline] [--no-decode] [--no-pages]
+                    [--no-backward]
 
 One step runs every part of the block forward once at T = 8192 tokens:
   * TANGO, bf16 compute, B = 1, T = 8192, d = 512, F = 2048, q/k width 128,
@@ -33,6 +34,10 @@ Alongside, with HIP events on the launch stream:
     own geometry at T = 8192 (16 heads of 32, F = 28,480, window and block
     64), with the block's operation count as the pages tally it (Table 5
     without the vocabulary projection) per second;
+  * backward: the TANGO aggregation's backward pass at the same T = 8192
+    shape (dq, dk, dg, dtheta from dgbar; the forward that saves the
+    denominators runs once, untimed), with its algorithmic flops
+    2 * pairs * (2 F + 3 * q/k width) per second against 2.5 PFLOP/s;
   * cpu_baseline: the float64 CPU oracle on a bounded sample of the same work
     (one of the four TANGO applications, scaled by 4, plus the WANGO block).
 The "traffic" of the two rooflines is the HBM traffic per launch measured by
@@ -70,6 +75,7 @@ def parse():
                     help="launches per roofline measurement (default: --steps)")
     ap.add_argument("--no-decode", action="store_true", help="skip the decode-step measurement")
     ap.add_argument("--no-pages", action="store_true", help="skip the pages'-geometry forward")
+    ap.add_argument("--no-backward", action="store_true", help="skip the aggregation backward")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a plain 256 MiB device copy (for counter calibration)")
     return ap.parse_args()
@@ -238,6 +244,75 @@ def pages_bench(steps: int, warmup: int, dev, stream) -> dict:
               f"count", file=sys.stderr, flush=True)
         del ws, x, ping, pong
         torch.cuda.empty_cache()
+    return out
+
+
+def backward_bench(steps: int, warmup: int, dev, stream) -> dict:
+    """Backward pass of the TANGO aggregation at the T = 8192 bench shape (one
+    head of 128, F = 2048, bf16): the forward that saves the denominators is
+    run once; the backward (all its kernels) is timed, median of `steps`."""
+    import numpy as np
+    import torch
+
+    from cross_token_gated_amd import api
+    from tests import helpers as H
+
+    T, F, Hh, dh = 8192, 2048, 1, 128
+    Tp = H.padded_len(T)
+    rng = np.random.default_rng(5)
+    q = rng.standard_normal((Tp, Hh * dh)).astype(np.float32)
+    k = rng.standard_normal((Tp, Hh * dh)).astype(np.float32)
+    q /= np.linalg.norm(q, axis=-1, keepdims=True)
+    k /= np.linalg.norm(k, axis=-1, keepdims=True)
+    q[T:] = 0
+    k[T:] = 0
+    g = rng.standard_normal((Tp, F)).astype(np.float32)
+    g[T:] = 0
+    bf = torch.bfloat16
+    qd = torch.from_numpy(q).to(dev).to(bf)
+    kd = torch.from_numpy(k).to(dev).to(bf)
+    gp = torch.from_numpy(H.pack_gates(g)).to(dev).to(bf).reshape(-1)
+    dgbar = torch.from_numpy(rng.standard_normal((Tp, F)).astype(np.float32)).to(dev).to(bf)
+    theta = torch.full((Hh,), math.log(10.0), dtype=torch.float32, device=dev)
+    shape = api.make_shape(1, T, 512, F, Hh, dh, bf)
+    gbar = torch.empty((Tp, F), dtype=bf, device=dev)
+    den = torch.empty((Tp, Hh), dtype=torch.float32, device=dev)
+    wsf = api.workspace(api.tango_workspace_size(shape), dev)
+    api.tango_aggregate_fwd_train(shape, theta, None, qd, kd, gp, gbar, den, wsf, stream=stream)
+    dq = torch.empty((Tp, Hh * dh), dtype=torch.float32, device=dev)
+    dk = torch.empty_like(dq)
+    dg = torch.empty((Tp, F), dtype=bf, device=dev)
+    dth = torch.empty((Hh,), dtype=torch.float32, device=dev)
+    wsb = api.workspace(api.tango_aggregate_bwd_workspace_size(shape), dev)
+
+    def bwd():
+        api.tango_aggregate_bwd(shape, theta, None, qd, kd, gp, gbar, den, dgbar, dq, dk, dg, dth, None, wsb,
+                                stream=stream)
+
+    for _ in range(warmup):
+        bwd()
+    torch.cuda.synchronize()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+    for a, b in ev:
+        a.record(stream)
+        bwd()
+        b.record(stream)
+    torch.cuda.synchronize()
+    t = sorted(a.elapsed_time(b) for a, b in ev)
+    ms = t[steps // 2] if steps % 2 else 0.5 * (t[steps // 2 - 1] + t[steps // 2])
+    pairs = T * (T + 1) / 2
+    # algorithmic work of the gradients: dg and u.g over F per pair, s, dq, dk over d_h
+    flops = 2.0 * pairs * Hh * (2 * F // Hh + 3 * dh)
+    achieved = flops / (ms * 1e-3)
+    out = {"workload": "tango_aggregate_bwd_bf16_t8192_f2048_h1", "ms_per_backward": ms,
+           "tokens_per_s": T / (ms * 1e-3),
+           "roofline": {"kernel": "whole aggregation backward (prep, reversed aggregation, dq, dk, finish)",
+                        "bound": "mfma", "achieved": achieved / 1e12, "peak": PEAK_BF16_FLOPS / 1e12,
+                        "unit": "TFLOP/s", "frac": achieved / PEAK_BF16_FLOPS, "flops_per_backward": flops}}
+    print(f"[bench] backward tango_aggregate_bwd T=8192 F=2048: {ms:.3f} ms, {achieved / 1e12:.0f} TFLOP/s "
+          f"({achieved / PEAK_BF16_FLOPS * 100:.1f}% of bf16 peak)", file=sys.stderr, flush=True)
+    del wsf, wsb
+    torch.cuda.empty_cache()
     return out
 
 
@@ -522,6 +597,8 @@ def main():
         result["decode"] = decode_bench(loops, min(args.warmup, 3), dev, stream)
     if not args.no_pages:
         result["pages_geometry"] = pages_bench(min(loops, 5), 1, dev, stream)
+    if not args.no_backward:
+        result["backward"] = backward_bench(loops, min(args.warmup, 3), dev, stream)
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(wt, wg)
     print(json.dumps(result), flush=True)

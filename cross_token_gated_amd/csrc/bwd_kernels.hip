@@ -174,6 +174,7 @@ template <int DH> struct BwdLds {
   __bf16 t2[2][T2];
   __bf16 t3[2][T3];
   __bf16 ds[kBwdWaves][16 * kStep];                // wave-private ds^T (own block x 64 other), region layout
+  float dl[2][kStep];                              // DIR 1: delta of the staged destinations
   float red[kBwdWaves];
 };
 
@@ -220,7 +221,9 @@ __global__ __launch_bounds__(kBwdThreads) void dqk_kernel(BwdArgs a, int rtiles,
   const float* delta = a.delta + (int64_t)h * a.B * a.Tp + mseq;
 
   // staging: other rows [o0, o0 + 64) of this sequence into buffer `buf`
-  auto fetch = [&](int o0, u32x4 (&r1)[P1], u32x4 (&r2)[P2], u32x4 (&r3)[P3]) {
+  auto fetch = [&](int o0, u32x4 (&r1)[P1], u32x4 (&r2)[P2], u32x4 (&r3)[P3], f32x4& rd) {
+    // DIR 1: delta of the 64 destinations (every wave loads, wave 0 stores)
+    if (DIR == 1) rd = *reinterpret_cast<const f32x4*>(delta + o0 + (lane & 15) * 4);
 #pragma unroll
     for (int q = 0; q < P1; ++q) {
       const int cc = (wave + kBwdWaves * q) % C1;
@@ -243,7 +246,9 @@ __global__ __launch_bounds__(kBwdThreads) void dqk_kernel(BwdArgs a, int rtiles,
           oth_pk + packed_offset((mseq + o0) / 32 + hf, lg, (int64_t)h * DH + db * 16 + li, HD));
     }
   };
-  auto stash = [&](int buf, const u32x4 (&r1)[P1], const u32x4 (&r2)[P2], const u32x4 (&r3)[P3]) {
+  auto stash = [&](int buf, const u32x4 (&r1)[P1], const u32x4 (&r2)[P2], const u32x4 (&r3)[P3],
+                   const f32x4& rd) {
+    if (DIR == 1 && wave == 0 && lane < 16) *reinterpret_cast<f32x4*>(&sm.dl[buf][lane * 4]) = rd;
 #pragma unroll
     for (int q = 0; q < P1; ++q) {
       if (C1 % kBwdWaves != 0 && wave + kBwdWaves * q >= C1) break;   // wave-uniform
@@ -298,44 +303,52 @@ __global__ __launch_bounds__(kBwdThreads) void dqk_kernel(BwdArgs a, int rtiles,
     {
       __syncthreads();   // the previous job's last stash is done with the buffers
       u32x4 r1[P1], r2[P2], r3[P3];
-      fetch(s_first * kStep, r1, r2, r3);
-      stash(0, r1, r2, r3);
+      f32x4 rd = {0.f, 0.f, 0.f, 0.f};
+      fetch(s_first * kStep, r1, r2, r3, rd);
+      stash(0, r1, r2, r3, rd);
       if (s_first + 1 <= s_last) {
-        fetch((s_first + 1) * kStep, r1, r2, r3);
-        stash(1, r1, r2, r3);
+        fetch((s_first + 1) * kStep, r1, r2, r3, rd);
+        stash(1, r1, r2, r3, rd);
       }
       __syncthreads();
     }
     for (int st = s_first; st <= s_last; ++st) {
       const int buf = (st - s_first) & 1;
       const int o0 = st * kStep;
-      // DIR 1: delta of the step's destinations (loaded in every chunk, used
-      // in chunk 0; issued before the staging loads so its wait stays short)
-      f32x4 dls[4];
-#pragma unroll
-      for (int t = 0; t < 4; ++t)
-        dls[t] = DIR == 1 ? *reinterpret_cast<const f32x4*>(delta + o0 + t * 16 + lg * 4) : f32x4{0.f, 0.f, 0.f, 0.f};
       u32x4 r1[P1], r2[P2], r3[P3];
-      fetch(min(st + 2, s_last) * kStep, r1, r2, r3);   // past the end: re-read the last step
+      f32x4 rd = {0.f, 0.f, 0.f, 0.f};
+      fetch(min(st + 2, s_last) * kStep, r1, r2, r3, rd);   // past the end: re-read the last step
       unsigned char* dsb = reinterpret_cast<unsigned char*>(sm.ds[wave]);
+      // S and dW of the four other blocks t side by side, k block by k block:
+      // four independent accumulation chains in the MFMA pipeline
+      f32x4 sacc[4], wacc[4];
+#pragma unroll
+      for (int t = 0; t < 4; ++t) {
+        sacc[t] = f32x4{-1.f, -1.f, -1.f, -1.f};
+        wacc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+      }
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks)
+#pragma unroll
+        for (int t = 0; t < 4; ++t) mma(sacc[t], region_frag(sm.t1[buf], KS, t, ks), bq[ks]);
+#pragma unroll
+      for (int kf = 0; kf < kChunkKB; ++kf)
+#pragma unroll
+        for (int t = 0; t < 4; ++t) mma(wacc[t], region_frag(sm.t2[buf], kChunkKB, t, kf), bu[kf]);
 #pragma unroll
       for (int t = 0; t < 4; ++t) {                    // other block t of the step
-        f32x4 sacc = {-1.f, -1.f, -1.f, -1.f}, wacc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int ks = 0; ks < KS; ++ks) mma(sacc, region_frag(sm.t1[buf], KS, t, ks), bq[ks]);
-#pragma unroll
-        for (int kf = 0; kf < kChunkKB; ++kf) mma(wacc, region_frag(sm.t2[buf], kChunkKB, t, kf), bu[kf]);
         float dsv[4];
-        const f32x4 dl = dls[t];
+        const f32x4 dl = DIR == 1 ? *reinterpret_cast<const f32x4*>(&sm.dl[buf][t * 16 + lg * 4])
+                                  : f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
           const int other = o0 + t * 16 + lg * 4 + r;
           const bool valid = DIR == 0 ? other <= own_row : own_row <= other;   // source <= destination
           const float dlt = first_chunk ? (DIR == 0 ? delta_own : dl[r]) : 0.f;
-          const float w = __builtin_amdgcn_exp2f(ktau * sacc[r]);
-          const float v = valid ? tau * w * (wacc[r] + dlt) : 0.f;
+          const float w = __builtin_amdgcn_exp2f(ktau * sacc[t][r]);
+          const float v = valid ? tau * w * (wacc[t][r] + dlt) : 0.f;
           dsv[r] = v;
-          if (DIR == 0) dtheta_part += v * (sacc[r] + 1.0f);
+          if (DIR == 0) dtheta_part += v * (sacc[t][r] + 1.0f);
         }
         // ds^T of block t: rows 4 lg + r of the block are slots r (t even) or
         // 4 + r (t odd) of this lane's fragment for the half t / 2
@@ -356,7 +369,7 @@ __global__ __launch_bounds__(kBwdThreads) void dqk_kernel(BwdArgs a, int rtiles,
         }
       }
       __syncthreads();   // every wave is done with buffer buf; buf ^ 1 (stashed a step ago) is visible
-      stash(buf, r1, r2, r3);
+      stash(buf, r1, r2, r3, rd);
     }
     // out^T block db: lane holds own row li, d_h columns 16 db + 4 lg + r
     float* dst = (DIR == 0 ? a.part_q : a.part_k) + ((int64_t)c * a.B * a.Tp + mseq + own_row) * HD + h * DH;

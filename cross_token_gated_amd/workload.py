@@ -101,6 +101,72 @@ DECODE_WORKLOADS = {
 }
 
 
+def three_set_schedule(n_apps: int) -> tuple:
+    """Set index of each application in the three-set model of "TANGO: Treating
+    Tokens as Operators" (abstract; Table 2): set 0 for the first application,
+    set 2 for the last and set 1 for every one between (one application uses
+    set 0 alone; two use sets 0 and 2)."""
+    if n_apps < 1:
+        raise ValueError("n_apps must be >= 1")
+    if n_apps == 1:
+        return (0,)
+    return (0,) + (1,) * (n_apps - 2) + (2,)
+
+
+@dataclass(frozen=True)
+class StackWorkload:
+    """A TANGO stack with several gated-projection sets: ``base`` gives the
+    shared sizes (its d_gate is unused), ``widths`` the gate width F of each
+    set and ``schedule`` the set of each application."""
+    name: str
+    base: Workload
+    widths: tuple
+    schedule: tuple
+
+    def set_workload(self, k: int) -> Workload:
+        return replace(self.base, d_gate=self.widths[k], repeats=1)
+
+    @property
+    def tokens(self) -> int:
+        return self.base.tokens
+
+
+# The three-set model at the T = 8192 TANGO geometry above, stacked 8 deep as in
+# the later revision's Table 2 (depth 8): three gated-projection sets whose
+# widths add up to the one-set model's F = 2048 (the sets hold the same number
+# of W_g / W_v / W_o parameters as the one-set block; widths are multiples of 64).
+STACK_WORKLOADS = {
+    "tango_3set_bf16_t8192_r8": StackWorkload(
+        "tango_3set_bf16_t8192_r8",
+        Workload("tango_3set_bf16_t8192_r8", "tango", "bf16", 1, 8192, 512, 704, 1, 128, seed=10,
+                 io_dtype="f32"),
+        (704, 640, 704), three_set_schedule(8)),
+}
+
+
+def make_stack_inputs(sw: StackWorkload, seed: Optional[int] = None) -> list:
+    """Inputs of every set of a stack workload, as a list of Inputs.  Drawn in
+    the order h, W_q, W_k, then W_g, W_v, W_o of set 0, 1, ...; every set shares
+    h, W_q, W_k, theta and the null bias (the same arrays), and has its own
+    W_g, W_v [F_k, d] and W_o [d, F_k] (scales as in make_inputs)."""
+    w = sw.base
+    rng = np.random.Generator(np.random.PCG64(w.seed if seed is None else seed))
+    d, hd = w.d_model, w.n_heads * w.head_dim
+    q = lambda a: quantize(a, w.dtype)  # noqa: E731
+    h = q(rng.standard_normal((w.B, w.T, d)))
+    w_q = q(rng.standard_normal((hd, d)) / math.sqrt(d))
+    w_k = q(rng.standard_normal((hd, d)) / math.sqrt(d))
+    theta = np.full(w.n_heads, w.theta, dtype=np.float32)
+    nb = None if w.null_bias is None else np.full(w.n_heads, w.null_bias, dtype=np.float32)
+    out = []
+    for F in sw.widths:
+        w_g = q(rng.standard_normal((F, d)) / math.sqrt(d))
+        w_v = q(rng.standard_normal((F, d)) / math.sqrt(d))
+        w_o = q(rng.standard_normal((d, F)) / math.sqrt(F))
+        out.append(Inputs(h, w_g, w_v, w_q, w_k, w_o, None, theta, nb))
+    return out
+
+
 def round_f32(a: np.ndarray) -> np.ndarray:
     """float64 -> float32 (round to nearest even)."""
     return np.asarray(a, dtype=np.float32)

@@ -411,6 +411,23 @@ def block_stack(h: np.ndarray, p: BlockParams, cfg: BlockConfig, repeats: int = 
     return cur
 
 
+def block_stack_sets(h: np.ndarray, sets: list, cfg: BlockConfig, schedule,
+                     io_dtype: str = "bf16") -> np.ndarray:
+    """h [B, T, d] -> output of a stack whose application r uses parameter set
+    ``sets[schedule[r]]`` (the three-set model of "TANGO: Treating Tokens as
+    Operators", abstract and Table 2, gives the first, the middle and the last
+    applications their own gated-projection set).  Each application is one
+    block of [TANGO] §2.1; the stream is rounded to the I/O dtype between
+    applications as in :func:`block_stack`."""
+    cur = np.asarray(h, dtype=np.float64)
+    n = len(schedule)
+    for r, k in enumerate(schedule):
+        p = sets[k]
+        nxt = np.stack([block_sequence(cur[b], p, cfg) for b in range(cur.shape[0])])
+        cur = nxt if r == n - 1 else round_to_dtype(nxt, io_dtype)
+    return cur
+
+
 # --------------------------------------------------------------------------
 # Brute force: pure-Python loops over the sums of eq. 5, for tiny sizes
 # --------------------------------------------------------------------------

@@ -7,6 +7,7 @@ import pytest
 
 import oracle.tango_oracle as O
 import tests.test_oracle_pins as P
+import tests.test_stack_oracle as SP
 
 
 def _pins():
@@ -25,6 +26,7 @@ def _pins():
         P.test_wango_scan_form_equals_direct_form,
         P.test_rope_is_a_rotation_with_relative_logits,
         P.test_counts_reproduce_tables,
+        lambda: SP.test_stack_sets_equal_brute_force_composition(True),
     ]
 
 
@@ -92,6 +94,13 @@ def _counts_no_scan(T, d, F, H, dh, vocab, repeats, mode, window=0):
     return repeats * (linear + pairs) + T * d * vocab
 
 
+_orig_stack_sets = O.block_stack_sets
+
+
+def _stack_sets_one_late(h, sets, cfg, schedule, io_dtype="bf16"):
+    return _orig_stack_sets(h, sets, cfg, (schedule[0],) + tuple(schedule[:-1]), io_dtype)
+
+
 MUTATIONS = {
     "phi drops epsilon": ("phi", lambda u, dh: _phi_no_eps(u, dh)),
     "ELU alpha 2": ("elu", _elu_alpha2),
@@ -103,6 +112,7 @@ MUTATIONS = {
     "temperature not clipped": ("temperature", _tau_unclipped),
     "blocked running sums one step late": ("wango_old_blocked", _blocked_shifted),
     "MAC count drops the running-sum term": ("forward_macs", _counts_no_scan),
+    "stack applies each set one application late": ("block_stack_sets", _stack_sets_one_late),
 }
 
 

@@ -1,7 +1,7 @@
 """Benchmark of the TANGO / WANGO block forward on one MI355X.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline] [--no-decode] [--no-pages]
-                    [--no-backward]
+                    [--no-backward] [--no-three-set]
 
 One step runs every part of the block forward once at T = 8192 tokens:
   * TANGO, bf16 compute, B = 1, T = 8192, d = 512, F = 2048, q/k width 128,
@@ -34,6 +34,10 @@ Alongside, with HIP events on the launch stream:
     own geometry at T = 8192 (16 heads of 32, F = 28,480, window and block
     64), with the block's operation count as the pages tally it (Table 5
     without the vocabulary projection) per second;
+  * three_set: the TANGO stack with three gated-projection sets (widths 704,
+    640 and 704 for the first, middle and last of 8 applications) through the
+    single call tango_stack_fwd, as tokens per second and per-application
+    speed against the one-set block (F = 2048);
   * backward: the TANGO aggregation's backward pass at the same T = 8192
     shape (dq, dk, dg, dtheta from dgbar; the forward that saves the
     denominators runs once, untimed), with its algorithmic flops
@@ -76,6 +80,7 @@ def parse():
     ap.add_argument("--no-decode", action="store_true", help="skip the decode-step measurement")
     ap.add_argument("--no-pages", action="store_true", help="skip the pages'-geometry forward")
     ap.add_argument("--no-backward", action="store_true", help="skip the aggregation backward")
+    ap.add_argument("--no-three-set", action="store_true", help="skip the three-set stack")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a plain 256 MiB device copy (for counter calibration)")
     return ap.parse_args()
@@ -243,6 +248,56 @@ def pages_bench(steps: int, warmup: int, dev, stream) -> dict:
               f"{w.tokens / (ms * 1e-3):.0f} tokens/s, {macs / (ms * 1e-3) / 1e12:.0f} T MAC/s of the pages' "
               f"count", file=sys.stderr, flush=True)
         del ws, x, ping, pong
+        torch.cuda.empty_cache()
+    return out
+
+
+def three_set_bench(steps: int, warmup: int, dev, stream, ms_one_set_app: float) -> dict:
+    """The three-set TANGO stack at T = 8192 (eight applications; gate widths
+    704, 640, 704 for the first, middle and last applications) through the one
+    C call tango_stack_fwd, against the one-set block (F = 2048) per
+    application."""
+    import torch
+
+    from cross_token_gated_amd import api
+    from cross_token_gated_amd import workload as wl
+    from tests.gpu_common import block_weights, dev_tensor
+
+    out = {}
+    for name, sw in wl.STACK_WORKLOADS.items():
+        inps = wl.make_stack_inputs(sw)
+        sets = [block_weights(sw.set_workload(k), inps[k], dev) for k in range(len(sw.widths))]
+        w = sw.base
+        x = dev_tensor(inps[0].h, w.io, dev)
+        y = torch.empty_like(x)
+        shapes = [api.shape_of(x, b, w.rope_base, w.rms_eps) for b in sets]
+        ws = api.workspace(api.tango_stack_workspace_size(shapes), dev)
+
+        def fwd():
+            api.tango_stack_fwd(x, sets, sw.schedule, out=y, ws=ws, rope_base=w.rope_base,
+                                rms_eps=w.rms_eps, stream=stream)
+
+        for _ in range(warmup):
+            fwd()
+        torch.cuda.synchronize()
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+              for _ in range(steps)]
+        for a, b in ev:
+            a.record(stream)
+            fwd()
+            b.record(stream)
+        torch.cuda.synchronize()
+        t = sorted(a.elapsed_time(b) for a, b in ev)
+        ms = t[steps // 2] if steps % 2 else 0.5 * (t[steps // 2 - 1] + t[steps // 2])
+        n = len(sw.schedule)
+        out[name] = {"ms_per_forward": ms, "tokens_per_s": sw.tokens / (ms * 1e-3), "applications": n,
+                     "widths": list(sw.widths), "schedule": list(sw.schedule),
+                     "ms_per_application": ms / n,
+                     "speedup_per_application_vs_one_set_f2048": ms_one_set_app / (ms / n)}
+        print(f"[bench] three-set stack {name}: {ms:.3f} ms per forward ({n} applications), "
+              f"{sw.tokens / (ms * 1e-3):.0f} tokens/s, {ms_one_set_app / (ms / n):.2f}x the one-set "
+              f"block per application", file=sys.stderr, flush=True)
+        del ws, x, y
         torch.cuda.empty_cache()
     return out
 
@@ -597,6 +652,8 @@ def main():
         result["decode"] = decode_bench(loops, min(args.warmup, 3), dev, stream)
     if not args.no_pages:
         result["pages_geometry"] = pages_bench(min(loops, 5), 1, dev, stream)
+    if not args.no_three_set:
+        result["three_set"] = three_set_bench(min(loops, 10), 1, dev, stream, ms_tango / wt.repeats)
     if not args.no_backward:
         result["backward"] = backward_bench(loops, min(args.warmup, 3), dev, stream)
     if not args.no_cpu_baseline:

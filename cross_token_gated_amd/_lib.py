@@ -26,6 +26,7 @@ EXPORTS = [
     "tango_decode_state_size", "tango_decode_workspace_size", "tango_decode_step",
     "wango_decode_state_size", "wango_decode_workspace_size", "wango_decode_step",
     "tango_aggregate_fwd_train", "tango_aggregate_bwd_workspace_size", "tango_aggregate_bwd",
+    "tango_stack_workspace_size", "tango_stack_fwd",
 ]
 
 
@@ -87,6 +88,8 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
         "wango_decode_step": (ctypes.c_int, [S, W, i32, i32, vp, vp, vp, vp, sz, vp, sz, vp]),
         "tango_aggregate_fwd_train": (ctypes.c_int, [S, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]),
         "tango_aggregate_bwd_workspace_size": (sz, [S]),
+        "tango_stack_workspace_size": (sz, [S, i32]),
+        "tango_stack_fwd": (ctypes.c_int, [S, W, i32, vp, i32, vp, vp, vp, sz, vp]),
         "tango_aggregate_bwd": (ctypes.c_int, [S, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz,
                                                vp]),
     }

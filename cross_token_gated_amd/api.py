@@ -106,6 +106,30 @@ def tango_block_fwd(x: torch.Tensor, w: BlockWeights, out: Optional[torch.Tensor
     return out
 
 
+def tango_stack_workspace_size(shapes) -> int:
+    arr = (Shape * len(shapes))(*shapes)
+    return int(load().tango_stack_workspace_size(arr, len(shapes)))
+
+
+def tango_stack_fwd(x: torch.Tensor, sets, schedule, out: Optional[torch.Tensor] = None,
+                    ws: Optional[torch.Tensor] = None, rope_base: float = 10000.0,
+                    rms_eps: float = 1e-6, stream=None) -> torch.Tensor:
+    """TANGO blocks with several parameter sets: application r uses
+    ``sets[schedule[r]]`` (a list of BlockWeights).  Returns out[B, T, d]
+    (out may be x for in place)."""
+    shapes = [shape_of(x, w, rope_base, rms_eps) for w in sets]
+    if out is None:
+        out = torch.empty_like(x)
+    if ws is None:
+        ws = workspace(tango_stack_workspace_size(shapes), x.device)
+    sh = (Shape * len(shapes))(*shapes)
+    cw = (Weights * len(sets))(*[w.c_struct() for w in sets])
+    sched = (ctypes.c_int32 * len(schedule))(*[int(k) for k in schedule])
+    check(load().tango_stack_fwd(sh, cw, len(sets), sched, len(schedule), _ptr(x), _ptr(out), _ptr(ws),
+                                 ws.numel(), _stream(stream)))
+    return out
+
+
 def wango_block_fwd(x: torch.Tensor, w: BlockWeights, window: int, phi_dim: int, chunk: int,
                     out: Optional[torch.Tensor] = None, ws: Optional[torch.Tensor] = None,
                     rope_base: float = 10000.0, rms_eps: float = 1e-6, stream=None) -> torch.Tensor:

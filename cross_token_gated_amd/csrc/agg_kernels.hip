@@ -53,6 +53,8 @@ template <> struct AggCfg<bf16> { static constexpr int BR = 128, WIDE = 64; };
 template <> struct AggCfg<float> { static constexpr int BR = 64, WIDE = 32; };
 constexpr int kNarrow = 16;
 constexpr int kMid = 32;
+constexpr int kShortBR = 64;       // bf16 TANGO tiles of 64 rows, for grids that would underfill
+constexpr int kFillItems = 256;    // work items that fill the 256 compute units once
 
 constexpr int kWaves = 8;                 // two waves per SIMD
 constexpr int BC = 64;                    // sources per step
@@ -81,8 +83,7 @@ __device__ __forceinline__ int region_pos(int region, int r, int g) {
   return region * 256 + (r ^ g) * 16;
 }
 
-template <typename T, int DH> struct AggLds {
-  static constexpr int BR = AggCfg<T>::BR;
+template <typename T, int DH, int BR> struct AggLds {
   T ks[2][BC * DH];   // key blocks, region layout (16-source block jj, k block, chunk, group)
   T ps[2][BR * BC];   // weights, region layout (16-destination block, 32-source half, chunk, group)
   float den[kWaves][BR];
@@ -98,16 +99,15 @@ __device__ __forceinline__ int64_t part_index(int blk, int r, int lane) {
   return ((int64_t)blk * 4 + r) * 64 + lane;
 }
 
-template <typename T, int MODE, int DH, int WCOLS>
+template <typename T, int MODE, int DH, int WCOLS, int BR>
 __global__ __launch_bounds__(kAggThreads) void agg_kernel(AggArgs a, int nfc, int rtiles,
                                                           int64_t items) {
-  constexpr int BR = AggCfg<T>::BR;
   constexpr int FS = kWaves * WCOLS, NFB = WCOLS / 16, NIB = BR / 16;
   constexpr int JBW = NIB * (BC / 16) / kWaves;  // S^T source blocks per wave (one dest block)
   constexpr int NSPLIT = kWaves / NIB;           // waves sharing one destination block
   constexpr int KS = DH / 32;
   constexpr int SPT = BR / BC;                    // source steps per destination tile
-  using L = AggLds<T, DH>;
+  using L = AggLds<T, DH, BR>;
   constexpr int PE = 16 / (int)sizeof(T);        // elements per 16-byte piece
   constexpr int PPF = frag_chunks<T>();
   constexpr int KCH = (BC / 16) * KS * PPF;       // 64-piece chunks of a key block
@@ -498,49 +498,88 @@ __global__ void zero_i32_kernel(int* p, int64_t n) {
   if (i < n) p[i] = 0;
 }
 
-template <typename T, int MODE, int WC>
+template <typename T, int MODE, int WC, int BR>
 hipError_t launch_agg_w(const AggArgs& a, int nfc, int rtiles, int64_t items, hipStream_t s) {
   const int64_t q8 = ceil_div(items, 8);
   dim3 grid((unsigned)(8 * q8)), block(kAggThreads);
   switch (a.dh) {
-    case 32: hipLaunchKernelGGL((agg_kernel<T, MODE, 32, WC>), grid, block, 0, s, a, nfc, rtiles, items); break;
-    case 64: hipLaunchKernelGGL((agg_kernel<T, MODE, 64, WC>), grid, block, 0, s, a, nfc, rtiles, items); break;
-    case 128: hipLaunchKernelGGL((agg_kernel<T, MODE, 128, WC>), grid, block, 0, s, a, nfc, rtiles, items); break;
+    case 32: hipLaunchKernelGGL((agg_kernel<T, MODE, 32, WC, BR>), grid, block, 0, s, a, nfc, rtiles, items); break;
+    case 64: hipLaunchKernelGGL((agg_kernel<T, MODE, 64, WC, BR>), grid, block, 0, s, a, nfc, rtiles, items); break;
+    case 128: hipLaunchKernelGGL((agg_kernel<T, MODE, 128, WC, BR>), grid, block, 0, s, a, nfc, rtiles, items); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
 }
 
-template <typename T> int agg_wcols(int Fh) {
-  if (Fh % (kWaves * AggCfg<T>::WIDE) == 0) return AggCfg<T>::WIDE;
-  if (Fh % (kWaves * kMid) == 0) return kMid;
-  return kNarrow;
+// Gate columns per wave for a head width Fh (padded to a multiple of 64) and
+// query/key width dh.  Each of the ceil(Fh / (kWaves wc)) column chunks of a
+// destination tile recomputes the scores and weights, and a chunk costs the
+// same whether or not every wave has columns (the waves past the width
+// multiply copies), so the choice weighs the chunk count against the work
+// per chunk: scores dh / 128, products wc / 16 and a fixed part 3.6 (the
+// exponentials, the row sums, the epilogue; the narrower variants also run
+// at a lower MFMA rate), in units of one 16-column product.  With 3.6 the
+// choice is the fastest of the three measured on gfx950 at T = 8192,
+// dh = 128 (64-row tiles where the grid would underfill): 64 columns for
+// Fh = 2048 (161 us against 198 and 281), 704 (106 against 112 and 153) and
+// 640 (107 against 114 and 153).
+template <typename T> int agg_wcols(int Fh, int dh) {
+  const int cand[3] = {AggCfg<T>::WIDE, kMid, kNarrow};
+  int best = cand[0];
+  double best_cost = 0.0;
+  for (int c = 0; c < 3; ++c) {
+    const int wc = cand[c];
+    const double cost = (double)ceil_div(Fh, kWaves * wc) * (dh / 128.0 + wc / 16.0 + 3.6);
+    if (c == 0 || cost < best_cost) {
+      best = wc;
+      best_cost = cost;
+    }
+  }
+  return best;
 }
-template <typename T> int agg_fs(int Fh) { return kWaves * agg_wcols<T>(Fh); }
+template <typename T> int agg_fs(int Fh, int dh) { return kWaves * agg_wcols<T>(Fh, dh); }
 
+// wc: gate columns per wave; br: destination rows per tile, AggCfg<T>::BR or
+// (bf16 TANGO) kShortBR.
+template <typename T, int MODE, int BR>
+hipError_t launch_agg_wc(const AggArgs& a, int wc, int nfc, int rtiles, int64_t items, hipStream_t s) {
+  if (wc == AggCfg<T>::WIDE) return launch_agg_w<T, MODE, AggCfg<T>::WIDE, BR>(a, nfc, rtiles, items, s);
+  if (wc == kMid) return launch_agg_w<T, MODE, kMid, BR>(a, nfc, rtiles, items, s);
+  if (wc == kNarrow) return launch_agg_w<T, MODE, kNarrow, BR>(a, nfc, rtiles, items, s);
+  return hipErrorInvalidValue;
+}
 template <typename T, int MODE>
-hipError_t launch_agg_t(const AggArgs& a, int nfc, int rtiles, int64_t items, hipStream_t s) {
-  const int wc = agg_wcols<T>(a.F / a.H);
-  if (wc == AggCfg<T>::WIDE) return launch_agg_w<T, MODE, AggCfg<T>::WIDE>(a, nfc, rtiles, items, s);
-  if (wc == kMid) return launch_agg_w<T, MODE, kMid>(a, nfc, rtiles, items, s);
-  return launch_agg_w<T, MODE, kNarrow>(a, nfc, rtiles, items, s);
+hipError_t launch_agg_t(const AggArgs& a, int wc, int nfc, int rtiles, int64_t items, int br, hipStream_t s) {
+  constexpr int BR = AggCfg<T>::BR;
+  if constexpr (MODE == 0 && BR != kShortBR) {
+    if (br == kShortBR) return launch_agg_wc<T, MODE, kShortBR>(a, wc, nfc, rtiles, items, s);
+  }
+  if (br != BR) return hipErrorInvalidValue;
+  return launch_agg_wc<T, MODE, BR>(a, wc, nfc, rtiles, items, s);
 }
 
 }  // namespace
 
-AggPlan tango_agg_plan(int B, int Tp, int F, int H, bool bf) {
+AggPlan tango_agg_plan(int B, int Tp, int F, int H, int dh, bool bf) {
   AggPlan p;
   const int Fh = F / H;
-  p.fs = bf ? agg_fs<bf16>(Fh) : agg_fs<float>(Fh);
-  p.br = bf ? AggCfg<bf16>::BR : AggCfg<float>::BR;
+  p.fs = bf ? agg_fs<bf16>(Fh, dh) : agg_fs<float>(Fh, dh);
   p.nfc = (int)ceil_div(Fh, p.fs);   // waves past the head's width skip
-  p.rtiles = Tp / p.br;
-  const int half = p.rtiles / 2;
   const int64_t groups = (int64_t)B * H * p.nfc;
-  const int64_t pair_items = groups * (half + (p.rtiles & 1));
-  p.split = pair_items < 256 ? 1 : 0;
-  p.items = p.split ? groups * (2 * half + (p.rtiles & 1)) : pair_items;
-  p.n_split_tiles = p.split ? groups * half : 0;
+  auto shape = [&](int br) {
+    p.br = br;
+    p.rtiles = Tp / br;
+    const int half = p.rtiles / 2;
+    const int64_t pair_items = groups * (half + (p.rtiles & 1));
+    p.split = pair_items < kFillItems ? 1 : 0;
+    p.items = p.split ? groups * (2 * half + (p.rtiles & 1)) : pair_items;
+    p.n_split_tiles = p.split ? groups * half : 0;
+  };
+  shape(bf ? AggCfg<bf16>::BR : AggCfg<float>::BR);
+  // Few column chunks (narrow heads, one sequence) leave compute units idle
+  // even with the long tiles split: halve the tile height to double the
+  // items (each streams the same gate blocks for half the rows).
+  if (bf && p.items < kFillItems && p.fs == kWaves * AggCfg<bf16>::WIDE) shape(kShortBR);
   return p;
 }
 
@@ -552,19 +591,19 @@ hipError_t launch_tango_agg(const AggArgs& a, const AggPlan& p, bool bf, bool co
   }
   AggArgs aa = a;
   aa.split = p.split;
-  return bf ? launch_agg_t<bf16, 0>(aa, p.nfc, p.rtiles, p.items, s)
-            : launch_agg_t<float, 0>(aa, p.nfc, p.rtiles, p.items, s);
+  return bf ? launch_agg_t<bf16, 0>(aa, p.fs / kWaves, p.nfc, p.rtiles, p.items, p.br, s)
+            : launch_agg_t<float, 0>(aa, p.fs / kWaves, p.nfc, p.rtiles, p.items, p.br, s);
 }
 
 hipError_t launch_wango_band(const AggArgs& a, bool bf, hipStream_t s) {
   const int Fh = a.F / a.H;
-  const int fs = bf ? agg_fs<bf16>(Fh) : agg_fs<float>(Fh);
+  const int fs = bf ? agg_fs<bf16>(Fh, a.dh) : agg_fs<float>(Fh, a.dh);
   const int br = bf ? AggCfg<bf16>::BR : AggCfg<float>::BR;
   const int nfc = (int)ceil_div(Fh, fs);
   const int rtiles = a.Tp / br;
   const int64_t items = (int64_t)a.B * a.H * nfc * rtiles;
-  return bf ? launch_agg_t<bf16, 1>(a, nfc, rtiles, items, s)
-            : launch_agg_t<float, 1>(a, nfc, rtiles, items, s);
+  return bf ? launch_agg_t<bf16, 1>(a, fs / kWaves, nfc, rtiles, items, br, s)
+            : launch_agg_t<float, 1>(a, fs / kWaves, nfc, rtiles, items, br, s);
 }
 
 hipError_t launch_zero_i32(int* p, int64_t n, hipStream_t s) {

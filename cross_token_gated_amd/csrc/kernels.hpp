@@ -95,7 +95,7 @@ struct AggPlan {
   int64_t n_split_tiles;
 };
 
-AggPlan tango_agg_plan(int B, int Tp, int F, int H, bool bf);
+AggPlan tango_agg_plan(int B, int Tp, int F, int H, int dh, bool bf);
 
 struct ScanPlan {
   int nseg, chunks_per_seg, fs;

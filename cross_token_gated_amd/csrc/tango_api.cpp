@@ -5,6 +5,7 @@
 
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
@@ -182,7 +183,7 @@ Layout make_layout(const tango_shape_t* s, bool wango, int32_t window, int32_t c
   L.xs = take(proj_parts_bytes(M, s->d_model, bf));
   L.rinv = take(M * sizeof(float));
   if (!wango) {
-    L.agg = tango_agg_plan(s->batch, (int)pad_rows(s->seq_len), (int)F, s->n_heads, bf);
+    L.agg = tango_agg_plan(s->batch, (int)pad_rows(s->seq_len), (int)F, s->n_heads, s->head_dim, bf);
     const int64_t n = L.agg.n_split_tiles;
     L.part = take((size_t)n * 2 * L.agg.br * L.agg.fs * sizeof(float));
     L.part_den = take((size_t)n * 2 * L.agg.br * sizeof(float));
@@ -381,7 +382,7 @@ int stage_proj_common(const tango_shape_t* s, const tango_weights_t* weights, co
 
 int block_common(const tango_shape_t* s, const tango_weights_t* w, bool wango, int32_t window,
                  int32_t phi_dim, int32_t chunk, const void* x, void* out, void* ws, size_t ws_bytes,
-                 void* stream) {
+                 void* stream, bool check_only = false) {
   int rc = check_shape(s);
   if (rc) return rc;
   if ((rc = check_weights(w, true))) return rc;
@@ -406,6 +407,7 @@ int block_common(const tango_shape_t* s, const tango_weights_t* w, bool wango, i
                        {w->null_bias, s->n_heads * sizeof(float), "null_bias"}};
   const Range outs[] = {{out, xb, "out"}, {ws, L.total, "workspace"}};
   if ((rc = check_ranges(ins, 9, outs, 2, x, out))) return rc;
+  if (check_only) return ok();
   if ((rc = ensure_init())) return rc;
 
   hipStream_t st = static_cast<hipStream_t>(stream);
@@ -477,6 +479,56 @@ int tango_block_fwd(const tango_shape_t* shape, const tango_weights_t* weights, 
                     void* workspace, size_t workspace_bytes, void* hip_stream) {
   return guarded([&] {
     return block_common(shape, weights, false, 0, 0, 0, x, out, workspace, workspace_bytes, hip_stream);
+  });
+}
+
+size_t tango_stack_workspace_size(const tango_shape_t* shapes, int32_t n_sets) {
+  if (!shapes || n_sets < 1) return 0;
+  size_t need = 0;
+  for (int32_t k = 0; k < n_sets; ++k) {
+    if (check_shape(&shapes[k])) return 0;
+    need = std::max(need, make_layout(&shapes[k], false, 0, 0).total);
+  }
+  return need;
+}
+
+int tango_stack_fwd(const tango_shape_t* shapes, const tango_weights_t* sets, int32_t n_sets,
+                    const int32_t* schedule, int32_t n_apps, const void* x, void* out, void* workspace,
+                    size_t workspace_bytes, void* hip_stream) {
+  return guarded([&]() -> int {
+    if (!shapes || !sets || !schedule) return fail(TANGO_ERR_NULL, "shapes, sets or schedule is NULL");
+    if (n_sets < 1 || n_apps < 1)
+      return fail(TANGO_ERR_SHAPE, "n_sets %d and n_apps %d must be >= 1", n_sets, n_apps);
+    // everything is checked before the first launch
+    size_t need = 0;
+    for (int32_t k = 0; k < n_sets; ++k) {
+      const tango_shape_t& a = shapes[k];
+      int rc = check_shape(&a);
+      if (rc) return rc;
+      if ((rc = check_weights(&sets[k], true))) return rc;
+      const tango_shape_t& z = shapes[0];
+      if (a.batch != z.batch || a.seq_len != z.seq_len || a.d_model != z.d_model || a.dtype != z.dtype ||
+          a.io_dtype != z.io_dtype)
+        return fail(TANGO_ERR_SHAPE, "set %d: batch, seq_len, d_model, dtype and io_dtype must match set 0",
+                    k);
+      need = std::max(need, make_layout(&a, false, 0, 0).total);
+    }
+    for (int32_t r = 0; r < n_apps; ++r)
+      if (schedule[r] < 0 || schedule[r] >= n_sets)
+        return fail(TANGO_ERR_SHAPE, "schedule[%d] = %d is not a set index below %d", r, schedule[r], n_sets);
+    if (!x || !out) return fail(TANGO_ERR_NULL, "x or out is NULL");
+    if (!workspace) return fail(TANGO_ERR_NULL, "workspace is NULL");
+    if (workspace_bytes < need)
+      return fail(TANGO_ERR_WORKSPACE, "workspace of %zu bytes is smaller than the %zu needed",
+                  workspace_bytes, need);
+    for (int pass = 0; pass < 2; ++pass)   // pass 0 checks every call, pass 1 launches
+      for (int32_t r = 0; r < n_apps; ++r) {
+        const int32_t k = schedule[r];
+        const int rc = block_common(&shapes[k], &sets[k], false, 0, 0, 0, r == 0 ? x : out, out, workspace,
+                                    workspace_bytes, hip_stream, pass == 0);
+        if (rc) return rc;
+      }
+    return ok();
   });
 }
 
@@ -606,7 +658,7 @@ BwdLayout make_bwd_layout(const tango_shape_t* s) {
   const int64_t M = (int64_t)s->batch * pad_rows(s->seq_len);
   const int64_t HD = (int64_t)s->n_heads * s->head_dim, Fp = gate_pad(s, false);
   L.plan = tango_bwd_plan(s->batch, (int)pad_rows(s->seq_len), head_width(s), s->n_heads);
-  L.agg = tango_agg_plan(s->batch, (int)pad_rows(s->seq_len), (int)Fp, s->n_heads, true);
+  L.agg = tango_agg_plan(s->batch, (int)pad_rows(s->seq_len), (int)Fp, s->n_heads, s->head_dim, true);
   size_t off = 0;
   auto take = [&](size_t bytes) {
     const size_t o = off;

@@ -60,7 +60,7 @@
 extern "C" {
 #endif
 
-#define TANGO_ABI_VERSION 5
+#define TANGO_ABI_VERSION 6
 
 typedef enum { TANGO_F32 = 0, TANGO_BF16 = 1 } tango_dtype_t;
 
@@ -121,6 +121,35 @@ size_t tango_workspace_size(const tango_shape_t* shape);
 int tango_block_fwd(const tango_shape_t* shape, const tango_weights_t* weights,
                     const void* x, void* out, void* workspace, size_t workspace_bytes,
                     void* hip_stream);
+
+/* ---- Stack of TANGO blocks with several parameter sets --------------------
+ *
+ * The shared-weight stack of [TANGO] §2.3 eq. 11 applies one block R times.
+ * The later revision ("TANGO: Treating Tokens as Operators", abstract and
+ * Table 2) also trains a variant with three narrower gated-projection sets,
+ * one for the first application, one for the middle ones and one for the
+ * last.  tango_stack_fwd applies any such schedule: application r uses
+ * parameter set schedule[r].
+ *
+ *   shapes[n_sets], sets[n_sets]: the sizes and parameters of each set.  The
+ *       sets must agree on batch, seq_len, d_model, dtype and io_dtype (the
+ *       residual stream); d_gate, n_heads, head_dim, rope_base and rms_eps may
+ *       differ.  Parameters that the sets share (the three-set model keeps
+ *       one W_q, W_k, gain, theta and null bias, and varies W_g, W_v and W_o)
+ *       are shared by passing the same pointers.
+ *   schedule[n_apps]: set index of each application, 0 <= schedule[r] <
+ *       n_sets; n_apps >= 1.  Host memory, read before the call returns.
+ *   x -> out: [B, T, d] in io_dtype; out may equal x (in place); after the
+ *       first application the stream is carried in out.
+ *   workspace: at least tango_stack_workspace_size(shapes, n_sets) bytes (the
+ *       largest tango_workspace_size of the sets); 0 is returned there if a
+ *       shape is invalid or n_sets < 1.
+ * Every argument is checked before the first launch: on an error nothing runs
+ * and out is untouched.  Launches are asynchronous on hip_stream. */
+size_t tango_stack_workspace_size(const tango_shape_t* shapes, int32_t n_sets);
+int tango_stack_fwd(const tango_shape_t* shapes, const tango_weights_t* sets, int32_t n_sets,
+                    const int32_t* schedule, int32_t n_apps, const void* x, void* out,
+                    void* workspace, size_t workspace_bytes, void* hip_stream);
 
 /* Bytes of workspace wango_block_fwd needs; 0 if the arguments are invalid. */
 size_t wango_workspace_size(const tango_shape_t* shape, int32_t window, int32_t phi_dim,

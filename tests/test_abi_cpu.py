@@ -189,3 +189,39 @@ def test_decode_entry_points_validate(lib):
                                FAKE + 0x100000000, 1 << 40, FAKE + 0x200000000, 1 << 40, None)
     assert rc == _lib.STATUS_CODE["TANGO_ERR_UNSUPPORTED"]
     assert lib.tango_decode_state_size(ctypes.byref(shape(d_gate=64 * 33, n_heads=33, head_dim=32))) == 0
+
+
+def test_stack_entry_point_validates(lib):
+    """tango_stack_fwd checks every set and application before the first launch
+    (the fake pointers would fault if anything ran)."""
+    S3 = _lib.Shape * 3
+    W3 = _lib.Weights * 3
+    shapes = S3(shape(d_gate=704), shape(d_gate=640), shape(d_gate=704))
+    need = lib.tango_stack_workspace_size(shapes, 3)
+    assert need == max(lib.tango_workspace_size(ctypes.byref(shapes[k])) for k in range(3)) > 0
+    assert lib.tango_stack_workspace_size(shapes, 0) == 0
+    assert lib.tango_stack_workspace_size(S3(shape(), shape(d_gate=100), shape()), 3) == 0
+    sets = W3(weights(), weights(w_g=FAKE + 0x11000000, w_v=FAKE + 0x21000000, w_o=FAKE + 0x41000000),
+              weights(w_g=FAKE + 0x12000000, w_v=FAKE + 0x22000000, w_o=FAKE + 0x42000000))
+    sched = (ctypes.c_int32 * 4)(0, 1, 1, 2)
+    ws = FAKE + 0x80000000
+
+    def run(sh=shapes, st=sets, n_sets=3, sc=sched, n_apps=4, x=FAKE, out=FAKE + 0x60000000, nbytes=need):
+        return lib.tango_stack_fwd(sh, st, n_sets, sc, n_apps, x, out, ws, nbytes, None)
+
+    code = _lib.STATUS_CODE
+    assert run(sc=(ctypes.c_int32 * 4)(0, 1, 3, 2)) == code["TANGO_ERR_SHAPE"]     # set index out of range
+    assert run(sc=(ctypes.c_int32 * 4)(0, -1, 1, 2)) == code["TANGO_ERR_SHAPE"]
+    assert run(n_apps=0) == code["TANGO_ERR_SHAPE"]
+    assert run(n_sets=0) == code["TANGO_ERR_SHAPE"]
+    assert lib.tango_stack_fwd(shapes, sets, 3, None, 4, FAKE, FAKE + 0x60000000, ws, need, None) == -1
+    assert run(sh=S3(shape(d_gate=704), shape(d_gate=640, seq_len=128), shape(d_gate=704))) == \
+        code["TANGO_ERR_SHAPE"]                                                    # stream shapes differ
+    assert run(sh=S3(shape(d_gate=704), shape(d_gate=640, io_dtype=0), shape(d_gate=704))) == \
+        code["TANGO_ERR_SHAPE"]
+    assert run(nbytes=need - 1) == code["TANGO_ERR_WORKSPACE"]
+    assert run(x=None) == -1
+    # set 2's W_o overlaps the output: caught before application 0 runs
+    bad = W3(sets[0], sets[1], weights(w_g=FAKE + 0x12000000, w_v=FAKE + 0x22000000, w_o=FAKE + 0x60000000))
+    assert run(st=bad) == code["TANGO_ERR_ALIAS"]
+    assert run(st=W3(sets[0], weights(theta=None), sets[2])) == -1

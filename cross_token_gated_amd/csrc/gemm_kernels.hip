@@ -826,6 +826,266 @@ template <typename K> hipError_t raise_lds(K* k, size_t bytes) {
 }
 }  // namespace
 
+// ---------------------------------------------------------------------------
+// Backward of the TANGO aggregation ("TANGO: Token-Aggregated Nonlinear Gating
+// Operators ...", §2.1 eqs. 4-5, §2.2 eq. 6): the ds tiles and the products by
+// them.  With the forward's shifted weights w_ij = e^{tau (s_ij - 1)}, u_i =
+// dgbar_i / den_i and delta_i = -u_i . gbar_i (bwd_kernels.hip),
+//     ds_ij = tau w_ij (u_i . g_j + delta_i)   (j <= i),
+//     dq_i = sum_j ds_ij k_j,   dk_j = sum_i ds_ij q_i,   dtheta = sum ds_ij s_ij.
+//
+// KD: one 128 x 128 tile of ds (destination rows i of tile it, source rows j
+// of tile jt <= it, one sequence and head) per workgroup.  S = Q_i K_j^T
+// (k = d_h) and dW = U_i G_j^T (k = the head's gate columns) run one after the
+// other on the main loop above, into two accumulator sets.  The tile is
+// stored in bf16 twice: transposed (rows j, for dk) straight from the
+// accumulators, whose lanes hold 4 consecutive rows i of one column j, and by
+// rows (for dq) through LDS.  The workgroup also sums ds * s for dtheta.
+//
+// KM: dq (DIR 0) or dk (DIR 1) for one 128-row tile r and one chunk of
+// kBwdChunkTiles ds tiles along the sum: A = the rows of the ds tiles (DIR 0:
+// tiles (r, jt), jt <= r; DIR 1: the transposed tiles (it, r), it >= r), B =
+// the keys (queries) transposed per head, k = the summed position.  Each
+// chunk writes a float32 partial, which bwd_finish_kernel adds up.
+// ---------------------------------------------------------------------------
+namespace {
+
+using DsCfg = TileCfg<kBwdTile, kBwdTile, 32, 2, 2, 3, 1>;
+// (d_h = 32 runs 64 B rows, the upper half zero: a load pass covers 64 rows)
+template <int DH> using MmCfg = TileCfg<kBwdTile, (DH < 64 ? 64 : DH), 32, 2, 2, 3, 1>;
+constexpr int kTileElems = kBwdTile * kBwdTile;
+constexpr int kDsStride = kBwdTile + 8;   // bf16 per staged row (rows stay 16-byte aligned)
+constexpr size_t kStageBytes = (size_t)kBwdTile * kDsStride * sizeof(bf16);
+constexpr size_t kDsLds = ops_bytes<DsCfg, bf16>() > kStageBytes ? ops_bytes<DsCfg, bf16>() : kStageBytes;
+constexpr float kLogTauMaxB = 2.995732273553991f;   // log 20: tau = exp(min(theta, log 20))
+
+__host__ __device__ __forceinline__ int64_t tri_index(int i, int j) { return (int64_t)i * (i + 1) / 2 + j; }
+
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2)))
+void ds_kernel(BwdArgs a, int64_t ntri, int64_t items) {
+  using CF = DsCfg;
+  typedef bf16 T;
+  constexpr int PA = tile_chunks<CF, T>(CF::BM) / 4, PB = tile_chunks<CF, T>(CF::BN) / 4;
+  __shared__ __align__(16) unsigned char smem[kDsLds];
+  __shared__ float red[kThreads / 64];
+  T* lds = reinterpret_cast<T*>(smem);
+
+  const int64_t q8 = gridDim.x / 8;
+  const int64_t item = (int64_t)(blockIdx.x % 8) * q8 + blockIdx.x / 8;
+  if (item >= items) return;
+  const int64_t bh = item / ntri;
+  const int64_t t = item - bh * ntri;
+  int it = (int)((sqrt(8.0 * (double)t + 1.0) - 1.0) * 0.5);
+  while (tri_index(it + 1, 0) <= t) ++it;
+  while (tri_index(it, 0) > t) --it;
+  const int jt = (int)(t - tri_index(it, 0));
+  const int h = (int)(bh % a.H);
+  const int64_t mseq = (bh / a.H) * a.Tp;
+  const int HD = a.H * a.dh, tid = threadIdx.x;
+  const int64_t ri = mseq + (int64_t)it * kBwdTile, rj = mseq + (int64_t)jt * kBwdTile;
+
+  f32x4 accS[CF::IB][CF::JB], accW[CF::IB][CF::JB];
+#pragma unroll
+  for (int i = 0; i < CF::IB; ++i)
+#pragma unroll
+    for (int j = 0; j < CF::JB; ++j) {
+      accS[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+      accW[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+    }
+  PartsSource<T, PA, 1> sa;
+  sa.part_stride = 0;
+  RowSource<T, PB> sb;
+  // S = Q_i K_j^T
+#pragma unroll
+  for (int p = 0; p < PA; ++p) {
+    const PiecePos<CF, T> pp = piece_pos<CF, T>(tid, p);
+    sa.ptr[p] = static_cast<const T*>(a.qh) + (ri + pp.row) * HD + h * a.dh + pp.kp * piece_elems<T>();
+  }
+#pragma unroll
+  for (int p = 0; p < PB; ++p) {
+    const PiecePos<CF, T> pp = piece_pos<CF, T>(tid, p);
+    sb.ptr[p] = static_cast<const T*>(a.kh) + (rj + pp.row) * HD + h * a.dh + pp.kp * piece_elems<T>();
+    sb.ok[p] = true;
+  }
+  gemm_mainloop<CF, T>(accS, lds, a.dh / CF::BK, sa, sb);   // ends with a barrier
+  // dW = U_i G_j^T
+#pragma unroll
+  for (int p = 0; p < PA; ++p) {
+    const PiecePos<CF, T> pp = piece_pos<CF, T>(tid, p);
+    sa.ptr[p] = static_cast<const T*>(a.u_rm) + ((ri + pp.row) * a.H + h) * a.FhC + pp.kp * piece_elems<T>();
+  }
+#pragma unroll
+  for (int p = 0; p < PB; ++p) {
+    const PiecePos<CF, T> pp = piece_pos<CF, T>(tid, p);
+    sb.ptr[p] = static_cast<const T*>(a.g_rm) + ((rj + pp.row) * a.H + h) * a.FhC + pp.kp * piece_elems<T>();
+  }
+  gemm_mainloop<CF, T>(accW, lds, a.FhC / CF::BK, sa, sb);
+
+  // ds, its transposed store, the staged row-major copy and dtheta
+  const float tau = __expf(fminf(a.theta[h], kLogTauMaxB));
+  const float ktau = tau * kLog2e;
+  const float* delta = a.delta + (int64_t)h * a.B * a.Tp;
+  const int lane = tid & 63, col = lane & 15, grp = lane >> 4;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wr = wave / CF::WN, wc = wave % CF::WN;
+  T* st = reinterpret_cast<T*>(smem);
+  T* dst_t = static_cast<T*>(a.ds_t) + item * (int64_t)kTileElems;
+  float th = 0.f;
+#pragma unroll
+  for (int i = 0; i < CF::IB; ++i) {
+    const int r0 = wr * CF::WTM + i * 16 + grp * 4;   // this lane's rows r0 .. r0 + 3
+    float dl[4];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) dl[r] = delta[ri + r0 + r];
+#pragma unroll
+    for (int j = 0; j < CF::JB; ++j) {
+      const int c = wc * CF::WTN + j * 16 + col;
+      bf16x4 q4;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const float sv = accS[i][j][r];
+        const float w = __builtin_amdgcn_exp2f(ktau * (sv - 1.0f));
+        const bool valid = jt < it || c <= r0 + r;   // source j <= destination i
+        const float v = valid ? tau * w * (accW[i][j][r] + dl[r]) : 0.f;
+        th += v * sv;
+        q4[r] = (T)v;
+        st[(r0 + r) * kDsStride + c] = q4[r];
+      }
+      *reinterpret_cast<bf16x4*>(dst_t + c * kBwdTile + r0) = q4;
+    }
+  }
+  th = wave_sum(th);
+  if (lane == 0) red[wave] = th;
+  __syncthreads();
+  if (tid == 0) a.part_theta[item] = red[0] + red[1] + red[2] + red[3];
+  T* dst_r = static_cast<T*>(a.ds_rm) + item * (int64_t)kTileElems;
+  for (int q = tid; q < kTileElems / 8; q += kThreads) {
+    const int row = q >> 4, c8 = (q & 15) * 8;
+    *reinterpret_cast<u32x4*>(dst_r + row * kBwdTile + c8) =
+        *reinterpret_cast<const u32x4*>(st + row * kDsStride + c8);
+  }
+}
+
+// A operand of KM: pieces of the rows of a run of ds tiles along k.
+template <int DIR, int P> struct DsRowSource {
+  struct raw {
+    u32x4 v;
+  };
+  const bf16* tiles;   // the (sequence, head)'s first tile
+  int off[P];          // row * 128 + piece column of each pass
+  int r, kbase;
+  __device__ __forceinline__ void fetch(raw& x, int p, int k0) const {
+    const int k = kbase + k0, kt = k >> 7;
+    const int64_t tile = DIR == 0 ? tri_index(r, kt) : tri_index(kt, r);
+    x.v = *reinterpret_cast<const u32x4*>(tiles + tile * kTileElems + off[p] + (k & (kBwdTile - 1)));
+  }
+  __device__ __forceinline__ Parts<1> convert(const raw& x, int) const {
+    Parts<1> o;
+    o.p[0] = x.v;
+    return o;
+  }
+};
+
+template <int DIR, int DH>
+__device__ __forceinline__ void dsmm_job(const BwdArgs& a, int64_t ntri, int nch, int64_t bh, int r, int c,
+                                         bf16* lds) {
+  using CF = MmCfg<DH>;
+  typedef bf16 T;
+  constexpr int PA = tile_chunks<CF, T>(CF::BM) / 4, PB = tile_chunks<CF, T>(CF::BN) / 4;
+  const int nt = a.Tp / kBwdTile;
+  // k tiles of this chunk: DIR 0 jt in [0, r], DIR 1 it in [r, nt)
+  int first = c * kBwdChunkTiles, last = first + kBwdChunkTiles - 1;
+  if (DIR == 0) {
+    last = min(last, r);
+  } else {
+    first = max(first, r);
+    last = min(last, nt - 1);
+  }
+  if (first > last) return;   // workgroup-uniform
+  const int tid = threadIdx.x;
+  DsRowSource<DIR, PA> sa;
+  sa.tiles = static_cast<const T*>(DIR == 0 ? a.ds_rm : a.ds_t) + bh * ntri * kTileElems;
+  sa.r = r;
+  sa.kbase = first * kBwdTile;
+#pragma unroll
+  for (int p = 0; p < PA; ++p) {
+    const PiecePos<CF, T> pp = piece_pos<CF, T>(tid, p);
+    sa.off[p] = pp.row * kBwdTile + pp.kp * piece_elems<T>();
+  }
+  RowSource<T, PB> sb;
+  const T* xT = static_cast<const T*>(DIR == 0 ? a.kT : a.qT) + bh * DH * (int64_t)a.Tp;
+#pragma unroll
+  for (int p = 0; p < PB; ++p) {
+    const PiecePos<CF, T> pp = piece_pos<CF, T>(tid, p);
+    sb.ptr[p] = xT + (int64_t)(pp.row % DH) * a.Tp + sa.kbase + pp.kp * piece_elems<T>();
+    sb.ok[p] = pp.row < DH;
+  }
+  f32x4 acc[CF::IB][CF::JB];
+#pragma unroll
+  for (int i = 0; i < CF::IB; ++i)
+#pragma unroll
+    for (int j = 0; j < CF::JB; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+  gemm_mainloop<CF, T>(acc, lds, (last - first + 1) * (kBwdTile / CF::BK), sa, sb);
+
+  const int64_t M = (int64_t)a.B * a.Tp;
+  const int HD = a.H * DH, h = (int)(bh % a.H);
+  const int64_t row0 = (bh / a.H) * a.Tp + (int64_t)r * kBwdTile;
+  float* out = a.part + ((int64_t)DIR * nch + c) * M * HD + row0 * HD + h * DH;
+  const int lane = tid & 63, col = lane & 15, grp = lane >> 4;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wr = wave / CF::WN, wc = wave % CF::WN;
+#pragma unroll
+  for (int i = 0; i < CF::IB; ++i)
+#pragma unroll
+    for (int j = 0; j < CF::JB; ++j) {
+      const int e = wc * CF::WTN + j * 16 + col;
+      if (e < DH)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) out[(int64_t)(wr * CF::WTM + i * 16 + grp * 4 + q) * HD + e] = acc[i][j][q];
+    }
+}
+
+template <int DH>
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2)))
+void dsmm_kernel(BwdArgs a, int64_t ntri, int nch, int64_t items) {
+  __shared__ __align__(16) unsigned char smem[ops_bytes<MmCfg<DH>, bf16>()];
+  const int64_t q8 = gridDim.x / 8;
+  const int64_t item = (int64_t)(blockIdx.x % 8) * q8 + blockIdx.x / 8;
+  if (item >= items) return;
+  const int nt = a.Tp / kBwdTile;
+  const int64_t per_dir = (int64_t)a.B * a.H * nt * nch;
+  const int dir = (int)(item / per_dir);
+  int64_t rem = item - dir * per_dir;
+  const int c = (int)(rem % nch);
+  rem /= nch;
+  const int r = (int)(rem % nt);
+  const int64_t bh = rem / nt;
+  bf16* lds = reinterpret_cast<bf16*>(smem);
+  if (dir == 0) dsmm_job<0, DH>(a, ntri, nch, bh, r, c, lds);
+  else dsmm_job<1, DH>(a, ntri, nch, bh, r, c, lds);
+}
+
+}  // namespace
+
+hipError_t launch_tango_ds(const BwdArgs& a, const BwdPlan& p, hipStream_t s) {
+  if (a.dh % 32 != 0 || a.FhC % 32 != 0 || a.Tp % kBwdTile != 0) return hipErrorInvalidValue;
+  const int64_t q8 = ceil_div(p.items_ds, 8);
+  hipLaunchKernelGGL(ds_kernel, dim3((unsigned)(8 * q8)), dim3(kThreads), 0, s, a, p.ntri, p.items_ds);
+  return hipGetLastError();
+}
+
+hipError_t launch_tango_dsmm(const BwdArgs& a, const BwdPlan& p, hipStream_t s) {
+  const int64_t q8 = ceil_div(p.items_mm, 8);
+  dim3 grid((unsigned)(8 * q8)), block(kThreads);
+  switch (a.dh) {
+    case 32: hipLaunchKernelGGL(dsmm_kernel<32>, grid, block, 0, s, a, p.ntri, p.nch, p.items_mm); break;
+    case 64: hipLaunchKernelGGL(dsmm_kernel<64>, grid, block, 0, s, a, p.ntri, p.nch, p.items_mm); break;
+    case 128: hipLaunchKernelGGL(dsmm_kernel<128>, grid, block, 0, s, a, p.ntri, p.nch, p.items_mm); break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
 hipError_t gemm_kernels_init() {
   hipError_t e;
 #define TANGO_RAISE(K, BYTES) \

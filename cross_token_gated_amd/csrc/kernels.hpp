@@ -139,15 +139,16 @@ struct BwdArgs {
   // scratch
   void* u_rm;              // [B*Tp][H][FhC] u = dgbar / den, row-major
   void* g_rm;              // [B*Tp][H][FhC] gates, row-major
-  void* qp;                // [B*Tp/32][4][H*dh][8] packed queries
-  void* kp;                // packed keys
+  void* qT;                // [B][H][dh][Tp] queries, transposed per head
+  void* kT;                // [B][H][dh][Tp] keys, transposed per head
   void* q_rev;             // [B*Tp, H*dh] queries, every sequence reversed
   void* k_rev;             // keys, reversed
   void* u_rev_pk;          // packed reversed u, [B*Tp/32][4][Fp][8]
   float* delta;            // [H][B*Tp] float32
-  float* part_q;           // [nchunk][B*Tp][H*dh] float32 chunk partials of dq
-  float* part_k;           // same for dk
-  float* part_theta;       // [items] float32
+  void* ds_rm;             // [B*H][ntri][128][128] ds tiles, rows i (destinations)
+  void* ds_t;              // [B*H][ntri][128][128] ds tiles transposed, rows j (sources)
+  float* part;             // [2][nch][B*Tp][H*dh] float32 chunk partials of dq (0) and dk (1)
+  float* part_theta;       // [B*H*ntri] float32: sum of ds * s per tile
   // outputs
   float* dq;               // [B*Tp, H*dh] float32 (zero on rows past the end)
   float* dk;               // [B*Tp, H*dh]
@@ -156,16 +157,25 @@ struct BwdArgs {
   int B, T, Tp, H, dh;
   int F, Fh;               // gate columns (unpadded) in all and per head
   int Fhp, Fp;             // head-padded width of the packed gates, H * Fhp
-  int FhC;                 // head width of u_rm / g_rm (a multiple of 256)
+  int FhC;                 // head width of u_rm / g_rm (Fhp: a multiple of 64)
 };
 
+constexpr int kBwdTile = 128;        // rows of a ds tile
+constexpr int kBwdChunkTiles = 8;    // ds tiles per chunk of the dq / dk sums
+
 struct BwdPlan {
-  int FhC, nchunk, rtiles, half;
-  int64_t items;
+  int FhC;
+  int nt;              // 128-row tiles per sequence
+  int64_t ntri;        // ds tiles per (sequence, head): nt (nt + 1) / 2
+  int nch;             // chunks of kBwdChunkTiles tiles along a sum
+  int64_t items_ds;    // B * H * ntri
+  int64_t items_mm;    // 2 * B * H * nt * nch (some empty)
 };
-BwdPlan tango_bwd_plan(int B, int Tp, int Fh, int H);
+BwdPlan tango_bwd_plan(int B, int Tp, int Fhp, int H);
 hipError_t launch_tango_bwd_prep(const BwdArgs& a, const BwdPlan& p, hipStream_t s);
-hipError_t launch_tango_dqk(const BwdArgs& a, const BwdPlan& p, hipStream_t s);
+// ds tiles and their products (gemm_kernels.hip)
+hipError_t launch_tango_ds(const BwdArgs& a, const BwdPlan& p, hipStream_t s);
+hipError_t launch_tango_dsmm(const BwdArgs& a, const BwdPlan& p, hipStream_t s);
 hipError_t launch_tango_bwd_finish(const BwdArgs& a, const BwdPlan& p, hipStream_t s);
 
 // ---- autoregressive decode -------------------------------------------------

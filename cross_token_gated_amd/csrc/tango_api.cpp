@@ -646,8 +646,8 @@ int tango_aggregate_fwd_train(const tango_shape_t* shape, const float* theta, co
 namespace {
 
 struct BwdLayout {
-  size_t u_rm, g_rm, qp, kp, q_rev, k_rev, u_rev_pk, delta, part_q, part_k, part_theta;
-  size_t part, part_den, counters;   // split scratch of the reversed aggregation (dg)
+  size_t u_rm, g_rm, qT, kT, q_rev, k_rev, u_rev_pk, delta, ds_rm, ds_t, part, part_theta;
+  size_t agg_part, part_den, counters;   // split scratch of the reversed aggregation (dg)
   size_t total;
   BwdPlan plan;
   AggPlan agg;
@@ -657,7 +657,7 @@ BwdLayout make_bwd_layout(const tango_shape_t* s) {
   BwdLayout L{};
   const int64_t M = (int64_t)s->batch * pad_rows(s->seq_len);
   const int64_t HD = (int64_t)s->n_heads * s->head_dim, Fp = gate_pad(s, false);
-  L.plan = tango_bwd_plan(s->batch, (int)pad_rows(s->seq_len), head_width(s), s->n_heads);
+  L.plan = tango_bwd_plan(s->batch, (int)pad_rows(s->seq_len), head_pad(s, false), s->n_heads);
   L.agg = tango_agg_plan(s->batch, (int)pad_rows(s->seq_len), (int)Fp, s->n_heads, s->head_dim, true);
   size_t off = 0;
   auto take = [&](size_t bytes) {
@@ -668,17 +668,19 @@ BwdLayout make_bwd_layout(const tango_shape_t* s) {
   const size_t es = 2;   // bfloat16
   L.u_rm = take((size_t)M * s->n_heads * L.plan.FhC * es);
   L.g_rm = take((size_t)M * s->n_heads * L.plan.FhC * es);
-  L.qp = take((size_t)M * HD * es);
-  L.kp = take((size_t)M * HD * es);
+  L.qT = take((size_t)M * HD * es);
+  L.kT = take((size_t)M * HD * es);
   L.q_rev = take((size_t)M * HD * es);
   L.k_rev = take((size_t)M * HD * es);
   L.u_rev_pk = take((size_t)M * Fp * es);
   L.delta = take((size_t)M * s->n_heads * sizeof(float));
-  L.part_q = take((size_t)L.plan.nchunk * M * HD * sizeof(float));
-  L.part_k = take((size_t)L.plan.nchunk * M * HD * sizeof(float));
-  L.part_theta = take((size_t)L.plan.items * sizeof(float));
+  const size_t tiles = (size_t)L.plan.items_ds * kBwdTile * kBwdTile * es;
+  L.ds_rm = take(tiles);
+  L.ds_t = take(tiles);
+  L.part = take((size_t)2 * L.plan.nch * M * HD * sizeof(float));
+  L.part_theta = take((size_t)L.plan.items_ds * sizeof(float));
   const int64_t n = L.agg.n_split_tiles;
-  L.part = take((size_t)n * 2 * L.agg.br * L.agg.fs * sizeof(float));
+  L.agg_part = take((size_t)n * 2 * L.agg.br * L.agg.fs * sizeof(float));
   L.part_den = take((size_t)n * 2 * L.agg.br * sizeof(float));
   L.counters = take((size_t)n * sizeof(int));
   L.total = off;
@@ -743,14 +745,15 @@ int tango_aggregate_bwd(const tango_shape_t* shape, const float* theta, const fl
     a.null_bias = null_bias;
     a.u_rm = base + L.u_rm;
     a.g_rm = base + L.g_rm;
-    a.qp = base + L.qp;
-    a.kp = base + L.kp;
+    a.qT = base + L.qT;
+    a.kT = base + L.kT;
     a.q_rev = base + L.q_rev;
     a.k_rev = base + L.k_rev;
     a.u_rev_pk = base + L.u_rev_pk;
     a.delta = reinterpret_cast<float*>(base + L.delta);
-    a.part_q = reinterpret_cast<float*>(base + L.part_q);
-    a.part_k = reinterpret_cast<float*>(base + L.part_k);
+    a.ds_rm = base + L.ds_rm;
+    a.ds_t = base + L.ds_t;
+    a.part = reinterpret_cast<float*>(base + L.part);
     a.part_theta = reinterpret_cast<float*>(base + L.part_theta);
     a.dq = dq;
     a.dk = dk;
@@ -770,14 +773,15 @@ int tango_aggregate_bwd(const tango_shape_t* shape, const float* theta, const fl
     if (e != hipSuccess) return hip_fail(e, "backward prep kernels");
     // dg: the aggregation of the time-reversed problem, numerator only
     AggArgs aa = agg_args(s, theta, nullptr, a.k_rev, a.q_rev, a.u_rev_pk, dg, false);
-    aa.part = reinterpret_cast<float*>(base + L.part);
+    aa.part = reinterpret_cast<float*>(base + L.agg_part);
     aa.part_den = reinterpret_cast<float*>(base + L.part_den);
     aa.counters = reinterpret_cast<int*>(base + L.counters);
     aa.num_only = 1;
     aa.rev_out = 1;
     if ((e = launch_tango_agg(aa, L.agg, true, false, st)) != hipSuccess)
       return hip_fail(e, "reversed aggregation (dg)");
-    if ((e = launch_tango_dqk(a, L.plan, st)) != hipSuccess) return hip_fail(e, "dq / dk kernels");
+    if ((e = launch_tango_ds(a, L.plan, st)) != hipSuccess) return hip_fail(e, "ds tile kernel");
+    if ((e = launch_tango_dsmm(a, L.plan, st)) != hipSuccess) return hip_fail(e, "dq / dk kernel");
     if ((e = launch_tango_bwd_finish(a, L.plan, st)) != hipSuccess) return hip_fail(e, "backward finish");
     return ok();
   });

@@ -312,22 +312,17 @@ def backward_bench(steps: int, warmup: int, dev, stream) -> dict:
     from cross_token_gated_amd import api
     from tests import helpers as H
 
-    T, F, Hh, dh = 8192, 2048, 1, 128
+    from cross_token_gated_amd import workload as wl
+
+    c = wl.BACKWARD_SHAPE
+    T, F, Hh, dh = c["T"], c["F"], c["H"], c["dh"]
     Tp = H.padded_len(T)
-    rng = np.random.default_rng(5)
-    q = rng.standard_normal((Tp, Hh * dh)).astype(np.float32)
-    k = rng.standard_normal((Tp, Hh * dh)).astype(np.float32)
-    q /= np.linalg.norm(q, axis=-1, keepdims=True)
-    k /= np.linalg.norm(k, axis=-1, keepdims=True)
-    q[T:] = 0
-    k[T:] = 0
-    g = rng.standard_normal((Tp, F)).astype(np.float32)
-    g[T:] = 0
+    q, k, g, dg_in = wl.aggregate_inputs(T, F, Hh, dh, c["seed"])
     bf = torch.bfloat16
-    qd = torch.from_numpy(q).to(dev).to(bf)
-    kd = torch.from_numpy(k).to(dev).to(bf)
-    gp = torch.from_numpy(H.pack_gates(g)).to(dev).to(bf).reshape(-1)
-    dgbar = torch.from_numpy(rng.standard_normal((Tp, F)).astype(np.float32)).to(dev).to(bf)
+    qd = torch.from_numpy(H.pad_rows(q.reshape(1, T, Hh * dh), Tp).reshape(Tp, Hh * dh)).to(dev).to(bf)
+    kd = torch.from_numpy(H.pad_rows(k.reshape(1, T, Hh * dh), Tp).reshape(Tp, Hh * dh)).to(dev).to(bf)
+    gp = torch.from_numpy(H.pack_gates(H.pad_rows(g[None], Tp)).reshape(-1)).to(dev).to(bf)
+    dgbar = torch.from_numpy(H.pad_rows(dg_in[None], Tp).reshape(Tp, F)).to(dev).to(bf)
     theta = torch.full((Hh,), math.log(10.0), dtype=torch.float32, device=dev)
     shape = api.make_shape(1, T, 512, F, Hh, dh, bf)
     gbar = torch.empty((Tp, F), dtype=bf, device=dev)

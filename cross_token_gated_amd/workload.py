@@ -167,6 +167,26 @@ def make_stack_inputs(sw: StackWorkload, seed: Optional[int] = None) -> list:
     return out
 
 
+# The aggregation backward at the T = 8192 bench shape: one head of 128,
+# F = 2048, bf16.
+BACKWARD_SHAPE = dict(T=8192, F=2048, H=1, dh=128, seed=5)
+
+
+def aggregate_inputs(T: int, F: int, H: int, dh: int, seed: int):
+    """Seeded inputs of the aggregation alone, as float32 arrays that bfloat16
+    holds exactly: unit query and key vectors q, k [T, H, d_h] (Gaussian
+    directions), gates g [T, F] and an incoming gradient dgbar [T, F], both
+    N(0, 1).  Drawn with PCG64 in the order q, k, g, dgbar."""
+    rng = np.random.Generator(np.random.PCG64(seed))
+    q = rng.standard_normal((T, H, dh))
+    k = rng.standard_normal((T, H, dh))
+    q /= np.linalg.norm(q, axis=-1, keepdims=True)
+    k /= np.linalg.norm(k, axis=-1, keepdims=True)
+    g = rng.standard_normal((T, F))
+    dgbar = rng.standard_normal((T, F))
+    return round_bf16(q), round_bf16(k), round_bf16(g), round_bf16(dgbar)
+
+
 def round_f32(a: np.ndarray) -> np.ndarray:
     """float64 -> float32 (round to nearest even)."""
     return np.asarray(a, dtype=np.float32)

@@ -20,6 +20,13 @@ last products): 2^-9 of each value, the floor of the forward stages too.
     gbar and u rounded to bf16 moves dtheta by up to 1.2% of its value on
     these cases, far less of that scale.
   * dnull: 5e-2 of the largest head's value (measured within 1%).
+At T = 8192 (the bench shape) the first rows, where one source holds nearly
+all the weight, make dg entries about 100 times its rms, so max|err|/rms is
+no longer a useful bar for dg there.  That test bounds every dg entry
+instead: dg_j = sum_i alpha_ij dgbar_i (alpha the normalised weights) is
+formed from bf16 u and bf16 weights and stored in bf16, three roundings of
+2^-9 each on terms whose absolute sum is sum_i alpha_ij |dgbar_i|; the bar is
+2^-6 of that sum (a factor 2 over 3 * 2^-9).
 """
 import math
 
@@ -130,6 +137,55 @@ def test_aggregate_backward(case, null):
     tau = O.temperature(theta)
     den_ref = np.stack([BW.aggregate_denominators(q[b], k[b], theta, nb) for b in range(B)]) * np.exp(-tau)
     np.testing.assert_allclose(H.unpad_rows(host(den), B, T), den_ref, rtol=1e-2)
+
+
+def test_aggregate_backward_full_size():
+    """The bench's backward shape (T = 8192, F = 2048, one head of 128, bf16)
+    against the whole float64 oracle, with the bars above."""
+    from cross_token_gated_amd import workload as wl
+    c = wl.BACKWARD_SHAPE
+    T, F, Hh, dh = c["T"], c["F"], c["H"], c["dh"]
+    Tp = H.padded_len(T)
+    q, k, g, dgbar = wl.aggregate_inputs(T, F, Hh, dh, c["seed"])
+    q, k, g, dgbar = (np.asarray(a, np.float64) for a in (q, k, g, dgbar))
+    theta = np.full(Hh, math.log(10.0), dtype=np.float32)
+    shape = api.make_shape(1, T, 128, F, Hh, dh, torch.bfloat16)
+    announce(f"aggregate_backward full size {c}")
+    qd = dev_tensor(H.pad_rows(q.reshape(1, T, Hh * dh), Tp), "bf16")
+    kd = dev_tensor(H.pad_rows(k.reshape(1, T, Hh * dh), Tp), "bf16")
+    gp = dev_tensor(H.pack_gates(H.pad_rows(g[None], Tp)).reshape(-1), "bf16")
+    dgd = dev_tensor(H.pad_rows(dgbar[None], Tp), "bf16")
+    th = dev_f32(theta)
+    gbar = torch.empty((Tp, F), dtype=torch.bfloat16, device="cuda:0")
+    den = torch.empty((Tp, Hh), dtype=torch.float32, device="cuda:0")
+    api.tango_aggregate_fwd_train(shape, th, None, qd, kd, gp, gbar, den,
+                                  api.workspace(api.tango_workspace_size(shape), "cuda:0"))
+    dq = torch.empty((Tp, Hh * dh), dtype=torch.float32, device="cuda:0")
+    dk = torch.empty_like(dq)
+    dgo = torch.empty((Tp, F), dtype=torch.bfloat16, device="cuda:0")
+    dth = torch.empty((Hh,), dtype=torch.float32, device="cuda:0")
+    api.tango_aggregate_bwd(shape, th, None, qd, kd, gp, gbar, den, dgd, dq, dk, dgo, dth, None,
+                            api.workspace(api.tango_aggregate_bwd_workspace_size(shape), "cuda:0"))
+    torch.cuda.synchronize()
+    dq_ref, dk_ref, dg_ref, dth_ref, _ = BW.tango_aggregate_backward(q, k, g, theta, None, dgbar)
+    _check(host(dq)[:T], dq_ref.reshape(T, Hh * dh), "dq")
+    _check(host(dk)[:T], dk_ref.reshape(T, Hh * dh), "dk")
+    got_dg = host(dgo)[:T]
+    print(f"dg: rms ratio {H.rms_ratio(got_dg, dg_ref):.2e}, max ratio {H.err_ratio(got_dg, dg_ref):.2e}")
+    assert H.rms_ratio(got_dg, dg_ref) <= BARS[0]
+    tau = float(O.temperature(theta)[0])
+    m = np.tril(np.exp(tau * (q[:, 0] @ k[:, 0].T)))
+    alpha = m / m.sum(axis=1, keepdims=True)
+    del m
+    bound = 2.0 ** -6 * (alpha.T @ np.abs(dgbar))
+    del alpha
+    worst = float(np.max(np.abs(got_dg - dg_ref) / bound))
+    print(f"dg: largest error / per-entry bound {worst:.3f}")
+    assert worst <= 1.0
+    scale = np.abs(np.einsum("the,the->th", q, dq_ref)).sum(axis=0)
+    err = np.abs(host(dth) - dth_ref)
+    print("dtheta", host(dth), dth_ref, "error / scale", err / scale)
+    assert np.all(err <= THETA_BAR * scale), (err, scale)
 
 
 def test_aggregate_backward_rejects_float32():

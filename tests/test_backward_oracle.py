@@ -98,3 +98,46 @@ def test_denominators_equal_loop_definition():
             ref = sum(math.exp(tau[a] * sum(q[i, a, e] * k[j, a, e] for e in range(4))) for j in range(i + 1))
             ref += (i + 1) * math.exp(nb[a])
             assert den[i, a] == pytest.approx(ref, rel=1e-13)
+
+
+def _wloss(q, k, g, theta, nb, dgbar, window):
+    tau = O.temperature(theta)
+    gbar = O.aggregate_direct(q, k, g, tau, nb, "wango", window)
+    return float((dgbar * gbar).sum())
+
+
+@pytest.mark.parametrize("null", [False, True])
+@pytest.mark.parametrize("T,H,dh,fh,window", [(6, 1, 4, 3, 1), (9, 2, 4, 5, 2), (12, 1, 8, 4, 4), (5, 1, 4, 3, 9)])
+def test_wango_backward_equals_central_differences(null, T, H, dh, fh, window):
+    q, k, g, theta, nb, dgbar = _inputs(17 + T + window, T, H, dh, fh)
+    nb = nb if null else None
+    dq, dk, dg, dtheta, dnull = BW.wango_aggregate_backward(q, k, g, theta, nb, dgbar, window)
+    rng = np.random.default_rng(4)
+    f = lambda **kw: _wloss(kw.get("q", q), kw.get("k", k), kw.get("g", g), kw.get("theta", theta),  # noqa: E731
+                            kw.get("nb", nb), dgbar, window)
+    for _ in range(12):
+        i = tuple(int(rng.integers(0, s)) for s in q.shape)
+        assert dq[i] == pytest.approx(_central(lambda x: f(q=x), q, i), rel=1e-6, abs=1e-8)
+        i = tuple(int(rng.integers(0, s)) for s in k.shape)
+        assert dk[i] == pytest.approx(_central(lambda x: f(k=x), k, i), rel=1e-6, abs=1e-8)
+        i = tuple(int(rng.integers(0, s)) for s in g.shape)
+        assert dg[i] == pytest.approx(_central(lambda x: f(g=x), g, i), rel=1e-6, abs=1e-8)
+    for a in range(H):
+        assert dtheta[a] == pytest.approx(_central(lambda x: f(theta=x), theta, a), rel=1e-6, abs=1e-8)
+        if null:
+            assert dnull[a] == pytest.approx(_central(lambda x: f(nb=x), nb, a), rel=1e-6, abs=1e-8)
+
+
+def test_wango_backward_with_a_window_over_everything_is_tango():
+    # W >= T: every source is in the window, so WANGO is TANGO
+    q, k, g, theta, nb, dgbar = _inputs(29, 7, 2, 4, 3)
+    a = BW.wango_aggregate_backward(q, k, g, theta, nb, dgbar, 7)
+    b = BW.tango_aggregate_backward(q, k, g, theta, nb, dgbar)
+    for x, y in zip(a, b):
+        np.testing.assert_allclose(x, y, rtol=1e-12, atol=1e-14)
+
+
+def test_phi_prime_is_the_derivative_of_phi():
+    x = np.linspace(-3.0, 3.0, 41) + 1e-3   # away from the kink at 0
+    num = (O.phi(x + 1e-6, 16) - O.phi(x - 1e-6, 16)) / 2e-6
+    np.testing.assert_allclose(BW.phi_prime(x, 16), num, rtol=1e-7, atol=1e-10)

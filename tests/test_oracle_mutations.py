@@ -127,3 +127,13 @@ def test_pins_catch_planted_mistake(name, monkeypatch):
         except AssertionError:
             failures += 1
     assert failures > 0, f"no pin caught: {name}"
+
+
+def test_backward_pins_catch_a_wrong_feature_derivative(monkeypatch):
+    """A planted mistake in the WANGO backward (the feature map's derivative
+    taken as exp(x) on both sides of 0) fails the central-difference pin."""
+    import oracle.backward_oracle as BW
+    import tests.test_backward_oracle as BP
+    monkeypatch.setattr(BW, "phi_prime", lambda x, dh: np.exp(np.minimum(x, 30.0)) / math.sqrt(dh))
+    with pytest.raises(AssertionError):
+        BP.test_wango_backward_equals_central_differences(False, 9, 2, 4, 5, 2)

@@ -27,6 +27,8 @@ EXPORTS = [
     "wango_decode_state_size", "wango_decode_workspace_size", "wango_decode_step",
     "tango_aggregate_fwd_train", "tango_aggregate_bwd_workspace_size", "tango_aggregate_bwd",
     "tango_stack_workspace_size", "tango_stack_fwd",
+    "wango_aggregate_fwd_train_workspace_size", "wango_aggregate_fwd_train",
+    "wango_aggregate_bwd_workspace_size", "wango_aggregate_bwd",
 ]
 
 
@@ -90,6 +92,10 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
         "tango_aggregate_bwd_workspace_size": (sz, [S]),
         "tango_stack_workspace_size": (sz, [S, i32]),
         "tango_stack_fwd": (ctypes.c_int, [S, W, i32, vp, i32, vp, vp, vp, sz, vp]),
+        "wango_aggregate_fwd_train_workspace_size": (sz, [S, i32, i32]),
+        "wango_aggregate_fwd_train": (ctypes.c_int, [S, i32, i32, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]),
+        "wango_aggregate_bwd_workspace_size": (sz, [S, i32, i32]),
+        "wango_aggregate_bwd": (ctypes.c_int, [S, i32, i32] + [vp] * 14 + [sz, vp]),
         "tango_aggregate_bwd": (ctypes.c_int, [S, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz,
                                                vp]),
     }

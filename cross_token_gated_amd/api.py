@@ -196,6 +196,28 @@ def tango_aggregate_bwd(shape: Shape, theta, null_bias, qh, kh, gp, gbar, den, d
                                      _stream(stream)))
 
 
+def wango_aggregate_fwd_train_workspace_size(shape: Shape, window: int, chunk: int) -> int:
+    return int(load().wango_aggregate_fwd_train_workspace_size(ctypes.byref(shape), window, chunk))
+
+
+def wango_aggregate_fwd_train(shape: Shape, window: int, chunk: int, theta, null_bias, qh, kh, gp, gbar, den,
+                              ws, stream=None) -> None:
+    check(load().wango_aggregate_fwd_train(ctypes.byref(shape), window, chunk, _ptr(theta), _ptr(null_bias),
+                                           _ptr(qh), _ptr(kh), _ptr(gp), _ptr(gbar), _ptr(den), _ptr(ws),
+                                           ws.numel(), _stream(stream)))
+
+
+def wango_aggregate_bwd_workspace_size(shape: Shape, window: int, chunk: int) -> int:
+    return int(load().wango_aggregate_bwd_workspace_size(ctypes.byref(shape), window, chunk))
+
+
+def wango_aggregate_bwd(shape: Shape, window: int, chunk: int, theta, null_bias, qh, kh, gp, gbar, den, dgbar,
+                        dq, dk, dg, dtheta, dnull, ws, stream=None) -> None:
+    check(load().wango_aggregate_bwd(ctypes.byref(shape), window, chunk, _ptr(theta), _ptr(null_bias), _ptr(qh),
+                                     _ptr(kh), _ptr(gp), _ptr(gbar), _ptr(den), _ptr(dgbar), _ptr(dq), _ptr(dk),
+                                     _ptr(dg), _ptr(dtheta), _ptr(dnull), _ptr(ws), ws.numel(), _stream(stream)))
+
+
 def tango_stage_out(shape: Shape, w_o, x, gbar, v, out, stream=None) -> None:
     check(load().tango_stage_out(ctypes.byref(shape), _ptr(w_o), _ptr(x), _ptr(gbar), _ptr(v),
                                  _ptr(out), _stream(stream)))

@@ -458,14 +458,13 @@ __global__ __launch_bounds__(kAggThreads) void agg_kernel(AggArgs a, int nfc, in
                                     __HIP_MEMORY_SCOPE_AGENT);
         dsum += null_w * (float)(i + 1);
         if (MODE == 1) dsum += escale * a.z_old[(mseq + i) * a.H + h];
-        // TANGO options: the denominator for a later backward pass (one
-        // writer per row: column chunk 0, wave 0); the numerator alone; rows
-        // stored in reverse order (rows past the end are not stored then)
-        if (MODE == 0 && a.den_out && fc == 0 && wave == 0 && lg == 0 && i < a.T)
-          a.den_out[(mseq + i) * a.H + h] = dsum;
-        const float inv = (MODE == 0 && a.num_only) ? 1.0f : 1.0f / dsum;
-        const int64_t orow = (MODE == 0 && a.rev_out) ? mseq + (a.T - 1 - i) : mseq + i;
-        const bool ostore = !(MODE == 0 && a.rev_out) || i < a.T;
+        // Options: the denominator for a later backward pass (one writer per
+        // row: column chunk 0, wave 0); the numerator alone; rows stored in
+        // reverse order (rows past the end are not stored then)
+        if (a.den_out && fc == 0 && wave == 0 && lg == 0 && i < a.T) a.den_out[(mseq + i) * a.H + h] = dsum;
+        const float inv = a.num_only ? 1.0f : 1.0f / dsum;
+        const int64_t orow = a.rev_out ? mseq + (a.T - 1 - i) : mseq + i;
+        const bool ostore = !a.rev_out || i < a.T;
 #pragma unroll
         for (int fb = 0; fb < NFB; ++fb) {
           f32x4 num = acc[ib][fb];

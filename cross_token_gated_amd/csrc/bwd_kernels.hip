@@ -33,6 +33,8 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
 constexpr float kLogTauMax = 2.995732273553991f;   // log 20: tau = exp(min(theta, log 20))
 
+thread_local const char* t_step = "";   // kernel of the last launch (named in error messages)
+
 // Row of position r (0..31) of a 32-row block in slot (grp, s) order.
 __device__ __forceinline__ void slot_of_row(int r, int& grp, int& s) {
   if (r < 16) {
@@ -69,7 +71,10 @@ __global__ __launch_bounds__(256) void bwd_rows_kernel(BwdArgs a) {
     u[c] = (T)uv;
   }
   dot = wave_sum(dot);
-  if (lane == 0) a.delta[(int64_t)h * a.B * a.Tp + m] = live ? -dot : 0.f;
+  if (lane == 0) {
+    a.delta[(int64_t)h * a.B * a.Tp + m] = live ? -dot : 0.f;
+    if (a.window > 0) u[a.Fhp] = (T)(live ? -dot : 0.f);   // WANGO: delta in the extra column
+  }
 }
 
 // Row-major [rows][ld] -> packed [rows/32][4][ncols][8].  Packed column n is
@@ -107,9 +112,12 @@ __global__ __launch_bounds__(256) void pack_kernel(const T* __restrict__ src, in
 
 // Packed gates [rows/32][4][H*src_hw][8] -> row-major [rows][H][dst_hw]
 // (columns past valid_w zero).
+// one_col >= 0: that column holds 1 on rows before the sequence end (the
+// extra column of WANGO's augmented gates).
 template <typename T>
 __global__ __launch_bounds__(256) void unpack_kernel(const T* __restrict__ gp, int src_F, T* __restrict__ dst,
-                                                     int H, int src_hw, int dst_hw, int valid_w, int64_t rows) {
+                                                     int H, int src_hw, int dst_hw, int valid_w, int64_t rows,
+                                                     int one_col, int Tp, int T_) {
   const int64_t id = (int64_t)blockIdx.x * 256 + threadIdx.x;
   const int64_t per_row = (int64_t)H * dst_hw;
   if (id >= rows * per_row) return;
@@ -119,6 +127,7 @@ __global__ __launch_bounds__(256) void unpack_kernel(const T* __restrict__ gp, i
   slot_of_row((int)(row % 32), grp, s);
   float v = 0.f;
   if (c < valid_w) v = (float)gp[packed_offset(row / 32, grp, (int64_t)hd * src_hw + c, src_F) + s];
+  else if (c == one_col && (int)(row % Tp) < T_) v = 1.0f;
   dst[id] = (T)v;
 }
 
@@ -150,6 +159,74 @@ __global__ __launch_bounds__(256) void transpose_kernel(const T* __restrict__ sr
   dst[id] = src[(b * Tp + i) * (int64_t)H * dh + (int64_t)h * dh + e];
 }
 
+// WANGO feature layouts of phi(sqrt(tau) x) for x = q or k ([TANGO] §2.2 eq. 8),
+// row-major [M][H*dh] (plain, and/or in the permuted feature order of each
+// group of 32 that the scan reads for its destination features).
+template <typename T>
+__global__ __launch_bounds__(256) void phi_kernel(const T* __restrict__ src, T* __restrict__ plain,
+                                                  T* __restrict__ perm, const float* theta, int H, int dh,
+                                                  int64_t n) {
+  const int64_t id = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (id >= n) return;
+  const int HD = H * dh;
+  const int64_t m = id / HD;
+  const int col = (int)(id % HD), h = col / dh, e = col % dh;
+  const float st = sqrtf(__expf(fminf(theta[h], kLogTauMax)));
+  const T v = (T)phi_feature(st * (float)src[id], 1.0f / sqrtf((float)dh));
+  if (plain) plain[id] = v;
+  if (perm) perm[m * HD + h * dh + (e / 32) * 32 + feature_slot(e % 32)] = v;
+}
+
+// Shifted prefix (S) or suffix (R) over the tiles of the per-tile sums, stored
+// in bf16: S[t] = sum_{t' <= t - nb} tsum[t'], R[t] = sum_{t' >= t + nb} tsum[t'].
+__global__ __launch_bounds__(256) void state_scan_kernel(WStateArgs w, int reverse) {
+  const int64_t E = (int64_t)w.dh * w.FhC;
+  const int64_t id = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (id >= (int64_t)w.B * w.H * E) return;
+  const int64_t bh = id / E, el = id % E;
+  const float* ts = w.tsum + bh * w.nt * E + el;
+  __bf16* st = static_cast<__bf16*>(w.state) + bh * w.nt * E + el;
+  float acc = 0.f;
+  if (!reverse) {
+    for (int t = 0; t < w.nt; ++t) {
+      if (t - w.nb >= 0) acc += ts[(int64_t)(t - w.nb) * E];
+      st[(int64_t)t * E] = (__bf16)acc;
+    }
+  } else {
+    for (int t = w.nt - 1; t >= 0; --t) {
+      if (t + w.nb <= w.nt - 1) acc += ts[(int64_t)(t + w.nb) * E];
+      st[(int64_t)t * E] = (__bf16)acc;
+    }
+  }
+}
+
+// WANGO finish: dq = window part + sqrt(tau) phi'(sqrt(tau) q) (near + far dp),
+// dk alike with da; each element's share of dtheta through the features,
+// sqrt(tau) / 2 (dp phi'(sqrt(tau) q) q + da phi'(sqrt(tau) k) k), goes to theta_el.
+__global__ __launch_bounds__(256) void wango_finish_kernel(BwdArgs a, float* theta_el) {
+  const int64_t M = (int64_t)a.B * a.Tp;
+  const int HD = a.H * a.dh;
+  const int64_t id = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (id >= M * HD) return;
+  const int64_t m = id / HD;
+  const int h = (int)(id % HD) / a.dh;
+  const bool live = (int)(m % a.Tp) < a.T;
+  const float st = sqrtf(__expf(fminf(a.theta[h], kLogTauMax)));
+  const float escale = st * st > 0.f ? __expf(-st * st) : 0.f;   // e^{-tau}: far read-outs are unscaled
+  const float isd = 1.0f / sqrtf((float)a.dh);
+  const float* P = a.part;
+  const float dp = P[2 * M * HD + id] + escale * P[4 * M * HD + id];
+  const float da = P[3 * M * HD + id] + escale * P[5 * M * HD + id];
+  const float q = (float)static_cast<const __bf16*>(a.qh)[id];
+  const float k = (float)static_cast<const __bf16*>(a.kh)[id];
+  const float xq = st * q, xk = st * k;
+  const float fq = (xq > 0.f ? 1.0f : __expf(xq)) * isd;   // phi'
+  const float fk = (xk > 0.f ? 1.0f : __expf(xk)) * isd;
+  a.dq[id] = live ? P[id] + st * fq * dp : 0.f;
+  a.dk[id] = live ? P[M * HD + id] + st * fk * da : 0.f;
+  theta_el[id] = live ? 0.5f * st * (dp * fq * q + da * fk * k) : 0.f;
+}
+
 // Sums the chunk partials into dq, dk: a row of tile r takes the dq chunks
 // 0 .. r / kBwdChunkTiles and the dk chunks r / kBwdChunkTiles .. (nt - 1) /
 // kBwdChunkTiles (the chunks that hold its terms).
@@ -171,7 +248,7 @@ __global__ __launch_bounds__(256) void bwd_finish_kernel(BwdArgs a, int nch) {
 
 // Per head: dtheta from the per-item partials, dnull from delta.  One block
 // per head.
-__global__ __launch_bounds__(256) void bwd_scalars_kernel(BwdArgs a, int64_t ntri) {
+__global__ __launch_bounds__(256) void bwd_scalars_kernel(BwdArgs a, int64_t ntri, const float* theta_el) {
   __shared__ float red[2][256];
   const int h = blockIdx.x, tid = threadIdx.x;
   const float tau = __expf(fminf(a.theta[h], kLogTauMax));
@@ -179,6 +256,14 @@ __global__ __launch_bounds__(256) void bwd_scalars_kernel(BwdArgs a, int64_t ntr
   // tiles of head h: (b * H + h) * ntri + t
   for (int64_t b = 0; b < a.B; ++b)
     for (int64_t k = tid; k < ntri; k += 256) th += a.part_theta[(b * a.H + h) * ntri + k];
+  if (theta_el) {   // WANGO: the features' share, per element of head h
+    const int64_t M = (int64_t)a.B * a.Tp;
+    const int HD = a.H * a.dh;
+    for (int64_t x = tid; x < M * a.dh; x += 256) {
+      const int64_t m = x / a.dh;
+      th += theta_el[m * HD + (int64_t)h * a.dh + x % a.dh];
+    }
+  }
   if (a.null_bias) {
     const float nw = __expf(a.null_bias[h] - tau);
     const int64_t M = (int64_t)a.B * a.Tp;
@@ -211,8 +296,25 @@ BwdPlan tango_bwd_plan(int B, int Tp, int Fhp, int H) {
   p.nt = Tp / kBwdTile;
   p.ntri = (int64_t)p.nt * (p.nt + 1) / 2;
   p.nch = (int)ceil_div(p.nt, kBwdChunkTiles);
+  p.nb = 0;
+  p.nprod = 2;
   p.items_ds = (int64_t)B * H * p.ntri;
-  p.items_mm = 2 * (int64_t)B * H * p.nt * p.nch;
+  p.items_mm = p.nprod * (int64_t)B * H * p.nt * p.nch;
+  return p;
+}
+
+BwdPlan wango_bwd_plan(int B, int Tp, int Fhp, int H, int window) {
+  BwdPlan p;
+  p.FhC = Fhp + 64;   // augmented rows: delta / 1 in column Fhp
+  p.nt = Tp / kBwdTile;
+  // near tiles: every window pair (i - j < W) lies in source tiles it - nb + 1 .. it
+  p.nb = (int)ceil_div(window - 1, kBwdTile) + 1;
+  if (p.nb > kBwdChunkTiles) p.nb = kBwdChunkTiles;   // (callers keep W <= 7 * 128 + 1)
+  p.ntri = (int64_t)p.nt * p.nb;
+  p.nch = 1;
+  p.nprod = 4;
+  p.items_ds = (int64_t)B * H * p.ntri;
+  p.items_mm = p.nprod * (int64_t)B * H * p.nt;
   return p;
 }
 
@@ -220,33 +322,41 @@ hipError_t launch_tango_bwd_prep(const BwdArgs& a, const BwdPlan& p, hipStream_t
   const int64_t M = (int64_t)a.B * a.Tp;
   const int HD = a.H * a.dh;
   typedef __bf16 T;
+  t_step = "bwd_rows_kernel";
   hipLaunchKernelGGL(bwd_rows_kernel<T>, dim3((unsigned)ceil_div(M, 4), a.H), dim3(256), 0, s, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   // gates row-major from the packed forward layout
   const int64_t ng = M * a.H * p.FhC;
+  t_step = "unpack_kernel";
   hipLaunchKernelGGL(unpack_kernel<T>, dim3((unsigned)ceil_div(ng, 256)), dim3(256), 0, s,
-                     static_cast<const T*>(a.gp), a.Fp, static_cast<T*>(a.g_rm), a.H, a.Fhp, p.FhC, a.Fh, M);
+                     static_cast<const T*>(a.gp), a.Fp, static_cast<T*>(a.g_rm), a.H, a.Fhp, p.FhC, a.Fh, M,
+                     a.window > 0 ? a.Fhp : -1, a.Tp, a.T);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   // queries and keys transposed per head (the B operands of dk and dq)
   const int64_t nblk = M / 32;
   const int64_t nqk = M * HD;
+  t_step = "transpose_kernel";
   hipLaunchKernelGGL(transpose_kernel<T>, dim3((unsigned)ceil_div(nqk, 256)), dim3(256), 0, s,
                      static_cast<const T*>(a.qh), static_cast<T*>(a.qT), a.H, a.dh, a.Tp, nqk);
   if ((e = hipGetLastError()) != hipSuccess) return e;
+  t_step = "transpose_kernel";
   hipLaunchKernelGGL(transpose_kernel<T>, dim3((unsigned)ceil_div(nqk, 256)), dim3(256), 0, s,
                      static_cast<const T*>(a.kh), static_cast<T*>(a.kT), a.H, a.dh, a.Tp, nqk);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   // the reversed problem of dg: reversed queries / keys, reversed u packed
   // with the forward's head padding
   const int64_t nr = M * HD;
+  t_step = "reverse_rows_kernel";
   hipLaunchKernelGGL(reverse_rows_kernel<T>, dim3((unsigned)ceil_div(nr, 256)), dim3(256), 0, s,
                      static_cast<const T*>(a.qh), static_cast<T*>(a.q_rev), HD, a.Tp, a.T, M);
   if ((e = hipGetLastError()) != hipSuccess) return e;
+  t_step = "reverse_rows_kernel";
   hipLaunchKernelGGL(reverse_rows_kernel<T>, dim3((unsigned)ceil_div(nr, 256)), dim3(256), 0, s,
                      static_cast<const T*>(a.kh), static_cast<T*>(a.k_rev), HD, a.Tp, a.T, M);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   const int64_t nu = nblk * 4 * a.Fp;
+  t_step = "pack_kernel";
   hipLaunchKernelGGL(pack_kernel<T>, dim3((unsigned)ceil_div(nu, 256)), dim3(256), 0, s,
                      static_cast<const T*>(a.u_rm), (int64_t)a.H * p.FhC, static_cast<T*>(a.u_rev_pk), a.Fp, a.Fhp,
                      p.FhC, a.Fh, a.Tp, a.T, 1, nblk);
@@ -258,7 +368,85 @@ hipError_t launch_tango_bwd_finish(const BwdArgs& a, const BwdPlan& p, hipStream
   hipLaunchKernelGGL(bwd_finish_kernel, dim3((unsigned)ceil_div(n, 256)), dim3(256), 0, s, a, p.nch);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(bwd_scalars_kernel, dim3(a.H), dim3(256), 0, s, a, p.ntri);
+  hipLaunchKernelGGL(bwd_scalars_kernel, dim3(a.H), dim3(256), 0, s, a, p.ntri, nullptr);
+  return hipGetLastError();
+}
+
+hipError_t launch_wango_state_scan(const WStateArgs& w, bool reverse, hipStream_t s) {
+  const int64_t n = (int64_t)w.B * w.H * w.dh * w.FhC;
+  hipLaunchKernelGGL(state_scan_kernel, dim3((unsigned)ceil_div(n, 256)), dim3(256), 0, s, w, reverse ? 1 : 0);
+  return hipGetLastError();
+}
+
+hipError_t launch_wango_bwd_features(const BwdArgs& a, void* fq_perm, void* tmp_rm, const void* q_src,
+                                     const void* k_src, void* fk_pk, hipStream_t s) {
+  typedef __bf16 T;
+  const int64_t M = (int64_t)a.B * a.Tp;
+  const int HD = a.H * a.dh;
+  const int64_t n = M * HD;
+  const dim3 grid((unsigned)ceil_div(n, 256)), block(256);
+  // destination features (permuted order) of q_src, source features of k_src packed
+  t_step = "phi_kernel";
+  hipLaunchKernelGGL(phi_kernel<T>, grid, block, 0, s, static_cast<const T*>(q_src), static_cast<T*>(nullptr),
+                     static_cast<T*>(fq_perm), a.theta, a.H, a.dh, n);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  t_step = "phi_kernel";
+  hipLaunchKernelGGL(phi_kernel<T>, grid, block, 0, s, static_cast<const T*>(k_src), static_cast<T*>(tmp_rm),
+                     static_cast<T*>(nullptr), a.theta, a.H, a.dh, n);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  const int64_t nblk = M / 32, nqk = nblk * 4 * HD;
+  t_step = "pack_kernel";
+  hipLaunchKernelGGL(pack_kernel<T>, dim3((unsigned)ceil_div(nqk, 256)), dim3(256), 0, s,
+                     static_cast<const T*>(tmp_rm), (int64_t)HD, static_cast<T*>(fk_pk), HD, HD, HD, HD, a.Tp, a.T, 0,
+                     nblk);
+  return hipGetLastError();
+}
+
+hipError_t launch_wango_bwd_prep(const BwdArgs& a, const BwdPlan& p, hipStream_t s) {
+  // the TANGO prep (augmented u and g rows, q/k transposes, the reversed problem), then
+  // the features p, a row-major and transposed, and the augmented rows transposed
+  hipError_t e = launch_tango_bwd_prep(a, p, s);
+  if (e != hipSuccess) return e;
+  typedef __bf16 T;
+  const int64_t M = (int64_t)a.B * a.Tp;
+  const int HD = a.H * a.dh;
+  const int64_t n = M * HD;
+  const dim3 grid((unsigned)ceil_div(n, 256)), block(256);
+  t_step = "phi_kernel";
+  hipLaunchKernelGGL(phi_kernel<T>, grid, block, 0, s, static_cast<const T*>(a.qh), static_cast<T*>(a.p_rm),
+                     static_cast<T*>(nullptr), a.theta, a.H, a.dh, n);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  t_step = "phi_kernel";
+  hipLaunchKernelGGL(phi_kernel<T>, grid, block, 0, s, static_cast<const T*>(a.kh), static_cast<T*>(a.a_rm),
+                     static_cast<T*>(nullptr), a.theta, a.H, a.dh, n);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  t_step = "transpose_kernel";
+  hipLaunchKernelGGL(transpose_kernel<T>, grid, block, 0, s, static_cast<const T*>(a.p_rm), static_cast<T*>(a.pT),
+                     a.H, a.dh, a.Tp, n);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  t_step = "transpose_kernel";
+  hipLaunchKernelGGL(transpose_kernel<T>, grid, block, 0, s, static_cast<const T*>(a.a_rm), static_cast<T*>(a.aT),
+                     a.H, a.dh, a.Tp, n);
+  return hipGetLastError();
+}
+
+const char* bwd_last_step() { return t_step; }
+
+hipError_t launch_head_transpose(const void* src, void* dst, int B, int H, int C, int Tp, hipStream_t s) {
+  typedef __bf16 T;
+  const int64_t n = (int64_t)B * Tp * H * C;
+  hipLaunchKernelGGL(transpose_kernel<T>, dim3((unsigned)ceil_div(n, 256)), dim3(256), 0, s,
+                     static_cast<const T*>(src), static_cast<T*>(dst), H, C, Tp, n);
+  return hipGetLastError();
+}
+
+hipError_t launch_wango_bwd_finish(const BwdArgs& a, const BwdPlan& p, float* theta_el, hipStream_t s) {
+  const int64_t n = (int64_t)a.B * a.Tp * a.H * a.dh;
+  hipLaunchKernelGGL(wango_finish_kernel, dim3((unsigned)ceil_div(n, 256)), dim3(256), 0, s, a, theta_el);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(bwd_scalars_kernel, dim3(a.H), dim3(256), 0, s, a, p.ntri, theta_el);
   return hipGetLastError();
 }
 

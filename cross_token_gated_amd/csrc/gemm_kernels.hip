@@ -827,26 +827,37 @@ template <typename K> hipError_t raise_lds(K* k, size_t bytes) {
 }  // namespace
 
 // ---------------------------------------------------------------------------
-// Backward of the TANGO aggregation ("TANGO: Token-Aggregated Nonlinear Gating
-// Operators ...", §2.1 eqs. 4-5, §2.2 eq. 6): the ds tiles and the products by
-// them.  With the forward's shifted weights w_ij = e^{tau (s_ij - 1)}, u_i =
-// dgbar_i / den_i and delta_i = -u_i . gbar_i (bwd_kernels.hip),
-//     ds_ij = tau w_ij (u_i . g_j + delta_i)   (j <= i),
-//     dq_i = sum_j ds_ij k_j,   dk_j = sum_i ds_ij q_i,   dtheta = sum ds_ij s_ij.
+// Backward of the aggregation ("TANGO: Token-Aggregated Nonlinear Gating
+// Operators ...", §2.1 eqs. 4-5, §2.2 eqs. 6-10): the tiles of ds (and, for
+// WANGO, dP) and the products by them.  With the forward's shifted weights
+// w_ij = e^{tau (s_ij - 1)}, u_i = dgbar_i / den_i and delta_i = -u_i . gbar_i
+// (bwd_kernels.hip) and dm_ij = u_i . g_j + delta_i,
+//     ds_ij = tau w_ij dm_ij        (TANGO: j <= i; WANGO: the window i-W < j <= i),
+//     dP_ij = e^{-tau} dm_ij        (WANGO: older pairs j <= i - W; dP = dL/d(p_i . a_j)),
+//     dq_i = sum_j ds_ij k_j, dk_j = sum_i ds_ij q_i, dp_i = sum_j dP_ij a_j, da_j = sum_i dP_ij p_i,
+//     dtheta += sum ds_ij s_ij.
 //
-// KD: one 128 x 128 tile of ds (destination rows i of tile it, source rows j
-// of tile jt <= it, one sequence and head) per workgroup.  S = Q_i K_j^T
-// (k = d_h) and dW = U_i G_j^T (k = the head's gate columns) run one after the
-// other on the main loop above, into two accumulator sets.  The tile is
-// stored in bf16 twice: transposed (rows j, for dk) straight from the
-// accumulators, whose lanes hold 4 consecutive rows i of one column j, and by
-// rows (for dq) through LDS.  The workgroup also sums ds * s for dtheta.
+// KD: one 128 x 128 tile (destination rows i of tile it, source rows j of
+// tile jt) of one sequence and head per workgroup: TANGO every jt <= it,
+// WANGO the nb "near" tiles jt = it - nb + 1 .. it that hold the window.
+// S = Q_i K_j^T (k = d_h) and dW = U_i G_j^T (k = the head's gate columns)
+// run one after the other on the main loop above, into two accumulator sets
+// (WANGO's u and g rows carry delta and 1 in one extra column, so dW is dm).
+// Each tile is stored in bf16 twice: transposed (rows j, for dk / da)
+// straight from the accumulators, whose lanes hold 4 consecutive rows i of
+// one column j, and by rows (for dq / dp) through LDS.  The workgroup also
+// sums ds * s for dtheta.
 //
-// KM: dq (DIR 0) or dk (DIR 1) for one 128-row tile r and one chunk of
-// kBwdChunkTiles ds tiles along the sum: A = the rows of the ds tiles (DIR 0:
-// tiles (r, jt), jt <= r; DIR 1: the transposed tiles (it, r), it >= r), B =
-// the keys (queries) transposed per head, k = the summed position.  Each
-// chunk writes a float32 partial, which bwd_finish_kernel adds up.
+// KM: one product for one 128-row tile r and one chunk of kBwdChunkTiles
+// tiles along the sum: A = the rows of the tiles ((r, jt) by rows for dq / dp,
+// (it, r) transposed for dk / da), B = the keys, queries or features
+// transposed per head, k = the summed position.  Each chunk writes a float32
+// partial, which the finish kernels add up.
+//
+// KW (WANGO older prefix, far tiles): per-tile sums a_j g^_j^T and p_i u^_i^T
+// ([d_h] x [FhC]), their shifted prefix / suffix (bwd_kernels-side scan), and
+// the read-outs dp_i += S_it u^_i, da_j += R_jt g^_j (e^{-tau} applied in the
+// finish), all on the same main loop.
 // ---------------------------------------------------------------------------
 namespace {
 
@@ -860,9 +871,47 @@ constexpr size_t kDsLds = ops_bytes<DsCfg, bf16>() > kStageBytes ? ops_bytes<DsC
 constexpr float kLogTauMaxB = 2.995732273553991f;   // log 20: tau = exp(min(theta, log 20))
 
 __host__ __device__ __forceinline__ int64_t tri_index(int i, int j) { return (int64_t)i * (i + 1) / 2 + j; }
+// Index of tile (it, jt) among a (sequence, head)'s stored tiles.
+template <bool W>
+__device__ __forceinline__ int64_t tile_index(int it, int jt, int nb) {
+  return W ? (int64_t)it * nb + (jt - it + nb - 1) : tri_index(it, jt);
+}
 
+// Stores a tile of values v(i, j) (this lane: rows r0 + 0..3 of column c, per
+// accumulator block) transposed straight from the registers and by rows
+// through LDS.
+template <class CF, class Fn>
+__device__ __forceinline__ void store_tile(bf16* dst_r, bf16* dst_t, bf16* st, Fn value) {
+  const int tid = threadIdx.x, lane = tid & 63, col = lane & 15, grp = lane >> 4;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wr = wave / CF::WN, wc = wave % CF::WN;
+#pragma unroll
+  for (int i = 0; i < CF::IB; ++i) {
+    const int r0 = wr * CF::WTM + i * 16 + grp * 4;
+#pragma unroll
+    for (int j = 0; j < CF::JB; ++j) {
+      const int c = wc * CF::WTN + j * 16 + col;
+      bf16x4 q4;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        q4[r] = (bf16)value(i, j, r, r0 + r, c);
+        st[(r0 + r) * kDsStride + c] = q4[r];
+      }
+      *reinterpret_cast<bf16x4*>(dst_t + c * kBwdTile + r0) = q4;
+    }
+  }
+  __syncthreads();
+  for (int q = tid; q < kTileElems / 8; q += kThreads) {
+    const int row = q >> 4, c8 = (q & 15) * 8;
+    *reinterpret_cast<u32x4*>(dst_r + row * kBwdTile + c8) =
+        *reinterpret_cast<const u32x4*>(st + row * kDsStride + c8);
+  }
+  __syncthreads();   // st is reused
+}
+
+template <bool W>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2)))
-void ds_kernel(BwdArgs a, int64_t ntri, int64_t items) {
+void ds_kernel(BwdArgs a, int64_t ntiles, int64_t items) {
   using CF = DsCfg;
   typedef bf16 T;
   constexpr int PA = tile_chunks<CF, T>(CF::BM) / 4, PB = tile_chunks<CF, T>(CF::BN) / 4;
@@ -873,12 +922,22 @@ void ds_kernel(BwdArgs a, int64_t ntri, int64_t items) {
   const int64_t q8 = gridDim.x / 8;
   const int64_t item = (int64_t)(blockIdx.x % 8) * q8 + blockIdx.x / 8;
   if (item >= items) return;
-  const int64_t bh = item / ntri;
-  const int64_t t = item - bh * ntri;
-  int it = (int)((sqrt(8.0 * (double)t + 1.0) - 1.0) * 0.5);
-  while (tri_index(it + 1, 0) <= t) ++it;
-  while (tri_index(it, 0) > t) --it;
-  const int jt = (int)(t - tri_index(it, 0));
+  const int64_t bh = item / ntiles;
+  const int64_t t = item - bh * ntiles;
+  int it, jt;
+  if (W) {
+    it = (int)(t / a.nb);
+    jt = it - a.nb + 1 + (int)(t % a.nb);
+    if (jt < 0) {         // before the first tile (workgroup-uniform)
+      if (threadIdx.x == 0) a.part_theta[item] = 0.f;
+      return;
+    }
+  } else {
+    it = (int)((sqrt(8.0 * (double)t + 1.0) - 1.0) * 0.5);
+    while (tri_index(it + 1, 0) <= t) ++it;
+    while (tri_index(it, 0) > t) --it;
+    jt = (int)(t - tri_index(it, 0));
+  }
   const int h = (int)(bh % a.H);
   const int64_t mseq = (bh / a.H) * a.Tp;
   const int HD = a.H * a.dh, tid = threadIdx.x;
@@ -921,62 +980,58 @@ void ds_kernel(BwdArgs a, int64_t ntri, int64_t items) {
   }
   gemm_mainloop<CF, T>(accW, lds, a.FhC / CF::BK, sa, sb);
 
-  // ds, its transposed store, the staged row-major copy and dtheta
+  // ds (and dP), their stores and dtheta
   const float tau = __expf(fminf(a.theta[h], kLogTauMaxB));
   const float ktau = tau * kLog2e;
   const float* delta = a.delta + (int64_t)h * a.B * a.Tp;
-  const int lane = tid & 63, col = lane & 15, grp = lane >> 4;
+  const int lane = tid & 63, grp = lane >> 4;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int wr = wave / CF::WN, wc = wave % CF::WN;
-  T* st = reinterpret_cast<T*>(smem);
-  T* dst_t = static_cast<T*>(a.ds_t) + item * (int64_t)kTileElems;
+  const int wr = wave / CF::WN;
+  float dl[CF::IB][4];   // TANGO: delta of this lane's rows (WANGO: already inside dW)
+#pragma unroll
+  for (int i = 0; i < CF::IB; ++i)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) dl[i][r] = W ? 0.f : delta[ri + wr * CF::WTM + i * 16 + grp * 4 + r];
+  const int di = (it - jt) * kBwdTile;   // i - j = di + (row - col)
   float th = 0.f;
-#pragma unroll
-  for (int i = 0; i < CF::IB; ++i) {
-    const int r0 = wr * CF::WTM + i * 16 + grp * 4;   // this lane's rows r0 .. r0 + 3
-    float dl[4];
-#pragma unroll
-    for (int r = 0; r < 4; ++r) dl[r] = delta[ri + r0 + r];
-#pragma unroll
-    for (int j = 0; j < CF::JB; ++j) {
-      const int c = wc * CF::WTN + j * 16 + col;
-      bf16x4 q4;
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const float sv = accS[i][j][r];
-        const float w = __builtin_amdgcn_exp2f(ktau * (sv - 1.0f));
-        const bool valid = jt < it || c <= r0 + r;   // source j <= destination i
-        const float v = valid ? tau * w * (accW[i][j][r] + dl[r]) : 0.f;
-        th += v * sv;
-        q4[r] = (T)v;
-        st[(r0 + r) * kDsStride + c] = q4[r];
-      }
-      *reinterpret_cast<bf16x4*>(dst_t + c * kBwdTile + r0) = q4;
-    }
+  auto ds_of = [&](int i, int j, int r, int row, int c) {
+    const float sv = accS[i][j][r];
+    const float w = __builtin_amdgcn_exp2f(ktau * (sv - 1.0f));
+    const int ij = di + row - c;   // i - j
+    const bool valid = W ? (ij >= 0 && ij < a.window) : ij >= 0;
+    const float v = valid ? tau * w * (accW[i][j][r] + dl[i][r]) : 0.f;
+    th += v * sv;
+    return v;
+  };
+  const int64_t tix = bh * ntiles + (W ? tile_index<true>(it, jt, a.nb) : t);
+  T* st = reinterpret_cast<T*>(smem);
+  store_tile<CF>(static_cast<T*>(a.ds_rm) + tix * kTileElems, static_cast<T*>(a.ds_t) + tix * kTileElems, st,
+                 ds_of);
+  if (W) {
+    const float escale = __expf(-tau);
+    auto dp_of = [&](int i, int j, int r, int row, int c) {
+      return di + row - c >= a.window ? escale * accW[i][j][r] : 0.f;
+    };
+    store_tile<CF>(static_cast<T*>(a.dp_rm) + tix * kTileElems, static_cast<T*>(a.dp_t) + tix * kTileElems, st,
+                   dp_of);
   }
   th = wave_sum(th);
   if (lane == 0) red[wave] = th;
   __syncthreads();
-  if (tid == 0) a.part_theta[item] = red[0] + red[1] + red[2] + red[3];
-  T* dst_r = static_cast<T*>(a.ds_rm) + item * (int64_t)kTileElems;
-  for (int q = tid; q < kTileElems / 8; q += kThreads) {
-    const int row = q >> 4, c8 = (q & 15) * 8;
-    *reinterpret_cast<u32x4*>(dst_r + row * kBwdTile + c8) =
-        *reinterpret_cast<const u32x4*>(st + row * kDsStride + c8);
-  }
+  if (tid == 0) a.part_theta[bh * ntiles + t] = red[0] + red[1] + red[2] + red[3];
 }
 
-// A operand of KM: pieces of the rows of a run of ds tiles along k.
-template <int DIR, int P> struct DsRowSource {
+// A operand of KM: pieces of the rows of a run of tiles along k.
+template <int DIR, bool W, int P> struct DsRowSource {
   struct raw {
     u32x4 v;
   };
   const bf16* tiles;   // the (sequence, head)'s first tile
   int off[P];          // row * 128 + piece column of each pass
-  int r, kbase;
+  int r, kbase, nb;
   __device__ __forceinline__ void fetch(raw& x, int p, int k0) const {
     const int k = kbase + k0, kt = k >> 7;
-    const int64_t tile = DIR == 0 ? tri_index(r, kt) : tri_index(kt, r);
+    const int64_t tile = DIR == 0 ? tile_index<W>(r, kt, nb) : tile_index<W>(kt, r, nb);
     x.v = *reinterpret_cast<const u32x4*>(tiles + tile * kTileElems + off[p] + (k & (kBwdTile - 1)));
   }
   __device__ __forceinline__ Parts<1> convert(const raw& x, int) const {
@@ -986,34 +1041,41 @@ template <int DIR, int P> struct DsRowSource {
   }
 };
 
-template <int DIR, int DH>
-__device__ __forceinline__ void dsmm_job(const BwdArgs& a, int64_t ntri, int nch, int64_t bh, int r, int c,
+// Product `prod` (0 dq, 1 dk, 2 dp, 3 da) for row tile r, chunk c.
+template <int PROD, bool W, int DH>
+__device__ __forceinline__ void dsmm_job(const BwdArgs& a, int64_t ntiles, int nch, int64_t bh, int r, int c,
                                          bf16* lds) {
   using CF = MmCfg<DH>;
   typedef bf16 T;
+  constexpr int DIR = PROD & 1;
   constexpr int PA = tile_chunks<CF, T>(CF::BM) / 4, PB = tile_chunks<CF, T>(CF::BN) / 4;
   const int nt = a.Tp / kBwdTile;
-  // k tiles of this chunk: DIR 0 jt in [0, r], DIR 1 it in [r, nt)
+  // k tiles of this chunk: DIR 0 jt <= r (WANGO jt > r - nb), DIR 1 it >= r (WANGO it < r + nb)
   int first = c * kBwdChunkTiles, last = first + kBwdChunkTiles - 1;
   if (DIR == 0) {
     last = min(last, r);
+    if (W) first = max(first, r - a.nb + 1);
   } else {
     first = max(first, r);
     last = min(last, nt - 1);
+    if (W) last = min(last, r + a.nb - 1);
   }
   if (first > last) return;   // workgroup-uniform
   const int tid = threadIdx.x;
-  DsRowSource<DIR, PA> sa;
-  sa.tiles = static_cast<const T*>(DIR == 0 ? a.ds_rm : a.ds_t) + bh * ntri * kTileElems;
+  DsRowSource<DIR, W, PA> sa;
+  const void* tiles = PROD == 0 ? a.ds_rm : PROD == 1 ? a.ds_t : PROD == 2 ? a.dp_rm : a.dp_t;
+  sa.tiles = static_cast<const T*>(tiles) + bh * ntiles * kTileElems;
   sa.r = r;
   sa.kbase = first * kBwdTile;
+  sa.nb = a.nb;
 #pragma unroll
   for (int p = 0; p < PA; ++p) {
     const PiecePos<CF, T> pp = piece_pos<CF, T>(tid, p);
     sa.off[p] = pp.row * kBwdTile + pp.kp * piece_elems<T>();
   }
   RowSource<T, PB> sb;
-  const T* xT = static_cast<const T*>(DIR == 0 ? a.kT : a.qT) + bh * DH * (int64_t)a.Tp;
+  const void* bsrc = PROD == 0 ? a.kT : PROD == 1 ? a.qT : PROD == 2 ? a.aT : a.pT;
+  const T* xT = static_cast<const T*>(bsrc) + bh * DH * (int64_t)a.Tp;
 #pragma unroll
   for (int p = 0; p < PB; ++p) {
     const PiecePos<CF, T> pp = piece_pos<CF, T>(tid, p);
@@ -1030,7 +1092,7 @@ __device__ __forceinline__ void dsmm_job(const BwdArgs& a, int64_t ntri, int nch
   const int64_t M = (int64_t)a.B * a.Tp;
   const int HD = a.H * DH, h = (int)(bh % a.H);
   const int64_t row0 = (bh / a.H) * a.Tp + (int64_t)r * kBwdTile;
-  float* out = a.part + ((int64_t)DIR * nch + c) * M * HD + row0 * HD + h * DH;
+  float* out = a.part + ((int64_t)PROD * nch + c) * M * HD + row0 * HD + h * DH;
   const int lane = tid & 63, col = lane & 15, grp = lane >> 4;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wr = wave / CF::WN, wc = wave % CF::WN;
@@ -1045,24 +1107,155 @@ __device__ __forceinline__ void dsmm_job(const BwdArgs& a, int64_t ntri, int nch
     }
 }
 
-template <int DH>
+template <bool W, int DH>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2)))
-void dsmm_kernel(BwdArgs a, int64_t ntri, int nch, int64_t items) {
+void dsmm_kernel(BwdArgs a, int64_t ntiles, int nch, int64_t items) {
   __shared__ __align__(16) unsigned char smem[ops_bytes<MmCfg<DH>, bf16>()];
   const int64_t q8 = gridDim.x / 8;
   const int64_t item = (int64_t)(blockIdx.x % 8) * q8 + blockIdx.x / 8;
   if (item >= items) return;
   const int nt = a.Tp / kBwdTile;
-  const int64_t per_dir = (int64_t)a.B * a.H * nt * nch;
-  const int dir = (int)(item / per_dir);
-  int64_t rem = item - dir * per_dir;
+  const int64_t per_prod = (int64_t)a.B * a.H * nt * nch;
+  const int prod = (int)(item / per_prod);
+  int64_t rem = item - prod * per_prod;
   const int c = (int)(rem % nch);
   rem /= nch;
   const int r = (int)(rem % nt);
   const int64_t bh = rem / nt;
   bf16* lds = reinterpret_cast<bf16*>(smem);
-  if (dir == 0) dsmm_job<0, DH>(a, ntri, nch, bh, r, c, lds);
-  else dsmm_job<1, DH>(a, ntri, nch, bh, r, c, lds);
+  switch (prod) {
+    case 0: dsmm_job<0, W, DH>(a, ntiles, nch, bh, r, c, lds); break;
+    case 1: dsmm_job<1, W, DH>(a, ntiles, nch, bh, r, c, lds); break;
+    case 2: if (W) dsmm_job<2, W, DH>(a, ntiles, nch, bh, r, c, lds); break;
+    default: if (W) dsmm_job<3, W, DH>(a, ntiles, nch, bh, r, c, lds); break;
+  }
+}
+
+// KW sums: per tile t of (sequence, head) bh, tsum[e][f] = sum_{rows of t} aT[e][row] xT[f][row]:
+// A = aT rows e (d_h of them, rows past d_h zero), B = xT rows f, k = the tile's 128 positions.
+using StCfg = TileCfg<64, 128, 32, 2, 2, 3, 1>;
+template <int P> struct GuardedRows {   // A rows with a validity flag (rows past the end read zeros)
+  struct raw {
+    u32x4 v;
+  };
+  const bf16* ptr[P];
+  bool ok[P];
+  __device__ __forceinline__ void fetch(raw& x, int p, int k0) const {
+    x.v = *reinterpret_cast<const u32x4*>(ptr[p] + k0);
+  }
+  __device__ __forceinline__ Parts<1> convert(const raw& x, int p) const {
+    Parts<1> o;
+    o.p[0] = ok[p] ? x.v : u32x4{0u, 0u, 0u, 0u};
+    return o;
+  }
+};
+
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2)))
+void state_sums_kernel(WStateArgs w) {
+  using CF = StCfg;
+  typedef bf16 T;
+  constexpr int PA = tile_chunks<CF, T>(CF::BM) / 4, PB = tile_chunks<CF, T>(CF::BN) / 4;
+  __shared__ __align__(16) unsigned char smem[ops_bytes<CF, T>()];
+  const int nmt = (w.dh + CF::BM - 1) / CF::BM, nnt = (w.FhC + CF::BN - 1) / CF::BN;
+  int64_t id = blockIdx.x;
+  const int nn = (int)(id % nnt);
+  id /= nnt;
+  const int mm = (int)(id % nmt);
+  id /= nmt;
+  const int t = (int)(id % w.nt);
+  const int64_t bh = id / w.nt;
+  const int tid = threadIdx.x;
+  const T* aT = static_cast<const T*>(w.aT) + bh * w.dh * (int64_t)w.Tp + (int64_t)t * kBwdTile;
+  const T* xT = static_cast<const T*>(w.xT) + bh * w.FhC * (int64_t)w.Tp + (int64_t)t * kBwdTile;
+  GuardedRows<PA> sa;
+#pragma unroll
+  for (int p = 0; p < PA; ++p) {
+    const PiecePos<CF, T> pp = piece_pos<CF, T>(tid, p);
+    const int e = mm * CF::BM + pp.row;
+    sa.ptr[p] = aT + (int64_t)(e < w.dh ? e : 0) * w.Tp + pp.kp * piece_elems<T>();
+    sa.ok[p] = e < w.dh;
+  }
+  RowSource<T, PB> sb;
+#pragma unroll
+  for (int p = 0; p < PB; ++p) {
+    const PiecePos<CF, T> pp = piece_pos<CF, T>(tid, p);
+    const int f = nn * CF::BN + pp.row;
+    sb.ptr[p] = xT + (int64_t)(f < w.FhC ? f : 0) * w.Tp + pp.kp * piece_elems<T>();
+    sb.ok[p] = f < w.FhC;
+  }
+  f32x4 acc[CF::IB][CF::JB];
+#pragma unroll
+  for (int i = 0; i < CF::IB; ++i)
+#pragma unroll
+    for (int j = 0; j < CF::JB; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+  gemm_mainloop<CF, T>(acc, reinterpret_cast<T*>(smem), kBwdTile / CF::BK, sa, sb);
+  float* out = w.tsum + ((bh * w.nt + t) * w.dh) * (int64_t)w.FhC;
+  const int lane = tid & 63, col = lane & 15, grp = lane >> 4;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wr = wave / CF::WN, wc = wave % CF::WN;
+#pragma unroll
+  for (int i = 0; i < CF::IB; ++i)
+#pragma unroll
+    for (int j = 0; j < CF::JB; ++j) {
+      const int f = nn * CF::BN + wc * CF::WTN + j * 16 + col;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int e = mm * CF::BM + wr * CF::WTM + i * 16 + grp * 4 + q;
+        if (e < w.dh && f < w.FhC) out[(int64_t)e * w.FhC + f] = acc[i][j][q];
+      }
+    }
+}
+
+// KW read-out: for tile t of (sequence, head) bh, out[row][e] = sum_f rows[row][f] state_t[e][f]
+// (S: rows = augmented u of destination tile t; R: augmented g of source tile t).
+template <int DH>
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2)))
+void state_readout_kernel(WStateArgs w) {
+  using CF = MmCfg<DH>;
+  typedef bf16 T;
+  constexpr int PA = tile_chunks<CF, T>(CF::BM) / 4, PB = tile_chunks<CF, T>(CF::BN) / 4;
+  __shared__ __align__(16) unsigned char smem[ops_bytes<CF, T>()];
+  const int64_t id = blockIdx.x;
+  const int t = (int)(id % w.nt);
+  const int64_t bh = id / w.nt;
+  const int h = (int)(bh % w.H);
+  const int64_t row0 = (bh / w.H) * w.Tp + (int64_t)t * kBwdTile;
+  const int tid = threadIdx.x;
+  PartsSource<T, PA, 1> sa;
+  sa.part_stride = 0;
+#pragma unroll
+  for (int p = 0; p < PA; ++p) {
+    const PiecePos<CF, T> pp = piece_pos<CF, T>(tid, p);
+    sa.ptr[p] = static_cast<const T*>(w.rows) + ((row0 + pp.row) * w.H + h) * w.FhC + pp.kp * piece_elems<T>();
+  }
+  const T* st = static_cast<const T*>(w.state) + ((bh * w.nt + t) * DH) * (int64_t)w.FhC;
+  RowSource<T, PB> sb;
+#pragma unroll
+  for (int p = 0; p < PB; ++p) {
+    const PiecePos<CF, T> pp = piece_pos<CF, T>(tid, p);
+    sb.ptr[p] = st + (int64_t)(pp.row % DH) * w.FhC + pp.kp * piece_elems<T>();
+    sb.ok[p] = pp.row < DH;
+  }
+  f32x4 acc[CF::IB][CF::JB];
+#pragma unroll
+  for (int i = 0; i < CF::IB; ++i)
+#pragma unroll
+    for (int j = 0; j < CF::JB; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+  gemm_mainloop<CF, T>(acc, reinterpret_cast<T*>(smem), w.FhC / CF::BK, sa, sb);
+  const int HD = w.H * DH;
+  float* out = w.out + row0 * HD + h * DH;
+  const int lane = tid & 63, col = lane & 15, grp = lane >> 4;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wr = wave / CF::WN, wc = wave % CF::WN;
+#pragma unroll
+  for (int i = 0; i < CF::IB; ++i)
+#pragma unroll
+    for (int j = 0; j < CF::JB; ++j) {
+      const int e = wc * CF::WTN + j * 16 + col;
+      if (e < DH)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) out[(int64_t)(wr * CF::WTM + i * 16 + grp * 4 + q) * HD + e] = acc[i][j][q];
+    }
 }
 
 }  // namespace
@@ -1070,17 +1263,45 @@ void dsmm_kernel(BwdArgs a, int64_t ntri, int nch, int64_t items) {
 hipError_t launch_tango_ds(const BwdArgs& a, const BwdPlan& p, hipStream_t s) {
   if (a.dh % 32 != 0 || a.FhC % 32 != 0 || a.Tp % kBwdTile != 0) return hipErrorInvalidValue;
   const int64_t q8 = ceil_div(p.items_ds, 8);
-  hipLaunchKernelGGL(ds_kernel, dim3((unsigned)(8 * q8)), dim3(kThreads), 0, s, a, p.ntri, p.items_ds);
+  if (a.window > 0)
+    hipLaunchKernelGGL(ds_kernel<true>, dim3((unsigned)(8 * q8)), dim3(kThreads), 0, s, a, p.ntri, p.items_ds);
+  else
+    hipLaunchKernelGGL(ds_kernel<false>, dim3((unsigned)(8 * q8)), dim3(kThreads), 0, s, a, p.ntri, p.items_ds);
+  return hipGetLastError();
+}
+
+template <bool W>
+static hipError_t launch_dsmm_w(const BwdArgs& a, const BwdPlan& p, hipStream_t s) {
+  const int64_t q8 = ceil_div(p.items_mm, 8);
+  dim3 grid((unsigned)(8 * q8)), block(kThreads);
+  switch (a.dh) {
+    case 32: hipLaunchKernelGGL((dsmm_kernel<W, 32>), grid, block, 0, s, a, p.ntri, p.nch, p.items_mm); break;
+    case 64: hipLaunchKernelGGL((dsmm_kernel<W, 64>), grid, block, 0, s, a, p.ntri, p.nch, p.items_mm); break;
+    case 128: hipLaunchKernelGGL((dsmm_kernel<W, 128>), grid, block, 0, s, a, p.ntri, p.nch, p.items_mm); break;
+    default: return hipErrorInvalidValue;
+  }
   return hipGetLastError();
 }
 
 hipError_t launch_tango_dsmm(const BwdArgs& a, const BwdPlan& p, hipStream_t s) {
-  const int64_t q8 = ceil_div(p.items_mm, 8);
-  dim3 grid((unsigned)(8 * q8)), block(kThreads);
-  switch (a.dh) {
-    case 32: hipLaunchKernelGGL(dsmm_kernel<32>, grid, block, 0, s, a, p.ntri, p.nch, p.items_mm); break;
-    case 64: hipLaunchKernelGGL(dsmm_kernel<64>, grid, block, 0, s, a, p.ntri, p.nch, p.items_mm); break;
-    case 128: hipLaunchKernelGGL(dsmm_kernel<128>, grid, block, 0, s, a, p.ntri, p.nch, p.items_mm); break;
+  return a.window > 0 ? launch_dsmm_w<true>(a, p, s) : launch_dsmm_w<false>(a, p, s);
+}
+
+hipError_t launch_wango_state_sums(const WStateArgs& w, hipStream_t s) {
+  using CF = StCfg;
+  if (w.FhC % CF::BK != 0) return hipErrorInvalidValue;
+  const int64_t n = (int64_t)w.B * w.H * w.nt * ceil_div(w.dh, CF::BM) * ceil_div(w.FhC, CF::BN);
+  hipLaunchKernelGGL(state_sums_kernel, dim3((unsigned)n), dim3(kThreads), 0, s, w);
+  return hipGetLastError();
+}
+
+hipError_t launch_wango_state_readout(const WStateArgs& w, bool, hipStream_t s) {
+  if (w.FhC % 32 != 0) return hipErrorInvalidValue;
+  const dim3 grid((unsigned)((int64_t)w.B * w.H * w.nt)), block(kThreads);
+  switch (w.dh) {
+    case 32: hipLaunchKernelGGL(state_readout_kernel<32>, grid, block, 0, s, w); break;
+    case 64: hipLaunchKernelGGL(state_readout_kernel<64>, grid, block, 0, s, w); break;
+    case 128: hipLaunchKernelGGL(state_readout_kernel<128>, grid, block, 0, s, w); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();

@@ -64,7 +64,7 @@ struct AggArgs {
   int Fo, Fho;             // gbar: [B*Tp, Fo] with Fho columns per head (not padded)
   int chunk;               // WANGO: n_old holds the state read-out at chunk boundaries
   int split;               // 1: split the long tiles in two (last finisher combines)
-  // TANGO options (all off when zero / null):
+  // options (all off when zero / null):
   float* den_out;          // [B*Tp, H]: the ratio's denominator, e^{-tau} units (rows < T)
   int num_only;            // 1: write the numerator alone (no row sums, no null, no division)
   int rev_out;             // 1: row i of a sequence is stored at row T - 1 - i (rows < T only)
@@ -145,10 +145,21 @@ struct BwdArgs {
   void* k_rev;             // keys, reversed
   void* u_rev_pk;          // packed reversed u, [B*Tp/32][4][Fp][8]
   float* delta;            // [H][B*Tp] float32
-  void* ds_rm;             // [B*H][ntri][128][128] ds tiles, rows i (destinations)
-  void* ds_t;              // [B*H][ntri][128][128] ds tiles transposed, rows j (sources)
-  float* part;             // [2][nch][B*Tp][H*dh] float32 chunk partials of dq (0) and dk (1)
-  float* part_theta;       // [B*H*ntri] float32: sum of ds * s per tile
+  void* ds_rm;             // [B*H][ntiles][128][128] ds tiles, rows i (destinations)
+  void* ds_t;              // [B*H][ntiles][128][128] ds tiles transposed, rows j (sources)
+  float* part;             // TANGO: [2][nch][B*Tp][H*dh] float32 chunk partials of dq (0) and dk (1);
+                           // WANGO: [6][B*Tp][H*dh]: dq, dk (window), dp, da (near older pairs),
+                           // dp, da (far older pairs, from the prefix states)
+  float* part_theta;       // [B*H*ntiles] float32: sum of ds * s per tile
+  // WANGO only (window > 0)
+  int window;              // W
+  int nb;                  // near tiles per row tile: source tiles it - nb + 1 .. it
+  void* dp_rm;             // [B*H][ntiles][128][128] dP tiles (older pairs), rows i
+  void* dp_t;              // transposed, rows j
+  void* pT;                // [B][H][dh][Tp] phi(sqrt(tau) q), transposed per head
+  void* aT;                // [B][H][dh][Tp] phi(sqrt(tau) k)
+  void* p_rm;              // [B*Tp][H*dh] phi(sqrt(tau) q), row-major
+  void* a_rm;              // phi(sqrt(tau) k)
   // outputs
   float* dq;               // [B*Tp, H*dh] float32 (zero on rows past the end)
   float* dk;               // [B*Tp, H*dh]
@@ -157,7 +168,8 @@ struct BwdArgs {
   int B, T, Tp, H, dh;
   int F, Fh;               // gate columns (unpadded) in all and per head
   int Fhp, Fp;             // head-padded width of the packed gates, H * Fhp
-  int FhC;                 // head width of u_rm / g_rm (Fhp: a multiple of 64)
+  int FhC;                 // head width of u_rm / g_rm: TANGO Fhp; WANGO Fhp + 64, with delta (u)
+                           // and 1 (g) in column Fhp, so that u . g over it is u . g + delta
 };
 
 constexpr int kBwdTile = 128;        // rows of a ds tile
@@ -166,17 +178,43 @@ constexpr int kBwdChunkTiles = 8;    // ds tiles per chunk of the dq / dk sums
 struct BwdPlan {
   int FhC;
   int nt;              // 128-row tiles per sequence
-  int64_t ntri;        // ds tiles per (sequence, head): nt (nt + 1) / 2
-  int nch;             // chunks of kBwdChunkTiles tiles along a sum
+  int64_t ntri;        // ds tiles per (sequence, head): TANGO nt (nt + 1) / 2, WANGO nt * nb
+  int nch;             // chunks of kBwdChunkTiles tiles along a sum (WANGO: 1)
+  int nb;              // WANGO: near tiles per row tile (0 for TANGO)
+  int nprod;           // products of the tiles: 2 (dq, dk), WANGO 4 (and dp, da)
   int64_t items_ds;    // B * H * ntri
-  int64_t items_mm;    // 2 * B * H * nt * nch (some empty)
+  int64_t items_mm;    // nprod * B * H * nt * nch (some empty)
 };
 BwdPlan tango_bwd_plan(int B, int Tp, int Fhp, int H);
+BwdPlan wango_bwd_plan(int B, int Tp, int Fhp, int H, int window);
 hipError_t launch_tango_bwd_prep(const BwdArgs& a, const BwdPlan& p, hipStream_t s);
 // ds tiles and their products (gemm_kernels.hip)
 hipError_t launch_tango_ds(const BwdArgs& a, const BwdPlan& p, hipStream_t s);
 hipError_t launch_tango_dsmm(const BwdArgs& a, const BwdPlan& p, hipStream_t s);
 hipError_t launch_tango_bwd_finish(const BwdArgs& a, const BwdPlan& p, hipStream_t s);
+
+// WANGO: the older-prefix states and their read-outs (gemm_kernels.hip), the
+// feature layouts and the finish (bwd_kernels.hip)
+struct WStateArgs {
+  const void* aT;      // [B*H][dh][Tp] source features (S) / destination features (R)
+  const void* xT;      // [B*H][FhC][Tp] augmented g (S) / u (R), transposed
+  float* tsum;         // [B*H][nt][dh][FhC] per-tile sums
+  void* state;         // [B*H][nt][dh][FhC] bf16: S exclusive prefix / R suffix from tile t + nb
+  const void* rows;    // [B*Tp][H][FhC] augmented u (S read-out) / g (R read-out)
+  float* out;          // [B*Tp][H*dh] read-out partial
+  int B, H, dh, Tp, FhC, nt, nb;
+};
+hipError_t launch_wango_state_sums(const WStateArgs& w, hipStream_t s);
+hipError_t launch_wango_state_readout(const WStateArgs& w, bool reverse, hipStream_t s);
+hipError_t launch_wango_state_scan(const WStateArgs& w, bool reverse, hipStream_t s);
+hipError_t launch_wango_bwd_features(const BwdArgs& a, void* fq_perm, void* tmp_rm, const void* q_src,
+                                     const void* k_src, void* fk_pk, hipStream_t s);
+hipError_t launch_wango_bwd_finish(const BwdArgs& a, const BwdPlan& p, float* theta_el, hipStream_t s);
+hipError_t launch_wango_bwd_prep(const BwdArgs& a, const BwdPlan& p, hipStream_t s);
+// Name of the kernel the backward prep launched last on this thread.
+const char* bwd_last_step();
+// row-major [B*Tp][H*C] -> [B][H][C][Tp]
+hipError_t launch_head_transpose(const void* src, void* dst, int B, int H, int C, int Tp, hipStream_t s);
 
 // ---- autoregressive decode -------------------------------------------------
 

@@ -787,6 +787,290 @@ int tango_aggregate_bwd(const tango_shape_t* shape, const float* theta, const fl
   });
 }
 
+}  // extern "C"
+
+namespace {
+
+constexpr int32_t kWangoBwdMaxWindow = 7 * kBwdTile + 1;   // near tiles of one product chunk
+
+int check_wango_bwd(const tango_shape_t* s, int32_t window, int32_t chunk) {
+  int rc = check_bwd_shape(s);
+  if (rc) return rc;
+  if ((rc = check_wango(s, window, s->head_dim, chunk))) return rc;
+  if (window > kWangoBwdMaxWindow)
+    return fail(TANGO_ERR_UNSUPPORTED, "window %d: the WANGO backward covers windows up to %d", window,
+                kWangoBwdMaxWindow);
+  return TANGO_OK;
+}
+
+// Scratch of the WANGO forward-train call: features, then the scan's.
+struct WFwdLayout {
+  size_t fq, fk, tmp, n_old, z_old, seg_state, seg_z, total;
+  ScanPlan scan;
+};
+WFwdLayout make_wfwd_layout(const tango_shape_t* s, int32_t chunk) {
+  WFwdLayout L{};
+  const int64_t M = (int64_t)s->batch * pad_rows(s->seq_len);
+  const int64_t F = gate_pad(s, true), HD = (int64_t)s->n_heads * s->head_dim;
+  size_t off = 0;
+  auto take = [&](size_t bytes) {
+    const size_t o = off;
+    off = align256(off + bytes);
+    return o;
+  };
+  L.scan = wango_scan_plan(s->batch, (int)pad_rows(s->seq_len), (int)F, s->n_heads, chunk);
+  L.fq = take((size_t)M * HD * 2);
+  L.fk = take((size_t)M * HD * 2);
+  L.tmp = take((size_t)M * HD * 2);
+  L.n_old = take((size_t)M * F * sizeof(float));
+  L.z_old = take((size_t)M * s->n_heads * sizeof(float));
+  const int64_t bh = (int64_t)s->batch * s->n_heads;
+  L.seg_state = take((size_t)bh * L.scan.nseg * s->head_dim * (F / s->n_heads) * sizeof(float));
+  L.seg_z = take((size_t)bh * L.scan.nseg * s->head_dim * sizeof(float));
+  L.total = off;
+  return L;
+}
+
+// The WANGO scan + band of one problem into gbar (options set by the caller).
+hipError_t wango_scan_band(const tango_shape_t* s, int32_t window, int32_t chunk, const WFwdLayout& L,
+                           char* base, const BwdArgs& fa, const void* q, const void* k, const void* gp,
+                           AggArgs aa, hipStream_t st) {
+  // destination features of q (permuted order), source features of k (packed)
+  hipError_t e = launch_wango_bwd_features(fa, base + L.fq, base + L.tmp, q, k, base + L.fk, st);
+  if (e != hipSuccess) return e;
+  float* n_old = reinterpret_cast<float*>(base + L.n_old);
+  float* z_old = reinterpret_cast<float*>(base + L.z_old);
+  ScanArgs sa = scan_args(s, window, chunk, base + L.fq, base + L.fk, gp, n_old, z_old,
+                          reinterpret_cast<float*>(base + L.seg_state), reinterpret_cast<float*>(base + L.seg_z));
+  if ((e = launch_wango_scan(sa, L.scan, true, st)) != hipSuccess) return e;
+  aa.n_old = n_old;
+  aa.z_old = z_old;
+  aa.window = window;
+  aa.chunk = chunk;
+  return launch_wango_band(aa, true, st);
+}
+
+struct WBwdLayout {
+  WFwdLayout f;   // the reversed problem's forward scratch (dg)
+  size_t u_rm, g_rm, qT, kT, pT, aT, p_rm, a_rm, q_rev, k_rev, u_rev_pk, delta;
+  size_t ds_rm, ds_t, dp_rm, dp_t, part, part_theta, theta_el, gT, uT, tsum, state, total;
+  BwdPlan plan;
+};
+WBwdLayout make_wbwd_layout(const tango_shape_t* s, int32_t window, int32_t chunk) {
+  WBwdLayout L{};
+  L.f = make_wfwd_layout(s, chunk);
+  const int64_t M = (int64_t)s->batch * pad_rows(s->seq_len);
+  const int64_t Fp = gate_pad(s, true), HD = (int64_t)s->n_heads * s->head_dim;
+  const int64_t bh = (int64_t)s->batch * s->n_heads;
+  L.plan = wango_bwd_plan(s->batch, (int)pad_rows(s->seq_len), head_pad(s, true), s->n_heads, window);
+  size_t off = L.f.total;
+  auto take = [&](size_t bytes) {
+    const size_t o = off;
+    off = align256(off + bytes);
+    return o;
+  };
+  const size_t es = 2, rows = (size_t)M * s->n_heads * L.plan.FhC * es;
+  L.u_rm = take(rows);
+  L.g_rm = take(rows);
+  L.qT = take((size_t)M * HD * es);
+  L.kT = take((size_t)M * HD * es);
+  L.pT = take((size_t)M * HD * es);
+  L.aT = take((size_t)M * HD * es);
+  L.p_rm = take((size_t)M * HD * es);
+  L.a_rm = take((size_t)M * HD * es);
+  L.q_rev = take((size_t)M * HD * es);
+  L.k_rev = take((size_t)M * HD * es);
+  L.u_rev_pk = take((size_t)M * Fp * es);
+  L.delta = take((size_t)M * s->n_heads * sizeof(float));
+  const size_t tiles = (size_t)L.plan.items_ds * kBwdTile * kBwdTile * es;
+  L.ds_rm = take(tiles);
+  L.ds_t = take(tiles);
+  L.dp_rm = take(tiles);
+  L.dp_t = take(tiles);
+  L.part = take((size_t)6 * M * HD * sizeof(float));
+  L.part_theta = take((size_t)L.plan.items_ds * sizeof(float));
+  L.theta_el = take((size_t)M * HD * sizeof(float));
+  L.gT = take(rows);
+  L.uT = take(rows);
+  const size_t st_el = (size_t)bh * L.plan.nt * s->head_dim * L.plan.FhC;
+  L.tsum = take(st_el * sizeof(float));
+  L.state = take(st_el * es);
+  L.total = off;
+  return L;
+}
+
+BwdArgs bwd_args(const tango_shape_t* s, const float* theta, const float* null_bias, const void* qh,
+                 const void* kh, const void* gp, const void* gbar, const float* den, const void* dgbar, bool wango) {
+  BwdArgs a{};
+  a.qh = qh;
+  a.kh = kh;
+  a.gp = gp;
+  a.gbar = gbar;
+  a.dgbar = dgbar;
+  a.den = den;
+  a.theta = theta;
+  a.null_bias = null_bias;
+  a.B = s->batch;
+  a.T = s->seq_len;
+  a.Tp = (int)pad_rows(s->seq_len);
+  a.H = s->n_heads;
+  a.dh = s->head_dim;
+  a.F = s->d_gate;
+  a.Fh = head_width(s);
+  a.Fhp = head_pad(s, wango);
+  a.Fp = (int)gate_pad(s, wango);
+  return a;
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t wango_aggregate_fwd_train_workspace_size(const tango_shape_t* shape, int32_t window, int32_t chunk) {
+  if (!shape || check_wango_bwd(shape, window, chunk) != TANGO_OK) return 0;
+  return make_wfwd_layout(shape, chunk).total;
+}
+
+int wango_aggregate_fwd_train(const tango_shape_t* shape, int32_t window, int32_t chunk, const float* theta,
+                              const float* null_bias, const void* qh, const void* kh, const void* gp, void* gbar,
+                              float* den, void* workspace, size_t workspace_bytes, void* hip_stream) {
+  return guarded([&] {
+    int rc = check_wango_bwd(shape, window, chunk);
+    if (rc) return rc;
+    if (!theta || !qh || !kh || !gp || !gbar || !den || !workspace)
+      return fail(TANGO_ERR_NULL, "a buffer pointer is NULL");
+    const tango_shape_t* s = shape;
+    const WFwdLayout L = make_wfwd_layout(s, chunk);
+    if (workspace_bytes < L.total)
+      return fail(TANGO_ERR_WORKSPACE, "workspace of %zu bytes is smaller than the %zu needed",
+                  workspace_bytes, L.total);
+    const size_t M = (size_t)s->batch * pad_rows(s->seq_len);
+    const size_t F = gate_pad(s, true), HD = (size_t)s->n_heads * s->head_dim;
+    const Range ins[] = {{qh, M * HD * 2, "qh"}, {kh, M * HD * 2, "kh"}, {gp, M * F * 2, "gp"},
+                         {theta, s->n_heads * sizeof(float), "theta"},
+                         {null_bias, s->n_heads * sizeof(float), "null_bias"}};
+    const Range outs[] = {{gbar, M * (size_t)s->d_gate * 2, "gbar"},
+                          {den, M * s->n_heads * sizeof(float), "den"},
+                          {workspace, L.total, "workspace"}};
+    if ((rc = check_ranges(ins, 5, outs, 3, nullptr, nullptr))) return rc;
+    if ((rc = ensure_init())) return rc;
+    const BwdArgs fa = bwd_args(s, theta, null_bias, qh, kh, gp, nullptr, nullptr, nullptr, true);
+    AggArgs aa = agg_args(s, theta, null_bias, qh, kh, gp, gbar, true);
+    aa.den_out = den;
+    hipError_t e = wango_scan_band(s, window, chunk, L, static_cast<char*>(workspace), fa, qh, kh, gp, aa,
+                                   static_cast<hipStream_t>(hip_stream));
+    return e == hipSuccess ? ok() : hip_fail(e, "WANGO scan / band kernels");
+  });
+}
+
+size_t wango_aggregate_bwd_workspace_size(const tango_shape_t* shape, int32_t window, int32_t chunk) {
+  if (!shape || check_wango_bwd(shape, window, chunk) != TANGO_OK) return 0;
+  return make_wbwd_layout(shape, window, chunk).total;
+}
+
+int wango_aggregate_bwd(const tango_shape_t* shape, int32_t window, int32_t chunk, const float* theta,
+                        const float* null_bias, const void* qh, const void* kh, const void* gp, const void* gbar,
+                        const float* den, const void* dgbar, float* dq, float* dk, void* dg, float* dtheta,
+                        float* dnull, void* workspace, size_t workspace_bytes, void* hip_stream) {
+  return guarded([&] {
+    int rc = check_wango_bwd(shape, window, chunk);
+    if (rc) return rc;
+    if (!theta || !qh || !kh || !gp || !gbar || !den || !dgbar || !dq || !dk || !dg || !dtheta || !workspace)
+      return fail(TANGO_ERR_NULL, "a buffer pointer is NULL");
+    if ((null_bias == nullptr) != (dnull == nullptr))
+      return fail(TANGO_ERR_NULL, "null_bias and dnull must both be given or both be NULL");
+    const tango_shape_t* s = shape;
+    const WBwdLayout L = make_wbwd_layout(s, window, chunk);
+    if (workspace_bytes < L.total)
+      return fail(TANGO_ERR_WORKSPACE, "workspace of %zu bytes is smaller than the %zu needed",
+                  workspace_bytes, L.total);
+    const size_t M = (size_t)s->batch * pad_rows(s->seq_len);
+    const size_t F = s->d_gate, Fp = gate_pad(s, true), HD = (size_t)s->n_heads * s->head_dim;
+    const size_t H = s->n_heads;
+    const Range ins[] = {{qh, M * HD * 2, "qh"},          {kh, M * HD * 2, "kh"},
+                         {gp, M * Fp * 2, "gp"},          {gbar, M * F * 2, "gbar"},
+                         {den, M * H * sizeof(float), "den"}, {dgbar, M * F * 2, "dgbar"},
+                         {theta, H * sizeof(float), "theta"}, {null_bias, H * sizeof(float), "null_bias"}};
+    const Range outs[] = {{dq, M * HD * sizeof(float), "dq"},  {dk, M * HD * sizeof(float), "dk"},
+                          {dg, M * F * 2, "dg"},               {dtheta, H * sizeof(float), "dtheta"},
+                          {dnull, H * sizeof(float), "dnull"}, {workspace, L.total, "workspace"}};
+    if ((rc = check_ranges(ins, 8, outs, 6, nullptr, nullptr))) return rc;
+    if ((rc = ensure_init())) return rc;
+    const hipStream_t st = static_cast<hipStream_t>(hip_stream);
+    char* base = static_cast<char*>(workspace);
+    BwdArgs a = bwd_args(s, theta, null_bias, qh, kh, gp, gbar, den, dgbar, true);
+    a.u_rm = base + L.u_rm;
+    a.g_rm = base + L.g_rm;
+    a.qT = base + L.qT;
+    a.kT = base + L.kT;
+    a.pT = base + L.pT;
+    a.aT = base + L.aT;
+    a.p_rm = base + L.p_rm;
+    a.a_rm = base + L.a_rm;
+    a.q_rev = base + L.q_rev;
+    a.k_rev = base + L.k_rev;
+    a.u_rev_pk = base + L.u_rev_pk;
+    a.delta = reinterpret_cast<float*>(base + L.delta);
+    a.ds_rm = base + L.ds_rm;
+    a.ds_t = base + L.ds_t;
+    a.dp_rm = base + L.dp_rm;
+    a.dp_t = base + L.dp_t;
+    a.part = reinterpret_cast<float*>(base + L.part);
+    a.part_theta = reinterpret_cast<float*>(base + L.part_theta);
+    a.dq = dq;
+    a.dk = dk;
+    a.dtheta = dtheta;
+    a.dnull = dnull;
+    a.window = window;
+    a.nb = L.plan.nb;
+    a.FhC = L.plan.FhC;
+    hipError_t e = launch_wango_bwd_prep(a, L.plan, st);
+    if (e != hipSuccess) return hip_fail(e, bwd_last_step());
+    // dg: the whole WANGO aggregation (scan + band) of the time-reversed
+    // problem, numerator only
+    AggArgs aa = agg_args(s, theta, nullptr, a.k_rev, a.q_rev, a.u_rev_pk, dg, true);
+    aa.num_only = 1;
+    aa.rev_out = 1;
+    if ((e = wango_scan_band(s, window, chunk, L.f, base, a, a.k_rev, a.q_rev, a.u_rev_pk, aa, st)) != hipSuccess)
+      return hip_fail(e, "reversed scan / band (dg)");   // (bwd_last_step() names a feature kernel)
+    // window and near older pairs
+    if ((e = launch_tango_ds(a, L.plan, st)) != hipSuccess) return hip_fail(e, "ds tile kernel");
+    if ((e = launch_tango_dsmm(a, L.plan, st)) != hipSuccess) return hip_fail(e, "tile product kernel");
+    // far older pairs: prefix states of a g^T and suffix states of p u^T
+    const int64_t MHD = (int64_t)M * HD;
+    WStateArgs w{};
+    w.tsum = reinterpret_cast<float*>(base + L.tsum);
+    w.state = base + L.state;
+    w.B = s->batch;
+    w.H = s->n_heads;
+    w.dh = s->head_dim;
+    w.Tp = a.Tp;
+    w.FhC = L.plan.FhC;
+    w.nt = L.plan.nt;
+    w.nb = L.plan.nb;
+    if ((e = launch_head_transpose(a.g_rm, base + L.gT, s->batch, s->n_heads, L.plan.FhC, a.Tp, st)) != hipSuccess ||
+        (e = launch_head_transpose(a.u_rm, base + L.uT, s->batch, s->n_heads, L.plan.FhC, a.Tp, st)) != hipSuccess)
+      return hip_fail(e, "row transposes");
+    w.aT = a.aT;
+    w.xT = base + L.gT;
+    w.rows = a.u_rm;
+    w.out = a.part + 4 * MHD;
+    if ((e = launch_wango_state_sums(w, st)) != hipSuccess || (e = launch_wango_state_scan(w, false, st)) != hipSuccess ||
+        (e = launch_wango_state_readout(w, false, st)) != hipSuccess)
+      return hip_fail(e, "prefix states (dp)");
+    w.aT = a.pT;
+    w.xT = base + L.uT;
+    w.rows = a.g_rm;
+    w.out = a.part + 5 * MHD;
+    if ((e = launch_wango_state_sums(w, st)) != hipSuccess || (e = launch_wango_state_scan(w, true, st)) != hipSuccess ||
+        (e = launch_wango_state_readout(w, true, st)) != hipSuccess)
+      return hip_fail(e, "suffix states (da)");
+    if ((e = launch_wango_bwd_finish(a, L.plan, reinterpret_cast<float*>(base + L.theta_el), st)) != hipSuccess)
+      return hip_fail(e, "backward finish");
+    return ok();
+  });
+}
+
 int tango_stage_out(const tango_shape_t* shape, const void* w_o, const void* x, const void* gbar,
                     const void* v, void* out, void* hip_stream) {
   return guarded([&] {

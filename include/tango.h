@@ -60,7 +60,7 @@
 extern "C" {
 #endif
 
-#define TANGO_ABI_VERSION 6
+#define TANGO_ABI_VERSION 7
 
 typedef enum { TANGO_F32 = 0, TANGO_BF16 = 1 } tango_dtype_t;
 
@@ -334,6 +334,42 @@ int tango_aggregate_bwd(const tango_shape_t* shape, const float* theta, const fl
                         const void* qh, const void* kh, const void* gp, const void* gbar,
                         const float* den, const void* dgbar, float* dq, float* dk, void* dg,
                         float* dtheta, float* dnull, void* workspace, size_t workspace_bytes,
+                        void* hip_stream);
+
+/* ---- Backward of the WANGO aggregation ------------------------------------
+ *
+ * Gradients of L = sum(dgbar * gbar) for the WANGO aggregation ([TANGO] §2.2
+ * eqs. 7-10; the pages train the block, §3, but print no gradient): window
+ * sources i-W < j <= i weighted by exp(tau q_i.k_j), older sources j <= i-W by
+ * phi(sqrt(tau) q_i) . phi(sqrt(tau) k_j) (eq. 8), one joint normalisation with
+ * the null term.  With p, a the two feature vectors and dm_ij = u_i.g_j +
+ * delta_i (u, delta as for TANGO):
+ *   ds_ij = tau w_ij dm_ij on window pairs, dP_ij = dm_ij on older pairs,
+ *   dq_i = sum_j ds_ij k_j + sqrt(tau) phi'(sqrt(tau) q_i) * sum_j dP_ij a_j,
+ *   dk_j alike, dg_j = sum_i (weight_ij) u_i, dtheta through tau in the
+ *   window weights and in the features (zero where theta >= log 20).
+ * bf16 only; window <= 897 and chunk as for wango_block_fwd.  Shapes, layouts
+ * and outputs as for tango_aggregate_bwd, with the gates packed at the WANGO
+ * head padding (F' columns as for wango_stage_scan).
+ *
+ * wango_aggregate_fwd_train: the WANGO aggregation (scan + band) from unit q,
+ * k and packed gates, also storing den [B, Tp, H] float32 (e^{-tau} units, rows
+ * < T) for the backward; workspace of
+ * wango_aggregate_fwd_train_workspace_size bytes.
+ * wango_aggregate_bwd: dq, dk [B, Tp, H*d_h] float32, dg [B, Tp, d_gate] bf16,
+ * dtheta [H], dnull [H] (or NULL with null_bias NULL); workspace of
+ * wango_aggregate_bwd_workspace_size bytes.  Both run on hip_stream without
+ * synchronising; buffers must not overlap; 0 sizes for invalid arguments. */
+size_t wango_aggregate_fwd_train_workspace_size(const tango_shape_t* shape, int32_t window, int32_t chunk);
+int wango_aggregate_fwd_train(const tango_shape_t* shape, int32_t window, int32_t chunk, const float* theta,
+                              const float* null_bias, const void* qh, const void* kh, const void* gp,
+                              void* gbar, float* den, void* workspace, size_t workspace_bytes,
+                              void* hip_stream);
+size_t wango_aggregate_bwd_workspace_size(const tango_shape_t* shape, int32_t window, int32_t chunk);
+int wango_aggregate_bwd(const tango_shape_t* shape, int32_t window, int32_t chunk, const float* theta,
+                        const float* null_bias, const void* qh, const void* kh, const void* gp,
+                        const void* gbar, const float* den, const void* dgbar, float* dq, float* dk,
+                        void* dg, float* dtheta, float* dnull, void* workspace, size_t workspace_bytes,
                         void* hip_stream);
 
 #ifdef __cplusplus

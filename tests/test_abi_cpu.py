@@ -225,3 +225,14 @@ def test_stack_entry_point_validates(lib):
     bad = W3(sets[0], sets[1], weights(w_g=FAKE + 0x12000000, w_v=FAKE + 0x22000000, w_o=FAKE + 0x60000000))
     assert run(st=bad) == code["TANGO_ERR_ALIAS"]
     assert run(st=W3(sets[0], weights(theta=None), sets[2])) == -1
+
+
+def test_binding_argument_counts_match_the_header(lib):
+    """Every ctypes signature takes as many arguments as the header's
+    declaration (a missing one would shift the stream into another slot)."""
+    text = re.sub(r"/\*.*?\*/", "", open(HEADER).read(), flags=re.S)
+    for name in header_functions():
+        m = re.search(r"\b" + name + r"\s*\(([^)]*)\)", text)
+        params = m.group(1).strip()
+        n = 0 if params in ("", "void") else params.count(",") + 1
+        assert len(getattr(lib, name).argtypes) == n, name

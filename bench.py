@@ -366,6 +366,78 @@ def backward_bench(steps: int, warmup: int, dev, stream) -> dict:
     return out
 
 
+def wango_backward_flops(T: int, F: int, H: int, dh: int, W: int) -> float:
+    """Algorithmic flops of the WANGO aggregation backward: per head, every
+    window pair forms u.g and its dg term over the head's F/H gate columns and
+    s, dq, dk over d_h (2 (2 F/H + 3 d_h) each); the older prefix is linear:
+    per position the two state sums and their two read-outs (d_h x F/H each
+    way) and the state update and read-out of dg, 12 d_h F/H in all."""
+    fh = F // H
+    pairs = sum(min(i + 1, W) for i in range(T))
+    return float(H * (2 * pairs * (2 * fh + 3 * dh) + 12 * T * dh * fh))
+
+
+def wango_backward_bench(steps: int, warmup: int, dev, stream) -> dict:
+    """Backward pass of the WANGO aggregation at the T = 8192 WANGO bench shape
+    (two heads of 64, F = 2048, window 256, chunk 128, bf16): the forward that
+    saves the denominators runs once; the backward is timed, median of `steps`."""
+    import torch
+
+    from cross_token_gated_amd import api
+    from cross_token_gated_amd import workload as wl
+    from tests import helpers as H
+
+    c = wl.WANGO_BACKWARD_SHAPE
+    T, F, Hh, dh, W, C = c["T"], c["F"], c["H"], c["dh"], c["window"], c["chunk"]
+    Tp = H.padded_len(T)
+    q, k, g, dg_in = wl.aggregate_inputs(T, F, Hh, dh, c["seed"])
+    bf = torch.bfloat16
+    qd = torch.from_numpy(H.pad_rows(q.reshape(1, T, Hh * dh), Tp)).to(dev).to(bf)
+    kd = torch.from_numpy(H.pad_rows(k.reshape(1, T, Hh * dh), Tp)).to(dev).to(bf)
+    gp = torch.from_numpy(H.pack_gates(H.pad_rows(g[None], Tp)).reshape(-1)).to(dev).to(bf)
+    dgbar = torch.from_numpy(H.pad_rows(dg_in[None], Tp)).to(dev).to(bf)
+    theta = torch.full((Hh,), math.log(10.0), dtype=torch.float32, device=dev)
+    shape = api.make_shape(1, T, 512, F, Hh, dh, bf)
+    gbar = torch.empty((Tp, F), dtype=bf, device=dev)
+    den = torch.empty((Tp, Hh), dtype=torch.float32, device=dev)
+    wsf = api.workspace(api.wango_aggregate_fwd_train_workspace_size(shape, W, C), dev)
+    api.wango_aggregate_fwd_train(shape, W, C, theta, None, qd, kd, gp, gbar, den, wsf, stream=stream)
+    dq = torch.empty((Tp, Hh * dh), dtype=torch.float32, device=dev)
+    dk = torch.empty_like(dq)
+    dg = torch.empty((Tp, F), dtype=bf, device=dev)
+    dth = torch.empty((Hh,), dtype=torch.float32, device=dev)
+    wsb = api.workspace(api.wango_aggregate_bwd_workspace_size(shape, W, C), dev)
+
+    def bwd():
+        api.wango_aggregate_bwd(shape, W, C, theta, None, qd, kd, gp, gbar, den, dgbar, dq, dk, dg, dth, None,
+                                wsb, stream=stream)
+
+    for _ in range(warmup):
+        bwd()
+    torch.cuda.synchronize()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+    for a, b in ev:
+        a.record(stream)
+        bwd()
+        b.record(stream)
+    torch.cuda.synchronize()
+    t = sorted(a.elapsed_time(b) for a, b in ev)
+    ms = t[steps // 2] if steps % 2 else 0.5 * (t[steps // 2 - 1] + t[steps // 2])
+    flops = wango_backward_flops(T, F, Hh, dh, W)
+    achieved = flops / (ms * 1e-3)
+    out = {"workload": "wango_aggregate_bwd_bf16_t8192_f2048_h2_w256", "ms_per_backward": ms,
+           "tokens_per_s": T / (ms * 1e-3),
+           "roofline": {"kernel": "whole WANGO aggregation backward", "bound": "mfma",
+                        "achieved": achieved / 1e12, "peak": PEAK_BF16_FLOPS / 1e12, "unit": "TFLOP/s",
+                        "frac": achieved / PEAK_BF16_FLOPS, "flops_per_backward": flops}}
+    print(f"[bench] backward wango_aggregate_bwd T=8192 F=2048 W=256: {ms:.3f} ms, "
+          f"{achieved / 1e12:.0f} TFLOP/s ({achieved / PEAK_BF16_FLOPS * 100:.1f}% of bf16 peak)",
+          file=sys.stderr, flush=True)
+    del wsf, wsb
+    torch.cuda.empty_cache()
+    return out
+
+
 def decode_bench(steps: int, warmup: int, dev, stream) -> dict:
     """One decode step (every layer) at position T - 1 of the decode workloads,
     timed with HIP events.  The state is filled with synthetic content of the
@@ -651,6 +723,7 @@ def main():
         result["three_set"] = three_set_bench(min(loops, 10), 1, dev, stream, ms_tango / wt.repeats)
     if not args.no_backward:
         result["backward"] = backward_bench(loops, min(args.warmup, 3), dev, stream)
+        result["backward_wango"] = wango_backward_bench(loops, min(args.warmup, 3), dev, stream)
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(wt, wg)
     print(json.dumps(result), flush=True)

@@ -33,6 +33,8 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
 constexpr float kLogTauMax = 2.995732273553991f;   // log 20: tau = exp(min(theta, log 20))
 
+constexpr int kMaxBwdHeads = 256;  // one finish thread per head sums its shares
+
 thread_local const char* t_step = "";   // kernel of the last launch (named in error messages)
 
 // Row of position r (0..31) of a 32-row block in slot (grp, s) order.
@@ -111,25 +113,43 @@ __global__ __launch_bounds__(256) void pack_kernel(const T* __restrict__ src, in
 }
 
 // Packed gates [rows/32][4][H*src_hw][8] -> row-major [rows][H][dst_hw]
-// (columns past valid_w zero).
-// one_col >= 0: that column holds 1 on rows before the sequence end (the
-// extra column of WANGO's augmented gates).
+// (columns past valid_w zero; one_col >= 0: that column holds 1 on rows before
+// the sequence end, the extra column of WANGO's augmented gates).  Through LDS
+// in tiles of 32 rows x 64 columns: grid (rows / 32) * H * (dst_hw / 64).
 template <typename T>
 __global__ __launch_bounds__(256) void unpack_kernel(const T* __restrict__ gp, int src_F, T* __restrict__ dst,
-                                                     int H, int src_hw, int dst_hw, int valid_w, int64_t rows,
-                                                     int one_col, int Tp, int T_) {
-  const int64_t id = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  const int64_t per_row = (int64_t)H * dst_hw;
-  if (id >= rows * per_row) return;
-  const int64_t row = id / per_row;
-  const int n = (int)(id % per_row), hd = n / dst_hw, c = n % dst_hw;
-  int grp, s;
-  slot_of_row((int)(row % 32), grp, s);
-  float v = 0.f;
-  if (c < valid_w) v = (float)gp[packed_offset(row / 32, grp, (int64_t)hd * src_hw + c, src_F) + s];
-  else if (c == one_col && (int)(row % Tp) < T_) v = 1.0f;
-  dst[id] = (T)v;
+                                                     int H, int src_hw, int dst_hw, int valid_w, int one_col, int Tp,
+                                                     int T_) {
+  __shared__ T tile[32][64 + 8];
+  int64_t id = blockIdx.x;
+  const int ct = (int)(id % (dst_hw / 64));
+  id /= dst_hw / 64;
+  const int hd = (int)(id % H);
+  const int64_t blk = id / H;
+  const int tid = threadIdx.x;
+  {   // 4 slot groups x 64 columns, 8 rows (slots) each
+    const int grp = tid >> 6, cl = tid & 63, c = ct * 64 + cl;
+    u32x4 v = {0u, 0u, 0u, 0u};
+    if (c < valid_w) v = *reinterpret_cast<const u32x4*>(gp + packed_offset(blk, grp, (int64_t)hd * src_hw + c, src_F));
+    const T* e8 = reinterpret_cast<const T*>(&v);
+#pragma unroll
+    for (int s = 0; s < 8; ++s) tile[perm_slot(grp, s)][cl] = e8[s];
+  }
+  __syncthreads();
+  {   // 32 rows x 8 pieces of 8 columns
+    const int r = tid >> 3, p = tid & 7;
+    const int64_t row = blk * 32 + r;
+    T out[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const int c = ct * 64 + p * 8 + e;
+      out[e] = (c == one_col && (int)(row % Tp) < T_) ? (T)1.0f : tile[r][p * 8 + e];
+    }
+    *reinterpret_cast<u32x4*>(dst + (row * H + hd) * (int64_t)dst_hw + ct * 64 + p * 8) =
+        *reinterpret_cast<const u32x4*>(out);
+  }
 }
+
 
 // Row-major copy with every sequence reversed (rows past the end zero).
 template <typename T>
@@ -144,20 +164,38 @@ __global__ __launch_bounds__(256) void reverse_rows_kernel(const T* __restrict__
   dst[id] = i < T_ ? src[(b * Tp + (T_ - 1 - i)) * cols + c] : (T)0.f;
 }
 
-// Row-major [B*Tp][H*dh] -> per head transposed [B][H][dh][Tp].
+// Row-major [B*Tp][H*C] -> per head transposed [B][H][C][Tp], through LDS in
+// tiles of 64 positions x 32 columns (16-byte loads and stores on both sides).
+// Grid: B * H * (C / 32) * (Tp / 64) workgroups of 256.
 template <typename T>
 __global__ __launch_bounds__(256) void transpose_kernel(const T* __restrict__ src, T* __restrict__ dst, int H,
-                                                        int dh, int Tp, int64_t n) {
-  const int64_t id = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  if (id >= n) return;
-  const int i = (int)(id % Tp);
-  int64_t rest = id / Tp;
-  const int e = (int)(rest % dh);
-  rest /= dh;
-  const int h = (int)(rest % H);
-  const int64_t b = rest / H;
-  dst[id] = src[(b * Tp + i) * (int64_t)H * dh + (int64_t)h * dh + e];
+                                                        int C, int Tp) {
+  __shared__ T tile[64][32 + 8];
+  int64_t id = blockIdx.x;
+  const int it = (int)(id % (Tp / 64));
+  id /= Tp / 64;
+  const int ct = (int)(id % (C / 32));
+  id /= C / 32;
+  const int h = (int)(id % H);
+  const int64_t b = id / H;
+  const int tid = threadIdx.x;
+  {   // 64 rows x 4 pieces of 8 columns
+    const int r = tid >> 2, p = tid & 3;
+    const u32x4 v = *reinterpret_cast<const u32x4*>(
+        src + (b * Tp + (int64_t)it * 64 + r) * (int64_t)H * C + (int64_t)h * C + ct * 32 + p * 8);
+    *reinterpret_cast<u32x4*>(&tile[r][p * 8]) = v;
+  }
+  __syncthreads();
+  {   // 32 columns x 8 pieces of 8 positions
+    const int c = tid >> 3, p = tid & 7;
+    T out[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) out[e] = tile[p * 8 + e][c];
+    *reinterpret_cast<u32x4*>(dst + ((b * H + h) * (int64_t)C + ct * 32 + c) * Tp + (int64_t)it * 64 + p * 8) =
+        *reinterpret_cast<const u32x4*>(out);
+  }
 }
+
 
 // WANGO feature layouts of phi(sqrt(tau) x) for x = q or k ([TANGO] §2.2 eq. 8),
 // row-major [M][H*dh] (plain, and/or in the permuted feature order of each
@@ -201,30 +239,57 @@ __global__ __launch_bounds__(256) void state_scan_kernel(WStateArgs w, int rever
 }
 
 // WANGO finish: dq = window part + sqrt(tau) phi'(sqrt(tau) q) (near + far dp),
-// dk alike with da; each element's share of dtheta through the features,
-// sqrt(tau) / 2 (dp phi'(sqrt(tau) q) q + da phi'(sqrt(tau) k) k), goes to theta_el.
-__global__ __launch_bounds__(256) void wango_finish_kernel(BwdArgs a, float* theta_el) {
+// dk alike with da.  Each element's share of dtheta through the features,
+// sqrt(tau) / 2 (dp phi'(sqrt(tau) q) q + da phi'(sqrt(tau) k) k), is summed per
+// head within the workgroup: theta_blk[block][H].
+__global__ __launch_bounds__(256) void wango_finish_kernel(BwdArgs a, float* theta_blk) {
+  __shared__ float val[8];
+  __shared__ int head[8];
   const int64_t M = (int64_t)a.B * a.Tp;
   const int HD = a.H * a.dh;
   const int64_t id = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  if (id >= M * HD) return;
-  const int64_t m = id / HD;
-  const int h = (int)(id % HD) / a.dh;
-  const bool live = (int)(m % a.Tp) < a.T;
-  const float st = sqrtf(__expf(fminf(a.theta[h], kLogTauMax)));
-  const float escale = st * st > 0.f ? __expf(-st * st) : 0.f;   // e^{-tau}: far read-outs are unscaled
-  const float isd = 1.0f / sqrtf((float)a.dh);
-  const float* P = a.part;
-  const float dp = P[2 * M * HD + id] + escale * P[4 * M * HD + id];
-  const float da = P[3 * M * HD + id] + escale * P[5 * M * HD + id];
-  const float q = (float)static_cast<const __bf16*>(a.qh)[id];
-  const float k = (float)static_cast<const __bf16*>(a.kh)[id];
-  const float xq = st * q, xk = st * k;
-  const float fq = (xq > 0.f ? 1.0f : __expf(xq)) * isd;   // phi'
-  const float fk = (xk > 0.f ? 1.0f : __expf(xk)) * isd;
-  a.dq[id] = live ? P[id] + st * fq * dp : 0.f;
-  a.dk[id] = live ? P[M * HD + id] + st * fk * da : 0.f;
-  theta_el[id] = live ? 0.5f * st * (dp * fq * q + da * fk * k) : 0.f;
+  float share = 0.f;
+  int h = -1;
+  if (id < M * HD) {
+    const int64_t m = id / HD;
+    h = (int)(id % HD) / a.dh;
+    const bool live = (int)(m % a.Tp) < a.T;
+    const float tau = __expf(fminf(a.theta[h], kLogTauMax));
+    const float st = sqrtf(tau), escale = __expf(-tau);   // far read-outs are unscaled
+    const float isd = 1.0f / sqrtf((float)a.dh);
+    const float* P = a.part;
+    const float dp = P[2 * M * HD + id] + escale * P[4 * M * HD + id];
+    const float da = P[3 * M * HD + id] + escale * P[5 * M * HD + id];
+    const float q = (float)static_cast<const __bf16*>(a.qh)[id];
+    const float k = (float)static_cast<const __bf16*>(a.kh)[id];
+    const float xq = st * q, xk = st * k;
+    const float fq = (xq > 0.f ? 1.0f : __expf(xq)) * isd;   // phi'
+    const float fk = (xk > 0.f ? 1.0f : __expf(xk)) * isd;
+    a.dq[id] = live ? P[id] + st * fq * dp : 0.f;
+    a.dk[id] = live ? P[M * HD + id] + st * fk * da : 0.f;
+    if (live) share = 0.5f * st * (dp * fq * q + da * fk * k);
+  }
+  // a wave spans at most two heads (d_h >= 32): two wave sums, then per head
+  // the four waves' partials in order (the sum does not depend on timing)
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int h0 = __shfl(h, 0);
+  int h1 = h != h0 ? h : -1;   // the other head of the wave, if any (the row may wrap to head 0)
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) h1 = max(h1, __shfl_xor(h1, o));
+  const float lo = wave_sum(h == h0 ? share : 0.f), hi = wave_sum(h != h0 ? share : 0.f);
+  if (lane == 0) {
+    val[wave * 2] = lo;
+    val[wave * 2 + 1] = hi;
+    head[wave * 2] = h0;
+    head[wave * 2 + 1] = h1;
+  }
+  __syncthreads();
+  if (threadIdx.x < a.H) {
+    float sum = 0.f;
+    for (int t = 0; t < 8; ++t)
+      if (head[t] == (int)threadIdx.x) sum += val[t];
+    theta_blk[(int64_t)blockIdx.x * a.H + threadIdx.x] = sum;
+  }
 }
 
 // Sums the chunk partials into dq, dk: a row of tile r takes the dq chunks
@@ -248,7 +313,7 @@ __global__ __launch_bounds__(256) void bwd_finish_kernel(BwdArgs a, int nch) {
 
 // Per head: dtheta from the per-item partials, dnull from delta.  One block
 // per head.
-__global__ __launch_bounds__(256) void bwd_scalars_kernel(BwdArgs a, int64_t ntri, const float* theta_el) {
+__global__ __launch_bounds__(256) void bwd_scalars_kernel(BwdArgs a, int64_t ntri, const float* theta_blk) {
   __shared__ float red[2][256];
   const int h = blockIdx.x, tid = threadIdx.x;
   const float tau = __expf(fminf(a.theta[h], kLogTauMax));
@@ -256,13 +321,9 @@ __global__ __launch_bounds__(256) void bwd_scalars_kernel(BwdArgs a, int64_t ntr
   // tiles of head h: (b * H + h) * ntri + t
   for (int64_t b = 0; b < a.B; ++b)
     for (int64_t k = tid; k < ntri; k += 256) th += a.part_theta[(b * a.H + h) * ntri + k];
-  if (theta_el) {   // WANGO: the features' share, per element of head h
-    const int64_t M = (int64_t)a.B * a.Tp;
-    const int HD = a.H * a.dh;
-    for (int64_t x = tid; x < M * a.dh; x += 256) {
-      const int64_t m = x / a.dh;
-      th += theta_el[m * HD + (int64_t)h * a.dh + x % a.dh];
-    }
+  if (theta_blk) {   // WANGO: the features' share, per finish workgroup
+    const int64_t nblk = ceil_div((int64_t)a.B * a.Tp * a.H * a.dh, 256);
+    for (int64_t x = tid; x < nblk; x += 256) th += theta_blk[x * a.H + h];
   }
   if (a.null_bias) {
     const float nw = __expf(a.null_bias[h] - tau);
@@ -327,22 +388,23 @@ hipError_t launch_tango_bwd_prep(const BwdArgs& a, const BwdPlan& p, hipStream_t
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   // gates row-major from the packed forward layout
-  const int64_t ng = M * a.H * p.FhC;
+  if (p.FhC % 64 != 0 || a.dh % 32 != 0) return hipErrorInvalidValue;
   t_step = "unpack_kernel";
-  hipLaunchKernelGGL(unpack_kernel<T>, dim3((unsigned)ceil_div(ng, 256)), dim3(256), 0, s,
-                     static_cast<const T*>(a.gp), a.Fp, static_cast<T*>(a.g_rm), a.H, a.Fhp, p.FhC, a.Fh, M,
+  hipLaunchKernelGGL(unpack_kernel<T>, dim3((unsigned)((M / 32) * a.H * (p.FhC / 64))), dim3(256), 0, s,
+                     static_cast<const T*>(a.gp), a.Fp, static_cast<T*>(a.g_rm), a.H, a.Fhp, p.FhC, a.Fh,
                      a.window > 0 ? a.Fhp : -1, a.Tp, a.T);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   // queries and keys transposed per head (the B operands of dk and dq)
   const int64_t nblk = M / 32;
   const int64_t nqk = M * HD;
   t_step = "transpose_kernel";
-  hipLaunchKernelGGL(transpose_kernel<T>, dim3((unsigned)ceil_div(nqk, 256)), dim3(256), 0, s,
-                     static_cast<const T*>(a.qh), static_cast<T*>(a.qT), a.H, a.dh, a.Tp, nqk);
+  const dim3 tgrid((unsigned)((int64_t)a.B * a.H * (a.dh / 32) * (a.Tp / 64)));
+  hipLaunchKernelGGL(transpose_kernel<T>, tgrid, dim3(256), 0, s, static_cast<const T*>(a.qh),
+                     static_cast<T*>(a.qT), a.H, a.dh, a.Tp);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   t_step = "transpose_kernel";
-  hipLaunchKernelGGL(transpose_kernel<T>, dim3((unsigned)ceil_div(nqk, 256)), dim3(256), 0, s,
-                     static_cast<const T*>(a.kh), static_cast<T*>(a.kT), a.H, a.dh, a.Tp, nqk);
+  hipLaunchKernelGGL(transpose_kernel<T>, tgrid, dim3(256), 0, s, static_cast<const T*>(a.kh),
+                     static_cast<T*>(a.kT), a.H, a.dh, a.Tp);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   // the reversed problem of dg: reversed queries / keys, reversed u packed
   // with the forward's head padding
@@ -422,12 +484,13 @@ hipError_t launch_wango_bwd_prep(const BwdArgs& a, const BwdPlan& p, hipStream_t
                      static_cast<T*>(nullptr), a.theta, a.H, a.dh, n);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   t_step = "transpose_kernel";
-  hipLaunchKernelGGL(transpose_kernel<T>, grid, block, 0, s, static_cast<const T*>(a.p_rm), static_cast<T*>(a.pT),
-                     a.H, a.dh, a.Tp, n);
+  const dim3 tgrid((unsigned)((int64_t)a.B * a.H * (a.dh / 32) * (a.Tp / 64)));
+  hipLaunchKernelGGL(transpose_kernel<T>, tgrid, block, 0, s, static_cast<const T*>(a.p_rm), static_cast<T*>(a.pT),
+                     a.H, a.dh, a.Tp);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   t_step = "transpose_kernel";
-  hipLaunchKernelGGL(transpose_kernel<T>, grid, block, 0, s, static_cast<const T*>(a.a_rm), static_cast<T*>(a.aT),
-                     a.H, a.dh, a.Tp, n);
+  hipLaunchKernelGGL(transpose_kernel<T>, tgrid, block, 0, s, static_cast<const T*>(a.a_rm), static_cast<T*>(a.aT),
+                     a.H, a.dh, a.Tp);
   return hipGetLastError();
 }
 
@@ -435,18 +498,19 @@ const char* bwd_last_step() { return t_step; }
 
 hipError_t launch_head_transpose(const void* src, void* dst, int B, int H, int C, int Tp, hipStream_t s) {
   typedef __bf16 T;
-  const int64_t n = (int64_t)B * Tp * H * C;
-  hipLaunchKernelGGL(transpose_kernel<T>, dim3((unsigned)ceil_div(n, 256)), dim3(256), 0, s,
-                     static_cast<const T*>(src), static_cast<T*>(dst), H, C, Tp, n);
+  if (C % 32 != 0 || Tp % 64 != 0) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(transpose_kernel<T>, dim3((unsigned)((int64_t)B * H * (C / 32) * (Tp / 64))), dim3(256), 0, s,
+                     static_cast<const T*>(src), static_cast<T*>(dst), H, C, Tp);
   return hipGetLastError();
 }
 
-hipError_t launch_wango_bwd_finish(const BwdArgs& a, const BwdPlan& p, float* theta_el, hipStream_t s) {
+hipError_t launch_wango_bwd_finish(const BwdArgs& a, const BwdPlan& p, float* theta_blk, hipStream_t s) {
+  if (a.H > kMaxBwdHeads) return hipErrorInvalidValue;
   const int64_t n = (int64_t)a.B * a.Tp * a.H * a.dh;
-  hipLaunchKernelGGL(wango_finish_kernel, dim3((unsigned)ceil_div(n, 256)), dim3(256), 0, s, a, theta_el);
+  hipLaunchKernelGGL(wango_finish_kernel, dim3((unsigned)ceil_div(n, 256)), dim3(256), 0, s, a, theta_blk);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(bwd_scalars_kernel, dim3(a.H), dim3(256), 0, s, a, p.ntri, theta_el);
+  hipLaunchKernelGGL(bwd_scalars_kernel, dim3(a.H), dim3(256), 0, s, a, p.ntri, theta_blk);
   return hipGetLastError();
 }
 

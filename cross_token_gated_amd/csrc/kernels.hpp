@@ -209,7 +209,8 @@ hipError_t launch_wango_state_readout(const WStateArgs& w, bool reverse, hipStre
 hipError_t launch_wango_state_scan(const WStateArgs& w, bool reverse, hipStream_t s);
 hipError_t launch_wango_bwd_features(const BwdArgs& a, void* fq_perm, void* tmp_rm, const void* q_src,
                                      const void* k_src, void* fk_pk, hipStream_t s);
-hipError_t launch_wango_bwd_finish(const BwdArgs& a, const BwdPlan& p, float* theta_el, hipStream_t s);
+// theta_blk: [ceil(B*Tp*H*dh / 256)][H] float32 scratch
+hipError_t launch_wango_bwd_finish(const BwdArgs& a, const BwdPlan& p, float* theta_blk, hipStream_t s);
 hipError_t launch_wango_bwd_prep(const BwdArgs& a, const BwdPlan& p, hipStream_t s);
 // Name of the kernel the backward prep launched last on this thread.
 const char* bwd_last_step();

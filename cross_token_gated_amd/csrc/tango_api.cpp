@@ -889,7 +889,7 @@ WBwdLayout make_wbwd_layout(const tango_shape_t* s, int32_t window, int32_t chun
   L.dp_t = take(tiles);
   L.part = take((size_t)6 * M * HD * sizeof(float));
   L.part_theta = take((size_t)L.plan.items_ds * sizeof(float));
-  L.theta_el = take((size_t)M * HD * sizeof(float));
+  L.theta_el = take((size_t)((M * HD + 255) / 256) * s->n_heads * sizeof(float));
   L.gT = take(rows);
   L.uT = take(rows);
   const size_t st_el = (size_t)bh * L.plan.nt * s->head_dim * L.plan.FhC;

@@ -170,6 +170,9 @@ def make_stack_inputs(sw: StackWorkload, seed: Optional[int] = None) -> list:
 # The aggregation backward at the T = 8192 bench shape: one head of 128,
 # F = 2048, bf16.
 BACKWARD_SHAPE = dict(T=8192, F=2048, H=1, dh=128, seed=5)
+# The WANGO aggregation backward at the T = 8192 WANGO bench shape: two heads
+# of 64, F = 2048, window 256, prefix chunk 128.
+WANGO_BACKWARD_SHAPE = dict(T=8192, F=2048, H=2, dh=64, window=256, chunk=128, seed=6)
 
 
 def aggregate_inputs(T: int, F: int, H: int, dh: int, seed: int):

@@ -6,7 +6,7 @@ differences of the forward oracle) on the same bf16 inputs.  The GPU side runs
 ``wango_aggregate_fwd_train`` (the scan and band that also store the
 denominators), then ``wango_aggregate_bwd``.  Cases cover windows of one to
 five 128-row tiles, windows at or past the sequence end (no older sources),
-several heads, d_h 32 / 64 / 128, prefix chunks 64 and 128, and the null gate.
+one to three heads, d_h 32 / 64 / 128, prefix chunks 64 and 128, and the null gate.
 
 Bars as for the TANGO backward (tests/test_gpu_backward.py, derived there from
 the bf16 storage of u, the gates, gbar, the weights and ds; here the older
@@ -39,6 +39,7 @@ CASES = [
     dict(B=1, T=700, H=1, dh=32, Fh=128, W=256, C=128),
     dict(B=1, T=1000, H=2, dh=64, Fh=192, W=512, C=128),
     dict(B=1, T=200, H=1, dh=64, Fh=128, W=256, C=128),   # window past the end: no older sources
+    dict(B=1, T=300, H=3, dh=32, Fh=128, W=128, C=64),    # odd head count: rows of 96 q/k columns
 ]
 
 

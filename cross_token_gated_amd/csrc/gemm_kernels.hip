@@ -1295,7 +1295,7 @@ hipError_t launch_wango_state_sums(const WStateArgs& w, hipStream_t s) {
   return hipGetLastError();
 }
 
-hipError_t launch_wango_state_readout(const WStateArgs& w, bool, hipStream_t s) {
+hipError_t launch_wango_state_readout(const WStateArgs& w, hipStream_t s) {
   if (w.FhC % 32 != 0) return hipErrorInvalidValue;
   const dim3 grid((unsigned)((int64_t)w.B * w.H * w.nt)), block(kThreads);
   switch (w.dh) {

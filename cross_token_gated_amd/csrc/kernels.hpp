@@ -205,7 +205,7 @@ struct WStateArgs {
   int B, H, dh, Tp, FhC, nt, nb;
 };
 hipError_t launch_wango_state_sums(const WStateArgs& w, hipStream_t s);
-hipError_t launch_wango_state_readout(const WStateArgs& w, bool reverse, hipStream_t s);
+hipError_t launch_wango_state_readout(const WStateArgs& w, hipStream_t s);
 hipError_t launch_wango_state_scan(const WStateArgs& w, bool reverse, hipStream_t s);
 hipError_t launch_wango_bwd_features(const BwdArgs& a, void* fq_perm, void* tmp_rm, const void* q_src,
                                      const void* k_src, void* fk_pk, hipStream_t s);

@@ -1032,7 +1032,7 @@ int wango_aggregate_bwd(const tango_shape_t* shape, int32_t window, int32_t chun
     aa.num_only = 1;
     aa.rev_out = 1;
     if ((e = wango_scan_band(s, window, chunk, L.f, base, a, a.k_rev, a.q_rev, a.u_rev_pk, aa, st)) != hipSuccess)
-      return hip_fail(e, "reversed scan / band (dg)");   // (bwd_last_step() names a feature kernel)
+      return hip_fail(e, "reversed scan / band (dg)");
     // window and near older pairs
     if ((e = launch_tango_ds(a, L.plan, st)) != hipSuccess) return hip_fail(e, "ds tile kernel");
     if ((e = launch_tango_dsmm(a, L.plan, st)) != hipSuccess) return hip_fail(e, "tile product kernel");
@@ -1056,14 +1056,14 @@ int wango_aggregate_bwd(const tango_shape_t* shape, int32_t window, int32_t chun
     w.rows = a.u_rm;
     w.out = a.part + 4 * MHD;
     if ((e = launch_wango_state_sums(w, st)) != hipSuccess || (e = launch_wango_state_scan(w, false, st)) != hipSuccess ||
-        (e = launch_wango_state_readout(w, false, st)) != hipSuccess)
+        (e = launch_wango_state_readout(w, st)) != hipSuccess)
       return hip_fail(e, "prefix states (dp)");
     w.aT = a.pT;
     w.xT = base + L.uT;
     w.rows = a.g_rm;
     w.out = a.part + 5 * MHD;
     if ((e = launch_wango_state_sums(w, st)) != hipSuccess || (e = launch_wango_state_scan(w, true, st)) != hipSuccess ||
-        (e = launch_wango_state_readout(w, true, st)) != hipSuccess)
+        (e = launch_wango_state_readout(w, st)) != hipSuccess)
       return hip_fail(e, "suffix states (da)");
     if ((e = launch_wango_bwd_finish(a, L.plan, reinterpret_cast<float*>(base + L.theta_el), st)) != hipSuccess)
       return hip_fail(e, "backward finish");

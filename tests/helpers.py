@@ -36,6 +36,27 @@ _PERM = np.array([[4 * g + s if s < 4 else 16 + 4 * g + (s - 4) for s in range(8
                   for g in range(4)])
 
 
+def head_pad(fh: int, wango: bool) -> int:
+    """The padded head width Fhp of the gate layouts (include/tango.h): fh when it
+    is a multiple of 64; else WANGO rounds up to 64, TANGO to 512 when that is at
+    most 1.2 fh, else to 64."""
+    if fh % 64 == 0:
+        return fh
+    p512 = (fh + 511) // 512 * 512
+    if not wango and 5 * p512 <= 6 * fh:
+        return p512
+    return (fh + 63) // 64 * 64
+
+
+def pad_heads(g_rows: np.ndarray, n_heads: int, fhp: int) -> np.ndarray:
+    """[M, H*Fh] -> [M, H*Fhp]: head a's column c moved to a*Fhp + c, pad columns zero."""
+    M, F = g_rows.shape
+    fh = F // n_heads
+    out = np.zeros((M, n_heads, fhp), dtype=g_rows.dtype)
+    out[:, :, :fh] = g_rows.reshape(M, n_heads, fh)
+    return out.reshape(M, n_heads * fhp)
+
+
 def pack_gates(g_rows: np.ndarray) -> np.ndarray:
     """[M, F] (M % 32 == 0) -> packed [M/32, 4, F, 8]."""
     M, F = g_rows.shape

@@ -48,10 +48,12 @@ SCALAR_BAR = 5e-2
 
 CASES = [
     dict(B=1, T=200, H=1, dh=128, Fh=256),
-    dict(B=2, T=300, H=2, dh=64, Fh=320),      # head width padded to 512 inside the backward
+    dict(B=2, T=300, H=2, dh=64, Fh=320),
     dict(B=1, T=257, H=4, dh=32, Fh=128),
     dict(B=1, T=1000, H=1, dh=128, Fh=512),
     dict(B=3, T=64, H=2, dh=64, Fh=64),
+    dict(B=1, T=200, H=16, dh=32, Fh=1780),    # the pages' heads: padded to 2048 inside
+    dict(B=1, T=130, H=2, dh=64, Fh=96),       # padded to 128
 ]
 
 
@@ -90,7 +92,7 @@ def test_aggregate_backward(case, null):
     shape = api.make_shape(B, T, 128, F, Hh, dh, torch.bfloat16)
     qd = dev_tensor(H.pad_rows(q.reshape(B, T, HD), Tp), "bf16")
     kd = dev_tensor(H.pad_rows(k.reshape(B, T, HD), Tp), "bf16")
-    gp = dev_tensor(H.pack_gates(H.pad_rows(g, Tp)).reshape(-1), "bf16")
+    gp = dev_tensor(H.pack_gates(H.pad_heads(H.pad_rows(g, Tp), Hh, H.head_pad(Fh, False))).reshape(-1), "bf16")
     th = dev_f32(theta)
     nbd = None if nb is None else dev_f32(nb)
     # the incoming gradient's padded rows hold garbage: they must be ignored

@@ -40,6 +40,7 @@ CASES = [
     dict(B=1, T=1000, H=2, dh=64, Fh=192, W=512, C=128),
     dict(B=1, T=200, H=1, dh=64, Fh=128, W=256, C=128),   # window past the end: no older sources
     dict(B=1, T=300, H=3, dh=32, Fh=128, W=128, C=64),    # odd head count: rows of 96 q/k columns
+    dict(B=1, T=200, H=16, dh=32, Fh=1780, W=64, C=64),   # the pages' geometry: heads padded to 1792
 ]
 
 
@@ -78,7 +79,7 @@ def test_wango_aggregate_backward(case, null):
     shape = api.make_shape(B, T, 128, F, Hh, dh, torch.bfloat16)
     qd = dev_tensor(H.pad_rows(q.reshape(B, T, HD), Tp), "bf16")
     kd = dev_tensor(H.pad_rows(k.reshape(B, T, HD), Tp), "bf16")
-    gp = dev_tensor(H.pack_gates(H.pad_rows(g, Tp)).reshape(-1), "bf16")
+    gp = dev_tensor(H.pack_gates(H.pad_heads(H.pad_rows(g, Tp), Hh, H.head_pad(Fh, True))).reshape(-1), "bf16")
     th = dev_f32(theta)
     nbd = None if nb is None else dev_f32(nb)
     dg_rows = H.pad_rows(dgbar, Tp).reshape(B, Tp, F)

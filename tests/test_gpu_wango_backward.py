@@ -122,6 +122,13 @@ def test_wango_aggregate_backward(case, null):
         dnl_ref = sum(r[4] for r in refs)
         print("dnull", host(dnl), dnl_ref)
         np.testing.assert_allclose(host(dnl), dnl_ref, rtol=SCALAR_BAR, atol=SCALAR_BAR * np.abs(dnl_ref).max())
+    # the saved denominators (window, older prefix and null terms), in e^{-tau} units
+    tau = O.temperature(theta)
+    rows = slice(0, T)
+    den_ref = np.stack([np.stack([O.pair_weights(q[b], k[b], tau, a, rows, "wango", W).sum(axis=1)
+                                  + O.null_weight(nb, a, rows) for a in range(Hh)], axis=1)
+                        for b in range(B)]) * np.exp(-tau)
+    np.testing.assert_allclose(H.unpad_rows(host(den), B, T), den_ref, rtol=1e-2)
 
 
 def test_wango_backward_rejects_unsupported():

@@ -42,6 +42,9 @@ Alongside, with HIP events on the launch stream:
     shape (dq, dk, dg, dtheta from dgbar; the forward that saves the
     denominators runs once, untimed), with its algorithmic flops
     2 * pairs * (2 F + 3 * q/k width) per second against 2.5 PFLOP/s;
+  * backward_wango: the WANGO aggregation's backward pass at the WANGO shape
+    above (two heads of 64, window 256, chunk 128), with the algorithmic
+    flops of wango_backward_flops;
   * cpu_baseline: the float64 CPU oracle on a bounded sample of the same work
     (one of the four TANGO applications, scaled by 4, plus the WANGO block).
 The "traffic" of the two rooflines is the HBM traffic per launch measured by

@@ -66,7 +66,7 @@ struct TileCfg {
 };
 
 template <typename T> struct ProjCfg;
-template <> struct ProjCfg<bf16> : TileCfg<128, 128, 32, 2, 2, 3, 2> {};
+template <> struct ProjCfg<bf16> : TileCfg<128, 128, 32, 2, 2, 2, 2> {};
 template <> struct ProjCfg<float> : TileCfg<64, 128, 32, 2, 2, 1, 1> {};
 template <typename T> struct OutCfg;
 template <> struct OutCfg<bf16> : TileCfg<64, 128, 32, 2, 2, 4, 2> {};

@@ -538,7 +538,7 @@ def main():
     args = parse()
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only; --gpus {args.gpus} is not supported "
-              f"(the block forward needs no collectives; see the sharding notes in DESIGN.md)",
+              f"(the block forward on one sequence batch needs no collectives)",
               file=sys.stderr)
         sys.exit(2)
 

@@ -79,10 +79,12 @@ def shape_of(x: torch.Tensor, w: BlockWeights, rope_base: float = 10000.0,
 
 
 def tango_workspace_size(shape: Shape) -> int:
+    """Bytes of workspace tango_block_fwd needs (0 for an invalid shape)."""
     return int(load().tango_workspace_size(ctypes.byref(shape)))
 
 
 def wango_workspace_size(shape: Shape, window: int, phi_dim: int, chunk: int) -> int:
+    """Bytes of workspace wango_block_fwd needs (0 for invalid arguments)."""
     return int(load().wango_workspace_size(ctypes.byref(shape), window, phi_dim, chunk))
 
 
@@ -107,6 +109,7 @@ def tango_block_fwd(x: torch.Tensor, w: BlockWeights, out: Optional[torch.Tensor
 
 
 def tango_stack_workspace_size(shapes) -> int:
+    """Bytes of workspace tango_stack_fwd needs for these per-set shapes (the largest block's)."""
     arr = (Shape * len(shapes))(*shapes)
     return int(load().tango_stack_workspace_size(arr, len(shapes)))
 
@@ -148,10 +151,12 @@ def wango_block_fwd(x: torch.Tensor, w: BlockWeights, window: int, phi_dim: int,
 # ---- stage entry points ---------------------------------------------------------
 
 def tango_proj_workspace_size(shape: Shape) -> int:
+    """Bytes of scratch the projection stages need (the prepared input rows)."""
     return int(load().tango_proj_workspace_size(ctypes.byref(shape)))
 
 
 def tango_stage_proj(shape: Shape, w: BlockWeights, x, gp, v, qh, kh, ws=None, stream=None) -> None:
+    """KP stage: gates (packed), v, unit q and k from x (include/tango.h layouts)."""
     cw = w.c_struct()
     if ws is None:
         ws = workspace(tango_proj_workspace_size(shape), x.device)
@@ -161,6 +166,7 @@ def tango_stage_proj(shape: Shape, w: BlockWeights, x, gp, v, qh, kh, ws=None, s
 
 def wango_stage_proj(shape: Shape, w: BlockWeights, x, gp, v, qh, kh, fq, fk, ws=None,
                      stream=None) -> None:
+    """KP stage for WANGO: as tango_stage_proj plus the feature maps fq, fk."""
     cw = w.c_struct()
     if ws is None:
         ws = workspace(tango_proj_workspace_size(shape), x.device)
@@ -170,6 +176,7 @@ def wango_stage_proj(shape: Shape, w: BlockWeights, x, gp, v, qh, kh, fq, fk, ws
 
 
 def tango_stage_aggregate(shape: Shape, theta, null_bias, qh, kh, gp, gbar, ws, stream=None) -> None:
+    """KA stage: gbar from q, k and the packed gates."""
     check(load().tango_stage_aggregate(ctypes.byref(shape), _ptr(theta), _ptr(null_bias), _ptr(qh),
                                        _ptr(kh), _ptr(gp), _ptr(gbar), _ptr(ws), ws.numel(),
                                        _stream(stream)))
@@ -184,6 +191,7 @@ def tango_aggregate_fwd_train(shape: Shape, theta, null_bias, qh, kh, gp, gbar, 
 
 
 def tango_aggregate_bwd_workspace_size(shape: Shape) -> int:
+    """Bytes of workspace tango_aggregate_bwd needs (0 unless bf16 and valid)."""
     return int(load().tango_aggregate_bwd_workspace_size(ctypes.byref(shape)))
 
 
@@ -197,40 +205,49 @@ def tango_aggregate_bwd(shape: Shape, theta, null_bias, qh, kh, gp, gbar, den, d
 
 
 def wango_aggregate_fwd_train_workspace_size(shape: Shape, window: int, chunk: int) -> int:
+    """Bytes of workspace wango_aggregate_fwd_train needs (0 for invalid arguments)."""
     return int(load().wango_aggregate_fwd_train_workspace_size(ctypes.byref(shape), window, chunk))
 
 
 def wango_aggregate_fwd_train(shape: Shape, window: int, chunk: int, theta, null_bias, qh, kh, gp, gbar, den,
                               ws, stream=None) -> None:
+    """WANGO aggregation (scan + band) from unit q, k and packed gates into gbar,
+    also storing the denominators den [B*Tp, H] for wango_aggregate_bwd."""
     check(load().wango_aggregate_fwd_train(ctypes.byref(shape), window, chunk, _ptr(theta), _ptr(null_bias),
                                            _ptr(qh), _ptr(kh), _ptr(gp), _ptr(gbar), _ptr(den), _ptr(ws),
                                            ws.numel(), _stream(stream)))
 
 
 def wango_aggregate_bwd_workspace_size(shape: Shape, window: int, chunk: int) -> int:
+    """Bytes of workspace wango_aggregate_bwd needs (0 for invalid arguments)."""
     return int(load().wango_aggregate_bwd_workspace_size(ctypes.byref(shape), window, chunk))
 
 
 def wango_aggregate_bwd(shape: Shape, window: int, chunk: int, theta, null_bias, qh, kh, gp, gbar, den, dgbar,
                         dq, dk, dg, dtheta, dnull, ws, stream=None) -> None:
+    """Gradients of sum(dgbar * gbar) for the WANGO aggregation: dq, dk (float32),
+    dg (bf16), dtheta and dnull (float32, dnull None with null_bias None)."""
     check(load().wango_aggregate_bwd(ctypes.byref(shape), window, chunk, _ptr(theta), _ptr(null_bias), _ptr(qh),
                                      _ptr(kh), _ptr(gp), _ptr(gbar), _ptr(den), _ptr(dgbar), _ptr(dq), _ptr(dk),
                                      _ptr(dg), _ptr(dtheta), _ptr(dnull), _ptr(ws), ws.numel(), _stream(stream)))
 
 
 def tango_stage_out(shape: Shape, w_o, x, gbar, v, out, stream=None) -> None:
+    """KO stage: out = x + (gbar * v) W_o^T."""
     check(load().tango_stage_out(ctypes.byref(shape), _ptr(w_o), _ptr(x), _ptr(gbar), _ptr(v),
                                  _ptr(out), _stream(stream)))
 
 
 def wango_stage_scan(shape: Shape, window: int, chunk: int, fq, fk, gp, n_old, z_old, ws,
                      stream=None) -> None:
+    """KS stage: the older-prefix read-outs n_old, z_old."""
     check(load().wango_stage_scan(ctypes.byref(shape), window, chunk, _ptr(fq), _ptr(fk), _ptr(gp),
                                   _ptr(n_old), _ptr(z_old), _ptr(ws), ws.numel(), _stream(stream)))
 
 
 def wango_stage_band(shape: Shape, theta, null_bias, window: int, chunk: int, qh, kh, gp, n_old,
                      z_old, gbar, stream=None) -> None:
+    """KB stage: the window band combined with n_old, z_old into gbar."""
     check(load().wango_stage_band(ctypes.byref(shape), _ptr(theta), _ptr(null_bias), window, chunk,
                                   _ptr(qh), _ptr(kh), _ptr(gp), _ptr(n_old), _ptr(z_old),
                                   _ptr(gbar), _stream(stream)))
@@ -247,18 +264,22 @@ def decode_shape(B: int, capacity: int, w: BlockWeights, io_dtype: torch.dtype, 
 
 
 def tango_decode_state_size(shape: Shape) -> int:
+    """Bytes of the TANGO decode state (key and gate cache) for shape."""
     return int(load().tango_decode_state_size(ctypes.byref(shape)))
 
 
 def tango_decode_workspace_size(shape: Shape) -> int:
+    """Bytes of scratch one TANGO decode step needs."""
     return int(load().tango_decode_workspace_size(ctypes.byref(shape)))
 
 
 def wango_decode_state_size(shape: Shape, window: int, phi_dim: int) -> int:
+    """Bytes of the WANGO decode state (running sums and window ring)."""
     return int(load().wango_decode_state_size(ctypes.byref(shape), window, phi_dim))
 
 
 def wango_decode_workspace_size(shape: Shape, window: int, phi_dim: int) -> int:
+    """Bytes of scratch one WANGO decode step needs."""
     return int(load().wango_decode_workspace_size(ctypes.byref(shape), window, phi_dim))
 
 

@@ -64,13 +64,18 @@ __global__ __launch_bounds__(256) void bwd_rows_kernel(BwdArgs a) {
   T* u = static_cast<T*>(a.u_rm) + (m * a.H + h) * a.FhC;
   const float rden = live ? 1.0f / a.den[m * a.H + h] : 0.f;
   float dot = 0.f;
-  for (int c = lane; c < a.FhC; c += 64) {
-    float uv = 0.f;
+  // 4 columns per lane (8-byte accesses; Fh and FhC are multiples of 4)
+  for (int c = lane * 4; c < a.FhC; c += 256) {
+    float uv[4] = {0.f, 0.f, 0.f, 0.f};
     if (live && c < a.Fh) {
-      uv = (float)dg[c] * rden;
-      dot += uv * (float)gb[c];
+      const Quad<T> d4 = load_quad<T>(dg + c), g4 = load_quad<T>(gb + c);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        uv[e] = (float)d4[e] * rden;
+        dot += uv[e] * (float)g4[e];
+      }
     }
-    u[c] = (T)uv;
+    store_quad<T>(u + c, cvt_quad<T>(f32x4{uv[0], uv[1], uv[2], uv[3]}));
   }
   dot = wave_sum(dot);
   if (lane == 0) {
@@ -82,34 +87,45 @@ __global__ __launch_bounds__(256) void bwd_rows_kernel(BwdArgs a) {
 // Row-major [rows][ld] -> packed [rows/32][4][ncols][8].  Packed column n is
 // head n / dst_hw, column c = n % dst_hw of it, taken from source column
 // (n / dst_hw) * src_hw + c when c < valid_w, else zero.  rev: packed row
-// b*Tp + i holds source row b*Tp + T-1-i (rows i >= T are zero).
+// b*Tp + i holds source row b*Tp + T-1-i (rows i >= T are zero).  Through LDS
+// in tiles of 32 rows x 32 packed columns (16-byte accesses on both sides):
+// grid nblk * (ncols / 32) workgroups of 128.  ncols and dst_hw are multiples
+// of 32, valid_w of 4, and src_hw >= dst_hw.
 template <typename T>
-__global__ __launch_bounds__(256) void pack_kernel(const T* __restrict__ src, int64_t ld, T* __restrict__ dst,
+__global__ __launch_bounds__(128) void pack_kernel(const T* __restrict__ src, int64_t ld, T* __restrict__ dst,
                                                    int ncols, int dst_hw, int src_hw, int valid_w, int Tp, int T_,
-                                                   int rev, int64_t nblk) {
-  const int64_t id = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  const int64_t per_blk = (int64_t)4 * ncols;
-  if (id >= nblk * per_blk) return;
-  const int64_t blk = id / per_blk;
-  const int grp = (int)((id / ncols) % 4), n = (int)(id % ncols);
-  const int hd = n / dst_hw, c = n % dst_hw;
-  T out[8];
-#pragma unroll
-  for (int s = 0; s < 8; ++s) {
-    const int64_t row = blk * 32 + perm_slot(grp, s);
-    const int64_t b = row / Tp;
+                                                   int rev) {
+  __shared__ T tile[32][32 + 8];
+  const int nct = ncols / 32;
+  const int64_t blk = blockIdx.x / nct;
+  const int n0 = (int)(blockIdx.x % nct) * 32;
+  const int tid = threadIdx.x;
+  {   // 32 rows x 4 pieces of 8 columns
+    const int r = tid >> 2, p = tid & 3;
+    const int64_t row = blk * 32 + r, b = row / Tp;
     const int i = (int)(row % Tp);
-    float v = 0.f;
-    if (c < valid_w) {
-      if (!rev) {
-        v = (float)src[row * ld + (int64_t)hd * src_hw + c];
-      } else if (i < T_) {
-        v = (float)src[(b * Tp + (T_ - 1 - i)) * ld + (int64_t)hd * src_hw + c];
-      }
+    const int n = n0 + p * 8, hd = n / dst_hw, c = n % dst_hw;
+    u32x4 v = {0u, 0u, 0u, 0u};
+    const bool live = !rev || i < T_;
+    if (live && c < valid_w) {
+      const int64_t srow = rev ? b * Tp + (T_ - 1 - i) : row;
+      v = *reinterpret_cast<const u32x4*>(src + srow * ld + (int64_t)hd * src_hw + c);
+      T* e8 = reinterpret_cast<T*>(&v);
+#pragma unroll
+      for (int e = 0; e < 8; ++e)
+        if (c + e >= valid_w) e8[e] = (T)0.f;
     }
-    out[s] = (T)v;
+    *reinterpret_cast<u32x4*>(&tile[r][p * 8]) = v;
   }
-  *reinterpret_cast<u32x4*>(dst + id * 8) = *reinterpret_cast<const u32x4*>(out);
+  __syncthreads();
+  {   // 4 slot groups x 32 columns, 8 rows each
+    const int grp = tid >> 5, cl = tid & 31;
+    T out[8];
+#pragma unroll
+    for (int s8 = 0; s8 < 8; ++s8) out[s8] = tile[perm_slot(grp, s8)][cl];
+    *reinterpret_cast<u32x4*>(dst + ((blk * 4 + grp) * (int64_t)ncols + n0 + cl) * 8) =
+        *reinterpret_cast<const u32x4*>(out);
+  }
 }
 
 // Packed gates [rows/32][4][H*src_hw][8] -> row-major [rows][H][dst_hw]
@@ -419,9 +435,9 @@ hipError_t launch_tango_bwd_prep(const BwdArgs& a, const BwdPlan& p, hipStream_t
   if ((e = hipGetLastError()) != hipSuccess) return e;
   const int64_t nu = nblk * 4 * a.Fp;
   t_step = "pack_kernel";
-  hipLaunchKernelGGL(pack_kernel<T>, dim3((unsigned)ceil_div(nu, 256)), dim3(256), 0, s,
+  hipLaunchKernelGGL(pack_kernel<T>, dim3((unsigned)(nblk * (a.Fp / 32))), dim3(128), 0, s,
                      static_cast<const T*>(a.u_rm), (int64_t)a.H * p.FhC, static_cast<T*>(a.u_rev_pk), a.Fp, a.Fhp,
-                     p.FhC, a.Fh, a.Tp, a.T, 1, nblk);
+                     p.FhC, a.Fh, a.Tp, a.T, 1);
   return hipGetLastError();
 }
 
@@ -459,9 +475,8 @@ hipError_t launch_wango_bwd_features(const BwdArgs& a, void* fq_perm, void* tmp_
   if ((e = hipGetLastError()) != hipSuccess) return e;
   const int64_t nblk = M / 32, nqk = nblk * 4 * HD;
   t_step = "pack_kernel";
-  hipLaunchKernelGGL(pack_kernel<T>, dim3((unsigned)ceil_div(nqk, 256)), dim3(256), 0, s,
-                     static_cast<const T*>(tmp_rm), (int64_t)HD, static_cast<T*>(fk_pk), HD, HD, HD, HD, a.Tp, a.T, 0,
-                     nblk);
+  hipLaunchKernelGGL(pack_kernel<T>, dim3((unsigned)(nblk * (HD / 32))), dim3(128), 0, s,
+                     static_cast<const T*>(tmp_rm), (int64_t)HD, static_cast<T*>(fk_pk), HD, HD, HD, HD, a.Tp, a.T, 0);
   return hipGetLastError();
 }
 

@@ -62,15 +62,17 @@ __device__ __forceinline__ bool pos_ok(const DecArgs& a, int p) {
 // The k-steps go in batches of NB whose loads are all issued before the first
 // product; a batch past the last step reloads the last step and multiplies it
 // by a zeroed A, so there is no branch for the compiler to wait at.
-template <typename T, int MT, int AS, int NB>
-__device__ __forceinline__ void skinny_mma(f32x4 (&acc)[MT], const T* wr, const T* xr, int64_t x_row16,
-                                           int64_t part_stride, int k_first, int k_stride, int steps) {
+template <typename T, int NT, int MT, int AS, int NB>
+__device__ __forceinline__ void skinny_mma(f32x4 (&acc)[NT][MT], const T* wr, int64_t w_row16, const T* xr,
+                                           int64_t x_row16, int64_t part_stride, int k_first, int k_stride,
+                                           int steps) {
   for (int s0 = 0; s0 < steps; s0 += NB) {
-    Frag<T> A[NB], X[NB][MT][AS];
+    Frag<T> A[NB][NT], X[NB][MT][AS];
 #pragma unroll
     for (int u = 0; u < NB; ++u) {
       const int k0 = k_first + min(s0 + u, steps - 1) * k_stride;
-      A[u] = load_frag<T>(wr + k0);
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt) A[u][nt] = load_frag<T>(wr + nt * w_row16 + k0);
 #pragma unroll
       for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
@@ -81,54 +83,66 @@ __device__ __forceinline__ void skinny_mma(f32x4 (&acc)[MT], const T* wr, const 
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int u = 0; u < NB; ++u) {
-      const Frag<T> Au = s0 + u < steps ? A[u] : Frag<T>{};
+      const bool live = s0 + u < steps;
 #pragma unroll
-      for (int mt = 0; mt < MT; ++mt)
+      for (int nt = 0; nt < NT; ++nt) {
+        const Frag<T> Au = live ? A[u][nt] : Frag<T>{};
 #pragma unroll
-        for (int part = 0; part < AS; ++part) mma(acc[mt], Au, X[u][mt][part]);
+        for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+          for (int part = 0; part < AS; ++part) mma(acc[nt][mt], Au, X[u][mt][part]);
+      }
     }
   }
 }
 
 // ---------------------------------------------------------------------------
 // dproj: [g | v | q | k] rows of the new tokens.  Workgroup: 16 rows of the
-// stacked [W_g; W_v; W_q; W_k] against MT tiles of 16 tokens; the k-steps of 32
+// stacked [W_g; W_v; W_q; W_k] (NT tiles of 16; the class boundaries F, 2F and
+// 2F + HD are multiples of 32, so a 32-row block never straddles two weights)
+// against MT tiles of 16 tokens; the k-steps of 32
 // are dealt round robin to the 8 waves, each of which has all of its loads in
 // flight at once, and the accumulators are summed through LDS.  Queries and
 // keys leave with RoPE applied but not normalised (a head's norm would span
 // several workgroups): the aggregation kernels normalise them on read.
 // ---------------------------------------------------------------------------
-template <typename T, int AS, int MT>
+template <typename T, int AS, int MT, int NT>
 __global__ __launch_bounds__(kDecThreads) void dproj_kernel(DecArgs a) {
-  __shared__ f32x4 red[kDecWaves][MT][64];
+  static_assert(NT * MT <= kDecWaves, "one (row tile, token tile) pair per wave in the epilogue");
+  __shared__ f32x4 red[kDecWaves][NT * MT][64];
   const int lane = threadIdx.x & 63, li = lane & 15, lg = lane >> 4;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int F = a.F, HD = a.HD, d = a.d;
-  const int n0 = blockIdx.x * 16;                   // N = 2F + 2HD is a multiple of 16
+  const int nb0 = blockIdx.x * NT * 16;             // N = 2F + 2HD is a multiple of 16 NT
   const int m0 = blockIdx.y * MT * 16;
-  const int cls = n0 < F ? 0 : n0 < 2 * F ? 1 : n0 < 2 * F + HD ? 2 : 3;
-  const int wrow = cls == 0 ? n0 : cls == 1 ? n0 - F : cls == 2 ? n0 - 2 * F : n0 - 2 * F - HD;
+  const int cls = nb0 < F ? 0 : nb0 < 2 * F ? 1 : nb0 < 2 * F + HD ? 2 : 3;
+  const int wrow = cls == 0 ? nb0 : cls == 1 ? nb0 - F : cls == 2 ? nb0 - 2 * F : nb0 - 2 * F - HD;
   const T* W = static_cast<const T*>(cls == 0 ? a.w_g : cls == 1 ? a.w_v : cls == 2 ? a.w_q : a.w_k);
   const T* xs = static_cast<const T*>(a.xs);
 
-  f32x4 acc[MT];
+  f32x4 acc[NT][MT];
 #pragma unroll
-  for (int mt = 0; mt < MT; ++mt) acc[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int nt = 0; nt < NT; ++nt)
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) acc[nt][mt] = f32x4{0.f, 0.f, 0.f, 0.f};
   const int nks = d / 32;
-  skinny_mma<T, MT, AS, 2>(acc, W + (int64_t)(wrow + li) * d + lg * 8, xs + (int64_t)(m0 + li) * d + lg * 8,
-                           (int64_t)16 * d, (int64_t)a.Mp * d, wave * 32, kDecWaves * 32,
-                           (nks - wave + kDecWaves - 1) / kDecWaves);
+  skinny_mma<T, NT, MT, AS, 2>(acc, W + (int64_t)(wrow + li) * d + lg * 8, (int64_t)16 * d,
+                               xs + (int64_t)(m0 + li) * d + lg * 8, (int64_t)16 * d, (int64_t)a.Mp * d, wave * 32,
+                               kDecWaves * 32, (nks - wave + kDecWaves - 1) / kDecWaves);
 #pragma unroll
-  for (int mt = 0; mt < MT; ++mt) red[wave][mt][lane] = acc[mt];
+  for (int nt = 0; nt < NT; ++nt)
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) red[wave][nt * MT + mt][lane] = acc[nt][mt];
   __syncthreads();
-  if (threadIdx.x >= MT * 64) return;
-  // thread (mt, l2) holds rows n0 + 4 lg2 + r of token m0 + 16 mt + li2
-  const int mt = threadIdx.x >> 6, l2 = threadIdx.x & 63, li2 = l2 & 15, lg2 = l2 >> 4;
+  if (threadIdx.x >= NT * MT * 64) return;
+  // thread (nt, mt, l2) holds rows n0 + 4 lg2 + r of token m0 + 16 mt + li2
+  const int pr = threadIdx.x >> 6, l2 = threadIdx.x & 63, li2 = l2 & 15, lg2 = l2 >> 4;
+  const int mt = pr % MT, n0 = nb0 + (pr / MT) * 16;
   const int m = m0 + mt * 16 + li2;
   if (m >= a.B) return;
   f32x4 sum = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-  for (int w2 = 0; w2 < kDecWaves; ++w2) sum += red[w2][mt][l2];
+  for (int w2 = 0; w2 < kDecWaves; ++w2) sum += red[w2][pr][l2];
   const float rs = a.rinv[m];
   float val[4];
 #pragma unroll
@@ -509,15 +523,15 @@ __global__ __launch_bounds__(kDecThreads) void dout_kernel(DecArgs a) {
   const int kq = blockIdx.z;
   const int nks = F / 32;
   const int ks0 = kq * nks / kOutSplit, ks1 = (kq + 1) * nks / kOutSplit;
-  f32x4 acc[MT];
+  f32x4 acc[1][MT];
 #pragma unroll
-  for (int mt = 0; mt < MT; ++mt) acc[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
-  skinny_mma<T, MT, AS, 2>(acc, static_cast<const T*>(a.w_o) + (int64_t)(n0 + li) * F + lg * 8,
-                           static_cast<const T*>(a.gv) + (int64_t)(m0 + li) * F + lg * 8, (int64_t)16 * F,
-                           (int64_t)a.Mp * F, (ks0 + wave) * 32, kDecWaves * 32,
-                           (ks1 - ks0 - wave + kDecWaves - 1) / kDecWaves);
+  for (int mt = 0; mt < MT; ++mt) acc[0][mt] = f32x4{0.f, 0.f, 0.f, 0.f};
+  skinny_mma<T, 1, MT, AS, 2>(acc, static_cast<const T*>(a.w_o) + (int64_t)(n0 + li) * F + lg * 8, 0,
+                              static_cast<const T*>(a.gv) + (int64_t)(m0 + li) * F + lg * 8, (int64_t)16 * F,
+                              (int64_t)a.Mp * F, (ks0 + wave) * 32, kDecWaves * 32,
+                              (ks1 - ks0 - wave + kDecWaves - 1) / kDecWaves);
 #pragma unroll
-  for (int mt = 0; mt < MT; ++mt) red[wave][mt][lane] = acc[mt];
+  for (int mt = 0; mt < MT; ++mt) red[wave][mt][lane] = acc[0][mt];
   __syncthreads();
   const int mt = threadIdx.x >> 6, l2 = threadIdx.x & 63;
   const int m = m0 + mt * 16 + (l2 & 15);
@@ -557,7 +571,10 @@ template <typename T, int AS, int MT>
 hipError_t launch_decode_mt(const DecArgs& a, bool io_bf, hipStream_t s) {
   const int N = 2 * a.F + 2 * a.HD;
   const unsigned mg = (unsigned)ceil_div(a.B, MT * 16);
-  hipLaunchKernelGGL((dproj_kernel<T, AS, MT>), dim3((unsigned)(N / 16), mg), dim3(kDecThreads), 0, s, a);
+  // 32 weight rows per workgroup: half the workgroups (N / 16 would overrun
+  // one round of the 256 CUs at the usual widths) and half the re-reads of the
+  // tokens' operand parts per weight row.
+  hipLaunchKernelGGL((dproj_kernel<T, AS, MT, 2>), dim3((unsigned)(N / 32), mg), dim3(kDecThreads), 0, s, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   if (a.window == 0) {

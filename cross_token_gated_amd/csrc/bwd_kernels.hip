@@ -54,6 +54,11 @@ __device__ __forceinline__ void slot_of_row(int r, int& grp, int& s) {
 // delta head-major [H][M].
 template <typename T>
 __global__ __launch_bounds__(256) void bwd_rows_kernel(BwdArgs a) {
+  if (a.zero_ints) {   // counters of a later kernel (no separate clearing launch)
+    const int64_t nthr = (int64_t)gridDim.x * gridDim.y * 256;
+    for (int64_t z = ((int64_t)blockIdx.y * gridDim.x + blockIdx.x) * 256 + threadIdx.x; z < a.n_zero_ints; z += nthr)
+      a.zero_ints[z] = 0;
+  }
   const int64_t m = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
   const int h = blockIdx.y, lane = threadIdx.x & 63;
   if (m >= (int64_t)a.B * a.Tp) return;

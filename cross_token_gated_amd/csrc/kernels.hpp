@@ -165,6 +165,8 @@ struct BwdArgs {
   float* dk;               // [B*Tp, H*dh]
   float* dtheta;           // [H]
   float* dnull;            // [H] or null
+  int* zero_ints;          // TANGO: the dg aggregation's split counters, cleared by the row prep; or null
+  int64_t n_zero_ints;
   int B, T, Tp, H, dh;
   int F, Fh;               // gate columns (unpadded) in all and per head
   int Fhp, Fp;             // head-padded width of the packed gates, H * Fhp

@@ -769,6 +769,10 @@ int tango_aggregate_bwd(const tango_shape_t* shape, const float* theta, const fl
     a.Fhp = head_pad(s, false);
     a.Fp = (int)Fp;
     a.FhC = L.plan.FhC;
+    if (L.agg.split) {   // the row prep clears the dg aggregation's split counters
+      a.zero_ints = reinterpret_cast<int*>(base + L.counters);
+      a.n_zero_ints = L.agg.n_split_tiles;
+    }
     hipError_t e = launch_tango_bwd_prep(a, L.plan, st);
     if (e != hipSuccess) return hip_fail(e, "backward prep kernels");
     // dg: the aggregation of the time-reversed problem, numerator only
@@ -778,7 +782,7 @@ int tango_aggregate_bwd(const tango_shape_t* shape, const float* theta, const fl
     aa.counters = reinterpret_cast<int*>(base + L.counters);
     aa.num_only = 1;
     aa.rev_out = 1;
-    if ((e = launch_tango_agg(aa, L.agg, true, false, st)) != hipSuccess)
+    if ((e = launch_tango_agg(aa, L.agg, true, true, st)) != hipSuccess)
       return hip_fail(e, "reversed aggregation (dg)");
     if ((e = launch_tango_ds(a, L.plan, st)) != hipSuccess) return hip_fail(e, "ds tile kernel");
     if ((e = launch_tango_dsmm(a, L.plan, st)) != hipSuccess) return hip_fail(e, "dq / dk kernel");

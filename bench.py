@@ -216,7 +216,7 @@ def pages_bench(steps: int, warmup: int, dev, stream) -> dict:
 
     from cross_token_gated_amd import api
     from cross_token_gated_amd import workload as wl
-    from tests.gpu_common import block_weights, dev_tensor
+    from cross_token_gated_amd.device import block_weights, dev_tensor
 
     out = {}
     for name, w in wl.PAGES_WORKLOADS.items():
@@ -274,7 +274,7 @@ def three_set_bench(steps: int, warmup: int, dev, stream, ms_one_set_app: float)
 
     from cross_token_gated_amd import api
     from cross_token_gated_amd import workload as wl
-    from tests.gpu_common import block_weights, dev_tensor
+    from cross_token_gated_amd.device import block_weights, dev_tensor
 
     out = {}
     for name, sw in wl.STACK_WORKLOADS.items():
@@ -323,19 +323,18 @@ def backward_bench(steps: int, warmup: int, dev, stream) -> dict:
     import torch
 
     from cross_token_gated_amd import api
-    from tests import helpers as H
-
+    from cross_token_gated_amd import layouts as lay
     from cross_token_gated_amd import workload as wl
 
     c = wl.BACKWARD_SHAPE
     T, F, Hh, dh = c["T"], c["F"], c["H"], c["dh"]
-    Tp = H.padded_len(T)
+    Tp = lay.padded_len(T)
     q, k, g, dg_in = wl.aggregate_inputs(T, F, Hh, dh, c["seed"])
     bf = torch.bfloat16
-    qd = torch.from_numpy(H.pad_rows(q.reshape(1, T, Hh * dh), Tp).reshape(Tp, Hh * dh)).to(dev).to(bf)
-    kd = torch.from_numpy(H.pad_rows(k.reshape(1, T, Hh * dh), Tp).reshape(Tp, Hh * dh)).to(dev).to(bf)
-    gp = torch.from_numpy(H.pack_gates(H.pad_rows(g[None], Tp)).reshape(-1)).to(dev).to(bf)
-    dgbar = torch.from_numpy(H.pad_rows(dg_in[None], Tp).reshape(Tp, F)).to(dev).to(bf)
+    qd = torch.from_numpy(lay.pad_rows(q.reshape(1, T, Hh * dh), Tp).reshape(Tp, Hh * dh)).to(dev).to(bf)
+    kd = torch.from_numpy(lay.pad_rows(k.reshape(1, T, Hh * dh), Tp).reshape(Tp, Hh * dh)).to(dev).to(bf)
+    gp = torch.from_numpy(lay.pack_gates(lay.pad_rows(g[None], Tp)).reshape(-1)).to(dev).to(bf)
+    dgbar = torch.from_numpy(lay.pad_rows(dg_in[None], Tp).reshape(Tp, F)).to(dev).to(bf)
     theta = torch.full((Hh,), math.log(10.0), dtype=torch.float32, device=dev)
     shape = api.make_shape(1, T, 512, F, Hh, dh, bf)
     gbar = torch.empty((Tp, F), dtype=bf, device=dev)
@@ -398,17 +397,17 @@ def wango_backward_bench(steps: int, warmup: int, dev, stream) -> dict:
 
     from cross_token_gated_amd import api
     from cross_token_gated_amd import workload as wl
-    from tests import helpers as H
+    from cross_token_gated_amd import layouts as lay
 
     c = wl.WANGO_BACKWARD_SHAPE
     T, F, Hh, dh, W, C = c["T"], c["F"], c["H"], c["dh"], c["window"], c["chunk"]
-    Tp = H.padded_len(T)
+    Tp = lay.padded_len(T)
     q, k, g, dg_in = wl.aggregate_inputs(T, F, Hh, dh, c["seed"])
     bf = torch.bfloat16
-    qd = torch.from_numpy(H.pad_rows(q.reshape(1, T, Hh * dh), Tp)).to(dev).to(bf)
-    kd = torch.from_numpy(H.pad_rows(k.reshape(1, T, Hh * dh), Tp)).to(dev).to(bf)
-    gp = torch.from_numpy(H.pack_gates(H.pad_rows(g[None], Tp)).reshape(-1)).to(dev).to(bf)
-    dgbar = torch.from_numpy(H.pad_rows(dg_in[None], Tp)).to(dev).to(bf)
+    qd = torch.from_numpy(lay.pad_rows(q.reshape(1, T, Hh * dh), Tp)).to(dev).to(bf)
+    kd = torch.from_numpy(lay.pad_rows(k.reshape(1, T, Hh * dh), Tp)).to(dev).to(bf)
+    gp = torch.from_numpy(lay.pack_gates(lay.pad_rows(g[None], Tp)).reshape(-1)).to(dev).to(bf)
+    dgbar = torch.from_numpy(lay.pad_rows(dg_in[None], Tp)).to(dev).to(bf)
     theta = torch.full((Hh,), math.log(10.0), dtype=torch.float32, device=dev)
     shape = api.make_shape(1, T, 512, F, Hh, dh, bf)
     gbar = torch.empty((Tp, F), dtype=bf, device=dev)
@@ -461,7 +460,7 @@ def decode_bench(steps: int, warmup: int, dev, stream) -> dict:
 
     from cross_token_gated_amd import api
     from cross_token_gated_amd import workload as wl
-    from tests.gpu_common import TORCH_DTYPE, block_weights
+    from cross_token_gated_amd.device import TORCH_DTYPE, block_weights
 
     out = {}
     for name, w in wl.DECODE_WORKLOADS.items():
@@ -556,7 +555,7 @@ def main():
 
     from cross_token_gated_amd import api
     from cross_token_gated_amd import workload as wl
-    from tests.gpu_common import block_weights, dev_f32, dev_tensor
+    from cross_token_gated_amd.device import block_weights, dev_f32, dev_tensor
 
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     dev = torch.device("cuda:0")

@@ -5,9 +5,9 @@
 // the block output (§2.1 eqs. 2-5 and 3) at the next position p of every
 // sequence from a state kept between steps.  TANGO keeps every unit key and
 // gate so far (eq. 6 sums over the whole prefix).  WANGO keeps the running sums
-// S, z of §2.2 eq. 10 -- the token that leaves the trailing window is added to
-// them when the position advances -- and the keys and gates of the last W + 1
-// positions, a state that does not grow with the position (§6.1).
+// S, z of §2.2 eq. 10 -- when p advances, the key and gate at p - W join S and
+// z -- and the keys and gates of the last W + 1 positions, a state whose size
+// does not depend on the position (§6.1).
 //
 // One step of one block is four or five launches on the caller's stream:
 //   prep  (the forward's row-prep kernel) RMSNorm scale, operand parts of h*gain;

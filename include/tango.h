@@ -117,7 +117,8 @@ size_t tango_workspace_size(const tango_shape_t* shape);
 
 /* TANGO block ([TANGO] §2.1 eqs. 2-5, §2.2 eq. 6): out[B,T,d] = h+ for
  * x[B,T,d] = h.  Apply it R times with out == x for the shared-weight stack of
- * §2.3 eq. 11 (the stream is stored in dtype between applications). */
+ * §2.3 eq. 11 (the stream is then stored in io_dtype between applications:
+ * float32 keeps it unrounded, bfloat16 rounds it once per application). */
 int tango_block_fwd(const tango_shape_t* shape, const tango_weights_t* weights,
                     const void* x, void* out, void* workspace, size_t workspace_bytes,
                     void* hip_stream);
@@ -171,7 +172,7 @@ int wango_block_fwd(const tango_shape_t* shape, const tango_weights_t* weights,
  * since no source lies after its destination (eq. 5) -- and advances a state
  * kept between calls.  TANGO's state is every unit key and gate so far (eq. 6
  * sums over the whole prefix).  WANGO's is the running sums S, z of §2.2
- * eq. 10, to which the token leaving the window is added when the position
+ * eq. 10, which take in the key and gate of position p - W as the position p
  * advances, plus the keys and gates of the last window + 1 positions: a state
  * whose size does not depend on the position (§6.1).
  *

@@ -1,61 +1,13 @@
-"""Shared pieces of the GPU tests: device upload, weight structs, block runs."""
+"""Shared pieces of the GPU tests: the case announcement, and the device
+plumbing of cross_token_gated_amd.device re-exported under its old names."""
 from __future__ import annotations
 
 import sys
 
-import numpy as np
-import torch
-
-from cross_token_gated_amd import api
-from cross_token_gated_amd import workload as wl
-
-TORCH_DTYPE = {"bf16": torch.bfloat16, "f32": torch.float32}
+from cross_token_gated_amd.device import (TORCH_DTYPE, block_weights, dev_f32,  # noqa: F401
+                                          dev_tensor, host, run_workload)
 
 
 def announce(msg: str) -> None:
     """Print the case name before a GPU step, so a failing run names it."""
     print(f"[gpu] {msg}", file=sys.stderr, flush=True)
-
-
-def dev_tensor(a: np.ndarray, dtype: str, device="cuda:0") -> torch.Tensor:
-    t = torch.from_numpy(np.ascontiguousarray(np.asarray(a, dtype=np.float32)))
-    return t.to(device=device).to(TORCH_DTYPE[dtype]).contiguous()
-
-
-def dev_f32(a: np.ndarray, device="cuda:0") -> torch.Tensor:
-    return torch.from_numpy(np.ascontiguousarray(np.asarray(a, dtype=np.float32))).to(device)
-
-
-def host(t: torch.Tensor) -> np.ndarray:
-    return t.detach().float().cpu().numpy().astype(np.float64)
-
-
-def block_weights(w: wl.Workload, inp: wl.Inputs, device="cuda:0") -> api.BlockWeights:
-    return api.BlockWeights(
-        w_g=dev_tensor(inp.w_g, w.dtype, device), w_v=dev_tensor(inp.w_v, w.dtype, device),
-        w_q=dev_tensor(inp.w_q, w.dtype, device), w_k=dev_tensor(inp.w_k, w.dtype, device),
-        w_o=dev_tensor(inp.w_o, w.dtype, device), theta=dev_f32(inp.theta, device),
-        n_heads=w.n_heads, head_dim=w.head_dim,
-        gain=None if inp.gain is None else dev_tensor(inp.gain, w.dtype, device),
-        null_bias=None if inp.null_bias is None else dev_f32(inp.null_bias, device))
-
-
-def run_workload(w: wl.Workload, inp: wl.Inputs, device="cuda:0", x=None, ws=None, stream=None):
-    """All R applications in place on one stream; returns the device output."""
-    bw = block_weights(w, inp, device)
-    if x is None:
-        x = dev_tensor(inp.h, w.io, device)
-    shape = api.shape_of(x, bw, w.rope_base, w.rms_eps)
-    if ws is None:
-        n = (api.tango_workspace_size(shape) if w.mode == "tango"
-             else api.wango_workspace_size(shape, w.window, w.head_dim, w.chunk))
-        assert n > 0
-        ws = api.workspace(n, device)
-    for _ in range(w.repeats):
-        if w.mode == "tango":
-            api.tango_block_fwd(x, bw, out=x, ws=ws, rope_base=w.rope_base, rms_eps=w.rms_eps,
-                                stream=stream)
-        else:
-            api.wango_block_fwd(x, bw, w.window, w.head_dim, w.chunk, out=x, ws=ws,
-                                rope_base=w.rope_base, rms_eps=w.rms_eps, stream=stream)
-    return x

@@ -23,6 +23,7 @@ def _pins():
         P.test_single_token_closed_form,
         P.test_two_token_closed_form,
         lambda: P.test_running_sums_equal_pairwise_old_weights(5, 3),
+        lambda: P.test_blocked_split_halves_equal_cut_pairwise(5, 8),
         P.test_wango_scan_form_equals_direct_form,
         P.test_rope_is_a_rotation_with_relative_logits,
         P.test_counts_reproduce_tables,
@@ -84,8 +85,17 @@ def _tau_unclipped(theta):
 _orig_blocked = O.wango_old_blocked
 
 
-def _blocked_shifted(qh, kh, g, tau, window, block=64):
-    return _orig_blocked(qh, kh, g, tau, window - 1 if window > 1 else window, block)
+def _blocked_shifted(qh, kh, g, tau, window, block=64, split=False):
+    return _orig_blocked(qh, kh, g, tau, window - 1 if window > 1 else window, block, split)
+
+
+def _blocked_split_all_in_state(qh, kh, g, tau, window, block=64, split=False):
+    """The whole older prefix attributed to the state read-out: the sum of the
+    two halves is unchanged, only the split is wrong."""
+    n, z, ni, zi = _orig_blocked(qh, kh, g, tau, window, block, split=True)
+    if split:
+        return n + ni, z + zi, np.zeros_like(ni), np.zeros_like(zi)
+    return n + ni, z + zi
 
 
 def _counts_no_scan(T, d, F, H, dh, vocab, repeats, mode, window=0):
@@ -111,6 +121,7 @@ MUTATIONS = {
     "RMSNorm uses sum for mean": ("rms_norm", _rms_sum),
     "temperature not clipped": ("temperature", _tau_unclipped),
     "blocked running sums one step late": ("wango_old_blocked", _blocked_shifted),
+    "block split puts the in-block sources in the state": ("wango_old_blocked", _blocked_split_all_in_state),
     "MAC count drops the running-sum term": ("forward_macs", _counts_no_scan),
     "stack applies each set one application late": ("block_stack_sets", _stack_sets_one_late),
 }

@@ -267,6 +267,44 @@ def test_running_sums_equal_pairwise_old_weights(W, block):
     assert rel(n_blk, n_pw) < 1e-12 and rel(z_blk, z_pw) < 1e-12
 
 
+def _phi_scalar(u, dh):
+    """The feature map of eq. 8 with the readings of the oracle's header, one
+    value at a time: ELU with alpha 1, plus 1 + 1e-4, floored at 1e-4, over
+    sqrt(d_h)."""
+    elu = u if u > 0 else math.exp(u) - 1.0
+    return max(elu + 1.0 + 1e-4, 1e-4) / math.sqrt(dh)
+
+
+@pytest.mark.parametrize("W, block", [(1, 2), (3, 4), (4, 4), (8, 2), (5, 8), (17, 4)])
+def test_blocked_split_halves_equal_cut_pairwise(W, block):
+    """Each half of wango_old_blocked(split=True) on its own, against pure-Python
+    pairwise loops: for a destination i >= W, with c_i = block * floor((i - W) /
+    block), the state half holds the older sources j < c_i (the running sums of
+    eq. 10 read at the block boundary) and the in-block half the sources
+    c_i <= j <= i - W; both are zero for i < W.  (Their sum, the whole older
+    prefix, is pinned by test_running_sums_equal_pairwise_old_weights.)"""
+    rng = np.random.default_rng(40 + 3 * W + block)
+    T, H, dh, fh = 29, 2, 4, 3
+    qh, kh, g = _qkg(rng, T=T, H=H, dh=dh, fh=fh)
+    tau = np.array([10.0, 3.0])
+    n_st, z_st, n_in, z_in = O.wango_old_blocked(qh, kh, g, tau, W, block, split=True)
+    e_st, ez_st = np.zeros((T, H * fh)), np.zeros((T, H))
+    e_in, ez_in = np.zeros((T, H * fh)), np.zeros((T, H))
+    for a in range(H):
+        st = math.sqrt(tau[a])
+        for i in range(W, T):
+            c = block * ((i - W) // block)
+            for j in range(0, i - W + 1):
+                w = sum(_phi_scalar(st * qh[i, a, e], dh) * _phi_scalar(st * kh[j, a, e], dh)
+                        for e in range(dh))
+                tn, tz = (e_st, ez_st) if j < c else (e_in, ez_in)
+                for f in range(fh):
+                    tn[i, a * fh + f] += w * g[j, a * fh + f]
+                tz[i, a] += w
+    assert rel(n_st, e_st) < 1e-12 and rel(z_st, ez_st) < 1e-12
+    assert rel(n_in, e_in) < 1e-12 and rel(z_in, ez_in) < 1e-12
+
+
 def test_wango_scan_form_equals_direct_form():
     rng = np.random.default_rng(13)
     d, F, H, dh, T = 32, 24, 2, 8, 300

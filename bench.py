@@ -1,7 +1,7 @@
 """Benchmark of the TANGO / WANGO block forward on one MI355X.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline] [--no-decode] [--no-pages]
-                    [--no-backward] [--no-three-set]
+                    [--no-backward] [--no-three-set] [--no-configs]
 
 One step runs every part of the block forward once at T = 8192 tokens:
   * TANGO, bf16 compute, B = 1, T = 8192, d = 512, F = 2048, q/k width 128,
@@ -15,16 +15,20 @@ sequence tokens per second: (8192 + 8192) tokens / step time.
 
 Alongside, with HIP events on the launch stream:
   * roofline: the TANGO aggregation kernel (the dominant one), useful MFMA
-    flops 2 * (causal pairs) * (q/k width + F) per launch over its median
-    launch time (each launch between its own events), against 2.5 PFLOP/s
-    dense bf16;
+    flops 2 * (causal pairs) * (q/k width + F) per launch over its mean
+    launch time (each launch between its own events on the launch stream; the
+    median, minimum and maximum beside it), against 2.5 PFLOP/s dense bf16;
   * roofline_scan: the WANGO running-sum scan (two launches), algorithmic
-    HBM bytes (q, k, g read once; n_old, z_old written once) over its median
+    HBM bytes (q, k, g read once; n_old, z_old written once) over its mean
     time, against 8 TB/s.  A 512 MiB read runs before each timed scan, so its
     inputs come from HBM, not from the 256 MB Infinity Cache that the
     producing projection would otherwise leave them in (the warm-cache median
     is reported beside it).  The flush reads rather than fills: a fill leaves
     dirty lines whose write-back would land in the timed launch;
+  * other_configs: the TANGO B = 8, T = 2048 block and the WANGO B = 2,
+    T = 65,536, window 512 stack of 8 applications, as tokens per second of
+    the whole forward, with the long stack's scan per application from a
+    flushed cache against 8 TB/s;
   * decode: one autoregressive decode step (every layer) at position 8192 of
     the decode workloads -- TANGO, 16 sequences, 4 stacked layers each with its
     own key/gate cache; WANGO, 64 sequences, window 256 -- as decoded tokens
@@ -84,6 +88,8 @@ def parse():
     ap.add_argument("--no-pages", action="store_true", help="skip the pages'-geometry forward")
     ap.add_argument("--no-backward", action="store_true", help="skip the aggregation backward")
     ap.add_argument("--no-three-set", action="store_true", help="skip the three-set stack")
+    ap.add_argument("--no-configs", action="store_true",
+                    help="skip the B=8 T=2048 TANGO and B=2 T=65536 WANGO workloads")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a plain 256 MiB device copy (for counter calibration)")
     return ap.parse_args()
@@ -135,6 +141,32 @@ def scan_bytes(w) -> float:
     return float(w.B * w.T * (2 * hd * 2 + w.d_gate * 2 + w.d_gate * 4 + w.n_heads * 4))
 
 
+def host_cpu() -> dict:
+    """The host's CPU model (from /proc/cpuinfo), the threads this process may
+    run on, and the BLAS numpy calls (library, version, threads)."""
+    model = "unknown"
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    blas = {"library": "unknown", "version": None, "threads": None}
+    try:
+        import numpy  # noqa: F401  (loads the BLAS that threadpoolctl then reports)
+        from threadpoolctl import threadpool_info
+        for i in threadpool_info():
+            if i.get("user_api") == "blas":
+                blas = {"library": i.get("internal_api"), "version": i.get("version"),
+                        "threads": i.get("num_threads"), "architecture": i.get("architecture")}
+                break
+    except Exception:  # noqa: BLE001
+        pass
+    return {"cpu_model": model, "affinity_threads": len(os.sched_getaffinity(0)), "blas": blas}
+
+
 def cpu_baseline(wt, wg) -> dict:
     """The float64 oracle, untuned, on a bounded sample of the step."""
     import numpy as np
@@ -143,11 +175,8 @@ def cpu_baseline(wt, wg) -> dict:
     from cross_token_gated_amd import workload as wl
     from tests import helpers as H
 
-    try:
-        from threadpoolctl import threadpool_info
-        cores = max(int(i.get("num_threads", 1)) for i in threadpool_info()) if threadpool_info() else 1
-    except Exception:  # noqa: BLE001
-        cores = len(os.sched_getaffinity(0))
+    info = host_cpu()
+    cores = info["blas"]["threads"] or info["affinity_threads"]
     # one TANGO application (timed x repeats) plus the WANGO application,
     # repeated until about 10 s of host time have passed; the mean is reported
     cases = []
@@ -168,6 +197,7 @@ def cpu_baseline(wt, wg) -> dict:
     secs = step_secs / runs
     tokens = wt.tokens + wg.tokens
     return {"value": tokens / secs, "unit": "tokens/s", "cores": cores, "kind": "oracle",
+            "cpu_model": info["cpu_model"], "blas": info["blas"], "affinity_threads": info["affinity_threads"],
             "sample": (f"one of the {wt.repeats} TANGO T={wt.T} applications (time x{wt.repeats}) "
                        f"plus the WANGO T={wg.T} application, float64 numpy, mean of {runs} runs "
                        f"({spent:.1f} s of host time); {secs:.1f} s for one step")}
@@ -260,6 +290,82 @@ def pages_bench(steps: int, warmup: int, dev, stream) -> dict:
         print(f"[bench] pages geometry {name}: {ms:.2f} ms per forward ({w.repeats} applications), "
               f"{w.tokens / (ms * 1e-3):.0f} tokens/s, {macs / (ms * 1e-3) / 1e12:.0f} T MAC/s of the pages' "
               f"count", file=sys.stderr, flush=True)
+        del ws, x, ping, pong
+        torch.cuda.empty_cache()
+    return out
+
+
+def configs_bench(steps: int, warmup: int, dev, stream, timed_each) -> dict:
+    """The other two block workloads at full size: TANGO B = 8, T = 2048 (one
+    application) and WANGO B = 2, T = 65,536, window 512, eight shared
+    applications -- tokens per second of the whole forward (median of `steps`
+    forwards, each between its own events).  For the long WANGO workload also
+    its running-sum scan per application from a flushed cache (its 1.68 GB do
+    not fit the Infinity Cache anyway), algorithmic bytes over the median
+    launch time against 8 TB/s."""
+    import torch
+
+    from cross_token_gated_amd import api
+    from cross_token_gated_amd import workload as wl
+    from cross_token_gated_amd.device import block_weights, dev_tensor
+
+    out = {}
+    for name in ("tango_bf16_b8_t2048", "wango_bf16_b2_t65536_w512_r8"):
+        w = wl.WORKLOADS[name]
+        inp = wl.make_inputs(w)
+        bw = block_weights(w, inp, dev)
+        x = dev_tensor(inp.h, w.io, dev)
+        ping, pong = torch.empty_like(x), torch.empty_like(x)
+        shape = api.shape_of(x, bw, w.rope_base, w.rms_eps)
+        n = (api.tango_workspace_size(shape) if w.mode == "tango"
+             else api.wango_workspace_size(shape, w.window, w.head_dim, w.chunk))
+        ws = api.workspace(n, dev)
+
+        def fwd():
+            src = x
+            for r in range(w.repeats):
+                dst = ping if r % 2 == 0 else pong
+                if w.mode == "tango":
+                    api.tango_block_fwd(src, bw, out=dst, ws=ws, rope_base=w.rope_base, rms_eps=w.rms_eps,
+                                        stream=stream)
+                else:
+                    api.wango_block_fwd(src, bw, w.window, w.head_dim, w.chunk, out=dst, ws=ws,
+                                        rope_base=w.rope_base, rms_eps=w.rms_eps, stream=stream)
+                src = dst
+
+        for _ in range(warmup):
+            fwd()
+        ms, ms_mean, _, _ = timed_each(fwd, steps, flush=False)
+        rec = {"ms_per_forward": ms, "ms_per_forward_mean": ms_mean, "tokens_per_s": w.tokens / (ms * 1e-3),
+               "applications": w.repeats, "B": w.B, "T": w.T, "d_gate": w.d_gate,
+               "heads": w.n_heads, "head_dim": w.head_dim}
+        msg = f"[bench] {name}: {ms:.3f} ms per forward, {w.tokens / (ms * 1e-3):.0f} tokens/s"
+        if w.mode == "wango":
+            M = w.B * api.padded_len(w.T)
+            HD = w.n_heads * w.head_dim
+            gp = torch.empty(M * w.d_gate, dtype=torch.bfloat16, device=dev)
+            v = torch.empty(M, w.d_gate, dtype=torch.float32, device=dev)
+            qh = torch.empty(M, HD, dtype=torch.bfloat16, device=dev)
+            kh = torch.empty(M, HD, dtype=torch.bfloat16, device=dev)
+            fq = torch.empty(M, HD, dtype=torch.bfloat16, device=dev)
+            fk = torch.empty(M * HD, dtype=torch.bfloat16, device=dev)
+            api.wango_stage_proj(shape, bw, x, gp, v, qh, kh, fq, fk, ws=ws, stream=stream)
+            del v, qh, kh
+            n_old = torch.empty(M * w.d_gate, dtype=torch.float32, device=dev)
+            z_old = torch.empty(M, w.n_heads, dtype=torch.float32, device=dev)
+            scan = lambda: api.wango_stage_scan(shape, w.window, w.chunk, fq, fk, gp, n_old, z_old,  # noqa: E731
+                                                ws, stream=stream)
+            sms, sms_mean, smin, smax = timed_each(scan, steps, flush=True)
+            sb = scan_bytes(w)
+            rec["scan"] = {"bound": "hbm", "bytes_per_launch": sb, "ms_per_launch": sms,
+                           "ms_per_launch_mean": sms_mean, "ms_min": smin, "ms_max": smax,
+                           "achieved": sb / (sms * 1e-3) / 1e9, "peak": PEAK_HBM_BYTES / 1e9, "unit": "GB/s",
+                           "frac": sb / (sms * 1e-3) / PEAK_HBM_BYTES, "cache": "flushed before each launch"}
+            msg += (f"; scan {sms * 1e3:.0f} us per application ({sb / 1e6:.0f} MB, "
+                    f"{100 * rec['scan']['frac']:.1f}% of HBM peak)")
+            del gp, fq, fk, n_old, z_old
+        out[name] = rec
+        print(msg, file=sys.stderr, flush=True)
         del ws, x, ping, pong
         torch.cuda.empty_cache()
     return out
@@ -603,7 +709,7 @@ def main():
     M = wt.B * Tp
     F, HD = wt.d_gate, wt.n_heads * wt.head_dim
     gp = torch.empty(M * F, dtype=torch.bfloat16, device=dev)
-    v = torch.empty(M, F, dtype=torch.bfloat16, device=dev)
+    v = torch.empty(M, F, dtype=torch.float32, device=dev)
     qh = torch.empty(M, HD, dtype=torch.bfloat16, device=dev)
     kh = torch.empty(M, HD, dtype=torch.bfloat16, device=dev)
     gbar = torch.empty(M, F, dtype=torch.bfloat16, device=dev)
@@ -644,7 +750,7 @@ def main():
         torch.cuda.synchronize()
         t = sorted(a.elapsed_time(b) for a, b in ev)
         med = t[n // 2] if n % 2 else 0.5 * (t[n // 2 - 1] + t[n // 2])
-        return med, sum(t) / n
+        return med, sum(t) / n, t[0], t[-1]
 
     def tango_only():
         src = xt
@@ -656,14 +762,14 @@ def main():
     ms_tango = timed(tango_only, loops)
     ms_wango = timed(lambda: api.wango_block_fwd(xg, bg, wg.window, wg.head_dim, wg.chunk, out=outg,
                                                  ws=ws_g, stream=stream), loops)
-    ms_agg, ms_agg_mean = timed_each(lambda: api.tango_stage_aggregate(st, bt.theta, None, qh, kh, gp,
+    ms_agg_med, ms_agg, agg_min, agg_max = timed_each(lambda: api.tango_stage_aggregate(st, bt.theta, None, qh, kh, gp,
                                                                        gbar, ws_t, stream=stream),
                                      loops, flush=False)
     # WANGO scan inputs (two heads of 64)
     Mg = wg.B * api.padded_len(wg.T)
     HDg = wg.n_heads * wg.head_dim
     gpg = torch.empty(Mg * wg.d_gate, dtype=torch.bfloat16, device=dev)
-    vg = torch.empty(Mg, wg.d_gate, dtype=torch.bfloat16, device=dev)
+    vg = torch.empty(Mg, wg.d_gate, dtype=torch.float32, device=dev)
     qg = torch.empty(Mg, HDg, dtype=torch.bfloat16, device=dev)
     kg = torch.empty(Mg, HDg, dtype=torch.bfloat16, device=dev)
     fqg = torch.empty(Mg, HDg, dtype=torch.bfloat16, device=dev)
@@ -673,8 +779,8 @@ def main():
     z_old = torch.empty(Mg, wg.n_heads, dtype=torch.float32, device=dev)
     scan_call = lambda: api.wango_stage_scan(sg, wg.window, wg.chunk, fqg, fkg, gpg, n_old, z_old,  # noqa: E731
                                              ws_g, stream=stream)
-    ms_scan_warm, _ = timed_each(scan_call, loops, flush=False)
-    ms_scan, ms_scan_mean = timed_each(scan_call, loops, flush=True)
+    ms_scan_warm_med, ms_scan_warm, _, _ = timed_each(scan_call, loops, flush=False)
+    ms_scan_med, ms_scan, scan_min, scan_max = timed_each(scan_call, loops, flush=True)
 
     agg_flops = tango_flops(wt)
     achieved = agg_flops / (ms_agg * 1e-3)
@@ -709,13 +815,15 @@ def main():
                      "achieved": achieved / 1e12, "peak": PEAK_BF16_FLOPS / 1e12, "unit": "TFLOP/s",
                      "frac": achieved / PEAK_BF16_FLOPS, "traffic": recorded_traffic("agg_kernel"),
                      "flops_per_launch": agg_flops, "ms_per_launch": ms_agg,
-                     "ms_per_launch_mean": ms_agg_mean},
+                     "ms_per_launch_median": ms_agg_med, "ms_min": agg_min, "ms_max": agg_max,
+                     "launches": loops, "time_basis": "mean of the launches, each between its own events"},
         "roofline_scan": {"kernel": "WANGO running-sum scan (2 launches, T=8192)", "bound": "hbm",
                           "achieved": s_ach / 1e9, "peak": PEAK_HBM_BYTES / 1e9, "unit": "GB/s",
                           "frac": s_ach / PEAK_HBM_BYTES, "traffic": recorded_traffic("scan"),
                           "bytes_per_launch": sbytes, "ms_per_launch": ms_scan,
-                          "ms_per_launch_mean": ms_scan_mean, "cache": "flushed before each launch",
-                          "ms_per_launch_warm_cache": ms_scan_warm},
+                          "ms_per_launch_median": ms_scan_med, "ms_min": scan_min, "ms_max": scan_max,
+                          "launches": loops, "time_basis": "mean of the launches, each between its own events",
+                          "cache": "flushed before each launch", "ms_per_launch_warm_cache": ms_scan_warm},
     }
     print(f"[bench] tango {ms_tango:.3f} ms, wango {ms_wango:.3f} ms, aggregation {ms_agg:.3f} ms "
           f"({result['roofline']['frac'] * 100:.1f}% of bf16 peak), scan {ms_scan:.4f} ms "
@@ -727,6 +835,8 @@ def main():
         for _ in range(3):
             dst.copy_(src)
         torch.cuda.synchronize()
+    if not args.no_configs:
+        result["other_configs"] = configs_bench(min(loops, 5), 1, dev, stream, timed_each)
     if not args.no_decode:
         result["decode"] = decode_bench(loops, min(args.warmup, 3), dev, stream)
     if not args.no_pages:

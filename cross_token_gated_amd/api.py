@@ -255,7 +255,7 @@ def _check_proj(shape: Shape, w: BlockWeights, x, gp, v, qh, kh, wango: bool):
     check_tensor(x, "x", device=dev, dtype=z.io, min_numel=z.x)
     w.check(shape.d_model, dev)
     check_tensor(gp, "gp", device=dev, dtype=z.dt, min_numel=z.M * z.Fp)
-    check_tensor(v, "v", device=dev, dtype=z.dt, min_numel=z.M * z.F)
+    check_tensor(v, "v", device=dev, dtype=torch.float32, min_numel=z.M * z.F)
     check_tensor(qh, "qh", device=dev, dtype=z.dt, min_numel=z.M * z.HD)
     check_tensor(kh, "kh", device=dev, dtype=z.dt, min_numel=z.M * z.HD)
     return dev, z
@@ -392,7 +392,7 @@ def tango_stage_out(shape: Shape, w_o, x, gbar, v, out, stream=None) -> None:
     check_tensor(out, "out", device=dev, dtype=z.io, min_numel=z.x)
     check_tensor(w_o, "w_o", device=dev, dtype=z.dt, shape=(shape.d_model, shape.d_gate))
     check_tensor(gbar, "gbar", device=dev, dtype=z.dt, min_numel=z.M * z.F)
-    check_tensor(v, "v", device=dev, dtype=z.dt, min_numel=z.M * z.F)
+    check_tensor(v, "v", device=dev, dtype=torch.float32, min_numel=z.M * z.F)
     check(load().tango_stage_out(ctypes.byref(shape), _ptr(w_o), _ptr(x), _ptr(gbar), _ptr(v),
                                  _ptr(out), _stream(stream)))
 

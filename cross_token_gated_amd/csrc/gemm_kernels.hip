@@ -328,23 +328,28 @@ __device__ __forceinline__ int pad_col(int n, int Fh, int Fhp) {
   return Fh == Fhp ? n : n + (n / Fh) * (Fhp - Fh);
 }
 
+// v is float32 for both dtypes (the projection stores it unrounded), so a
+// piece of PE gates meets PE / 4 16-byte loads of v.
 template <typename T, int P, int AS> struct GatedSource {
   static constexpr int PE = piece_elems<T>();
+  static constexpr int VP = PE / 4;
   struct raw {
-    u32x4 g, v;
+    u32x4 g;
+    u32x4 v[VP];
   };
   const T* gptr[P];     // at the piece's row and column
-  const T* vptr[P];
+  const float* vptr[P];
   __device__ __forceinline__ void fetch(raw& r, int p, int k0) const {
     r.g = *reinterpret_cast<const u32x4*>(gptr[p] + k0);
-    r.v = *reinterpret_cast<const u32x4*>(vptr[p] + k0);
+#pragma unroll
+    for (int q = 0; q < VP; ++q) r.v[q] = *reinterpret_cast<const u32x4*>(vptr[p] + k0 + 4 * q);
   }
   __device__ __forceinline__ Parts<AS> convert(const raw& r, int) const {
     const T* ge = reinterpret_cast<const T*>(&r.g);
-    const T* ve = reinterpret_cast<const T*>(&r.v);
+    const float* ve = reinterpret_cast<const float*>(&r.v[0]);
     float e[PE];
 #pragma unroll
-    for (int q = 0; q < PE; ++q) e[q] = tof<T>(ge[q]) * tof<T>(ve[q]);
+    for (int q = 0; q < PE; ++q) e[q] = tof<T>(ge[q]) * ve[q];
     return split_parts<T, AS, PE>(e);
   }
 };
@@ -567,18 +572,18 @@ void proj_kernel(ProjArgs args) {
         store_frag<T>(gp + packed_offset(mp / 32 + rb, grp, pad_col(n, args.Fh, args.Fhp), args.Fp), out);
       }
     }
-    // features: row-major [M_pad, F]
+    // features: row-major [M_pad, F], float32 (unrounded: the output GEMM
+    // forms gbar * v in float32, and a bf16 v would add one more rounding
+    // that compounds through stacked applications)
     if (n0 + CF::BN > F && n0 < 2 * F) {
-      T* v = static_cast<T*>(args.v);
-      constexpr int P8 = CF::BN / 8;
-      for (int it = tid; it < kEpiRows * P8; it += kThreads) {
-        const int row = it / P8, c = (it % P8) * 8;
+      float* v = static_cast<float*>(args.v);
+      constexpr int P4 = CF::BN / 4;
+      for (int it = tid; it < kEpiRows * P4; it += kThreads) {
+        const int row = it / P4, c = (it % P4) * 4;
         const int n = n0 + c;
         if (n < F || n >= 2 * F) continue;
-        Frag<T> out;
-#pragma unroll
-        for (int s = 0; s < 8; ++s) out[s] = cvt<T>(Cs[row * kCStride + c + s]);
-        store_frag<T>(v + (mp + row) * F + (n - F), out);
+        *reinterpret_cast<f32x4*>(v + (mp + row) * F + (n - F)) =
+            *reinterpret_cast<const f32x4*>(&Cs[row * kCStride + c]);
       }
     }
     // queries and keys: RoPE on interleaved pairs, then unit length per head.
@@ -697,7 +702,7 @@ __global__ __launch_bounds__(kThreads) void out_kernel(OutArgs args) {
     const PiecePos<CF, T> pp = piece_pos<CF, T>(tid, p);
     const int64_t off = (m0 + pp.row) * F + pp.kp * piece_elems<T>();
     sa.gptr[p] = static_cast<const T*>(args.gbar) + off;
-    sa.vptr[p] = static_cast<const T*>(args.v) + off;
+    sa.vptr[p] = static_cast<const float*>(args.v) + off;
   }
   RowSource<T, PB> sb;
 #pragma unroll

@@ -175,7 +175,7 @@ Layout make_layout(const tango_shape_t* s, bool wango, int32_t window, int32_t c
     return o;
   };
   L.gp = take(M * F * es);
-  L.v = take(M * Fv * es);
+  L.v = take(M * Fv * sizeof(float));   // v is float32 for both dtypes
   L.qh = take(M * HD * es);
   L.kh = take(M * HD * es);
   L.gbar = take(M * Fv * es);
@@ -362,7 +362,7 @@ int stage_proj_common(const tango_shape_t* s, const tango_weights_t* weights, co
                        {weights->rms_gain, d * es, "rms_gain"},
                        {wango ? weights->theta : nullptr, s->n_heads * sizeof(float), "theta"}};
   const size_t Fp = gate_pad(s, wango);
-  const Range outs[] = {{gp, M * Fp * es, "gp"}, {v, M * F * es, "v"}, {qh, M * HD * es, "qh"},
+  const Range outs[] = {{gp, M * Fp * es, "gp"}, {v, M * F * sizeof(float), "v"}, {qh, M * HD * es, "qh"},
                         {kh, M * HD * es, "kh"}, {ws, ps.total, "workspace"},
                         {fq, M * HD * es, "fq"}, {fk, M * HD * es, "fk"}};
   if ((rc = check_ranges(ins, 7, outs, wango ? 7 : 5, nullptr, nullptr))) return rc;
@@ -1086,7 +1086,7 @@ int tango_stage_out(const tango_shape_t* shape, const void* w_o, const void* x, 
     const size_t d = s->d_model, F = s->d_gate;
     const size_t xb = (size_t)s->batch * s->seq_len * d * elem_size(s->io_dtype);
     const Range ins[] = {{w_o, d * F * es, "w_o"}, {x, xb, "x"}, {gbar, M * F * es, "gbar"},
-                         {v, M * F * es, "v"}};
+                         {v, M * F * sizeof(float), "v"}};
     const Range outs[] = {{out, xb, "out"}};
     if ((rc = check_ranges(ins, 4, outs, 1, x, out))) return rc;
     if ((rc = ensure_init())) return rc;

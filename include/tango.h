@@ -60,7 +60,7 @@
 extern "C" {
 #endif
 
-#define TANGO_ABI_VERSION 7
+#define TANGO_ABI_VERSION 8
 
 typedef enum { TANGO_F32 = 0, TANGO_BF16 = 1 } tango_dtype_t;
 
@@ -233,7 +233,10 @@ int tango_version(void);                      /* TANGO_ABI_VERSION              
  *   F'        = n_heads * Fhp: gp and n_old have F' columns, head a's gate
  *               column c at a * Fhp + c, and the projection stages write zeros
  *               into the gates' pad columns c >= Fh;
- *   V, gbar   = [B, Tp, d_gate] row-major, dtype (not padded);
+ *   V         = [B, Tp, d_gate] row-major, float32 for both dtypes (the
+ *               output stage forms gbar * v in float32, so v is kept
+ *               unrounded; not padded);
+ *   gbar      = [B, Tp, d_gate] row-major, dtype (not padded);
  *   qh, kh    = [B, Tp, H*d_h] row-major, dtype, unit length per head;
  *   gp        = the gates g in the source-packed layout [B][Tp/32][4][F'][8]:
  *               element (b, blk, grp, f, s) holds g[b, t, f] for

@@ -46,7 +46,7 @@ def _upload_intermediates(w, g, v, qh, kh):
     Tp = H.padded_len(w.T)
     HD = w.n_heads * w.head_dim
     gp = dev_tensor(H.pack_gates(H.pad_rows(g, Tp)), w.dtype)
-    vd = dev_tensor(H.pad_rows(v, Tp), w.dtype)
+    vd = dev_tensor(H.pad_rows(v, Tp), "f32")   # v is float32 for both dtypes
     qd = dev_tensor(H.pad_rows(qh.reshape(w.B, w.T, HD), Tp), w.dtype)
     kd = dev_tensor(H.pad_rows(kh.reshape(w.B, w.T, HD), Tp), w.dtype)
     return gp, vd, qd, kd
@@ -75,7 +75,7 @@ def test_stage_proj(case, with_gain):
     M = w.B * Tp
     dt = x.dtype
     gp = torch.full((M * F,), float("nan"), dtype=dt, device="cuda:0")
-    v = torch.full((M, F), float("nan"), dtype=dt, device="cuda:0")
+    v = torch.full((M, F), float("nan"), dtype=torch.float32, device="cuda:0")
     qh = torch.full((M, HD), float("nan"), dtype=dt, device="cuda:0")
     kh = torch.full((M, HD), float("nan"), dtype=dt, device="cuda:0")
     ws = api.workspace(api.tango_proj_workspace_size(shape), "cuda:0")
@@ -95,7 +95,12 @@ def test_stage_proj(case, with_gain):
     q_ref = np.stack([p["qh"].reshape(w.T, HD) for p in parts])
     k_ref = np.stack([p["kh"].reshape(w.T, HD) for p in parts])
     H.check_stage(g_got, g_ref, w.dtype, "g")
-    H.check_stage(v_got, v_ref, w.dtype, "v")
+    # v is stored in float32 for both dtypes: what remains is the float32
+    # accumulation and, in bf16, the two-part operand (h * gain as hi + lo, about
+    # 2^-16 relative), so 1e-4 on the rms and 1e-3 on the largest entries
+    rv, mv = H.rms_ratio(v_got, v_ref), H.err_ratio(v_got, v_ref)
+    print(f"v: rms ratio {rv:.2e}, max ratio {mv:.2e}")
+    assert rv <= 1e-4 and mv <= 1e-3
     H.check_stage(q_got, q_ref, w.dtype, "q")
     H.check_stage(k_got, k_ref, w.dtype, "k")
 
@@ -171,7 +176,7 @@ def test_stage_out(case, inplace):
     shape = api.make_shape(w.B, w.T, w.d_model, w.d_gate, w.n_heads, w.head_dim, x.dtype)
     announce(f"stage_out {case} inplace={inplace}")
     api.tango_stage_out(shape, dev_tensor(inp.w_o, w.dtype), x, dev_tensor(H.pad_rows(gbar, Tp), w.dtype),
-                        dev_tensor(H.pad_rows(v, Tp), w.dtype), out)
+                        dev_tensor(H.pad_rows(v, Tp), "f32"), out)
     torch.cuda.synchronize()
     ref = np.asarray(inp.h, np.float64) + (gbar * v) @ np.asarray(inp.w_o, np.float64).T
     assert H.err_ratio(host(out), ref) < H.tol(w.dtype)
@@ -231,7 +236,7 @@ def test_stage_wango_proj(case):
     M = w.B * Tp
     dt = x.dtype
     bufs = dict(gp=torch.full((M * F,), float("nan"), dtype=dt, device="cuda:0"),
-                v=torch.full((M, F), float("nan"), dtype=dt, device="cuda:0"),
+                v=torch.full((M, F), float("nan"), dtype=torch.float32, device="cuda:0"),
                 qh=torch.full((M, HD), float("nan"), dtype=dt, device="cuda:0"),
                 kh=torch.full((M, HD), float("nan"), dtype=dt, device="cuda:0"),
                 fq=torch.full((M, HD), float("nan"), dtype=dt, device="cuda:0"),

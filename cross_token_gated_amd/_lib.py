@@ -29,7 +29,10 @@ EXPORTS = [
     "tango_stack_workspace_size", "tango_stack_fwd",
     "wango_aggregate_fwd_train_workspace_size", "wango_aggregate_fwd_train",
     "wango_aggregate_bwd_workspace_size", "wango_aggregate_bwd",
+    "wango_decode_step_noalloc",
 ]
+
+NOALLOC_SCRATCH_BYTES = 16 << 20   # TANGO_NOALLOC_SCRATCH_BYTES
 
 
 class Shape(ctypes.Structure):
@@ -88,6 +91,7 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
         "wango_decode_state_size": (sz, [S, i32, i32]),
         "wango_decode_workspace_size": (sz, [S, i32, i32]),
         "wango_decode_step": (ctypes.c_int, [S, W, i32, i32, vp, vp, vp, vp, sz, vp, sz, vp]),
+        "wango_decode_step_noalloc": (ctypes.c_int, [S, W, i32, i32, vp, vp, vp, vp, sz, vp]),
         "tango_aggregate_fwd_train": (ctypes.c_int, [S, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]),
         "tango_aggregate_bwd_workspace_size": (sz, [S]),
         "tango_stack_workspace_size": (sz, [S, i32]),

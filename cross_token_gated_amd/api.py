@@ -487,3 +487,13 @@ def wango_decode_step(shape: Shape, w: BlockWeights, window: int, phi_dim: int, 
     check(load().wango_decode_step(ctypes.byref(shape), ctypes.byref(cw), window, phi_dim, _ptr(pos),
                                    _ptr(x), _ptr(out), _ptr(state), _nbytes(state), _ptr(ws), _nbytes(ws),
                                    _stream(stream)))
+
+
+def wango_decode_step_noalloc(shape: Shape, w: BlockWeights, window: int, phi_dim: int, pos: torch.Tensor,
+                              x: torch.Tensor, out: torch.Tensor, state: torch.Tensor, stream=None) -> None:
+    """wango_decode_step with the library's own scratch array (no workspace and
+    no allocation; see include/tango.h for its size limit and sharing rules)."""
+    _check_decode(shape, w, pos, x, out, state)
+    cw = w.c_struct()
+    check(load().wango_decode_step_noalloc(ctypes.byref(shape), ctypes.byref(cw), window, phi_dim, _ptr(pos),
+                                           _ptr(x), _ptr(out), _ptr(state), _nbytes(state), _stream(stream)))

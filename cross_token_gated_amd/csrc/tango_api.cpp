@@ -15,6 +15,13 @@
 
 #include "kernels.hpp"
 
+// Scratch of wango_decode_step_noalloc: one array per device, in the code
+// object, held until the process ends.  On the host, `scratch` names a host
+// stand-in, not the device array: its device address comes from
+// hipGetSymbolAddress in ensure_init (with the device current), and only that
+// address is ever handed to a kernel.
+static __device__ __align__(256) unsigned char scratch[TANGO_NOALLOC_SCRATCH_BYTES];
+
 namespace {
 
 using namespace tango;
@@ -203,10 +210,11 @@ Layout make_layout(const tango_shape_t* s, bool wango, int32_t window, int32_t c
   return L;
 }
 
-// ---- one-time kernel attributes (per device) ----------------------------------
+// ---- one-time set-up (per device) -----------------------------------------------
 
 std::mutex g_init_mu;
 bool g_init_done[64];
+void* g_scratch[64];   // device address of `scratch` on each device
 
 int ensure_init() {
   int dev = 0;
@@ -216,8 +224,22 @@ int ensure_init() {
   std::lock_guard<std::mutex> lk(g_init_mu);
   if (g_init_done[dev]) return TANGO_OK;
   if ((e = gemm_kernels_init()) != hipSuccess) return hip_fail(e, "kernel attributes");
+  void* ptr = nullptr;
+  if ((e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch))) != hipSuccess)
+    return hip_fail(e, "hipGetSymbolAddress(scratch)");
+  if (!ptr || ((uintptr_t)ptr & 255u) != 0)
+    return fail(TANGO_ERR_HIP, "the scratch array of device %d is not 256-byte aligned", dev);
+  g_scratch[dev] = ptr;
   g_init_done[dev] = true;
   return TANGO_OK;
+}
+
+// The current device's scratch array (after ensure_init), or NULL.
+void* device_scratch() {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return nullptr;
+  std::lock_guard<std::mutex> lk(g_init_mu);
+  return g_init_done[dev] ? g_scratch[dev] : nullptr;
 }
 
 // ---- argument blocks ------------------------------------------------------------
@@ -1237,22 +1259,34 @@ DecLayout make_dec_layout(const tango_shape_t* s, bool wango, int32_t window) {
   return L;
 }
 
+// lib_scratch: the scratch is the library's own array of the current device
+// (ws and ws_bytes are ignored; the size is checked against the array), taken
+// after every argument has been validated.
 int decode_common(const tango_shape_t* s, const tango_weights_t* w, bool wango, int32_t window,
                   int32_t phi_dim, const int32_t* pos, const void* x, void* out, void* state,
-                  size_t state_bytes, void* ws, size_t ws_bytes, void* stream) {
+                  size_t state_bytes, void* ws, size_t ws_bytes, void* stream, bool lib_scratch = false) {
   int rc = check_decode(s, wango, window, phi_dim);
   if (rc) return rc;
   if ((rc = check_weights(w, true))) return rc;
   if (!pos || !x || !out) return fail(TANGO_ERR_NULL, "pos, x or out is NULL");
   if (!state) return fail(TANGO_ERR_NULL, "state is NULL");
-  if (!ws) return fail(TANGO_ERR_NULL, "workspace is NULL");
+  if (!lib_scratch && !ws) return fail(TANGO_ERR_NULL, "workspace is NULL");
   const DecLayout L = make_dec_layout(s, wango, window);
   if (state_bytes < L.state_total)
     return fail(TANGO_ERR_WORKSPACE, "state of %zu bytes is smaller than the %zu needed", state_bytes,
                 L.state_total);
-  if (ws_bytes < L.ws_total)
+  if (lib_scratch) {
+    if (L.ws_total > TANGO_NOALLOC_SCRATCH_BYTES)
+      return fail(TANGO_ERR_WORKSPACE,
+                  "this decode step needs %zu bytes of scratch; the library's array holds %zu "
+                  "(TANGO_NOALLOC_SCRATCH_BYTES): decode fewer sequences per call or pass a workspace",
+                  L.ws_total, (size_t)TANGO_NOALLOC_SCRATCH_BYTES);
+    ws = nullptr;   // taken below, once the arguments are valid
+    ws_bytes = 0;
+  } else if (ws_bytes < L.ws_total) {
     return fail(TANGO_ERR_WORKSPACE, "workspace of %zu bytes is smaller than the %zu needed", ws_bytes,
                 L.ws_total);
+  }
   const size_t es = elem_size(s->dtype);
   const size_t d = s->d_model, F = s->d_gate, HD = (size_t)s->n_heads * s->head_dim;
   const size_t xb = (size_t)s->batch * d * elem_size(s->io_dtype);
@@ -1267,6 +1301,7 @@ int decode_common(const tango_shape_t* s, const tango_weights_t* w, bool wango, 
                        {w->theta, s->n_heads * sizeof(float), "theta"},
                        {w->null_bias, s->n_heads * sizeof(float), "null_bias"}};
   const Range outs[] = {{out, xb, "out"}, {state, L.state_total, "state"}, {ws, L.ws_total, "workspace"}};
+  const int n_outs = lib_scratch ? 2 : 3;   // the library's array cannot alias the caller's buffers
   // pos only needs 4-byte alignment
   for (const Range& r : ins)
     if (r.p && r.p != pos && !aligned(r.p)) return fail(TANGO_ERR_ALIGN, "%s is not 16-byte aligned", r.name);
@@ -1275,10 +1310,14 @@ int decode_common(const tango_shape_t* s, const tango_weights_t* w, bool wango, 
   int n16 = 0;
   for (const Range& r : ins)
     if (r.p != pos) ins16[n16++] = r;
-  if ((rc = check_ranges(ins16, n16, outs, 3, x, out))) return rc;
-  for (const Range& o : outs)
-    if (overlap(o, ins[1])) return fail(TANGO_ERR_ALIAS, "%s overlaps pos", o.name);
+  if ((rc = check_ranges(ins16, n16, outs, n_outs, x, out))) return rc;
+  for (int o = 0; o < n_outs; ++o)
+    if (overlap(outs[o], ins[1])) return fail(TANGO_ERR_ALIAS, "%s overlaps pos", outs[o].name);
   if ((rc = ensure_init())) return rc;
+  if (lib_scratch) {
+    ws = device_scratch();
+    if (!ws) return fail(TANGO_ERR_HIP, "no scratch array on the current device");
+  }
 
   hipStream_t st = static_cast<hipStream_t>(stream);
   const bool bf = s->dtype == TANGO_BF16, io_bf = s->io_dtype == TANGO_BF16;
@@ -1376,6 +1415,15 @@ int wango_decode_step(const tango_shape_t* shape, const tango_weights_t* weights
   return guarded([&] {
     return decode_common(shape, weights, true, window, phi_dim, pos, x, out, state, state_bytes, workspace,
                          workspace_bytes, hip_stream);
+  });
+}
+
+int wango_decode_step_noalloc(const tango_shape_t* shape, const tango_weights_t* weights, int32_t window,
+                              int32_t phi_dim, const int32_t* pos, const void* x, void* out, void* state,
+                              size_t state_bytes, void* hip_stream) {
+  return guarded([&] {
+    return decode_common(shape, weights, true, window, phi_dim, pos, x, out, state, state_bytes, nullptr, 0,
+                         hip_stream, true);
   });
 }
 

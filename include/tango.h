@@ -60,7 +60,7 @@
 extern "C" {
 #endif
 
-#define TANGO_ABI_VERSION 8
+#define TANGO_ABI_VERSION 9
 
 typedef enum { TANGO_F32 = 0, TANGO_BF16 = 1 } tango_dtype_t;
 
@@ -213,6 +213,31 @@ size_t wango_decode_workspace_size(const tango_shape_t* shape, int32_t window, i
 int wango_decode_step(const tango_shape_t* shape, const tango_weights_t* weights, int32_t window,
                       int32_t phi_dim, const int32_t* pos, const void* x, void* out, void* state,
                       size_t state_bytes, void* workspace, size_t workspace_bytes, void* hip_stream);
+
+/* ---- WANGO decode step that allocates nothing ---------------------------
+ *
+ * For callers that cannot allocate device memory or provide a workspace: code
+ * under HIP graph capture, tight serving loops, harnesses that forbid
+ * allocation.  Same arguments, results and errors as wango_decode_step
+ * without the workspace: its scratch is a library-owned device array of
+ * TANGO_NOALLOC_SCRATCH_BYTES bytes, one per GPU the library runs on, held
+ * from the first call on that GPU until the process ends.  The call allocates
+ * nothing (no hipMalloc, no allocating library routine).
+ *   - A shape whose scratch, wango_decode_workspace_size(shape, window,
+ *     phi_dim), exceeds TANGO_NOALLOC_SCRATCH_BYTES is TANGO_ERR_WORKSPACE
+ *     before anything runs (at d_model 512 and d_gate 2048: up to 640
+ *     sequences per call).
+ *   - Every call on one GPU shares that GPU's array, which keeps the last
+ *     call's contents.  The step clears what must start at zero (its output
+ *     counters) in its own first kernel and writes everything else before
+ *     reading it, so calls ordered on one stream are independent; calls that
+ *     can overlap on one GPU (unordered streams, or several host threads)
+ *     race on the array and must be serialised by the caller.
+ *   - The state is the caller's, as for wango_decode_step. */
+#define TANGO_NOALLOC_SCRATCH_BYTES ((size_t)16 << 20)
+int wango_decode_step_noalloc(const tango_shape_t* shape, const tango_weights_t* weights, int32_t window,
+                              int32_t phi_dim, const int32_t* pos, const void* x, void* out, void* state,
+                              size_t state_bytes, void* hip_stream);
 
 /* ---- Diagnostics --------------------------------------------------------- */
 

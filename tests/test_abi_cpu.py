@@ -236,3 +236,33 @@ def test_binding_argument_counts_match_the_header(lib):
         params = m.group(1).strip()
         n = 0 if params in ("", "void") else params.count(",") + 1
         assert len(getattr(lib, name).argtypes) == n, name
+
+
+def test_noalloc_decode_validates_before_touching_the_device(lib):
+    """wango_decode_step_noalloc checks every argument, and that the step fits
+    the library's scratch array, before it takes the array (the fake pointers
+    would fault if anything ran, and there is no device here to take it from)."""
+    code = _lib.STATUS_CODE
+    w = weights()
+    s = shape(batch=64, d_gate=2048, n_heads=2, head_dim=64)
+    ns = lib.wango_decode_state_size(ctypes.byref(s), 256, 64)
+    need = lib.wango_decode_workspace_size(ctypes.byref(s), 256, 64)
+    assert 0 < need <= _lib.NOALLOC_SCRATCH_BYTES
+    pos = FAKE + 0x90000000
+
+    def call(sh=s, window=256, phi=64, p=pos, x=FAKE, out=FAKE + 0x60000000, st=FAKE + 0x100000000, n=ns):
+        return lib.wango_decode_step_noalloc(ctypes.byref(sh), ctypes.byref(w), window, phi, p, x, out, st, n, None)
+    assert call(p=None) == code["TANGO_ERR_NULL"]
+    assert call(st=None) == code["TANGO_ERR_NULL"]
+    assert call(n=ns - 1) == code["TANGO_ERR_WORKSPACE"]
+    assert call(phi=32) == code["TANGO_ERR_SHAPE"]
+    assert call(window=0) == code["TANGO_ERR_SHAPE"]
+    assert call(out=FAKE + 0x100000000 + 4096) == code["TANGO_ERR_ALIAS"]
+    # a batch whose scratch exceeds the array is refused, with the sizes named
+    big = shape(batch=4096, d_gate=2048, n_heads=2, head_dim=64)
+    assert lib.wango_decode_workspace_size(ctypes.byref(big), 256, 64) > _lib.NOALLOC_SCRATCH_BYTES
+    nsb = lib.wango_decode_state_size(ctypes.byref(big), 256, 64)
+    assert call(sh=big, n=nsb) == code["TANGO_ERR_WORKSPACE"]
+    assert b"TANGO_NOALLOC_SCRATCH_BYTES" in lib.tango_last_error()
+    m = re.search(r"#define TANGO_NOALLOC_SCRATCH_BYTES \(\(size_t\)(\d+) << (\d+)\)", open(HEADER).read())
+    assert int(m.group(1)) << int(m.group(2)) == _lib.NOALLOC_SCRATCH_BYTES

@@ -16,19 +16,20 @@ sequence tokens per second: (8192 + 8192) tokens / step time.
 Alongside, with HIP events on the launch stream:
   * roofline: the TANGO aggregation kernel (the dominant one), useful MFMA
     flops 2 * (causal pairs) * (q/k width + F) per launch over its mean
-    launch time (each launch between its own events on the launch stream; the
-    median, minimum and maximum beside it), against 2.5 PFLOP/s dense bf16;
+    launch time: five batches of back-to-back launches, one event pair per
+    batch on the launch stream (an event pair around every launch would add
+    the dispatch latency, about 10 us, to each), the fastest and slowest batch
+    beside it; against 2.5 PFLOP/s dense bf16;
   * roofline_scan: the WANGO running-sum scan (two launches), algorithmic
     HBM bytes (q, k, g read once; n_old, z_old written once) over its mean
-    time, against 8 TB/s.  A 512 MiB read runs before each timed scan, so its
-    inputs come from HBM, not from the 256 MB Infinity Cache that the
-    producing projection would otherwise leave them in (the warm-cache median
-    is reported beside it).  The flush reads rather than fills: a fill leaves
-    dirty lines whose write-back would land in the timed launch;
+    time, against 8 TB/s, timed the same way with a cold cache: the launches
+    cycle through 8 copies of the scan's inputs and outputs, so every launch
+    reads data the others have evicted from the 256 MB Infinity Cache (the
+    warm-cache time, one copy over and over, is reported beside it);
   * other_configs: the TANGO B = 8, T = 2048 block and the WANGO B = 2,
     T = 65,536, window 512 stack of 8 applications, as tokens per second of
-    the whole forward, with the long stack's scan per application from a
-    flushed cache against 8 TB/s;
+    the whole forward, with the long stack's scan per application (cold:
+    each launch moves 1.68 GB) against 8 TB/s;
   * decode: one autoregressive decode step (every layer) at position 8192 of
     the decode workloads -- TANGO, 16 sequences, 4 stacked layers each with its
     own key/gate cache; WANGO, 64 sequences, window 256 -- as decoded tokens
@@ -295,14 +296,15 @@ def pages_bench(steps: int, warmup: int, dev, stream) -> dict:
     return out
 
 
-def configs_bench(steps: int, warmup: int, dev, stream, timed_each) -> dict:
+def configs_bench(steps: int, warmup: int, dev, stream, timed_batches) -> dict:
     """The other two block workloads at full size: TANGO B = 8, T = 2048 (one
     application) and WANGO B = 2, T = 65,536, window 512, eight shared
-    applications -- tokens per second of the whole forward (median of `steps`
-    forwards, each between its own events).  For the long WANGO workload also
-    its running-sum scan per application from a flushed cache (its 1.68 GB do
-    not fit the Infinity Cache anyway), algorithmic bytes over the median
-    launch time against 8 TB/s."""
+    applications -- tokens per second of the whole forward (mean over batches
+    of back-to-back forwards).  For the long WANGO workload also its
+    running-sum scan per application, launched back to back: each launch moves
+    1.68 GB, so the previous one has evicted its inputs from the 256 MB
+    Infinity Cache and every launch reads from HBM; algorithmic bytes over the
+    mean launch time against 8 TB/s."""
     import torch
 
     from cross_token_gated_amd import api
@@ -335,8 +337,9 @@ def configs_bench(steps: int, warmup: int, dev, stream, timed_each) -> dict:
 
         for _ in range(warmup):
             fwd()
-        ms, ms_mean, _, _ = timed_each(fwd, steps, flush=False)
-        rec = {"ms_per_forward": ms, "ms_per_forward_mean": ms_mean, "tokens_per_s": w.tokens / (ms * 1e-3),
+        ms, ms_lo, ms_hi = timed_batches(fwd, steps, 3)
+        rec = {"ms_per_forward": ms, "ms_batch_min": ms_lo, "ms_batch_max": ms_hi,
+               "tokens_per_s": w.tokens / (ms * 1e-3),
                "applications": w.repeats, "B": w.B, "T": w.T, "d_gate": w.d_gate,
                "heads": w.n_heads, "head_dim": w.head_dim}
         msg = f"[bench] {name}: {ms:.3f} ms per forward, {w.tokens / (ms * 1e-3):.0f} tokens/s"
@@ -355,12 +358,13 @@ def configs_bench(steps: int, warmup: int, dev, stream, timed_each) -> dict:
             z_old = torch.empty(M, w.n_heads, dtype=torch.float32, device=dev)
             scan = lambda: api.wango_stage_scan(shape, w.window, w.chunk, fq, fk, gp, n_old, z_old,  # noqa: E731
                                                 ws, stream=stream)
-            sms, sms_mean, smin, smax = timed_each(scan, steps, flush=True)
+            sms, smin, smax = timed_batches(scan, steps, 3)
             sb = scan_bytes(w)
             rec["scan"] = {"bound": "hbm", "bytes_per_launch": sb, "ms_per_launch": sms,
-                           "ms_per_launch_mean": sms_mean, "ms_min": smin, "ms_max": smax,
+                           "ms_batch_min": smin, "ms_batch_max": smax,
                            "achieved": sb / (sms * 1e-3) / 1e9, "peak": PEAK_HBM_BYTES / 1e9, "unit": "GB/s",
-                           "frac": sb / (sms * 1e-3) / PEAK_HBM_BYTES, "cache": "flushed before each launch"}
+                           "frac": sb / (sms * 1e-3) / PEAK_HBM_BYTES,
+                           "cache": "cold: each launch moves 1.68 GB, over 6x the Infinity Cache"}
             msg += (f"; scan {sms * 1e3:.0f} us per application ({sb / 1e6:.0f} MB, "
                     f"{100 * rec['scan']['frac']:.1f}% of HBM peak)")
             del gp, fq, fk, n_old, z_old
@@ -726,31 +730,23 @@ def main():
         torch.cuda.synchronize()
         return a.elapsed_time(b) / n
 
-    # 512 MiB, twice the MI355X Infinity Cache: reading it evicts every earlier
-    # line from the L2s and the cache before a cold-cache launch.  A read, not a
-    # fill: a fill leaves the cache full of dirty lines whose write-back would
-    # then be charged to the timed kernel (a cold 32 MiB read measured 16 us
-    # after a fill, 9 us after a read of the same buffer, 6 us warm).
-    flush_buf = torch.ones(1 << 27, dtype=torch.float32, device=dev)
-    flush_sink = torch.empty((), dtype=torch.float32, device=dev)
-
-    def timed_each(fn, n, flush):
-        """Median and mean of n launches of fn, each bracketed by its own events
-        on the launch stream; with flush, a 512 MiB read runs before each."""
+    def timed_batches(fn, n, batches):
+        """Mean launch time of fn over `batches` batches of n back-to-back
+        launches, one event pair around each batch on the launch stream (events
+        around single launches would add the dispatch latency, ~10 us, to each):
+        (mean over all launches, fastest batch mean, slowest batch mean)."""
         fn()
         torch.cuda.synchronize()
         ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-              for _ in range(n)]
+              for _ in range(batches)]
         for a, b in ev:
-            if flush:
-                torch.sum(flush_buf, 0, out=flush_sink)
             a.record(stream)
-            fn()
+            for _ in range(n):
+                fn()
             b.record(stream)
         torch.cuda.synchronize()
-        t = sorted(a.elapsed_time(b) for a, b in ev)
-        med = t[n // 2] if n % 2 else 0.5 * (t[n // 2 - 1] + t[n // 2])
-        return med, sum(t) / n, t[0], t[-1]
+        t = [a.elapsed_time(b) / n for a, b in ev]
+        return sum(t) / batches, min(t), max(t)
 
     def tango_only():
         src = xt
@@ -762,10 +758,16 @@ def main():
     ms_tango = timed(tango_only, loops)
     ms_wango = timed(lambda: api.wango_block_fwd(xg, bg, wg.window, wg.head_dim, wg.chunk, out=outg,
                                                  ws=ws_g, stream=stream), loops)
-    ms_agg_med, ms_agg, agg_min, agg_max = timed_each(lambda: api.tango_stage_aggregate(st, bt.theta, None, qh, kh, gp,
-                                                                       gbar, ws_t, stream=stream),
-                                     loops, flush=False)
-    # WANGO scan inputs (two heads of 64)
+    n_batches = 5
+    ms_agg, agg_min, agg_max = timed_batches(
+        lambda: api.tango_stage_aggregate(st, bt.theta, None, qh, kh, gp, gbar, ws_t, stream=stream),
+        loops, n_batches)
+    # WANGO scan inputs (two heads of 64).  For the cold-cache time the scan
+    # cycles through NCOPY copies of its inputs and outputs: between two uses of
+    # one copy the other copies move about 7 x 105 MB through the memory system,
+    # more than twice the 256 MB Infinity Cache, so every launch reads its inputs
+    # from HBM, and the launches still run back to back between one event pair.
+    NCOPY = 8
     Mg = wg.B * api.padded_len(wg.T)
     HDg = wg.n_heads * wg.head_dim
     gpg = torch.empty(Mg * wg.d_gate, dtype=torch.bfloat16, device=dev)
@@ -775,12 +777,25 @@ def main():
     fqg = torch.empty(Mg, HDg, dtype=torch.bfloat16, device=dev)
     fkg = torch.empty(Mg * HDg, dtype=torch.bfloat16, device=dev)
     api.wango_stage_proj(sg, bg, xg, gpg, vg, qg, kg, fqg, fkg, ws=ws_g, stream=stream)
-    n_old = torch.empty(Mg * wg.d_gate, dtype=torch.float32, device=dev)
-    z_old = torch.empty(Mg, wg.n_heads, dtype=torch.float32, device=dev)
-    scan_call = lambda: api.wango_stage_scan(sg, wg.window, wg.chunk, fqg, fkg, gpg, n_old, z_old,  # noqa: E731
-                                             ws_g, stream=stream)
-    ms_scan_warm_med, ms_scan_warm, _, _ = timed_each(scan_call, loops, flush=False)
-    ms_scan_med, ms_scan, scan_min, scan_max = timed_each(scan_call, loops, flush=True)
+    copies = [(fqg, fkg, gpg)] + [(fqg.clone(), fkg.clone(), gpg.clone()) for _ in range(NCOPY - 1)]
+    outs_s = [(torch.empty(Mg * wg.d_gate, dtype=torch.float32, device=dev),
+               torch.empty(Mg, wg.n_heads, dtype=torch.float32, device=dev)) for _ in range(NCOPY)]
+    turn = [0]
+
+    def scan_cold():
+        k = turn[0] % NCOPY
+        turn[0] += 1
+        fq_k, fk_k, gp_k = copies[k]
+        api.wango_stage_scan(sg, wg.window, wg.chunk, fq_k, fk_k, gp_k, outs_s[k][0], outs_s[k][1], ws_g,
+                             stream=stream)
+
+    def scan_warm():
+        api.wango_stage_scan(sg, wg.window, wg.chunk, fqg, fkg, gpg, outs_s[0][0], outs_s[0][1], ws_g,
+                             stream=stream)
+
+    ms_scan_warm, _, _ = timed_batches(scan_warm, loops, n_batches)
+    ms_scan, scan_min, scan_max = timed_batches(scan_cold, loops, n_batches)
+    del copies, outs_s
 
     agg_flops = tango_flops(wt)
     achieved = agg_flops / (ms_agg * 1e-3)
@@ -815,15 +830,21 @@ def main():
                      "achieved": achieved / 1e12, "peak": PEAK_BF16_FLOPS / 1e12, "unit": "TFLOP/s",
                      "frac": achieved / PEAK_BF16_FLOPS, "traffic": recorded_traffic("agg_kernel"),
                      "flops_per_launch": agg_flops, "ms_per_launch": ms_agg,
-                     "ms_per_launch_median": ms_agg_med, "ms_min": agg_min, "ms_max": agg_max,
-                     "launches": loops, "time_basis": "mean of the launches, each between its own events"},
+                     "ms_batch_min": agg_min, "ms_batch_max": agg_max,
+                     "launches": loops * n_batches,
+                     "time_basis": f"mean launch time over {n_batches} batches of {loops} back-to-back launches, "
+                                   "one event pair per batch on the launch stream"},
         "roofline_scan": {"kernel": "WANGO running-sum scan (2 launches, T=8192)", "bound": "hbm",
                           "achieved": s_ach / 1e9, "peak": PEAK_HBM_BYTES / 1e9, "unit": "GB/s",
                           "frac": s_ach / PEAK_HBM_BYTES, "traffic": recorded_traffic("scan"),
                           "bytes_per_launch": sbytes, "ms_per_launch": ms_scan,
-                          "ms_per_launch_median": ms_scan_med, "ms_min": scan_min, "ms_max": scan_max,
-                          "launches": loops, "time_basis": "mean of the launches, each between its own events",
-                          "cache": "flushed before each launch", "ms_per_launch_warm_cache": ms_scan_warm},
+                          "ms_batch_min": scan_min, "ms_batch_max": scan_max,
+                          "launches": loops * n_batches,
+                          "time_basis": f"mean launch time over {n_batches} batches of {loops} back-to-back launches, "
+                                        "one event pair per batch on the launch stream",
+                          "cache": f"cold: the launches cycle through {NCOPY} copies of the inputs and outputs "
+                                   f"(about {NCOPY * sbytes / 1e6:.0f} MB, over 3x the 256 MB Infinity Cache)",
+                          "ms_per_launch_warm_cache": ms_scan_warm},
     }
     print(f"[bench] tango {ms_tango:.3f} ms, wango {ms_wango:.3f} ms, aggregation {ms_agg:.3f} ms "
           f"({result['roofline']['frac'] * 100:.1f}% of bf16 peak), scan {ms_scan:.4f} ms "
@@ -836,7 +857,7 @@ def main():
             dst.copy_(src)
         torch.cuda.synchronize()
     if not args.no_configs:
-        result["other_configs"] = configs_bench(min(loops, 5), 1, dev, stream, timed_each)
+        result["other_configs"] = configs_bench(min(loops, 5), 1, dev, stream, timed_batches)
     if not args.no_decode:
         result["decode"] = decode_bench(loops, min(args.warmup, 3), dev, stream)
     if not args.no_pages:

@@ -26,6 +26,9 @@ Alongside, with HIP events on the launch stream:
     cycle through 8 copies of the scan's inputs and outputs, so every launch
     reads data the others have evicted from the 256 MB Infinity Cache (the
     warm-cache time, one copy over and over, is reported beside it);
+  * gemm_reference: context for the projection and output GEMMs -- the
+    vendor library (torch.matmul) on plain bf16 GEMMs of the same shapes next
+    to this build's stage calls (off the measured path);
   * other_configs: the TANGO B = 8, T = 2048 block and the WANGO B = 2,
     T = 65,536, window 512 stack of 8 applications, as tokens per second of
     the whole forward, with the long stack's scan per application (cold:
@@ -372,6 +375,36 @@ def configs_bench(steps: int, warmup: int, dev, stream, timed_batches) -> dict:
         print(msg, file=sys.stderr, flush=True)
         del ws, x, ping, pong
         torch.cuda.empty_cache()
+    return out
+
+
+def gemm_reference(steps: int, dev, stream, timed_batches, ours: dict) -> dict:
+    """Context for the two GEMM kernels, outside the timed step: the vendor
+    library's dense bf16 GEMM (torch.matmul, i.e. hipBLASLt) on plain products
+    of the same shapes -- the projection with its two-part activation operand
+    stacked along K (8192 x 1024 times 1024 x 4352), the output product
+    likewise (8192 x 4096 times 4096 x 512) -- with the weights stored [N, K]
+    as the library takes them, next to this build's kernels on the same shapes
+    (which also do their epilogues: SiLU and the packed gate layout, RoPE and
+    unit length; the gated product and the residual).  None of this is on the
+    measured path."""
+    import torch
+
+    out = {}
+    for name, (M, K, N) in (("projection", (8192, 1024, 4352)), ("output", (8192, 4096, 512))):
+        A = torch.randn(M, K, device=dev, dtype=torch.bfloat16)
+        Wt = torch.randn(N, K, device=dev, dtype=torch.bfloat16)
+        C = torch.empty(M, N, device=dev, dtype=torch.bfloat16)
+        ms, _, _ = timed_batches(lambda: torch.matmul(A, Wt.t(), out=C), steps, 3)
+        flops = 2.0 * M * N * K
+        out[name] = {"shape_mkn": [M, K, N], "library_ms": ms,
+                     "library_frac_of_bf16_peak": flops / (ms * 1e-3) / PEAK_BF16_FLOPS,
+                     "this_build_ms": ours[name],
+                     "this_build_frac_of_bf16_peak": flops / (ours[name] * 1e-3) / PEAK_BF16_FLOPS}
+        print(f"[bench] {name} GEMM shape {M}x{K}x{N}: library {ms * 1e3:.1f} us "
+              f"({100 * out[name]['library_frac_of_bf16_peak']:.1f}% of peak), this build {ours[name] * 1e3:.1f} us",
+              file=sys.stderr, flush=True)
+        del A, Wt, C
     return out
 
 
@@ -856,6 +889,16 @@ def main():
         for _ in range(3):
             dst.copy_(src)
         torch.cuda.synchronize()
+    # this build's projection (row prep + projection GEMM with its epilogue) and
+    # output GEMM on the T = 8192 TANGO shapes, for the library comparison
+    vt = torch.empty(M, F, dtype=torch.float32, device=dev)
+    vt.copy_(v)
+    ms_proj, _, _ = timed_batches(lambda: api.tango_stage_proj(st, bt, xt, gp, v, qh, kh, ws=ws_t, stream=stream),
+                                  loops, 3)
+    ms_out, _, _ = timed_batches(lambda: api.tango_stage_out(st, bt.w_o, xt, gbar, vt, ping, stream=stream),
+                                 loops, 3)
+    result["gemm_reference"] = gemm_reference(loops, dev, stream, timed_batches,
+                                              {"projection": ms_proj, "output": ms_out})
     if not args.no_configs:
         result["other_configs"] = configs_bench(min(loops, 5), 1, dev, stream, timed_batches)
     if not args.no_decode:

@@ -236,8 +236,105 @@ __global__ __launch_bounds__(256) void phi_kernel(const T* __restrict__ src, T* 
   if (perm) perm[m * HD + h * dh + (e / 32) * 32 + feature_slot(e % 32)] = v;
 }
 
+// Everything the WANGO backward derives from the unit queries and keys, in one
+// pass over tiles of 64 positions x 32 columns (a group of 32 columns of one
+// head), 16-byte accesses throughout:
+//   forward order: q and k transposed per head; p = phi(sqrt(tau) q) and
+//   a = phi(sqrt(tau) k) ([TANGO] §2.2 eq. 8) row-major and transposed;
+//   the time-reversed problem of dg (destination row i' reads source row
+//   T-1-i', zero past the end): the reversed q and k row-major, the
+//   destination features phi(sqrt(tau) k_rev) in the permuted feature order of
+//   each group of 32, and the source features phi(sqrt(tau) q_rev) packed
+//   [M/32][4][H*dh][8].
+// The same values as the transpose, reversal, phi and pack kernels would
+// produce one launch at a time.  Grid: B * H * (dh / 32) * (Tp / 64).
+template <typename T>
+__global__ __launch_bounds__(256) void qk_prep_kernel(BwdArgs a, T* __restrict__ fq_perm, T* __restrict__ fk_pk) {
+  __shared__ T tile[4][64][32 + 8];
+  const int dh = a.dh, HD = a.H * dh, Tp = a.Tp;
+  int64_t id = blockIdx.x;
+  const int it = (int)(id % (Tp / 64));
+  id /= Tp / 64;
+  const int ct = (int)(id % (dh / 32));
+  id /= dh / 32;
+  const int h = (int)(id % a.H);
+  const int64_t b = id / a.H;
+  const int tid = threadIdx.x, r = tid >> 2, p8 = tid & 3;
+  const float st = sqrtf(__expf(fminf(a.theta[h], kLogTauMax))), isd = 1.0f / sqrtf((float)dh);
+  const int64_t col = (int64_t)h * dh + ct * 32 + p8 * 8;
+  const T* qh = static_cast<const T*>(a.qh);
+  const T* kh = static_cast<const T*>(a.kh);
+  auto phi8 = [&](const u32x4& x) {
+    const T* e8 = reinterpret_cast<const T*>(&x);
+    u32x4 y;
+    T* o8 = reinterpret_cast<T*>(&y);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) o8[e] = (T)phi_feature(st * (float)e8[e], isd);
+    return y;
+  };
+  // forward order: row-major features, then the four transposed tiles
+  {
+    const int64_t m = b * Tp + (int64_t)it * 64 + r;
+    const u32x4 q8 = *reinterpret_cast<const u32x4*>(qh + m * HD + col);
+    const u32x4 k8 = *reinterpret_cast<const u32x4*>(kh + m * HD + col);
+    const u32x4 pv = phi8(q8), av = phi8(k8);
+    *reinterpret_cast<u32x4*>(static_cast<T*>(a.p_rm) + m * HD + col) = pv;
+    *reinterpret_cast<u32x4*>(static_cast<T*>(a.a_rm) + m * HD + col) = av;
+    *reinterpret_cast<u32x4*>(&tile[0][r][p8 * 8]) = q8;
+    *reinterpret_cast<u32x4*>(&tile[1][r][p8 * 8]) = k8;
+    *reinterpret_cast<u32x4*>(&tile[2][r][p8 * 8]) = pv;
+    *reinterpret_cast<u32x4*>(&tile[3][r][p8 * 8]) = av;
+  }
+  __syncthreads();
+  {   // 32 columns x 8 pieces of 8 positions, per array
+    const int c = tid >> 3, p = tid & 7;
+    const int64_t dst = ((b * a.H + h) * (int64_t)dh + ct * 32 + c) * Tp + (int64_t)it * 64 + p * 8;
+    T* outs[4] = {static_cast<T*>(a.qT), static_cast<T*>(a.kT), static_cast<T*>(a.pT), static_cast<T*>(a.aT)};
+#pragma unroll
+    for (int x = 0; x < 4; ++x) {
+      T out[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) out[e] = tile[x][p * 8 + e][c];
+      *reinterpret_cast<u32x4*>(outs[x] + dst) = *reinterpret_cast<const u32x4*>(out);
+    }
+  }
+  __syncthreads();   // the tiles are reused below
+  // reversed problem: destination rows it*64 .. it*64+63
+  {
+    const int i2 = it * 64 + r;
+    const bool live = i2 < a.T;
+    const int64_t m2 = b * Tp + i2, src = b * Tp + (live ? a.T - 1 - i2 : 0);
+    const u32x4 z = {0u, 0u, 0u, 0u};
+    const u32x4 q8 = live ? *reinterpret_cast<const u32x4*>(qh + src * HD + col) : z;
+    const u32x4 k8 = live ? *reinterpret_cast<const u32x4*>(kh + src * HD + col) : z;
+    *reinterpret_cast<u32x4*>(static_cast<T*>(a.q_rev) + m2 * HD + col) = q8;
+    *reinterpret_cast<u32x4*>(static_cast<T*>(a.k_rev) + m2 * HD + col) = k8;
+    const u32x4 fq = phi8(k8), fk = phi8(q8);
+    const T* f8 = reinterpret_cast<const T*>(&fq);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) tile[0][r][feature_slot(p8 * 8 + e)] = f8[e];
+    *reinterpret_cast<u32x4*>(&tile[1][r][p8 * 8]) = fk;
+  }
+  __syncthreads();
+  {
+    const int64_t m2 = b * Tp + (int64_t)it * 64 + r;
+    *reinterpret_cast<u32x4*>(fq_perm + m2 * HD + col) = *reinterpret_cast<const u32x4*>(&tile[0][r][p8 * 8]);
+    // packed source features: two 32-row blocks, 4 slot groups x 32 columns each
+    const int bb = tid >> 7, grp = (tid >> 5) & 3, cl = tid & 31;
+    T out[8];
+#pragma unroll
+    for (int s8 = 0; s8 < 8; ++s8) out[s8] = tile[1][bb * 32 + perm_slot(grp, s8)][cl];
+    const int64_t blk = (b * Tp + (int64_t)it * 64) / 32 + bb;
+    *reinterpret_cast<u32x4*>(fk_pk + ((blk * 4 + grp) * (int64_t)HD + h * dh + ct * 32 + cl) * 8) =
+        *reinterpret_cast<const u32x4*>(out);
+  }
+}
+
 // Shifted prefix (S) or suffix (R) over the tiles of the per-tile sums, stored
 // in bf16: S[t] = sum_{t' <= t - nb} tsum[t'], R[t] = sum_{t' >= t + nb} tsum[t'].
+// One thread per element; the tiles go in batches of kScanBatch whose loads are
+// all issued before the first add (the loads do not depend on the sum).
+constexpr int kScanBatch = 16;
 __global__ __launch_bounds__(256) void state_scan_kernel(WStateArgs w, int reverse) {
   const int64_t E = (int64_t)w.dh * w.FhC;
   const int64_t id = (int64_t)blockIdx.x * 256 + threadIdx.x;
@@ -246,15 +343,20 @@ __global__ __launch_bounds__(256) void state_scan_kernel(WStateArgs w, int rever
   const float* ts = w.tsum + bh * w.nt * E + el;
   __bf16* st = static_cast<__bf16*>(w.state) + bh * w.nt * E + el;
   float acc = 0.f;
-  if (!reverse) {
-    for (int t = 0; t < w.nt; ++t) {
-      if (t - w.nb >= 0) acc += ts[(int64_t)(t - w.nb) * E];
-      st[(int64_t)t * E] = (__bf16)acc;
+  for (int n0 = 0; n0 < w.nt; n0 += kScanBatch) {
+    // step n visits tile t = n (prefix) or nt - 1 - n (suffix), adding the
+    // tile nb before (after) it
+    float v[kScanBatch];
+#pragma unroll
+    for (int u = 0; u < kScanBatch; ++u) {
+      const int n = n0 + u, t = reverse ? w.nt - 1 - n : n, src = reverse ? t + w.nb : t - w.nb;
+      v[u] = (n < w.nt && src >= 0 && src < w.nt) ? ts[(int64_t)src * E] : 0.f;
     }
-  } else {
-    for (int t = w.nt - 1; t >= 0; --t) {
-      if (t + w.nb <= w.nt - 1) acc += ts[(int64_t)(t + w.nb) * E];
-      st[(int64_t)t * E] = (__bf16)acc;
+#pragma unroll
+    for (int u = 0; u < kScanBatch; ++u) {
+      const int n = n0 + u, t = reverse ? w.nt - 1 - n : n;
+      acc += v[u];
+      if (n < w.nt) st[(int64_t)t * E] = (__bf16)acc;
     }
   }
 }
@@ -400,7 +502,7 @@ BwdPlan wango_bwd_plan(int B, int Tp, int Fhp, int H, int window) {
   return p;
 }
 
-hipError_t launch_tango_bwd_prep(const BwdArgs& a, const BwdPlan& p, hipStream_t s) {
+hipError_t launch_tango_bwd_prep(const BwdArgs& a, const BwdPlan& p, hipStream_t s, bool qk) {
   const int64_t M = (int64_t)a.B * a.Tp;
   const int HD = a.H * a.dh;
   typedef __bf16 T;
@@ -415,30 +517,30 @@ hipError_t launch_tango_bwd_prep(const BwdArgs& a, const BwdPlan& p, hipStream_t
                      static_cast<const T*>(a.gp), a.Fp, static_cast<T*>(a.g_rm), a.H, a.Fhp, p.FhC, a.Fh,
                      a.window > 0 ? a.Fhp : -1, a.Tp, a.T);
   if ((e = hipGetLastError()) != hipSuccess) return e;
-  // queries and keys transposed per head (the B operands of dk and dq)
   const int64_t nblk = M / 32;
-  const int64_t nqk = M * HD;
-  t_step = "transpose_kernel";
-  const dim3 tgrid((unsigned)((int64_t)a.B * a.H * (a.dh / 32) * (a.Tp / 64)));
-  hipLaunchKernelGGL(transpose_kernel<T>, tgrid, dim3(256), 0, s, static_cast<const T*>(a.qh),
-                     static_cast<T*>(a.qT), a.H, a.dh, a.Tp);
-  if ((e = hipGetLastError()) != hipSuccess) return e;
-  t_step = "transpose_kernel";
-  hipLaunchKernelGGL(transpose_kernel<T>, tgrid, dim3(256), 0, s, static_cast<const T*>(a.kh),
-                     static_cast<T*>(a.kT), a.H, a.dh, a.Tp);
-  if ((e = hipGetLastError()) != hipSuccess) return e;
-  // the reversed problem of dg: reversed queries / keys, reversed u packed
-  // with the forward's head padding
-  const int64_t nr = M * HD;
-  t_step = "reverse_rows_kernel";
-  hipLaunchKernelGGL(reverse_rows_kernel<T>, dim3((unsigned)ceil_div(nr, 256)), dim3(256), 0, s,
-                     static_cast<const T*>(a.qh), static_cast<T*>(a.q_rev), HD, a.Tp, a.T, M);
-  if ((e = hipGetLastError()) != hipSuccess) return e;
-  t_step = "reverse_rows_kernel";
-  hipLaunchKernelGGL(reverse_rows_kernel<T>, dim3((unsigned)ceil_div(nr, 256)), dim3(256), 0, s,
-                     static_cast<const T*>(a.kh), static_cast<T*>(a.k_rev), HD, a.Tp, a.T, M);
-  if ((e = hipGetLastError()) != hipSuccess) return e;
-  const int64_t nu = nblk * 4 * a.Fp;
+  if (qk) {
+    // queries and keys transposed per head (the B operands of dk and dq)
+    t_step = "transpose_kernel";
+    const dim3 tgrid((unsigned)((int64_t)a.B * a.H * (a.dh / 32) * (a.Tp / 64)));
+    hipLaunchKernelGGL(transpose_kernel<T>, tgrid, dim3(256), 0, s, static_cast<const T*>(a.qh),
+                       static_cast<T*>(a.qT), a.H, a.dh, a.Tp);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    t_step = "transpose_kernel";
+    hipLaunchKernelGGL(transpose_kernel<T>, tgrid, dim3(256), 0, s, static_cast<const T*>(a.kh),
+                       static_cast<T*>(a.kT), a.H, a.dh, a.Tp);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    // the reversed problem of dg: reversed queries / keys, reversed u packed
+    // with the forward's head padding
+    const int64_t nr = M * HD;
+    t_step = "reverse_rows_kernel";
+    hipLaunchKernelGGL(reverse_rows_kernel<T>, dim3((unsigned)ceil_div(nr, 256)), dim3(256), 0, s,
+                       static_cast<const T*>(a.qh), static_cast<T*>(a.q_rev), HD, a.Tp, a.T, M);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    t_step = "reverse_rows_kernel";
+    hipLaunchKernelGGL(reverse_rows_kernel<T>, dim3((unsigned)ceil_div(nr, 256)), dim3(256), 0, s,
+                       static_cast<const T*>(a.kh), static_cast<T*>(a.k_rev), HD, a.Tp, a.T, M);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+  }
   t_step = "pack_kernel";
   hipLaunchKernelGGL(pack_kernel<T>, dim3((unsigned)(nblk * (a.Fp / 32))), dim3(128), 0, s,
                      static_cast<const T*>(a.u_rm), (int64_t)a.H * p.FhC, static_cast<T*>(a.u_rev_pk), a.Fp, a.Fhp,
@@ -485,32 +587,16 @@ hipError_t launch_wango_bwd_features(const BwdArgs& a, void* fq_perm, void* tmp_
   return hipGetLastError();
 }
 
-hipError_t launch_wango_bwd_prep(const BwdArgs& a, const BwdPlan& p, hipStream_t s) {
-  // the TANGO prep (augmented u and g rows, q/k transposes, the reversed problem), then
-  // the features p, a row-major and transposed, and the augmented rows transposed
-  hipError_t e = launch_tango_bwd_prep(a, p, s);
+hipError_t launch_wango_bwd_prep(const BwdArgs& a, const BwdPlan& p, void* fq_perm, void* fk_pk, hipStream_t s) {
+  // the TANGO prep's augmented u and g rows and reversed packed u, then every
+  // q/k-derived array (including the reversed scan's features) in one launch
+  hipError_t e = launch_tango_bwd_prep(a, p, s, false);
   if (e != hipSuccess) return e;
   typedef __bf16 T;
-  const int64_t M = (int64_t)a.B * a.Tp;
-  const int HD = a.H * a.dh;
-  const int64_t n = M * HD;
-  const dim3 grid((unsigned)ceil_div(n, 256)), block(256);
-  t_step = "phi_kernel";
-  hipLaunchKernelGGL(phi_kernel<T>, grid, block, 0, s, static_cast<const T*>(a.qh), static_cast<T*>(a.p_rm),
-                     static_cast<T*>(nullptr), a.theta, a.H, a.dh, n);
-  if ((e = hipGetLastError()) != hipSuccess) return e;
-  t_step = "phi_kernel";
-  hipLaunchKernelGGL(phi_kernel<T>, grid, block, 0, s, static_cast<const T*>(a.kh), static_cast<T*>(a.a_rm),
-                     static_cast<T*>(nullptr), a.theta, a.H, a.dh, n);
-  if ((e = hipGetLastError()) != hipSuccess) return e;
-  t_step = "transpose_kernel";
-  const dim3 tgrid((unsigned)((int64_t)a.B * a.H * (a.dh / 32) * (a.Tp / 64)));
-  hipLaunchKernelGGL(transpose_kernel<T>, tgrid, block, 0, s, static_cast<const T*>(a.p_rm), static_cast<T*>(a.pT),
-                     a.H, a.dh, a.Tp);
-  if ((e = hipGetLastError()) != hipSuccess) return e;
-  t_step = "transpose_kernel";
-  hipLaunchKernelGGL(transpose_kernel<T>, tgrid, block, 0, s, static_cast<const T*>(a.a_rm), static_cast<T*>(a.aT),
-                     a.H, a.dh, a.Tp);
+  if (a.dh % 32 != 0 || a.Tp % 64 != 0) return hipErrorInvalidValue;
+  t_step = "qk_prep_kernel";
+  hipLaunchKernelGGL(qk_prep_kernel<T>, dim3((unsigned)((int64_t)a.B * a.H * (a.dh / 32) * (a.Tp / 64))), dim3(256),
+                     0, s, a, static_cast<T*>(fq_perm), static_cast<T*>(fk_pk));
   return hipGetLastError();
 }
 

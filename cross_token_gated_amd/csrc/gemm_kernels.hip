@@ -69,7 +69,10 @@ template <typename T> struct ProjCfg;
 template <> struct ProjCfg<bf16> : TileCfg<128, 128, 32, 2, 2, 2, 2> {};
 template <> struct ProjCfg<float> : TileCfg<64, 128, 32, 2, 2, 1, 1> {};
 template <typename T> struct OutCfg;
-template <> struct OutCfg<bf16> : TileCfg<64, 128, 32, 2, 2, 4, 2> {};
+// KO's K is the gate width (a multiple of 64): k-tiles of 64 halve its barriers
+// (53 against 57 us at T = 8192, F = 2048, d = 512 with k-tiles of 32 and four
+// tiles of prefetch)
+template <> struct OutCfg<bf16> : TileCfg<64, 128, 64, 2, 2, 2, 2> {};
 template <> struct OutCfg<float> : TileCfg<64, 128, 32, 2, 2, 1, 1> {};
 
 template <typename T> constexpr int piece_elems() { return 16 / (int)sizeof(T); }

@@ -189,7 +189,7 @@ struct BwdPlan {
 };
 BwdPlan tango_bwd_plan(int B, int Tp, int Fhp, int H);
 BwdPlan wango_bwd_plan(int B, int Tp, int Fhp, int H, int window);
-hipError_t launch_tango_bwd_prep(const BwdArgs& a, const BwdPlan& p, hipStream_t s);
+hipError_t launch_tango_bwd_prep(const BwdArgs& a, const BwdPlan& p, hipStream_t s, bool qk = true);
 // ds tiles and their products (gemm_kernels.hip)
 hipError_t launch_tango_ds(const BwdArgs& a, const BwdPlan& p, hipStream_t s);
 hipError_t launch_tango_dsmm(const BwdArgs& a, const BwdPlan& p, hipStream_t s);
@@ -213,7 +213,9 @@ hipError_t launch_wango_bwd_features(const BwdArgs& a, void* fq_perm, void* tmp_
                                      const void* k_src, void* fk_pk, hipStream_t s);
 // theta_blk: [ceil(B*Tp*H*dh / 256)][H] float32 scratch
 hipError_t launch_wango_bwd_finish(const BwdArgs& a, const BwdPlan& p, float* theta_blk, hipStream_t s);
-hipError_t launch_wango_bwd_prep(const BwdArgs& a, const BwdPlan& p, hipStream_t s);
+// fq_perm, fk_pk: the reversed scan's destination (permuted) and source (packed)
+// features, written here so that the scan does not redo them
+hipError_t launch_wango_bwd_prep(const BwdArgs& a, const BwdPlan& p, void* fq_perm, void* fk_pk, hipStream_t s);
 // Name of the kernel the backward prep launched last on this thread.
 const char* bwd_last_step();
 // row-major [B*Tp][H*C] -> [B][H][C][Tp]

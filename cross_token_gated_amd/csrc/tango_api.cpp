@@ -860,10 +860,12 @@ WFwdLayout make_wfwd_layout(const tango_shape_t* s, int32_t chunk) {
 // The WANGO scan + band of one problem into gbar (options set by the caller).
 hipError_t wango_scan_band(const tango_shape_t* s, int32_t window, int32_t chunk, const WFwdLayout& L,
                            char* base, const BwdArgs& fa, const void* q, const void* k, const void* gp,
-                           AggArgs aa, hipStream_t st) {
-  // destination features of q (permuted order), source features of k (packed)
-  hipError_t e = launch_wango_bwd_features(fa, base + L.fq, base + L.tmp, q, k, base + L.fk, st);
-  if (e != hipSuccess) return e;
+                           AggArgs aa, hipStream_t st, bool features_ready = false) {
+  // destination features of q (permuted order), source features of k (packed),
+  // unless the caller has written them already
+  hipError_t e = hipSuccess;
+  if (!features_ready && (e = launch_wango_bwd_features(fa, base + L.fq, base + L.tmp, q, k, base + L.fk, st)) != hipSuccess)
+    return e;
   float* n_old = reinterpret_cast<float*>(base + L.n_old);
   float* z_old = reinterpret_cast<float*>(base + L.z_old);
   ScanArgs sa = scan_args(s, window, chunk, base + L.fq, base + L.fk, gp, n_old, z_old,
@@ -1050,14 +1052,14 @@ int wango_aggregate_bwd(const tango_shape_t* shape, int32_t window, int32_t chun
     a.window = window;
     a.nb = L.plan.nb;
     a.FhC = L.plan.FhC;
-    hipError_t e = launch_wango_bwd_prep(a, L.plan, st);
+    hipError_t e = launch_wango_bwd_prep(a, L.plan, base + L.f.fq, base + L.f.fk, st);
     if (e != hipSuccess) return hip_fail(e, bwd_last_step());
     // dg: the whole WANGO aggregation (scan + band) of the time-reversed
-    // problem, numerator only
+    // problem, numerator only (its features come from the prep)
     AggArgs aa = agg_args(s, theta, nullptr, a.k_rev, a.q_rev, a.u_rev_pk, dg, true);
     aa.num_only = 1;
     aa.rev_out = 1;
-    if ((e = wango_scan_band(s, window, chunk, L.f, base, a, a.k_rev, a.q_rev, a.u_rev_pk, aa, st)) != hipSuccess)
+    if ((e = wango_scan_band(s, window, chunk, L.f, base, a, a.k_rev, a.q_rev, a.u_rev_pk, aa, st, true)) != hipSuccess)
       return hip_fail(e, "reversed scan / band (dg)");
     // window and near older pairs
     if ((e = launch_tango_ds(a, L.plan, st)) != hipSuccess) return hip_fail(e, "ds tile kernel");

@@ -334,7 +334,7 @@ __global__ __launch_bounds__(256) void qk_prep_kernel(BwdArgs a, T* __restrict__
 // in bf16: S[t] = sum_{t' <= t - nb} tsum[t'], R[t] = sum_{t' >= t + nb} tsum[t'].
 // One thread per element; the tiles go in batches of kScanBatch whose loads are
 // all issued before the first add (the loads do not depend on the sum).
-constexpr int kScanBatch = 16;
+constexpr int kScanBatch = 32;
 __global__ __launch_bounds__(256) void state_scan_kernel(WStateArgs w, int reverse) {
   const int64_t E = (int64_t)w.dh * w.FhC;
   const int64_t id = (int64_t)blockIdx.x * 256 + threadIdx.x;

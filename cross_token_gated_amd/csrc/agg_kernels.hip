@@ -71,16 +71,19 @@ struct Job {
 // block of 16 rows x 32 k is stored as 256-byte regions, one per (chunk h,
 // k group g) with g covering k = 8g .. 8g + 7 in the order of the fragment's
 // slots (PPF chunks of 16 bytes per fragment: 1 for bf16, 2 for float32);
-// row r of the block sits at position r xor g of its region.  An MFMA
-// fragment read (lanes 16g .. 16g + 15: rows 0 .. 15 of group g) then covers
-// one region, which gfx950 serves at its full 256 bytes per clock, and so
-// does the key loader (four consecutive lanes fetch the 64 contiguous bytes
-// of one row, keeping its global loads coalesced) at the LDS write rate.
-// Measured on gfx950: a rotation by 4g instead halves the read rate, and the
-// plain order r makes the loader's writes 4-way conflicted.
+// row r of the block sits at slot r xor 2g of its region.  gfx950 serves a
+// 16-byte LDS read 16 lanes (256 bytes) per clock and a 16-byte write 8 lanes
+// (128 bytes) per clock, conflict-free when the lanes of the group hit
+// distinct 16-byte slots modulo 256 or 128 bytes: an MFMA fragment read
+// (lanes 16g .. 16g + 15: rows 0 .. 15 of group g) takes a permutation of one
+// region, and the key loader's 8-lane groups (two rows x four groups; four
+// consecutive lanes fetch the 64 contiguous bytes of one row, keeping its
+// global loads coalesced) land on 8 distinct slots modulo 8.  Measured on
+// gfx950 with SQ_LDS_BANK_CONFLICT: 8 LDS cycles per loader write
+// instruction, against 16 with slot r xor g and 32 with slot r.
 template <typename T> constexpr int frag_chunks() { return (int)sizeof(T) / 2; }
 __device__ __forceinline__ int region_pos(int region, int r, int g) {
-  return region * 256 + (r ^ g) * 16;
+  return region * 256 + (r ^ (2 * g)) * 16;
 }
 
 template <typename T, int DH, int BR> struct AggLds {

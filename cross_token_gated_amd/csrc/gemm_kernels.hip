@@ -53,10 +53,12 @@ constexpr int kEpiRows = 64;     // output rows staged in LDS per epilogue pass
 constexpr int kCStride = 128 + 4;
 
 // BM x BN output tile, BK-wide k-tiles, WM x WN waves, register prefetch D
-// k-tiles ahead, AS parts (1, or hi and lo) of the A operand.
-template <int BM_, int BN_, int BK_, int WM_, int WN_, int D_, int AS_>
+// k-tiles ahead, AS parts (1, or hi and lo) of the A operand; SW selects the
+// LDS slot order (1: conflict-free loader writes, 0: the older order, see
+// lds_slot).
+template <int BM_, int BN_, int BK_, int WM_, int WN_, int D_, int AS_, int SW_ = 1>
 struct TileCfg {
-  static constexpr int BM = BM_, BN = BN_, BK = BK_, WM = WM_, WN = WN_, D = D_, AS = AS_;
+  static constexpr int BM = BM_, BN = BN_, BK = BK_, WM = WM_, WN = WN_, D = D_, AS = AS_, SW = SW_;
   static constexpr int WTM = BM / WM, WTN = BN / WN;   // wave tile
   static constexpr int IB = WTM / 16, JB = WTN / 16;   // 16 x 16 blocks per wave
   static_assert(WM * WN * 64 == kThreads, "four waves");
@@ -66,7 +68,9 @@ struct TileCfg {
 };
 
 template <typename T> struct ProjCfg;
-template <> struct ProjCfg<bf16> : TileCfg<128, 128, 32, 2, 2, 2, 2> {};
+// (the older slot order: with the conflict-free one the kernel needs two more
+// VGPRs and drops from three waves per SIMD to two, 110 against 101 us)
+template <> struct ProjCfg<bf16> : TileCfg<128, 128, 32, 2, 2, 2, 2, 0> {};
 template <> struct ProjCfg<float> : TileCfg<64, 128, 32, 2, 2, 1, 1> {};
 template <typename T> struct OutCfg;
 // KO's K is the gate width (a multiple of 64): k-tiles of 64 halve its barriers
@@ -80,14 +84,22 @@ template <typename T> constexpr int piece_elems() { return 16 / (int)sizeof(T); 
 // LDS operand layout.  A tile of R rows x BK columns is stored as blocks of
 // 16 rows x 32 columns; the 16-byte pieces of a block (row r, k group g =
 // columns 8g .. 8g + 7, in PPF chunks h of PE elements: PPF = 1 for bf16, 2
-// for float32) live in 256-byte regions, one per (chunk, group), at position
-// r xor g.  An MFMA fragment read (16 lanes per group: rows 0..15 of one
-// group) then covers one whole region, which gfx950 serves at its full 256
-// bytes per clock, and the loaders (four consecutive lanes fetch 64
-// contiguous bytes of one row, which keeps the global loads coalesced) write
-// at the LDS write rate.  Measured on gfx950: a rotation (r + 4g) mod 16
-// halves the read rate, and the plain order r makes the loader's writes
-// 4-way conflicted.
+// for float32) live in 256-byte regions, one per (chunk, group), at slot
+// r xor 2g xor x, x the parity of (k block + chunk).  gfx950 serves a 16-byte
+// LDS read 16 lanes (256 bytes) per clock and a 16-byte write 8 lanes (128
+// bytes) per clock, each conflict-free when the lanes of the group hit
+// distinct 16-byte slots modulo 256 or 128 bytes.  An MFMA fragment read (16
+// lanes: rows 0..15 of one group) takes a permutation of one region; a loader
+// write (consecutive lanes fetch 64 or 128 contiguous bytes of a row, which
+// keeps the global loads coalesced) puts its 8 lanes -- two rows x four
+// groups, or one row x (two k blocks or chunks) x four groups -- on 8
+// distinct slots modulo 8.  Measured on gfx950 with SQ_LDS_BANK_CONFLICT: 8
+// LDS cycles per loader write instruction, against 16 with slot r xor g and
+// 32 with slot r.  SW = 0 keeps the older slot r xor g (2-way conflicted
+// writes).
+template <int SW> __device__ __forceinline__ int lds_slot(int r, int g, int x) {
+  return SW ? r ^ (2 * g) ^ (x & 1) : r ^ g;
+}
 template <typename T> constexpr int frag_chunks() { return (int)sizeof(T) / 2; }   // PPF
 template <class CF, typename T> constexpr int tile_chunks(int rows) {
   return rows / 16 * (CF::BK / 32) * frag_chunks<T>();
@@ -99,7 +111,7 @@ __device__ __forceinline__ int piece_offset(int row, int kp) {
   const int kb = kp * PE / 32, within = kp % (32 / PE);
   const int g = within / PPF, h = within % PPF, r = row & 15;
   const int region = (((row >> 4) * NKB + kb) * PPF + h) * 4 + g;
-  return region * 256 + (r ^ g) * 16;
+  return region * 256 + lds_slot<CF::SW>(r, g, kb + h) * 16;
 }
 template <class CF, typename T> constexpr size_t ops_bytes() {
   return 2 * (size_t)tile_chunks<CF, T>(CF::AS * CF::BM + CF::BN) * 1024;
@@ -165,13 +177,12 @@ template <class CF, typename T>
 __device__ __forceinline__ Frag<T> lds_frag(const T* tile, int rb, int kb, int lane) {
   constexpr int PPF = frag_chunks<T>(), NKB = CF::BK / 32;
   const int r = lane & 15, g = lane >> 4;
-  const unsigned char* base = reinterpret_cast<const unsigned char*>(tile) +
-                              ((rb * NKB + kb) * PPF * 4 + g) * 256 + (r ^ g) * 16;
+  const unsigned char* base = reinterpret_cast<const unsigned char*>(tile) + ((rb * NKB + kb) * PPF * 4 + g) * 256;
   if constexpr (PPF == 1) {
-    return load_frag<T>(reinterpret_cast<const T*>(base));
+    return load_frag<T>(reinterpret_cast<const T*>(base + lds_slot<CF::SW>(r, g, kb) * 16));
   } else {
-    return join(load_quad<T>(reinterpret_cast<const T*>(base)),
-                load_quad<T>(reinterpret_cast<const T*>(base + 4 * 256)));
+    return join(load_quad<T>(reinterpret_cast<const T*>(base + lds_slot<CF::SW>(r, g, kb) * 16)),
+                load_quad<T>(reinterpret_cast<const T*>(base + 4 * 256 + lds_slot<CF::SW>(r, g, kb + 1) * 16)));
   }
 }
 

@@ -112,6 +112,11 @@ AGG_CASES = [
     dict(dtype="bf16", B=2, T=300, d_model=128, d_gate=512, n_heads=2, head_dim=64),
     dict(dtype="bf16", B=1, T=257, d_model=128, d_gate=256, n_heads=4, head_dim=32),
     dict(dtype="bf16", B=64, T=200, d_model=128, d_gate=256, n_heads=4, head_dim=32),  # pair mode
+    # wider shapes: two heads of 64 at B = 8; an odd tile count (a middle tile of its own)
+    # at B = 16; four heads of 32 at a gate width of 4096
+    dict(dtype="bf16", B=8, T=1000, d_model=128, d_gate=2048, n_heads=2, head_dim=64),
+    dict(dtype="bf16", B=16, T=1100, d_model=128, d_gate=1024, n_heads=1, head_dim=128),
+    dict(dtype="bf16", B=6, T=700, d_model=128, d_gate=4096, n_heads=4, head_dim=32),
     dict(dtype="f32", B=1, T=333, d_model=128, d_gate=256, n_heads=1, head_dim=128),
     dict(dtype="f32", B=2, T=64, d_model=128, d_gate=128, n_heads=2, head_dim=64),
 ]

@@ -191,11 +191,17 @@ __global__ __launch_bounds__(kDecThreads) void dproj_kernel(DecArgs a) {
 // TANGO dagg: chunk c of sequence b, sources j in [c kChunk, min(c kChunk +
 // kChunk, p + 1)).  Partial numerators [F] and denominators [H] in float32,
 // row stride F + 64 floats.
+// All workgroups of a step are resident at once, so the kernel takes about
+// as long as one workgroup's chain of memory round trips: each key row is
+// read by two lanes (half of d_h each) with all of their loads issued
+// together, and each thread keeps 16 gate rows in flight.
 // ---------------------------------------------------------------------------
-template <typename T>
+template <typename T, int DH>
 __global__ __launch_bounds__(kAggThreadsD) void dagg_kernel(DecArgs a) {
+  constexpr int HALF = DH / 2, NF = HALF / 8, GB = 16;
   __shared__ float qs[1024];
   __shared__ float pw[kDecChunk * 32];
+  __shared__ float qinv[32];
   const int tid = threadIdx.x;
   const int64_t b = blockIdx.y;
   const int c = blockIdx.x;
@@ -204,62 +210,83 @@ __global__ __launch_bounds__(kAggThreadsD) void dagg_kernel(DecArgs a) {
   const int j0 = c * kDecChunk;
   if (j0 > p) return;
   const int nj = min(kDecChunk, p + 1 - j0);
-  const int F = a.F, HD = a.HD, H = a.H, dh = a.dh, Fh = F / H;
+  const int F = a.F, HD = a.HD, H = a.H, Fh = F / H;
   const T* kc = static_cast<const T*>(a.kc);
   const T* gc = static_cast<const T*>(a.gc);
-  __shared__ float qinv[32];
   for (int i = tid; i < HD; i += kAggThreadsD) qs[i] = tof<T>(static_cast<const T*>(a.q)[b * HD + i]);
   __syncthreads();
   if (tid < H) {
     float ss = 0.f;
-    for (int e = 0; e < dh; ++e) ss += qs[tid * dh + e] * qs[tid * dh + e];
+    for (int e = 0; e < DH; ++e) ss += qs[tid * DH + e] * qs[tid * DH + e];
     qinv[tid] = 1.0f / fmaxf(sqrtf(ss), 1e-12f);   // unit query ([TANGO] §2.1)
   }
   __syncthreads();
-  // exp weights, one (source, head) item per thread and pass; s = q.k / |q| |k|
-  for (int it = tid; it < kDecChunk * H; it += kAggThreadsD) {
+  // exp weights, one (source, head) item per pair of lanes and pass; s = q.k / |q| |k|
+  // (zero weight for sources past the chunk's end)
+  const int n_items = kDecChunk * H, part = tid & 1;
+  for (int it0 = 0; it0 < n_items; it0 += kAggThreadsD / 2) {
+    const int it = it0 + (tid >> 1);
     const int jl = it / H, h = it - (it / H) * H;
-    float w = 0.f;
-    if (jl < nj) {
-      const T* kr = kc + (b * a.P + j0 + jl) * HD + h * dh;
-      float s = 0.f, kk = 0.f;
-      for (int e = 0; e < dh; e += 8) {
-        const Frag<T> kf = load_frag<T>(kr + e);
+    const bool live = it < n_items && jl < nj;
+    float s = 0.f, kk = 0.f;
+    if (live) {
+      const T* kr = kc + (b * a.P + j0 + jl) * HD + h * DH + part * HALF;
+      Frag<T> kf[NF];
+#pragma unroll
+      for (int q = 0; q < NF; ++q) kf[q] = load_frag<T>(kr + q * 8);
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int q = 0; q < NF; ++q)
 #pragma unroll
         for (int s8 = 0; s8 < 8; ++s8) {
-          const float kv = tof<T>(kf[s8]);
-          s += qs[h * dh + e + s8] * kv;
+          const float kv = tof<T>(kf[q][s8]);
+          s += qs[h * DH + part * HALF + q * 8 + s8] * kv;
           kk += kv * kv;
         }
-      }
-      s *= qinv[h] / fmaxf(sqrtf(kk), 1e-12f);
-      w = __builtin_amdgcn_exp2f(tau_of(a.theta, h) * kLog2e * (s - 1.0f));
     }
-    pw[jl * H + h] = w;
+    s += __shfl_xor(s, 1, 64);
+    kk += __shfl_xor(kk, 1, 64);
+    if (part == 0 && it < n_items) {
+      float w = 0.f;
+      if (live) {
+        const float sn = s * qinv[h] / fmaxf(sqrtf(kk), 1e-12f);
+        w = __builtin_amdgcn_exp2f(tau_of(a.theta, h) * kLog2e * (sn - 1.0f));
+      }
+      pw[jl * H + h] = w;
+    }
   }
   __syncthreads();
-  float* part = a.part + ((int64_t)b * a.nch + c) * (F + 64);
+  float* part_out = a.part + ((int64_t)b * a.nch + c) * (F + 64);
   for (int f0 = 0; f0 < F; f0 += kAggThreadsD * 8) {
     const int col = f0 + tid * 8;
     if (col < F) {
       const int h = col / Fh;
       float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
       const T* gr = gc + (b * a.P + j0) * F + col;
-#pragma unroll 8
-      for (int jl = 0; jl < nj; ++jl) {
-        const Frag<T> g = load_frag<T>(gr + (int64_t)jl * F);
-        const float w = pw[jl * H + h];
+      // all kDecChunk rows in batches of GB loads; rows past the chunk's end
+      // re-read its last row and carry weight zero
+      for (int jb = 0; jb < kDecChunk; jb += GB) {
+        Frag<T> g[GB];
 #pragma unroll
-        for (int e = 0; e < 8; ++e) acc[e] += w * tof<T>(g[e]);
+        for (int u = 0; u < GB; ++u) g[u] = load_frag<T>(gr + (int64_t)min(jb + u, nj - 1) * F);
+        // keep the batch together: left alone, the compiler issues one load per
+        // wait to save VGPRs for occupancy, which serialises the round trips
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int u = 0; u < GB; ++u) {
+          const float w = pw[(jb + u) * H + h];
+#pragma unroll
+          for (int e = 0; e < 8; ++e) acc[e] += w * tof<T>(g[u][e]);
+        }
       }
-      *reinterpret_cast<f32x4*>(part + col) = f32x4{acc[0], acc[1], acc[2], acc[3]};
-      *reinterpret_cast<f32x4*>(part + col + 4) = f32x4{acc[4], acc[5], acc[6], acc[7]};
+      *reinterpret_cast<f32x4*>(part_out + col) = f32x4{acc[0], acc[1], acc[2], acc[3]};
+      *reinterpret_cast<f32x4*>(part_out + col + 4) = f32x4{acc[4], acc[5], acc[6], acc[7]};
     }
   }
   if (tid < H) {
     float s = 0.f;
     for (int jl = 0; jl < nj; ++jl) s += pw[jl * H + tid];
-    part[F + tid] = s;
+    part_out[F + tid] = s;
   }
 }
 
@@ -578,7 +605,13 @@ hipError_t launch_decode_mt(const DecArgs& a, bool io_bf, hipStream_t s) {
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   if (a.window == 0) {
-    hipLaunchKernelGGL((dagg_kernel<T>), dim3((unsigned)a.nch, (unsigned)a.B), dim3(kAggThreadsD), 0, s, a);
+    const dim3 ga((unsigned)a.nch, (unsigned)a.B);
+    switch (a.dh) {
+      case 32: hipLaunchKernelGGL((dagg_kernel<T, 32>), ga, dim3(kAggThreadsD), 0, s, a); break;
+      case 64: hipLaunchKernelGGL((dagg_kernel<T, 64>), ga, dim3(kAggThreadsD), 0, s, a); break;
+      case 128: hipLaunchKernelGGL((dagg_kernel<T, 128>), ga, dim3(kAggThreadsD), 0, s, a); break;
+      default: return hipErrorInvalidValue;
+    }
     if ((e = hipGetLastError()) != hipSuccess) return e;
     hipLaunchKernelGGL((dcomb_kernel<T, AS>), dim3((unsigned)ceil_div(a.F, kCombCols), (unsigned)a.B), dim3(256),
                        0, s, a);

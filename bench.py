@@ -26,6 +26,9 @@ Alongside, with HIP events on the launch stream:
     cycle through 8 copies of the scan's inputs and outputs, so every launch
     reads data the others have evicted from the 256 MB Infinity Cache (the
     warm-cache time, one copy over and over, is reported beside it);
+  * ceilings: what the vendor's kernels reach here -- a 1 GiB device copy and
+    a square 8192^3 bf16 GEMM (torch.matmul) -- as context for the fractions
+    of the published peaks (off the measured path);
   * gemm_reference: context for the projection and output GEMMs -- the
     vendor library (torch.matmul) on plain bf16 GEMMs of the same shapes next
     to this build's stage calls (off the measured path);
@@ -405,6 +408,36 @@ def gemm_reference(steps: int, dev, stream, timed_batches, ours: dict) -> dict:
               f"({100 * out[name]['library_frac_of_bf16_peak']:.1f}% of peak), this build {ours[name] * 1e3:.1f} us",
               file=sys.stderr, flush=True)
         del A, Wt, C
+    return out
+
+
+def ceilings(dev, stream, timed_batches) -> dict:
+    """What the vendor's own kernels reach on this part, as context for the
+    fractions of the published peaks: a plain device copy of 1 GiB (torch
+    copy_: 1 GiB read, 1 GiB written, cold by size against the 256 MB Infinity
+    Cache) and a square bf16 GEMM (8192^3, torch.matmul -> hipBLASLt).  Off the
+    measured path."""
+    import torch
+
+    n = 1 << 28
+    src = torch.ones(n, dtype=torch.float32, device=dev)
+    dst = torch.empty_like(src)
+    ms_c, _, _ = timed_batches(lambda: dst.copy_(src), 10, 3)
+    del src, dst
+    m = 8192
+    A = torch.randn(m, m, device=dev, dtype=torch.bfloat16)
+    Bm = torch.randn(m, m, device=dev, dtype=torch.bfloat16)
+    C = torch.empty(m, m, device=dev, dtype=torch.bfloat16)
+    ms_g, _, _ = timed_batches(lambda: torch.matmul(A, Bm, out=C), 10, 3)
+    del A, Bm, C
+    copy_gbs = 2 * 4 * n / (ms_c * 1e-3) / 1e9
+    gemm_tf = 2.0 * m ** 3 / (ms_g * 1e-3) / 1e12
+    out = {"copy_1gib": {"ms": ms_c, "GB_per_s": copy_gbs, "frac_of_hbm_peak": copy_gbs * 1e9 / PEAK_HBM_BYTES},
+           "gemm_bf16_8192": {"ms": ms_g, "TFLOP_per_s": gemm_tf,
+                              "frac_of_bf16_peak": gemm_tf * 1e12 / PEAK_BF16_FLOPS}}
+    print(f"[bench] ceilings: device copy {copy_gbs:.0f} GB/s ({100 * out['copy_1gib']['frac_of_hbm_peak']:.1f}% of "
+          f"the HBM peak), bf16 GEMM 8192^3 {gemm_tf:.0f} TFLOP/s "
+          f"({100 * out['gemm_bf16_8192']['frac_of_bf16_peak']:.1f}% of the bf16 peak)", file=sys.stderr, flush=True)
     return out
 
 
@@ -899,6 +932,7 @@ def main():
                                  loops, 3)
     result["gemm_reference"] = gemm_reference(loops, dev, stream, timed_batches,
                                               {"projection": ms_proj, "output": ms_out})
+    result["ceilings"] = ceilings(dev, stream, timed_batches)
     if not args.no_configs:
         result["other_configs"] = configs_bench(min(loops, 5), 1, dev, stream, timed_batches)
     if not args.no_decode:

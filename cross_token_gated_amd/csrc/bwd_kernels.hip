@@ -330,6 +330,71 @@ __global__ __launch_bounds__(256) void qk_prep_kernel(BwdArgs a, T* __restrict__
   }
 }
 
+// KW sums: per tile t of (sequence, head) bh, tsum[e][f] = sum over the
+// tile's rows j of aT[e][j] x[j][f], x the augmented g (S) or u (R) rows as
+// they lie (row-major).  A workgroup stages a 128-row x 64-column tile of x in
+// LDS with 16-byte writes and assembles each MFMA B fragment (8 consecutive
+// rows of one column) from 2-byte reads; the A fragments come straight from
+// the per-head transposed features.  Wave w takes columns 16 w .. 16 w + 15 of
+// the block and every d_h row, over the tile's four k-steps in order (the
+// same MFMA sequence per output block as a GEMM over transposed operands).
+// Grid: B*H * nt * (FhC / 64) workgroups of 256.
+template <int DH>
+__global__ __launch_bounds__(256) void state_sums_kernel(WStateArgs w) {
+  typedef __bf16 T;
+  constexpr int NE = DH / 16, XS = 64 + 8;   // row stride of the staged tile (16-byte aligned)
+  __shared__ __align__(16) T xs[kBwdTile][XS];
+  const int nfb = w.FhC / 64;
+  int64_t id = blockIdx.x;
+  const int fb = (int)(id % nfb);
+  id /= nfb;
+  const int t = (int)(id % w.nt);
+  const int64_t bh = id / w.nt;
+  const int h = (int)(bh % w.H);
+  const int64_t b = bh / w.H;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int li = lane & 15, lg = lane >> 4;
+  const T* x = static_cast<const T*>(w.xrm);
+  const int64_t row0 = b * w.Tp + (int64_t)t * kBwdTile;
+  // every global load of the workgroup is issued before the first wait (left
+  // alone, the compiler spreads them over the k-steps, one round trip each)
+  const T* aT = static_cast<const T*>(w.aT) + bh * DH * (int64_t)w.Tp + (int64_t)t * kBwdTile;
+  Frag<T> af[kBwdTile / 32][NE];
+#pragma unroll
+  for (int ks = 0; ks < kBwdTile / 32; ++ks)
+#pragma unroll
+    for (int eb = 0; eb < NE; ++eb) af[ks][eb] = load_frag<T>(aT + (int64_t)(eb * 16 + li) * w.Tp + ks * 32 + lg * 8);
+  u32x4 xv[kBwdTile * 8 / 256];
+#pragma unroll
+  for (int pp = 0; pp < kBwdTile * 8 / 256; ++pp) {   // 128 rows x 8 pieces of 8 columns
+    const int pc = tid + 256 * pp, r = pc >> 3, q = pc & 7;
+    xv[pp] = *reinterpret_cast<const u32x4*>(x + ((row0 + r) * w.H + h) * w.FhC + fb * 64 + q * 8);
+  }
+  __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+  for (int pp = 0; pp < kBwdTile * 8 / 256; ++pp) {
+    const int pc = tid + 256 * pp, r = pc >> 3, q = pc & 7;
+    *reinterpret_cast<u32x4*>(&xs[r][q * 8]) = xv[pp];
+  }
+  __syncthreads();
+  f32x4 acc[NE];
+#pragma unroll
+  for (int eb = 0; eb < NE; ++eb) acc[eb] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int ks = 0; ks < kBwdTile / 32; ++ks) {
+    Frag<T> bf;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) bf[i] = xs[ks * 32 + lg * 8 + i][wave * 16 + li];
+#pragma unroll
+    for (int eb = 0; eb < NE; ++eb) mma(acc[eb], af[ks][eb], bf);
+  }
+  float* out = w.tsum + ((bh * w.nt + t) * DH) * (int64_t)w.FhC + fb * 64 + wave * 16 + li;
+#pragma unroll
+  for (int eb = 0; eb < NE; ++eb)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) out[(int64_t)(eb * 16 + lg * 4 + r) * w.FhC] = acc[eb][r];
+}
+
 // Shifted prefix (S) or suffix (R) over the tiles of the per-tile sums, stored
 // in bf16: S[t] = sum_{t' <= t - nb} tsum[t'], R[t] = sum_{t' >= t + nb} tsum[t'].
 // One thread per element; the tiles go in batches of kScanBatch whose loads are
@@ -557,6 +622,18 @@ hipError_t launch_tango_bwd_finish(const BwdArgs& a, const BwdPlan& p, hipStream
   return hipGetLastError();
 }
 
+hipError_t launch_wango_state_sums(const WStateArgs& w, hipStream_t s) {
+  if (w.FhC % 64 != 0 || w.Tp % kBwdTile != 0) return hipErrorInvalidValue;
+  const dim3 grid((unsigned)((int64_t)w.B * w.H * w.nt * (w.FhC / 64))), block(256);
+  switch (w.dh) {
+    case 32: hipLaunchKernelGGL(state_sums_kernel<32>, grid, block, 0, s, w); break;
+    case 64: hipLaunchKernelGGL(state_sums_kernel<64>, grid, block, 0, s, w); break;
+    case 128: hipLaunchKernelGGL(state_sums_kernel<128>, grid, block, 0, s, w); break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
 hipError_t launch_wango_state_scan(const WStateArgs& w, bool reverse, hipStream_t s) {
   const int64_t n = (int64_t)w.B * w.H * w.dh * w.FhC;
   hipLaunchKernelGGL(state_scan_kernel, dim3((unsigned)ceil_div(n, 256)), dim3(256), 0, s, w, reverse ? 1 : 0);
@@ -601,14 +678,6 @@ hipError_t launch_wango_bwd_prep(const BwdArgs& a, const BwdPlan& p, void* fq_pe
 }
 
 const char* bwd_last_step() { return t_step; }
-
-hipError_t launch_head_transpose(const void* src, void* dst, int B, int H, int C, int Tp, hipStream_t s) {
-  typedef __bf16 T;
-  if (C % 32 != 0 || Tp % 64 != 0) return hipErrorInvalidValue;
-  hipLaunchKernelGGL(transpose_kernel<T>, dim3((unsigned)((int64_t)B * H * (C / 32) * (Tp / 64))), dim3(256), 0, s,
-                     static_cast<const T*>(src), static_cast<T*>(dst), H, C, Tp);
-  return hipGetLastError();
-}
 
 hipError_t launch_wango_bwd_finish(const BwdArgs& a, const BwdPlan& p, float* theta_blk, hipStream_t s) {
   if (a.H > kMaxBwdHeads) return hipErrorInvalidValue;

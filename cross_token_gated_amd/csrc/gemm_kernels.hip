@@ -1150,81 +1150,6 @@ void dsmm_kernel(BwdArgs a, int64_t ntiles, int nch, int64_t items) {
   }
 }
 
-// KW sums: per tile t of (sequence, head) bh, tsum[e][f] = sum_{rows of t} aT[e][row] xT[f][row]:
-// A = aT rows e (d_h of them, rows past d_h zero), B = xT rows f, k = the tile's 128 positions.
-using StCfg = TileCfg<64, 128, 32, 2, 2, 3, 1>;
-template <int P> struct GuardedRows {   // A rows with a validity flag (rows past the end read zeros)
-  struct raw {
-    u32x4 v;
-  };
-  const bf16* ptr[P];
-  bool ok[P];
-  __device__ __forceinline__ void fetch(raw& x, int p, int k0) const {
-    x.v = *reinterpret_cast<const u32x4*>(ptr[p] + k0);
-  }
-  __device__ __forceinline__ Parts<1> convert(const raw& x, int p) const {
-    Parts<1> o;
-    o.p[0] = ok[p] ? x.v : u32x4{0u, 0u, 0u, 0u};
-    return o;
-  }
-};
-
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2)))
-void state_sums_kernel(WStateArgs w) {
-  using CF = StCfg;
-  typedef bf16 T;
-  constexpr int PA = tile_chunks<CF, T>(CF::BM) / 4, PB = tile_chunks<CF, T>(CF::BN) / 4;
-  __shared__ __align__(16) unsigned char smem[ops_bytes<CF, T>()];
-  const int nmt = (w.dh + CF::BM - 1) / CF::BM, nnt = (w.FhC + CF::BN - 1) / CF::BN;
-  int64_t id = blockIdx.x;
-  const int nn = (int)(id % nnt);
-  id /= nnt;
-  const int mm = (int)(id % nmt);
-  id /= nmt;
-  const int t = (int)(id % w.nt);
-  const int64_t bh = id / w.nt;
-  const int tid = threadIdx.x;
-  const T* aT = static_cast<const T*>(w.aT) + bh * w.dh * (int64_t)w.Tp + (int64_t)t * kBwdTile;
-  const T* xT = static_cast<const T*>(w.xT) + bh * w.FhC * (int64_t)w.Tp + (int64_t)t * kBwdTile;
-  GuardedRows<PA> sa;
-#pragma unroll
-  for (int p = 0; p < PA; ++p) {
-    const PiecePos<CF, T> pp = piece_pos<CF, T>(tid, p);
-    const int e = mm * CF::BM + pp.row;
-    sa.ptr[p] = aT + (int64_t)(e < w.dh ? e : 0) * w.Tp + pp.kp * piece_elems<T>();
-    sa.ok[p] = e < w.dh;
-  }
-  RowSource<T, PB> sb;
-#pragma unroll
-  for (int p = 0; p < PB; ++p) {
-    const PiecePos<CF, T> pp = piece_pos<CF, T>(tid, p);
-    const int f = nn * CF::BN + pp.row;
-    sb.ptr[p] = xT + (int64_t)(f < w.FhC ? f : 0) * w.Tp + pp.kp * piece_elems<T>();
-    sb.ok[p] = f < w.FhC;
-  }
-  f32x4 acc[CF::IB][CF::JB];
-#pragma unroll
-  for (int i = 0; i < CF::IB; ++i)
-#pragma unroll
-    for (int j = 0; j < CF::JB; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
-  gemm_mainloop<CF, T>(acc, reinterpret_cast<T*>(smem), kBwdTile / CF::BK, sa, sb);
-  float* out = w.tsum + ((bh * w.nt + t) * w.dh) * (int64_t)w.FhC;
-  const int lane = tid & 63, col = lane & 15, grp = lane >> 4;
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int wr = wave / CF::WN, wc = wave % CF::WN;
-#pragma unroll
-  for (int i = 0; i < CF::IB; ++i)
-#pragma unroll
-    for (int j = 0; j < CF::JB; ++j) {
-      const int f = nn * CF::BN + wc * CF::WTN + j * 16 + col;
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const int e = mm * CF::BM + wr * CF::WTM + i * 16 + grp * 4 + q;
-        if (e < w.dh && f < w.FhC) out[(int64_t)e * w.FhC + f] = acc[i][j][q];
-      }
-    }
-}
-
 // KW read-out: for tile t of (sequence, head) bh, out[row][e] = sum_f rows[row][f] state_t[e][f]
 // (S: rows = augmented u of destination tile t; R: augmented g of source tile t).
 template <int DH>
@@ -1304,14 +1229,6 @@ static hipError_t launch_dsmm_w(const BwdArgs& a, const BwdPlan& p, hipStream_t 
 
 hipError_t launch_tango_dsmm(const BwdArgs& a, const BwdPlan& p, hipStream_t s) {
   return a.window > 0 ? launch_dsmm_w<true>(a, p, s) : launch_dsmm_w<false>(a, p, s);
-}
-
-hipError_t launch_wango_state_sums(const WStateArgs& w, hipStream_t s) {
-  using CF = StCfg;
-  if (w.FhC % CF::BK != 0) return hipErrorInvalidValue;
-  const int64_t n = (int64_t)w.B * w.H * w.nt * ceil_div(w.dh, CF::BM) * ceil_div(w.FhC, CF::BN);
-  hipLaunchKernelGGL(state_sums_kernel, dim3((unsigned)n), dim3(kThreads), 0, s, w);
-  return hipGetLastError();
 }
 
 hipError_t launch_wango_state_readout(const WStateArgs& w, hipStream_t s) {

@@ -199,7 +199,7 @@ hipError_t launch_tango_bwd_finish(const BwdArgs& a, const BwdPlan& p, hipStream
 // feature layouts and the finish (bwd_kernels.hip)
 struct WStateArgs {
   const void* aT;      // [B*H][dh][Tp] source features (S) / destination features (R)
-  const void* xT;      // [B*H][FhC][Tp] augmented g (S) / u (R), transposed
+  const void* xrm;     // [B*Tp][H][FhC] augmented g (S) / u (R), row-major
   float* tsum;         // [B*H][nt][dh][FhC] per-tile sums
   void* state;         // [B*H][nt][dh][FhC] bf16: S exclusive prefix / R suffix from tile t + nb
   const void* rows;    // [B*Tp][H][FhC] augmented u (S read-out) / g (R read-out)
@@ -218,8 +218,6 @@ hipError_t launch_wango_bwd_finish(const BwdArgs& a, const BwdPlan& p, float* th
 hipError_t launch_wango_bwd_prep(const BwdArgs& a, const BwdPlan& p, void* fq_perm, void* fk_pk, hipStream_t s);
 // Name of the kernel the backward prep launched last on this thread.
 const char* bwd_last_step();
-// row-major [B*Tp][H*C] -> [B][H][C][Tp]
-hipError_t launch_head_transpose(const void* src, void* dst, int B, int H, int C, int Tp, hipStream_t s);
 
 // ---- autoregressive decode -------------------------------------------------
 

@@ -881,7 +881,7 @@ hipError_t wango_scan_band(const tango_shape_t* s, int32_t window, int32_t chunk
 struct WBwdLayout {
   WFwdLayout f;   // the reversed problem's forward scratch (dg)
   size_t u_rm, g_rm, qT, kT, pT, aT, p_rm, a_rm, q_rev, k_rev, u_rev_pk, delta;
-  size_t ds_rm, ds_t, dp_rm, dp_t, part, part_theta, theta_el, gT, uT, tsum, state, total;
+  size_t ds_rm, ds_t, dp_rm, dp_t, part, part_theta, theta_el, tsum, state, total;
   BwdPlan plan;
 };
 WBwdLayout make_wbwd_layout(const tango_shape_t* s, int32_t window, int32_t chunk) {
@@ -918,8 +918,6 @@ WBwdLayout make_wbwd_layout(const tango_shape_t* s, int32_t window, int32_t chun
   L.part = take((size_t)6 * M * HD * sizeof(float));
   L.part_theta = take((size_t)L.plan.items_ds * sizeof(float));
   L.theta_el = take((size_t)((M * HD + 255) / 256) * s->n_heads * sizeof(float));
-  L.gT = take(rows);
-  L.uT = take(rows);
   const size_t st_el = (size_t)bh * L.plan.nt * s->head_dim * L.plan.FhC;
   L.tsum = take(st_el * sizeof(float));
   L.state = take(st_el * es);
@@ -1076,18 +1074,15 @@ int wango_aggregate_bwd(const tango_shape_t* shape, int32_t window, int32_t chun
     w.FhC = L.plan.FhC;
     w.nt = L.plan.nt;
     w.nb = L.plan.nb;
-    if ((e = launch_head_transpose(a.g_rm, base + L.gT, s->batch, s->n_heads, L.plan.FhC, a.Tp, st)) != hipSuccess ||
-        (e = launch_head_transpose(a.u_rm, base + L.uT, s->batch, s->n_heads, L.plan.FhC, a.Tp, st)) != hipSuccess)
-      return hip_fail(e, "row transposes");
     w.aT = a.aT;
-    w.xT = base + L.gT;
+    w.xrm = a.g_rm;
     w.rows = a.u_rm;
     w.out = a.part + 4 * MHD;
     if ((e = launch_wango_state_sums(w, st)) != hipSuccess || (e = launch_wango_state_scan(w, false, st)) != hipSuccess ||
         (e = launch_wango_state_readout(w, st)) != hipSuccess)
       return hip_fail(e, "prefix states (dp)");
     w.aT = a.pT;
-    w.xT = base + L.uT;
+    w.xrm = a.u_rm;
     w.rows = a.g_rm;
     w.out = a.part + 5 * MHD;
     if ((e = launch_wango_state_sums(w, st)) != hipSuccess || (e = launch_wango_state_scan(w, true, st)) != hipSuccess ||

@@ -37,6 +37,8 @@
 // split in two source ranges done by two workgroups, each writing a float32
 // partial; the second to finish adds the two (a commutative sum, so the result
 // does not depend on which finishes first) and writes gbar.
+#include <type_traits>
+
 #include "common.hpp"
 #include "kernels.hpp"
 
@@ -450,44 +452,84 @@ __global__ __launch_bounds__(kAggThreads) void agg_kernel(AggArgs a, int nfc, in
     }
 
     if (finish && has_cols) {
+      // The loads of a destination block (the partner's partial, or WANGO's
+      // older-prefix terms) are issued together, one block ahead of its sums
+      // and stores: left to itself, the compiler waits for each batch before
+      // issuing the next, one memory round trip apiece.  The additions keep
+      // their order (the stored values do not change).
+      struct Extra {
+        float part[NFB][4];
+        f32x4 nold[NFB];
+        float pden, zold;
+      };
+      auto epilogue = [&](auto comb) {
+        constexpr bool C = decltype(comb)::value;
+        auto fetch = [&](int ib, Extra& e) {
+          const int i = i0 + ib * 16 + li;
+          if constexpr (C) {
+            e.pden = __hip_atomic_load(a.part_den + odbase + ib * 16 + li, __ATOMIC_RELAXED,
+                                       __HIP_MEMORY_SCOPE_AGENT);
 #pragma unroll
-      for (int ib = 0; ib < NIB; ++ib) {
-        const int i = i0 + ib * 16 + li;
-        // the two partials are added first: mine + other is the same float
-        // whichever workgroup finishes last
-        float dsum = den[ib];
-        if (combine)
-          dsum += __hip_atomic_load(a.part_den + odbase + ib * 16 + li, __ATOMIC_RELAXED,
-                                    __HIP_MEMORY_SCOPE_AGENT);
-        dsum += null_w * (float)(i + 1);
-        if (MODE == 1) dsum += escale * a.z_old[(mseq + i) * a.H + h];
-        // Options: the denominator for a later backward pass (one writer per
-        // row: column chunk 0, wave 0); the numerator alone; rows stored in
-        // reverse order (rows past the end are not stored then)
-        if (a.den_out && fc == 0 && wave == 0 && lg == 0 && i < a.T) a.den_out[(mseq + i) * a.H + h] = dsum;
-        const float inv = a.num_only ? 1.0f : 1.0f / dsum;
-        const int64_t orow = a.rev_out ? mseq + (a.T - 1 - i) : mseq + i;
-        const bool ostore = !a.rev_out || i < a.T;
+            for (int fb = 0; fb < NFB; ++fb)
 #pragma unroll
-        for (int fb = 0; fb < NFB; ++fb) {
-          f32x4 num = acc[ib][fb];
-          if (combine) {
-#pragma unroll
-            for (int r = 0; r < 4; ++r)
-              num[r] += __hip_atomic_load(a.part + obase + part_index(ib * (FS / 16) + wave * NFB + fb, r, lane),
-                                          __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+              for (int r = 0; r < 4; ++r)
+                e.part[fb][r] = __hip_atomic_load(a.part + obase + part_index(ib * (FS / 16) + wave * NFB + fb, r, lane),
+                                                  __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
           }
-          if (MODE == 1) {
-            const int64_t nblk = ((mseq + i0) / 16 + ib) * (F / 16) + (col0 / 16 + fb);
-            const f32x4 no = *reinterpret_cast<const f32x4*>(a.n_old + (nblk * 64 + lane) * 4);
-            num += escale * no;
+          if constexpr (MODE == 1) {
+            e.zold = a.z_old[(mseq + i) * a.H + h];
+#pragma unroll
+            for (int fb = 0; fb < NFB; ++fb) {
+              const int64_t nblk = ((mseq + i0) / 16 + ib) * (F / 16) + (col0 / 16 + fb);
+              e.nold[fb] = *reinterpret_cast<const f32x4*>(a.n_old + (nblk * 64 + lane) * 4);
+            }
           }
-          // gbar is not head-padded: columns past the head's width are pad
-          const int c = f_base + fb * 16 + lg * 4;
-          if (c < a.Fho && ostore)
-            store_quad<T>(gbar + orow * a.Fo + (int64_t)h * a.Fho + c, cvt_quad<T>(num * inv));
+        };
+        auto store_block = [&](int ib, const Extra& e) {
+          const int i = i0 + ib * 16 + li;
+          // the two partials are added first: mine + other is the same float
+          // whichever workgroup finishes last
+          float dsum = den[ib];
+          if constexpr (C) dsum += e.pden;
+          dsum += null_w * (float)(i + 1);
+          if constexpr (MODE == 1) dsum += escale * e.zold;
+          // Options: the denominator for a later backward pass (one writer per
+          // row: column chunk 0, wave 0); the numerator alone; rows stored in
+          // reverse order (rows past the end are not stored then)
+          if (a.den_out && fc == 0 && wave == 0 && lg == 0 && i < a.T) a.den_out[(mseq + i) * a.H + h] = dsum;
+          const float inv = a.num_only ? 1.0f : 1.0f / dsum;
+          const int64_t orow = a.rev_out ? mseq + (a.T - 1 - i) : mseq + i;
+          const bool ostore = !a.rev_out || i < a.T;
+#pragma unroll
+          for (int fb = 0; fb < NFB; ++fb) {
+            f32x4 num = acc[ib][fb];
+            if constexpr (C) {
+#pragma unroll
+              for (int r = 0; r < 4; ++r) num[r] += e.part[fb][r];
+            }
+            if constexpr (MODE == 1) num += escale * e.nold[fb];
+            // gbar is not head-padded: columns past the head's width are pad
+            const int c = f_base + fb * 16 + lg * 4;
+            if (c < a.Fho && ostore)
+              store_quad<T>(gbar + orow * a.Fo + (int64_t)h * a.Fho + c, cvt_quad<T>(num * inv));
+          }
+        };
+        Extra e0, e1;
+        fetch(0, e0);
+#pragma unroll
+        for (int ib = 0; ib < NIB; ib += 2) {
+          if (ib + 1 < NIB) fetch(ib + 1, e1);
+          __builtin_amdgcn_sched_barrier(0);
+          store_block(ib, e0);
+          if (ib + 1 < NIB) {
+            if (ib + 2 < NIB) fetch(ib + 2, e0);
+            __builtin_amdgcn_sched_barrier(0);
+            store_block(ib + 1, e1);
+          }
         }
-      }
+      };
+      if (combine) epilogue(std::true_type{});
+      else epilogue(std::false_type{});
     }
     __syncthreads();   // LDS is reused by the next job
   };

@@ -39,7 +39,8 @@ namespace {
 constexpr int kScanWaves = 4;
 constexpr int kScanThreads = 64 * kScanWaves;
 // Source-unit register sets per wave (ring depth): all but one are in flight.
-// (Five or six sets for bf16 measured no faster than four.)
+// (Five or six sets for bf16 measured no faster than four; with the features
+// shared through LDS, six or eight in pass 1 and five in pass 2 neither.)
 template <typename T, int DH, bool MAIN> constexpr int ring_sets() { return sizeof(T) == 4 ? 2 : 4; }
 // Segment sums loaded per batch while the starting state is summed: about 64
 // registers of loads in flight.
@@ -77,46 +78,67 @@ __device__ __forceinline__ ScanWg scan_wg(int64_t id, int nslices, int H, int ns
   return w;
 }
 
-// A unit of sources in registers: the gate fragments of this wave's columns
-// and the key-feature fragments (A operand of S += phi_K^T G).  The unit is 64
-// sources, 32 for d_h = 128 (whose key fragments are twice as many registers).
+// A unit of sources: the gate fragments of this wave's columns in registers,
+// and the key-feature fragments (A operand of S += phi_K^T G), which every wave
+// of the workgroup needs, shared through an LDS ring: each wave loads KW of
+// the unit's KF fragments and stashes them one unit ahead.  The unit is 64
+// sources, 32 for d_h = 128.
 template <int DH> constexpr int unit_len() { return DH >= 128 ? 32 : 64; }
+template <int DH> constexpr int unit_kf() { return unit_len<DH>() / 32 * (DH / 16); }   // KF
 template <typename T, int DH, int NFB> struct UnitRegs {
-  static constexpr int U = unit_len<DH>();
+  static constexpr int U = unit_len<DH>(), KW = unit_kf<DH>() / kScanWaves;
+  static_assert(unit_kf<DH>() % kScanWaves == 0, "feature fragments per wave");
   Frag<T> g[U / 32][NFB];
-  Frag<T> k[U / 32][DH / 16];
+  Frag<T> kq[KW];   // fragments wave * KW .. wave * KW + KW - 1 of the unit (ks-major)
 };
+// LDS ring of the units' feature fragments: [NS][KF][64 lanes].
+template <typename T, int DH, int NS> using FeatRing = Frag<T>[NS][unit_kf<DH>()][64];
 
 template <typename T, int DH, int NFB>
 __device__ __forceinline__ void load_unit(UnitRegs<T, DH, NFB>& c, const T* __restrict__ fk,
                                           const T* __restrict__ gp, int64_t row0, int HD, int hcol,
-                                          int64_t col, int F, int li, int lg) {
+                                          int64_t col, int F, int li, int lg, int wave) {
+  constexpr int KW = UnitRegs<T, DH, NFB>::KW;
 #pragma unroll
   for (int ks = 0; ks < unit_len<DH>() / 32; ++ks) {
     const int64_t blk = row0 / 32 + ks;
 #pragma unroll
     for (int fb = 0; fb < NFB; ++fb) c.g[ks][fb] = load_frag<T>(gp + packed_offset(blk, lg, col + fb * 16 + li, F));
+  }
 #pragma unroll
-    for (int eb = 0; eb < DH / 16; ++eb) c.k[ks][eb] = load_frag<T>(fk + packed_offset(blk, lg, hcol + eb * 16 + li, HD));
+  for (int q = 0; q < KW; ++q) {
+    const int fi = wave * KW + q, ks = fi / (DH / 16), eb = fi % (DH / 16);
+    c.kq[q] = load_frag<T>(fk + packed_offset(row0 / 32 + ks, lg, hcol + eb * 16 + li, HD));
   }
 }
 
-// S (this wave's DH x 16*NFB slice; DH/16 x NFB accumulator blocks) += phi_K^T G
-// over one unit, and Sz += phi_K^T 1 when with_z.
-template <typename T, int DH, int NFB>
-__device__ __forceinline__ void apply_unit(f32x4 (&S)[DH / 16][NFB], f32x4 (&Sz)[DH / 16], bool with_z,
-                                           const UnitRegs<T, DH, NFB>& c) {
+template <typename T, int DH, int NFB, int NS>
+__device__ __forceinline__ void stash_unit(FeatRing<T, DH, NS>& ring, int slot, const UnitRegs<T, DH, NFB>& c,
+                                           int wave, int lane) {
+  constexpr int KW = UnitRegs<T, DH, NFB>::KW;
 #pragma unroll
-  for (int ks = 0; ks < unit_len<DH>() / 32; ++ks)
+  for (int q = 0; q < KW; ++q) ring[slot][wave * KW + q][lane] = c.kq[q];
+}
+
+// S (this wave's DH x 16*NFB slice; DH/16 x NFB accumulator blocks) += phi_K^T G
+// over one unit (features from ring slot `slot`), and Sz += phi_K^T 1 when with_z.
+template <typename T, int DH, int NFB, int NS>
+__device__ __forceinline__ void apply_unit(f32x4 (&S)[DH / 16][NFB], f32x4 (&Sz)[DH / 16], bool with_z,
+                                           const UnitRegs<T, DH, NFB>& c, const FeatRing<T, DH, NS>& ring,
+                                           int slot, int lane) {
+#pragma unroll
+  for (int ks = 0; ks < unit_len<DH>() / 32; ++ks) {
+    Frag<T> k[DH / 16];
+#pragma unroll
+    for (int eb = 0; eb < DH / 16; ++eb) k[eb] = ring[slot][ks * (DH / 16) + eb][lane];
 #pragma unroll
     for (int eb = 0; eb < DH / 16; ++eb)
 #pragma unroll
-      for (int fb = 0; fb < NFB; ++fb) mma(S[eb][fb], c.k[ks][eb], c.g[ks][fb]);
-  if (with_z) {
+      for (int fb = 0; fb < NFB; ++fb) mma(S[eb][fb], k[eb], c.g[ks][fb]);
+    if (with_z) {
 #pragma unroll
-    for (int ks = 0; ks < unit_len<DH>() / 32; ++ks)
-#pragma unroll
-      for (int eb = 0; eb < DH / 16; ++eb) mma(Sz[eb], c.k[ks][eb], ones_frag<T>());
+      for (int eb = 0; eb < DH / 16; ++eb) mma(Sz[eb], k[eb], ones_frag<T>());
+    }
   }
 }
 
@@ -128,22 +150,33 @@ __device__ __forceinline__ int64_t seg_block(int64_t slice_seg, int wave, int eb
   return slice_seg * (int64_t)(DH * FSC) + (((wave * (DH / 16) + eb) * NFB + fb) * 64 + lane) * 4;
 }
 
-// One segment: its source units in order through a ring of NS register sets.  MAIN adds, before the first unit of every chunk, the read-out of the
-// state for the destination chunk that chunk feeds (through `boundary`).
+// One segment: its source units in order through a ring of NS register sets
+// (and NS LDS slots for the features).  Before unit u is applied, the
+// features of unit u + 1 (loaded NS - 2 units earlier) go to their slot and an
+// LDS-only barrier publishes them; unit u's slot was published one unit ago,
+// and a slot is rewritten NS - 1 barriers after it was last read.  MAIN adds,
+// before the first unit of every chunk, the read-out of the state for the
+// destination chunk that chunk feeds (through `boundary`).  The caller has
+// loaded units u0 .. u0 + NS - 2, stashed unit u0 and synchronised.
 template <typename T, int DH, int NFB, int UPC, int NS, typename Boundary>
 __device__ __forceinline__ void walk_units(f32x4 (&S)[DH / 16][NFB], f32x4 (&Sz)[DH / 16], bool with_z,
-                                           UnitRegs<T, DH, NFB> (&R)[NS], int u0, int u1,
-                                           const T* fk, const T* gp, int64_t mseq, int HD, int hcol,
-                                           int64_t col, int F, int li, int lg, Boundary&& boundary) {
+                                           UnitRegs<T, DH, NFB> (&R)[NS], FeatRing<T, DH, NS>& ring, int u0,
+                                           int u1, const T* fk, const T* gp, int64_t mseq, int HD, int hcol,
+                                           int64_t col, int F, int li, int lg, int wave, Boundary&& boundary) {
+  const int lane = lg * 16 + li;
   auto load = [&](UnitRegs<T, DH, NFB>& r, int u) {
-    load_unit<T, DH, NFB>(r, fk, gp, mseq + (int64_t)min(u, u1 - 1) * unit_len<DH>(), HD, hcol, col, F, li, lg);
+    load_unit<T, DH, NFB>(r, fk, gp, mseq + (int64_t)min(u, u1 - 1) * unit_len<DH>(), HD, hcol, col, F, li, lg,
+                          wave);
   };
   for (int u = u0; u < u1; u += NS) {
 #pragma unroll
     for (int j = 0; j < NS; ++j) {
       load(R[(j + NS - 1) % NS], u + j + NS - 1);
+      // units past the end re-read the last one: stashing them is harmless
+      stash_unit<T, DH, NFB, NS>(ring, (j + 1) % NS, R[(j + 1) % NS], wave, lane);
+      lds_sync();
       if ((u + j) % UPC == 0 && u + j < u1) boundary((u + j) / UPC);
-      if (u + j < u1) apply_unit<T, DH, NFB>(S, Sz, with_z, R[j]);
+      if (u + j < u1) apply_unit<T, DH, NFB, NS>(S, Sz, with_z, R[j], ring, j, lane);
     }
   }
 }
@@ -176,13 +209,16 @@ void scan_partial_kernel(ScanArgs a) {
   const int c0 = w.seg * a.chunks_per_seg, c1 = min(nchunks, c0 + a.chunks_per_seg);
   constexpr int UPC = CH / unit_len<DH>(), NS = ring_sets<T, DH, false>();
   const int u0 = c0 * UPC, u1 = c1 * UPC;
+  __shared__ FeatRing<T, DH, NS> ring;
   UnitRegs<T, DH, NFB> R[NS];
 #pragma unroll
   for (int j = 0; j < NS - 1; ++j)
     load_unit<T, DH, NFB>(R[j], fk, gp, mseq + (int64_t)min(u0 + j, u1 - 1) * unit_len<DH>(), HD, w.h * DH,
-                          col, a.F, li, lg);
-  walk_units<T, DH, NFB, UPC, NS>(S, Sz, with_z, R, u0, u1, fk, gp, mseq, HD, w.h * DH, col, a.F, li, lg,
-                                  [](int) {});
+                          col, a.F, li, lg, wave);
+  stash_unit<T, DH, NFB, NS>(ring, 0, R[0], wave, lane);
+  lds_sync();
+  walk_units<T, DH, NFB, UPC, NS>(S, Sz, with_z, R, ring, u0, u1, fk, gp, mseq, HD, w.h * DH, col, a.F, li, lg,
+                                  wave, [](int) {});
 
   const int64_t slice_seg = (((w.b * a.H + w.h) * nslices + w.fsl) * (int64_t)a.nseg + w.seg);
 #pragma unroll
@@ -239,11 +275,12 @@ void scan_main_kernel(ScanArgs a) {
   load_q(c0);   // first: the ring loads issued after it keep later waits on it precise
 
   // first source units in flight
+  __shared__ FeatRing<T, DH, NS> ring;
   UnitRegs<T, DH, NFB> R[NS];
 #pragma unroll
   for (int j = 0; j < NS - 1; ++j)
     load_unit<T, DH, NFB>(R[j], fk, gp, mseq + (int64_t)min(u0 + j, u1 - 1) * unit_len<DH>(), HD, w.h * DH,
-                          col, F, li, lg);
+                          col, F, li, lg, wave);
   // starting state: sum of the segment sums before this one
   f32x4 S[DH / 16][NFB], Sz[DH / 16];
 #pragma unroll
@@ -364,7 +401,10 @@ void scan_main_kernel(ScanArgs a) {
     }
     if (c + 1 < c1) load_q(c + 1);   // after the stores: waits on it stay precise
   };
-  walk_units<T, DH, NFB, UPC, NS>(S, Sz, with_z, R, u0, u1, fk, gp, mseq, HD, w.h * DH, col, F, li, lg, boundary);
+  stash_unit<T, DH, NFB, NS>(ring, 0, R[0], wave, lane);
+  lds_sync();
+  walk_units<T, DH, NFB, UPC, NS>(S, Sz, with_z, R, ring, u0, u1, fk, gp, mseq, HD, w.h * DH, col, F, li, lg, wave,
+                                  boundary);
 }
 
 template <typename T, int DH, int CH, int NFB>

@@ -28,7 +28,9 @@
 // replays its segment and emits the read-outs.  Both passes are bound by the
 // latency of their loads, so each wave keeps a ring of register sets of source
 // units with all but one in flight, and pass 2 stages the query
-// features of the next chunk through LDS while the current chunk runs.
+// features of the next chunk through LDS while the current chunk runs.  The
+// key features of a unit, which all four waves multiply, are loaded once per
+// workgroup (a quarter by each wave) and shared through an LDS ring.
 #include "common.hpp"
 #include "kernels.hpp"
 

@@ -1069,15 +1069,23 @@ __device__ __forceinline__ void dsmm_job(const BwdArgs& a, int64_t ntiles, int n
   constexpr int DIR = PROD & 1;
   constexpr int PA = tile_chunks<CF, T>(CF::BM) / 4, PB = tile_chunks<CF, T>(CF::BN) / 4;
   const int nt = a.Tp / kBwdTile;
-  // k tiles of this chunk: DIR 0 jt <= r (WANGO jt > r - nb), DIR 1 it >= r (WANGO it < r + nb)
-  int first = c * kBwdChunkTiles, last = first + kBwdChunkTiles - 1;
-  if (DIR == 0) {
-    last = min(last, r);
-    if (W) first = max(first, r - a.nb + 1);
+  // k tiles of this chunk.  TANGO: chunk c holds tiles 8c .. 8c + 7 of the
+  // sum, DIR 0 those with jt <= r, DIR 1 those with it >= r.  WANGO: one chunk,
+  // the near tiles of row tile r (nb <= 8 of them): DIR 0 jt = r - nb + 1 .. r,
+  // DIR 1 it = r .. r + nb - 1, clipped to the sequence.
+  int first, last;
+  if (W) {
+    first = DIR == 0 ? max(0, r - a.nb + 1) : r;
+    last = DIR == 0 ? r : min(nt - 1, r + a.nb - 1);
   } else {
-    first = max(first, r);
-    last = min(last, nt - 1);
-    if (W) last = min(last, r + a.nb - 1);
+    first = c * kBwdChunkTiles;
+    last = first + kBwdChunkTiles - 1;
+    if (DIR == 0) {
+      last = min(last, r);
+    } else {
+      first = max(first, r);
+      last = min(last, nt - 1);
+    }
   }
   if (first > last) return;   // workgroup-uniform
   const int tid = threadIdx.x;

@@ -6,7 +6,8 @@ differences of the forward oracle) on the same bf16 inputs.  The GPU side runs
 ``wango_aggregate_fwd_train`` (the scan and band that also store the
 denominators), then ``wango_aggregate_bwd``.  Cases cover windows of one to
 five 128-row tiles, windows at or past the sequence end (no older sources),
-one to three heads, d_h 32 / 64 / 128, prefix chunks 64 and 128, and the null gate.
+one to three heads, d_h 32 / 64 / 128, prefix chunks 64 and 128, sequences of
+up to 20 row tiles, and the null gate.
 
 Bars as for the TANGO backward (tests/test_gpu_backward.py, derived there from
 the bf16 storage of u, the gates, gbar, the weights and ds; here the older
@@ -41,6 +42,10 @@ CASES = [
     dict(B=1, T=200, H=1, dh=64, Fh=128, W=256, C=128),   # window past the end: no older sources
     dict(B=1, T=300, H=3, dh=32, Fh=128, W=128, C=64),    # odd head count: rows of 96 q/k columns
     dict(B=1, T=200, H=16, dh=32, Fh=1780, W=64, C=64),   # the pages' geometry: heads padded to 1792
+    # more than eight 128-row tiles: every row tile's near tiles are summed
+    # (row tiles past the eighth once lost their window terms of dq and dk)
+    dict(B=1, T=2500, H=2, dh=64, Fh=128, W=256, C=128),
+    dict(B=1, T=1900, H=1, dh=32, Fh=128, W=512, C=64),
 ]
 
 

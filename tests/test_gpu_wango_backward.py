@@ -7,7 +7,7 @@ differences of the forward oracle) on the same bf16 inputs.  The GPU side runs
 denominators), then ``wango_aggregate_bwd``.  Cases cover windows of one to
 five 128-row tiles, windows at or past the sequence end (no older sources),
 one to three heads, d_h 32 / 64 / 128, prefix chunks 64 and 128, sequences of
-up to 20 row tiles, and the null gate.
+up to 33 row tiles, and the null gate.
 
 Bars as for the TANGO backward (tests/test_gpu_backward.py, derived there from
 the bf16 storage of u, the gates, gbar, the weights and ds; here the older
@@ -46,6 +46,8 @@ CASES = [
     # (row tiles past the eighth once lost their window terms of dq and dk)
     dict(B=1, T=2500, H=2, dh=64, Fh=128, W=256, C=128),
     dict(B=1, T=1900, H=1, dh=32, Fh=128, W=512, C=64),
+    # 33 row tiles: the tile-sum prefix and suffix run in two batches of tiles
+    dict(B=1, T=4200, H=1, dh=32, Fh=64, W=128, C=64),
 ]
 
 

@@ -117,3 +117,45 @@ def test_backward_scratch_independent(mode):
                                     ws)
             return [dq, dk, dg[:T], dth, dnl]
     _twice(f"{mode} backward T={T}", n, bwd)
+
+
+def test_concurrent_streams_share_nothing():
+    """The block calls keep no state between calls: a TANGO and a WANGO block
+    at T = 8192 enqueued alternately on two streams (each with its own
+    workspace and output, so that their kernels can overlap) give bitwise the
+    outputs of the same calls run one after the other."""
+    cases = []
+    for name in ("tango_bf16_t8192_r4", "wango_bf16_t8192_w256"):
+        w = wl.WORKLOADS[name]
+        inp = wl.make_inputs(w)
+        b = block_weights(w, inp, DEV)
+        x = dev_tensor(inp.h, w.io, DEV)
+        shape = api.shape_of(x, b, w.rope_base, w.rms_eps)
+        if w.mode == "tango":
+            ws = api.workspace(api.tango_workspace_size(shape), DEV)
+            fn = (lambda x, b, w, ws: lambda out, s: api.tango_block_fwd(
+                x, b, out=out, ws=ws, rope_base=w.rope_base, rms_eps=w.rms_eps, stream=s))(x, b, w, ws)
+        else:
+            ws = api.workspace(api.wango_workspace_size(shape, w.window, w.head_dim, w.chunk), DEV)
+            fn = (lambda x, b, w, ws: lambda out, s: api.wango_block_fwd(
+                x, b, w.window, w.head_dim, w.chunk, out=out, ws=ws, rope_base=w.rope_base, rms_eps=w.rms_eps,
+                stream=s))(x, b, w, ws)
+        cases.append((name, x, fn))
+    announce("scratch: the two blocks one after the other")
+    ref = []
+    for name, x, fn in cases:
+        out = torch.empty_like(x)
+        fn(out, torch.cuda.current_stream())
+        torch.cuda.synchronize()
+        ref.append(out)
+    announce("scratch: the two blocks interleaved on two streams")
+    streams = [torch.cuda.Stream(), torch.cuda.Stream()]
+    outs = [[torch.empty_like(x) for _ in range(3)] for _, x, _ in cases]
+    torch.cuda.synchronize()
+    for r in range(3):
+        for k, (name, x, fn) in enumerate(cases):
+            fn(outs[k][r], streams[k])
+    torch.cuda.synchronize()
+    for k, (name, x, fn) in enumerate(cases):
+        for r in range(3):
+            assert torch.equal(_bits(outs[k][r]), _bits(ref[k])), f"{name}, launch {r} on its own stream"

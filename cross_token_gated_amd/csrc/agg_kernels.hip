@@ -46,15 +46,17 @@ namespace tango {
 
 namespace {
 
-// Destination rows per tile and gate columns per wave: WIDE where the head's
-// gate width is a multiple of 8 * WIDE, else 32 where it is a multiple of 256,
-// else 16 (narrow); in the narrow variant a wave whose columns lie past the
-// head's width skips the product (a wave-uniform branch).
+// Destination rows per tile and gate columns per wave.  The columns per wave
+// (WIDE, 48, 32 or 16) are chosen per head width by a cost model (agg_wcols
+// below); where the width is not a multiple of 8 waves' columns, the last
+// column chunk has waves with fewer or no columns inside the head, which
+// multiply copies and store nothing past the width.
 template <typename T> struct AggCfg;
 template <> struct AggCfg<bf16> { static constexpr int BR = 128, WIDE = 64; };
 template <> struct AggCfg<float> { static constexpr int BR = 64, WIDE = 32; };
 constexpr int kNarrow = 16;
 constexpr int kMid = 32;
+constexpr int kMid48 = 48;                // bf16 only
 constexpr int kShortBR = 64;       // bf16 TANGO tiles of 64 rows, for grids that would underfill
 constexpr int kFillItems = 256;    // work items that fill the 256 compute units once
 
@@ -245,11 +247,18 @@ __global__ __launch_bounds__(kAggThreads) void agg_kernel(AggArgs a, int nfc, in
   // which keeps the compiler's load-counter waits exact across the loop.
   const int64_t gcol0 = has_cols ? col0 : (int64_t)h * Fh;
   const int g_lane = (lg * F + li) * 8;   // packed_offset(blk, lg, col, F) - packed_offset(blk, 0, col - li, F)
+  // 16-column blocks of this wave inside the head: with 48 columns a wave
+  // can straddle the head's end (the head width is a multiple of 64); its
+  // blocks past the end re-read the last block inside and are never stored.
+  // Other widths keep constant offsets.
+  constexpr bool kStraddle = 64 % WCOLS != 0;
+  const int nvb = has_cols ? min(NFB, (Fh - f_base) / 16) : NFB;
+  auto in_head = [&](int fb) { return kStraddle ? min(fb, nvb - 1) : fb; };
   auto gate_fetch = [&](int jb, int ks, Frag<T> (&gf)[NFB]) {
     const int64_t blk = (mseq + (int64_t)jb * BC) / 32 + ks;
     const T* base = gp + packed_offset(blk, 0, gcol0, F);   // wave-uniform
 #pragma unroll
-    for (int fb = 0; fb < NFB; ++fb) gf[fb] = load_frag<T>(base + g_lane + fb * 16 * 8);
+    for (int fb = 0; fb < NFB; ++fb) gf[fb] = load_frag<T>(base + g_lane + in_head(fb) * 16 * 8);
   };
 
   // one destination tile over a range of source steps (called once or twice)
@@ -487,7 +496,7 @@ __global__ __launch_bounds__(kAggThreads) void agg_kernel(AggArgs a, int nfc, in
             e.zold = a.z_old[(mseq + i) * a.H + h];
 #pragma unroll
             for (int fb = 0; fb < NFB; ++fb) {
-              const int64_t nblk = ((mseq + i0) / 16 + ib) * (F / 16) + (col0 / 16 + fb);
+              const int64_t nblk = ((mseq + i0) / 16 + ib) * (F / 16) + (col0 / 16 + in_head(fb));
               e.nold[fb] = *reinterpret_cast<const f32x4*>(a.n_old + (nblk * 64 + lane) * 4);
             }
           }
@@ -570,15 +579,16 @@ hipError_t launch_agg_w(const AggArgs& a, int nfc, int rtiles, int64_t items, hi
 // per chunk: scores dh / 128, products wc / 16 and a fixed part 3.6 (the
 // exponentials, the row sums, the epilogue; the narrower variants also run
 // at a lower MFMA rate), in units of one 16-column product.  With 3.6 the
-// choice is the fastest of the three measured on gfx950 at T = 8192,
-// dh = 128 (64-row tiles where the grid would underfill): 64 columns for
-// Fh = 2048 (161 us against 198 and 281), 704 (106 against 112 and 153) and
-// 640 (107 against 114 and 153).
+// choice is the fastest measured on gfx950 at T = 8192, dh = 128 (64-row
+// tiles where the grid would underfill): 64 columns for Fh = 2048 (161 us
+// against 198 with 32 and 281 with 16); 48 for Fh = 704 and 640 (two chunks
+// of 384 that leave one or two wave slots idle, 86 us against 101 with 64,
+// 112 with 32 and 153 with 16).  48 is a bf16 variant only.
 template <typename T> int agg_wcols(int Fh, int dh) {
-  const int cand[3] = {AggCfg<T>::WIDE, kMid, kNarrow};
+  const int cand[4] = {AggCfg<T>::WIDE, kMid, kNarrow, sizeof(T) == 2 ? kMid48 : kMid};
   int best = cand[0];
   double best_cost = 0.0;
-  for (int c = 0; c < 3; ++c) {
+  for (int c = 0; c < 4; ++c) {
     const int wc = cand[c];
     const double cost = (double)ceil_div(Fh, kWaves * wc) * (dh / 128.0 + wc / 16.0 + 3.6);
     if (c == 0 || cost < best_cost) {
@@ -596,6 +606,9 @@ template <typename T, int MODE, int BR>
 hipError_t launch_agg_wc(const AggArgs& a, int wc, int nfc, int rtiles, int64_t items, hipStream_t s) {
   if (wc == AggCfg<T>::WIDE) return launch_agg_w<T, MODE, AggCfg<T>::WIDE, BR>(a, nfc, rtiles, items, s);
   if (wc == kMid) return launch_agg_w<T, MODE, kMid, BR>(a, nfc, rtiles, items, s);
+  if constexpr (sizeof(T) == 2) {
+    if (wc == kMid48) return launch_agg_w<T, MODE, kMid48, BR>(a, nfc, rtiles, items, s);
+  }
   if (wc == kNarrow) return launch_agg_w<T, MODE, kNarrow, BR>(a, nfc, rtiles, items, s);
   return hipErrorInvalidValue;
 }
@@ -630,7 +643,8 @@ AggPlan tango_agg_plan(int B, int Tp, int F, int H, int dh, bool bf) {
   // Few column chunks (narrow heads, one sequence) leave compute units idle
   // even with the long tiles split: halve the tile height to double the
   // items (each streams the same gate blocks for half the rows).
-  if (bf && p.items < kFillItems && p.fs == kWaves * AggCfg<bf16>::WIDE) shape(kShortBR);
+  if (bf && p.items < kFillItems && (p.fs == kWaves * AggCfg<bf16>::WIDE || p.fs == kWaves * kMid48))
+    shape(kShortBR);
   return p;
 }
 

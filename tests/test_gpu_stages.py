@@ -117,6 +117,12 @@ AGG_CASES = [
     dict(dtype="bf16", B=8, T=1000, d_model=128, d_gate=2048, n_heads=2, head_dim=64),
     dict(dtype="bf16", B=16, T=1100, d_model=128, d_gate=1024, n_heads=1, head_dim=128),
     dict(dtype="bf16", B=6, T=700, d_model=128, d_gate=4096, n_heads=4, head_dim=32),
+    # heads of 704, 320 and 1152 columns take waves of 48 columns: the first
+    # two end inside a wave (its last block past the head is dropped) and
+    # leave the wave after it without columns; 1152 fills three chunks
+    dict(dtype="bf16", B=1, T=1000, d_model=128, d_gate=704, n_heads=1, head_dim=128),
+    dict(dtype="bf16", B=2, T=300, d_model=128, d_gate=640, n_heads=2, head_dim=64),
+    dict(dtype="bf16", B=1, T=520, d_model=128, d_gate=2304, n_heads=2, head_dim=64),
     dict(dtype="f32", B=1, T=333, d_model=128, d_gate=256, n_heads=1, head_dim=128),
     dict(dtype="f32", B=2, T=64, d_model=128, d_gate=128, n_heads=2, head_dim=64),
 ]
@@ -299,6 +305,9 @@ BAND_CASES = [
     dict(dtype="bf16", B=2, T=333, d_model=128, d_gate=512, n_heads=2, head_dim=64, window=64, chunk=64),
     dict(dtype="bf16", B=1, T=700, d_model=128, d_gate=512, n_heads=2, head_dim=64, window=192, chunk=64),
     dict(dtype="bf16", B=1, T=200, d_model=128, d_gate=256, n_heads=4, head_dim=32, window=512, chunk=128),
+    # waves of 48 columns: a head of 704 ends inside a wave; two heads of 384
+    dict(dtype="bf16", B=1, T=700, d_model=128, d_gate=704, n_heads=1, head_dim=128, window=192, chunk=64),
+    dict(dtype="bf16", B=2, T=333, d_model=128, d_gate=768, n_heads=2, head_dim=64, window=128, chunk=64),
     dict(dtype="f32", B=1, T=300, d_model=128, d_gate=128, n_heads=1, head_dim=64, window=128, chunk=64),
     dict(dtype="f32", B=1, T=400, d_model=128, d_gate=128, n_heads=1, head_dim=64, window=128, chunk=128),
 ]

@@ -13,7 +13,8 @@
 // KO (§2.1, eq. 3): out_m = h_m + (gbar_m * v_m) W_o^T, the gated product
 // formed while the A tile is staged, the residual added in the epilogue.
 //
-// Both use a 256-thread workgroup (four waves) over a BM x BN output tile.  K
+// Both use a workgroup of four waves (eight for KO's wide tile) over a BM x BN
+// output tile.  K
 // streams through double-buffered LDS tiles of BK columns; global loads run D
 // k-tiles ahead in registers and are converted (gating) only when they are
 // written to LDS, so their latency overlaps D tiles of MFMA work.  Every
@@ -50,7 +51,6 @@ namespace {
 constexpr int kThreads = 256;
 constexpr int kGroupRows = 8;    // GM: row tiles per launch group
 constexpr int kEpiRows = 64;     // output rows staged in LDS per epilogue pass
-constexpr int kCStride = 128 + 4;
 
 // BM x BN output tile, BK-wide k-tiles, WM x WN waves, register prefetch D
 // k-tiles ahead, AS parts (1, or hi and lo) of the A operand; SW selects the
@@ -61,8 +61,10 @@ struct TileCfg {
   static constexpr int BM = BM_, BN = BN_, BK = BK_, WM = WM_, WN = WN_, D = D_, AS = AS_, SW = SW_;
   static constexpr int WTM = BM / WM, WTN = BN / WN;   // wave tile
   static constexpr int IB = WTM / 16, JB = WTN / 16;   // 16 x 16 blocks per wave
-  static_assert(WM * WN * 64 == kThreads, "four waves");
-  static_assert(BN <= 128 && BM % kEpiRows == 0 && BK % 32 == 0, "tile shape");
+  static constexpr int NT = WM * WN * 64;              // threads per workgroup
+  static constexpr int CSTR = BN + 4;                  // row stride of the fp32 epilogue tile
+  static_assert(NT == 256 || NT == 512, "four or eight waves");
+  static_assert(BN <= 256 && BM % kEpiRows == 0 && BK % 32 == 0, "tile shape");
   static_assert(D >= 1 && D <= 4, "prefetch depth");
   static_assert(AS == 1 || AS == 2, "operand parts");
 };
@@ -75,9 +77,14 @@ template <> struct ProjCfg<float> : TileCfg<64, 128, 32, 2, 2, 1, 1> {};
 template <typename T> struct OutCfg;
 // KO's K is the gate width (a multiple of 64): k-tiles of 64 halve its barriers
 // (53 against 57 us at T = 8192, F = 2048, d = 512 with k-tiles of 32 and four
-// tiles of prefetch)
-template <> struct OutCfg<bf16> : TileCfg<64, 128, 64, 2, 2, 2, 2> {};
+// tiles of prefetch).  In bf16 the A operand costs more to form than to
+// multiply (gbar * v, then its two parts), and every column tile of a row
+// block forms it again: where 256 divides d the tile is 64 x 256 over eight
+// waves (two per SIMD), which forms it half as often and re-reads the rows
+// half as often (41 against 46 us at that shape); otherwise 64 x 128 over four.
+template <> struct OutCfg<bf16> : TileCfg<64, 256, 64, 2, 4, 2, 2> {};
 template <> struct OutCfg<float> : TileCfg<64, 128, 32, 2, 2, 1, 1> {};
+struct OutCfgNarrow : TileCfg<64, 128, 64, 2, 2, 2, 2> {};
 
 template <typename T> constexpr int piece_elems() { return 16 / (int)sizeof(T); }
 
@@ -116,12 +123,12 @@ __device__ __forceinline__ int piece_offset(int row, int kp) {
 template <class CF, typename T> constexpr size_t ops_bytes() {
   return 2 * (size_t)tile_chunks<CF, T>(CF::AS * CF::BM + CF::BN) * 1024;
 }
-constexpr size_t kEpiBytes = (size_t)kEpiRows * kCStride * sizeof(float);
+template <class CF> constexpr size_t epi_bytes() { return (size_t)kEpiRows * CF::CSTR * sizeof(float); }
 // Operand buffers (reused for the epilogue tile), then BM row scales, then
 // the RoPE frequencies of one head (at most 64 pairs, float64).
 constexpr int kMaxPairs = 64;
 template <class CF, typename T> constexpr size_t main_bytes() {
-  return (ops_bytes<CF, T>() > kEpiBytes ? ops_bytes<CF, T>() : kEpiBytes) +
+  return (ops_bytes<CF, T>() > epi_bytes<CF>() ? ops_bytes<CF, T>() : epi_bytes<CF>()) +
          (size_t)CF::BM * sizeof(float) + kMaxPairs * sizeof(double);
 }
 
@@ -213,7 +220,7 @@ template <class CF, typename T> struct PiecePos {
 };
 template <class CF, typename T>
 __device__ __forceinline__ PiecePos<CF, T> piece_pos(int tid, int p) {
-  constexpr int PR = CF::BK / (16 / (int)sizeof(T)), RPP = kThreads / PR;
+  constexpr int PR = CF::BK / (16 / (int)sizeof(T)), RPP = CF::NT / PR;
   return {tid / PR + p * RPP, tid % PR};
 }
 
@@ -228,7 +235,8 @@ template <class CF, typename T, class SA, class SB>
 __device__ __forceinline__ void gemm_mainloop(f32x4 (&acc)[CF::IB][CF::JB], T* lds, int nk, SA& sa,
                                               SB& sb) {
   constexpr int PE = piece_elems<T>(), D = CF::D;
-  constexpr int PA = tile_chunks<CF, T>(CF::BM) / 4, PB = tile_chunks<CF, T>(CF::BN) / 4;
+  constexpr int PA = tile_chunks<CF, T>(CF::BM) * 64 / CF::NT, PB = tile_chunks<CF, T>(CF::BN) * 64 / CF::NT;
+  static_assert(PA >= 1 && PB >= 1, "every thread loads a piece of each tile");
   constexpr int TA = tile_chunks<CF, T>(CF::AS * CF::BM) * 64 * PE;   // elements
   constexpr int TB = tile_chunks<CF, T>(CF::BN) * 64 * PE;
   constexpr int PART = tile_chunks<CF, T>(CF::BM) * 64 * PE;          // A part stride
@@ -370,7 +378,7 @@ template <typename T, int P, int AS> struct GatedSource {
 
 // Write the accumulator blocks that fall into epilogue pass `pass` (tile rows
 // [64 pass, 64 pass + 64)), times the row scale rs[row] (or 1), to the fp32
-// LDS tile Cs[64][kCStride].
+// LDS tile Cs[64][CF::CSTR].
 template <class CF>
 __device__ __forceinline__ void acc_to_lds(const f32x4 (&acc)[CF::IB][CF::JB], float* Cs,
                                            const float* rs, int pass) {
@@ -387,7 +395,7 @@ __device__ __forceinline__ void acc_to_lds(const f32x4 (&acc)[CF::IB][CF::JB], f
       for (int r = 0; r < 4; ++r) {
         const int row = r0 + grp * 4 + r;
         const float s = rs ? rs[row] : 1.0f;
-        Cs[(row - pass * kEpiRows) * kCStride + wc * CF::WTN + j * 16 + col] = acc[i][j][r] * s;
+        Cs[(row - pass * kEpiRows) * CF::CSTR + wc * CF::WTN + j * 16 + col] = acc[i][j][r] * s;
       }
   }
 }
@@ -580,7 +588,7 @@ void proj_kernel(ProjArgs args) {
         Frag<T> out;
 #pragma unroll
         for (int s = 0; s < 8; ++s) {
-          const float a = Cs[(rb * 32 + perm_slot(grp, s)) * kCStride + c];
+          const float a = Cs[(rb * 32 + perm_slot(grp, s)) * CF::CSTR + c];
           out[s] = cvt<T>(a * __builtin_amdgcn_rcpf(1.0f + __expf(-a)));
         }
         store_frag<T>(gp + packed_offset(mp / 32 + rb, grp, pad_col(n, args.Fh, args.Fhp), args.Fp), out);
@@ -597,7 +605,7 @@ void proj_kernel(ProjArgs args) {
         const int n = n0 + c;
         if (n < F || n >= 2 * F) continue;
         *reinterpret_cast<f32x4*>(v + (mp + row) * F + (n - F)) =
-            *reinterpret_cast<const f32x4*>(&Cs[row * kCStride + c]);
+            *reinterpret_cast<const f32x4*>(&Cs[row * CF::CSTR + c]);
       }
     }
     // queries and keys: RoPE on interleaved pairs, then unit length per head.
@@ -616,7 +624,7 @@ void proj_kernel(ProjArgs args) {
         float u[32];
 #pragma unroll
         for (int e4 = 0; e4 < 8; ++e4) {
-          const f32x4 t4 = *reinterpret_cast<const f32x4*>(&Cs[row * kCStride + hcol + e4 * 4]);
+          const f32x4 t4 = *reinterpret_cast<const f32x4*>(&Cs[row * CF::CSTR + hcol + e4 * 4]);
 #pragma unroll
           for (int r = 0; r < 4; ++r) u[e4 * 4 + r] = t4[r];
         }
@@ -667,7 +675,7 @@ void proj_kernel(ProjArgs args) {
           } else {
 #pragma unroll
             for (int e4 = 0; e4 < 8; ++e4)
-              *reinterpret_cast<f32x4*>(&Cs[row * kCStride + hcol + e4 * 4]) =
+              *reinterpret_cast<f32x4*>(&Cs[row * CF::CSTR + hcol + e4 * 4]) =
                   f32x4{ph[e4 * 4], ph[e4 * 4 + 1], ph[e4 * 4 + 2], ph[e4 * 4 + 3]};
           }
         }
@@ -684,7 +692,7 @@ void proj_kernel(ProjArgs args) {
             Frag<T> out;
 #pragma unroll
             for (int s2 = 0; s2 < 8; ++s2)
-              out[s2] = cvt<T>(Cs[(rb * 32 + perm_slot(grp, s2)) * kCStride + c2]);
+              out[s2] = cvt<T>(Cs[(rb * 32 + perm_slot(grp, s2)) * CF::CSTR + c2]);
             store_frag<T>(fk + packed_offset(mp / 32 + rb, grp, n0 + c2 - 2 * F - HD, HD), out);
           }
         }
@@ -696,10 +704,9 @@ void proj_kernel(ProjArgs args) {
 // ---------------------------------------------------------------------------
 // KO: out = x + (gbar * v) W_o^T.  1-D grid over (M_pad / BM) x (d / BN) tiles.
 // ---------------------------------------------------------------------------
-template <typename T, typename IO>
-__global__ __launch_bounds__(kThreads) void out_kernel(OutArgs args) {
-  using CF = OutCfg<T>;
-  constexpr int PA = tile_chunks<CF, T>(CF::BM) / 4, PB = tile_chunks<CF, T>(CF::BN) / 4;
+template <typename T, typename IO, class CF>
+__global__ __launch_bounds__(CF::NT) void out_kernel(OutArgs args) {
+  constexpr int PA = tile_chunks<CF, T>(CF::BM) * 64 / CF::NT, PB = tile_chunks<CF, T>(CF::BN) * 64 / CF::NT;
   extern __shared__ __align__(16) unsigned char smem_raw[];
   T* lds = reinterpret_cast<T*>(smem_raw);
   const int d = args.d, F = args.F, T_len = args.T, Tp = args.Tp;
@@ -742,7 +749,7 @@ __global__ __launch_bounds__(kThreads) void out_kernel(OutArgs args) {
     if (pass) __syncthreads();   // the previous pass is done with Cs
     acc_to_lds<CF>(acc, Cs, nullptr, pass);
     __syncthreads();
-    for (int it = tid; it < kEpiRows * P8; it += kThreads) {
+    for (int it = tid; it < kEpiRows * P8; it += CF::NT) {
       const int row = it / P8, c = (it % P8) * 8;
       const int t = t0 + pass * kEpiRows + row;
       if (t >= T_len) continue;
@@ -750,7 +757,7 @@ __global__ __launch_bounds__(kThreads) void out_kernel(OutArgs args) {
       float o[8];
       load_io<IO, 8>(x + off, o);
 #pragma unroll
-      for (int s = 0; s < 8; ++s) o[s] += Cs[row * kCStride + c + s];
+      for (int s = 0; s < 8; ++s) o[s] += Cs[row * CF::CSTR + c + s];
       store_io<IO, 8>(out + off, o);
     }
   }
@@ -774,13 +781,20 @@ hipError_t launch_proj_t(const ProjArgs& a, hipStream_t s) {
   return hipGetLastError();
 }
 
-template <typename T, typename IO>
-hipError_t launch_out_t(const OutArgs& a, hipStream_t s) {
-  using CF = OutCfg<T>;
+template <typename T, typename IO, class CF>
+hipError_t launch_out_cf(const OutArgs& a, hipStream_t s) {
+  if (a.d % CF::BN != 0) return hipErrorInvalidValue;
   const int64_t tiles = ((int64_t)a.B * a.Tp / CF::BM) * (a.d / CF::BN);
   const size_t lds = main_bytes<CF, T>();
-  hipLaunchKernelGGL((out_kernel<T, IO>), dim3((unsigned)tiles), dim3(kThreads), lds, s, a);
+  hipLaunchKernelGGL((out_kernel<T, IO, CF>), dim3((unsigned)tiles), dim3(CF::NT), lds, s, a);
   return hipGetLastError();
+}
+template <typename T, typename IO>
+hipError_t launch_out_t(const OutArgs& a, hipStream_t s) {
+  if constexpr (std::is_same<T, bf16>::value) {
+    if (a.d % OutCfg<T>::BN != 0) return launch_out_cf<T, IO, OutCfgNarrow>(a, s);
+  }
+  return launch_out_cf<T, IO, OutCfg<T>>(a, s);
 }
 
 // Pad columns of the head-padded packed gates: one 16-byte piece (8 rows of
@@ -1259,10 +1273,12 @@ hipError_t gemm_kernels_init() {
   TANGO_RAISE((proj_kernel<bf16, float>), (main_bytes<ProjCfg<bf16>, bf16>()))
   TANGO_RAISE((proj_kernel<float, bf16>), (main_bytes<ProjCfg<float>, float>()))
   TANGO_RAISE((proj_kernel<float, float>), (main_bytes<ProjCfg<float>, float>()))
-  TANGO_RAISE((out_kernel<bf16, bf16>), (main_bytes<OutCfg<bf16>, bf16>()))
-  TANGO_RAISE((out_kernel<bf16, float>), (main_bytes<OutCfg<bf16>, bf16>()))
-  TANGO_RAISE((out_kernel<float, bf16>), (main_bytes<OutCfg<float>, float>()))
-  TANGO_RAISE((out_kernel<float, float>), (main_bytes<OutCfg<float>, float>()))
+  TANGO_RAISE((out_kernel<bf16, bf16, OutCfg<bf16>>), (main_bytes<OutCfg<bf16>, bf16>()))
+  TANGO_RAISE((out_kernel<bf16, float, OutCfg<bf16>>), (main_bytes<OutCfg<bf16>, bf16>()))
+  TANGO_RAISE((out_kernel<bf16, bf16, OutCfgNarrow>), (main_bytes<OutCfgNarrow, bf16>()))
+  TANGO_RAISE((out_kernel<bf16, float, OutCfgNarrow>), (main_bytes<OutCfgNarrow, bf16>()))
+  TANGO_RAISE((out_kernel<float, bf16, OutCfg<float>>), (main_bytes<OutCfg<float>, float>()))
+  TANGO_RAISE((out_kernel<float, float, OutCfg<float>>), (main_bytes<OutCfg<float>, float>()))
 #undef TANGO_RAISE
   return hipSuccess;
 }

@@ -34,6 +34,9 @@
  *    stream) and never synchronise the host.  The library allocates no memory
  *    on any call and keeps no per-call state; scratch space is the caller's
  *    `workspace`, whose minimum size the *_workspace_size functions return.
+ *    A call only launches kernels on `hip_stream` (no memset, copy or host
+ *    wait; the first call on a device also sets kernel attributes), so after
+ *    one call on the device it can be captured into a HIP graph and replayed.
  *  - A workspace must not be shared by calls that can run concurrently.
  *  - Inputs are never modified.  `out` may equal `x` (in place); any other
  *    overlap between `out`, `workspace` and the inputs is TANGO_ERR_ALIAS.

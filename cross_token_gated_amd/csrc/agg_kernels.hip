@@ -273,7 +273,7 @@ __global__ __launch_bounds__(kAggThreads) void agg_kernel(AggArgs a, int nfc, in
     // WANGO: phi(sqrt(tau) q) of the same fragment, for the older sources of
     // the chunk next to the window
     Frag<T> fqf[KS];
-    if (MODE == 1) {
+    if (MODE != 0) {
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks)
 #pragma unroll
@@ -295,7 +295,7 @@ __global__ __launch_bounds__(kAggThreads) void agg_kernel(AggArgs a, int nfc, in
     for (int e = 0; e < 8; ++e) ones[e] = cvt<T>(1.0f);
     const int i_me = i0 + wib * 16 + li;     // this lane's destination in S^T
     // older sources of destination i read pairwise here: C floor((i-W)/C) <= j <= i-W
-    const int jphi_lo = (MODE == 1 && i_me >= a.window) ? (i_me - a.window) / a.chunk * a.chunk : 0;
+    const int jphi_lo = (MODE != 0 && i_me >= a.window) ? (i_me - a.window) / a.chunk * a.chunk : 0;
 
     // weights of source step jb (key block in ks[buf]) into ps[buf].  The
     // S^T accumulator starts at -1, so it holds s - 1 and the weight is
@@ -305,7 +305,7 @@ __global__ __launch_bounds__(kAggThreads) void agg_kernel(AggArgs a, int nfc, in
     auto weights = [&](int jb, int buf) {
       const int j0 = jb * BC;
       // WANGO: does this step hold older sources of some row of the tile?
-      const bool phi_step = MODE == 1 && i0 + BR - 1 >= a.window && j0 <= i0 + BR - 1 - a.window;
+      const bool phi_step = MODE != 0 && i0 + BR - 1 >= a.window && j0 <= i0 + BR - 1 - a.window;
       const bool unmasked = MODE == 0 && j0 + (wjb + JBW) * 16 - 1 <= i0 + wib * 16;   // wave-uniform
       Quad<T> pq_even;
 #pragma unroll
@@ -499,6 +499,34 @@ __global__ __launch_bounds__(kAggThreads) void agg_kernel(AggArgs a, int nfc, in
               const int64_t nblk = ((mseq + i0) / 16 + ib) * (F / 16) + (col0 / 16 + in_head(fb));
               e.nold[fb] = *reinterpret_cast<const f32x4*>(a.n_old + (nblk * 64 + lane) * 4);
             }
+          } else if constexpr (MODE == 2) {
+            // the read-out of the state of this block's destination chunk,
+            // n_old^T = S^T phi_Q^T and z_old likewise: the products the
+            // scan's read-out would make, on the same bf16 parts
+            constexpr int KE = DH / 32;
+            const int dchunk = (i0 + ib * 16) / a.chunk;
+            f32x4 nz = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int fb = 0; fb < NFB; ++fb) e.nold[fb] = f32x4{0.f, 0.f, 0.f, 0.f};
+            if (dchunk >= a.window / a.chunk) {   // block-uniform; earlier chunks have no state
+              const T* st = static_cast<const T*>(a.states);
+              const T* zt = static_cast<const T*>(a.zstates);
+              const T* fq = static_cast<const T*>(a.fq);
+              const int64_t dbase = (b * a.H + h) * (int64_t)(Tp / a.chunk) + dchunk;
+              Frag<T> qb[KE];
+#pragma unroll
+              for (int ke = 0; ke < KE; ++ke) qb[ke] = load_frag<T>(fq + (mseq + i) * HD + h * DH + ke * 32 + lg * 8);
+#pragma unroll
+              for (int fb = 0; fb < NFB; ++fb)
+#pragma unroll
+                for (int ke = 0; ke < KE; ++ke)
+                  mma(e.nold[fb],
+                      load_frag<T>(st + (((dbase * (Fh / 16) + f_base / 16 + in_head(fb)) * KE + ke) * 64 + lane) * 8),
+                      qb[ke]);
+#pragma unroll
+              for (int ke = 0; ke < KE; ++ke) mma(nz, load_frag<T>(zt + ((dbase * KE + ke) * 64 + lane) * 8), qb[ke]);
+            }
+            e.zold = nz[0];
           }
         };
         auto store_block = [&](int ib, const Extra& e) {
@@ -508,7 +536,7 @@ __global__ __launch_bounds__(kAggThreads) void agg_kernel(AggArgs a, int nfc, in
           float dsum = den[ib];
           if constexpr (C) dsum += e.pden;
           dsum += null_w * (float)(i + 1);
-          if constexpr (MODE == 1) dsum += escale * e.zold;
+          if constexpr (MODE != 0) dsum += escale * e.zold;
           // Options: the denominator for a later backward pass (one writer per
           // row: column chunk 0, wave 0); the numerator alone; rows stored in
           // reverse order (rows past the end are not stored then)
@@ -523,7 +551,7 @@ __global__ __launch_bounds__(kAggThreads) void agg_kernel(AggArgs a, int nfc, in
 #pragma unroll
               for (int r = 0; r < 4; ++r) num[r] += e.part[fb][r];
             }
-            if constexpr (MODE == 1) num += escale * e.nold[fb];
+            if constexpr (MODE != 0) num += escale * e.nold[fb];
             // gbar is not head-padded: columns past the head's width are pad
             const int c = f_base + fb * 16 + lg * 4;
             if (c < a.Fho && ostore)
@@ -667,6 +695,9 @@ hipError_t launch_wango_band(const AggArgs& a, bool bf, hipStream_t s) {
   const int nfc = (int)ceil_div(Fh, fs);
   const int rtiles = a.Tp / br;
   const int64_t items = (int64_t)a.B * a.H * nfc * rtiles;
+  if (a.states)   // the read-out of the chunk states in the epilogue
+    return bf ? launch_agg_t<bf16, 2>(a, fs / kWaves, nfc, rtiles, items, br, s)
+              : launch_agg_t<float, 2>(a, fs / kWaves, nfc, rtiles, items, br, s);
   return bf ? launch_agg_t<bf16, 1>(a, fs / kWaves, nfc, rtiles, items, br, s)
             : launch_agg_t<float, 1>(a, fs / kWaves, nfc, rtiles, items, br, s);
 }

@@ -57,6 +57,11 @@ struct AggArgs {
   const float* null_bias;  // [H] or null
   const float* n_old;      // WANGO: blocked [B*Tp/16][F/16][64][4]
   const float* z_old;      // WANGO: [B*Tp, H]
+  // WANGO with the read-out in the band (instead of n_old, z_old): the chunk
+  // states and the query features they are read out with (see ScanArgs)
+  const void* states;
+  const void* zstates;
+  const void* fq;          // phi(sqrt(tau) q), permuted feature order [B*Tp, HD]
   float* part;             // TANGO split mode: partial numerators
   float* part_den;         // TANGO split mode: partial denominators
   int* counters;           // TANGO split mode: one per split tile
@@ -77,6 +82,12 @@ struct ScanArgs {
   const void* gp;
   float* n_old;            // blocked [B*Tp/16][F/16][64][4]
   float* z_old;            // [B*Tp, H]
+  // Instead of n_old, z_old (when non-null): the state of every destination
+  // chunk d >= window / chunk in the A-operand layout of the read-out, bf16
+  // (or float32) fragments [B][H][Tp/chunk][Fh/16][dh/32][64 lanes], and the
+  // z state likewise [B][H][Tp/chunk][dh/32][64 lanes]
+  void* states;
+  void* zstates;
   float* seg_state;        // segment sums: [B][H][column slice][nseg] blocks of dh x slice, accumulator order
   float* seg_z;            // [B][H][nseg][dh]
   int B, T, Tp, F, H, dh, window, chunk;

@@ -236,8 +236,10 @@ void scan_partial_kernel(ScanArgs a) {
 }
 
 // Pass 2: the segment's starting state (sum of the sums of the segments before
-// it), then the replay of its sources with the read-outs of n_old, z_old.
-template <typename T, int DH, int CH, int NFB>
+// it), then the replay of its sources with, at every chunk boundary, either
+// the read-outs of n_old, z_old (RO) or the state itself in the read-out's
+// A-operand layout, for the band kernel to read out (no query features then).
+template <typename T, int DH, int CH, int NFB, bool RO>
 __global__ __launch_bounds__(kScanThreads) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void scan_main_kernel(ScanArgs a) {
   constexpr int FSC = kScanWaves * 16 * NFB, NIB = CH / 16, KE = DH / 32;
@@ -245,7 +247,7 @@ void scan_main_kernel(ScanArgs a) {
   constexpr int QPT = QF / kScanThreads;            // ... per thread
   constexpr int NQB = sizeof(T) == 2 ? 2 : 1;       // LDS query buffers
   static_assert(QF % kScanThreads == 0, "query fragments per chunk");
-  __shared__ Frag<T> qs[NQB][QF];
+  __shared__ Frag<T> qs[RO ? NQB : 1][RO ? QF : 1];
   const int Fh = a.F / a.H, HD = a.H * DH, F = a.F;
   const int nslices = Fh / FSC;
   const ScanWg w = scan_wg(blockIdx.x, nslices, a.H, a.nseg);
@@ -274,7 +276,7 @@ void scan_main_kernel(ScanArgs a) {
       qn[q] = load_frag<T>(fq + (drow + ib * 16 + (fl & 15)) * HD + w.h * DH + ke * 32 + (fl >> 4) * 8);
     }
   };
-  load_q(c0);   // first: the ring loads issued after it keep later waits on it precise
+  if constexpr (RO) load_q(c0);   // first: the ring loads issued after it keep later waits on it precise
 
   // first source units in flight
   __shared__ FeatRing<T, DH, NS> ring;
@@ -346,8 +348,8 @@ void scan_main_kernel(ScanArgs a) {
     }
   }
 
-  // destinations with no older chunk: zeros
-  if (w.seg == 0) {
+  // destinations with no older chunk: zeros (the band reads no state for them)
+  if (RO && w.seg == 0) {
     for (int dchunk = 0; dchunk < min(lag, nchunks); ++dchunk) {
 #pragma unroll
       for (int ib = 0; ib < NIB; ++ib)
@@ -362,46 +364,69 @@ void scan_main_kernel(ScanArgs a) {
     }
   }
 
-  // chunk c: stage its query features, read S_{<cCH} out for destination chunk
-  // c + lag (n_old^T = S^T phi_Q^T), then fetch the next chunk's features
+  // chunk c: the state S_{<cCH} of destination chunk c + lag.  RO: stage the
+  // chunk's query features, read the state out (n_old^T = S^T phi_Q^T), then
+  // fetch the next chunk's features; otherwise store the state's A-operand
+  // fragments (the same bf16 parts the read-out multiplies)
   auto boundary = [&](int c) {
-    Frag<T>* buf = qs[NQB == 2 ? (c & 1) : 0];
-    if constexpr (NQB == 1) lds_sync();   // the previous read-out is done with the buffer
+    if constexpr (!RO) {
+      const int dchunk = c + lag;
+      if (dchunk < nchunks) {
+        T* st = static_cast<T*>(a.states);
+        const int64_t dbase = (w.b * a.H + w.h) * (int64_t)nchunks + dchunk;
 #pragma unroll
-    for (int q = 0; q < QPT; ++q) buf[threadIdx.x + q * kScanThreads] = qn[q];
-    lds_sync();
-    const int dchunk = c + lag;
-    if (dchunk < nchunks) {
-      Frag<T> sa[KE][NFB], za[KE];
+        for (int fb = 0; fb < NFB; ++fb)
 #pragma unroll
-      for (int ke = 0; ke < KE; ++ke) {
-#pragma unroll
-        for (int fb = 0; fb < NFB; ++fb) sa[ke][fb] = join(cvt_quad<T>(S[2 * ke][fb]), cvt_quad<T>(S[2 * ke + 1][fb]));
-        za[ke] = join(cvt_quad<T>(Sz[2 * ke]), cvt_quad<T>(Sz[2 * ke + 1]));
-      }
-      const int64_t drow = mseq + (int64_t)dchunk * CH;
-#pragma unroll
-      for (int ib = 0; ib < NIB; ++ib) {
-        Frag<T> qb[KE];
-#pragma unroll
-        for (int ke = 0; ke < KE; ++ke) qb[ke] = buf[(ib * KE + ke) * 64 + lane];
-#pragma unroll
-        for (int fb = 0; fb < NFB; ++fb) {
-          f32x4 n = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-          for (int ke = 0; ke < KE; ++ke) mma(n, sa[ke][fb], qb[ke]);
-          const int64_t nblk = (drow / 16 + ib) * (F / 16) + col / 16 + fb;
-          *reinterpret_cast<f32x4*>(a.n_old + (nblk * 64 + lane) * 4) = n;
-        }
+          for (int ke = 0; ke < KE; ++ke)
+            store_frag<T>(st + (((dbase * (Fh / 16) + cf / 16 + fb) * KE + ke) * 64 + lane) * 8,
+                          join(cvt_quad<T>(S[2 * ke][fb]), cvt_quad<T>(S[2 * ke + 1][fb])));
         if (with_z) {
-          f32x4 nz = {0.f, 0.f, 0.f, 0.f};
+          T* zt = static_cast<T*>(a.zstates);
 #pragma unroll
-          for (int ke = 0; ke < KE; ++ke) mma(nz, za[ke], qb[ke]);
-          if (lg == 0) a.z_old[(drow + ib * 16 + li) * a.H + w.h] = nz[0];
+          for (int ke = 0; ke < KE; ++ke)
+            store_frag<T>(zt + ((dbase * KE + ke) * 64 + lane) * 8,
+                          join(cvt_quad<T>(Sz[2 * ke]), cvt_quad<T>(Sz[2 * ke + 1])));
         }
       }
+    } else {
+      Frag<T>* buf = qs[NQB == 2 ? (c & 1) : 0];
+      if constexpr (NQB == 1) lds_sync();   // the previous read-out is done with the buffer
+#pragma unroll
+      for (int q = 0; q < QPT; ++q) buf[threadIdx.x + q * kScanThreads] = qn[q];
+      lds_sync();
+      const int dchunk = c + lag;
+      if (dchunk < nchunks) {
+        Frag<T> sa[KE][NFB], za[KE];
+#pragma unroll
+        for (int ke = 0; ke < KE; ++ke) {
+#pragma unroll
+          for (int fb = 0; fb < NFB; ++fb) sa[ke][fb] = join(cvt_quad<T>(S[2 * ke][fb]), cvt_quad<T>(S[2 * ke + 1][fb]));
+          za[ke] = join(cvt_quad<T>(Sz[2 * ke]), cvt_quad<T>(Sz[2 * ke + 1]));
+        }
+        const int64_t drow = mseq + (int64_t)dchunk * CH;
+#pragma unroll
+        for (int ib = 0; ib < NIB; ++ib) {
+          Frag<T> qb[KE];
+#pragma unroll
+          for (int ke = 0; ke < KE; ++ke) qb[ke] = buf[(ib * KE + ke) * 64 + lane];
+#pragma unroll
+          for (int fb = 0; fb < NFB; ++fb) {
+            f32x4 n = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int ke = 0; ke < KE; ++ke) mma(n, sa[ke][fb], qb[ke]);
+            const int64_t nblk = (drow / 16 + ib) * (F / 16) + col / 16 + fb;
+            *reinterpret_cast<f32x4*>(a.n_old + (nblk * 64 + lane) * 4) = n;
+          }
+          if (with_z) {
+            f32x4 nz = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int ke = 0; ke < KE; ++ke) mma(nz, za[ke], qb[ke]);
+            if (lg == 0) a.z_old[(drow + ib * 16 + li) * a.H + w.h] = nz[0];
+          }
+        }
+      }
+      if (c + 1 < c1) load_q(c + 1);   // after the stores: waits on it stay precise
     }
-    if (c + 1 < c1) load_q(c + 1);   // after the stores: waits on it stay precise
   };
   stash_unit<T, DH, NFB, NS>(ring, 0, R[0], wave, lane);
   lds_sync();
@@ -420,8 +445,12 @@ hipError_t launch_scan_t(const ScanArgs& a, hipStream_t s) {
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
-  hipLaunchKernelGGL((scan_main_kernel<T, DH, CH, NFB>), dim3((unsigned)(groups * a.nseg)),
-                     dim3(kScanThreads), 0, s, a);
+  if (a.states)
+    hipLaunchKernelGGL((scan_main_kernel<T, DH, CH, NFB, false>), dim3((unsigned)(groups * a.nseg)),
+                       dim3(kScanThreads), 0, s, a);
+  else
+    hipLaunchKernelGGL((scan_main_kernel<T, DH, CH, NFB, true>), dim3((unsigned)(groups * a.nseg)),
+                       dim3(kScanThreads), 0, s, a);
   return hipGetLastError();
 }
 

@@ -163,11 +163,19 @@ struct Layout {
   size_t xs, rinv;                      // projection input parts, RMSNorm scales
   size_t fq, fk;                        // WANGO features
   size_t part, part_den, counters;      // TANGO split scratch
-  size_t n_old, z_old, seg_state, seg_z;
+  size_t states, zstates, seg_state, seg_z;   // WANGO chunk states, segment sums
   size_t total;
   AggPlan agg;
   ScanPlan scan;
 };
+
+// Bytes of the WANGO chunk states the scan leaves for the band's read-out
+// (ScanArgs::states; with z: ScanArgs::zstates).
+size_t wango_states_bytes(const tango_shape_t* s, int32_t chunk, bool z) {
+  const int64_t nch = pad_rows(s->seq_len) / chunk;
+  const int64_t per = z ? 1 : gate_pad(s, true) / s->n_heads / 16;
+  return (size_t)s->batch * s->n_heads * nch * per * (s->head_dim / 32) * 64 * 8 * elem_size(s->dtype);
+}
 
 Layout make_layout(const tango_shape_t* s, bool wango, int32_t window, int32_t chunk) {
   Layout L{};
@@ -200,8 +208,8 @@ Layout make_layout(const tango_shape_t* s, bool wango, int32_t window, int32_t c
     L.scan = wango_scan_plan(s->batch, (int)pad_rows(s->seq_len), (int)F, s->n_heads, chunk);
     L.fq = take(M * HD * es);
     L.fk = take(M * HD * es);
-    L.n_old = take(M * F * sizeof(float));
-    L.z_old = take(M * s->n_heads * sizeof(float));
+    L.states = take(wango_states_bytes(s, chunk, false));
+    L.zstates = take(wango_states_bytes(s, chunk, true));
     const int64_t bh = (int64_t)s->batch * s->n_heads;
     L.seg_state = take((size_t)bh * L.scan.nseg * s->head_dim * (F / s->n_heads) * sizeof(float));
     L.seg_z = take((size_t)bh * L.scan.nseg * s->head_dim * sizeof(float));
@@ -464,15 +472,17 @@ int block_common(const tango_shape_t* s, const tango_weights_t* w, bool wango, i
     e = launch_tango_agg(aa, L.agg, bf, true, st);
     if (e != hipSuccess) return hip_fail(e, "aggregation kernel");
   } else {
-    float* n_old = reinterpret_cast<float*>(base + L.n_old);
-    float* z_old = reinterpret_cast<float*>(base + L.z_old);
-    ScanArgs sa = scan_args(s, window, chunk, base + L.fq, base + L.fk, gp, n_old, z_old,
+    // the scan leaves the chunk states, the band reads them out
+    ScanArgs sa = scan_args(s, window, chunk, base + L.fq, base + L.fk, gp, nullptr, nullptr,
                             reinterpret_cast<float*>(base + L.seg_state),
                             reinterpret_cast<float*>(base + L.seg_z));
+    sa.states = base + L.states;
+    sa.zstates = base + L.zstates;
     e = launch_wango_scan(sa, L.scan, bf, st);
     if (e != hipSuccess) return hip_fail(e, "scan kernels");
-    aa.n_old = n_old;
-    aa.z_old = z_old;
+    aa.states = base + L.states;
+    aa.zstates = base + L.zstates;
+    aa.fq = base + L.fq;
     aa.window = window;
     aa.chunk = chunk;
     e = launch_wango_band(aa, bf, st);
@@ -831,7 +841,7 @@ int check_wango_bwd(const tango_shape_t* s, int32_t window, int32_t chunk) {
 
 // Scratch of the WANGO forward-train call: features, then the scan's.
 struct WFwdLayout {
-  size_t fq, fk, tmp, n_old, z_old, seg_state, seg_z, total;
+  size_t fq, fk, tmp, states, zstates, seg_state, seg_z, total;
   ScanPlan scan;
 };
 WFwdLayout make_wfwd_layout(const tango_shape_t* s, int32_t chunk) {
@@ -848,8 +858,8 @@ WFwdLayout make_wfwd_layout(const tango_shape_t* s, int32_t chunk) {
   L.fq = take((size_t)M * HD * 2);
   L.fk = take((size_t)M * HD * 2);
   L.tmp = take((size_t)M * HD * 2);
-  L.n_old = take((size_t)M * F * sizeof(float));
-  L.z_old = take((size_t)M * s->n_heads * sizeof(float));
+  L.states = take(wango_states_bytes(s, chunk, false));
+  L.zstates = take(wango_states_bytes(s, chunk, true));
   const int64_t bh = (int64_t)s->batch * s->n_heads;
   L.seg_state = take((size_t)bh * L.scan.nseg * s->head_dim * (F / s->n_heads) * sizeof(float));
   L.seg_z = take((size_t)bh * L.scan.nseg * s->head_dim * sizeof(float));
@@ -866,13 +876,14 @@ hipError_t wango_scan_band(const tango_shape_t* s, int32_t window, int32_t chunk
   hipError_t e = hipSuccess;
   if (!features_ready && (e = launch_wango_bwd_features(fa, base + L.fq, base + L.tmp, q, k, base + L.fk, st)) != hipSuccess)
     return e;
-  float* n_old = reinterpret_cast<float*>(base + L.n_old);
-  float* z_old = reinterpret_cast<float*>(base + L.z_old);
-  ScanArgs sa = scan_args(s, window, chunk, base + L.fq, base + L.fk, gp, n_old, z_old,
+  ScanArgs sa = scan_args(s, window, chunk, base + L.fq, base + L.fk, gp, nullptr, nullptr,
                           reinterpret_cast<float*>(base + L.seg_state), reinterpret_cast<float*>(base + L.seg_z));
+  sa.states = base + L.states;
+  sa.zstates = base + L.zstates;
   if ((e = launch_wango_scan(sa, L.scan, true, st)) != hipSuccess) return e;
-  aa.n_old = n_old;
-  aa.z_old = z_old;
+  aa.states = base + L.states;
+  aa.zstates = base + L.zstates;
+  aa.fq = base + L.fq;
   aa.window = window;
   aa.chunk = chunk;
   return launch_wango_band(aa, true, st);

@@ -41,9 +41,13 @@ namespace {
 constexpr int kScanWaves = 4;
 constexpr int kScanThreads = 64 * kScanWaves;
 // Source-unit register sets per wave (ring depth): all but one are in flight.
+// The LDS feature ring has as many slots, and at least three: the slot a unit
+// is stashed into was last read two units earlier, and only with three or more
+// slots does a barrier lie between that read and the write (with two, a wave
+// ahead of the others overwrites features another wave is still multiplying).
 // (Five or six sets for bf16 measured no faster than four; with the features
 // shared through LDS, six or eight in pass 1 and five in pass 2 neither.)
-template <typename T, int DH, bool MAIN> constexpr int ring_sets() { return sizeof(T) == 4 ? 2 : 4; }
+template <typename T, int DH, bool MAIN> constexpr int ring_sets() { return sizeof(T) == 4 ? 3 : 4; }
 // Segment sums loaded per batch while the starting state is summed: about 64
 // registers of loads in flight.
 template <int DH, int NFB> constexpr int prefix_batch() {
@@ -156,7 +160,7 @@ __device__ __forceinline__ int64_t seg_block(int64_t slice_seg, int wave, int eb
 // (and NS LDS slots for the features).  Before unit u is applied, the
 // features of unit u + 1 (loaded NS - 2 units earlier) go to their slot and an
 // LDS-only barrier publishes them; unit u's slot was published one unit ago,
-// and a slot is rewritten NS - 1 barriers after it was last read.  MAIN adds,
+// and a slot is rewritten NS - 2 barriers after it was last read (NS >= 3).  MAIN adds,
 // before the first unit of every chunk, the read-out of the state for the
 // destination chunk that chunk feeds (through `boundary`).  The caller has
 // loaded units u0 .. u0 + NS - 2, stashed unit u0 and synchronised.
@@ -165,6 +169,7 @@ __device__ __forceinline__ void walk_units(f32x4 (&S)[DH / 16][NFB], f32x4 (&Sz)
                                            UnitRegs<T, DH, NFB> (&R)[NS], FeatRing<T, DH, NS>& ring, int u0,
                                            int u1, const T* fk, const T* gp, int64_t mseq, int HD, int hcol,
                                            int64_t col, int F, int li, int lg, int wave, Boundary&& boundary) {
+  static_assert(NS >= 3, "a barrier must separate a slot's last read from its next write");
   const int lane = lg * 16 + li;
   auto load = [&](UnitRegs<T, DH, NFB>& r, int u) {
     load_unit<T, DH, NFB>(r, fk, gp, mseq + (int64_t)min(u, u1 - 1) * unit_len<DH>(), HD, hcol, col, F, li, lg,

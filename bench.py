@@ -263,7 +263,7 @@ def pages_bench(steps: int, warmup: int, dev, stream) -> dict:
         bw = block_weights(w, inp, dev)
         x = dev_tensor(inp.h, w.io, dev)
         ping, pong = torch.empty_like(x), torch.empty_like(x)
-        shape = api.shape_of(x, bw, w.rope_base, w.rms_eps)
+        shape = api.shape_of(x, bw, w.rope_base, w.rms_eps, w.operand_parts)
         n = (api.tango_workspace_size(shape) if w.mode == "tango"
              else api.wango_workspace_size(shape, w.window, w.head_dim, w.chunk))
         ws = api.workspace(n, dev)
@@ -273,11 +273,11 @@ def pages_bench(steps: int, warmup: int, dev, stream) -> dict:
             for r in range(w.repeats):
                 dst = ping if r % 2 == 0 else pong
                 if w.mode == "tango":
-                    api.tango_block_fwd(src, bw, out=dst, ws=ws, rope_base=w.rope_base, rms_eps=w.rms_eps,
+                    api.tango_block_fwd(src, bw, out=dst, ws=ws, rope_base=w.rope_base, rms_eps=w.rms_eps, operand_parts=w.operand_parts,
                                         stream=stream)
                 else:
                     api.wango_block_fwd(src, bw, w.window, w.head_dim, w.chunk, out=dst, ws=ws,
-                                        rope_base=w.rope_base, rms_eps=w.rms_eps, stream=stream)
+                                        rope_base=w.rope_base, rms_eps=w.rms_eps, operand_parts=w.operand_parts, stream=stream)
                 src = dst
 
         for _ in range(warmup):
@@ -326,7 +326,7 @@ def configs_bench(steps: int, warmup: int, dev, stream, timed_batches) -> dict:
         bw = block_weights(w, inp, dev)
         x = dev_tensor(inp.h, w.io, dev)
         ping, pong = torch.empty_like(x), torch.empty_like(x)
-        shape = api.shape_of(x, bw, w.rope_base, w.rms_eps)
+        shape = api.shape_of(x, bw, w.rope_base, w.rms_eps, w.operand_parts)
         n = (api.tango_workspace_size(shape) if w.mode == "tango"
              else api.wango_workspace_size(shape, w.window, w.head_dim, w.chunk))
         ws = api.workspace(n, dev)
@@ -336,11 +336,11 @@ def configs_bench(steps: int, warmup: int, dev, stream, timed_batches) -> dict:
             for r in range(w.repeats):
                 dst = ping if r % 2 == 0 else pong
                 if w.mode == "tango":
-                    api.tango_block_fwd(src, bw, out=dst, ws=ws, rope_base=w.rope_base, rms_eps=w.rms_eps,
+                    api.tango_block_fwd(src, bw, out=dst, ws=ws, rope_base=w.rope_base, rms_eps=w.rms_eps, operand_parts=w.operand_parts,
                                         stream=stream)
                 else:
                     api.wango_block_fwd(src, bw, w.window, w.head_dim, w.chunk, out=dst, ws=ws,
-                                        rope_base=w.rope_base, rms_eps=w.rms_eps, stream=stream)
+                                        rope_base=w.rope_base, rms_eps=w.rms_eps, operand_parts=w.operand_parts, stream=stream)
                 src = dst
 
         for _ in range(warmup):
@@ -461,12 +461,12 @@ def three_set_bench(steps: int, warmup: int, dev, stream, ms_one_set_app: float)
         w = sw.base
         x = dev_tensor(inps[0].h, w.io, dev)
         y = torch.empty_like(x)
-        shapes = [api.shape_of(x, b, w.rope_base, w.rms_eps) for b in sets]
+        shapes = [api.shape_of(x, b, w.rope_base, w.rms_eps, w.operand_parts) for b in sets]
         ws = api.workspace(api.tango_stack_workspace_size(shapes), dev)
 
         def fwd():
             api.tango_stack_fwd(x, sets, sw.schedule, out=y, ws=ws, rope_base=w.rope_base,
-                                rms_eps=w.rms_eps, stream=stream)
+                                rms_eps=w.rms_eps, operand_parts=w.operand_parts, stream=stream)
 
         for _ in range(warmup):
             fwd()
@@ -743,8 +743,8 @@ def main():
     xt = dev_tensor(it.h, wt.io)
     xg = dev_tensor(ig.h, wg.io)
     ping, pong, outg = torch.empty_like(xt), torch.empty_like(xt), torch.empty_like(xg)
-    st = api.shape_of(xt, bt, wt.rope_base, wt.rms_eps)
-    sg = api.shape_of(xg, bg, wg.rope_base, wg.rms_eps)
+    st = api.shape_of(xt, bt, wt.rope_base, wt.rms_eps, wt.operand_parts)
+    sg = api.shape_of(xg, bg, wg.rope_base, wg.rms_eps, wg.operand_parts)
     ws_t = api.workspace(api.tango_workspace_size(st), dev)
     ws_g = api.workspace(api.wango_workspace_size(sg, wg.window, wg.head_dim, wg.chunk), dev)
     stream = torch.cuda.current_stream()
@@ -754,10 +754,10 @@ def main():
         for r in range(wt.repeats):            # x -> ping -> pong -> ping -> pong
             dst = ping if r % 2 == 0 else pong
             api.tango_block_fwd(src, bt, out=dst, ws=ws_t, rope_base=wt.rope_base,
-                                rms_eps=wt.rms_eps, stream=stream)
+                                rms_eps=wt.rms_eps, operand_parts=wt.operand_parts, stream=stream)
             src = dst
         api.wango_block_fwd(xg, bg, wg.window, wg.head_dim, wg.chunk, out=outg, ws=ws_g,
-                            rope_base=wg.rope_base, rms_eps=wg.rms_eps, stream=stream)
+                            rope_base=wg.rope_base, rms_eps=wg.rms_eps, operand_parts=wg.operand_parts, stream=stream)
 
     for _ in range(args.warmup):
         step()
@@ -820,12 +820,13 @@ def main():
         src = xt
         for r in range(wt.repeats):
             dst = ping if r % 2 == 0 else pong
-            api.tango_block_fwd(src, bt, out=dst, ws=ws_t, stream=stream)
+            api.tango_block_fwd(src, bt, out=dst, ws=ws_t, stream=stream, operand_parts=wt.operand_parts)
             src = dst
 
     ms_tango = timed(tango_only, loops)
     ms_wango = timed(lambda: api.wango_block_fwd(xg, bg, wg.window, wg.head_dim, wg.chunk, out=outg,
-                                                 ws=ws_g, stream=stream), loops)
+                                                 ws=ws_g, stream=stream, operand_parts=wg.operand_parts),
+                     loops)
     n_batches = 5
     ms_agg, agg_min, agg_max = timed_batches(
         lambda: api.tango_stage_aggregate(st, bt.theta, None, qh, kh, gp, gbar, ws_t, stream=stream),

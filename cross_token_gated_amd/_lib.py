@@ -41,7 +41,7 @@ class Shape(ctypes.Structure):
                 ("n_heads", ctypes.c_int32), ("head_dim", ctypes.c_int32),
                 ("dtype", ctypes.c_int32), ("io_dtype", ctypes.c_int32),
                 ("rope_base", ctypes.c_float),
-                ("rms_eps", ctypes.c_float)]
+                ("rms_eps", ctypes.c_float), ("operand_parts", ctypes.c_int32)]
 
 
 class Weights(ctypes.Structure):

@@ -117,18 +117,21 @@ def _stream(stream) -> Optional[int]:
 
 def make_shape(B: int, T: int, d: int, F: int, H: int, dh: int, dtype: torch.dtype,
                rope_base: float = 10000.0, rms_eps: float = 1e-6,
-               io_dtype: Optional[torch.dtype] = None) -> Shape:
+               io_dtype: Optional[torch.dtype] = None, operand_parts: int = 1) -> Shape:
     """dtype: weights and intermediate activations; io_dtype: x and out
-    (defaults to dtype)."""
+    (defaults to dtype); operand_parts: 1 or 2 bf16 parts of the GEMMs'
+    activation operand (2 only with bfloat16)."""
     io_dtype = dtype if io_dtype is None else io_dtype
     for t in (dtype, io_dtype):
         if t not in _DTYPES:
             raise TypeError(f"unsupported dtype {t}")
-    return Shape(B, T, d, F, H, dh, _DTYPES[dtype], _DTYPES[io_dtype], rope_base, rms_eps)
+    if operand_parts not in (1, 2) or (operand_parts == 2 and dtype != torch.bfloat16):
+        raise ValueError(f"operand_parts {operand_parts}: need 1, or 2 with bfloat16")
+    return Shape(B, T, d, F, H, dh, _DTYPES[dtype], _DTYPES[io_dtype], rope_base, rms_eps, operand_parts)
 
 
 def shape_of(x: torch.Tensor, w: BlockWeights, rope_base: float = 10000.0,
-             rms_eps: float = 1e-6) -> Shape:
+             rms_eps: float = 1e-6, operand_parts: int = 1) -> Shape:
     """Shape of a call: compute dtype from the weights, I/O dtype from x.
     Checks x ([B, T, d] on a GPU, float32 or bfloat16) and the weights first."""
     check_tensor(x, "x", dtype=tuple(_DTYPES))
@@ -137,7 +140,7 @@ def shape_of(x: torch.Tensor, w: BlockWeights, rope_base: float = 10000.0,
     w.check(x.shape[2], x.device)
     B, T, d = x.shape
     return make_shape(B, T, d, w.w_g.shape[0], w.n_heads, w.head_dim, w.w_g.dtype, rope_base,
-                      rms_eps, io_dtype=x.dtype)
+                      rms_eps, io_dtype=x.dtype, operand_parts=operand_parts)
 
 
 class _Sizes:
@@ -179,9 +182,9 @@ def workspace(nbytes: int, device) -> torch.Tensor:
 
 def tango_block_fwd(x: torch.Tensor, w: BlockWeights, out: Optional[torch.Tensor] = None,
                     ws: Optional[torch.Tensor] = None, rope_base: float = 10000.0,
-                    rms_eps: float = 1e-6, stream=None) -> torch.Tensor:
+                    rms_eps: float = 1e-6, stream=None, operand_parts: int = 1) -> torch.Tensor:
     """One TANGO block: returns out[B, T, d] (out may be x for in place)."""
-    shape = shape_of(x, w, rope_base, rms_eps)
+    shape = shape_of(x, w, rope_base, rms_eps, operand_parts)
     if out is None:
         out = torch.empty_like(x)
     if ws is None:
@@ -202,11 +205,11 @@ def tango_stack_workspace_size(shapes) -> int:
 
 def tango_stack_fwd(x: torch.Tensor, sets, schedule, out: Optional[torch.Tensor] = None,
                     ws: Optional[torch.Tensor] = None, rope_base: float = 10000.0,
-                    rms_eps: float = 1e-6, stream=None) -> torch.Tensor:
+                    rms_eps: float = 1e-6, stream=None, operand_parts: int = 1) -> torch.Tensor:
     """TANGO blocks with several parameter sets: application r uses
     ``sets[schedule[r]]`` (a list of BlockWeights).  Returns out[B, T, d]
     (out may be x for in place)."""
-    shapes = [shape_of(x, w, rope_base, rms_eps) for w in sets]
+    shapes = [shape_of(x, w, rope_base, rms_eps, operand_parts) for w in sets]
     if out is None:
         out = torch.empty_like(x)
     if ws is None:
@@ -223,9 +226,10 @@ def tango_stack_fwd(x: torch.Tensor, sets, schedule, out: Optional[torch.Tensor]
 
 def wango_block_fwd(x: torch.Tensor, w: BlockWeights, window: int, phi_dim: int, chunk: int,
                     out: Optional[torch.Tensor] = None, ws: Optional[torch.Tensor] = None,
-                    rope_base: float = 10000.0, rms_eps: float = 1e-6, stream=None) -> torch.Tensor:
+                    rope_base: float = 10000.0, rms_eps: float = 1e-6, stream=None,
+                    operand_parts: int = 1) -> torch.Tensor:
     """One WANGO block: returns out[B, T, d] (out may be x for in place)."""
-    shape = shape_of(x, w, rope_base, rms_eps)
+    shape = shape_of(x, w, rope_base, rms_eps, operand_parts)
     if out is None:
         out = torch.empty_like(x)
     if ws is None:

@@ -26,12 +26,15 @@
 // each redo the conversion).
 //
 // In bf16 the weights are exact, but the activation operand of both products
-// (h * gain, and gbar * v) is a float32 value.  It is carried as two bf16
-// parts, hi = bf16(e) and lo = bf16(e - hi), each multiplied on MFMA into the
-// same float32 accumulator, so the product sees e to about 2^-16 relative
-// instead of 2^-9: without it the error of a stack of eight shared-weight
-// applications at the first positions of a sequence (whose aggregate is their
-// own gate, so their updates are the largest) exceeds 2e-2 of the output rms.
+// (h * gain, and gbar * v) is a float32 value.  The shape's operand_parts picks
+// how it enters the MFMA: one part, bf16(e), the plain bf16 compute of the
+// pages; or two parts, hi = bf16(e) and lo = bf16(e - hi), each multiplied
+// into the same float32 accumulator, so the product sees e to about 2^-16
+// relative instead of 2^-9 at twice the MFMA work.  Long stacks of shared-weight
+// applications need the second part: at the first positions of a sequence
+// (whose aggregate is their own gate, so their updates are the largest) the
+// operand roundings compound over eight applications past 2e-2 of the output
+// rms.
 //
 // Row tiles never straddle two sequences (the padded length is a multiple of
 // 128), so a workgroup resolves its (batch, position) once.  The 1-D grid is
@@ -69,22 +72,26 @@ struct TileCfg {
   static_assert(AS == 1 || AS == 2, "operand parts");
 };
 
-template <typename T> struct ProjCfg;
-// (the older slot order: with the conflict-free one the kernel needs two more
-// VGPRs and drops from three waves per SIMD to two, 110 against 101 us)
-template <> struct ProjCfg<bf16> : TileCfg<128, 128, 32, 2, 2, 2, 2, 0> {};
-template <> struct ProjCfg<float> : TileCfg<64, 128, 32, 2, 2, 1, 1> {};
-template <typename T> struct OutCfg;
+template <typename T, int AS> struct ProjCfg;
+// (two parts keep the older slot order: with the conflict-free one the kernel
+// needs two more VGPRs and drops from three waves per SIMD to two, 110 against
+// 101 us)
+template <> struct ProjCfg<bf16, 2> : TileCfg<128, 128, 32, 2, 2, 2, 2, 0> {};
+template <> struct ProjCfg<bf16, 1> : TileCfg<128, 128, 32, 2, 2, 2, 1, 1> {};
+template <> struct ProjCfg<float, 1> : TileCfg<64, 128, 32, 2, 2, 1, 1> {};
+template <typename T, int AS> struct OutCfg;
 // KO's K is the gate width (a multiple of 64): k-tiles of 64 halve its barriers
 // (53 against 57 us at T = 8192, F = 2048, d = 512 with k-tiles of 32 and four
 // tiles of prefetch).  In bf16 the A operand costs more to form than to
-// multiply (gbar * v, then its two parts), and every column tile of a row
-// block forms it again: where 256 divides d the tile is 64 x 256 over eight
-// waves (two per SIMD), which forms it half as often and re-reads the rows
-// half as often (41 against 46 us at that shape); otherwise 64 x 128 over four.
-template <> struct OutCfg<bf16> : TileCfg<64, 256, 64, 2, 4, 2, 2> {};
-template <> struct OutCfg<float> : TileCfg<64, 128, 32, 2, 2, 1, 1> {};
-struct OutCfgNarrow : TileCfg<64, 128, 64, 2, 2, 2, 2> {};
+// multiply (gbar * v, then its parts), and every column tile of a row block
+// forms it again: where 256 divides d the tile is 64 x 256 over eight waves
+// (two per SIMD), which forms it half as often and re-reads the rows half as
+// often (41 against 46 us at that shape with two parts); otherwise 64 x 128
+// over four.
+template <> struct OutCfg<bf16, 2> : TileCfg<64, 256, 64, 2, 4, 2, 2> {};
+template <> struct OutCfg<bf16, 1> : TileCfg<64, 256, 64, 2, 4, 2, 1> {};
+template <> struct OutCfg<float, 1> : TileCfg<64, 128, 32, 2, 2, 1, 1> {};
+template <int AS> struct OutCfgNarrow : TileCfg<64, 128, 64, 2, 2, 2, AS> {};
 
 template <typename T> constexpr int piece_elems() { return 16 / (int)sizeof(T); }
 
@@ -472,10 +479,10 @@ __global__ __launch_bounds__(kThreads) void prep_kernel(ProjArgs args) {
 // KP: [W_g; W_v; W_q; W_k] projection of the prepared rows + epilogue.
 // 1-D grid over (M_pad / BM) x ceil(N / BN) tiles, N = 2F + 2HD, M_pad = B * Tp.
 // ---------------------------------------------------------------------------
-template <typename T, typename IO>
+template <typename T, typename IO, int AS>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2)))
 void proj_kernel(ProjArgs args) {
-  using CF = ProjCfg<T>;
+  using CF = ProjCfg<T, AS>;
   constexpr int PA = tile_chunks<CF, T>(CF::BM) / 4, PB = tile_chunks<CF, T>(CF::BN) / 4;
   extern __shared__ __align__(16) unsigned char smem_raw[];
   T* lds = reinterpret_cast<T*>(smem_raw);
@@ -766,18 +773,17 @@ __global__ __launch_bounds__(CF::NT) void out_kernel(OutArgs args) {
 // ---------------------------------------------------------------------------
 // Launchers
 // ---------------------------------------------------------------------------
-template <typename T, typename IO>
+template <typename T, typename IO, int AS>
 hipError_t launch_proj_t(const ProjArgs& a, hipStream_t s) {
-  using CF = ProjCfg<T>;
+  using CF = ProjCfg<T, AS>;
   const int64_t M = (int64_t)a.B * a.Tp;
-  hipLaunchKernelGGL((prep_kernel<T, IO, CF::AS>), dim3((unsigned)(M / (kThreads / 64))), dim3(kThreads),
-                     0, s, a);
+  hipLaunchKernelGGL((prep_kernel<T, IO, AS>), dim3((unsigned)(M / (kThreads / 64))), dim3(kThreads), 0, s, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const int N = 2 * a.F + 2 * a.HD;
   const int64_t tiles = (M / CF::BM) * ceil_div(N, CF::BN);
   const size_t lds = main_bytes<CF, T>();
-  hipLaunchKernelGGL((proj_kernel<T, IO>), dim3((unsigned)tiles), dim3(kThreads), lds, s, a);
+  hipLaunchKernelGGL((proj_kernel<T, IO, AS>), dim3((unsigned)tiles), dim3(kThreads), lds, s, a);
   return hipGetLastError();
 }
 
@@ -789,12 +795,12 @@ hipError_t launch_out_cf(const OutArgs& a, hipStream_t s) {
   hipLaunchKernelGGL((out_kernel<T, IO, CF>), dim3((unsigned)tiles), dim3(CF::NT), lds, s, a);
   return hipGetLastError();
 }
-template <typename T, typename IO>
+template <typename T, typename IO, int AS>
 hipError_t launch_out_t(const OutArgs& a, hipStream_t s) {
   if constexpr (std::is_same<T, bf16>::value) {
-    if (a.d % OutCfg<T>::BN != 0) return launch_out_cf<T, IO, OutCfgNarrow>(a, s);
+    if (a.d % OutCfg<T, AS>::BN != 0) return launch_out_cf<T, IO, OutCfgNarrow<AS>>(a, s);
   }
-  return launch_out_cf<T, IO, OutCfg<T>>(a, s);
+  return launch_out_cf<T, IO, OutCfg<T, AS>>(a, s);
 }
 
 // Pad columns of the head-padded packed gates: one 16-byte piece (8 rows of
@@ -813,12 +819,10 @@ __global__ void zero_pad_kernel(T* gp, int64_t M, int H, int Fh, int Fhp) {
   }
 }
 
-template <typename T, typename IO>
+template <typename T, typename IO, int AS>
 hipError_t launch_prep_t(const ProjArgs& a, hipStream_t s) {
-  using CF = ProjCfg<T>;
   const int64_t M = (int64_t)a.B * a.Tp;
-  hipLaunchKernelGGL((prep_kernel<T, IO, CF::AS>), dim3((unsigned)(M / (kThreads / 64))), dim3(kThreads),
-                     0, s, a);
+  hipLaunchKernelGGL((prep_kernel<T, IO, AS>), dim3((unsigned)(M / (kThreads / 64))), dim3(kThreads), 0, s, a);
   return hipGetLastError();
 }
 
@@ -833,23 +837,26 @@ hipError_t launch_zero_pad(void* gp, int64_t M, int H, int Fh, int Fhp, bool bf,
   return hipGetLastError();
 }
 
+// bf16 takes one or two operand parts (a.parts); float32 one.
 hipError_t launch_prep(const ProjArgs& a, bool bf, bool io_bf, hipStream_t s) {
-  if (bf) return io_bf ? launch_prep_t<bf16, bf16>(a, s) : launch_prep_t<bf16, float>(a, s);
-  return io_bf ? launch_prep_t<float, bf16>(a, s) : launch_prep_t<float, float>(a, s);
+  if (bf && a.parts == 2) return io_bf ? launch_prep_t<bf16, bf16, 2>(a, s) : launch_prep_t<bf16, float, 2>(a, s);
+  if (bf) return io_bf ? launch_prep_t<bf16, bf16, 1>(a, s) : launch_prep_t<bf16, float, 1>(a, s);
+  return io_bf ? launch_prep_t<float, bf16, 1>(a, s) : launch_prep_t<float, float, 1>(a, s);
 }
 
 hipError_t launch_proj(const ProjArgs& a, bool bf, bool io_bf, hipStream_t s) {
-  if (bf) return io_bf ? launch_proj_t<bf16, bf16>(a, s) : launch_proj_t<bf16, float>(a, s);
-  return io_bf ? launch_proj_t<float, bf16>(a, s) : launch_proj_t<float, float>(a, s);
+  if (bf && a.parts == 2) return io_bf ? launch_proj_t<bf16, bf16, 2>(a, s) : launch_proj_t<bf16, float, 2>(a, s);
+  if (bf) return io_bf ? launch_proj_t<bf16, bf16, 1>(a, s) : launch_proj_t<bf16, float, 1>(a, s);
+  return io_bf ? launch_proj_t<float, bf16, 1>(a, s) : launch_proj_t<float, float, 1>(a, s);
 }
 hipError_t launch_out(const OutArgs& a, bool bf, bool io_bf, hipStream_t s) {
-  if (bf) return io_bf ? launch_out_t<bf16, bf16>(a, s) : launch_out_t<bf16, float>(a, s);
-  return io_bf ? launch_out_t<float, bf16>(a, s) : launch_out_t<float, float>(a, s);
+  if (bf && a.parts == 2) return io_bf ? launch_out_t<bf16, bf16, 2>(a, s) : launch_out_t<bf16, float, 2>(a, s);
+  if (bf) return io_bf ? launch_out_t<bf16, bf16, 1>(a, s) : launch_out_t<bf16, float, 1>(a, s);
+  return io_bf ? launch_out_t<float, bf16, 1>(a, s) : launch_out_t<float, float, 1>(a, s);
 }
 
-size_t proj_parts_bytes(int64_t rows, int d, bool bf) {
-  const size_t per = bf ? (size_t)ProjCfg<bf16>::AS * sizeof(bf16) : (size_t)ProjCfg<float>::AS * sizeof(float);
-  return per * rows * d;
+size_t proj_parts_bytes(int64_t rows, int d, bool bf, int parts) {
+  return (size_t)(bf ? parts : 1) * (bf ? sizeof(bf16) : sizeof(float)) * rows * d;
 }
 
 namespace {
@@ -1269,16 +1276,22 @@ hipError_t gemm_kernels_init() {
   hipError_t e;
 #define TANGO_RAISE(K, BYTES) \
   if ((e = raise_lds(&K, BYTES)) != hipSuccess) return e;
-  TANGO_RAISE((proj_kernel<bf16, bf16>), (main_bytes<ProjCfg<bf16>, bf16>()))
-  TANGO_RAISE((proj_kernel<bf16, float>), (main_bytes<ProjCfg<bf16>, bf16>()))
-  TANGO_RAISE((proj_kernel<float, bf16>), (main_bytes<ProjCfg<float>, float>()))
-  TANGO_RAISE((proj_kernel<float, float>), (main_bytes<ProjCfg<float>, float>()))
-  TANGO_RAISE((out_kernel<bf16, bf16, OutCfg<bf16>>), (main_bytes<OutCfg<bf16>, bf16>()))
-  TANGO_RAISE((out_kernel<bf16, float, OutCfg<bf16>>), (main_bytes<OutCfg<bf16>, bf16>()))
-  TANGO_RAISE((out_kernel<bf16, bf16, OutCfgNarrow>), (main_bytes<OutCfgNarrow, bf16>()))
-  TANGO_RAISE((out_kernel<bf16, float, OutCfgNarrow>), (main_bytes<OutCfgNarrow, bf16>()))
-  TANGO_RAISE((out_kernel<float, bf16, OutCfg<float>>), (main_bytes<OutCfg<float>, float>()))
-  TANGO_RAISE((out_kernel<float, float, OutCfg<float>>), (main_bytes<OutCfg<float>, float>()))
+  TANGO_RAISE((proj_kernel<bf16, bf16, 2>), (main_bytes<ProjCfg<bf16, 2>, bf16>()))
+  TANGO_RAISE((proj_kernel<bf16, bf16, 1>), (main_bytes<ProjCfg<bf16, 1>, bf16>()))
+  TANGO_RAISE((proj_kernel<bf16, float, 2>), (main_bytes<ProjCfg<bf16, 2>, bf16>()))
+  TANGO_RAISE((proj_kernel<bf16, float, 1>), (main_bytes<ProjCfg<bf16, 1>, bf16>()))
+  TANGO_RAISE((proj_kernel<float, bf16, 1>), (main_bytes<ProjCfg<float, 1>, float>()))
+  TANGO_RAISE((proj_kernel<float, float, 1>), (main_bytes<ProjCfg<float, 1>, float>()))
+  TANGO_RAISE((out_kernel<bf16, bf16, OutCfg<bf16, 2>>), (main_bytes<OutCfg<bf16, 2>, bf16>()))
+  TANGO_RAISE((out_kernel<bf16, bf16, OutCfgNarrow<2>>), (main_bytes<OutCfgNarrow<2>, bf16>()))
+  TANGO_RAISE((out_kernel<bf16, float, OutCfg<bf16, 2>>), (main_bytes<OutCfg<bf16, 2>, bf16>()))
+  TANGO_RAISE((out_kernel<bf16, float, OutCfgNarrow<2>>), (main_bytes<OutCfgNarrow<2>, bf16>()))
+  TANGO_RAISE((out_kernel<bf16, bf16, OutCfg<bf16, 1>>), (main_bytes<OutCfg<bf16, 1>, bf16>()))
+  TANGO_RAISE((out_kernel<bf16, bf16, OutCfgNarrow<1>>), (main_bytes<OutCfgNarrow<1>, bf16>()))
+  TANGO_RAISE((out_kernel<bf16, float, OutCfg<bf16, 1>>), (main_bytes<OutCfg<bf16, 1>, bf16>()))
+  TANGO_RAISE((out_kernel<bf16, float, OutCfgNarrow<1>>), (main_bytes<OutCfgNarrow<1>, bf16>()))
+  TANGO_RAISE((out_kernel<float, bf16, OutCfg<float, 1>>), (main_bytes<OutCfg<float, 1>, float>()))
+  TANGO_RAISE((out_kernel<float, float, OutCfg<float, 1>>), (main_bytes<OutCfg<float, 1>, float>()))
 #undef TANGO_RAISE
   return hipSuccess;
 }

@@ -33,10 +33,12 @@ struct ProjArgs {
   int Fh, Fhp, Fp;     // gate columns per head, padded to a multiple of 64, and H * Fhp:
                        // gp holds head a's column c at a * Fhp + c (v is not padded)
   float rope_base, eps;
+  int parts;           // operand parts of h * gain in bf16 (1 or 2; float32: 1)
 };
 
-// Bytes of the operand parts xs for `rows` padded rows of width d.
-size_t proj_parts_bytes(int64_t rows, int d, bool bf);
+// Bytes of the operand parts xs for `rows` padded rows of width d (parts
+// counts for bf16 only).
+size_t proj_parts_bytes(int64_t rows, int d, bool bf, int parts);
 
 struct OutArgs {
   const void* x;       // [B, T, d] in the I/O dtype
@@ -45,6 +47,7 @@ struct OutArgs {
   const void* v;       // [B*Tp, F] float32
   void* out;           // [B, T, d] in the I/O dtype
   int B, T, Tp, d, F;
+  int parts;           // operand parts of gbar * v in bf16 (1 or 2; float32: 1)
 };
 
 // Aggregation (TANGO full prefix, or the WANGO window band + combine).

@@ -72,6 +72,8 @@ int head_pad(const tango_shape_t* s, bool wango) {
   return (fh + 63) / 64 * 64;
 }
 int64_t gate_pad(const tango_shape_t* s, bool wango) { return (int64_t)s->n_heads * head_pad(s, wango); }
+// Operand parts of the projection and output GEMMs' activation operand.
+int op_parts(const tango_shape_t* s) { return s->dtype == TANGO_BF16 && s->operand_parts == 2 ? 2 : 1; }
 
 // ---- validation -----------------------------------------------------------
 
@@ -91,6 +93,8 @@ int check_shape(const tango_shape_t* s) {
     return fail(TANGO_ERR_SHAPE, "rms_eps must be finite and > 0");
   if (!(s->rope_base >= 0.f) || !std::isfinite(s->rope_base))
     return fail(TANGO_ERR_SHAPE, "rope_base must be finite and >= 0");
+  if (s->operand_parts < 0 || s->operand_parts > 2 || (s->operand_parts == 2 && s->dtype != TANGO_BF16))
+    return fail(TANGO_ERR_SHAPE, "operand_parts %d: need 0 or 1, or 2 with dtype TANGO_BF16", s->operand_parts);
   if ((int64_t)s->batch * pad_rows(s->seq_len) > ((int64_t)1 << 26))
     return fail(TANGO_ERR_UNSUPPORTED, "batch * padded seq_len exceeds 2^26 rows");
   if (s->d_model % 128 != 0 || s->d_model > 4096)
@@ -195,7 +199,7 @@ Layout make_layout(const tango_shape_t* s, bool wango, int32_t window, int32_t c
   L.kh = take(M * HD * es);
   L.gbar = take(M * Fv * es);
   const bool bf = s->dtype == TANGO_BF16;
-  L.xs = take(proj_parts_bytes(M, s->d_model, bf));
+  L.xs = take(proj_parts_bytes(M, s->d_model, bf, op_parts(s)));
   L.rinv = take(M * sizeof(float));
   if (!wango) {
     L.agg = tango_agg_plan(s->batch, (int)pad_rows(s->seq_len), (int)F, s->n_heads, s->head_dim, bf);
@@ -278,6 +282,7 @@ ProjArgs proj_args(const tango_shape_t* s, const tango_weights_t* w, const void*
   a.dh = s->head_dim;
   a.rope_base = s->rope_base;
   a.eps = s->rms_eps;
+  a.parts = op_parts(s);
   return a;
 }
 
@@ -294,6 +299,7 @@ OutArgs out_args(const tango_shape_t* s, const void* w_o, const void* x, const v
   a.Tp = (int)pad_rows(s->seq_len);
   a.d = s->d_model;
   a.F = s->d_gate;
+  a.parts = op_parts(s);
   return a;
 }
 
@@ -364,7 +370,7 @@ struct ProjScratch {
 ProjScratch proj_scratch(const tango_shape_t* s) {
   const int64_t M = (int64_t)s->batch * pad_rows(s->seq_len);
   ProjScratch p{};
-  p.rinv = align256(proj_parts_bytes(M, s->d_model, s->dtype == TANGO_BF16));
+  p.rinv = align256(proj_parts_bytes(M, s->d_model, s->dtype == TANGO_BF16, op_parts(s)));
   p.total = p.rinv + M * sizeof(float);
   return p;
 }
@@ -1254,7 +1260,7 @@ DecLayout make_dec_layout(const tango_shape_t* s, bool wango, int32_t window) {
   L.state_total = off;
   off = 0;
   const bool bf = s->dtype == TANGO_BF16;
-  L.xs = take(proj_parts_bytes(L.Mp, s->d_model, bf));
+  L.xs = take(proj_parts_bytes(L.Mp, s->d_model, bf, decode_parts(bf)));
   L.rinv = take((size_t)L.Mp * sizeof(float));
   L.v = take((size_t)L.Mp * F * es);
   L.q = take((size_t)L.Mp * HD * es);
@@ -1342,6 +1348,7 @@ int decode_common(const tango_shape_t* s, const tango_weights_t* w, bool wango, 
   pa.Tp = (int)L.Mp;
   pa.d = s->d_model;
   pa.eps = s->rms_eps;
+  pa.parts = decode_parts(bf);
   pa.zero = reinterpret_cast<int*>(wb + L.ocount);   // the output GEMM's counters
   pa.zero_n = L.n_ocount;
   hipError_t e = launch_prep(pa, bf, io_bf, st);

@@ -44,7 +44,7 @@ def run_workload(w: wl.Workload, inp: wl.Inputs, device="cuda:0", x=None, ws=Non
     bw = block_weights(w, inp, device)
     if x is None:
         x = dev_tensor(inp.h, w.io, device)
-    shape = api.shape_of(x, bw, w.rope_base, w.rms_eps)
+    shape = api.shape_of(x, bw, w.rope_base, w.rms_eps, w.operand_parts)
     if ws is None:
         n = (api.tango_workspace_size(shape) if w.mode == "tango"
              else api.wango_workspace_size(shape, w.window, w.head_dim, w.chunk))
@@ -53,8 +53,9 @@ def run_workload(w: wl.Workload, inp: wl.Inputs, device="cuda:0", x=None, ws=Non
     for _ in range(w.repeats):
         if w.mode == "tango":
             api.tango_block_fwd(x, bw, out=x, ws=ws, rope_base=w.rope_base, rms_eps=w.rms_eps,
-                                stream=stream)
+                                stream=stream, operand_parts=w.operand_parts)
         else:
             api.wango_block_fwd(x, bw, w.window, w.head_dim, w.chunk, out=x, ws=ws,
-                                rope_base=w.rope_base, rms_eps=w.rms_eps, stream=stream)
+                                rope_base=w.rope_base, rms_eps=w.rms_eps, stream=stream,
+                                operand_parts=w.operand_parts)
     return x

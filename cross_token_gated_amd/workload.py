@@ -24,7 +24,11 @@ class Workload:
     intermediate activation ("f32" or "bf16"); accumulation is always float32.
     ``io_dtype`` is the dtype of the residual stream x/out between
     applications; the bf16 workloads carry it in float32.  The input values
-    are rounded to ``dtype`` in either case."""
+    are rounded to ``dtype`` in either case.  ``operand_parts`` is the number
+    of bf16 parts in which the float32 activation operand of the projection
+    and output GEMMs enters the MFMA: 1 is the plain bf16 compute; the long
+    stacks (eight shared-weight applications) take 2, without which their
+    first positions' rounding compounds past the 2e-2 bar."""
     name: str
     mode: str
     dtype: str
@@ -43,6 +47,7 @@ class Workload:
     rms_eps: float = 1e-6
     null_bias: Optional[float] = None  # None: null gate off
     io_dtype: str = ""                 # dtype of the residual stream x/out ("" = dtype)
+    operand_parts: int = 1             # bf16 parts of the GEMMs' activation operand
 
     @property
     def io(self) -> str:
@@ -71,7 +76,7 @@ WORKLOADS = {
                                       io_dtype="f32"),
     "wango_bf16_b2_t65536_w512_r8": Workload("wango_bf16_b2_t65536_w512_r8", "wango", "bf16", 2,
                                              65536, 512, 2048, 1, 128, window=512, chunk=128,
-                                             repeats=8, seed=4, io_dtype="f32"),
+                                             repeats=8, seed=4, io_dtype="f32", operand_parts=2),
 }
 WORKLOAD_ORDER = list(WORKLOADS)
 
@@ -139,7 +144,7 @@ STACK_WORKLOADS = {
     "tango_3set_bf16_t8192_r8": StackWorkload(
         "tango_3set_bf16_t8192_r8",
         Workload("tango_3set_bf16_t8192_r8", "tango", "bf16", 1, 8192, 512, 704, 1, 128, seed=10,
-                 io_dtype="f32"),
+                 io_dtype="f32", operand_parts=2),
         (704, 640, 704), three_set_schedule(8)),
 }
 

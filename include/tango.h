@@ -63,7 +63,7 @@
 extern "C" {
 #endif
 
-#define TANGO_ABI_VERSION 9
+#define TANGO_ABI_VERSION 10
 
 typedef enum { TANGO_F32 = 0, TANGO_BF16 = 1 } tango_dtype_t;
 
@@ -96,6 +96,16 @@ typedef struct {
                          applications)                                     */
   float rope_base;    /* RoPE base (10000 in the shipped workloads); 0 = off */
   float rms_eps;      /* RMSNorm epsilon (1e-6 in the shipped workloads)  */
+  int32_t operand_parts; /* How the float32 activation operand of the
+                         projection and output GEMMs (h*gain, gbar*v;
+                         [TANGO] §2.1 eqs. 2-3) enters the bf16 MFMA:
+                         0 or 1 = rounded once to bf16 (the pages' bf16
+                         compute); 2 = as two bf16 parts hi = bf16(e),
+                         lo = bf16(e - hi) summed into one float32
+                         accumulator (about 2^-16 relative, twice the MFMA
+                         work; for long shared-weight stacks).  2 requires
+                         dtype TANGO_BF16, else TANGO_ERR_SHAPE.  The
+                         decode step always takes two parts in bf16.      */
 } tango_shape_t;
 
 /* Block parameters ([TANGO] §2.1; the count in Table 1 fixes this list):

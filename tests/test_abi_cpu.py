@@ -76,6 +76,9 @@ def call_tango(lib, s, w=None, x=FAKE, out=FAKE + 0x60000000, ws=FAKE + 0x800000
     (dict(d_gate=2048, n_heads=3), "TANGO_ERR_SHAPE"),
     (dict(rms_eps=0.0), "TANGO_ERR_SHAPE"),
     (dict(rope_base=-1.0), "TANGO_ERR_SHAPE"),
+    (dict(operand_parts=3), "TANGO_ERR_SHAPE"),
+    (dict(operand_parts=-1), "TANGO_ERR_SHAPE"),
+    (dict(operand_parts=2, dtype=0, io_dtype=0), "TANGO_ERR_SHAPE"),
     (dict(d_model=448), "TANGO_ERR_UNSUPPORTED"),
     (dict(head_dim=96), "TANGO_ERR_UNSUPPORTED"),
     (dict(d_gate=2080), "TANGO_ERR_UNSUPPORTED"),
@@ -266,3 +269,14 @@ def test_noalloc_decode_validates_before_touching_the_device(lib):
     assert b"TANGO_NOALLOC_SCRATCH_BYTES" in lib.tango_last_error()
     m = re.search(r"#define TANGO_NOALLOC_SCRATCH_BYTES \(\(size_t\)(\d+) << (\d+)\)", open(HEADER).read())
     assert int(m.group(1)) << int(m.group(2)) == _lib.NOALLOC_SCRATCH_BYTES
+
+
+def test_operand_parts_size_the_projection_scratch(lib):
+    # two bf16 parts of h * gain need one more [rows, d] bf16 array than one part;
+    # 0 reads as one part
+    one = lib.tango_proj_workspace_size(ctypes.byref(shape(operand_parts=1)))
+    two = lib.tango_proj_workspace_size(ctypes.byref(shape(operand_parts=2)))
+    assert lib.tango_proj_workspace_size(ctypes.byref(shape(operand_parts=0))) == one
+    assert two - one >= 256 * 512 * 2
+    assert lib.tango_workspace_size(ctypes.byref(shape(operand_parts=2))) > \
+        lib.tango_workspace_size(ctypes.byref(shape(operand_parts=1)))

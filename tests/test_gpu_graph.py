@@ -51,18 +51,18 @@ def test_block_graph_replays(name):
     inp = wl.make_inputs(w)
     b = block_weights(w, inp, DEV)
     x = dev_tensor(inp.h, w.io, DEV)
-    shape = api.shape_of(x, b, w.rope_base, w.rms_eps)
+    shape = api.shape_of(x, b, w.rope_base, w.rms_eps, w.operand_parts)
     if w.mode == "tango":
         ws = api.workspace(api.tango_workspace_size(shape), DEV)
 
         def call(out):
-            api.tango_block_fwd(x, b, out=out, ws=ws, rope_base=w.rope_base, rms_eps=w.rms_eps)
+            api.tango_block_fwd(x, b, out=out, ws=ws, rope_base=w.rope_base, rms_eps=w.rms_eps, operand_parts=w.operand_parts)
     else:
         ws = api.workspace(api.wango_workspace_size(shape, w.window, w.head_dim, w.chunk), DEV)
 
         def call(out):
             api.wango_block_fwd(x, b, w.window, w.head_dim, w.chunk, out=out, ws=ws, rope_base=w.rope_base,
-                                rms_eps=w.rms_eps)
+                                rms_eps=w.rms_eps, operand_parts=w.operand_parts)
     announce(f"graph {name}: eager call")
     ref = torch.empty_like(x)
     call(ref)

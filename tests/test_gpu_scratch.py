@@ -54,14 +54,14 @@ def test_block_scratch_independent(name):
     inp = wl.make_inputs(w)
     b = block_weights(w, inp, DEV)
     x = dev_tensor(inp.h, w.io, DEV)
-    shape = api.shape_of(x, b, w.rope_base, w.rms_eps)
+    shape = api.shape_of(x, b, w.rope_base, w.rms_eps, w.operand_parts)
     if w.mode == "tango":
         n = api.tango_workspace_size(shape)
-        _twice(name, n, lambda ws: [api.tango_block_fwd(x, b, ws=ws, rope_base=w.rope_base, rms_eps=w.rms_eps)])
+        _twice(name, n, lambda ws: [api.tango_block_fwd(x, b, ws=ws, rope_base=w.rope_base, rms_eps=w.rms_eps, operand_parts=w.operand_parts)])
     else:
         n = api.wango_workspace_size(shape, w.window, w.head_dim, w.chunk)
         _twice(name, n, lambda ws: [api.wango_block_fwd(x, b, w.window, w.head_dim, w.chunk, ws=ws,
-                                                        rope_base=w.rope_base, rms_eps=w.rms_eps)])
+                                                        rope_base=w.rope_base, rms_eps=w.rms_eps, operand_parts=w.operand_parts)])
 
 
 def test_stack_scratch_independent():
@@ -70,10 +70,10 @@ def test_stack_scratch_independent():
         sets = [block_weights(sw.set_workload(k), inps[k], DEV) for k in range(len(sw.widths))]
         w = sw.base
         x = dev_tensor(inps[0].h, w.io, DEV)
-        shapes = [api.shape_of(x, s, w.rope_base, w.rms_eps) for s in sets]
+        shapes = [api.shape_of(x, s, w.rope_base, w.rms_eps, w.operand_parts) for s in sets]
         _twice(name, api.tango_stack_workspace_size(shapes),
                lambda ws: [api.tango_stack_fwd(x, sets, sw.schedule, ws=ws, rope_base=w.rope_base,
-                                               rms_eps=w.rms_eps)])
+                                               rms_eps=w.rms_eps, operand_parts=w.operand_parts)])
 
 
 @pytest.mark.parametrize("mode", ["tango", "wango"])
@@ -130,15 +130,15 @@ def test_concurrent_streams_share_nothing():
         inp = wl.make_inputs(w)
         b = block_weights(w, inp, DEV)
         x = dev_tensor(inp.h, w.io, DEV)
-        shape = api.shape_of(x, b, w.rope_base, w.rms_eps)
+        shape = api.shape_of(x, b, w.rope_base, w.rms_eps, w.operand_parts)
         if w.mode == "tango":
             ws = api.workspace(api.tango_workspace_size(shape), DEV)
             fn = (lambda x, b, w, ws: lambda out, s: api.tango_block_fwd(
-                x, b, out=out, ws=ws, rope_base=w.rope_base, rms_eps=w.rms_eps, stream=s))(x, b, w, ws)
+                x, b, out=out, ws=ws, rope_base=w.rope_base, rms_eps=w.rms_eps, operand_parts=w.operand_parts, stream=s))(x, b, w, ws)
         else:
             ws = api.workspace(api.wango_workspace_size(shape, w.window, w.head_dim, w.chunk), DEV)
             fn = (lambda x, b, w, ws: lambda out, s: api.wango_block_fwd(
-                x, b, w.window, w.head_dim, w.chunk, out=out, ws=ws, rope_base=w.rope_base, rms_eps=w.rms_eps,
+                x, b, w.window, w.head_dim, w.chunk, out=out, ws=ws, rope_base=w.rope_base, rms_eps=w.rms_eps, operand_parts=w.operand_parts,
                 stream=s))(x, b, w, ws)
         cases.append((name, x, fn))
     announce("scratch: the two blocks one after the other")

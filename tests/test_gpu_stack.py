@@ -29,7 +29,7 @@ def _run(sw: wl.StackWorkload, inps, in_place=True):
     w = sw.base
     x = dev_tensor(inps[0].h, w.io)
     out = x if in_place else torch.full_like(x, float("nan"))
-    api.tango_stack_fwd(x, sets, sw.schedule, out=out, rope_base=w.rope_base, rms_eps=w.rms_eps)
+    api.tango_stack_fwd(x, sets, sw.schedule, out=out, rope_base=w.rope_base, rms_eps=w.rms_eps, operand_parts=w.operand_parts)
     torch.cuda.synchronize()
     return host(out), host(x)
 

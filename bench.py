@@ -889,7 +889,9 @@ def main():
                    "wango": {"B": wg.B, "T": wg.T, "d_model": wg.d_model, "d_gate": wg.d_gate,
                              "qk_dim": HDg, "heads": wg.n_heads, "window": wg.window,
                              "phi_dim": wg.head_dim, "chunk": wg.chunk},
-                   "residual_dtype": "f32", "parallelism": "single GPU"},
+                   "residual_dtype": "f32",
+                   "gemm_operand_parts": {"tango": wt.operand_parts, "wango": wg.operand_parts},
+                   "parallelism": "single GPU"},
         "per_workload": {
             TANGO: {"tokens_per_s": wt.tokens / (ms_tango * 1e-3), "ms": ms_tango,
                     "ms_per_application": ms_tango / wt.repeats},

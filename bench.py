@@ -355,7 +355,7 @@ def configs_bench(steps: int, warmup: int, dev, stream, timed_batches) -> dict:
             M = w.B * api.padded_len(w.T)
             HD = w.n_heads * w.head_dim
             gp = torch.empty(M * w.d_gate, dtype=torch.bfloat16, device=dev)
-            v = torch.empty(M, w.d_gate, dtype=torch.float32, device=dev)
+            v = torch.empty(M, w.d_gate, dtype=api.v_dtype(shape), device=dev)
             qh = torch.empty(M, HD, dtype=torch.bfloat16, device=dev)
             kh = torch.empty(M, HD, dtype=torch.bfloat16, device=dev)
             fq = torch.empty(M, HD, dtype=torch.bfloat16, device=dev)
@@ -781,7 +781,7 @@ def main():
     M = wt.B * Tp
     F, HD = wt.d_gate, wt.n_heads * wt.head_dim
     gp = torch.empty(M * F, dtype=torch.bfloat16, device=dev)
-    v = torch.empty(M, F, dtype=torch.float32, device=dev)
+    v = torch.empty(M, F, dtype=api.v_dtype(st), device=dev)
     qh = torch.empty(M, HD, dtype=torch.bfloat16, device=dev)
     kh = torch.empty(M, HD, dtype=torch.bfloat16, device=dev)
     gbar = torch.empty(M, F, dtype=torch.bfloat16, device=dev)
@@ -840,7 +840,7 @@ def main():
     Mg = wg.B * api.padded_len(wg.T)
     HDg = wg.n_heads * wg.head_dim
     gpg = torch.empty(Mg * wg.d_gate, dtype=torch.bfloat16, device=dev)
-    vg = torch.empty(Mg, wg.d_gate, dtype=torch.float32, device=dev)
+    vg = torch.empty(Mg, wg.d_gate, dtype=api.v_dtype(sg), device=dev)
     qg = torch.empty(Mg, HDg, dtype=torch.bfloat16, device=dev)
     kg = torch.empty(Mg, HDg, dtype=torch.bfloat16, device=dev)
     fqg = torch.empty(Mg, HDg, dtype=torch.bfloat16, device=dev)
@@ -929,7 +929,7 @@ def main():
         torch.cuda.synchronize()
     # this build's projection (row prep + projection GEMM with its epilogue) and
     # output GEMM on the T = 8192 TANGO shapes, for the library comparison
-    vt = torch.empty(M, F, dtype=torch.float32, device=dev)
+    vt = torch.empty(M, F, dtype=api.v_dtype(st), device=dev)
     vt.copy_(v)
     ms_proj, _, _ = timed_batches(lambda: api.tango_stage_proj(st, bt, xt, gp, v, qh, kh, ws=ws_t, stream=stream),
                                   loops, 3)

@@ -130,6 +130,13 @@ def make_shape(B: int, T: int, d: int, F: int, H: int, dh: int, dtype: torch.dty
     return Shape(B, T, d, F, H, dh, _DTYPES[dtype], _DTYPES[io_dtype], rope_base, rms_eps, operand_parts)
 
 
+def v_dtype(shape: Shape) -> torch.dtype:
+    """dtype of the projection's v buffer: bfloat16 with bf16 compute and one
+    operand part, else float32."""
+    return torch.bfloat16 if shape.dtype == _DTYPES[torch.bfloat16] and shape.operand_parts <= 1 \
+        else torch.float32
+
+
 def shape_of(x: torch.Tensor, w: BlockWeights, rope_base: float = 10000.0,
              rms_eps: float = 1e-6, operand_parts: int = 1) -> Shape:
     """Shape of a call: compute dtype from the weights, I/O dtype from x.
@@ -259,7 +266,7 @@ def _check_proj(shape: Shape, w: BlockWeights, x, gp, v, qh, kh, wango: bool):
     check_tensor(x, "x", device=dev, dtype=z.io, min_numel=z.x)
     w.check(shape.d_model, dev)
     check_tensor(gp, "gp", device=dev, dtype=z.dt, min_numel=z.M * z.Fp)
-    check_tensor(v, "v", device=dev, dtype=torch.float32, min_numel=z.M * z.F)
+    check_tensor(v, "v", device=dev, dtype=v_dtype(shape), min_numel=z.M * z.F)
     check_tensor(qh, "qh", device=dev, dtype=z.dt, min_numel=z.M * z.HD)
     check_tensor(kh, "kh", device=dev, dtype=z.dt, min_numel=z.M * z.HD)
     return dev, z
@@ -396,7 +403,7 @@ def tango_stage_out(shape: Shape, w_o, x, gbar, v, out, stream=None) -> None:
     check_tensor(out, "out", device=dev, dtype=z.io, min_numel=z.x)
     check_tensor(w_o, "w_o", device=dev, dtype=z.dt, shape=(shape.d_model, shape.d_gate))
     check_tensor(gbar, "gbar", device=dev, dtype=z.dt, min_numel=z.M * z.F)
-    check_tensor(v, "v", device=dev, dtype=torch.float32, min_numel=z.M * z.F)
+    check_tensor(v, "v", device=dev, dtype=v_dtype(shape), min_numel=z.M * z.F)
     check(load().tango_stage_out(ctypes.byref(shape), _ptr(w_o), _ptr(x), _ptr(gbar), _ptr(v),
                                  _ptr(out), _stream(stream)))
 

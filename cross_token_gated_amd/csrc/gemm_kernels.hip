@@ -140,6 +140,12 @@ template <class CF, typename T> constexpr size_t main_bytes() {
 }
 
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+// v (the W_v projection) is stored in T with one bf16 operand part: the output
+// GEMM rounds gbar * v to bf16 anyway.  With two parts (and in float32) it is
+// float32, unrounded: the output GEMM then carries gbar * v to about 2^-16,
+// and a bf16 v would add a rounding that compounds through stacked
+// applications.
+template <typename T, int AS> constexpr bool v_half() { return std::is_same<T, bf16>::value && AS == 1; }
 // One 16-byte LDS piece per operand part.
 template <int AS> struct Parts {
   u32x4 p[AS];
@@ -357,28 +363,30 @@ __device__ __forceinline__ int pad_col(int n, int Fh, int Fhp) {
   return Fh == Fhp ? n : n + (n / Fh) * (Fhp - Fh);
 }
 
-// v is float32 for both dtypes (the projection stores it unrounded), so a
-// piece of PE gates meets PE / 4 16-byte loads of v.
+// A piece of PE gates meets the PE values of v in VP 16-byte loads (one when
+// v is stored in T, PE / 4 when it is float32).
 template <typename T, int P, int AS> struct GatedSource {
   static constexpr int PE = piece_elems<T>();
-  static constexpr int VP = PE / 4;
+  using VT = typename std::conditional<v_half<T, AS>(), T, float>::type;
+  static constexpr int VE = 16 / (int)sizeof(VT);   // v values per 16-byte load
+  static constexpr int VP = PE / VE;
   struct raw {
     u32x4 g;
     u32x4 v[VP];
   };
   const T* gptr[P];     // at the piece's row and column
-  const float* vptr[P];
+  const VT* vptr[P];
   __device__ __forceinline__ void fetch(raw& r, int p, int k0) const {
     r.g = *reinterpret_cast<const u32x4*>(gptr[p] + k0);
 #pragma unroll
-    for (int q = 0; q < VP; ++q) r.v[q] = *reinterpret_cast<const u32x4*>(vptr[p] + k0 + 4 * q);
+    for (int q = 0; q < VP; ++q) r.v[q] = *reinterpret_cast<const u32x4*>(vptr[p] + k0 + VE * q);
   }
   __device__ __forceinline__ Parts<AS> convert(const raw& r, int) const {
     const T* ge = reinterpret_cast<const T*>(&r.g);
-    const float* ve = reinterpret_cast<const float*>(&r.v[0]);
+    const VT* ve = reinterpret_cast<const VT*>(&r.v[0]);
     float e[PE];
 #pragma unroll
-    for (int q = 0; q < PE; ++q) e[q] = tof<T>(ge[q]) * ve[q];
+    for (int q = 0; q < PE; ++q) e[q] = tof<T>(ge[q]) * tof<VT>(ve[q]);
     return split_parts<T, AS, PE>(e);
   }
 };
@@ -601,10 +609,21 @@ void proj_kernel(ProjArgs args) {
         store_frag<T>(gp + packed_offset(mp / 32 + rb, grp, pad_col(n, args.Fh, args.Fhp), args.Fp), out);
       }
     }
-    // features: row-major [M_pad, F], float32 (unrounded: the output GEMM
-    // forms gbar * v in float32, and a bf16 v would add one more rounding
-    // that compounds through stacked applications)
-    if (n0 + CF::BN > F && n0 < 2 * F) {
+    // v: row-major [M_pad, F], in T with one bf16 operand part, else float32
+    // (v_half)
+    if (v_half<T, AS>() && n0 + CF::BN > F && n0 < 2 * F) {
+      T* v = static_cast<T*>(args.v);
+      constexpr int P8 = CF::BN / 8;
+      for (int it = tid; it < kEpiRows * P8; it += kThreads) {
+        const int row = it / P8, c = (it % P8) * 8;
+        const int n = n0 + c;
+        if (n < F || n >= 2 * F) continue;   // F is a multiple of 64: pieces lie on one side
+        Frag<T> o;
+#pragma unroll
+        for (int s = 0; s < 8; ++s) o[s] = cvt<T>(Cs[row * CF::CSTR + c + s]);
+        store_frag<T>(v + (mp + row) * F + (n - F), o);
+      }
+    } else if (n0 + CF::BN > F && n0 < 2 * F) {
       float* v = static_cast<float*>(args.v);
       constexpr int P4 = CF::BN / 4;
       for (int it = tid; it < kEpiRows * P4; it += kThreads) {
@@ -730,7 +749,7 @@ __global__ __launch_bounds__(CF::NT) void out_kernel(OutArgs args) {
     const PiecePos<CF, T> pp = piece_pos<CF, T>(tid, p);
     const int64_t off = (m0 + pp.row) * F + pp.kp * piece_elems<T>();
     sa.gptr[p] = static_cast<const T*>(args.gbar) + off;
-    sa.vptr[p] = static_cast<const float*>(args.v) + off;
+    sa.vptr[p] = static_cast<const typename GatedSource<T, PA, CF::AS>::VT*>(args.v) + off;
   }
   RowSource<T, PB> sb;
 #pragma unroll

@@ -74,6 +74,8 @@ int head_pad(const tango_shape_t* s, bool wango) {
 int64_t gate_pad(const tango_shape_t* s, bool wango) { return (int64_t)s->n_heads * head_pad(s, wango); }
 // Operand parts of the projection and output GEMMs' activation operand.
 int op_parts(const tango_shape_t* s) { return s->dtype == TANGO_BF16 && s->operand_parts == 2 ? 2 : 1; }
+// Bytes of one element of v: bf16 with one bf16 operand part, else float32.
+size_t v_elem(const tango_shape_t* s) { return s->dtype == TANGO_BF16 && op_parts(s) == 1 ? 2 : 4; }
 
 // ---- validation -----------------------------------------------------------
 
@@ -194,7 +196,7 @@ Layout make_layout(const tango_shape_t* s, bool wango, int32_t window, int32_t c
     return o;
   };
   L.gp = take(M * F * es);
-  L.v = take(M * Fv * sizeof(float));   // v is float32 for both dtypes
+  L.v = take(M * Fv * v_elem(s));
   L.qh = take(M * HD * es);
   L.kh = take(M * HD * es);
   L.gbar = take(M * Fv * es);
@@ -398,7 +400,7 @@ int stage_proj_common(const tango_shape_t* s, const tango_weights_t* weights, co
                        {weights->rms_gain, d * es, "rms_gain"},
                        {wango ? weights->theta : nullptr, s->n_heads * sizeof(float), "theta"}};
   const size_t Fp = gate_pad(s, wango);
-  const Range outs[] = {{gp, M * Fp * es, "gp"}, {v, M * F * sizeof(float), "v"}, {qh, M * HD * es, "qh"},
+  const Range outs[] = {{gp, M * Fp * es, "gp"}, {v, M * F * v_elem(s), "v"}, {qh, M * HD * es, "qh"},
                         {kh, M * HD * es, "kh"}, {ws, ps.total, "workspace"},
                         {fq, M * HD * es, "fq"}, {fk, M * HD * es, "fk"}};
   if ((rc = check_ranges(ins, 7, outs, wango ? 7 : 5, nullptr, nullptr))) return rc;
@@ -1122,7 +1124,7 @@ int tango_stage_out(const tango_shape_t* shape, const void* w_o, const void* x, 
     const size_t d = s->d_model, F = s->d_gate;
     const size_t xb = (size_t)s->batch * s->seq_len * d * elem_size(s->io_dtype);
     const Range ins[] = {{w_o, d * F * es, "w_o"}, {x, xb, "x"}, {gbar, M * F * es, "gbar"},
-                         {v, M * F * sizeof(float), "v"}};
+                         {v, M * F * v_elem(s), "v"}};
     const Range outs[] = {{out, xb, "out"}};
     if ((rc = check_ranges(ins, 4, outs, 1, x, out))) return rc;
     if ((rc = ensure_init())) return rc;

@@ -271,9 +271,11 @@ int tango_version(void);                      /* TANGO_ABI_VERSION              
  *   F'        = n_heads * Fhp: gp and n_old have F' columns, head a's gate
  *               column c at a * Fhp + c, and the projection stages write zeros
  *               into the gates' pad columns c >= Fh;
- *   V         = [B, Tp, d_gate] row-major, float32 for both dtypes (the
- *               output stage forms gbar * v in float32, so v is kept
- *               unrounded; not padded);
+ *   V         = [B, Tp, d_gate] row-major, not padded: bfloat16 with dtype
+ *               bf16 and one operand part (the output stage rounds gbar * v
+ *               to bf16 anyway), else float32 (with two parts the output
+ *               stage carries gbar * v to about 2^-16, so v is kept
+ *               unrounded);
  *   gbar      = [B, Tp, d_gate] row-major, dtype (not padded);
  *   qh, kh    = [B, Tp, H*d_h] row-major, dtype, unit length per head;
  *   gp        = the gates g in the source-packed layout [B][Tp/32][4][F'][8]:

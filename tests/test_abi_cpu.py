@@ -138,8 +138,11 @@ def test_workspace_sizes_cover_the_layout(lib):
     # and the float32 split partials
     n = lib.tango_workspace_size(ctypes.byref(shape(seq_len=8192)))
     assert n >= 3 * 8192 * 2048 * 2 + 2 * 8192 * 128 * 2
+    # gates, gbar and features in bf16; v in bf16 with one operand part, float32 with two
     n5 = lib.wango_workspace_size(ctypes.byref(shape(batch=2, seq_len=65536)), 512, 128, 128)
-    assert n5 >= 2 * 65536 * 2048 * (3 * 2 + 4)
+    assert n5 >= 2 * 65536 * 2048 * (3 * 2 + 2)
+    n5_two = lib.wango_workspace_size(ctypes.byref(shape(batch=2, seq_len=65536, operand_parts=2)), 512, 128, 128)
+    assert n5_two >= 2 * 65536 * 2048 * (3 * 2 + 4) and n5_two - n5 >= 2 * 65536 * 2048 * 2
 
 
 def test_stage_entry_points_validate(lib):

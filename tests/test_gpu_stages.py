@@ -78,7 +78,7 @@ def test_stage_proj(case, with_gain, op_parts):
     M = w.B * Tp
     dt = x.dtype
     gp = torch.full((M * F,), float("nan"), dtype=dt, device="cuda:0")
-    v = torch.full((M, F), float("nan"), dtype=torch.float32, device="cuda:0")
+    v = torch.full((M, F), float("nan"), dtype=api.v_dtype(shape), device="cuda:0")
     qh = torch.full((M, HD), float("nan"), dtype=dt, device="cuda:0")
     kh = torch.full((M, HD), float("nan"), dtype=dt, device="cuda:0")
     ws = api.workspace(api.tango_proj_workspace_size(shape), "cuda:0")
@@ -199,7 +199,8 @@ def test_stage_out(case, inplace, op_parts):
                            operand_parts=op_parts)
     announce(f"stage_out {case} inplace={inplace} op_parts={op_parts}")
     api.tango_stage_out(shape, dev_tensor(inp.w_o, w.dtype), x, dev_tensor(H.pad_rows(gbar, Tp), w.dtype),
-                        dev_tensor(H.pad_rows(v, Tp), "f32"), out)
+                        dev_tensor(H.pad_rows(v, Tp), "bf16" if api.v_dtype(shape) == torch.bfloat16 else "f32"),
+                        out)
     torch.cuda.synchronize()
     ref = np.asarray(inp.h, np.float64) + (gbar * v) @ np.asarray(inp.w_o, np.float64).T
     assert H.err_ratio(host(out), ref) < H.tol(w.dtype)
@@ -262,7 +263,7 @@ def test_stage_wango_proj(case, op_parts):
     M = w.B * Tp
     dt = x.dtype
     bufs = dict(gp=torch.full((M * F,), float("nan"), dtype=dt, device="cuda:0"),
-                v=torch.full((M, F), float("nan"), dtype=torch.float32, device="cuda:0"),
+                v=torch.full((M, F), float("nan"), dtype=api.v_dtype(shape), device="cuda:0"),
                 qh=torch.full((M, HD), float("nan"), dtype=dt, device="cuda:0"),
                 kh=torch.full((M, HD), float("nan"), dtype=dt, device="cuda:0"),
                 fq=torch.full((M, HD), float("nan"), dtype=dt, device="cuda:0"),

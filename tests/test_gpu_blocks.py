@@ -68,6 +68,25 @@ def test_workload_full_size(name):
     assert e < H.tol(w.dtype)
 
 
+@pytest.mark.parametrize("name", ["tango_bf16_t8192_r4", "wango_bf16_t8192_w256"])
+def test_two_operand_parts_full_size(name):
+    """The bench workloads with the activation operand of both GEMMs carried as
+    two bf16 parts (and v in float32): the bar holds, and the error is no larger
+    than with one part (the second part only removes a rounding)."""
+    w1 = wl.WORKLOADS[name]
+    w2 = w1.scaled(operand_parts=2)
+    inp = wl.make_inputs(w1)
+    ref = H.oracle_stack(w1, inp)
+    errs = []
+    for w in (w1, w2):
+        announce(f"workload {name} operand_parts={w.operand_parts}")
+        out = run_workload(w, inp)
+        torch.cuda.synchronize()
+        errs.append(H.err_ratio(host(out), ref))
+    print(f"{name}: max|err|/rms with one operand part {errs[0]:.3e}, with two {errs[1]:.3e}")
+    assert errs[1] < H.tol(w2.dtype) and errs[1] <= errs[0]
+
+
 @pytest.mark.parametrize("repeats", [1, 4])
 def test_bf16_residual_full_size(repeats):
     """The T = 8192 TANGO workload with the residual stream x/out stored in

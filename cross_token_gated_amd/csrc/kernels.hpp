@@ -19,7 +19,7 @@ struct ProjArgs {
   const void* w_k;     // [HD, d]
   const void* gain;    // [d] or null
   void* gp;            // packed gates [B*Tp/32][4][F][8]
-  void* v;             // [B*Tp, F] float32
+  void* v;             // [B*Tp, F]: bf16 with one bf16 operand part, else float32
   void* qh;            // [B*Tp, HD]
   void* kh;            // [B*Tp, HD]
   void* fq;            // WANGO only (else null): phi(sqrt(tau) q) [B*Tp, HD], permuted feature order
@@ -44,7 +44,7 @@ struct OutArgs {
   const void* x;       // [B, T, d] in the I/O dtype
   const void* w_o;     // [d, F]
   const void* gbar;    // [B*Tp, F]
-  const void* v;       // [B*Tp, F] float32
+  const void* v;       // [B*Tp, F]: bf16 with one bf16 operand part, else float32
   void* out;           // [B, T, d] in the I/O dtype
   int B, T, Tp, d, F;
   int parts;           // operand parts of gbar * v in bf16 (1 or 2; float32: 1)
